@@ -1,0 +1,110 @@
+"""Reference (oracle) for the Kimi Delta Attention operator -- TEST INFRASTRUCTURE ONLY.
+
+This module is the slow, obviously-correct CPU definition that the HIP library is checked
+against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it; the product path never does.  It shares no code with the HIP
+library (the two meet only in the seeded input generators, which hold none of the method's
+arithmetic).
+
+What it computes (Kimi K3: Open Frontier Intelligence, §2.1.1, eq. (1)): for every sequence n
+and head h independently, starting from the entering state S0[n, h] (zeros when absent), every
+token t applies
+
+    S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
+
+with alpha_t = exp(g_t) per key channel (§2.1.1, eq. (5): g is a natural-log decay).  The
+channel-wise decay acts before the delta-rule erase/write (the text right above eq. (1)), and
+the output reads the state after the current token's update (the remark under eq. (4) that the
+causal mask keeps its diagonal for this reason).  The loop below is the same update written
+without the dense dk x dk matrix: decay the rows of S, form the delta-rule residual
+u = beta (v - S^T k) against the decayed state, add the rank-one write k u^T, read out S^T q.
+
+Every input is upcast from its stored dtype to float64; the arithmetic is float64 throughout.
+``scale`` multiplies q (eq. (1) has no scale; tests pass 1.0).
+
+Pinned by tests/test_oracle_pins.py: closed forms (beta = 0, a single token, orthonormal keys
+with g = 0), exact rational brute force on tiny shapes, read-after-write, linearity/affinity in
+(V, S0) (§5.1.2, eq. (17)), resume, varlen independence, and agreement with the independent
+chunkwise algorithm in ``oracle/chunkwise.py`` for every chunk size.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x):
+    """Stored values -> float64 numpy (accepts numpy arrays or CPU torch tensors)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: go through float32 first (bf16 is exact in fp32)
+        x = x.detach().cpu()
+        if x.dtype != x.new_zeros(()).double().dtype:
+            x = x.float()
+        x = x.double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def kda_token_step(S, q, k, v, g, beta, scale=1.0):
+    """One token of eq. (1) on one head.  S: [dk, dv] float64 (not modified).
+
+    Returns (o [dv], S_new [dk, dv])."""
+    S = np.exp(g)[:, None] * S                # Diag(alpha_t) S_{t-1}
+    u = beta * (v - S.T @ k)                  # delta-rule residual against the decayed state
+    S = S + np.outer(k, u)                    # (I - beta k k^T) Diag(alpha) S + beta k v^T
+    o = S.T @ (scale * q)                     # read-out after the update
+    return o, S
+
+
+def _sequence_bounds(B, T, cu_seqlens):
+    if cu_seqlens is None:
+        return [(b, 0, T) for b in range(B)]
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    if B != 1:
+        raise ValueError("packed (cu_seqlens) inputs have batch dimension 1")
+    if cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu[:-1], cu[1:])):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+
+
+def kda_forward(q, k, v, g, beta, S0=None, cu_seqlens=None, scale=1.0, heads=None):
+    """Token-by-token KDA over whole sequences.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv]; g: [B, T, H, dk] (natural-log decay);
+    beta: [B, T, H]; S0: [N, H, dk, dv] or None (zeros); cu_seqlens: None (N = B, one
+    sequence per row) or int array [N + 1] with B = 1 (packed sequences).
+    ``heads``: optional list of head indices to evaluate (others are left zero).
+
+    Returns (o [B, T, H, dv] float64, S_T [N, H, dk, dv] float64)."""
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    seqs = _sequence_bounds(B, T, cu_seqlens)
+    N = len(seqs)
+    S0 = np.zeros((N, H, dk, dv)) if S0 is None else _f64(S0)
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((N, H, dk, dv))
+    for n, (b, bos, eos) in enumerate(seqs):
+        for h in (range(H) if heads is None else heads):
+            S = S0[n, h].copy()
+            for t in range(bos, eos):
+                o[b, t, h], S = kda_token_step(S, q[b, t, h], k[b, t, h], v[b, t, h],
+                                               g[b, t, h], beta[b, t, h], scale)
+            ST[n, h] = S
+    return o, ST
+
+
+def kda_decode_step(q, k, v, g, beta, S, scale=1.0):
+    """One decode token per (sequence, head): eq. (1) with T = 1 (§5.4.2: the state is updated
+    in place every step; here the new state is returned).
+
+    q, k: [N, H, dk]; v: [N, H, dv]; g: [N, H, dk]; beta: [N, H]; S: [N, H, dk, dv].
+    Returns (o [N, H, dv], S_new [N, H, dk, dv]) in float64."""
+    q, k, v, g, beta, S = (_f64(a) for a in (q, k, v, g, beta, S))
+    N, H = q.shape[:2]
+    o = np.zeros(v.shape)
+    Snew = np.zeros(S.shape)
+    for n in range(N):
+        for h in range(H):
+            o[n, h], Snew[n, h] = kda_token_step(S[n, h], q[n, h], k[n, h], v[n, h],
+                                                 g[n, h], beta[n, h], scale)
+    return o, Snew

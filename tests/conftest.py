@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libkda")
+    config.addinivalue_line("markers", "slow: long-running GPU parity case at full workload size")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP library, loaded for GPU tests; fails loudly if it is missing."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected on a machine without a GPU")
+    from linear_attention_chunkwise_amd import binding
+    binding.load()
+    return binding

@@ -1,0 +1,374 @@
+"""Pins of the reference implementations against what the pages and the mathematics fix.
+
+Each pin is a function of a forward callable ``fwd(q, k, v, g, beta, S0, cu_seqlens) -> (o, S_T)``
+that returns an error; the numpy oracle and the C oracle must both pass every pin, and planted
+mistakes (in copies of the oracle, on the CPU) must each fail at least one pin.
+
+Sources (Kimi K3: Open Frontier Intelligence):
+- §2.1.1 eq. (1): the recurrence, decay before the delta update, output after the update;
+- §2.1.1 eqs. (3)-(4): the chunkwise form (exact algebra, so chunk-size invariant);
+- §2.1.1 eq. (5) and the paragraph after it: g in (g_min, 0), g_min = -5, the printed bounds;
+- §5.1.2 eq. (17): the state after a segment is affine in the entering state, S = M S0 + S~.
+DeltaNet (the recurrence with no decay) is the g = 0 special case named at the top of §2.1.1.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import c_oracle, chunkwise, kda_oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _np_fwd(q, k, v, g, beta, S0=None, cu=None):
+    return kda_oracle.kda_forward(q, k, v, g, beta, S0, cu)
+
+
+def _c_fwd(q, k, v, g, beta, S0=None, cu=None):
+    return c_oracle.kda_forward(q, k, v, g, beta, S0, cu)
+
+
+FORWARDS = {"numpy": _np_fwd, "c": _c_fwd}
+
+
+def _rand_inputs(B=1, T=24, H=2, dk=6, dv=5, seed=0, g_scale=1.0, beta_one=False,
+                 S0_std=0.3, cu=None):
+    """float32-stored inputs (every value exact in float64)."""
+    gen = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, T, H, dk, generator=gen)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = torch.randn(B, T, H, dk, generator=gen)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn(B, T, H, dv, generator=gen)
+    g = (-5.0 * torch.sigmoid(torch.randn(B, T, H, dk, generator=gen))) * g_scale
+    beta = torch.ones(B, T, H) if beta_one else torch.sigmoid(torch.randn(B, T, H, generator=gen))
+    N = B if cu is None else len(cu) - 1
+    S0 = torch.randn(N, H, dk, dv, generator=gen) * S0_std
+    return q.float(), k.float(), v.float(), g.float(), beta.float(), S0.float()
+
+
+def _f64(t):
+    return t.double().numpy()
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# ----------------------------------------------------------------------------- pin functions
+
+def pin_beta_zero(fwd):
+    """beta = 0: pure per-channel decay.  S_T = Diag(exp(sum g)) S0 and
+    o_t = S0^T (exp(G_t) * q_t) with G_t the running sum of g (eq. (1) with the write off)."""
+    q, k, v, g, beta, S0 = _rand_inputs(T=20, dk=6, dv=4)
+    beta = torch.zeros_like(beta)
+    o, ST = fwd(q, k, v, g, beta, S0)
+    G = np.cumsum(_f64(g)[0], axis=0)                       # [T, H, dk]
+    o_exp = np.einsum("hcd,thc->thd", _f64(S0)[0], np.exp(G) * _f64(q)[0])
+    ST_exp = np.exp(G[-1])[:, :, None] * _f64(S0)[0]
+    return max(_rel(o[0], o_exp), _rel(ST[0], ST_exp))
+
+
+def pin_single_token_dense(fwd):
+    """One token, eq. (1) evaluated literally with dense matrices:
+    S_1 = (I - beta k k^T) Diag(alpha) S0 + beta k v^T,  o = S_1^T q."""
+    q, k, v, g, beta, S0 = _rand_inputs(T=1, H=3, dk=5, dv=7, seed=3)
+    o, ST = fwd(q, k, v, g, beta, S0)
+    err = 0.0
+    for h in range(3):
+        qq, kk, vv = _f64(q)[0, 0, h], _f64(k)[0, 0, h], _f64(v)[0, 0, h]
+        a = np.exp(_f64(g)[0, 0, h])
+        b = float(beta[0, 0, h])
+        S1 = (np.eye(5) - b * np.outer(kk, kk)) @ np.diag(a) @ _f64(S0)[0, h] + b * np.outer(kk, vv)
+        err = max(err, _rel(ST[0, h], S1), _rel(o[0, 0, h], S1.T @ qq))
+    return err
+
+
+def pin_orthonormal_overwrite(fwd):
+    """g = 0 (DeltaNet), beta = 1, k_t = e_{j(t)}: each token overwrites row j(t) of the state
+    with v_t exactly, so S_T[j] = v at the last t with j(t) = j (else S0[j]) and
+    o_t = S_t^T q_t."""
+    T, dk, dv = 12, 4, 3
+    gen = torch.Generator().manual_seed(5)
+    js = [int(x) for x in torch.randint(0, dk - 1, (T,), generator=gen)]   # row dk-1 untouched
+    k = torch.zeros(1, T, 1, dk)
+    for t, j in enumerate(js):
+        k[0, t, 0, j] = 1.0
+    q = torch.randn(1, T, 1, dk, generator=gen)
+    v = torch.randn(1, T, 1, dv, generator=gen)
+    g = torch.zeros(1, T, 1, dk)
+    beta = torch.ones(1, T, 1)
+    S0 = torch.randn(1, 1, dk, dv, generator=gen)
+    o, ST = fwd(q, k, v, g, beta, S0)
+    S = _f64(S0)[0, 0].copy()
+    err = 0.0
+    for t, j in enumerate(js):
+        S[j] = _f64(v)[0, t, 0]
+        err = max(err, float(np.abs(o[0, t, 0] - S.T @ _f64(q)[0, t, 0]).max()))
+    return max(err, float(np.abs(ST[0, 0] - S).max()))
+
+
+def pin_read_after_write(fwd):
+    """beta = 1 and |k| = 1: after token t the state maps k_t to v_t exactly (the delta rule
+    writes the residual so that S_t^T k_t = v_t).  Checked through o_t with q_t = k_t."""
+    q, k, v, g, beta, S0 = _rand_inputs(T=16, dk=8, dv=5, seed=7, beta_one=True)
+    k = k.double()
+    k = (k / k.norm(dim=-1, keepdim=True)).float()
+    o, _ = fwd(k, k, v, g, beta, S0)
+    kn = np.linalg.norm(_f64(k), axis=-1)                     # float32 rounding of |k| ~ 1e-7
+    assert np.abs(kn - 1).max() < 1e-6
+    return float(np.abs(o - _f64(v)).max())
+
+
+def pin_brute_force_rational(fwd):
+    """Exact rational arithmetic on a tiny case: the dense products of eq. (1) over 5 tokens with
+    dk = 2, dv = 3, all inputs dyadic (exact in float32) and alpha = exp(g) taken as the exact
+    rational value of the float64 exp.  Returns the relative error of the oracle."""
+    T, dk, dv = 5, 2, 3
+    gen = torch.Generator().manual_seed(11)
+
+    def dy(shape, den=64):
+        return (torch.randint(-den, den + 1, shape, generator=gen).float() / den)
+
+    q, k, v = dy((1, T, 1, dk)), dy((1, T, 1, dk)), dy((1, T, 1, dv))
+    g = -(torch.randint(1, 64, (1, T, 1, dk), generator=gen).float() / 16)
+    beta = torch.randint(1, 16, (1, T, 1), generator=gen).float() / 16
+    S0 = dy((1, 1, dk, dv))
+    o, ST = fwd(q, k, v, g, beta, S0)
+
+    F = Fraction
+    S = [[F(float(S0[0, 0, i, j])) for j in range(dv)] for i in range(dk)]
+    o_exact = []
+    for t in range(T):
+        kk = [F(float(k[0, t, 0, i])) for i in range(dk)]
+        qq = [F(float(q[0, t, 0, i])) for i in range(dk)]
+        vv = [F(float(v[0, t, 0, j])) for j in range(dv)]
+        al = [F(math.exp(float(g[0, t, 0, i]))) for i in range(dk)]
+        b = F(float(beta[0, t, 0]))
+        M = [[(1 if i == r else 0) - b * kk[i] * kk[r] for r in range(dk)] for i in range(dk)]
+        DS = [[al[r] * S[r][j] for j in range(dv)] for r in range(dk)]
+        S = [[sum(M[i][r] * DS[r][j] for r in range(dk)) + b * kk[i] * vv[j] for j in range(dv)]
+             for i in range(dk)]
+        o_exact.append([sum(S[i][j] * qq[i] for i in range(dk)) for j in range(dv)])
+    oe = np.array([[float(x) for x in row] for row in o_exact])
+    Se = np.array([[float(x) for x in row] for row in S])
+    return max(_rel(o[0, :, 0], oe), _rel(ST[0, 0], Se))
+
+
+def pin_chunkwise(fwd, chunks=(1, 2, 3, 4, 8, 16, 32, 64, 96)):
+    """The chunkwise form (eqs. (3)-(4), with the UT transform written out) is exact algebra, so
+    the independent chunkwise algorithm must reproduce the token loop for every chunk size."""
+    q, k, v, g, beta, S0 = _rand_inputs(T=96, H=2, dk=16, dv=8, seed=13)
+    o, ST = fwd(q, k, v, g, beta, S0)
+    err = 0.0
+    for C in chunks:
+        oc, STc = chunkwise.kda_forward_chunkwise(_f64(q)[0], _f64(k)[0], _f64(v)[0], _f64(g)[0],
+                                                  _f64(beta)[0], _f64(S0)[0], chunk=C)
+        err = max(err, _rel(o[0], oc), _rel(ST[0], STc))
+    return err
+
+
+def pin_affine_transition(fwd):
+    """eq. (17): the state after a segment is S = M S0 + S~, where S~ is the state reached from
+    S0 = 0 and M (dk x dk) is the product of the per-token transitions, obtained by running the
+    same recurrence on V = 0 with S0 = I.  Also linear in (V, S0) jointly."""
+    q, k, v, g, beta, S0 = _rand_inputs(T=30, H=2, dk=6, dv=4, seed=17)
+    _, ST = fwd(q, k, v, g, beta, S0)
+    _, S_tilde = fwd(q, k, v, g, beta, torch.zeros_like(S0))
+    eye = torch.eye(6).expand(1, 2, 6, 6).contiguous()
+    _, M = fwd(q, k, torch.zeros(1, 30, 2, 6), g, beta, eye)
+    pred = np.einsum("nhij,nhjd->nhid", M, _f64(S0)) + S_tilde
+    err = _rel(ST, pred)
+    # joint linearity in (V, S0); dyadic values keep v + 2 v2 and S0 + 2 S02 exact in float32
+    def dyadic(t):
+        return torch.round(t * 256) / 256
+    v, S0 = dyadic(v), dyadic(S0)
+    v2 = dyadic(torch.randn(v.shape, generator=torch.Generator().manual_seed(1)))
+    S02 = dyadic(torch.randn(S0.shape, generator=torch.Generator().manual_seed(2)))
+    o1, ST1 = fwd(q, k, v, g, beta, S0)
+    o2, ST2 = fwd(q, k, v2, g, beta, S02)
+    o3, ST3 = fwd(q, k, v + 2 * v2, g, beta, S0 + 2 * S02)
+    return max(err, _rel(o3, o1 + 2 * o2), _rel(ST3, ST1 + 2 * ST2))
+
+
+def pin_resume(fwd):
+    """Running a sequence in two pieces, the second entered with the first's final state, gives
+    the same outputs and final state (eq. (17) with two segments)."""
+    q, k, v, g, beta, S0 = _rand_inputs(T=40, H=2, dk=5, dv=6, seed=19)
+    o, ST = fwd(q, k, v, g, beta, S0)
+    t = 17
+    oa, Sa = fwd(q[:, :t], k[:, :t], v[:, :t], g[:, :t], beta[:, :t], S0)
+    ob, Sb = fwd(q[:, t:], k[:, t:], v[:, t:], g[:, t:], beta[:, t:], torch.from_numpy(Sa).float())
+    # Sa is rounded to float32 when re-entered; allow that rounding.
+    return max(_rel(o, np.concatenate([oa, ob], axis=1)), _rel(ST, Sb)) * 1e-2
+
+
+def pin_varlen_independence(fwd):
+    """Packed sequences are independent: the packed call equals separate calls."""
+    lens = [5, 0, 13, 1, 9]
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    q, k, v, g, beta, S0 = _rand_inputs(B=1, T=cu[-1], H=2, dk=4, dv=3, seed=23, cu=cu)
+    o, ST = fwd(q, k, v, g, beta, S0, cu)
+    err = 0.0
+    for n in range(len(lens)):
+        s, e = cu[n], cu[n + 1]
+        on, STn = fwd(q[:, s:e], k[:, s:e], v[:, s:e], g[:, s:e], beta[:, s:e], S0[n:n + 1])
+        d_o = np.abs(o[:, s:e] - on)
+        err = max(err, float(d_o.max()) if d_o.size else 0.0, float(np.abs(ST[n] - STn[0]).max()))
+    return err
+
+
+PINS = {
+    "beta_zero": (pin_beta_zero, 1e-13),
+    "single_token_dense": (pin_single_token_dense, 1e-13),
+    "orthonormal_overwrite": (pin_orthonormal_overwrite, 1e-13),
+    "read_after_write": (pin_read_after_write, 1e-5),
+    "brute_force_rational": (pin_brute_force_rational, 1e-13),
+    "chunkwise": (pin_chunkwise, 1e-11),
+    "affine_transition": (pin_affine_transition, 1e-12),
+    "resume": (pin_resume, 1e-8),
+    "varlen_independence": (pin_varlen_independence, 0.0),
+}
+
+
+@pytest.mark.parametrize("impl", sorted(FORWARDS))
+@pytest.mark.parametrize("pin", sorted(PINS))
+def test_pin(impl, pin):
+    fn, tol = PINS[pin]
+    err = fn(FORWARDS[impl])
+    assert err <= tol, f"{impl} oracle fails pin {pin}: error {err:.3e} > {tol:.1e}"
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def _mutant(step):
+    def fwd(q, k, v, g, beta, S0=None, cu=None):
+        orig = kda_oracle.kda_token_step
+        kda_oracle.kda_token_step = step
+        try:
+            return kda_oracle.kda_forward(q, k, v, g, beta, S0, cu)
+        finally:
+            kda_oracle.kda_token_step = orig
+    return fwd
+
+
+def _read_before_update(S, q, k, v, g, beta, scale=1.0):
+    S = np.exp(g)[:, None] * S
+    o = S.T @ q
+    S = S + np.outer(k, beta * (v - S.T @ k))
+    return o, S
+
+
+def _decay_after_delta(S, q, k, v, g, beta, scale=1.0):
+    S = S + np.outer(k, beta * (v - S.T @ k))
+    S = np.exp(g)[:, None] * S
+    return S.T @ q, S
+
+
+def _decay_on_columns(S, q, k, v, g, beta, scale=1.0):
+    a = np.exp(g)
+    S = S * np.resize(a, S.shape[1])[None, :]
+    S = S + np.outer(k, beta * (v - S.T @ k))
+    return S.T @ q, S
+
+
+def _sign_flip(S, q, k, v, g, beta, scale=1.0):
+    S = np.exp(g)[:, None] * S
+    S = S + np.outer(k, beta * (v + S.T @ k))
+    return S.T @ q, S
+
+
+def _residual_on_old_state(S, q, k, v, g, beta, scale=1.0):
+    u = beta * (v - S.T @ k)
+    S = np.exp(g)[:, None] * S + np.outer(k, u)
+    return S.T @ q, S
+
+
+def _beta_dropped(S, q, k, v, g, beta, scale=1.0):
+    S = np.exp(g)[:, None] * S
+    S = S + np.outer(k, (v - S.T @ k))
+    return S.T @ q, S
+
+
+def _base2_decay(S, q, k, v, g, beta, scale=1.0):
+    S = np.exp2(g)[:, None] * S
+    S = S + np.outer(k, beta * (v - S.T @ k))
+    return S.T @ q, S
+
+
+MUTANTS = {
+    "read_before_update": _read_before_update,
+    "decay_after_delta": _decay_after_delta,
+    "decay_on_columns": _decay_on_columns,
+    "sign_flip": _sign_flip,
+    "residual_on_old_state": _residual_on_old_state,
+    "beta_dropped": _beta_dropped,
+    "base2_decay": _base2_decay,
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    fwd = _mutant(MUTANTS[name])
+    failed = []
+    for pin, (fn, tol) in PINS.items():
+        if pin in ("chunkwise",):
+            continue  # the chunkwise algorithm is independent; compare via closed forms only
+        try:
+            if fn(fwd) > max(tol, 1e-9):
+                failed.append(pin)
+        except AssertionError:
+            failed.append(pin)
+    assert failed, f"planted mistake {name} passes every pin"
+
+
+def test_chunkwise_catches_planted_mistakes():
+    """The chunkwise cross-check alone also rejects each planted mistake."""
+    for name, step in MUTANTS.items():
+        assert pin_chunkwise(_mutant(step), chunks=(16,)) > 1e-6, name
+
+
+# ----------------------------------------------------------------------------- page constants
+
+def test_page_decay_bounds():
+    """The numbers printed after eq. (5): exp(-5) ~ 6.7e-3, 16-token log-decay > -80, and
+    exp(80) inside the BF16 range; the synthetic gate respects them."""
+    d = json.load(open(os.path.join(GOLDEN, "decay_bounds.json")))
+    assert abs(math.exp(d["g_min"]) - d["alpha_lower_bound_printed"]) < 0.05e-3
+    assert d["tile_tokens"] * d["g_min"] == d["tile_log_decay_lower_bound"]
+    assert math.exp(d["reciprocal_bound_log"]) < d["bf16_max"]
+    bf16_max = float(torch.finfo(torch.bfloat16).max)
+    assert bf16_max == d["bf16_max"]
+    from linear_attention_chunkwise_amd import inputs
+    x = inputs.make_prefill_inputs(1, 256, 4, 32, 8, seed=3, near_gmin_frac=0.1)
+    g = x["g"].double()
+    assert float(g.max()) < 0 and float(g.min()) > d["g_min"]
+    win = g.unfold(1, 16, 1).sum(-1)
+    assert float(win.min()) > d["tile_log_decay_lower_bound"]
+
+
+def test_c_matches_numpy_on_bf16():
+    """The two token loops agree on bf16-stored inputs with packed sequences."""
+    from linear_attention_chunkwise_amd import inputs
+    cu = inputs.cu_from_lengths([7, 33, 1, 20])
+    x = inputs.make_prefill_inputs(1, int(cu[-1]), 3, 16, 12, seed=4, cu_seqlens=cu)
+    a = kda_oracle.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], cu)
+    b = c_oracle.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], cu)
+    assert _rel(b[0], a[0]) < 1e-13 and _rel(b[1], a[1]) < 1e-13
+
+
+def test_decode_step_is_one_token():
+    from linear_attention_chunkwise_amd import inputs
+    x = inputs.make_decode_inputs(3, 2, 8, 6, seed=2)
+    o, S = kda_oracle.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S"])
+    o2, S2 = kda_oracle.kda_forward(x["q"][:, None], x["k"][:, None], x["v"][:, None],
+                                    x["g"][:, None], x["beta"][:, None], x["S"])
+    assert np.array_equal(o, o2[:, 0]) and np.array_equal(S, S2)
