@@ -1,0 +1,167 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic batch:
+  * kda_chunk_fwd on the prefill workload B=4, H=32, T=32768, dk=dv=128 (bf16 q/k/v/beta,
+    float32 g and state, bf16 output, final state returned), and
+  * kda_recurrent_step on the decode workload 1024 sequences x 32 heads (float32 128x128 states
+    updated in place, one token each).
+Inputs are generated on the GPU before the timed region (seeded; see inputs.py for the recipe).
+
+Prints one JSON line.  ``value`` is prefill tokens per second of the whole step (B*T tokens per
+step / step time, decode included).  ``roofline`` is for the prefill kernel (the dominant one):
+algorithmic HBM bytes per launch / its average launch time measured with HIP events on the
+launch stream.  ``decode`` reports the decode kernel against HBM the same way.  ``cpu_baseline``
+times the C float64 reference token loop on a bounded sample of the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def prefill_alg_bytes(B, T, H, dk, dv, N, in_bytes=2, out_bytes=2):
+    """Algorithmic HBM bytes of one prefill launch: every input read once, the output and the
+    final state written once (q, k, v, beta in the input dtype; g float32; S0, S_T float32)."""
+    th = B * T * H
+    per_th = (2 * dk + dv) * in_bytes + dk * 4 + in_bytes + dv * out_bytes
+    return th * per_th + 2 * N * H * dk * dv * 4
+
+
+def prefill_alg_flops(B, T, H, dk, dv, C=64):
+    """Algorithmic MFMA flops of the chunkwise form per launch, counting causal 16x16 tiles only
+    (intra: A_kk, A_qk, T K~, T V; inter: W S, Q~ S, K_end^T V~, A_qk V~)."""
+    th = B * T * H
+    tiles = C // 16
+    causal = tiles * (tiles + 1) // 2 / (tiles * tiles)       # fraction of causal tiles
+    intra = 2 * (2 * C * dk * causal) + 2 * C * dk * causal + 2 * C * dv * causal
+    inter = 2 * dk * dv * 3 + 2 * C * dv * causal
+    return th * (intra + inter)
+
+
+def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2):
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * in_bytes + dk * 4 + in_bytes + dv * out_bytes)
+
+
+def cpu_baseline(x, units_wanted=64):
+    """The C float64 reference token loop on the first `units_wanted` (sequence, head) units."""
+    from oracle import c_oracle
+    B, T, H, dk = x["q"].shape
+    units = [(n, h) for n in range(B) for h in range(H)][:units_wanted]
+    seqs = sorted({n for n, _ in units})
+    sub = {k: x[k][seqs].cpu() for k in ("q", "k", "v", "g", "beta")}
+    S0 = x["S0"][seqs].cpu()
+    remap = {n: i for i, n in enumerate(seqs)}
+    u2 = [(remap[n], h) for n, h in units]
+    threads = c_oracle.threads()
+    t0 = time.perf_counter()
+    c_oracle.kda_units(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], S0, None, u2)
+    dt = time.perf_counter() - t0
+    token_heads = len(units) * T
+    return {"value": token_heads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(units)} of {B * H} (sequence, head) units x {T} tokens of the same "
+                      f"workload ({token_heads} token-heads, float64 C token loop, "
+                      f"{dt:.1f} s wall); tokens/s = token-heads/s / H"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="profile helper: run only the prefill launch per step")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: every workload here fits "
+                                   "one MI355X; --gpus must be 1"}))
+        sys.exit(2)
+
+    from linear_attention_chunkwise_amd import binding, inputs
+    binding.load()
+    dev = torch.device("cuda:0")
+    cfg = inputs.CONFIGS["prefill_b4_h32_t32k_d128"]
+    dcfg = inputs.DECODE_CONFIG
+    x = inputs.make_config_inputs(cfg, seed=0, device=dev)
+    d = inputs.make_decode_inputs(dcfg.N, dcfg.H, dcfg.dk, dcfg.dv, seed=0, device=dev)
+    B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    od = torch.empty((dcfg.N, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)
+    S = d["S"]
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], o=o, S_T=ST)
+        if evs: evs[1].record()
+        if not args.prefill_only:
+            binding.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], S, o=od)
+        if evs: evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    pbytes = prefill_alg_bytes(B, T, H, dk, dv, B)
+    pflops = prefill_alg_flops(B, T, H, dk, dv)
+    dbytes = decode_alg_bytes(dcfg.N, dcfg.H, dcfg.dk, dcfg.dv)
+    achieved = pbytes / (pre_ms * 1e-3) / 1e9
+    res = {
+        "metric": "KDA prefill tokens/s (H=32,d=128,T=32K) + %MFMA peak; decode GB/s vs HBM",
+        "value": B * T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, generated on the GPU: q,k L2-normalised N(0,1), v N(0,1), "
+                "g=-5*sigmoid(exp(A)z), beta=sigmoid(N(0,1)), S0 N(0,0.1))",
+        "config": {"workload": "prefill B=4 H=32 T=32768 dk=dv=128 bf16 + decode 1024 seq x 32 "
+                               "heads fp32 128x128 state", "global_batch": B, "seq_len": T,
+                   "heads": H, "dk": dk, "dv": dv, "decode_sequences": dcfg.N,
+                   "parallelism": "single GPU"},
+        "prefill": {"ms": pre_ms, "tokens_per_s": B * T / (pre_ms * 1e-3),
+                    "alg_bytes": pbytes, "alg_GBps": achieved,
+                    "alg_mfma_tflops": pflops / (pre_ms * 1e-3) / 1e12,
+                    "mfma_frac": pflops / (pre_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+        "decode": None if args.prefill_only else {
+            "us": dec_ms * 1e3, "alg_bytes": dbytes, "GBps": dbytes / (dec_ms * 1e-3) / 1e9,
+            "frac_hbm": dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "prefill_kernel<128,bf16,bf16 out>"},
+    }
+    if not args.no_cpu_baseline:
+        del o, od
+        res["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,95 @@
+/* libkda -- Kimi Delta Attention (KDA) forward operator for AMD MI355X (gfx950).
+ *
+ * The operator (Kimi K3: Open Frontier Intelligence, §2.1.1, eq. (1)): for every sequence n and
+ * head h independently, with state S in R^{dk x dv} entering as S0[n, h] (or zero),
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
+ *
+ * where g_t is the per-key-channel natural-log decay, expected in [g_min, 0] with g_min = -5
+ * (§2.1.1, eq. (5)), and beta_t in [0, 1] is the delta-rule write strength.  The decay acts before
+ * the delta update and o_t reads the state after token t's update.  q is multiplied by `scale`.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library allocates no
+ *    device memory and keeps no pointer after the call's work has run on `stream`.
+ *  - Dense row-major layouts, token-major with heads interleaved ("B, T, H, d"):
+ *      q, k  [B, T, H, dk]     v, o  [B, T, H, dv]     g [B, T, H, dk] (float32)
+ *      beta  [B, T, H]         S0, S_T [N, H, dk, dv] (float32)
+ *    q, k, v and beta share `in_dtype`; o has `out_dtype`.
+ *  - Every pointer must be 16-byte aligned (beta: 4-byte aligned is enough).
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream); nothing synchronises the
+ *    host.  All argument checks run on the host before any launch: on error nothing is enqueued.
+ *  - Results are deterministic: no atomics, fixed reduction orders.
+ *  - Re-entrant; no global mutable state.
+ */
+#ifndef LIBKDA_KDA_H
+#define LIBKDA_KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size, aliasing, bad dtype   */
+    KDA_ERR_UNSUPPORTED = 2,      /* a valid request this build does not implement (e.g. dk=96) */
+    KDA_ERR_RANGE = 3,            /* reserved: input values outside the documented domain       */
+    KDA_ERR_HIP = 4               /* the HIP runtime reported an error (launch, no device)      */
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+/* Chunkwise prefill (§2.1.1, eqs. (3)-(4): recurrent across chunks, parallel inside a chunk).
+ *
+ * Sequences: without `cu_seqlens` (NULL), N = B and row b of every [B, T, ...] tensor is one
+ * sequence of T tokens.  With `cu_seqlens` (device int32 [N + 1], non-decreasing, cu[0] = 0,
+ * cu[N] = T), B must be 1 and sequence n is tokens [cu[n], cu[n+1]) of the packed row; lengths
+ * may be 0 (then S_T[n] = S0[n] and no output row belongs to it).  Out-of-range cu_seqlens
+ * values are clamped inside the kernel (never an out-of-bounds access) but give meaningless
+ * results.
+ *
+ * S0 may be NULL (zero entering state).  S_T may be NULL (final state not wanted) and may alias
+ * S0 exactly (in-place state advance).  o must not overlap any input.
+ *
+ * Supported: dk in {64, 128}; dv in {64, 128}; in_dtype KDA_BF16, or KDA_F32 at dk = 64 (float32
+ * inputs are carried at higher internal precision); out_dtype KDA_BF16 or KDA_F32; T >= 0;
+ * B, H >= 1.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const void* beta, const float* S0, const int32_t* cu_seqlens,
+                         int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
+                         kda_dtype in_dtype, kda_dtype out_dtype, float scale,
+                         void* o, float* S_T, hipStream_t stream);
+
+/* One decode token per (sequence, head), state updated IN PLACE (§5.4.2: at decode the state is
+ * advanced in place every step and its traffic dominates).  eq. (1) with T = 1:
+ *
+ *     S <- Diag(exp(g)) S;  u = beta (v - S^T k);  S <- S + k u^T;  o = S^T (scale q).
+ *
+ * Layouts: q, k, g [N, H, dk]; v, o [N, H, dv]; beta [N, H]; S [N, H, dk, dv] float32.
+ * o must not overlap S or any input.  Supported: dk, dv in {64, 128}.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                              const void* beta, float* S, int32_t N, int32_t H, int32_t dk,
+                              int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
+                              void* o, hipStream_t stream);
+
+/* Static description of a status code.  Never NULL. */
+const char* kda_status_string(kda_status status);
+
+/* Human-readable detail of the last error returned on the calling host thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Library ABI version: (major << 16) | minor. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_KDA_H */

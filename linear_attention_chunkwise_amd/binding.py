@@ -1,0 +1,157 @@
+"""ctypes binding of libkda (include/kda.h): argument marshalling only.
+
+Every step of the operator runs in the HIP kernels behind the C ABI; this module checks tensor
+metadata, allocates outputs with torch (device memory is the caller's), passes raw device
+pointers and the current HIP stream, and turns status codes into exceptions.  There is no
+fallback: if libkda.so is missing or the GPU is absent, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_RANGE, KDA_ERR_HIP = range(5)
+KDA_BF16, KDA_F32 = 0, 1
+
+# every symbol include/kda.h declares
+EXPORTS = ("kda_chunk_fwd", "kda_recurrent_step", "kda_status_string", "kda_last_error",
+           "kda_version")
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m "
+                           "linear_attention_chunkwise_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_float, vp, vp]
+    lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != KDA_OK:
+        lib = load()
+        raise KdaError(status, "%s: %s" % (lib.kda_status_string(status).decode(),
+                                           lib.kda_last_error().decode()))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name, device, dtype=None, shape=None):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, scale: float = 1.0,
+              out_dtype=None, output_final_state: bool = True, o=None, S_T=None):
+    """KDA chunkwise prefill: returns (o [B,T,H,dv], S_T [N,H,dk,dv] float32 or None).
+
+    q, k [B,T,H,dk], v [B,T,H,dv], beta [B,T,H] share a dtype (bf16, or f32 at dk = 64);
+    g [B,T,H,dk] float32; S0 [N,H,dk,dv] float32 or None; cu_seqlens int32 [N+1] (device) with
+    B = 1 for packed sequences.  ``S_T`` may be passed as S0 itself to advance the state in
+    place.  ``out_dtype`` defaults to q's dtype."""
+    lib = load()
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dev, dt)
+    _require(k, "k", dev, dt, (B, T, H, dk))
+    _require(v, "v", dev, dt, (B, T, H, dv))
+    _require(g, "g", dev, torch.float32, (B, T, H, dk))
+    _require(beta, "beta", dev, dt, (B, T, H))
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
+    out_dtype = out_dtype or dt
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _require(o, "o", dev, out_dtype, (B, T, H, dv))
+    if S_T is None and output_final_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
+    st = lib.kda_chunk_fwd(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(cu_seqlens), B, T, H,
+                           N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T), _stream(dev))
+    _check(st)
+    return o, S_T
+
+
+def recurrent_step(q, k, v, g, beta, S, *, scale: float = 1.0, out_dtype=None, o=None):
+    """One KDA decode token per (sequence, head); S [N,H,dk,dv] float32 is updated IN PLACE.
+
+    q, k [N,H,dk], v [N,H,dv], beta [N,H] share a dtype; g [N,H,dk] float32.  Returns o [N,H,dv]."""
+    lib = load()
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dev, dt)
+    _require(k, "k", dev, dt, (N, H, dk))
+    _require(v, "v", dev, dt, (N, H, dv))
+    _require(g, "g", dev, torch.float32, (N, H, dk))
+    _require(beta, "beta", dev, dt, (N, H))
+    _require(S, "S", dev, torch.float32, (N, H, dk, dv))
+    out_dtype = out_dtype or dt
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _require(o, "o", dev, out_dtype, (N, H, dv))
+    st = lib.kda_recurrent_step(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), N, H, dk, dv, _dt(q),
+                                _dt(o), float(scale), _p(o), _stream(dev))
+    _check(st)
+    return o

@@ -1,0 +1,167 @@
+// C ABI of libkda (declared in include/kda.h): host-side argument checks and dispatch.
+//
+// Every check runs before anything is enqueued, so an error return leaves the stream untouched.
+#include <stdio.h>
+#include <string.h>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status fail(kda_status s, const char* fmt, const char* what, long long x = 0) {
+    snprintf(g_last_error, sizeof g_last_error, fmt, what, x);
+    return s;
+}
+
+kda_status ok() {
+    g_last_error[0] = '\0';
+    return KDA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + nb && y < x + na;
+}
+
+kda_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return ok();
+    snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+    return KDA_ERR_HIP;
+}
+
+size_t dsize(kda_dtype d) { return d == KDA_F32 ? 4 : 2; }
+
+kda_status check_dtype(kda_dtype d, const char* what) {
+    if (d != KDA_BF16 && d != KDA_F32)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown dtype code %lld", what, (long long)d);
+    return KDA_OK;
+}
+
+kda_status check_ptr(const void* p, size_t align, const char* what) {
+    if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL%.0lld", what);
+    if (!aligned(p, align))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %lld-byte aligned", what, (long long)align);
+    return KDA_OK;
+}
+
+#define KDA_TRY(expr)                      \
+    do {                                   \
+        kda_status _s = (expr);            \
+        if (_s != KDA_OK) return _s;       \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_version(void) { return (1 << 16) | 0; }
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_RANGE: return "KDA_ERR_RANGE";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const void* beta, const float* S0, const int32_t* cu_seqlens,
+                         int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
+                         kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
+                         float* S_T, hipStream_t stream) {
+    KDA_TRY(check_dtype(in_dtype, "in_dtype"));
+    KDA_TRY(check_dtype(out_dtype, "out_dtype"));
+    if (B < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "B", B);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "H", H);
+    if (T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "T", T);
+    if (dk < 1 || dv < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "dk/dv", dk < 1 ? dk : dv);
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: packed sequences need B == 1 (got %lld)", "cu_seqlens", B);
+        if (N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "N", N);
+        if (!aligned(cu_seqlens, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %lld-byte aligned", "cu_seqlens", 4);
+    } else if (N != B) {
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s must equal B without cu_seqlens (got %lld)", "N", N);
+    }
+    if (!(dk == 64 || dk == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dk", dk);
+    if (!(dv == 64 || dv == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dv", dv);
+    if ((int64_t)N * H > (int64_t)1 << 30) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "N*H", (long long)N * H);
+    if (in_dtype == KDA_F32 && dk != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: float32 inputs are supported at dk = 64 only (got %lld)", "in_dtype", dk);
+
+    const int64_t tokens = (int64_t)B * T;
+    const size_t es = dsize(in_dtype);
+    const size_t nqk = (size_t)tokens * H * dk, nv = (size_t)tokens * H * dv;
+    if (tokens > 0) {
+        KDA_TRY(check_ptr(q, 16, "q"));
+        KDA_TRY(check_ptr(k, 16, "k"));
+        KDA_TRY(check_ptr(v, 16, "v"));
+        KDA_TRY(check_ptr(g, 16, "g"));
+        KDA_TRY(check_ptr(beta, es, "beta"));
+        KDA_TRY(check_ptr(o, 16, "o"));
+        const size_t no = nv * dsize(out_dtype);
+        if (overlaps(o, no, q, nqk * es) || overlaps(o, no, k, nqk * es) ||
+            overlaps(o, no, v, nv * es) || overlaps(o, no, g, nqk * 4) ||
+            overlaps(o, no, beta, (size_t)tokens * H * es))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps an input%.0lld", "o");
+    }
+    if (cu_seqlens == nullptr && N == 0) return ok();
+    const size_t nst = (size_t)N * H * dk * dv * 4;
+    if (S0) KDA_TRY(check_ptr(S0, 16, "S0"));
+    if (S_T) {
+        KDA_TRY(check_ptr(S_T, 16, "S_T"));
+        if (S_T != S0 && overlaps(S_T, nst, S0, nst))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s partially overlaps S0 (only exact aliasing is allowed)%.0lld", "S_T");
+        if (tokens > 0 && overlaps(S_T, nst, o, nv * dsize(out_dtype)))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps o%.0lld", "S_T");
+    }
+    if (N == 0) return ok();
+
+    kda::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, T, H, N, dk, dv,
+                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T, stream};
+    return hip_status(kda::launch_chunk_fwd(a));
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                              const void* beta, float* S, int32_t N, int32_t H, int32_t dk,
+                              int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
+                              void* o, hipStream_t stream) {
+    KDA_TRY(check_dtype(in_dtype, "in_dtype"));
+    KDA_TRY(check_dtype(out_dtype, "out_dtype"));
+    if (N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "N", N);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "H", H);
+    if (!(dk == 64 || dk == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dk", dk);
+    if (!(dv == 64 || dv == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dv", dv);
+    if ((int64_t)N * H > (int64_t)1 << 30) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "N*H", (long long)N * H);
+    if (N == 0) return ok();
+    const size_t es = dsize(in_dtype);
+    KDA_TRY(check_ptr(q, 16, "q"));
+    KDA_TRY(check_ptr(k, 16, "k"));
+    KDA_TRY(check_ptr(v, 16, "v"));
+    KDA_TRY(check_ptr(g, 16, "g"));
+    KDA_TRY(check_ptr(beta, es, "beta"));
+    KDA_TRY(check_ptr(S, 16, "S"));
+    KDA_TRY(check_ptr(o, 16, "o"));
+    const size_t nh = (size_t)N * H;
+    const size_t no = nh * dv * dsize(out_dtype);
+    if (overlaps(o, no, S, nh * dk * dv * 4) || overlaps(o, no, q, nh * dk * es) ||
+        overlaps(o, no, k, nh * dk * es) || overlaps(o, no, v, nh * dv * es) ||
+        overlaps(o, no, g, nh * dk * 4) || overlaps(o, no, beta, nh * es))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps the state or an input%.0lld", "o");
+    kda::DecodeArgs a{q, k, v, g, beta, S, (int32_t)nh, dk, dv,
+                      in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, stream};
+    return hip_status(kda::launch_decode_step(a));
+}
+
+}  // extern "C"

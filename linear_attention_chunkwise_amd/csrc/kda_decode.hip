@@ -1,0 +1,122 @@
+// KDA decode step: one token per (sequence, head), state advanced in place.
+//
+// Kimi K3: Open Frontier Intelligence, §2.1.1 eq. (1) with a single token, as used at decode
+// time (§5.4.2: the recurrent state is updated in place at every step, and at large batch the
+// state traffic is the cost):
+//     S' = Diag(exp(g)) S;  u = beta (v - S'^T k);  S <- S' + k u^T;  o = S^T (scale q)
+//        = scale (S'^T q + (q . k) u).
+//
+// Bound: HBM.  Per (sequence, head) the algorithmic traffic is the state read once and written
+// once (2 * dk * dv * 4 bytes) plus q, k, v, g, beta and o; the arithmetic is ~7 dk dv fp32 ops.
+//
+// Mapping: one 256-thread workgroup per (sequence, head).  Thread t owns four adjacent value
+// columns (one float4 per state row) and a contiguous group of dk / (1024 / dv) state rows, so
+// every state row is read and written by full 16-byte lanes, 512 contiguous bytes per row at
+// dv = 128.  The two column reductions over dk (S'^T k and S'^T q) and the scalar q . k are
+// finished across the row groups through LDS in a fixed order (deterministic).
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <int DK, int DV, bool IN_F32, bool OUT_F32>
+__global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qp,
+                                                     const void* __restrict__ kp,
+                                                     const void* __restrict__ vp,
+                                                     const float* __restrict__ g,
+                                                     const void* __restrict__ betap,
+                                                     float* __restrict__ S, int32_t NH,
+                                                     float scale, void* __restrict__ op) {
+    constexpr int CG = DV / 4;          // column groups (float4 each)
+    constexpr int NRG = 256 / CG;       // row groups
+    constexpr int RPG = DK / NRG;       // state rows per thread
+    static_assert(RPG >= 1 && DK % NRG == 0, "decode tiling");
+    __shared__ f32x4 red_y[NRG][CG];
+    __shared__ f32x4 red_z[NRG][CG];
+    __shared__ float red_qk[NRG];
+
+    const int unit = blockIdx.x;        // sequence * H + head
+    if (unit >= NH) return;
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    const int r0 = rg * RPG;
+
+    float* Su = S + (size_t)unit * DK * DV;
+    f32x4 s[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) s[i] = ld<f32x4>(Su + (size_t)(r0 + i) * DV + 4 * cg);
+
+    auto in_at = [&](const void* p, size_t idx) -> float {
+        if constexpr (IN_F32) return reinterpret_cast<const float*>(p)[idx];
+        else return bf2f(reinterpret_cast<const bf16*>(p)[idx]);
+    };
+    const size_t kb = (size_t)unit * DK;
+    f32x4 y = zero4(), z = zero4();
+    float qk = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+        const float a = __expf(g[kb + r0 + i]);
+        const float kv = in_at(kp, kb + r0 + i);
+        const float qv = in_at(qp, kb + r0 + i);
+        s[i] *= a;
+        y += kv * s[i];
+        z += qv * s[i];
+        qk += qv * kv;
+    }
+    red_y[rg][cg] = y;
+    red_z[rg][cg] = z;
+    if (cg == 0) red_qk[rg] = qk;  // every column group holds the same partial dot product
+    __syncthreads();
+    f32x4 yt = zero4(), zt = zero4();
+    float qkt = 0.f;
+#pragma unroll
+    for (int j = 0; j < NRG; ++j) {
+        yt += red_y[j][cg];
+        zt += red_z[j][cg];
+        qkt += red_qk[j];
+    }
+    const float b = in_at(betap, (size_t)unit);
+    const size_t vb = (size_t)unit * DV + 4 * cg;
+    f32x4 u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) u[c] = b * (in_at(vp, vb + c) - yt[c]);
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+        const float kv = in_at(kp, kb + r0 + i);
+        st<f32x4>(Su + (size_t)(r0 + i) * DV + 4 * cg, s[i] + kv * u);
+    }
+    if (rg == 0) {
+        const f32x4 o = scale * (zt + qkt * u);
+        if constexpr (OUT_F32) {
+            st<f32x4>(reinterpret_cast<float*>(op) + vb, o);
+        } else {
+            bf16x4 ob{f2bf(o[0]), f2bf(o[1]), f2bf(o[2]), f2bf(o[3])};
+            st<bf16x4>(reinterpret_cast<bf16*>(op) + vb, ob);
+        }
+    }
+}
+
+template <int DK, int DV, bool IN_F32, bool OUT_F32>
+static hipError_t launch_decode(const DecodeArgs& a) {
+    if (a.NH == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, IN_F32, OUT_F32>), dim3(a.NH), dim3(256), 0,
+                       a.stream, a.q, a.k, a.v, a.g, a.beta, a.S, a.NH, a.scale, a.o);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t dispatch_io(const DecodeArgs& a) {
+    if (a.in_f32) return a.out_f32 ? launch_decode<DK, DV, true, true>(a)
+                                   : launch_decode<DK, DV, true, false>(a);
+    return a.out_f32 ? launch_decode<DK, DV, false, true>(a) : launch_decode<DK, DV, false, false>(a);
+}
+
+hipError_t launch_decode_step(const DecodeArgs& a) {
+    if (a.dk == 128 && a.dv == 128) return dispatch_io<128, 128>(a);
+    if (a.dk == 128 && a.dv == 64) return dispatch_io<128, 64>(a);
+    if (a.dk == 64 && a.dv == 128) return dispatch_io<64, 128>(a);
+    if (a.dk == 64 && a.dv == 64) return dispatch_io<64, 64>(a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -1,6 +1,6 @@
 """ctypes wrapper of the C reference token loop -- TEST INFRASTRUCTURE ONLY.
 
-Builds ``oracle/libkda_oracle.so`` from ``oracle/kda_oracle.c`` with gcc (plain -O2, OpenMP
+Builds ``oracle/libkda_oracle.so`` from ``oracle/kda_oracle.c`` with gcc (plain -O3, no fast-math; OpenMP
 over independent (sequence, head) units) and evaluates the definition of eq. (1) of Kimi K3:
 Open Frontier Intelligence, §2.1.1 on chosen units.  Inputs are CPU torch tensors in their
 stored dtype (bfloat16 or float32), so nothing is widened to float64 in memory; results are
@@ -25,7 +25,7 @@ def build(force: bool = True) -> str:
     """Compile the C oracle (always when force, else only if the library is missing)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC,
+        subprocess.run(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC,
                         "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB

@@ -1,0 +1,103 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load, export every function include/kda.h declares, and reject bad arguments
+on the host with the documented status codes before anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_chunkwise_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from linear_attention_chunkwise_amd import build
+        build.build()
+    return binding.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARGUMENT"
+    assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(4) == b"KDA_ERR_HIP"
+    assert lib.kda_status_string(99) == b"KDA_ERR_UNKNOWN"
+    assert lib.kda_version() >> 16 == 1
+
+
+FAKE = 1 << 20   # an aligned, never-dereferenced address: every case below fails before use
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2, N=1,
+             dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"],
+                             a["T"], a["H"], a["N"], a["dk"], a["dv"], a["ind"], a["outd"],
+                             ctypes.c_float(a["scale"]), a["o"], a["ST"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(k=FAKE + 8), binding.KDA_ERR_INVALID_ARGUMENT),          # misaligned
+    (dict(ind=7), binding.KDA_ERR_INVALID_ARGUMENT),               # unknown dtype
+    (dict(B=0, N=0), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(N=3), binding.KDA_ERR_INVALID_ARGUMENT),                 # N != B without cu_seqlens
+    (dict(B=2, N=2, cu=FAKE), binding.KDA_ERR_INVALID_ARGUMENT),   # packed needs B == 1
+    (dict(dk=96), binding.KDA_ERR_UNSUPPORTED),
+    (dict(dv=32), binding.KDA_ERR_UNSUPPORTED),
+    (dict(ind=1), binding.KDA_ERR_UNSUPPORTED),                    # f32 inputs at dk = 128
+    (dict(o=FAKE), binding.KDA_ERR_INVALID_ARGUMENT),              # o aliases q
+    (dict(S0=FAKE * 64, ST=FAKE * 64 + 16), binding.KDA_ERR_INVALID_ARGUMENT),  # partial alias
+])
+def test_chunk_fwd_rejects_on_host(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.kda_last_error() != b""
+
+
+def _step(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S=FAKE * 16, N=4, H=2, dk=128, dv=128,
+             ind=0, outd=0, scale=1.0, o=FAKE * 64)
+    a.update(kw)
+    return lib.kda_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["N"],
+                                  a["H"], a["dk"], a["dv"], a["ind"], a["outd"],
+                                  ctypes.c_float(a["scale"]), a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=None), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(g=FAKE + 4), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(N=-1), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dk=256), binding.KDA_ERR_UNSUPPORTED),
+    (dict(o=FAKE * 16), binding.KDA_ERR_INVALID_ARGUMENT),         # o aliases S
+])
+def test_recurrent_step_rejects_on_host(lib, kw, status):
+    assert _step(lib, **kw) == status
+
+
+def test_empty_work_is_ok_without_touching_memory(lib):
+    assert _step(lib, N=0, q=None, S=None) == binding.KDA_OK

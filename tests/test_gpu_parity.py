@@ -1,0 +1,262 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 oracle.
+
+Tolerance (whole tensor, against the oracle fed the same stored inputs): relative L2
+||x - y|| / ||y|| <= 2e-3 and max |x - y| <= 1e-2, on the output and on the final state.  A bf16
+output rounded from the exact value already sits at a relative L2 of about 1.66e-3 (8-bit
+significand), so bf16-output cases pass only if the kernel itself adds little error; the float32
+output cases show the kernel's own error.
+
+Small cases are compared element by element on every unit; the full-size workloads are run in the
+benchmark's launch configuration and compared on sampled (sequence, head) units, each evaluated by
+the oracle over its whole sequence.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_chunkwise_amd import inputs
+from oracle import c_oracle
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 2e-3
+MAX_ABS = 1e-2
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+
+
+def _maxabs(a, b):
+    d = np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))
+    return float(d.max()) if d.size else 0.0
+
+
+def assert_close(name, got, ref):
+    r, m = _rel(got, ref), _maxabs(got, ref)
+    print(f"  {name}: rel_l2={r:.3e} max_abs={m:.3e}", flush=True)
+    assert r <= REL_L2 and m <= MAX_ABS, f"{name}: rel_l2 {r:.3e} max_abs {m:.3e}"
+
+
+def _to_dev(x, dev="cuda"):
+    return {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in x.items()}
+
+
+def run_gpu(x, out_dtype, scale=1.0):
+    from linear_attention_chunkwise_amd import binding
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["cu_seqlens"],
+                              scale=scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), ST.cpu().numpy()
+
+
+def oracle_all(x, scale=1.0):
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu()
+    return c_oracle.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], cu, scale)
+
+
+# ------------------------------------------------------------------ small shapes, every element
+
+SMALL = [
+    # (B, T, H, dk, dv, S0)
+    (1, 1, 2, 128, 128, True),
+    (1, 15, 2, 128, 128, True),
+    (2, 32, 2, 128, 128, False),
+    (1, 33, 3, 128, 128, True),
+    (1, 100, 2, 128, 64, True),
+    (2, 257, 2, 128, 128, True),
+    (1, 130, 2, 64, 64, True),
+    (1, 70, 1, 64, 128, False),
+]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["o_f32", "o_bf16"])
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}T{c[1]}H{c[2]}k{c[3]}v{c[4]}" for c in SMALL])
+def test_prefill_small(gpu_lib, case, out_dtype):
+    B, T, H, dk, dv, s0 = case
+    x = inputs.make_prefill_inputs(B, T, H, dk, dv, seed=T + H, S0_std=0.1 if s0 else None)
+    print(f"prefill B={B} T={T} H={H} dk={dk} dv={dv}", flush=True)
+    o, ST = run_gpu(x, out_dtype)
+    ro, rST = oracle_all(x)
+    assert_close("o", o, ro)
+    assert_close("S_T", ST, rST)
+
+
+def test_prefill_scale_and_near_gmin(gpu_lib):
+    x = inputs.make_prefill_inputs(1, 160, 2, 128, 128, seed=3, near_gmin_frac=0.5)
+    o, ST = run_gpu(x, torch.float32, scale=0.125)
+    ro, rST = oracle_all(x, scale=0.125)
+    assert_close("o", o, ro)
+    assert_close("S_T", ST, rST)
+
+
+def test_prefill_varlen_with_empty_and_ragged(gpu_lib):
+    lens = [0, 1, 31, 32, 33, 0, 100, 5]
+    cu = inputs.cu_from_lengths(lens)
+    x = inputs.make_prefill_inputs(1, int(cu[-1]), 3, 128, 128, seed=9, cu_seqlens=cu)
+    o, ST = run_gpu(x, torch.float32)
+    ro, rST = oracle_all(x)
+    assert_close("o", o, ro)
+    assert_close("S_T", ST, rST)
+    # empty sequences leave their state untouched
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(ST[n], x["S0"][n].numpy())
+
+
+def test_prefill_no_final_state_and_inplace(gpu_lib):
+    from linear_attention_chunkwise_amd import binding
+    x = _to_dev(inputs.make_prefill_inputs(2, 77, 2, 128, 128, seed=5))
+    o1, ST1 = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    o2, none = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
+                                 output_final_state=False)
+    assert none is None and torch.equal(o1, o2)
+    S = x["S0"].clone()
+    o3, S_out = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], S, S_T=S)
+    torch.cuda.synchronize()
+    assert S_out.data_ptr() == S.data_ptr()
+    assert torch.equal(o1, o3) and torch.equal(ST1, S)
+
+
+def test_prefill_deterministic(gpu_lib):
+    from linear_attention_chunkwise_amd import binding
+    x = _to_dev(inputs.make_prefill_inputs(2, 200, 4, 128, 128, seed=6))
+    a = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    b = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_prefill_resume_matches_one_pass(gpu_lib):
+    """Splitting a sequence and re-entering with the first part's final state (eq. (17) with two
+    segments) agrees with the single pass within the parity tolerance."""
+    from linear_attention_chunkwise_amd import binding
+    x = _to_dev(inputs.make_prefill_inputs(1, 300, 2, 128, 128, seed=8))
+    o, ST = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
+                              out_dtype=torch.float32)
+    t = 113
+    sl = lambda a, s: a[:, s].contiguous()
+    oa, Sa = binding.chunk_fwd(*(sl(x[n], slice(0, t)) for n in ("q", "k", "v", "g", "beta")),
+                               x["S0"], out_dtype=torch.float32)
+    ob, Sb = binding.chunk_fwd(*(sl(x[n], slice(t, None)) for n in ("q", "k", "v", "g", "beta")),
+                               Sa, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close("o", torch.cat([oa, ob], 1).cpu().numpy(), o.cpu().numpy())
+    assert_close("S_T", Sb.cpu().numpy(), ST.cpu().numpy())
+
+
+# ------------------------------------------------------------------ the named workloads
+
+def test_workload_tiny_fp32_t256_d64(gpu_lib):
+    cfg = inputs.CONFIGS["tiny_fp32_t256_d64"]
+    x = inputs.make_config_inputs(cfg, seed=0)
+    for od in (torch.float32, torch.bfloat16):
+        o, ST = run_gpu(x, od)
+        ro, rST = oracle_all(x)
+        assert_close(f"o[{od}]", o, ro)
+        assert_close(f"S_T[{od}]", ST, rST)
+
+
+def test_workload_h16_t4096_d128(gpu_lib):
+    cfg = inputs.CONFIGS["h16_t4096_d128"]
+    x = inputs.make_config_inputs(cfg, seed=0)
+    ro, rST = oracle_all(x)
+    for od in (torch.float32, torch.bfloat16):
+        o, ST = run_gpu(x, od)
+        assert_close(f"o[{od}]", o, ro)
+        assert_close(f"S_T[{od}]", ST, rST)
+
+
+def _sampled_check(cfg, units, out_dtype=torch.bfloat16, seed=0):
+    """Full-size run on the GPU (inputs generated on the GPU), oracle on sampled units."""
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_config_inputs(cfg, seed=seed, device="cuda")
+    o, ST = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["cu_seqlens"],
+                              out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu().tolist()
+    for (n, h) in units:
+        if cu is None:
+            b, s, e = n, 0, x["q"].shape[1]
+        else:
+            b, s, e = 0, cu[n], cu[n + 1]
+        sel = lambda t: t[b:b + 1, s:e, h:h + 1].contiguous().cpu()
+        S0 = None if x["S0"] is None else x["S0"][n:n + 1, h:h + 1].contiguous().cpu()
+        print(f"  unit n={n} h={h} tokens={e - s}", flush=True)
+        outs, rST = c_oracle.kda_units(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["g"]),
+                                       sel(x["beta"]), S0, None, [(0, 0)])
+        assert_close(f"o[n={n},h={h}]", o[b, s:e, h].float().cpu().numpy(), outs[0])
+        assert_close(f"S_T[n={n},h={h}]", ST[n, h].cpu().numpy(), rST[0])
+    del x, o, ST
+    torch.cuda.empty_cache()
+
+
+def test_workload_prefill_b4_h32_t32k(gpu_lib):
+    cfg = inputs.CONFIGS["prefill_b4_h32_t32k_d128"]
+    _sampled_check(cfg, [(0, 0), (1, 17), (2, 31), (3, 5)])
+
+
+def test_workload_varlen64(gpu_lib):
+    cfg = inputs.CONFIGS["varlen64_h32_d128"]
+    lens = inputs.varlen_lengths(cfg.n_varlen, 0)
+    longest = int(np.argmax(lens))
+    shortest = int(np.argmin(lens))
+    _sampled_check(cfg, [(longest, 3), (shortest, 30), (10, 0), (40, 21)])
+
+
+@pytest.mark.slow
+def test_workload_long_t1m(gpu_lib):
+    cfg = inputs.CONFIGS["long_b1_h32_t1m_d128"]
+    _sampled_check(cfg, [(0, 0), (0, 19)])
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128), (64, 64)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["o_f32", "o_bf16"])
+def test_decode_small(gpu_lib, dk, dv, out_dtype):
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_decode_inputs(5, 3, dk, dv, seed=dk + dv)
+    d = _to_dev(x)
+    S = d["S"].clone()
+    o = binding.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], S, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rS = c_oracle.kda_forward(x["q"][:, None], x["k"][:, None], x["v"][:, None],
+                                  x["g"][:, None], x["beta"][:, None], x["S"])
+    assert_close("o", o.float().cpu().numpy(), ro[:, 0])
+    assert_close("S", S.cpu().numpy(), rS)
+
+
+def test_decode_workload_n1024_h32(gpu_lib):
+    from linear_attention_chunkwise_amd import binding
+    cfg = inputs.DECODE_CONFIG
+    x = inputs.make_decode_inputs(cfg.N, cfg.H, cfg.dk, cfg.dv, seed=0, device="cuda")
+    S = x["S"].clone()
+    o = binding.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], S)
+    torch.cuda.synchronize()
+    idx = torch.arange(0, cfg.N, 37)
+    sub = {k: x[k][idx].cpu() for k in ("q", "k", "v", "g", "beta", "S")}
+    ro, rS = c_oracle.kda_forward(sub["q"][:, None], sub["k"][:, None], sub["v"][:, None],
+                                  sub["g"][:, None], sub["beta"][:, None], sub["S"])
+    assert_close("o", o[idx].float().cpu().numpy(), ro[:, 0])
+    assert_close("S", S[idx].cpu().numpy(), rS)
+
+
+def test_decode_matches_prefill_t1(gpu_lib):
+    """Decode is eq. (1) with T = 1: the two entry points agree."""
+    from linear_attention_chunkwise_amd import binding
+    x = _to_dev(inputs.make_decode_inputs(6, 4, 128, 128, seed=4))
+    S = x["S"].clone()
+    o1 = binding.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], S,
+                                out_dtype=torch.float32)
+    o2, S2 = binding.chunk_fwd(*(x[n][:, None].contiguous() for n in ("q", "k", "v", "g", "beta")),
+                               x["S"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close("o", o1.cpu().numpy(), o2[:, 0].cpu().numpy())
+    assert_close("S", S.cpu().numpy(), S2.cpu().numpy())
