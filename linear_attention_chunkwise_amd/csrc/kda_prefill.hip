@@ -19,19 +19,28 @@
 // 16 tokens), <= 1 off it: both representable in bf16, so every causal tile, diagonal included,
 // is a dense MFMA product.
 //
-// Grid: one 256-thread workgroup (4 waves) per (sequence, head, 64-column slice of dv).  Wave w
-// owns value columns [16w, 16w + 16) of the slice: its slice of the state S (dk x 16, fp32) lives
-// in MFMA accumulator registers for the whole sequence and doubles as the B operand of W S and
-// Q~ S, so the state never leaves the chip between chunks.  The state-independent intra-chunk work
-// (decay prefix, Gram tiles, the triangular inverse, W) is recomputed by each column slice of a
-// head; the slices of one head are placed on the same XCD so their re-reads of q, k, g hit L2.
+// Grid: one 256-thread workgroup (4 waves) per (sequence, head, 64-column slice of dv); the
+// slices of one head go to the same XCD so their reads of q, k, g share L2.  Per 32-token chunk:
+//   A (intra, channel-parallel): wave w owns key channels [32w, 32w + 32).  Each lane holds one
+//     token of a 16-token tile and 8 channels, loaded straight from HBM (prefetched one chunk
+//     ahead).  The in-tile decay prefix is a DPP scan across the 16 lanes of a row; the decayed
+//     operands are built in registers and feed MFMA directly: partial Gram tiles over the wave's
+//     channels (summed across waves through LDS), and "transposes" (product with an identity
+//     block) that turn token-per-lane fragments into channel-per-lane ones for K~, K_end and V.
+//   B (solve, one wave): A_kk is reduced, the two 16x16 diagonal blocks of (I + A_kk) are inverted
+//     by forward substitution (one lane per column) and the off-diagonal block is assembled with
+//     split MFMA products; the other waves reduce A_qk meanwhile.
+//   C: W^T = K~^T T_b^T for the wave's channels; U = T_b V for the wave's value columns.
+//   D (inter, column-parallel): wave w owns value columns [16w, 16w + 16) of the slice: its slice
+//     of the state (dk x 16, fp32) lives in MFMA accumulators for the whole sequence and doubles
+//     as the B operand of W S and Q~ S.
 //
 // Precision: bf16 MFMA with fp32 accumulation.  Operands whose rounding would dominate the error
 // are carried as hi + lo bf16 pairs (products hi*hi + lo*hi + hi*lo): the decayed Gram operands,
-// A_qk, V~ in both of its uses, and both operands of the inter-chunk output term (Q * exp(G)) S,
-// which dominates short sequences entered with a large state.  T_b, K~, W and K_end, and the
-// state as the operand of W S, are single bf16; U and the state stay fp32.  Float32 inputs
-// (kFull) carry every operand as a pair.
+// A_qk, V~ in both of its uses, and both operands of (Q * exp(G)) S, which dominates short
+// sequences entered with a large state.  T_b, K~, W, K_end and the state as the operand of W S
+// are single bf16; U and the state stay fp32.  Float32 inputs (kFull) carry every operand as a
+// pair.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -46,51 +55,70 @@ constexpr int kNT = 256;   // threads per workgroup (4 waves)
 template <int DK, bool F32IN>
 struct Layout {
     static constexpr bool kFull = F32IN;
-    static constexpr int kNP = kFull ? 2 : 1;            // bf16 planes of "single" operands
-    using IT = typename std::conditional<F32IN, float, bf16>::type;
-    static constexpr int RB = DK + 8;                      // bf16 row-major [token][DK] stride
-    static constexpr int RF = DK + 4;                      // fp32 row-major stride
-    static constexpr int RI = F32IN ? RF : RB;             // raw input row stride
-    static constexpr int TB = kC + 8;                      // bf16 [*][token] stride
-    static constexpr int AB = kC + 8;                      // bf16 [C][C] stride
-    static constexpr int AF = kC + 4;                      // fp32 [C][C] stride
-    // Group A (raw chunk and decay factors; dead after the operand pass), later reused.
-    static constexpr int o_rq = 0;
-    static constexpr int o_rk = o_rq + kC * RI * (int)sizeof(IT);
-    static constexpr int o_P = o_rk + kC * RI * (int)sizeof(IT);
-    static constexpr int o_Pi = o_P + kC * RF * 4;
-    static constexpr int endA1 = o_Pi + kC * RF * 4;
-    static constexpr int o_Akk = 0;                        // fp32 [C][AF]
-    static constexpr int o_Tm = o_Akk + kC * AF * 4;       // fp32 [C][AF]
-    static constexpr int o_Tb = o_Tm + kC * AF * 4;        // bf16 planes [C][AB]
-    static constexpr int o_W = o_Tb + kNP * kC * AB * 2;   // bf16 planes [C][RB]
-    static constexpr int endA2 = o_W + kNP * kC * RB * 2;
-    static constexpr int endA = endA1 > endA2 ? endA1 : endA2;
-    // Group G: split Gram operands (hi plane, lo plane).
-    static constexpr int o_Qs = endA;
-    static constexpr int o_Kr = o_Qs + 2 * kC * RB * 2;
-    static constexpr int o_Kd = o_Kr + 2 * kC * RB * 2;
-    static constexpr int o_Kc = o_Kd + 2 * kC * RB * 2;    // 16 rows
-    static constexpr int endG = o_Kc + 2 * 16 * RB * 2;
-    // Persistent within a chunk (the split Qs of group G also stays live until the outputs).
-    static constexpr int o_Kt = endG;                      // bf16 planes [DK][TB]  (K~ transposed)
-    static constexpr int o_Ke = o_Kt + kNP * DK * TB * 2;  // bf16 planes [DK][TB]  (K_end transp.)
-    static constexpr int o_Vt = o_Ke + kNP * DK * TB * 2;  // bf16 planes [DVT][TB] (V transposed)
-    static constexpr int o_Aq = o_Vt + kNP * kDVT * TB * 2;// bf16 hi, lo [C][AB]
-    static constexpr int o_beta = o_Aq + 2 * kC * AB * 2;  // fp32 [C]
-    static constexpr int o_gam = o_beta + kC * 4;          // fp32 [DK]
-    static constexpr int o_D = o_gam + DK * 4;             // fp32 [2][DK] tile log2-decay totals
-    static constexpr int o_F0 = o_D + 2 * DK * 4;          // fp32 [DK] exp of tile-0 total
-    static constexpr int total = o_F0 + DK * 4;
+    static constexpr int kNP = kFull ? 2 : 1;               // bf16 planes of "single" operands
+    static constexpr int NCB = DK / 32;                       // 32-channel blocks = intra waves
+    static constexpr int RB = DK + 8;                         // bf16 [token][DK] row stride
+    static constexpr int TB = kC + 8;                         // bf16 [*][token] row stride
+    static constexpr int AF = kC + 4;                         // fp32 [C][C] row stride
+    static constexpr int o_Gp = 0;                            // fp32 [NCB][6][64][4] partials
+    static constexpr int o_Akk = o_Gp + NCB * 6 * 64 * 16;    // fp32 [C][AF]
+    static constexpr int o_T0t = o_Akk + kC * AF * 4;         // fp32 [16][20] T00 transposed
+    static constexpr int o_T1 = o_T0t + 16 * 20 * 4;          // fp32 [16][20] T11
+    static constexpr int o_Tb = o_T1 + 16 * 20 * 4;           // bf16 planes [C][TB]
+    static constexpr int o_Aq = o_Tb + kNP * kC * TB * 2;     // bf16 hi, lo [C][TB]
+    static constexpr int o_W = o_Aq + 2 * kC * TB * 2;        // bf16 planes [C][RB]
+    static constexpr int o_Qt = o_W + kNP * kC * RB * 2;      // bf16 hi, lo [C][RB]
+    static constexpr int o_Ke = o_Qt + 2 * kC * RB * 2;       // bf16 planes [DK][TB] (K_end^T)
+    static constexpr int o_gam = o_Ke + kNP * DK * TB * 2;    // fp32 [DK]
+    static constexpr int o_beta = o_gam + DK * 4;             // fp32 [C]
+    static constexpr int total = o_beta + kC * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
-template <typename L>
-struct Smem {
-    char* base;
-    __device__ bf16* bfp(int off) const { return reinterpret_cast<bf16*>(base + off); }
-    __device__ float* f32p(int off) const { return reinterpret_cast<float*>(base + off); }
-};
+// DPP row shift right by N lanes inside each 16-lane row, zero fill.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x110 + N, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float row_scan16(float x) {   // inclusive prefix sum over a row
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = f2bf(x[e]);
+    return r;
+}
+
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bf16 h, l;
+        split_bf16(x[e], h, l);
+        hi[e] = h;
+        lo[e] = l;
+    }
+}
+
+// Fragment of an f32x4 accumulator pair as an operand with the accumulator-compatible contraction
+// order (element e < 4 from `a`, e >= 4 from `b`).
+__device__ __forceinline__ bf16x8 acc_pair(f32x4 a, f32x4 b) {
+    return bf16x8{f2bf(a[0]), f2bf(a[1]), f2bf(a[2]), f2bf(a[3]),
+                  f2bf(b[0]), f2bf(b[1]), f2bf(b[2]), f2bf(b[3])};
+}
+__device__ __forceinline__ void acc_pair_split(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+    float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    split8(x, hi, lo);
+}
 
 // One block of the grid -> (unit, column slice), slices of a unit on one XCD (the dispatcher
 // places consecutive workgroups on consecutive XCDs, 8 of them).
@@ -101,17 +129,40 @@ __device__ __forceinline__ void block_coords(int nslices, int& unit, int& slice)
     slice = slot % nslices;
 }
 
+// Raw 8-element fragment of one token row as stored (bf16: one 16-byte piece; f32: two).
+template <bool F32IN>
+struct Raw8 {
+    uint4 p[F32IN ? 2 : 1];
+    __device__ void load(const void* src, bool valid) {
+#pragma unroll
+        for (int i = 0; i < (F32IN ? 2 : 1); ++i)
+            p[i] = valid ? reinterpret_cast<const uint4*>(src)[i] : uint4{0u, 0u, 0u, 0u};
+    }
+    __device__ void to_f32(float* x) const {
+        if constexpr (F32IN) {
+            const float* f = reinterpret_cast<const float*>(p);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = f[e];
+        } else {
+            const bf16* b = reinterpret_cast<const bf16*>(p);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = bf2f(b[e]);
+        }
+    }
+};
+
 template <int DK, bool F32IN, bool OUT_F32>
-__global__ __launch_bounds__(kNT, 1) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     using Lay = Layout<DK, F32IN>;
-    using IT = typename Lay::IT;
+    using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr bool kFull = Lay::kFull;
     constexpr int KS = DK / 32;          // 32-channel contraction steps
     constexpr int CT = DK / 16;          // 16-channel tiles of the state
-    constexpr int RB = Lay::RB, RF = Lay::RF, RI = Lay::RI, TB = Lay::TB, AB = Lay::AB,
-                  AF = Lay::AF;
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    Smem<Lay> sm{smem_raw};
+    constexpr int NCB = Lay::NCB;
+    constexpr int RB = Lay::RB, TB = Lay::TB, AF = Lay::AF;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    auto bfp = [&](int off) { return reinterpret_cast<bf16*>(smem + off); };
+    auto f32p = [&](int off) { return reinterpret_cast<float*>(smem + off); };
 
     const int nslices = a.dv / kDVT;
     int unit, slice;
@@ -134,70 +185,62 @@ __global__ __launch_bounds__(kNT, 1) void prefill_kernel(PrefillArgs a) {
     const int H = a.H;
     const size_t sq = (size_t)H * DK;          // token stride of q, k, g (elements)
     const size_t sv = (size_t)H * a.dv;        // token stride of v, o
-    const IT* qg = reinterpret_cast<const IT*>(a.q) + (size_t)row0 * sq + (size_t)h * DK;
-    const IT* kg = reinterpret_cast<const IT*>(a.k) + (size_t)row0 * sq + (size_t)h * DK;
-    const float* gg = a.g + (size_t)row0 * sq + (size_t)h * DK;
-    const IT* vg = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv +
-                   (size_t)slice * kDVT;
-    const IT* bg = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * H + h;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int i16 = lane & 15, g4 = lane >> 4;
+    const bool intra = wave < NCB;              // owns key channels [32 wave, 32 wave + 32)
+    const int ch0 = 32 * wave + 8 * g4;         // this lane's 8 key channels (intra waves)
     const int col0 = slice * kDVT + 16 * wave;  // first value column of this wave
+    const bool vlane = g4 < 2;                  // lanes that load this wave's 16 v columns
+
+    const IT* qg = reinterpret_cast<const IT*>(a.q) + (size_t)row0 * sq + (size_t)h * DK + ch0;
+    const IT* kg = reinterpret_cast<const IT*>(a.k) + (size_t)row0 * sq + (size_t)h * DK + ch0;
+    const float* gg = a.g + (size_t)row0 * sq + (size_t)h * DK + ch0;
+    const IT* vg = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv + col0 +
+                   8 * (g4 & 1);
+    const IT* bg = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * H + h;
 
     // ---- state slice in accumulators: Sacc[ct][j] = S[16 ct + 4 g4 + j][col0 + i16]
     f32x4 Sacc[CT];
-    {
-        const float* S0 = a.S0 ? a.S0 + ((size_t)n * H + h) * DK * a.dv : nullptr;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();
+    if (a.S0) {
+        const float* S0 = a.S0 + ((size_t)n * H + h) * DK * a.dv;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                Sacc[ct][j] = S0 ? S0[(size_t)(16 * ct + 4 * g4 + j) * a.dv + col0 + i16] : 0.f;
+                Sacc[ct][j] = S0[(size_t)(16 * ct + 4 * g4 + j) * a.dv + col0 + i16];
     }
 
-    // ---- prefetch plan (registers), loaded one chunk ahead
-    constexpr int PPR = DK * (int)sizeof(IT) / 16;        // 16-byte pieces per q/k row
-    constexpr int NQK = 2 * kC * PPR / kNT;                // q and k pieces per thread
-    static_assert((2 * kC * PPR) % kNT == 0, "q/k piece split");
-    constexpr int PPV = kDVT * (int)sizeof(IT) / 16;      // pieces per v row
-    constexpr int NV = (kC * PPV + kNT - 1) / kNT;         // v pieces per thread
-    const bool gcol = tid < 2 * DK;                         // column-pass threads
-    const int gc = tid % DK, ga = tid / DK;                 // (channel, 16-row tile)
-    uint4 pqk[NQK];
-    uint4 pv[NV];
-    float pg[16];
-    float pb = 0.f;
+    // identity blocks: B operand selecting channel half hh of a 32-long contraction step
+    bf16x8 Id[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Id[hh][e] = f2bf((8 * g4 + e == 16 * hh + i16) ? 1.f : 0.f);
 
+    // ---- prefetch registers (one chunk ahead): token 16 t + i16 of tile t
+    Raw8<F32IN> pq[2], pk[2], pv[2];
+    float4 pg[2][2];
+    IT pb[2];
     auto prefetch = [&](int64_t c0) {
-        const int nvalid = (int)((len - c0) < kC ? (len - c0) : kC);
+        const int64_t rem = len - c0;
 #pragma unroll
-        for (int i = 0; i < NQK; ++i) {
-            const int p = tid + kNT * i;
-            const int arr = p / (kC * PPR), rem = p % (kC * PPR);
-            const int r = rem / PPR, pc = rem % PPR;
-            const IT* src = (arr ? kg : qg) + (size_t)(c0 + r) * sq;
-            pqk[i] = r < nvalid ? ld<uint4>(reinterpret_cast<const char*>(src) + 16 * pc)
-                                : uint4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int p = tid + kNT * i;
-            const int r = p / PPV, pc = p % PPV;
-            pv[i] = (p < kC * PPV && r < nvalid)
-                        ? ld<uint4>(reinterpret_cast<const char*>(vg + (size_t)(c0 + r) * sv) +
-                                    16 * pc)
-                        : uint4{0u, 0u, 0u, 0u};
-        }
-        if (gcol) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = 16 * ga + r;
-                pg[r] = rr < nvalid ? gg[(size_t)(c0 + rr) * sq + gc] : 0.f;
+        for (int t = 0; t < 2; ++t) {
+            const int r = 16 * t + i16;
+            const bool ok = r < rem;
+            const size_t off = (size_t)(c0 + r);
+            if (intra) {
+                pq[t].load(qg + off * sq, ok);
+                pk[t].load(kg + off * sq, ok);
+                pg[t][0] = ok ? reinterpret_cast<const float4*>(gg + off * sq)[0] : float4{0, 0, 0, 0};
+                pg[t][1] = ok ? reinterpret_cast<const float4*>(gg + off * sq)[1] : float4{0, 0, 0, 0};
             }
+            pv[t].load(vg + off * sv, ok && vlane);
+            pb[t] = ok ? bg[off * H] : IT(0.f);
         }
-        if (tid < kC) pb = tid < nvalid ? static_cast<float>(bg[(size_t)(c0 + tid) * H]) : 0.f;
     };
 
     const int64_t nchunks = (len + kC - 1) / kC;
@@ -207,321 +250,359 @@ __global__ __launch_bounds__(kNT, 1) void prefill_kernel(PrefillArgs a) {
         const int64_t c0 = ci * kC;
         const int nvalid = (int)((len - c0) < kC ? (len - c0) : kC);
 
-        // ---------------- step 0: raw chunk -> LDS
+        // ======================= A: intra-chunk operands (channel-parallel) ==================
+        float qv[2][8], kv[2][8], vv[2][8], L[2][8];
+        float bt[2];
 #pragma unroll
-        for (int i = 0; i < NQK; ++i) {
-            const int p = tid + kNT * i;
-            const int arr = p / (kC * PPR), rem = p % (kC * PPR);
-            const int r = rem / PPR, pc = rem % PPR;
-            char* dst = sm.base + (arr ? Lay::o_rk : Lay::o_rq) + (r * RI) * (int)sizeof(IT) + 16 * pc;
-            st<uint4>(dst, pqk[i]);
-        }
+        for (int t = 0; t < 2; ++t) {
+            pq[t].to_f32(qv[t]);
+            pk[t].to_f32(kv[t]);
+            pv[t].to_f32(vv[t]);
+            bt[t] = static_cast<float>(pb[t]);
+            const float gl[8] = {pg[t][0].x, pg[t][0].y, pg[t][0].z, pg[t][0].w,
+                                 pg[t][1].x, pg[t][1].y, pg[t][1].z, pg[t][1].w};
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int p = tid + kNT * i;
-            if (p < kC * PPV) {
-                const int r = p / PPV, pc = p % PPV;
-                if constexpr (F32IN) {
-                    const float* x = reinterpret_cast<const float*>(&pv[i]);
+            for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
+            if (!vlane) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bf16 hi, lo;
-                        split_bf16(x[e], hi, lo);
-                        const int col = 4 * pc + e;
-                        sm.bfp(Lay::o_Vt)[col * TB + r] = hi;
-                        sm.bfp(Lay::o_Vt + kDVT * TB * 2)[col * TB + r] = lo;
-                    }
-                } else {
-                    const bf16* x = reinterpret_cast<const bf16*>(&pv[i]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sm.bfp(Lay::o_Vt)[(8 * pc + e) * TB + r] = x[e];
-                }
+                for (int e = 0; e < 8; ++e) vv[t][e] = 0.f;
             }
         }
-        if (tid < kC) sm.f32p(Lay::o_beta)[tid] = pb;
-
-        // ---------------- step 1: per-channel decay prefix inside each 16-token tile (log2 units)
-        float Pc[16], Pic[16];
-        if (gcol) {
-            float L = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                L += pg[r] * kLog2e;
-                Pc[r] = exp2f(L);
-                Pic[r] = exp2f(-L);
-                sm.f32p(Lay::o_P)[(16 * ga + r) * RF + gc] = Pc[r];
-                sm.f32p(Lay::o_Pi)[(16 * ga + r) * RF + gc] = Pic[r];
-            }
-            sm.f32p(Lay::o_D)[ga * DK + gc] = L;
-            if (ga == 0) sm.f32p(Lay::o_F0)[gc] = exp2f(L);
-        }
-        __syncthreads();
-        // the column values are consumed: fetch the next chunk while this one is computed
+        // the raw registers are consumed: fetch the next chunk while this one is computed
         if (ci + 1 < nchunks) prefetch(c0 + kC);
+        if (wave == 0 && g4 == 0) {
+            f32p(Lay::o_beta)[i16] = bt[0];
+            f32p(Lay::o_beta)[16 + i16] = bt[1];
+        }
 
-        // ---------------- step 2a: transposed K~ = k exp(G) and K_end = k exp(G_last - G)
-        if (gcol) {
-            const float D0 = sm.f32p(Lay::o_D)[gc], D1 = sm.f32p(Lay::o_D)[DK + gc];
-            const float Eprev = ga ? D0 : 0.f;       // log2 decay from chunk start to tile start
-            const float fK = exp2f(Eprev), fE = exp2f(D0 + D1 - Eprev);
-            if (ga == 0) sm.f32p(Lay::o_gam)[gc] = exp2f(D0 + D1);
-            bf16 kt_h[16], ke_h[16], kt_l[16], ke_l[16];
+        // V^T fragments for U = T_b V (this wave's 16 value columns): token-per-lane ->
+        // column-per-lane through a product with the identity.
+        f32x4 Vf[2], Vfl[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float kv =
-                    static_cast<float>(reinterpret_cast<const IT*>(sm.base + Lay::o_rk)[(16 * ga + r) * RI + gc]);
-                const float xt = kv * Pc[r] * fK, xe = kv * Pic[r] * fE;
-                if constexpr (kFull) {
-                    split_bf16(xt, kt_h[r], kt_l[r]);
-                    split_bf16(xe, ke_h[r], ke_l[r]);
-                } else {
-                    kt_h[r] = f2bf(xt);
-                    ke_h[r] = f2bf(xe);
-                }
-            }
-            bf16* Kt = sm.bfp(Lay::o_Kt) + gc * TB + 16 * ga;
-            bf16* Ke = sm.bfp(Lay::o_Ke) + gc * TB + 16 * ga;
-#pragma unroll
-            for (int r = 0; r < 16; r += 8) {
-                st<bf16x8>(Kt + r, bf16x8{kt_h[r], kt_h[r + 1], kt_h[r + 2], kt_h[r + 3],
-                                          kt_h[r + 4], kt_h[r + 5], kt_h[r + 6], kt_h[r + 7]});
-                st<bf16x8>(Ke + r, bf16x8{ke_h[r], ke_h[r + 1], ke_h[r + 2], ke_h[r + 3],
-                                          ke_h[r + 4], ke_h[r + 5], ke_h[r + 6], ke_h[r + 7]});
-                if constexpr (kFull) {
-                    st<bf16x8>(Kt + DK * TB + r,
-                               bf16x8{kt_l[r], kt_l[r + 1], kt_l[r + 2], kt_l[r + 3], kt_l[r + 4],
-                                      kt_l[r + 5], kt_l[r + 6], kt_l[r + 7]});
-                    st<bf16x8>(Ke + DK * TB + r,
-                               bf16x8{ke_l[r], ke_l[r + 1], ke_l[r + 2], ke_l[r + 3], ke_l[r + 4],
-                                      ke_l[r + 5], ke_l[r + 6], ke_l[r + 7]});
-                }
+        for (int t = 0; t < 2; ++t) {
+            if constexpr (kFull) {
+                bf16x8 vh, vl;
+                split8(vv[t], vh, vl);
+                Vf[t] = mma(vh, Id[0], zero4());
+                Vfl[t] = mma(vl, Id[0], zero4());
+            } else {
+                Vf[t] = mma(to_bf16x8(vv[t]), Id[0], zero4());
             }
         }
 
-        // ---------------- step 2b: row-major decayed operands (split Gram operands, Q~)
-        {
-            constexpr int NG8 = DK / 8;
-            constexpr int NTASK = kC * NG8;
+        f32x4 Ktf[2][2], Ktfl[2][2];   // K~^T fragments [tile][channel half]
+        if (intra) {
+            // in-tile prefix of the log2 decay (DPP scan across the 16 token lanes of a row)
+            float D[2][8];
 #pragma unroll
-            for (int it = 0; it < (NTASK + kNT - 1) / kNT; ++it) {
-                const int id = tid + kNT * it;
-                if (NTASK % kNT == 0 || id < NTASK) {
-                    const int r = id / NG8, c8 = 8 * (id % NG8);
-                    const int tile = r >> 4;
-                    float qv[8], kv[8];
-                    const IT* rq = reinterpret_cast<const IT*>(sm.base + Lay::o_rq) + r * RI + c8;
-                    const IT* rk = reinterpret_cast<const IT*>(sm.base + Lay::o_rk) + r * RI + c8;
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        qv[e] = static_cast<float>(rq[e]) * a.scale;
-                        kv[e] = static_cast<float>(rk[e]);
-                    }
-                    const float* P = sm.f32p(Lay::o_P) + r * RF + c8;
-                    const float* Pi = sm.f32p(Lay::o_Pi) + r * RF + c8;
-                    const float* F0 = sm.f32p(Lay::o_F0) + c8;
-                    bf16x8 qh, ql, krh, krl, kdh, kdl, kch, kcl;
+                for (int e = 0; e < 8; ++e) {
+                    L[t][e] = row_scan16(L[t][e]);
+                    D[t][e] = __shfl(L[t][e], (lane & ~15) | 15, 64);   // tile total
+                }
+            float P[2][8], Pi[2][8], F0[8], F1[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float p = P[e], pi = Pi[e];
-                        const float qs = qv[e] * p, kr = kv[e] * p, kd = kv[e] * pi;
-                        bf16 h_, l_;
-                        split_bf16(qs, h_, l_); qh[e] = h_; ql[e] = l_;
-                        split_bf16(kr, h_, l_); krh[e] = h_; krl[e] = l_;
-                        split_bf16(kd, h_, l_); kdh[e] = h_; kdl[e] = l_;
-                        if (tile == 0) { split_bf16(kd * F0[e], h_, l_); kch[e] = h_; kcl[e] = l_; }
-                    }
-                    const int off = r * RB + c8;
-                    st<bf16x8>(sm.bfp(Lay::o_Qs) + off, qh);
-                    st<bf16x8>(sm.bfp(Lay::o_Qs) + kC * RB + off, ql);
-                    st<bf16x8>(sm.bfp(Lay::o_Kr) + off, krh);
-                    st<bf16x8>(sm.bfp(Lay::o_Kr) + kC * RB + off, krl);
-                    st<bf16x8>(sm.bfp(Lay::o_Kd) + off, kdh);
-                    st<bf16x8>(sm.bfp(Lay::o_Kd) + kC * RB + off, kdl);
-                    if (tile == 0) {
-                        st<bf16x8>(sm.bfp(Lay::o_Kc) + off, kch);
-                        st<bf16x8>(sm.bfp(Lay::o_Kc) + 16 * RB + off, kcl);
+            for (int e = 0; e < 8; ++e) {
+                F0[e] = fast_exp2(D[0][e]);      // decay over tile 0
+                F1[e] = fast_exp2(D[1][e]);      // decay over tile 1
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    P[t][e] = fast_exp2(L[t][e]);        // tile start -> token, <= 1
+                    Pi[t][e] = fast_exp2(-L[t][e]);      // token -> tile start, >= 1
+                }
+            }
+            if (i16 == 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f32p(Lay::o_gam)[ch0 + e] = F0[e] * F1[e];
+            }
+            // decayed operands (fp32), then Gram partial products over this wave's channels
+            float Qs[2][8], Kr[2][8], Kd[2][8], Kc[8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    Qs[t][e] = qv[t][e] * a.scale * P[t][e];
+                    Kr[t][e] = kv[t][e] * P[t][e];
+                    Kd[t][e] = kv[t][e] * Pi[t][e];
+                }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Kc[e] = Kd[0][e] * F0[e];   // tile 0 seen from tile 1
+            bf16x8 Qh[2], Ql[2], Krh[2], Krl[2], Kdh[2], Kdl[2], Kch, Kcl;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                split8(Qs[t], Qh[t], Ql[t]);
+                split8(Kr[t], Krh[t], Krl[t]);
+                split8(Kd[t], Kdh[t], Kdl[t]);
+            }
+            split8(Kc, Kch, Kcl);
+            // Gram tiles transposed (column side as the A operand): the accumulator of lane
+            // (row r = i16, g4) holds A[r][16 b + 4 g4 + j].  m: 0 qk00, 1 qk11, 2 qk10,
+            // 3 kk00, 4 kk11, 5 kk10.
+            f32x4 G[6];
+#pragma unroll
+            for (int m = 0; m < 6; ++m) {
+                const int ta = (m % 3 == 0) ? 0 : 1;
+                const bf16x8 ch = (m % 3 == 2) ? Kch : Kdh[ta];
+                const bf16x8 cl = (m % 3 == 2) ? Kcl : Kdl[ta];
+                const bf16x8 rh = (m < 3) ? Qh[ta] : Krh[ta];
+                const bf16x8 rl = (m < 3) ? Ql[ta] : Krl[ta];
+                f32x4 acc = mma(ch, rh, zero4());
+                acc = mma(cl, rh, acc);
+                acc = mma(ch, rl, acc);
+                G[m] = acc;
+            }
+#pragma unroll
+            for (int m = 0; m < 6; ++m)
+                st<f32x4>(smem + Lay::o_Gp + ((wave * 6 + m) * 64 + lane) * 16, G[m]);
+
+            // Q~ = Q exp(G) (split, row-major [token][DK]); tile 1 carries the tile-0 decay
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 hh = Qh[t], ll = Ql[t];
+                if (t == 1) {
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = Qs[1][e] * F0[e];
+                    split8(x, hh, ll);
+                }
+                st<bf16x8>(bfp(Lay::o_Qt) + (16 * t + i16) * RB + ch0, hh);
+                st<bf16x8>(bfp(Lay::o_Qt) + kC * RB + (16 * t + i16) * RB + ch0, ll);
+            }
+            // K~ = K exp(G) and K_end = K exp(G_last - G), transposed through the identity:
+            // the accumulator of lane (channel i16 of half hh, g4) holds tokens 16 t + 4 g4 + j.
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                float xt[8], xe[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xt[e] = t ? Kr[1][e] * F0[e] : Kr[0][e];
+                    xe[e] = t ? Kd[1][e] * F1[e] : Kc[e] * F1[e];
+                }
+                bf16x8 th, tl, eh, el;
+                if constexpr (kFull) {
+                    split8(xt, th, tl);
+                    split8(xe, eh, el);
+                } else {
+                    th = to_bf16x8(xt);
+                    eh = to_bf16x8(xe);
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    Ktf[t][hh] = mma(th, Id[hh], zero4());
+                    const f32x4 ke = mma(eh, Id[hh], zero4());
+                    bf16* dst = bfp(Lay::o_Ke) + (32 * wave + 16 * hh + i16) * TB + 16 * t + 4 * g4;
+                    st<bf16x4>(dst, bf16x4{f2bf(ke[0]), f2bf(ke[1]), f2bf(ke[2]), f2bf(ke[3])});
+                    if constexpr (kFull) {
+                        Ktfl[t][hh] = mma(tl, Id[hh], zero4());
+                        const f32x4 kel = mma(el, Id[hh], zero4());
+                        st<bf16x4>(dst + DK * TB, bf16x4{f2bf(kel[0]), f2bf(kel[1]), f2bf(kel[2]), f2bf(kel[3])});
                     }
                 }
             }
         }
         __syncthreads();
 
-        // ---------------- step 3: Gram tiles A_qk, A_kk (split operands, 3 MFMAs per step)
-        if (wave < 3) {
-            const int ta = wave == 0 ? 0 : 1;             // row tile
-            const int tb = wave == 1 ? 1 : 0;             // column tile
-            const bf16* Qh = sm.bfp(Lay::o_Qs) + (16 * ta + i16) * RB + 8 * g4;
-            const bf16* Kh = sm.bfp(Lay::o_Kr) + (16 * ta + i16) * RB + 8 * g4;
-            const bf16* Bh = (ta == tb) ? sm.bfp(Lay::o_Kd) + (16 * tb + i16) * RB + 8 * g4
-                                        : sm.bfp(Lay::o_Kc) + i16 * RB + 8 * g4;
-            const int Blo = (ta == tb) ? kC * RB : 16 * RB;
-            f32x4 aq = zero4(), ak = zero4();
+        // ======================= B: Gram reduction and the UT solve =========================
+        if (wave == 0) {
+            // A_kk tiles (masked, rows scaled by beta) -> fp32 row-major
+            const float* beta = f32p(Lay::o_beta);
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 qh = ld<bf16x8>(Qh + 32 * s), ql = ld<bf16x8>(Qh + kC * RB + 32 * s);
-                const bf16x8 kh = ld<bf16x8>(Kh + 32 * s), kl = ld<bf16x8>(Kh + kC * RB + 32 * s);
-                const bf16x8 bh = ld<bf16x8>(Bh + 32 * s), bl = ld<bf16x8>(Bh + Blo + 32 * s);
-                aq = mma(qh, bh, aq);
-                aq = mma(ql, bh, aq);
-                aq = mma(qh, bl, aq);
-                ak = mma(kh, bh, ak);
-                ak = mma(kl, bh, ak);
-                ak = mma(kh, bl, ak);
+            for (int m = 3; m < 6; ++m) {
+                f32x4 s = zero4();
+#pragma unroll
+                for (int w = 0; w < NCB; ++w) s += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
+                const int ta = (m == 3) ? 0 : 1, tb = (m == 4) ? 1 : 0;
+                const int r = 16 * ta + i16;
+                const float br = beta[r];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 16 * tb + 4 * g4 + j;
+                    s[j] = (i < r) ? s[j] * br : 0.f;
+                }
+                st<f32x4>(f32p(Lay::o_Akk) + r * AF + 16 * tb + 4 * g4, s);
             }
-            const int col = 16 * tb + i16;
+            // inverses of the two unit-lower-triangular diagonal blocks, one lane per column:
+            // lanes 0-15 block 0, lanes 16-31 block 1
+            const int bb = (lane >> 4) & 1, c = i16;
+            if (lane < 32) {
+                float x[16];
+                const float* Ab = f32p(Lay::o_Akk) + (16 * bb) * AF + 16 * bb;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * ta + 4 * g4 + j;
-                const float vq = (col <= row) ? aq[j] : 0.f;
-                const float vk = (col < row) ? ak[j] * sm.f32p(Lay::o_beta)[row] : 0.f;
-                bf16 hq, lq;
-                split_bf16(vq, hq, lq);
-                sm.bfp(Lay::o_Aq)[row * AB + col] = hq;
-                sm.bfp(Lay::o_Aq + kC * AB * 2)[row * AB + col] = lq;
-                sm.f32p(Lay::o_Akk)[row * AF + col] = vk;
+                for (int r = 0; r < 16; ++r) {
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int j = 0; j < r; ++j) {
+                        if (j & 1) s1 += Ab[r * AF + j] * x[j];
+                        else s0 += Ab[r * AF + j] * x[j];
+                    }
+                    x[r] = (r == c) ? 1.f : ((r > c) ? -(s0 + s1) : 0.f);
+                }
+                const float bc = beta[16 * bb + c];
+                bf16* Tb = bfp(Lay::o_Tb) + (16 * bb) * TB + 16 * bb + c;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if constexpr (kFull) {
+                        bf16 hh, ll;
+                        split_bf16(x[r] * bc, hh, ll);
+                        Tb[r * TB] = hh;
+                        Tb[kC * TB + r * TB] = ll;
+                    } else {
+                        Tb[r * TB] = f2bf(x[r] * bc);
+                    }
+                }
+                if (bb == 0) {
+#pragma unroll
+                    for (int r = 0; r < 16; r += 4)
+                        st<f32x4>(f32p(Lay::o_T0t) + c * 20 + r, f32x4{x[r], x[r + 1], x[r + 2], x[r + 3]});
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) f32p(Lay::o_T1)[r * 20 + c] = x[r];
+                }
+            } else {
+                // upper-right block of T_b is zero
+                const int lz = lane - 32;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int idx = lz * 8 + q, r = idx >> 4, cc = idx & 15;
+                    bfp(Lay::o_Tb)[r * TB + 16 + cc] = f2bf(0.f);
+                    if constexpr (kFull) bfp(Lay::o_Tb)[kC * TB + r * TB + 16 + cc] = f2bf(0.f);
+                }
+            }
+            // X = A_kk[1,0] T00 and T10 = -T11 X with split MFMA products (contraction 16, the
+            // upper half of each 32-long step is zero)
+            {
+                float xa[8], xb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xa[e] = g4 < 2 ? f32p(Lay::o_Akk)[(16 + i16) * AF + 8 * g4 + e] : 0.f;
+                    xb[e] = g4 < 2 ? f32p(Lay::o_T0t)[i16 * 20 + 8 * g4 + e] : 0.f;
+                }
+                bf16x8 ah, al, bh, bl;
+                split8(xa, ah, al);
+                split8(xb, bh, bl);
+                f32x4 X = mma(ah, bh, zero4());
+                X = mma(al, bh, X);
+                X = mma(ah, bl, X);
+                // X accumulator: lane (column c, g4) holds X[4 g4 + j][c]; as a B operand with
+                // contraction index 4 g4 + e (e < 4) it pairs with T11[r][4 g4 + e]
+                float x1[8], x2[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    x1[e] = e < 4 ? f32p(Lay::o_T1)[i16 * 20 + 4 * g4 + e] : 0.f;
+                    x2[e] = e < 4 ? X[e] : 0.f;
+                }
+                split8(x1, ah, al);
+                split8(x2, bh, bl);
+                f32x4 T10 = mma(ah, bh, zero4());
+                T10 = mma(al, bh, T10);
+                T10 = mma(ah, bl, T10);
+                const float bc = beta[i16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v = -T10[j] * bc;
+                    bf16* Tb = bfp(Lay::o_Tb) + (16 + 4 * g4 + j) * TB + i16;
+                    if constexpr (kFull) {
+                        bf16 hh, ll;
+                        split_bf16(v, hh, ll);
+                        Tb[0] = hh;
+                        Tb[kC * TB] = ll;
+                    } else {
+                        Tb[0] = f2bf(v);
+                    }
+                }
             }
         } else {
-            // upper-right block of A_qk (row tile 0, column tile 1) is zero
+            // A_qk tiles (masked) -> split bf16 row-major; wave 1 also zeroes the upper block
+            const int m = wave - 1;
+            f32x4 s = zero4();
+#pragma unroll
+            for (int w = 0; w < NCB; ++w) s += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
+            const int ta = (m == 0) ? 0 : 1, tb = (m == 1) ? 1 : 0;
+            const int r = 16 * ta + i16;
+            bf16x4 hv, lv;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = 4 * g4 + j, col = 16 + i16;
-                sm.bfp(Lay::o_Aq)[row * AB + col] = f2bf(0.f);
-                sm.bfp(Lay::o_Aq + kC * AB * 2)[row * AB + col] = f2bf(0.f);
-            }
-        }
-        __syncthreads();
-
-        // ---------------- step 4: inverses of the two unit-lower-triangular diagonal blocks
-        if (wave == 0 && lane < 32) {
-            const int bb = lane >> 4, c = i16;
-            const float* Ab = sm.f32p(Lay::o_Akk) + (16 * bb) * AF + 16 * bb;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < r; ++j) s += Ab[r * AF + j] * x[j];
-                x[r] = (r == c) ? 1.f : ((r > c) ? -s : 0.f);
-            }
-            float* Tb = sm.f32p(Lay::o_Tm) + (16 * bb) * AF + 16 * bb;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Tb[r * AF + c] = x[r];
-        }
-        __syncthreads();
-
-        // ---------------- step 5: X = A_kk[1,0] T00, kept in the unused upper block of A_kk
-        {
-            const int r = tid >> 4, c = tid & 15;
-            const float* A10 = sm.f32p(Lay::o_Akk) + (16 + r) * AF;
-            const float* T00 = sm.f32p(Lay::o_Tm);
-            float s = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) s += A10[m] * T00[m * AF + c];
-            sm.f32p(Lay::o_Akk)[r * AF + 16 + c] = s;
-        }
-        __syncthreads();
-
-        // ---------------- step 6: T10 = -T11 X, then T_b = T Diag(beta) in bf16
-        {
-            const int r = tid >> 4, c = tid & 15;
-            const float* T11 = sm.f32p(Lay::o_Tm) + (16 + r) * AF + 16;
-            float s = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) s += T11[m] * sm.f32p(Lay::o_Akk)[m * AF + 16 + c];
-            const float* beta = sm.f32p(Lay::o_beta);
-            const float t00 = sm.f32p(Lay::o_Tm)[r * AF + c] * beta[c];
-            const float t11 = sm.f32p(Lay::o_Tm)[(16 + r) * AF + 16 + c] * beta[16 + c];
-            const float t10 = -s * beta[c];
-            bf16* Tb = sm.bfp(Lay::o_Tb);
-            if constexpr (kFull) {
+                const int i = 16 * tb + 4 * g4 + j;
                 bf16 hh, ll;
-                split_bf16(t00, hh, ll); Tb[r * AB + c] = hh; Tb[kC * AB + r * AB + c] = ll;
-                split_bf16(t11, hh, ll); Tb[(16 + r) * AB + 16 + c] = hh; Tb[kC * AB + (16 + r) * AB + 16 + c] = ll;
-                split_bf16(t10, hh, ll); Tb[(16 + r) * AB + c] = hh; Tb[kC * AB + (16 + r) * AB + c] = ll;
-                Tb[r * AB + 16 + c] = f2bf(0.f); Tb[kC * AB + r * AB + 16 + c] = f2bf(0.f);
-            } else {
-                Tb[r * AB + c] = f2bf(t00);
-                Tb[(16 + r) * AB + 16 + c] = f2bf(t11);
-                Tb[(16 + r) * AB + c] = f2bf(t10);
-                Tb[r * AB + 16 + c] = f2bf(0.f);
+                split_bf16((i <= r) ? s[j] : 0.f, hh, ll);
+                hv[j] = hh;
+                lv[j] = ll;
+            }
+            st<bf16x4>(bfp(Lay::o_Aq) + r * TB + 16 * tb + 4 * g4, hv);
+            st<bf16x4>(bfp(Lay::o_Aq) + kC * TB + r * TB + 16 * tb + 4 * g4, lv);
+            if (m == 0) {
+                const bf16x4 z{f2bf(0.f), f2bf(0.f), f2bf(0.f), f2bf(0.f)};
+                st<bf16x4>(bfp(Lay::o_Aq) + i16 * TB + 16 + 4 * g4, z);
+                st<bf16x4>(bfp(Lay::o_Aq) + kC * TB + i16 * TB + 16 + 4 * g4, z);
             }
         }
         __syncthreads();
 
-        // ---------------- step 7: W^T = K~^T T_b^T (all waves) and U = T_b V (own columns)
-        {
-            const bf16* Tb = sm.bfp(Lay::o_Tb);
-            constexpr int NWT = CT * 2;                    // output tiles of W^T
+        // ======================= C: W (this wave's channels) and U (its value columns) =======
+        auto ldTb = [&](int row, int plane) -> bf16x8 {   // T_b[row][4 g4 + e | 16 + 4 g4 + e]
+            const bf16* p = bfp(Lay::o_Tb) + plane * kC * TB + row * TB;
+            return cat44(ld<bf16x4>(p + 4 * g4), ld<bf16x4>(p + 16 + 4 * g4));
+        };
+        if (intra) {
 #pragma unroll
-            for (int tt = wave; tt < NWT; tt += 4) {
-                const int ct = tt >> 1, tk = tt & 1;
-                const bf16* Ka = sm.bfp(Lay::o_Kt) + (16 * ct + i16) * TB + 8 * g4;
-                const bf16* Bt = Tb + (16 * tk + i16) * AB + 8 * g4;
-                f32x4 acc = mma(ld<bf16x8>(Ka), ld<bf16x8>(Bt), zero4());
-                if constexpr (kFull) {
-                    acc = mma(ld<bf16x8>(Ka + DK * TB), ld<bf16x8>(Bt), acc);
-                    acc = mma(ld<bf16x8>(Ka), ld<bf16x8>(Bt + kC * AB), acc);
-                }
-                // acc[j] = W[16 tk + i16][16 ct + 4 g4 + j]
-                bf16* Wd = sm.bfp(Lay::o_W) + (16 * tk + i16) * RB + 16 * ct + 4 * g4;
-                if constexpr (kFull) {
-                    bf16x4 hv, lv;
+            for (int hh = 0; hh < 2; ++hh) {
+                const bf16x8 ka = acc_pair(Ktf[0][hh], Ktf[1][hh]);
+                bf16x8 kal;
+                if constexpr (kFull) kal = acc_pair(Ktfl[0][hh], Ktfl[1][hh]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) { bf16 hh, ll; split_bf16(acc[j], hh, ll); hv[j] = hh; lv[j] = ll; }
-                    st<bf16x4>(Wd, hv);
-                    st<bf16x4>(Wd + kC * RB, lv);
-                } else {
-                    st<bf16x4>(Wd, bf16x4{f2bf(acc[0]), f2bf(acc[1]), f2bf(acc[2]), f2bf(acc[3])});
+                for (int tt = 0; tt < 2; ++tt) {
+                    const bf16x8 tb = ldTb(16 * tt + i16, 0);
+                    f32x4 acc = mma(ka, tb, zero4());
+                    if constexpr (kFull) {
+                        acc = mma(kal, tb, acc);
+                        acc = mma(ka, ldTb(16 * tt + i16, 1), acc);
+                    }
+                    // acc[j] = W[16 tt + i16][32 wave + 16 hh + 4 g4 + j]
+                    bf16* Wd = bfp(Lay::o_W) + (16 * tt + i16) * RB + 32 * wave + 16 * hh + 4 * g4;
+                    if constexpr (kFull) {
+                        bf16x4 hv, lv;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) { bf16 h1, l1; split_bf16(acc[j], h1, l1); hv[j] = h1; lv[j] = l1; }
+                        st<bf16x4>(Wd, hv);
+                        st<bf16x4>(Wd + kC * RB, lv);
+                    } else {
+                        st<bf16x4>(Wd, bf16x4{f2bf(acc[0]), f2bf(acc[1]), f2bf(acc[2]), f2bf(acc[3])});
+                    }
                 }
             }
         }
         f32x4 U[2];
         {
-            const bf16* Tb = sm.bfp(Lay::o_Tb);
-            const bf16* Vb = sm.bfp(Lay::o_Vt) + (16 * wave + i16) * TB + 8 * g4;
-            const bf16x8 vh = ld<bf16x8>(Vb);
+            const bf16x8 vb = acc_pair(Vf[0], Vf[1]);
+            bf16x8 vbl;
+            if constexpr (kFull) vbl = acc_pair(Vfl[0], Vfl[1]);
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta) {
-                const bf16* Ta = Tb + (16 * ta + i16) * AB + 8 * g4;
-                U[ta] = mma(ld<bf16x8>(Ta), vh, zero4());
+                const bf16x8 tr = ldTb(16 * ta + i16, 0);
+                U[ta] = mma(tr, vb, zero4());
                 if constexpr (kFull) {
-                    U[ta] = mma(ld<bf16x8>(Ta + kC * AB), vh, U[ta]);
-                    U[ta] = mma(ld<bf16x8>(Ta), ld<bf16x8>(Vb + kDVT * TB), U[ta]);
+                    U[ta] = mma(ldTb(16 * ta + i16, 1), vb, U[ta]);
+                    U[ta] = mma(tr, vbl, U[ta]);
                 }
             }
         }
         __syncthreads();
 
-        // ---------------- step 8: inter-chunk part on this wave's 16 state columns
+        // ======================= D: inter-chunk part on this wave's 16 state columns =========
         {
             // state as B operand: contraction index (32-channel step s, g4, e) ->
-            // channel 32 s + 4 g4 + e (e < 4), 32 s + 16 + 4 g4 + (e - 4) (e >= 4).
-            // Sh/Sl: the state split hi + lo; Fh/Fl: Diag(exp(G at the end of tile 0)) S, the
-            // entering state seen from the start of tile 1, so that tile 1's (Q * exp(G)) S is
-            // Qs S' with the same split Qs operand as the Gram tiles.
-            bf16x8 Sh[KS], Sl[KS], Fh[KS], Fl[KS];
-            const float* F0 = sm.f32p(Lay::o_F0);
+            // channel 32 s + 4 g4 + e (e < 4), 32 s + 16 + 4 g4 + (e - 4) (e >= 4)
+            bf16x8 Sh[KS], Sl[KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int ct = 2 * s + (e >> 2), j = e & 3;
-                    const float x = Sacc[ct][j];
-                    bf16 hh, ll;
-                    split_bf16(x, hh, ll);
-                    Sh[s][e] = hh;
-                    Sl[s][e] = ll;
-                    split_bf16(x * F0[16 * ct + 4 * g4 + j], hh, ll);
-                    Fh[s][e] = hh;
-                    Fl[s][e] = ll;
-                }
+            for (int s = 0; s < KS; ++s) acc_pair_split(Sacc[2 * s], Sacc[2 * s + 1], Sh[s], Sl[s]);
             auto ldA = [&](const bf16* rowp, int s) -> bf16x8 {   // same channel selection
                 return cat44(ld<bf16x4>(rowp + 32 * s + 4 * g4), ld<bf16x4>(rowp + 32 * s + 16 + 4 * g4));
             };
             f32x4 Vt[2];
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta) {
-                const bf16* Wr = sm.bfp(Lay::o_W) + (16 * ta + i16) * RB;
+                const bf16* Wr = bfp(Lay::o_W) + (16 * ta + i16) * RB;
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
@@ -536,30 +617,23 @@ __global__ __launch_bounds__(kNT, 1) void prefill_kernel(PrefillArgs a) {
             }
             // V~ as B operand: token index (g4, e) -> 4 g4 + e (e < 4), 16 + 4 g4 + (e - 4)
             bf16x8 Vh, Vl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16 hh, ll;
-                split_bf16(Vt[e >> 2][e & 3], hh, ll);
-                Vh[e] = hh;
-                Vl[e] = ll;
-            }
-            // outputs O = Q~ S + A_qk V~ (Q~ S as split Qs times the split (rescaled) state)
+            acc_pair_split(Vt[0], Vt[1], Vh, Vl);
+            // outputs O = Q~ S + A_qk V~
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta) {
-                const bf16* Qr = sm.bfp(Lay::o_Qs) + (16 * ta + i16) * RB;
+                const bf16* Qr = bfp(Lay::o_Qt) + (16 * ta + i16) * RB;
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
                     const bf16x8 qa = ldA(Qr, s), ql = ldA(Qr + kC * RB, s);
-                    const bf16x8 bh = ta ? Fh[s] : Sh[s], bl = ta ? Fl[s] : Sl[s];
-                    acc = mma(qa, bh, acc);
-                    acc = mma(ql, bh, acc);
-                    acc = mma(qa, bl, acc);
+                    acc = mma(qa, Sh[s], acc);
+                    acc = mma(ql, Sh[s], acc);
+                    acc = mma(qa, Sl[s], acc);
                 }
-                const bf16* Ar = sm.bfp(Lay::o_Aq) + (16 * ta + i16) * AB;
+                const bf16* Ar = bfp(Lay::o_Aq) + (16 * ta + i16) * TB;
                 const bf16x8 ah = cat44(ld<bf16x4>(Ar + 4 * g4), ld<bf16x4>(Ar + 16 + 4 * g4));
-                const bf16x8 al = cat44(ld<bf16x4>(Ar + kC * AB + 4 * g4),
-                                        ld<bf16x4>(Ar + kC * AB + 16 + 4 * g4));
+                const bf16x8 al = cat44(ld<bf16x4>(Ar + kC * TB + 4 * g4),
+                                        ld<bf16x4>(Ar + kC * TB + 16 + 4 * g4));
                 acc = mma(ah, Vh, acc);
                 acc = mma(al, Vh, acc);
                 acc = mma(ah, Vl, acc);
@@ -574,14 +648,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill_kernel(PrefillArgs a) {
                 }
             }
             // state: S <- Diag(gamma_last) S + K_end^T V~
-            const float* gam = sm.f32p(Lay::o_gam);
+            const float* gam = f32p(Lay::o_gam);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const bf16* Kr = sm.bfp(Lay::o_Ke) + (16 * ct + i16) * TB;
+                const bf16* Kr = bfp(Lay::o_Ke) + (16 * ct + i16) * TB;
                 const bf16x8 ka = cat44(ld<bf16x4>(Kr + 4 * g4), ld<bf16x4>(Kr + 16 + 4 * g4));
-                f32x4 s = Sacc[ct];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s[j] *= gam[16 * ct + 4 * g4 + j];
+                const f32x4 gm = ld<f32x4>(gam + 16 * ct + 4 * g4);
+                f32x4 s = Sacc[ct] * gm;
                 s = mma(ka, Vh, s);
                 s = mma(ka, Vl, s);
                 if constexpr (kFull)
@@ -623,7 +696,7 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
 
 hipError_t launch_chunk_fwd(const PrefillArgs& a) {
     if (a.dk == 128) {
-        // float32 inputs at dk = 128 would not fit the 160 KB LDS (rejected by the ABI)
+        // float32 inputs are supported at dk = 64 (the ABI rejects them at dk = 128)
         if (a.in_f32) return hipErrorInvalidValue;
         return a.out_f32 ? launch_prefill<128, false, true>(a) : launch_prefill<128, false, false>(a);
     }
