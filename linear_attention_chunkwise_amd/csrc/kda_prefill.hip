@@ -27,9 +27,10 @@
 //     operands are built in registers and feed MFMA directly: partial Gram tiles over the wave's
 //     channels (summed across waves through LDS), and "transposes" (product with an identity
 //     block) that turn token-per-lane fragments into channel-per-lane ones for K~, K_end and V.
-//   B (solve, one wave): A_kk is reduced, the two 16x16 diagonal blocks of (I + A_kk) are inverted
-//     by forward substitution (one lane per column) and the off-diagonal block is assembled with
-//     split MFMA products; the other waves reduce A_qk meanwhile.
+//   B (solve): waves 0 and 1 each reduce one diagonal 16x16 block of A_kk and invert I + A_kk
+//     there by forward substitution (one lane per column, the matrix entries broadcast from the
+//     reduced accumulators with v_readlane); the off-diagonal block of the inverse is assembled
+//     with split MFMA products; waves 2 and 3 reduce A_qk meanwhile.
 //   C: W^T = K~^T T_b^T for the wave's channels; U = T_b V for the wave's value columns.
 //   D (inter, column-parallel): wave w owns value columns [16w, 16w + 16) of the slice: its slice
 //     of the state (dk x 16, fp32) lives in MFMA accumulators for the whole sequence and doubles
@@ -59,11 +60,9 @@ struct Layout {
     static constexpr int NCB = DK / 32;                       // 32-channel blocks = intra waves
     static constexpr int RB = DK + 8;                         // bf16 [token][DK] row stride
     static constexpr int TB = kC + 8;                         // bf16 [*][token] row stride
-    static constexpr int AF = kC + 4;                         // fp32 [C][C] row stride
     static constexpr int o_Gp = 0;                            // fp32 [NCB][6][64][4] partials
-    static constexpr int o_Akk = o_Gp + NCB * 6 * 64 * 16;    // fp32 [C][AF]
-    static constexpr int o_T0t = o_Akk + kC * AF * 4;         // fp32 [16][20] T00 transposed
-    static constexpr int o_T1 = o_T0t + 16 * 20 * 4;          // fp32 [16][20] T11
+    static constexpr int o_Y = o_Gp + NCB * 6 * 64 * 16;      // fp32 [64][4] A_kk[1,0] T00
+    static constexpr int o_T1 = o_Y + 64 * 16;                // fp32 [16][20] T11
     static constexpr int o_Tb = o_T1 + 16 * 20 * 4;           // bf16 planes [C][TB]
     static constexpr int o_Aq = o_Tb + kNP * kC * TB * 2;     // bf16 hi, lo [C][TB]
     static constexpr int o_W = o_Aq + 2 * kC * TB * 2;        // bf16 planes [C][RB]
@@ -120,6 +119,13 @@ __device__ __forceinline__ void acc_pair_split(f32x4 a, f32x4 b, bf16x8& hi, bf1
     split8(x, hi, lo);
 }
 
+// Storage order of every 32-long contraction index in LDS: position pm(c) puts the elements one
+// lane feeds to a 16x16x32 MFMA with the accumulator-compatible order (4 g4 + e for e < 4,
+// 16 + 4 g4 + e - 4 for e >= 4) next to each other, so an operand is one 16-byte read.
+__device__ __forceinline__ constexpr int pm(int c) {
+    return (c & 16) ? ((c & 15) >> 2) * 8 + 4 + (c & 3) : (c >> 2) * 8 + (c & 3);
+}
+
 // One block of the grid -> (unit, column slice), slices of a unit on one XCD (the dispatcher
 // places consecutive workgroups on consecutive XCDs, 8 of them).
 __device__ __forceinline__ void block_coords(int nslices, int& unit, int& slice) {
@@ -129,14 +135,31 @@ __device__ __forceinline__ void block_coords(int nslices, int& unit, int& slice)
     slice = slot % nslices;
 }
 
+// Buffer resource over [base, base + bytes): loads at or past `bytes` return zero, so the ragged
+// tail of a sequence needs neither branches nor clamped addresses.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+constexpr uint32_t kOOB = 0x80000000u;   // an offset past every resource: reads zero
+
+// Redefine a prefetched register at the point of use.  Without this the compiler moves the
+// conversions of next-chunk data up to the loads at the end of the previous iteration, which
+// forces an immediate wait for HBM there instead of one chunk later.
+__device__ __forceinline__ void pin(uint4& u) {
+    asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+}
+__device__ __forceinline__ void pin(uint32_t& u) { asm volatile("" : "+v"(u)); }
+
 // Raw 8-element fragment of one token row as stored (bf16: one 16-byte piece; f32: two).
 template <bool F32IN>
 struct Raw8 {
     uint4 p[F32IN ? 2 : 1];
-    __device__ void load(const void* src, bool valid) {
+    __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
-        for (int i = 0; i < (F32IN ? 2 : 1); ++i)
-            p[i] = valid ? reinterpret_cast<const uint4*>(src)[i] : uint4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < (F32IN ? 2 : 1); ++i) p[i] = bload16(r, off + 16 * i);
     }
     __device__ void to_f32(float* x) const {
         if constexpr (F32IN) {
@@ -144,9 +167,13 @@ struct Raw8 {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = f[e];
         } else {
-            const bf16* b = reinterpret_cast<const bf16*>(p);
+            // whole 32-bit words: element 2i is the low half, 2i+1 the high half
+            const uint32_t w[4] = {p[0].x, p[0].y, p[0].z, p[0].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = bf2f(b[e]);
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+                x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+            }
         }
     }
 };
@@ -159,7 +186,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     constexpr int KS = DK / 32;          // 32-channel contraction steps
     constexpr int CT = DK / 16;          // 16-channel tiles of the state
     constexpr int NCB = Lay::NCB;
-    constexpr int RB = Lay::RB, TB = Lay::TB, AF = Lay::AF;
+    constexpr int RB = Lay::RB, TB = Lay::TB;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     auto bfp = [&](int off) { return reinterpret_cast<bf16*>(smem + off); };
     auto f32p = [&](int off) { return reinterpret_cast<float*>(smem + off); };
@@ -187,19 +214,30 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     const size_t sv = (size_t)H * a.dv;        // token stride of v, o
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int i16 = lane & 15, g4 = lane >> 4;
     const bool intra = wave < NCB;              // owns key channels [32 wave, 32 wave + 32)
     const int ch0 = 32 * wave + 8 * g4;         // this lane's 8 key channels (intra waves)
     const int col0 = slice * kDVT + 16 * wave;  // first value column of this wave
     const bool vlane = g4 < 2;                  // lanes that load this wave's 16 v columns
 
-    const IT* qg = reinterpret_cast<const IT*>(a.q) + (size_t)row0 * sq + (size_t)h * DK + ch0;
-    const IT* kg = reinterpret_cast<const IT*>(a.k) + (size_t)row0 * sq + (size_t)h * DK + ch0;
-    const float* gg = a.g + (size_t)row0 * sq + (size_t)h * DK + ch0;
-    const IT* vg = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv + col0 +
-                   8 * (g4 & 1);
-    const IT* bg = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * H + h;
+    // per-chunk buffer resources start at the chunk's first token of this head; per-lane byte
+    // offsets select (token, channels); lanes with nothing to load use an out-of-range offset
+    const IT* qh = reinterpret_cast<const IT*>(a.q) + (size_t)row0 * sq + (size_t)h * DK;
+    const IT* kh = reinterpret_cast<const IT*>(a.k) + (size_t)row0 * sq + (size_t)h * DK;
+    const float* gh = a.g + (size_t)row0 * sq + (size_t)h * DK;
+    const IT* vh = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv + col0;
+    const IT* bh = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * H + h;
+    uint32_t off_qk[2], off_g[2], off_v[2], off_b[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t r = 16 * t + i16;
+        off_qk[t] = intra ? (uint32_t)((r * sq + ch0) * sizeof(IT)) : kOOB;
+        off_g[t] = intra ? (uint32_t)((r * sq + ch0) * 4) : kOOB;
+        off_v[t] = vlane ? (uint32_t)((r * sv + 8 * g4) * sizeof(IT)) : kOOB;
+        off_b[t] = (uint32_t)(r * H * sizeof(IT));
+    }
 
     // ---- state slice in accumulators: Sacc[ct][j] = S[16 ct + 4 g4 + j][col0 + i16]
     f32x4 Sacc[CT];
@@ -223,23 +261,24 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
 
     // ---- prefetch registers (one chunk ahead): token 16 t + i16 of tile t
     Raw8<F32IN> pq[2], pk[2], pv[2];
-    float4 pg[2][2];
-    IT pb[2];
+    uint4 pg[2][2];
+    uint32_t pb[2];
     auto prefetch = [&](int64_t c0) {
-        const int64_t rem = len - c0;
+        const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT)));
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT)));
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gh + (size_t)c0 * sq, nv * (uint32_t)(sq * 4));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)c0 * sv, nv * (uint32_t)(sv * sizeof(IT)));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bh + (size_t)c0 * H, nv * (uint32_t)(H * sizeof(IT)));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int r = 16 * t + i16;
-            const bool ok = r < rem;
-            const size_t off = (size_t)(c0 + r);
-            if (intra) {
-                pq[t].load(qg + off * sq, ok);
-                pk[t].load(kg + off * sq, ok);
-                pg[t][0] = ok ? reinterpret_cast<const float4*>(gg + off * sq)[0] : float4{0, 0, 0, 0};
-                pg[t][1] = ok ? reinterpret_cast<const float4*>(gg + off * sq)[1] : float4{0, 0, 0, 0};
-            }
-            pv[t].load(vg + off * sv, ok && vlane);
-            pb[t] = ok ? bg[off * H] : IT(0.f);
+            pq[t].load(rq, off_qk[t]);
+            pk[t].load(rk, off_qk[t]);
+            pg[t][0] = bload16(rg, off_g[t]);
+            pg[t][1] = bload16(rg, off_g[t] + 16);
+            pv[t].load(rv, off_v[t]);
+            if constexpr (F32IN) pb[t] = __builtin_amdgcn_raw_buffer_load_b32(rb, off_b[t], 0, 0);
+            else pb[t] = __builtin_amdgcn_raw_buffer_load_b16(rb, off_b[t], 0, 0);
         }
     };
 
@@ -255,18 +294,26 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         float bt[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int i = 0; i < (F32IN ? 2 : 1); ++i) {
+                pin(pq[t].p[i]);
+                pin(pk[t].p[i]);
+                pin(pv[t].p[i]);
+            }
+            pin(pg[t][0]);
+            pin(pg[t][1]);
+            pin(pb[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
             pq[t].to_f32(qv[t]);
             pk[t].to_f32(kv[t]);
             pv[t].to_f32(vv[t]);
-            bt[t] = static_cast<float>(pb[t]);
-            const float gl[8] = {pg[t][0].x, pg[t][0].y, pg[t][0].z, pg[t][0].w,
-                                 pg[t][1].x, pg[t][1].y, pg[t][1].z, pg[t][1].w};
+            if constexpr (F32IN) bt[t] = __builtin_bit_cast(float, pb[t]);
+            else bt[t] = __builtin_bit_cast(float, pb[t] << 16);
+            const float* gl = reinterpret_cast<const float*>(pg[t]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
-            if (!vlane) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vv[t][e] = 0.f;
-            }
         }
         // the raw registers are consumed: fetch the next chunk while this one is computed
         if (ci + 1 < nchunks) prefetch(c0 + kC);
@@ -366,8 +413,12 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                     for (int e = 0; e < 8; ++e) x[e] = Qs[1][e] * F0[e];
                     split8(x, hh, ll);
                 }
-                st<bf16x8>(bfp(Lay::o_Qt) + (16 * t + i16) * RB + ch0, hh);
-                st<bf16x8>(bfp(Lay::o_Qt) + kC * RB + (16 * t + i16) * RB + ch0, ll);
+                bf16* qd = bfp(Lay::o_Qt) + (16 * t + i16) * RB + 32 * wave;
+                const int p0 = pm(8 * g4), p1 = pm(8 * g4 + 4);
+                st<bf16x4>(qd + p0, bf16x4{hh[0], hh[1], hh[2], hh[3]});
+                st<bf16x4>(qd + p1, bf16x4{hh[4], hh[5], hh[6], hh[7]});
+                st<bf16x4>(qd + kC * RB + p0, bf16x4{ll[0], ll[1], ll[2], ll[3]});
+                st<bf16x4>(qd + kC * RB + p1, bf16x4{ll[4], ll[5], ll[6], ll[7]});
             }
             // K~ = K exp(G) and K_end = K exp(G_last - G), transposed through the identity:
             // the accumulator of lane (channel i16 of half hh, g4) holds tokens 16 t + 4 g4 + j.
@@ -391,7 +442,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                 for (int hh = 0; hh < 2; ++hh) {
                     Ktf[t][hh] = mma(th, Id[hh], zero4());
                     const f32x4 ke = mma(eh, Id[hh], zero4());
-                    bf16* dst = bfp(Lay::o_Ke) + (32 * wave + 16 * hh + i16) * TB + 16 * t + 4 * g4;
+                    bf16* dst = bfp(Lay::o_Ke) + (32 * wave + 16 * hh + i16) * TB + pm(16 * t + 4 * g4);
                     st<bf16x4>(dst, bf16x4{f2bf(ke[0]), f2bf(ke[1]), f2bf(ke[2]), f2bf(ke[3])});
                     if constexpr (kFull) {
                         Ktfl[t][hh] = mma(tl, Id[hh], zero4());
@@ -404,145 +455,146 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ======================= B: Gram reduction and the UT solve =========================
-        if (wave == 0) {
-            // A_kk tiles (masked, rows scaled by beta) -> fp32 row-major
+        // T = (I + A_kk)^-1 blockwise: T00, T11 by forward substitution (waves 0 and 1 at once),
+        // T10 = -T11 (A_kk[1,0] T00).  T_b = T Diag(beta) is stored with pm() on columns.
+        {
             const float* beta = f32p(Lay::o_beta);
+            bf16* Tb = bfp(Lay::o_Tb);
+            auto reduce = [&](int m) -> f32x4 {
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 3; m < 6; ++m) {
-                f32x4 s = zero4();
-#pragma unroll
-                for (int w = 0; w < NCB; ++w) s += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
-                const int ta = (m == 3) ? 0 : 1, tb = (m == 4) ? 1 : 0;
-                const int r = 16 * ta + i16;
-                const float br = beta[r];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = 16 * tb + 4 * g4 + j;
-                    s[j] = (i < r) ? s[j] * br : 0.f;
+                for (int w = 0; w < NCB; ++w) acc += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
+                return acc;
+            };
+            auto put_tb = [&](int r, int c, float v) {   // T_b[r][c] (one or two bf16 planes)
+                if constexpr (kFull) {
+                    bf16 hh, ll;
+                    split_bf16(v, hh, ll);
+                    Tb[r * TB + pm(c)] = hh;
+                    Tb[kC * TB + r * TB + pm(c)] = ll;
+                } else {
+                    Tb[r * TB + pm(c)] = f2bf(v);
                 }
-                st<f32x4>(f32p(Lay::o_Akk) + r * AF + 16 * tb + 4 * g4, s);
-            }
-            // inverses of the two unit-lower-triangular diagonal blocks, one lane per column:
-            // lanes 0-15 block 0, lanes 16-31 block 1
-            const int bb = (lane >> 4) & 1, c = i16;
-            if (lane < 32) {
-                float x[16];
-                const float* Ab = f32p(Lay::o_Akk) + (16 * bb) * AF + 16 * bb;
+            };
+            // Unit-lower-triangular inverse of one diagonal block: the reduced tile holds N[r][j]
+            // in lane (r, j / 4), element j % 4 (wave-uniform values read with v_readlane); lane
+            // c = i16 computes column c: x[r] = T[r][c].
+            // (The element is picked with explicit selects: this compiler reads element 0 for every
+            // j when v_readlane is fed N[j & 3] directly.)
+            auto diag_inverse = [&](f32x4 N, float* x) {
+                const float n0 = N[0], n1 = N[1], n2 = N[2], n3 = N[3];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
                     for (int j = 0; j < r; ++j) {
-                        if (j & 1) s1 += Ab[r * AF + j] * x[j];
-                        else s0 += Ab[r * AF + j] * x[j];
+                        const float src = (j & 3) == 0 ? n0 : (j & 3) == 1 ? n1 : (j & 3) == 2 ? n2 : n3;
+                        const float n = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                            __builtin_bit_cast(int, src), 16 * (j >> 2) + r));
+                        if (j & 1) s1 += n * x[j];
+                        else s0 += n * x[j];
                     }
-                    x[r] = (r == c) ? 1.f : ((r > c) ? -(s0 + s1) : 0.f);
+                    x[r] = (r == i16) ? 1.f : ((r > i16) ? -(s0 + s1) : 0.f);
                 }
-                const float bc = beta[16 * bb + c];
-                bf16* Tb = bfp(Lay::o_Tb) + (16 * bb) * TB + 16 * bb + c;
+            };
+            if (wave < 2) {
+                const int tb = wave;                    // diagonal block of this wave
+                f32x4 N = reduce(3 + tb);               // A_kk diagonal tile, rows scaled by beta
+                const float br = beta[16 * tb + i16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if constexpr (kFull) {
-                        bf16 hh, ll;
-                        split_bf16(x[r] * bc, hh, ll);
-                        Tb[r * TB] = hh;
-                        Tb[kC * TB + r * TB] = ll;
-                    } else {
-                        Tb[r * TB] = f2bf(x[r] * bc);
+                for (int j = 0; j < 4; ++j) N[j] = (4 * g4 + j < i16) ? N[j] * br : 0.f;
+                float x[16];
+                diag_inverse(N, x);
+                if (g4 == 0) {
+                    const float bc = beta[16 * tb + i16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) put_tb(16 * tb + r, 16 * tb + i16, x[r] * bc);
+                }
+                if (wave == 0) {
+                    // Y = A_kk[1,0] T00 (contraction 16: operand element e < 4 pairs with 4 g4 + e)
+                    f32x4 A10 = reduce(5);
+                    const float b1 = beta[16 + i16];
+                    float xa[8], xb[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        xa[e] = e < 4 ? A10[e] * b1 : 0.f;
+                        const float t0 = x[e & 3], t1 = x[4 + (e & 3)], t2 = x[8 + (e & 3)], t3 = x[12 + (e & 3)];
+                        xb[e] = e < 4 ? (g4 == 0 ? t0 : g4 == 1 ? t1 : g4 == 2 ? t2 : t3) : 0.f;
                     }
-                }
-                if (bb == 0) {
-#pragma unroll
-                    for (int r = 0; r < 16; r += 4)
-                        st<f32x4>(f32p(Lay::o_T0t) + c * 20 + r, f32x4{x[r], x[r + 1], x[r + 2], x[r + 3]});
+                    bf16x8 ah, al, bh, bl;
+                    split8(xa, ah, al);
+                    split8(xb, bh, bl);
+                    f32x4 Y = mma(ah, bh, zero4());
+                    Y = mma(al, bh, Y);
+                    Y = mma(ah, bl, Y);
+                    st<f32x4>(smem + Lay::o_Y + lane * 16, Y);   // lane (c, g4): Y[4 g4 + j][c]
                 } else {
+                    if (g4 == 0) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) f32p(Lay::o_T1)[r * 20 + c] = x[r];
+                        for (int r = 0; r < 16; ++r) f32p(Lay::o_T1)[r * 20 + i16] = x[r];
+                    }
+                    // upper-right block of T_b is zero
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int idx = lane * 4 + q;
+                        put_tb(idx >> 4, 16 + (idx & 15), 0.f);
+                    }
                 }
             } else {
-                // upper-right block of T_b is zero
-                const int lz = lane - 32;
+                // A_qk tiles (masked) -> split bf16 [row][pm(col)]
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int idx = lz * 8 + q, r = idx >> 4, cc = idx & 15;
-                    bfp(Lay::o_Tb)[r * TB + 16 + cc] = f2bf(0.f);
-                    if constexpr (kFull) bfp(Lay::o_Tb)[kC * TB + r * TB + 16 + cc] = f2bf(0.f);
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int m = (wave == 2) ? mm : 2;
+                    if (wave == 3 && mm == 1) break;
+                    const f32x4 acc = reduce(m);
+                    const int ta = (m == 0) ? 0 : 1, tb = (m == 1) ? 1 : 0;
+                    const int r = 16 * ta + i16;
+                    bf16x4 hv, lv;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        bf16 hh, ll;
+                        split_bf16((16 * tb + 4 * g4 + j <= r) ? acc[j] : 0.f, hh, ll);
+                        hv[j] = hh;
+                        lv[j] = ll;
+                    }
+                    bf16* ad = bfp(Lay::o_Aq) + r * TB + pm(16 * tb + 4 * g4);
+                    st<bf16x4>(ad, hv);
+                    st<bf16x4>(ad + kC * TB, lv);
+                }
+                if (wave == 3) {
+                    const bf16x4 z{f2bf(0.f), f2bf(0.f), f2bf(0.f), f2bf(0.f)};
+                    bf16* ad = bfp(Lay::o_Aq) + i16 * TB + pm(16 + 4 * g4);
+                    st<bf16x4>(ad, z);
+                    st<bf16x4>(ad + kC * TB, z);
                 }
             }
-            // X = A_kk[1,0] T00 and T10 = -T11 X with split MFMA products (contraction 16, the
-            // upper half of each 32-long step is zero)
-            {
+            __syncthreads();
+            if (wave == 1) {
+                // T10 = -T11 Y, contraction 16 (element e < 4 pairs with 4 g4 + e)
+                const f32x4 t11 = ld<f32x4>(f32p(Lay::o_T1) + i16 * 20 + 4 * g4);
+                const f32x4 Y = ld<f32x4>(smem + Lay::o_Y + lane * 16);
                 float xa[8], xb[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    xa[e] = g4 < 2 ? f32p(Lay::o_Akk)[(16 + i16) * AF + 8 * g4 + e] : 0.f;
-                    xb[e] = g4 < 2 ? f32p(Lay::o_T0t)[i16 * 20 + 8 * g4 + e] : 0.f;
+                    xa[e] = e < 4 ? t11[e] : 0.f;
+                    xb[e] = e < 4 ? Y[e] : 0.f;
                 }
                 bf16x8 ah, al, bh, bl;
                 split8(xa, ah, al);
                 split8(xb, bh, bl);
-                f32x4 X = mma(ah, bh, zero4());
-                X = mma(al, bh, X);
-                X = mma(ah, bl, X);
-                // X accumulator: lane (column c, g4) holds X[4 g4 + j][c]; as a B operand with
-                // contraction index 4 g4 + e (e < 4) it pairs with T11[r][4 g4 + e]
-                float x1[8], x2[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    x1[e] = e < 4 ? f32p(Lay::o_T1)[i16 * 20 + 4 * g4 + e] : 0.f;
-                    x2[e] = e < 4 ? X[e] : 0.f;
-                }
-                split8(x1, ah, al);
-                split8(x2, bh, bl);
                 f32x4 T10 = mma(ah, bh, zero4());
                 T10 = mma(al, bh, T10);
                 T10 = mma(ah, bl, T10);
                 const float bc = beta[i16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float v = -T10[j] * bc;
-                    bf16* Tb = bfp(Lay::o_Tb) + (16 + 4 * g4 + j) * TB + i16;
-                    if constexpr (kFull) {
-                        bf16 hh, ll;
-                        split_bf16(v, hh, ll);
-                        Tb[0] = hh;
-                        Tb[kC * TB] = ll;
-                    } else {
-                        Tb[0] = f2bf(v);
-                    }
-                }
-            }
-        } else {
-            // A_qk tiles (masked) -> split bf16 row-major; wave 1 also zeroes the upper block
-            const int m = wave - 1;
-            f32x4 s = zero4();
-#pragma unroll
-            for (int w = 0; w < NCB; ++w) s += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
-            const int ta = (m == 0) ? 0 : 1, tb = (m == 1) ? 1 : 0;
-            const int r = 16 * ta + i16;
-            bf16x4 hv, lv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 16 * tb + 4 * g4 + j;
-                bf16 hh, ll;
-                split_bf16((i <= r) ? s[j] : 0.f, hh, ll);
-                hv[j] = hh;
-                lv[j] = ll;
-            }
-            st<bf16x4>(bfp(Lay::o_Aq) + r * TB + 16 * tb + 4 * g4, hv);
-            st<bf16x4>(bfp(Lay::o_Aq) + kC * TB + r * TB + 16 * tb + 4 * g4, lv);
-            if (m == 0) {
-                const bf16x4 z{f2bf(0.f), f2bf(0.f), f2bf(0.f), f2bf(0.f)};
-                st<bf16x4>(bfp(Lay::o_Aq) + i16 * TB + 16 + 4 * g4, z);
-                st<bf16x4>(bfp(Lay::o_Aq) + kC * TB + i16 * TB + 16 + 4 * g4, z);
+                for (int j = 0; j < 4; ++j) put_tb(16 + 4 * g4 + j, i16, -T10[j] * bc);
             }
         }
         __syncthreads();
 
         // ======================= C: W (this wave's channels) and U (its value columns) =======
         auto ldTb = [&](int row, int plane) -> bf16x8 {   // T_b[row][4 g4 + e | 16 + 4 g4 + e]
-            const bf16* p = bfp(Lay::o_Tb) + plane * kC * TB + row * TB;
-            return cat44(ld<bf16x4>(p + 4 * g4), ld<bf16x4>(p + 16 + 4 * g4));
+            return ld<bf16x8>(bfp(Lay::o_Tb) + plane * kC * TB + row * TB + 8 * g4);
         };
         if (intra) {
 #pragma unroll
@@ -559,7 +611,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                         acc = mma(ka, ldTb(16 * tt + i16, 1), acc);
                     }
                     // acc[j] = W[16 tt + i16][32 wave + 16 hh + 4 g4 + j]
-                    bf16* Wd = bfp(Lay::o_W) + (16 * tt + i16) * RB + 32 * wave + 16 * hh + 4 * g4;
+                    bf16* Wd = bfp(Lay::o_W) + (16 * tt + i16) * RB + 32 * wave + pm(16 * hh + 4 * g4);
                     if constexpr (kFull) {
                         bf16x4 hv, lv;
 #pragma unroll
@@ -596,8 +648,8 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
             bf16x8 Sh[KS], Sl[KS];
 #pragma unroll
             for (int s = 0; s < KS; ++s) acc_pair_split(Sacc[2 * s], Sacc[2 * s + 1], Sh[s], Sl[s]);
-            auto ldA = [&](const bf16* rowp, int s) -> bf16x8 {   // same channel selection
-                return cat44(ld<bf16x4>(rowp + 32 * s + 4 * g4), ld<bf16x4>(rowp + 32 * s + 16 + 4 * g4));
+            auto ldA = [&](const bf16* rowp, int s) -> bf16x8 {   // same channel selection (pm)
+                return ld<bf16x8>(rowp + 32 * s + 8 * g4);
             };
             f32x4 Vt[2];
 #pragma unroll
@@ -631,9 +683,8 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                     acc = mma(qa, Sl[s], acc);
                 }
                 const bf16* Ar = bfp(Lay::o_Aq) + (16 * ta + i16) * TB;
-                const bf16x8 ah = cat44(ld<bf16x4>(Ar + 4 * g4), ld<bf16x4>(Ar + 16 + 4 * g4));
-                const bf16x8 al = cat44(ld<bf16x4>(Ar + kC * TB + 4 * g4),
-                                        ld<bf16x4>(Ar + kC * TB + 16 + 4 * g4));
+                const bf16x8 ah = ld<bf16x8>(Ar + 8 * g4);
+                const bf16x8 al = ld<bf16x8>(Ar + kC * TB + 8 * g4);
                 acc = mma(ah, Vh, acc);
                 acc = mma(al, Vh, acc);
                 acc = mma(ah, Vl, acc);
@@ -652,13 +703,13 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 const bf16* Kr = bfp(Lay::o_Ke) + (16 * ct + i16) * TB;
-                const bf16x8 ka = cat44(ld<bf16x4>(Kr + 4 * g4), ld<bf16x4>(Kr + 16 + 4 * g4));
+                const bf16x8 ka = ld<bf16x8>(Kr + 8 * g4);
                 const f32x4 gm = ld<f32x4>(gam + 16 * ct + 4 * g4);
                 f32x4 s = Sacc[ct] * gm;
                 s = mma(ka, Vh, s);
                 s = mma(ka, Vl, s);
                 if constexpr (kFull)
-                    s = mma(cat44(ld<bf16x4>(Kr + DK * TB + 4 * g4), ld<bf16x4>(Kr + DK * TB + 16 + 4 * g4)), Vh, s);
+                    s = mma(ld<bf16x8>(Kr + DK * TB + 8 * g4), Vh, s);
                 Sacc[ct] = s;
             }
         }
