@@ -16,6 +16,7 @@ times the C float64 reference token loop on a bounded sample of the same prefill
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,7 +40,7 @@ def prefill_alg_bytes(B, T, H, dk, dv, N, in_bytes=2, out_bytes=2):
     return th * per_th + 2 * N * H * dk * dv * 4
 
 
-def prefill_alg_flops(B, T, H, dk, dv, C=64):
+def prefill_alg_flops(B, T, H, dk, dv, C=32):
     """Algorithmic MFMA flops of the chunkwise form per launch, counting causal 16x16 tiles only
     (intra: A_kk, A_qk, T K~, T V; inter: W S, Q~ S, K_end^T V~, A_qk V~)."""
     th = B * T * H
@@ -52,6 +53,39 @@ def prefill_alg_flops(B, T, H, dk, dv, C=64):
 
 def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2):
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * in_bytes + dk * 4 + in_bytes + dv * out_bytes)
+
+
+def kernel_source_hash(name):
+    path = os.path.join(ROOT, "linear_attention_chunkwise_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, source_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE per dispatch, each scaled by what the counter reads for a plain device copy of
+    known size).  None when the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != kernel_source_hash(source_name):
+        return None
+    return (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024
+
+
+def calibrate_copy():
+    """A plain 1 GiB device-to-device copy (1 GiB read + 1 GiB written per launch), run under
+    rocprofv3 to find the scale of the FETCH_SIZE / WRITE_SIZE counters."""
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    x.fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": x.numel() * 4,
+                      "bytes_written": x.numel() * 4, "launches": 2}), flush=True)
 
 
 def cpu_baseline(x, units_wanted=64):
@@ -83,7 +117,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="profile helper: run only the prefill launch per step")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: every workload here fits "
                                    "one MI355X; --gpus must be 1"}))
@@ -152,9 +191,11 @@ def main():
                     "mfma_frac": pflops / (pre_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
         "decode": None if args.prefill_only else {
             "us": dec_ms * 1e3, "alg_bytes": dbytes, "GBps": dbytes / (dec_ms * 1e-3) / 1e9,
-            "frac_hbm": dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "frac_hbm": dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": measured_traffic("decode_kernel<128,128,bf16,bf16>", "kda_decode.hip")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("prefill_kernel<128,bf16,bf16>", "kda_prefill.hip"),
                      "kernel": "prefill_kernel<128,bf16,bf16 out>"},
     }
     if not args.no_cpu_baseline:
