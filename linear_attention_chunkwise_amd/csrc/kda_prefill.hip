@@ -37,11 +37,12 @@
 //     as the B operand of W S and Q~ S.
 //
 // Precision: bf16 MFMA with fp32 accumulation.  Operands whose rounding would dominate the error
-// are carried as hi + lo bf16 pairs (products hi*hi + lo*hi + hi*lo): the decayed Gram operands,
-// A_qk, V~ in both of its uses, and both operands of (Q * exp(G)) S, which dominates short
-// sequences entered with a large state.  T_b, K~, W, K_end and the state as the operand of W S
-// are single bf16; U and the state stay fp32.  Float32 inputs (kFull) carry every operand as a
-// pair.
+// are carried as hi + lo bf16 pairs (products hi*hi + lo*hi + hi*lo): the decayed operands of
+// A_qk, A_qk itself, V~ in both of its uses, and both operands of (Q * exp(G)) S, which dominates
+// short sequences entered with a large state.  A_kk, T_b, K~, W, K_end and the state as the
+// operand of W S are single bf16; U and the state stay fp32.  Float32 inputs (kFull) carry every
+// operand but A_kk's as a pair.  The scale on q is applied to the outputs (everything is linear
+// in q).
 #include <type_traits>
 
 #include "kda_device.h"
@@ -63,7 +64,8 @@ struct Layout {
     static constexpr int o_Gp = 0;                            // fp32 [NCB][6][64][4] partials
     static constexpr int o_Y = o_Gp + NCB * 6 * 64 * 16;      // fp32 [64][4] A_kk[1,0] T00
     static constexpr int o_T1 = o_Y + 64 * 16;                // fp32 [16][20] T11
-    static constexpr int o_Tb = o_T1 + 16 * 20 * 4;           // bf16 planes [C][TB]
+    static constexpr int o_N = o_T1 + 16 * 20 * 4;            // fp32 [2][16][20] A_kk diag blocks
+    static constexpr int o_Tb = o_N + 2 * 16 * 20 * 4;        // bf16 planes [C][TB]
     static constexpr int o_Aq = o_Tb + kNP * kC * TB * 2;     // bf16 hi, lo [C][TB]
     static constexpr int o_W = o_Aq + 2 * kC * TB * 2;        // bf16 planes [C][RB]
     static constexpr int o_Qt = o_W + kNP * kC * RB * 2;      // bf16 hi, lo [C][RB]
@@ -322,88 +324,89 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
             f32p(Lay::o_beta)[16 + i16] = bt[1];
         }
 
-        // V^T fragments for U = T_b V (this wave's 16 value columns): token-per-lane ->
-        // column-per-lane through a product with the identity.
-        f32x4 Vf[2], Vfl[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if constexpr (kFull) {
-                bf16x8 vh, vl;
-                split8(vv[t], vh, vl);
-                Vf[t] = mma(vh, Id[0], zero4());
-                Vfl[t] = mma(vl, Id[0], zero4());
-            } else {
-                Vf[t] = mma(to_bf16x8(vv[t]), Id[0], zero4());
-            }
-        }
-
-        f32x4 Ktf[2][2], Ktfl[2][2];   // K~^T fragments [tile][channel half]
+        // ---- A1: decay prefix, decayed operands and the partial Gram tiles (the only part the
+        // solve waits for); the rest of the operand work (A2) runs after the barrier, alongside
+        // the latency-bound solve.
+        float P[2][8], Pi[2][8], F0[8], F1[8];
+        float Qs[2][8], Kr[2][8], Kd[2][8], Kc[8];
+        bf16x8 Qh[2], Ql[2], Krh[2], Kdh[2], Kdl[2], Kch, Kcl;
         if (intra) {
             // in-tile prefix of the log2 decay (DPP scan across the 16 token lanes of a row)
-            float D[2][8];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     L[t][e] = row_scan16(L[t][e]);
-                    D[t][e] = __shfl(L[t][e], (lane & ~15) | 15, 64);   // tile total
-                }
-            float P[2][8], Pi[2][8], F0[8], F1[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                F0[e] = fast_exp2(D[0][e]);      // decay over tile 0
-                F1[e] = fast_exp2(D[1][e]);      // decay over tile 1
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
                     P[t][e] = fast_exp2(L[t][e]);        // tile start -> token, <= 1
                     Pi[t][e] = fast_exp2(-L[t][e]);      // token -> tile start, >= 1
                 }
-            }
-            if (i16 == 0) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) f32p(Lay::o_gam)[ch0 + e] = F0[e] * F1[e];
+            for (int e = 0; e < 8; ++e) {
+                F0[e] = __shfl(P[0][e], (lane & ~15) | 15, 64);   // decay over tile 0
+                F1[e] = __shfl(P[1][e], (lane & ~15) | 15, 64);   // decay over tile 1
             }
-            // decayed operands (fp32), then Gram partial products over this wave's channels
-            float Qs[2][8], Kr[2][8], Kd[2][8], Kc[8];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    Qs[t][e] = qv[t][e] * a.scale * P[t][e];
+                    Qs[t][e] = qv[t][e] * P[t][e];
                     Kr[t][e] = kv[t][e] * P[t][e];
                     Kd[t][e] = kv[t][e] * Pi[t][e];
                 }
 #pragma unroll
             for (int e = 0; e < 8; ++e) Kc[e] = Kd[0][e] * F0[e];   // tile 0 seen from tile 1
-            bf16x8 Qh[2], Ql[2], Krh[2], Krl[2], Kdh[2], Kdl[2], Kch, Kcl;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 split8(Qs[t], Qh[t], Ql[t]);
-                split8(Kr[t], Krh[t], Krl[t]);
+                Krh[t] = to_bf16x8(Kr[t]);
                 split8(Kd[t], Kdh[t], Kdl[t]);
             }
             split8(Kc, Kch, Kcl);
             // Gram tiles transposed (column side as the A operand): the accumulator of lane
             // (row r = i16, g4) holds A[r][16 b + 4 g4 + j].  m: 0 qk00, 1 qk11, 2 qk10,
-            // 3 kk00, 4 kk11, 5 kk10.
-            f32x4 G[6];
+            // 3 kk00, 4 kk11, 5 kk10.  A_qk with split operands (3 products); A_kk feeds only the
+            // triangular inverse, where single bf16 operands cost no measurable accuracy.
 #pragma unroll
             for (int m = 0; m < 6; ++m) {
                 const int ta = (m % 3 == 0) ? 0 : 1;
                 const bf16x8 ch = (m % 3 == 2) ? Kch : Kdh[ta];
                 const bf16x8 cl = (m % 3 == 2) ? Kcl : Kdl[ta];
-                const bf16x8 rh = (m < 3) ? Qh[ta] : Krh[ta];
-                const bf16x8 rl = (m < 3) ? Ql[ta] : Krl[ta];
-                f32x4 acc = mma(ch, rh, zero4());
-                acc = mma(cl, rh, acc);
-                acc = mma(ch, rl, acc);
-                G[m] = acc;
+                f32x4 acc;
+                if (m < 3) {
+                    acc = mma(ch, Qh[ta], zero4());
+                    acc = mma(cl, Qh[ta], acc);
+                    acc = mma(ch, Ql[ta], acc);
+                } else {
+                    acc = mma(ch, Krh[ta], zero4());
+                }
+                st<f32x4>(smem + Lay::o_Gp + ((wave * 6 + m) * 64 + lane) * 16, acc);
             }
-#pragma unroll
-            for (int m = 0; m < 6; ++m)
-                st<f32x4>(smem + Lay::o_Gp + ((wave * 6 + m) * 64 + lane) * 16, G[m]);
+        }
+        __syncthreads();
 
-            // Q~ = Q exp(G) (split, row-major [token][DK]); tile 1 carries the tile-0 decay
+        // ---- A2 (after the barrier): V^T fragments for U; Q~, K~^T, K_end^T for the rest
+        f32x4 Vf[2], Vfl[2];
+        f32x4 Ktf[2][2], Ktfl[2][2];   // K~^T fragments [tile][channel half]
+        auto finish_operands = [&]() {
+            // V (this wave's 16 value columns): token-per-lane -> column-per-lane through a
+            // product with the identity
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if constexpr (kFull) {
+                    bf16x8 vh, vl;
+                    split8(vv[t], vh, vl);
+                    Vf[t] = mma(vh, Id[0], zero4());
+                    Vfl[t] = mma(vl, Id[0], zero4());
+                } else {
+                    Vf[t] = mma(to_bf16x8(vv[t]), Id[0], zero4());
+                }
+            }
+            if (!intra) return;
+            if (i16 == 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f32p(Lay::o_gam)[ch0 + e] = F0[e] * F1[e];
+            }
+            // Q~ = Q exp(G) (split, [token][pm(channel)]); tile 1 carries the tile-0 decay
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 bf16x8 hh = Qh[t], ll = Ql[t];
@@ -451,8 +454,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                     }
                 }
             }
-        }
-        __syncthreads();
+        };
 
         // ======================= B: Gram reduction and the UT solve =========================
         // T = (I + A_kk)^-1 blockwise: T00, T11 by forward substitution (waves 0 and 1 at once),
@@ -476,35 +478,45 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                     Tb[r * TB + pm(c)] = f2bf(v);
                 }
             };
-            // Unit-lower-triangular inverse of one diagonal block: the reduced tile holds N[r][j]
-            // in lane (r, j / 4), element j % 4 (wave-uniform values read with v_readlane); lane
-            // c = i16 computes column c: x[r] = T[r][c].
-            // (The element is picked with explicit selects: this compiler reads element 0 for every
-            // j when v_readlane is fed N[j & 3] directly.)
-            auto diag_inverse = [&](f32x4 N, float* x) {
-                const float n0 = N[0], n1 = N[1], n2 = N[2], n3 = N[3];
+            // Column c = i16 of (I + N)^-1 for a strictly lower 16x16 N stored row-major in LDS
+            // (fp32, stride 20): forward substitution in blocks of 4 rows; each step needs the
+            // N rows only through 16-byte broadcast reads that do not depend on x.
+            auto diag_inverse = [&](const float* Nb, float* x) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float s0 = 0.f, s1 = 0.f;
+                for (int I = 0; I < 4; ++I) {
+                    float y[4];
 #pragma unroll
-                    for (int j = 0; j < r; ++j) {
-                        const float src = (j & 3) == 0 ? n0 : (j & 3) == 1 ? n1 : (j & 3) == 2 ? n2 : n3;
-                        const float n = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                            __builtin_bit_cast(int, src), 16 * (j >> 2) + r));
-                        if (j & 1) s1 += n * x[j];
-                        else s0 += n * x[j];
-                    }
-                    x[r] = (r == i16) ? 1.f : ((r > i16) ? -(s0 + s1) : 0.f);
+                    for (int i = 0; i < 4; ++i) y[i] = (4 * I + i == i16) ? 1.f : 0.f;
+#pragma unroll
+                    for (int K = 0; K < I; ++K)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const f32x4 n = ld<f32x4>(Nb + (4 * I + i) * 20 + 4 * K);
+                            y[i] -= (n[0] * x[4 * K] + n[1] * x[4 * K + 1]) +
+                                    (n[2] * x[4 * K + 2] + n[3] * x[4 * K + 3]);
+                        }
+                    const f32x4 n1 = ld<f32x4>(Nb + (4 * I + 1) * 20 + 4 * I);
+                    const f32x4 n2 = ld<f32x4>(Nb + (4 * I + 2) * 20 + 4 * I);
+                    const f32x4 n3 = ld<f32x4>(Nb + (4 * I + 3) * 20 + 4 * I);
+                    x[4 * I] = y[0];
+                    x[4 * I + 1] = y[1] - n1[0] * x[4 * I];
+                    x[4 * I + 2] = y[2] - n2[0] * x[4 * I] - n2[1] * x[4 * I + 1];
+                    x[4 * I + 3] = y[3] - n3[0] * x[4 * I] - n3[1] * x[4 * I + 1] - n3[2] * x[4 * I + 2];
                 }
             };
             if (wave < 2) {
                 const int tb = wave;                    // diagonal block of this wave
                 f32x4 N = reduce(3 + tb);               // A_kk diagonal tile, rows scaled by beta
+                f32x4 A10 = zero4();
+                if (wave == 0) A10 = reduce(5);
                 const float br = beta[16 * tb + i16];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) N[j] = (4 * g4 + j < i16) ? N[j] * br : 0.f;
+                float* Nb = f32p(Lay::o_N) + tb * 16 * 20;
+                st<f32x4>(Nb + i16 * 20 + 4 * g4, N);
                 float x[16];
-                diag_inverse(N, x);
+                diag_inverse(Nb, x);
+                finish_operands();
                 if (g4 == 0) {
                     const float bc = beta[16 * tb + i16];
 #pragma unroll
@@ -512,7 +524,6 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                 }
                 if (wave == 0) {
                     // Y = A_kk[1,0] T00 (contraction 16: operand element e < 4 pairs with 4 g4 + e)
-                    f32x4 A10 = reduce(5);
                     const float b1 = beta[16 + i16];
                     float xa[8], xb[8];
 #pragma unroll
@@ -567,6 +578,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                     st<bf16x4>(ad, z);
                     st<bf16x4>(ad + kC * TB, z);
                 }
+                finish_operands();
             }
             __syncthreads();
             if (wave == 1) {
@@ -693,8 +705,8 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                     const int r = 16 * ta + 4 * g4 + j;
                     if (r < nvalid) {
                         const size_t off = (size_t)(row0 + c0 + r) * sv + (size_t)h * a.dv + col0 + i16;
-                        if constexpr (OUT_F32) reinterpret_cast<float*>(a.o)[off] = acc[j];
-                        else reinterpret_cast<bf16*>(a.o)[off] = f2bf(acc[j]);
+                        if constexpr (OUT_F32) reinterpret_cast<float*>(a.o)[off] = a.scale * acc[j];
+                        else reinterpret_cast<bf16*>(a.o)[off] = f2bf(a.scale * acc[j]);
                     }
                 }
             }
