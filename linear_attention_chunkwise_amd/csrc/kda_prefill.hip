@@ -19,22 +19,26 @@
 // 16 tokens), <= 1 off it: both representable in bf16, so every causal tile, diagonal included,
 // is a dense MFMA product.
 //
-// Grid: one 256-thread workgroup (4 waves) per (sequence, head, 64-column slice of dv); the
-// slices of one head go to the same XCD so their reads of q, k, g share L2.  Per 32-token chunk:
-//   A (intra, channel-parallel): wave w owns key channels [32w, 32w + 32).  Each lane holds one
-//     token of a 16-token tile and 8 channels, loaded straight from HBM (prefetched one chunk
-//     ahead).  The in-tile decay prefix is a DPP scan across the 16 lanes of a row; the decayed
-//     operands are built in registers and feed MFMA directly: partial Gram tiles over the wave's
-//     channels (summed across waves through LDS), and "transposes" (product with an identity
-//     block) that turn token-per-lane fragments into channel-per-lane ones for K~, K_end and V.
-//   B (solve): waves 0 and 1 each reduce one diagonal 16x16 block of A_kk and invert I + A_kk
-//     there by forward substitution (one lane per column, the matrix entries broadcast from the
-//     reduced accumulators with v_readlane); the off-diagonal block of the inverse is assembled
-//     with split MFMA products; waves 2 and 3 reduce A_qk meanwhile.
-//   C: W^T = K~^T T_b^T for the wave's channels; U = T_b V for the wave's value columns.
-//   D (inter, column-parallel): wave w owns value columns [16w, 16w + 16) of the slice: its slice
-//     of the state (dk x 16, fp32) lives in MFMA accumulators for the whole sequence and doubles
-//     as the B operand of W S and Q~ S.
+// Grid: one 512-thread workgroup per (sequence, head, 64-column slice of dv); the slices of one
+// head go to the same XCD so their reads of q, k, g share L2.  Only the last of the steps below
+// depends on the state, so the workgroup is a two-stage pipeline: four producer waves prepare
+// chunk i while four consumer waves advance the state through chunk i - 1.  Each SIMD runs one
+// wave of each kind, so one kind's latency hides behind the other's issue.  Three workgroup
+// barriers per iteration; every hand-off buffer is written after the barrier that ends its last
+// read, so one copy of each suffices.
+//   interval 1  producers: inputs of chunk i (prefetched one chunk ahead), in-tile decay prefix
+//               (DPP scan over the 16 token lanes of a row), decayed operands in registers and the
+//               partial Gram tiles of A_kk and A_qk over each wave's 32 key channels.
+//               consumers: the inter-chunk step of chunk i - 1 on their 16 value columns: U,
+//               V~ = U - W S, O = Q~ S + A_qk V~ (written out), S <- Diag(gamma) S + K_end^T V~.
+//               The state slice (dk x 16, fp32) stays in MFMA accumulators for the whole sequence.
+//   interval 2  producers: Q~, K_end^T and the decay of the chunk to LDS; K~^T fragments kept in
+//               registers ("transposes" are products with an identity block).
+//               consumer 0: T_b from the reduced Gram tiles: both diagonal 16x16 blocks of
+//               (I + A_kk)^-1 at once by forward substitution (lanes 0-15 one block, 16-31 the
+//               other), the off-diagonal block with split MFMA products.
+//               consumers 1-3: one masked A_qk tile each.
+//   interval 3  producers: W = T_b K~ for their channels.
 //
 // Precision: bf16 MFMA with fp32 accumulation.  Operands whose rounding would dominate the error
 // are carried as hi + lo bf16 pairs (products hi*hi + lo*hi + hi*lo): the decayed operands of
@@ -52,7 +56,8 @@ namespace kda {
 
 constexpr int kC = 32;     // chunk length (two 16-token sub-tiles)
 constexpr int kDVT = 64;   // value columns per workgroup
-constexpr int kNT = 256;   // threads per workgroup (4 waves)
+constexpr int kNW = 4;     // producer waves = consumer waves
+constexpr int kNT = 128 * kNW;
 
 template <int DK, bool F32IN>
 struct Layout {
@@ -61,18 +66,17 @@ struct Layout {
     static constexpr int NCB = DK / 32;                       // 32-channel blocks = intra waves
     static constexpr int RB = DK + 8;                         // bf16 [token][DK] row stride
     static constexpr int TB = kC + 8;                         // bf16 [*][token] row stride
+    static constexpr int SB = 16 * 20 + 16;                   // fp32 16x16 block stride (banks +16)
     static constexpr int o_Gp = 0;                            // fp32 [NCB][6][64][4] partials
-    static constexpr int o_Y = o_Gp + NCB * 6 * 64 * 16;      // fp32 [64][4] A_kk[1,0] T00
-    static constexpr int o_T1 = o_Y + 64 * 16;                // fp32 [16][20] T11
-    static constexpr int o_N = o_T1 + 16 * 20 * 4;            // fp32 [2][16][20] A_kk diag blocks
-    static constexpr int o_Tb = o_N + 2 * 16 * 20 * 4;        // bf16 planes [C][TB]
+    static constexpr int o_N = o_Gp + NCB * 6 * 64 * 16;      // fp32 2 blocks [16][20]: A_kk diag
+    static constexpr int o_T = o_N + 2 * SB * 4;              // fp32 2 blocks [col][20]: T00, T11
+    static constexpr int o_Tb = o_T + 2 * SB * 4;             // bf16 planes [C][TB]
     static constexpr int o_Aq = o_Tb + kNP * kC * TB * 2;     // bf16 hi, lo [C][TB]
     static constexpr int o_W = o_Aq + 2 * kC * TB * 2;        // bf16 planes [C][RB]
     static constexpr int o_Qt = o_W + kNP * kC * RB * 2;      // bf16 hi, lo [C][RB]
     static constexpr int o_Ke = o_Qt + 2 * kC * RB * 2;       // bf16 planes [DK][TB] (K_end^T)
     static constexpr int o_gam = o_Ke + kNP * DK * TB * 2;    // fp32 [DK]
-    static constexpr int o_beta = o_gam + DK * 4;             // fp32 [C]
-    static constexpr int total = o_beta + kC * 4;
+    static constexpr int total = o_gam + DK * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -121,6 +125,23 @@ __device__ __forceinline__ void acc_pair_split(f32x4 a, f32x4 b, bf16x8& hi, bf1
     split8(x, hi, lo);
 }
 
+// hi*hi + lo*hi + hi*lo of two fp32 fragments whose contraction is 16 long (elements 0-3 from
+// `a` and `b`, the rest zero).
+__device__ __forceinline__ f32x4 mma16_split(const float* a, const float* b) {
+    float xa[8], xb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        xa[e] = e < 4 ? a[e] : 0.f;
+        xb[e] = e < 4 ? b[e] : 0.f;
+    }
+    bf16x8 ah, al, bh, bl;
+    split8(xa, ah, al);
+    split8(xb, bh, bl);
+    f32x4 r = mma(ah, bh, zero4());
+    r = mma(al, bh, r);
+    return mma(ah, bl, r);
+}
+
 // Storage order of every 32-long contraction index in LDS: position pm(c) puts the elements one
 // lane feeds to a 16x16x32 MFMA with the accumulator-compatible order (4 g4 + e for e < 4,
 // 16 + 4 g4 + e - 4 for e >= 4) next to each other, so an operand is one 16-byte read.
@@ -155,6 +176,10 @@ __device__ __forceinline__ void pin(uint4& u) {
 }
 __device__ __forceinline__ void pin(uint32_t& u) { asm volatile("" : "+v"(u)); }
 
+// Keeps the compiler from moving LDS accesses across this point; the hardware executes one
+// wave's LDS instructions in order, so lanes of a wave then see each other's earlier writes.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
 // Raw 8-element fragment of one token row as stored (bf16: one 16-byte piece; f32: two).
 template <bool F32IN>
 struct Raw8 {
@@ -162,6 +187,10 @@ struct Raw8 {
     __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
         for (int i = 0; i < (F32IN ? 2 : 1); ++i) p[i] = bload16(r, off + 16 * i);
+    }
+    __device__ void pin_all() {
+#pragma unroll
+        for (int i = 0; i < (F32IN ? 2 : 1); ++i) pin(p[i]);
     }
     __device__ void to_f32(float* x) const {
         if constexpr (F32IN) {
@@ -180,27 +209,8 @@ struct Raw8 {
     }
 };
 
-template <int DK, bool F32IN, bool OUT_F32>
-__global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
-    using Lay = Layout<DK, F32IN>;
-    using IT = typename std::conditional<F32IN, float, bf16>::type;
-    constexpr bool kFull = Lay::kFull;
-    constexpr int KS = DK / 32;          // 32-channel contraction steps
-    constexpr int CT = DK / 16;          // 16-channel tiles of the state
-    constexpr int NCB = Lay::NCB;
-    constexpr int RB = Lay::RB, TB = Lay::TB;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    auto bfp = [&](int off) { return reinterpret_cast<bf16*>(smem + off); };
-    auto f32p = [&](int off) { return reinterpret_cast<float*>(smem + off); };
-
-    const int nslices = a.dv / kDVT;
-    int unit, slice;
-    block_coords(nslices, unit, slice);
-    if (unit >= a.N * a.H) return;
-    const int n = unit / a.H, h = unit % a.H;
-
-    // Sequence bounds (clamped: malformed cu_seqlens never produce out-of-bounds accesses).
-    int64_t row0, len;
+// Sequence bounds (clamped: malformed cu_seqlens never produce out-of-bounds accesses).
+__device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t& row0, int64_t& len) {
     if (a.cu) {
         int64_t s0 = a.cu[n], s1 = a.cu[n + 1];
         s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
@@ -211,47 +221,34 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         row0 = (int64_t)n * a.T;
         len = a.T;
     }
-    const int H = a.H;
-    const size_t sq = (size_t)H * DK;          // token stride of q, k, g (elements)
-    const size_t sv = (size_t)H * a.dv;        // token stride of v, o
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+// ==================================== producer waves =========================================
+// Wave p owns key channels [32 p, 32 p + 32) (none when p >= DK / 32).  Per chunk: the decayed
+// operands, the partial Gram tiles (interval 1), Q~ / K_end^T / gamma (interval 2), W (interval 3).
+template <int DK, bool F32IN>
+__device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p, int lane,
+                                         int64_t row0, int64_t len, int h) {
+    using Lay = Layout<DK, F32IN>;
+    using IT = typename std::conditional<F32IN, float, bf16>::type;
+    constexpr bool kFull = Lay::kFull;
+    constexpr int RB = Lay::RB, TB = Lay::TB;
+    auto bfp = [&](int off) { return reinterpret_cast<bf16*>(smem + off); };
+    auto f32p = [&](int off) { return reinterpret_cast<float*>(smem + off); };
     const int i16 = lane & 15, g4 = lane >> 4;
-    const bool intra = wave < NCB;              // owns key channels [32 wave, 32 wave + 32)
-    const int ch0 = 32 * wave + 8 * g4;         // this lane's 8 key channels (intra waves)
-    const int col0 = slice * kDVT + 16 * wave;  // first value column of this wave
-    const bool vlane = g4 < 2;                  // lanes that load this wave's 16 v columns
+    const bool intra = p < Lay::NCB;
+    const int ch0 = 32 * p + 8 * g4;          // this lane's 8 key channels
+    const size_t sq = (size_t)a.H * DK;       // token stride of q, k, g (elements)
 
-    // per-chunk buffer resources start at the chunk's first token of this head; per-lane byte
-    // offsets select (token, channels); lanes with nothing to load use an out-of-range offset
     const IT* qh = reinterpret_cast<const IT*>(a.q) + (size_t)row0 * sq + (size_t)h * DK;
     const IT* kh = reinterpret_cast<const IT*>(a.k) + (size_t)row0 * sq + (size_t)h * DK;
     const float* gh = a.g + (size_t)row0 * sq + (size_t)h * DK;
-    const IT* vh = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv + col0;
-    const IT* bh = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * H + h;
-    uint32_t off_qk[2], off_g[2], off_v[2], off_b[2];
+    uint32_t off_qk[2], off_g[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const uint32_t r = 16 * t + i16;
-        off_qk[t] = intra ? (uint32_t)((r * sq + ch0) * sizeof(IT)) : kOOB;
-        off_g[t] = intra ? (uint32_t)((r * sq + ch0) * 4) : kOOB;
-        off_v[t] = vlane ? (uint32_t)((r * sv + 8 * g4) * sizeof(IT)) : kOOB;
-        off_b[t] = (uint32_t)(r * H * sizeof(IT));
-    }
-
-    // ---- state slice in accumulators: Sacc[ct][j] = S[16 ct + 4 g4 + j][col0 + i16]
-    f32x4 Sacc[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();
-    if (a.S0) {
-        const float* S0 = a.S0 + ((size_t)n * H + h) * DK * a.dv;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                Sacc[ct][j] = S0[(size_t)(16 * ct + 4 * g4 + j) * a.dv + col0 + i16];
+        off_qk[t] = (uint32_t)((r * sq + ch0) * sizeof(IT));
+        off_g[t] = (uint32_t)((r * sq + ch0) * 4);
     }
 
     // identity blocks: B operand selecting channel half hh of a 32-long contraction step
@@ -261,76 +258,54 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) Id[hh][e] = f2bf((8 * g4 + e == 16 * hh + i16) ? 1.f : 0.f);
 
-    // ---- prefetch registers (one chunk ahead): token 16 t + i16 of tile t
-    Raw8<F32IN> pq[2], pk[2], pv[2];
+    // prefetch registers (one chunk ahead): token 16 t + i16 of tile t
+    Raw8<F32IN> pq[2], pk[2];
     uint4 pg[2][2];
-    uint32_t pb[2];
     auto prefetch = [&](int64_t c0) {
         const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT)));
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT)));
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(gh + (size_t)c0 * sq, nv * (uint32_t)(sq * 4));
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)c0 * sv, nv * (uint32_t)(sv * sizeof(IT)));
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bh + (size_t)c0 * H, nv * (uint32_t)(H * sizeof(IT)));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             pq[t].load(rq, off_qk[t]);
             pk[t].load(rk, off_qk[t]);
             pg[t][0] = bload16(rg, off_g[t]);
             pg[t][1] = bload16(rg, off_g[t] + 16);
-            pv[t].load(rv, off_v[t]);
-            if constexpr (F32IN) pb[t] = __builtin_amdgcn_raw_buffer_load_b32(rb, off_b[t], 0, 0);
-            else pb[t] = __builtin_amdgcn_raw_buffer_load_b16(rb, off_b[t], 0, 0);
         }
     };
 
     const int64_t nchunks = (len + kC - 1) / kC;
-    if (nchunks > 0) prefetch(0);
+    if (intra && nchunks > 0) prefetch(0);
 
-    for (int64_t ci = 0; ci < nchunks; ++ci) {
-        const int64_t c0 = ci * kC;
-        const int nvalid = (int)((len - c0) < kC ? (len - c0) : kC);
+    for (int64_t it = 0; it <= nchunks; ++it) {
+        const bool work = intra && it < nchunks;   // wave-uniform
+        float F0[8], F1[8], Qs1[8], Kr[2][8], Kd1[8], Kc[8];
+        bf16x8 Qh0, Ql0;
+        f32x4 Ktf[2][2], Ktfl[2][2];   // K~^T fragments [tile][channel half]
 
-        // ======================= A: intra-chunk operands (channel-parallel) ==================
-        float qv[2][8], kv[2][8], vv[2][8], L[2][8];
-        float bt[2];
+        // ---- interval 1: decay prefix, decayed operands, partial Gram tiles
+        if (work) {
+            float qv[2][8], kv[2][8], L[2][8];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int i = 0; i < (F32IN ? 2 : 1); ++i) {
-                pin(pq[t].p[i]);
-                pin(pk[t].p[i]);
-                pin(pv[t].p[i]);
+            for (int t = 0; t < 2; ++t) {
+                pq[t].pin_all();
+                pk[t].pin_all();
+                pin(pg[t][0]);
+                pin(pg[t][1]);
             }
-            pin(pg[t][0]);
-            pin(pg[t][1]);
-            pin(pb[t]);
-        }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            pq[t].to_f32(qv[t]);
-            pk[t].to_f32(kv[t]);
-            pv[t].to_f32(vv[t]);
-            if constexpr (F32IN) bt[t] = __builtin_bit_cast(float, pb[t]);
-            else bt[t] = __builtin_bit_cast(float, pb[t] << 16);
-            const float* gl = reinterpret_cast<const float*>(pg[t]);
+            for (int t = 0; t < 2; ++t) {
+                pq[t].to_f32(qv[t]);
+                pk[t].to_f32(kv[t]);
+                const float* gl = reinterpret_cast<const float*>(pg[t]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
-        }
-        // the raw registers are consumed: fetch the next chunk while this one is computed
-        if (ci + 1 < nchunks) prefetch(c0 + kC);
-        if (wave == 0 && g4 == 0) {
-            f32p(Lay::o_beta)[i16] = bt[0];
-            f32p(Lay::o_beta)[16 + i16] = bt[1];
-        }
+                for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
+            }
+            // the raw registers are consumed: fetch the next chunk while this one is computed
+            if (it + 1 < nchunks) prefetch((it + 1) * kC);
 
-        // ---- A1: decay prefix, decayed operands and the partial Gram tiles (the only part the
-        // solve waits for); the rest of the operand work (A2) runs after the barrier, alongside
-        // the latency-bound solve.
-        float P[2][8], Pi[2][8], F0[8], F1[8];
-        float Qs[2][8], Kr[2][8], Kd[2][8], Kc[8];
-        bf16x8 Qh[2], Ql[2], Krh[2], Kdh[2], Kdl[2], Kch, Kcl;
-        if (intra) {
+            float P[2][8], Pi[2][8], Qs[2][8], Kd0[8];
             // in-tile prefix of the log2 decay (DPP scan across the 16 token lanes of a row)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -351,16 +326,21 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                 for (int e = 0; e < 8; ++e) {
                     Qs[t][e] = qv[t][e] * P[t][e];
                     Kr[t][e] = kv[t][e] * P[t][e];
-                    Kd[t][e] = kv[t][e] * Pi[t][e];
                 }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Kc[e] = Kd[0][e] * F0[e];   // tile 0 seen from tile 1
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                split8(Qs[t], Qh[t], Ql[t]);
-                Krh[t] = to_bf16x8(Kr[t]);
-                split8(Kd[t], Kdh[t], Kdl[t]);
+            for (int e = 0; e < 8; ++e) {
+                Kd0[e] = kv[0][e] * Pi[0][e];
+                Kd1[e] = kv[1][e] * Pi[1][e];
+                Kc[e] = Kd0[e] * F0[e];                  // tile 0 seen from tile 1
+                Qs1[e] = Qs[1][e];
             }
+            bf16x8 Qh1, Ql1, Krh[2], Kdh[2], Kdl[2], Kch, Kcl;
+            split8(Qs[0], Qh0, Ql0);
+            split8(Qs[1], Qh1, Ql1);
+            Krh[0] = to_bf16x8(Kr[0]);
+            Krh[1] = to_bf16x8(Kr[1]);
+            split8(Kd0, Kdh[0], Kdl[0]);
+            split8(Kd1, Kdh[1], Kdl[1]);
             split8(Kc, Kch, Kcl);
             // Gram tiles transposed (column side as the A operand): the accumulator of lane
             // (row r = i16, g4) holds A[r][16 b + 4 g4 + j].  m: 0 qk00, 1 qk11, 2 qk10,
@@ -373,35 +353,20 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                 const bf16x8 cl = (m % 3 == 2) ? Kcl : Kdl[ta];
                 f32x4 acc;
                 if (m < 3) {
-                    acc = mma(ch, Qh[ta], zero4());
-                    acc = mma(cl, Qh[ta], acc);
-                    acc = mma(ch, Ql[ta], acc);
+                    const bf16x8 rh = ta ? Qh1 : Qh0, rl = ta ? Ql1 : Ql0;
+                    acc = mma(ch, rh, zero4());
+                    acc = mma(cl, rh, acc);
+                    acc = mma(ch, rl, acc);
                 } else {
                     acc = mma(ch, Krh[ta], zero4());
                 }
-                st<f32x4>(smem + Lay::o_Gp + ((wave * 6 + m) * 64 + lane) * 16, acc);
+                st<f32x4>(smem + Lay::o_Gp + ((p * 6 + m) * 64 + lane) * 16, acc);
             }
         }
         __syncthreads();
 
-        // ---- A2 (after the barrier): V^T fragments for U; Q~, K~^T, K_end^T for the rest
-        f32x4 Vf[2], Vfl[2];
-        f32x4 Ktf[2][2], Ktfl[2][2];   // K~^T fragments [tile][channel half]
-        auto finish_operands = [&]() {
-            // V (this wave's 16 value columns): token-per-lane -> column-per-lane through a
-            // product with the identity
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                if constexpr (kFull) {
-                    bf16x8 vh, vl;
-                    split8(vv[t], vh, vl);
-                    Vf[t] = mma(vh, Id[0], zero4());
-                    Vfl[t] = mma(vl, Id[0], zero4());
-                } else {
-                    Vf[t] = mma(to_bf16x8(vv[t]), Id[0], zero4());
-                }
-            }
-            if (!intra) return;
+        // ---- interval 2: Q~, K_end^T, gamma to LDS; K~^T fragments in registers
+        if (work) {
             if (i16 == 0) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f32p(Lay::o_gam)[ch0 + e] = F0[e] * F1[e];
@@ -409,14 +374,14 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
             // Q~ = Q exp(G) (split, [token][pm(channel)]); tile 1 carries the tile-0 decay
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                bf16x8 hh = Qh[t], ll = Ql[t];
+                bf16x8 hh = Qh0, ll = Ql0;
                 if (t == 1) {
                     float x[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = Qs[1][e] * F0[e];
+                    for (int e = 0; e < 8; ++e) x[e] = Qs1[e] * F0[e];
                     split8(x, hh, ll);
                 }
-                bf16* qd = bfp(Lay::o_Qt) + (16 * t + i16) * RB + 32 * wave;
+                bf16* qd = bfp(Lay::o_Qt) + (16 * t + i16) * RB + 32 * p;
                 const int p0 = pm(8 * g4), p1 = pm(8 * g4 + 4);
                 st<bf16x4>(qd + p0, bf16x4{hh[0], hh[1], hh[2], hh[3]});
                 st<bf16x4>(qd + p1, bf16x4{hh[4], hh[5], hh[6], hh[7]});
@@ -431,7 +396,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     xt[e] = t ? Kr[1][e] * F0[e] : Kr[0][e];
-                    xe[e] = t ? Kd[1][e] * F1[e] : Kc[e] * F1[e];
+                    xe[e] = t ? Kd1[e] * F1[e] : Kc[e] * F1[e];
                 }
                 bf16x8 th, tl, eh, el;
                 if constexpr (kFull) {
@@ -445,7 +410,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                 for (int hh = 0; hh < 2; ++hh) {
                     Ktf[t][hh] = mma(th, Id[hh], zero4());
                     const f32x4 ke = mma(eh, Id[hh], zero4());
-                    bf16* dst = bfp(Lay::o_Ke) + (32 * wave + 16 * hh + i16) * TB + pm(16 * t + 4 * g4);
+                    bf16* dst = bfp(Lay::o_Ke) + (32 * p + 16 * hh + i16) * TB + pm(16 * t + 4 * g4);
                     st<bf16x4>(dst, bf16x4{f2bf(ke[0]), f2bf(ke[1]), f2bf(ke[2]), f2bf(ke[3])});
                     if constexpr (kFull) {
                         Ktfl[t][hh] = mma(tl, Id[hh], zero4());
@@ -454,161 +419,11 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                     }
                 }
             }
-        };
-
-        // ======================= B: Gram reduction and the UT solve =========================
-        // T = (I + A_kk)^-1 blockwise: T00, T11 by forward substitution (waves 0 and 1 at once),
-        // T10 = -T11 (A_kk[1,0] T00).  T_b = T Diag(beta) is stored with pm() on columns.
-        {
-            const float* beta = f32p(Lay::o_beta);
-            bf16* Tb = bfp(Lay::o_Tb);
-            auto reduce = [&](int m) -> f32x4 {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int w = 0; w < NCB; ++w) acc += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
-                return acc;
-            };
-            auto put_tb = [&](int r, int c, float v) {   // T_b[r][c] (one or two bf16 planes)
-                if constexpr (kFull) {
-                    bf16 hh, ll;
-                    split_bf16(v, hh, ll);
-                    Tb[r * TB + pm(c)] = hh;
-                    Tb[kC * TB + r * TB + pm(c)] = ll;
-                } else {
-                    Tb[r * TB + pm(c)] = f2bf(v);
-                }
-            };
-            // Column c = i16 of (I + N)^-1 for a strictly lower 16x16 N stored row-major in LDS
-            // (fp32, stride 20): forward substitution in blocks of 4 rows; each step needs the
-            // N rows only through 16-byte broadcast reads that do not depend on x.
-            auto diag_inverse = [&](const float* Nb, float* x) {
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    float y[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) y[i] = (4 * I + i == i16) ? 1.f : 0.f;
-#pragma unroll
-                    for (int K = 0; K < I; ++K)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const f32x4 n = ld<f32x4>(Nb + (4 * I + i) * 20 + 4 * K);
-                            y[i] -= (n[0] * x[4 * K] + n[1] * x[4 * K + 1]) +
-                                    (n[2] * x[4 * K + 2] + n[3] * x[4 * K + 3]);
-                        }
-                    const f32x4 n1 = ld<f32x4>(Nb + (4 * I + 1) * 20 + 4 * I);
-                    const f32x4 n2 = ld<f32x4>(Nb + (4 * I + 2) * 20 + 4 * I);
-                    const f32x4 n3 = ld<f32x4>(Nb + (4 * I + 3) * 20 + 4 * I);
-                    x[4 * I] = y[0];
-                    x[4 * I + 1] = y[1] - n1[0] * x[4 * I];
-                    x[4 * I + 2] = y[2] - n2[0] * x[4 * I] - n2[1] * x[4 * I + 1];
-                    x[4 * I + 3] = y[3] - n3[0] * x[4 * I] - n3[1] * x[4 * I + 1] - n3[2] * x[4 * I + 2];
-                }
-            };
-            if (wave < 2) {
-                const int tb = wave;                    // diagonal block of this wave
-                f32x4 N = reduce(3 + tb);               // A_kk diagonal tile, rows scaled by beta
-                f32x4 A10 = zero4();
-                if (wave == 0) A10 = reduce(5);
-                const float br = beta[16 * tb + i16];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) N[j] = (4 * g4 + j < i16) ? N[j] * br : 0.f;
-                float* Nb = f32p(Lay::o_N) + tb * 16 * 20;
-                st<f32x4>(Nb + i16 * 20 + 4 * g4, N);
-                float x[16];
-                diag_inverse(Nb, x);
-                finish_operands();
-                if (g4 == 0) {
-                    const float bc = beta[16 * tb + i16];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) put_tb(16 * tb + r, 16 * tb + i16, x[r] * bc);
-                }
-                if (wave == 0) {
-                    // Y = A_kk[1,0] T00 (contraction 16: operand element e < 4 pairs with 4 g4 + e)
-                    const float b1 = beta[16 + i16];
-                    float xa[8], xb[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        xa[e] = e < 4 ? A10[e] * b1 : 0.f;
-                        const float t0 = x[e & 3], t1 = x[4 + (e & 3)], t2 = x[8 + (e & 3)], t3 = x[12 + (e & 3)];
-                        xb[e] = e < 4 ? (g4 == 0 ? t0 : g4 == 1 ? t1 : g4 == 2 ? t2 : t3) : 0.f;
-                    }
-                    bf16x8 ah, al, bh, bl;
-                    split8(xa, ah, al);
-                    split8(xb, bh, bl);
-                    f32x4 Y = mma(ah, bh, zero4());
-                    Y = mma(al, bh, Y);
-                    Y = mma(ah, bl, Y);
-                    st<f32x4>(smem + Lay::o_Y + lane * 16, Y);   // lane (c, g4): Y[4 g4 + j][c]
-                } else {
-                    if (g4 == 0) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) f32p(Lay::o_T1)[r * 20 + i16] = x[r];
-                    }
-                    // upper-right block of T_b is zero
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int idx = lane * 4 + q;
-                        put_tb(idx >> 4, 16 + (idx & 15), 0.f);
-                    }
-                }
-            } else {
-                // A_qk tiles (masked) -> split bf16 [row][pm(col)]
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    const int m = (wave == 2) ? mm : 2;
-                    if (wave == 3 && mm == 1) break;
-                    const f32x4 acc = reduce(m);
-                    const int ta = (m == 0) ? 0 : 1, tb = (m == 1) ? 1 : 0;
-                    const int r = 16 * ta + i16;
-                    bf16x4 hv, lv;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        bf16 hh, ll;
-                        split_bf16((16 * tb + 4 * g4 + j <= r) ? acc[j] : 0.f, hh, ll);
-                        hv[j] = hh;
-                        lv[j] = ll;
-                    }
-                    bf16* ad = bfp(Lay::o_Aq) + r * TB + pm(16 * tb + 4 * g4);
-                    st<bf16x4>(ad, hv);
-                    st<bf16x4>(ad + kC * TB, lv);
-                }
-                if (wave == 3) {
-                    const bf16x4 z{f2bf(0.f), f2bf(0.f), f2bf(0.f), f2bf(0.f)};
-                    bf16* ad = bfp(Lay::o_Aq) + i16 * TB + pm(16 + 4 * g4);
-                    st<bf16x4>(ad, z);
-                    st<bf16x4>(ad + kC * TB, z);
-                }
-                finish_operands();
-            }
-            __syncthreads();
-            if (wave == 1) {
-                // T10 = -T11 Y, contraction 16 (element e < 4 pairs with 4 g4 + e)
-                const f32x4 t11 = ld<f32x4>(f32p(Lay::o_T1) + i16 * 20 + 4 * g4);
-                const f32x4 Y = ld<f32x4>(smem + Lay::o_Y + lane * 16);
-                float xa[8], xb[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xa[e] = e < 4 ? t11[e] : 0.f;
-                    xb[e] = e < 4 ? Y[e] : 0.f;
-                }
-                bf16x8 ah, al, bh, bl;
-                split8(xa, ah, al);
-                split8(xb, bh, bl);
-                f32x4 T10 = mma(ah, bh, zero4());
-                T10 = mma(al, bh, T10);
-                T10 = mma(ah, bl, T10);
-                const float bc = beta[i16];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put_tb(16 + 4 * g4 + j, i16, -T10[j] * bc);
-            }
         }
         __syncthreads();
 
-        // ======================= C: W (this wave's channels) and U (its value columns) =======
-        auto ldTb = [&](int row, int plane) -> bf16x8 {   // T_b[row][4 g4 + e | 16 + 4 g4 + e]
-            return ld<bf16x8>(bfp(Lay::o_Tb) + plane * kC * TB + row * TB + 8 * g4);
-        };
-        if (intra) {
+        // ---- interval 3: W = T_b K~ on this wave's channels, [token][pm(channel)]
+        if (work) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const bf16x8 ka = acc_pair(Ktf[0][hh], Ktf[1][hh]);
@@ -616,14 +431,15 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                 if constexpr (kFull) kal = acc_pair(Ktfl[0][hh], Ktfl[1][hh]);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    const bf16x8 tb = ldTb(16 * tt + i16, 0);
+                    const bf16* tbr = bfp(Lay::o_Tb) + (16 * tt + i16) * TB + 8 * g4;
+                    const bf16x8 tb = ld<bf16x8>(tbr);
                     f32x4 acc = mma(ka, tb, zero4());
                     if constexpr (kFull) {
                         acc = mma(kal, tb, acc);
-                        acc = mma(ka, ldTb(16 * tt + i16, 1), acc);
+                        acc = mma(ka, ld<bf16x8>(tbr + kC * TB), acc);
                     }
-                    // acc[j] = W[16 tt + i16][32 wave + 16 hh + 4 g4 + j]
-                    bf16* Wd = bfp(Lay::o_W) + (16 * tt + i16) * RB + 32 * wave + pm(16 * hh + 4 * g4);
+                    // acc[j] = W[16 tt + i16][32 p + 16 hh + 4 g4 + j]
+                    bf16* Wd = bfp(Lay::o_W) + (16 * tt + i16) * RB + 32 * p + pm(16 * hh + 4 * g4);
                     if constexpr (kFull) {
                         bf16x4 hv, lv;
 #pragma unroll
@@ -636,25 +452,156 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
                 }
             }
         }
-        f32x4 U[2];
-        {
-            const bf16x8 vb = acc_pair(Vf[0], Vf[1]);
-            bf16x8 vbl;
-            if constexpr (kFull) vbl = acc_pair(Vfl[0], Vfl[1]);
+        __syncthreads();
+    }
+}
+
+// ==================================== consumer waves =========================================
+// Wave 4 + cw owns value columns [16 cw, 16 cw + 16) of the slice and its dk x 16 state slice.
+// Interval 1 of iteration i: the inter-chunk step of chunk i - 1.  Interval 2: chunk i's T_b
+// (cw = 0) or one A_qk tile (cw = 1..3).
+template <int DK, bool F32IN, bool OUT_F32>
+__device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
+                                         int64_t row0, int64_t len, int n, int h, int slice) {
+    using Lay = Layout<DK, F32IN>;
+    using IT = typename std::conditional<F32IN, float, bf16>::type;
+    constexpr bool kFull = Lay::kFull;
+    constexpr int KS = DK / 32;          // 32-channel contraction steps
+    constexpr int CT = DK / 16;          // 16-channel tiles of the state
+    constexpr int NCB = Lay::NCB;
+    constexpr int RB = Lay::RB, TB = Lay::TB, SB = Lay::SB;
+    auto bfp = [&](int off) { return reinterpret_cast<bf16*>(smem + off); };
+    auto f32p = [&](int off) { return reinterpret_cast<float*>(smem + off); };
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int H = a.H;
+    const size_t sv = (size_t)H * a.dv;        // token stride of v, o
+    const int col0 = slice * kDVT + 16 * cw;   // first value column of this wave
+    const bool vlane = g4 < 2;                 // lanes that load this wave's 16 v columns
+
+    const IT* vh = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv + col0;
+    const IT* bh = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * H + h;
+    uint32_t off_v[2], off_b[2];
 #pragma unroll
-            for (int ta = 0; ta < 2; ++ta) {
-                const bf16x8 tr = ldTb(16 * ta + i16, 0);
-                U[ta] = mma(tr, vb, zero4());
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t r = 16 * t + i16;
+        off_v[t] = vlane ? (uint32_t)((r * sv + 8 * g4) * sizeof(IT)) : kOOB;
+        off_b[t] = (uint32_t)(r * H * sizeof(IT));
+    }
+
+    // ---- state slice in accumulators: Sacc[ct][j] = S[16 ct + 4 g4 + j][col0 + i16]
+    f32x4 Sacc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();
+    if (a.S0) {
+        const float* S0 = a.S0 + ((size_t)n * H + h) * DK * a.dv;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                Sacc[ct][j] = S0[(size_t)(16 * ct + 4 * g4 + j) * a.dv + col0 + i16];
+    }
+
+    // the upper-right 16x16 blocks of T_b and A_qk are zero for every chunk
+    if (cw == 1) {
+        const bf16x4 z{f2bf(0.f), f2bf(0.f), f2bf(0.f), f2bf(0.f)};
+        bf16* ad = bfp(Lay::o_Aq) + i16 * TB + pm(16 + 4 * g4);
+        st<bf16x4>(ad, z);
+        st<bf16x4>(ad + kC * TB, z);
+        bf16* td = bfp(Lay::o_Tb) + i16 * TB + pm(16 + 4 * g4);
+#pragma unroll
+        for (int pl = 0; pl < Lay::kNP; ++pl) st<bf16x4>(td + pl * kC * TB, z);
+    }
+
+    bf16x8 Id0;   // identity block: B operand selecting columns 0..15 of a 32-long step
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Id0[e] = f2bf((8 * g4 + e == i16) ? 1.f : 0.f);
+
+    Raw8<F32IN> pv[2];
+    uint32_t pb[2];
+    auto prefetch_v = [&](int64_t c0) {
+        const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)c0 * sv, nv * (uint32_t)(sv * sizeof(IT)));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pv[t].load(rv, off_v[t]);
+    };
+    auto prefetch_b = [&](int64_t c0) {
+        const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bh + (size_t)c0 * H, nv * (uint32_t)(H * sizeof(IT)));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if constexpr (F32IN) pb[t] = __builtin_amdgcn_raw_buffer_load_b32(rb, off_b[t], 0, 0);
+            else pb[t] = __builtin_amdgcn_raw_buffer_load_b16(rb, off_b[t], 0, 0);
+        }
+    };
+    auto reduce = [&](int m) -> f32x4 {   // sum of the producers' partial Gram tiles
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int w = 0; w < NCB; ++w) acc += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
+        return acc;
+    };
+    auto put_tb = [&](int r, int c, float v) {   // T_b[r][c] (one or two bf16 planes)
+        bf16* Tb = bfp(Lay::o_Tb);
+        if constexpr (kFull) {
+            bf16 hh, ll;
+            split_bf16(v, hh, ll);
+            Tb[r * TB + pm(c)] = hh;
+            Tb[kC * TB + r * TB + pm(c)] = ll;
+        } else {
+            Tb[r * TB + pm(c)] = f2bf(v);
+        }
+    };
+
+    const int64_t nchunks = (len + kC - 1) / kC;
+    if (nchunks > 0) {
+        prefetch_v(0);
+        if (cw == 0) prefetch_b(0);
+    }
+
+    for (int64_t it = 0; it <= nchunks; ++it) {
+        // ---- interval 1: inter-chunk step of chunk it - 1 on this wave's 16 state columns
+        if (it > 0) {
+            const int64_t c0 = (it - 1) * kC;
+            const int nvalid = (int)((len - c0) < kC ? (len - c0) : kC);
+            float vv[2][8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) pv[t].pin_all();
+#pragma unroll
+            for (int t = 0; t < 2; ++t) pv[t].to_f32(vv[t]);
+            if (it < nchunks) prefetch_v(it * kC);
+
+            // V: token-per-lane -> column-per-lane through a product with the identity; the
+            // accumulator of lane (column i16, g4) holds tokens 16 t + 4 g4 + j
+            f32x4 Vf[2], Vfl[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
                 if constexpr (kFull) {
-                    U[ta] = mma(ldTb(16 * ta + i16, 1), vb, U[ta]);
-                    U[ta] = mma(tr, vbl, U[ta]);
+                    bf16x8 vh, vl;
+                    split8(vv[t], vh, vl);
+                    Vf[t] = mma(vh, Id0, zero4());
+                    Vfl[t] = mma(vl, Id0, zero4());
+                } else {
+                    Vf[t] = mma(to_bf16x8(vv[t]), Id0, zero4());
                 }
             }
-        }
-        __syncthreads();
-
-        // ======================= D: inter-chunk part on this wave's 16 state columns =========
-        {
+            // U = T_b V
+            auto ldTb = [&](int row, int plane) -> bf16x8 {   // T_b[row][4 g4 + e | 16 + 4 g4 + e]
+                return ld<bf16x8>(bfp(Lay::o_Tb) + plane * kC * TB + row * TB + 8 * g4);
+            };
+            f32x4 U[2];
+            {
+                const bf16x8 vb = acc_pair(Vf[0], Vf[1]);
+                bf16x8 vbl;
+                if constexpr (kFull) vbl = acc_pair(Vfl[0], Vfl[1]);
+#pragma unroll
+                for (int ta = 0; ta < 2; ++ta) {
+                    const bf16x8 tr = ldTb(16 * ta + i16, 0);
+                    U[ta] = mma(tr, vb, zero4());
+                    if constexpr (kFull) {
+                        U[ta] = mma(ldTb(16 * ta + i16, 1), vb, U[ta]);
+                        U[ta] = mma(tr, vbl, U[ta]);
+                    }
+                }
+            }
             // state as B operand: contraction index (32-channel step s, g4, e) ->
             // channel 32 s + 4 g4 + e (e < 4), 32 s + 16 + 4 g4 + (e - 4) (e >= 4)
             bf16x8 Sh[KS], Sl[KS];
@@ -726,6 +673,106 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
             }
         }
         __syncthreads();
+
+        // ---- interval 2: the UT solve (cw = 0) and the A_qk tiles (cw = 1..3) of chunk it
+        if (it < nchunks) {
+            if (cw == 0) {
+                float bt[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    pin(pb[t]);
+                    if constexpr (F32IN) bt[t] = __builtin_bit_cast(float, pb[t]);
+                    else bt[t] = __builtin_bit_cast(float, pb[t] << 16);
+                }
+                if (it + 1 < nchunks) prefetch_b((it + 1) * kC);
+                // A_kk diagonal blocks (rows scaled by beta, strictly lower part) to LDS
+                f32x4 N0 = reduce(3), N1 = reduce(4);
+                const f32x4 A10 = reduce(5);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool low = 4 * g4 + j < i16;
+                    N0[j] = low ? N0[j] * bt[0] : 0.f;
+                    N1[j] = low ? N1[j] * bt[1] : 0.f;
+                }
+                float* Nb = f32p(Lay::o_N);
+                st<f32x4>(Nb + i16 * 20 + 4 * g4, N0);
+                st<f32x4>(Nb + SB + i16 * 20 + 4 * g4, N1);
+                wave_lds_order();
+                // column c = i16 of (I + N_bb)^-1, bb = g4 & 1, by forward substitution in blocks
+                // of 4 rows; each step reads N rows through 16-byte broadcast loads that do not
+                // depend on x (the two blocks sit 16 banks apart)
+                const int bb = g4 & 1;
+                const float* Nm = Nb + bb * SB;
+                float x[16];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    float y[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[i] = (4 * I + i == i16) ? 1.f : 0.f;
+#pragma unroll
+                    for (int K = 0; K < I; ++K)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const f32x4 nr = ld<f32x4>(Nm + (4 * I + i) * 20 + 4 * K);
+                            y[i] -= (nr[0] * x[4 * K] + nr[1] * x[4 * K + 1]) +
+                                    (nr[2] * x[4 * K + 2] + nr[3] * x[4 * K + 3]);
+                        }
+                    const f32x4 n1 = ld<f32x4>(Nm + (4 * I + 1) * 20 + 4 * I);
+                    const f32x4 n2 = ld<f32x4>(Nm + (4 * I + 2) * 20 + 4 * I);
+                    const f32x4 n3 = ld<f32x4>(Nm + (4 * I + 3) * 20 + 4 * I);
+                    x[4 * I] = y[0];
+                    x[4 * I + 1] = y[1] - n1[0] * x[4 * I];
+                    x[4 * I + 2] = y[2] - n2[0] * x[4 * I] - n2[1] * x[4 * I + 1];
+                    x[4 * I + 3] = y[3] - n3[0] * x[4 * I] - n3[1] * x[4 * I + 1] - n3[2] * x[4 * I + 2];
+                }
+                // diagonal blocks of T_b, and T_bb column-major (fp32) for the off-diagonal block
+                if (g4 < 2) {
+                    const float bc = bt[bb];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) put_tb(16 * bb + r, 16 * bb + i16, x[r] * bc);
+                    float* Tt = f32p(Lay::o_T) + bb * SB + i16 * 20;
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        st<f32x4>(Tt + 4 * r4, f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]});
+                }
+                wave_lds_order();
+                // Y = A_kk[1,0] T00 (rows scaled by beta), then T10 = -T11 Y; contraction 16:
+                // operand element e < 4 pairs with index 4 g4 + e
+                float ya[4], yb[4], za[4];
+                const f32x4 t00 = ld<f32x4>(f32p(Lay::o_T) + i16 * 20 + 4 * g4);   // T00[4 g4 + e][i16]
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ya[e] = A10[e] * bt[1];
+                    yb[e] = t00[e];
+                    za[e] = f32p(Lay::o_T)[SB + (4 * g4 + e) * 20 + i16];               // T11[i16][4 g4 + e]
+                }
+                const f32x4 Y = mma16_split(ya, yb);   // lane (c, g4): Y[4 g4 + j][c]
+                const float yv[4] = {Y[0], Y[1], Y[2], Y[3]};
+                const f32x4 T10 = mma16_split(za, yv);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put_tb(16 + 4 * g4 + j, i16, -T10[j] * bt[0]);
+            } else {
+                // A_qk tile m (masked) -> split bf16 [row][pm(col)]
+                const int m = cw - 1;   // 0: rows 0-15 x cols 0-15, 1: 16-31 x 16-31, 2: 16-31 x 0-15
+                const f32x4 acc = reduce(m);
+                const int ta = (m == 0) ? 0 : 1, tb = (m == 1) ? 1 : 0;
+                const int r = 16 * ta + i16;
+                bf16x4 hv, lv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    bf16 hh, ll;
+                    split_bf16((16 * tb + 4 * g4 + j <= r) ? acc[j] : 0.f, hh, ll);
+                    hv[j] = hh;
+                    lv[j] = ll;
+                }
+                bf16* ad = bfp(Lay::o_Aq) + r * TB + pm(16 * tb + 4 * g4);
+                st<bf16x4>(ad, hv);
+                st<bf16x4>(ad + kC * TB, lv);
+            }
+        }
+        __syncthreads();
+        // ---- interval 3: nothing here (the producers form W)
+        __syncthreads();
     }
 
     if (a.ST) {
@@ -736,6 +783,23 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
             for (int j = 0; j < 4; ++j)
                 ST[(size_t)(16 * ct + 4 * g4 + j) * a.dv + col0 + i16] = Sacc[ct][j];
     }
+}
+
+// Both roles run the same number of iterations (chunks + 1) with three barriers each.
+template <int DK, bool F32IN, bool OUT_F32>
+__global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int nslices = a.dv / kDVT;
+    int unit, slice;
+    block_coords(nslices, unit, slice);
+    if (unit >= a.N * a.H) return;
+    const int n = unit / a.H, h = unit % a.H;
+    int64_t row0, len;
+    seq_bounds(a, n, row0, len);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
+    if (wave < kNW) producer<DK, F32IN>(a, smem, wave, lane, row0, len, h);
+    else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice);
 }
 
 template <int DK, bool F32IN, bool OUT_F32>
