@@ -76,7 +76,8 @@ struct Layout {
     static constexpr int o_Qt = o_W + kNP * kC * RB * 2;      // bf16 hi, lo [C][RB]
     static constexpr int o_Ke = o_Qt + 2 * kC * RB * 2;       // bf16 planes [DK][TB] (K_end^T)
     static constexpr int o_gam = o_Ke + kNP * DK * TB * 2;    // fp32 [DK]
-    static constexpr int total = o_gam + DK * 4;
+    static constexpr int o_beta = o_gam + DK * 4;             // fp32 [C]
+    static constexpr int total = o_beta + kC * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -97,32 +98,52 @@ __device__ __forceinline__ float row_scan16(float x) {   // inclusive prefix sum
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = f2bf(x[e]);
-    return r;
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, as a packed word.
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
+    const uint4 w{cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3]), cvt_pk(x[4], x[5]), cvt_pk(x[6], x[7])};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// x = hi + lo, hi = bf16(x), lo = bf16(x - hi): pairs are converted together and hi is widened
+// back with a shift or a mask, three operations per element.
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        bf16 h, l;
-        split_bf16(x[e], h, l);
-        hi[e] = h;
-        lo[e] = l;
+    for (int i = 0; i < 4; ++i) {
+        h[i] = cvt_pk(x[2 * i], x[2 * i + 1]);
+        const float h0 = __builtin_bit_cast(float, h[i] << 16);
+        const float h1 = __builtin_bit_cast(float, h[i] & 0xffff0000u);
+        l[i] = cvt_pk(x[2 * i] - h0, x[2 * i + 1] - h1);
     }
+    hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
 }
 
 // Fragment of an f32x4 accumulator pair as an operand with the accumulator-compatible contraction
 // order (element e < 4 from `a`, e >= 4 from `b`).
 __device__ __forceinline__ bf16x8 acc_pair(f32x4 a, f32x4 b) {
-    return bf16x8{f2bf(a[0]), f2bf(a[1]), f2bf(a[2]), f2bf(a[3]),
-                  f2bf(b[0]), f2bf(b[1]), f2bf(b[2]), f2bf(b[3])};
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return to_bf16x8(x);
 }
 __device__ __forceinline__ void acc_pair_split(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
-    float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     split8(x, hi, lo);
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 a) {
+    return __builtin_bit_cast(bf16x4, uint2{cvt_pk(a[0], a[1]), cvt_pk(a[2], a[3])});
+}
+__device__ __forceinline__ void split4(f32x4 a, bf16x4& hi, bf16x4& lo) {
+    const float x[8] = {a[0], a[1], a[2], a[3], 0.f, 0.f, 0.f, 0.f};
+    bf16x8 h, l;
+    split8(x, h, l);
+    hi = bf16x4{h[0], h[1], h[2], h[3]};
+    lo = bf16x4{l[0], l[1], l[2], l[3]};
 }
 
 // hi*hi + lo*hi + hi*lo of two fp32 fragments whose contraction is 16 long (elements 0-3 from
@@ -175,6 +196,10 @@ __device__ __forceinline__ void pin(uint4& u) {
     asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
 }
 __device__ __forceinline__ void pin(uint32_t& u) { asm volatile("" : "+v"(u)); }
+// Forces loaded values to be complete here: the loads of a batch are then issued together
+// instead of each right before its first use.
+__device__ __forceinline__ void pin(f32x4& u) { asm volatile("" : "+v"(u)); }
+__device__ __forceinline__ void pin(bf16x8& u) { asm volatile("" : "+v"(u)); }
 
 // Keeps the compiler from moving LDS accesses across this point; the hardware executes one
 // wave's LDS instructions in order, so lanes of a wave then see each other's earlier writes.
@@ -243,12 +268,14 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
     const IT* qh = reinterpret_cast<const IT*>(a.q) + (size_t)row0 * sq + (size_t)h * DK;
     const IT* kh = reinterpret_cast<const IT*>(a.k) + (size_t)row0 * sq + (size_t)h * DK;
     const float* gh = a.g + (size_t)row0 * sq + (size_t)h * DK;
-    uint32_t off_qk[2], off_g[2];
+    const IT* bh = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * a.H + h;
+    uint32_t off_qk[2], off_g[2], off_b[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const uint32_t r = 16 * t + i16;
         off_qk[t] = (uint32_t)((r * sq + ch0) * sizeof(IT));
         off_g[t] = (uint32_t)((r * sq + ch0) * 4);
+        off_b[t] = (p == 0 && g4 == 0) ? (uint32_t)(r * a.H * sizeof(IT)) : kOOB;   // beta: wave 0
     }
 
     // identity blocks: B operand selecting channel half hh of a 32-long contraction step
@@ -261,17 +288,23 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
     // prefetch registers (one chunk ahead): token 16 t + i16 of tile t
     Raw8<F32IN> pq[2], pk[2];
     uint4 pg[2][2];
+    uint32_t pb[2];
     auto prefetch = [&](int64_t c0) {
         const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT)));
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT)));
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(gh + (size_t)c0 * sq, nv * (uint32_t)(sq * 4));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bh + (size_t)c0 * a.H, nv * (uint32_t)(a.H * sizeof(IT)));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             pq[t].load(rq, off_qk[t]);
             pk[t].load(rk, off_qk[t]);
             pg[t][0] = bload16(rg, off_g[t]);
             pg[t][1] = bload16(rg, off_g[t] + 16);
+            if (p == 0) {
+                if constexpr (F32IN) pb[t] = __builtin_amdgcn_raw_buffer_load_b32(rb, off_b[t], 0, 0);
+                else pb[t] = __builtin_amdgcn_raw_buffer_load_b16(rb, off_b[t], 0, 0);
+            }
         }
     };
 
@@ -301,6 +334,15 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                 const float* gl = reinterpret_cast<const float*>(pg[t]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
+            }
+            if (p == 0) {   // beta of the chunk for the solve
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    pin(pb[t]);
+                    if (g4 == 0)
+                        f32p(Lay::o_beta)[16 * t + i16] =
+                            F32IN ? __builtin_bit_cast(float, pb[t]) : __builtin_bit_cast(float, pb[t] << 16);
+                }
             }
             // the raw registers are consumed: fetch the next chunk while this one is computed
             if (it + 1 < nchunks) prefetch((it + 1) * kC);
@@ -411,11 +453,11 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                     Ktf[t][hh] = mma(th, Id[hh], zero4());
                     const f32x4 ke = mma(eh, Id[hh], zero4());
                     bf16* dst = bfp(Lay::o_Ke) + (32 * p + 16 * hh + i16) * TB + pm(16 * t + 4 * g4);
-                    st<bf16x4>(dst, bf16x4{f2bf(ke[0]), f2bf(ke[1]), f2bf(ke[2]), f2bf(ke[3])});
+                    st<bf16x4>(dst, to_bf16x4(ke));
                     if constexpr (kFull) {
                         Ktfl[t][hh] = mma(tl, Id[hh], zero4());
                         const f32x4 kel = mma(el, Id[hh], zero4());
-                        st<bf16x4>(dst + DK * TB, bf16x4{f2bf(kel[0]), f2bf(kel[1]), f2bf(kel[2]), f2bf(kel[3])});
+                        st<bf16x4>(dst + DK * TB, to_bf16x4(kel));
                     }
                 }
             }
@@ -442,12 +484,11 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                     bf16* Wd = bfp(Lay::o_W) + (16 * tt + i16) * RB + 32 * p + pm(16 * hh + 4 * g4);
                     if constexpr (kFull) {
                         bf16x4 hv, lv;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) { bf16 h1, l1; split_bf16(acc[j], h1, l1); hv[j] = h1; lv[j] = l1; }
+                        split4(acc, hv, lv);
                         st<bf16x4>(Wd, hv);
                         st<bf16x4>(Wd + kC * RB, lv);
                     } else {
-                        st<bf16x4>(Wd, bf16x4{f2bf(acc[0]), f2bf(acc[1]), f2bf(acc[2]), f2bf(acc[3])});
+                        st<bf16x4>(Wd, to_bf16x4(acc));
                     }
                 }
             }
@@ -479,13 +520,16 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     const bool vlane = g4 < 2;                 // lanes that load this wave's 16 v columns
 
     const IT* vh = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv + col0;
-    const IT* bh = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * H + h;
-    uint32_t off_v[2], off_b[2];
+    using OT = typename std::conditional<OUT_F32, float, bf16>::type;
+    OT* ob = reinterpret_cast<OT*>(a.o) + (size_t)row0 * sv + (size_t)h * a.dv + col0;
+    uint32_t off_v[2], off_o[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const uint32_t r = 16 * t + i16;
         off_v[t] = vlane ? (uint32_t)((r * sv + 8 * g4) * sizeof(IT)) : kOOB;
-        off_b[t] = (uint32_t)(r * H * sizeof(IT));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)   // output row 16 t + 4 g4 + j, column i16
+            off_o[t][j] = (uint32_t)(((16 * t + 4 * g4 + j) * sv + i16) * sizeof(OT));
     }
 
     // ---- state slice in accumulators: Sacc[ct][j] = S[16 ct + 4 g4 + j][col0 + i16]
@@ -517,26 +561,16 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     for (int e = 0; e < 8; ++e) Id0[e] = f2bf((8 * g4 + e == i16) ? 1.f : 0.f);
 
     Raw8<F32IN> pv[2];
-    uint32_t pb[2];
     auto prefetch_v = [&](int64_t c0) {
         const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)c0 * sv, nv * (uint32_t)(sv * sizeof(IT)));
 #pragma unroll
         for (int t = 0; t < 2; ++t) pv[t].load(rv, off_v[t]);
     };
-    auto prefetch_b = [&](int64_t c0) {
-        const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bh + (size_t)c0 * H, nv * (uint32_t)(H * sizeof(IT)));
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if constexpr (F32IN) pb[t] = __builtin_amdgcn_raw_buffer_load_b32(rb, off_b[t], 0, 0);
-            else pb[t] = __builtin_amdgcn_raw_buffer_load_b16(rb, off_b[t], 0, 0);
-        }
-    };
     auto reduce = [&](int m) -> f32x4 {   // sum of the producers' partial Gram tiles
-        f32x4 acc = zero4();
+        f32x4 acc = ld<f32x4>(smem + Lay::o_Gp + (m * 64 + lane) * 16);
 #pragma unroll
-        for (int w = 0; w < NCB; ++w) acc += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
+        for (int w = 1; w < NCB; ++w) acc += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
         return acc;
     };
     auto put_tb = [&](int r, int c, float v) {   // T_b[r][c] (one or two bf16 planes)
@@ -552,21 +586,36 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     };
 
     const int64_t nchunks = (len + kC - 1) / kC;
-    if (nchunks > 0) {
-        prefetch_v(0);
-        if (cw == 0) prefetch_b(0);
-    }
+    if (nchunks > 0) prefetch_v(0);
 
     for (int64_t it = 0; it <= nchunks; ++it) {
-        // ---- interval 1: inter-chunk step of chunk it - 1 on this wave's 16 state columns
+        // ---- interval 1: inter-chunk step of chunk it - 1 on this wave's 16 state columns.
+        // LDS operands come in three batches, each issued ahead of independent work and pinned
+        // at its first use (without this each MFMA waits for its own read).
         if (it > 0) {
             const int64_t c0 = (it - 1) * kC;
-            const int nvalid = (int)((len - c0) < kC ? (len - c0) : kC);
-            float vv[2][8];
+            const uint32_t nvalid = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
+            // output rows of the chunk: stores at or past row nvalid fall outside the resource
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob + (size_t)c0 * sv, nvalid * (uint32_t)(sv * sizeof(OT)));
+            // operand fragments read from [row][pm(index)] storage: elements 4 g4 + e (e < 4) and
+            // 16 + 4 g4 + e - 4 (e >= 4) of each 32-long contraction step are one 16-byte read
+            auto frag = [&](int off, int row, int stride, int col) -> bf16x8 {
+                return ld<bf16x8>(bfp(off) + row * stride + col + 8 * g4);
+            };
+            // batch 1: rows of T_b (for U) and of W (for W S)
+            bf16x8 tbr[2][Lay::kNP], wr[2][KS][Lay::kNP];
+#pragma unroll
+            for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+                for (int pl = 0; pl < Lay::kNP; ++pl) {
+                    tbr[ta][pl] = frag(Lay::o_Tb + pl * kC * TB * 2, 16 * ta + i16, TB, 0);
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) wr[ta][s][pl] = frag(Lay::o_W + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
+                }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < 2; ++t) pv[t].pin_all();
-#pragma unroll
-            for (int t = 0; t < 2; ++t) pv[t].to_f32(vv[t]);
+            Raw8<F32IN> vr[2] = {pv[0], pv[1]};
             if (it < nchunks) prefetch_v(it * kC);
 
             // V: token-per-lane -> column-per-lane through a product with the identity; the
@@ -575,31 +624,14 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 if constexpr (kFull) {
+                    float vv[8];
+                    vr[t].to_f32(vv);
                     bf16x8 vh, vl;
-                    split8(vv[t], vh, vl);
+                    split8(vv, vh, vl);
                     Vf[t] = mma(vh, Id0, zero4());
                     Vfl[t] = mma(vl, Id0, zero4());
                 } else {
-                    Vf[t] = mma(to_bf16x8(vv[t]), Id0, zero4());
-                }
-            }
-            // U = T_b V
-            auto ldTb = [&](int row, int plane) -> bf16x8 {   // T_b[row][4 g4 + e | 16 + 4 g4 + e]
-                return ld<bf16x8>(bfp(Lay::o_Tb) + plane * kC * TB + row * TB + 8 * g4);
-            };
-            f32x4 U[2];
-            {
-                const bf16x8 vb = acc_pair(Vf[0], Vf[1]);
-                bf16x8 vbl;
-                if constexpr (kFull) vbl = acc_pair(Vfl[0], Vfl[1]);
-#pragma unroll
-                for (int ta = 0; ta < 2; ++ta) {
-                    const bf16x8 tr = ldTb(16 * ta + i16, 0);
-                    U[ta] = mma(tr, vb, zero4());
-                    if constexpr (kFull) {
-                        U[ta] = mma(ldTb(16 * ta + i16, 1), vb, U[ta]);
-                        U[ta] = mma(tr, vbl, U[ta]);
-                    }
+                    Vf[t] = mma(__builtin_bit_cast(bf16x8, vr[t].p[0]), Id0, zero4());   // bf16 as stored
                 }
             }
             // state as B operand: contraction index (32-channel step s, g4, e) ->
@@ -607,68 +639,113 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
             bf16x8 Sh[KS], Sl[KS];
 #pragma unroll
             for (int s = 0; s < KS; ++s) acc_pair_split(Sacc[2 * s], Sacc[2 * s + 1], Sh[s], Sl[s]);
-            auto ldA = [&](const bf16* rowp, int s) -> bf16x8 {   // same channel selection (pm)
-                return ld<bf16x8>(rowp + 32 * s + 8 * g4);
-            };
-            f32x4 Vt[2];
 #pragma unroll
-            for (int ta = 0; ta < 2; ++ta) {
-                const bf16* Wr = bfp(Lay::o_W) + (16 * ta + i16) * RB;
-                f32x4 acc = zero4();
+            for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const bf16x8 wa = ldA(Wr, s);
-                    acc = mma(wa, Sh[s], acc);
-                    if constexpr (kFull) {
-                        acc = mma(ldA(Wr + kC * RB, s), Sh[s], acc);
-                        acc = mma(wa, Sl[s], acc);
-                    }
+                for (int pl = 0; pl < Lay::kNP; ++pl) {
+                    pin(tbr[ta][pl]);
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) pin(wr[ta][s][pl]);
                 }
-                Vt[ta] = U[ta] - acc;
+            // batch 2: rows of Q~ (hi, lo) and of A_qk (hi, lo)
+            bf16x8 qr[2][KS][2], ar[2][2];
+#pragma unroll
+            for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl) {
+                    ar[ta][pl] = frag(Lay::o_Aq + pl * kC * TB * 2, 16 * ta + i16, TB, 0);
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) qr[ta][s][pl] = frag(Lay::o_Qt + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            // U = T_b V, V~ = U - W S
+            f32x4 Vt[2];
+            {
+                const bf16x8 vb = acc_pair(Vf[0], Vf[1]);
+                bf16x8 vbl;
+                if constexpr (kFull) vbl = acc_pair(Vfl[0], Vfl[1]);
+#pragma unroll
+                for (int ta = 0; ta < 2; ++ta) {
+                    f32x4 U = mma(tbr[ta][0], vb, zero4());
+                    if constexpr (kFull) {
+                        U = mma(tbr[ta][1], vb, U);
+                        U = mma(tbr[ta][0], vbl, U);
+                    }
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        acc = mma(wr[ta][s][0], Sh[s], acc);
+                        if constexpr (kFull) {
+                            acc = mma(wr[ta][s][1], Sh[s], acc);
+                            acc = mma(wr[ta][s][0], Sl[s], acc);
+                        }
+                    }
+                    Vt[ta] = U - acc;
+                }
             }
             // V~ as B operand: token index (g4, e) -> 4 g4 + e (e < 4), 16 + 4 g4 + (e - 4)
             bf16x8 Vh, Vl;
             acc_pair_split(Vt[0], Vt[1], Vh, Vl);
+#pragma unroll
+            for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl) {
+                    pin(ar[ta][pl]);
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) pin(qr[ta][s][pl]);
+                }
             // outputs O = Q~ S + A_qk V~
+            f32x4 Oacc[2];
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta) {
-                const bf16* Qr = bfp(Lay::o_Qt) + (16 * ta + i16) * RB;
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    const bf16x8 qa = ldA(Qr, s), ql = ldA(Qr + kC * RB, s);
-                    acc = mma(qa, Sh[s], acc);
-                    acc = mma(ql, Sh[s], acc);
-                    acc = mma(qa, Sl[s], acc);
+                    acc = mma(qr[ta][s][0], Sh[s], acc);
+                    acc = mma(qr[ta][s][1], Sh[s], acc);
+                    acc = mma(qr[ta][s][0], Sl[s], acc);
                 }
-                const bf16* Ar = bfp(Lay::o_Aq) + (16 * ta + i16) * TB;
-                const bf16x8 ah = ld<bf16x8>(Ar + 8 * g4);
-                const bf16x8 al = ld<bf16x8>(Ar + kC * TB + 8 * g4);
-                acc = mma(ah, Vh, acc);
-                acc = mma(al, Vh, acc);
-                acc = mma(ah, Vl, acc);
+                Oacc[ta] = acc;
+            }
+            // batch 3: rows of K_end^T and the chunk decay gamma
+            bf16x8 kr[CT][Lay::kNP];
+            f32x4 gm[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int pl = 0; pl < Lay::kNP; ++pl) kr[ct][pl] = frag(Lay::o_Ke + pl * DK * TB * 2, 16 * ct + i16, TB, 0);
+                gm[ct] = ld<f32x4>(f32p(Lay::o_gam) + 16 * ct + 4 * g4);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ta = 0; ta < 2; ++ta) {
+                f32x4 acc = Oacc[ta];
+                acc = mma(ar[ta][0], Vh, acc);
+                acc = mma(ar[ta][1], Vh, acc);
+                acc = mma(ar[ta][0], Vl, acc);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * ta + 4 * g4 + j;
-                    if (r < nvalid) {
-                        const size_t off = (size_t)(row0 + c0 + r) * sv + (size_t)h * a.dv + col0 + i16;
-                        if constexpr (OUT_F32) reinterpret_cast<float*>(a.o)[off] = a.scale * acc[j];
-                        else reinterpret_cast<bf16*>(a.o)[off] = f2bf(a.scale * acc[j]);
-                    }
+                    if constexpr (OUT_F32)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, a.scale * acc[j]), ro,
+                                                              off_o[ta][j], 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, f2bf(a.scale * acc[j])), ro,
+                                                              off_o[ta][j], 0, 0);
                 }
             }
             // state: S <- Diag(gamma_last) S + K_end^T V~
-            const float* gam = f32p(Lay::o_gam);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const bf16* Kr = bfp(Lay::o_Ke) + (16 * ct + i16) * TB;
-                const bf16x8 ka = ld<bf16x8>(Kr + 8 * g4);
-                const f32x4 gm = ld<f32x4>(gam + 16 * ct + 4 * g4);
-                f32x4 s = Sacc[ct] * gm;
-                s = mma(ka, Vh, s);
-                s = mma(ka, Vl, s);
-                if constexpr (kFull)
-                    s = mma(ld<bf16x8>(Kr + DK * TB + 8 * g4), Vh, s);
+#pragma unroll
+                for (int pl = 0; pl < Lay::kNP; ++pl) pin(kr[ct][pl]);
+                pin(gm[ct]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                f32x4 s = Sacc[ct] * gm[ct];
+                s = mma(kr[ct][0], Vh, s);
+                s = mma(kr[ct][0], Vl, s);
+                if constexpr (kFull) s = mma(kr[ct][1], Vh, s);
                 Sacc[ct] = s;
             }
         }
@@ -677,14 +754,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         // ---- interval 2: the UT solve (cw = 0) and the A_qk tiles (cw = 1..3) of chunk it
         if (it < nchunks) {
             if (cw == 0) {
-                float bt[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    pin(pb[t]);
-                    if constexpr (F32IN) bt[t] = __builtin_bit_cast(float, pb[t]);
-                    else bt[t] = __builtin_bit_cast(float, pb[t] << 16);
-                }
-                if (it + 1 < nchunks) prefetch_b((it + 1) * kC);
+                const float bt[2] = {f32p(Lay::o_beta)[i16], f32p(Lay::o_beta)[16 + i16]};
                 // A_kk diagonal blocks (rows scaled by beta, strictly lower part) to LDS
                 f32x4 N0 = reduce(3), N1 = reduce(4);
                 const f32x4 A10 = reduce(5);
@@ -699,31 +769,49 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 st<f32x4>(Nb + SB + i16 * 20 + 4 * g4, N1);
                 wave_lds_order();
                 // column c = i16 of (I + N_bb)^-1, bb = g4 & 1, by forward substitution in blocks
-                // of 4 rows; each step reads N rows through 16-byte broadcast loads that do not
-                // depend on x (the two blocks sit 16 banks apart)
+                // of 4 rows.  The row pieces a block needs (16-byte broadcast reads; the two
+                // matrices sit 16 banks apart) are read together and pinned, so the dependent
+                // chain waits on LDS once per block.
                 const int bb = g4 & 1;
                 const float* Nm = Nb + bb * SB;
+                f32x4 nv[16][4];
+                auto load_block = [&](int I) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int K = 0; K <= I; ++K)
+                            if (K < I || i > 0) nv[4 * I + i][K] = ld<f32x4>(Nm + (4 * I + i) * 20 + 4 * K);
+                };
                 float x[16];
+                // an opaque lane index: keeps the compiler from hoisting the 16 identity entries
+                // of this lane (or their compare masks) out of the chunk loop into registers
+                int col = i16;
+                asm volatile("" : "+v"(col));
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
+                    load_block(I);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int K = 0; K <= I; ++K)
+                            if (K < I || i > 0) pin(nv[4 * I + i][K]);
                     float y[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) y[i] = (4 * I + i == i16) ? 1.f : 0.f;
+                    for (int i = 0; i < 4; ++i) {
+                        y[i] = (4 * I + i == col) ? 1.f : 0.f;
 #pragma unroll
-                    for (int K = 0; K < I; ++K)
+                        for (int K = 0; K < I; ++K) {
+                            const f32x4 nr = nv[4 * I + i][K];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const f32x4 nr = ld<f32x4>(Nm + (4 * I + i) * 20 + 4 * K);
-                            y[i] -= (nr[0] * x[4 * K] + nr[1] * x[4 * K + 1]) +
-                                    (nr[2] * x[4 * K + 2] + nr[3] * x[4 * K + 3]);
+                            for (int e = 0; e < 4; ++e) y[i] = __builtin_fmaf(-nr[e], x[4 * K + e], y[i]);
                         }
-                    const f32x4 n1 = ld<f32x4>(Nm + (4 * I + 1) * 20 + 4 * I);
-                    const f32x4 n2 = ld<f32x4>(Nm + (4 * I + 2) * 20 + 4 * I);
-                    const f32x4 n3 = ld<f32x4>(Nm + (4 * I + 3) * 20 + 4 * I);
+                    }
+                    const f32x4 n1 = nv[4 * I + 1][I], n2 = nv[4 * I + 2][I], n3 = nv[4 * I + 3][I];
                     x[4 * I] = y[0];
-                    x[4 * I + 1] = y[1] - n1[0] * x[4 * I];
-                    x[4 * I + 2] = y[2] - n2[0] * x[4 * I] - n2[1] * x[4 * I + 1];
-                    x[4 * I + 3] = y[3] - n3[0] * x[4 * I] - n3[1] * x[4 * I + 1] - n3[2] * x[4 * I + 2];
+                    x[4 * I + 1] = __builtin_fmaf(-n1[0], x[4 * I], y[1]);
+                    x[4 * I + 2] = __builtin_fmaf(-n2[1], x[4 * I + 1], __builtin_fmaf(-n2[0], x[4 * I], y[2]));
+                    x[4 * I + 3] = __builtin_fmaf(-n3[2], x[4 * I + 2],
+                                                  __builtin_fmaf(-n3[1], x[4 * I + 1], __builtin_fmaf(-n3[0], x[4 * I], y[3])));
                 }
                 // diagonal blocks of T_b, and T_bb column-major (fp32) for the off-diagonal block
                 if (g4 < 2) {
@@ -754,17 +842,13 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
             } else {
                 // A_qk tile m (masked) -> split bf16 [row][pm(col)]
                 const int m = cw - 1;   // 0: rows 0-15 x cols 0-15, 1: 16-31 x 16-31, 2: 16-31 x 0-15
-                const f32x4 acc = reduce(m);
+                f32x4 acc = reduce(m);
                 const int ta = (m == 0) ? 0 : 1, tb = (m == 1) ? 1 : 0;
                 const int r = 16 * ta + i16;
-                bf16x4 hv, lv;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf16 hh, ll;
-                    split_bf16((16 * tb + 4 * g4 + j <= r) ? acc[j] : 0.f, hh, ll);
-                    hv[j] = hh;
-                    lv[j] = ll;
-                }
+                for (int j = 0; j < 4; ++j) acc[j] = (16 * tb + 4 * g4 + j <= r) ? acc[j] : 0.f;
+                bf16x4 hv, lv;
+                split4(acc, hv, lv);
                 bf16* ad = bfp(Lay::o_Aq) + r * TB + pm(16 * tb + 4 * g4);
                 st<bf16x4>(ad, hv);
                 st<bf16x4>(ad + kC * TB, lv);
