@@ -5,8 +5,9 @@
 // sum of g inside the chunk (log of the cumulative decay gamma of eq. (3)), and unrolling eq. (1)
 // over the chunk gives (the UT transform the pages defer to Kimi Linear):
 //     A_kk[r,i] = beta_r sum_c k_rc k_ic exp(G_rc - G_ic)        i < r   (strictly lower)
-//     T = (I + A_kk)^-1,  T_b = T Diag(beta)
-//     W = T_b (K * exp(G)),  U = T_b V,  V~ = U - W S                      (pseudo-values)
+//     T = (I + A_kk)^-1,  T_b = T Diag(beta),  K~ = K * exp(G)
+//     V~ = T_b (V - K~ S)            (pseudo-values; the same as U - W S with U = T_b V and
+//                                     W = T_b K~, computed without forming W)
 //     A_qk[r,i] = sum_c q_rc k_ic exp(G_rc - G_ic)             i <= r  (eq. (4): Tril keeps
 //                                                                        the diagonal)
 //     O = (Q * exp(G)) S + A_qk V~                                        (eq. (4))
@@ -23,30 +24,30 @@
 // head go to the same XCD so their reads of q, k, g share L2.  Only the last of the steps below
 // depends on the state, so the workgroup is a two-stage pipeline: four producer waves prepare
 // chunk i while four consumer waves advance the state through chunk i - 1.  Each SIMD runs one
-// wave of each kind, so one kind's latency hides behind the other's issue.  Three workgroup
+// wave of each kind, so one kind's latency hides behind the other's issue.  Two workgroup
 // barriers per iteration; every hand-off buffer is written after the barrier that ends its last
 // read, so one copy of each suffices.
 //   interval 1  producers: inputs of chunk i (prefetched one chunk ahead), in-tile decay prefix
 //               (DPP scan over the 16 token lanes of a row), decayed operands in registers and the
 //               partial Gram tiles of A_kk and A_qk over each wave's 32 key channels.
-//               consumers: the inter-chunk step of chunk i - 1 on their 16 value columns: U,
-//               V~ = U - W S, O = Q~ S + A_qk V~ (written out), S <- Diag(gamma) S + K_end^T V~.
-//               The state slice (dk x 16, fp32) stays in MFMA accumulators for the whole sequence.
-//   interval 2  producers: Q~, K_end^T and the decay of the chunk to LDS; K~^T fragments kept in
-//               registers ("transposes" are products with an identity block).
+//               consumers: the inter-chunk step of chunk i - 1 on their 16 value columns:
+//               V~ = T_b (V - K~ S), O = Q~ S + A_qk V~ (written out),
+//               S <- Diag(gamma) S + K_end^T V~.  The state slice (dk x 16, fp32) stays in MFMA
+//               accumulators for the whole sequence.
+//   interval 2  producers: Q~, K~, K_end^T ("transposed" by a product with an identity block)
+//               and the decay of the chunk to LDS.
 //               consumer 0: T_b from the reduced Gram tiles: both diagonal 16x16 blocks of
 //               (I + A_kk)^-1 at once by forward substitution (lanes 0-15 one block, 16-31 the
 //               other), the off-diagonal block with split MFMA products.
 //               consumers 1-3: one masked A_qk tile each.
-//   interval 3  producers: W = T_b K~ for their channels.
 //
 // Precision: bf16 MFMA with fp32 accumulation.  Operands whose rounding would dominate the error
 // are carried as hi + lo bf16 pairs (products hi*hi + lo*hi + hi*lo): the decayed operands of
-// A_qk, A_qk itself, V~ in both of its uses, and both operands of (Q * exp(G)) S, which dominates
-// short sequences entered with a large state.  A_kk, T_b, K~, W, K_end and the state as the
-// operand of W S are single bf16; U and the state stay fp32.  Float32 inputs (kFull) carry every
-// operand but A_kk's as a pair.  The scale on q is applied to the outputs (everything is linear
-// in q).
+// A_qk, A_qk itself, V - K~ S, V~ in both of its uses, and both operands of (Q * exp(G)) S,
+// which dominates short sequences entered with a large state.  A_kk, T_b, K~, K_end and the
+// state as the operand of K~ S are single bf16; the state stays fp32.  Float32 inputs (kFull)
+// carry every operand but A_kk's as a pair.  The scale on q is applied to the outputs
+// (everything is linear in q).
 #include <type_traits>
 
 #include "kda_device.h"
@@ -72,8 +73,8 @@ struct Layout {
     static constexpr int o_T = o_N + 2 * SB * 4;              // fp32 2 blocks [col][20]: T00, T11
     static constexpr int o_Tb = o_T + 2 * SB * 4;             // bf16 planes [C][TB]
     static constexpr int o_Aq = o_Tb + kNP * kC * TB * 2;     // bf16 hi, lo [C][TB]
-    static constexpr int o_W = o_Aq + 2 * kC * TB * 2;        // bf16 planes [C][RB]
-    static constexpr int o_Qt = o_W + kNP * kC * RB * 2;      // bf16 hi, lo [C][RB]
+    static constexpr int o_Kt = o_Aq + 2 * kC * TB * 2;       // bf16 planes [C][RB]: K~
+    static constexpr int o_Qt = o_Kt + kNP * kC * RB * 2;     // bf16 hi, lo [C][RB]: Q~
     static constexpr int o_Ke = o_Qt + 2 * kC * RB * 2;       // bf16 planes [DK][TB] (K_end^T)
     static constexpr int o_gam = o_Ke + kNP * DK * TB * 2;    // fp32 [DK]
     static constexpr int o_beta = o_gam + DK * 4;             // fp32 [C]
@@ -250,7 +251,7 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t&
 
 // ==================================== producer waves =========================================
 // Wave p owns key channels [32 p, 32 p + 32) (none when p >= DK / 32).  Per chunk: the decayed
-// operands, the partial Gram tiles (interval 1), Q~ / K_end^T / gamma (interval 2), W (interval 3).
+// operands and the partial Gram tiles (interval 1); Q~, K~, K_end^T and gamma (interval 2).
 template <int DK, bool F32IN>
 __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p, int lane,
                                          int64_t row0, int64_t len, int h) {
@@ -315,7 +316,6 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
         const bool work = intra && it < nchunks;   // wave-uniform
         float F0[8], F1[8], Qs1[8], Kr[2][8], Kd1[8], Kc[8];
         bf16x8 Qh0, Ql0;
-        f32x4 Ktf[2][2], Ktfl[2][2];   // K~^T fragments [tile][channel half]
 
         // ---- interval 1: decay prefix, decayed operands, partial Gram tiles
         if (work) {
@@ -407,89 +407,58 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
         }
         __syncthreads();
 
-        // ---- interval 2: Q~, K_end^T, gamma to LDS; K~^T fragments in registers
+        // ---- interval 2: Q~ (split), K~ and K_end^T to LDS, and the decay of the chunk
         if (work) {
             if (i16 == 0) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f32p(Lay::o_gam)[ch0 + e] = F0[e] * F1[e];
             }
-            // Q~ = Q exp(G) (split, [token][pm(channel)]); tile 1 carries the tile-0 decay
+            // 8 channels of token 16 t + i16 into [token][pm(channel)] storage
+            auto put_row = [&](int off, int t, bf16x8 v) {
+                bf16* d = bfp(off) + (16 * t + i16) * RB + 32 * p;
+                st<bf16x4>(d + pm(8 * g4), bf16x4{v[0], v[1], v[2], v[3]});
+                st<bf16x4>(d + pm(8 * g4 + 4), bf16x4{v[4], v[5], v[6], v[7]});
+            };
+            // Q~ = Q exp(G), K~ = K exp(G) from the chunk start; tile 1 carries the tile-0 decay
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 bf16x8 hh = Qh0, ll = Ql0;
+                float xt[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xt[e] = t ? Kr[1][e] * F0[e] : Kr[0][e];
                 if (t == 1) {
                     float x[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[e] = Qs1[e] * F0[e];
                     split8(x, hh, ll);
                 }
-                bf16* qd = bfp(Lay::o_Qt) + (16 * t + i16) * RB + 32 * p;
-                const int p0 = pm(8 * g4), p1 = pm(8 * g4 + 4);
-                st<bf16x4>(qd + p0, bf16x4{hh[0], hh[1], hh[2], hh[3]});
-                st<bf16x4>(qd + p1, bf16x4{hh[4], hh[5], hh[6], hh[7]});
-                st<bf16x4>(qd + kC * RB + p0, bf16x4{ll[0], ll[1], ll[2], ll[3]});
-                st<bf16x4>(qd + kC * RB + p1, bf16x4{ll[4], ll[5], ll[6], ll[7]});
+                put_row(Lay::o_Qt, t, hh);
+                put_row(Lay::o_Qt + kC * RB * 2, t, ll);
+                if constexpr (kFull) {
+                    bf16x8 th, tl;
+                    split8(xt, th, tl);
+                    put_row(Lay::o_Kt, t, th);
+                    put_row(Lay::o_Kt + kC * RB * 2, t, tl);
+                } else {
+                    put_row(Lay::o_Kt, t, to_bf16x8(xt));
+                }
             }
-            // K~ = K exp(G) and K_end = K exp(G_last - G), transposed through the identity:
-            // the accumulator of lane (channel i16 of half hh, g4) holds tokens 16 t + 4 g4 + j.
+            // K_end = K exp(G_last - G), transposed through the identity: the accumulator of lane
+            // (channel i16 of half hh, g4) holds tokens 16 t + 4 g4 + j.
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                float xt[8], xe[8];
+                float xe[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xt[e] = t ? Kr[1][e] * F0[e] : Kr[0][e];
-                    xe[e] = t ? Kd1[e] * F1[e] : Kc[e] * F1[e];
-                }
-                bf16x8 th, tl, eh, el;
-                if constexpr (kFull) {
-                    split8(xt, th, tl);
-                    split8(xe, eh, el);
-                } else {
-                    th = to_bf16x8(xt);
-                    eh = to_bf16x8(xe);
-                }
+                for (int e = 0; e < 8; ++e) xe[e] = t ? Kd1[e] * F1[e] : Kc[e] * F1[e];
+                bf16x8 eh, el;
+                if constexpr (kFull) split8(xe, eh, el);
+                else eh = to_bf16x8(xe);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    Ktf[t][hh] = mma(th, Id[hh], zero4());
                     const f32x4 ke = mma(eh, Id[hh], zero4());
                     bf16* dst = bfp(Lay::o_Ke) + (32 * p + 16 * hh + i16) * TB + pm(16 * t + 4 * g4);
                     st<bf16x4>(dst, to_bf16x4(ke));
-                    if constexpr (kFull) {
-                        Ktfl[t][hh] = mma(tl, Id[hh], zero4());
-                        const f32x4 kel = mma(el, Id[hh], zero4());
-                        st<bf16x4>(dst + DK * TB, to_bf16x4(kel));
-                    }
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- interval 3: W = T_b K~ on this wave's channels, [token][pm(channel)]
-        if (work) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const bf16x8 ka = acc_pair(Ktf[0][hh], Ktf[1][hh]);
-                bf16x8 kal;
-                if constexpr (kFull) kal = acc_pair(Ktfl[0][hh], Ktfl[1][hh]);
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const bf16* tbr = bfp(Lay::o_Tb) + (16 * tt + i16) * TB + 8 * g4;
-                    const bf16x8 tb = ld<bf16x8>(tbr);
-                    f32x4 acc = mma(ka, tb, zero4());
-                    if constexpr (kFull) {
-                        acc = mma(kal, tb, acc);
-                        acc = mma(ka, ld<bf16x8>(tbr + kC * TB), acc);
-                    }
-                    // acc[j] = W[16 tt + i16][32 p + 16 hh + 4 g4 + j]
-                    bf16* Wd = bfp(Lay::o_W) + (16 * tt + i16) * RB + 32 * p + pm(16 * hh + 4 * g4);
-                    if constexpr (kFull) {
-                        bf16x4 hv, lv;
-                        split4(acc, hv, lv);
-                        st<bf16x4>(Wd, hv);
-                        st<bf16x4>(Wd + kC * RB, lv);
-                    } else {
-                        st<bf16x4>(Wd, to_bf16x4(acc));
-                    }
+                    if constexpr (kFull) st<bf16x4>(dst + DK * TB, to_bf16x4(mma(el, Id[hh], zero4())));
                 }
             }
         }
@@ -602,15 +571,15 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
             auto frag = [&](int off, int row, int stride, int col) -> bf16x8 {
                 return ld<bf16x8>(bfp(off) + row * stride + col + 8 * g4);
             };
-            // batch 1: rows of T_b (for U) and of W (for W S)
-            bf16x8 tbr[2][Lay::kNP], wr[2][KS][Lay::kNP];
+            // batch 1: rows of K~ (for K~ S) and of T_b
+            bf16x8 tbr[2][Lay::kNP], kt[2][KS][Lay::kNP];
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
                 for (int pl = 0; pl < Lay::kNP; ++pl) {
                     tbr[ta][pl] = frag(Lay::o_Tb + pl * kC * TB * 2, 16 * ta + i16, TB, 0);
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) wr[ta][s][pl] = frag(Lay::o_W + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
+                    for (int s = 0; s < KS; ++s) kt[ta][s][pl] = frag(Lay::o_Kt + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
                 }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -620,7 +589,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
 
             // V: token-per-lane -> column-per-lane through a product with the identity; the
             // accumulator of lane (column i16, g4) holds tokens 16 t + 4 g4 + j
-            f32x4 Vf[2], Vfl[2];
+            f32x4 Vf[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 if constexpr (kFull) {
@@ -628,8 +597,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                     vr[t].to_f32(vv);
                     bf16x8 vh, vl;
                     split8(vv, vh, vl);
-                    Vf[t] = mma(vh, Id0, zero4());
-                    Vfl[t] = mma(vl, Id0, zero4());
+                    Vf[t] = mma(vl, Id0, mma(vh, Id0, zero4()));
                 } else {
                     Vf[t] = mma(__builtin_bit_cast(bf16x8, vr[t].p[0]), Id0, zero4());   // bf16 as stored
                 }
@@ -645,7 +613,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 for (int pl = 0; pl < Lay::kNP; ++pl) {
                     pin(tbr[ta][pl]);
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) pin(wr[ta][s][pl]);
+                    for (int s = 0; s < KS; ++s) pin(kt[ta][s][pl]);
                 }
             // batch 2: rows of Q~ (hi, lo) and of A_qk (hi, lo)
             bf16x8 qr[2][KS][2], ar[2][2];
@@ -658,29 +626,32 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                     for (int s = 0; s < KS; ++s) qr[ta][s][pl] = frag(Lay::o_Qt + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
                 }
             __builtin_amdgcn_sched_barrier(0);
-            // U = T_b V, V~ = U - W S
+            // V~ = T_b (V - K~ S): the residual R = V - K~ S in fp32, then one product with T_b
+            // (R split, so only T_b is rounded)
             f32x4 Vt[2];
             {
-                const bf16x8 vb = acc_pair(Vf[0], Vf[1]);
-                bf16x8 vbl;
-                if constexpr (kFull) vbl = acc_pair(Vfl[0], Vfl[1]);
+                f32x4 R[2];
 #pragma unroll
                 for (int ta = 0; ta < 2; ++ta) {
-                    f32x4 U = mma(tbr[ta][0], vb, zero4());
-                    if constexpr (kFull) {
-                        U = mma(tbr[ta][1], vb, U);
-                        U = mma(tbr[ta][0], vbl, U);
-                    }
                     f32x4 acc = zero4();
 #pragma unroll
                     for (int s = 0; s < KS; ++s) {
-                        acc = mma(wr[ta][s][0], Sh[s], acc);
+                        acc = mma(kt[ta][s][0], Sh[s], acc);
                         if constexpr (kFull) {
-                            acc = mma(wr[ta][s][1], Sh[s], acc);
-                            acc = mma(wr[ta][s][0], Sl[s], acc);
+                            acc = mma(kt[ta][s][1], Sh[s], acc);
+                            acc = mma(kt[ta][s][0], Sl[s], acc);
                         }
                     }
-                    Vt[ta] = U - acc;
+                    R[ta] = Vf[ta] - acc;
+                }
+                bf16x8 Rh, Rl;   // R as B operand: token index (g4, e) as for V~ below
+                acc_pair_split(R[0], R[1], Rh, Rl);
+#pragma unroll
+                for (int ta = 0; ta < 2; ++ta) {
+                    f32x4 v = mma(tbr[ta][0], Rh, zero4());
+                    v = mma(tbr[ta][0], Rl, v);
+                    if constexpr (kFull) v = mma(tbr[ta][1], Rh, v);
+                    Vt[ta] = v;
                 }
             }
             // V~ as B operand: token index (g4, e) -> 4 g4 + e (e < 4), 16 + 4 g4 + (e - 4)
@@ -854,8 +825,6 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 st<bf16x4>(ad + kC * TB, lv);
             }
         }
-        __syncthreads();
-        // ---- interval 3: nothing here (the producers form W)
         __syncthreads();
     }
 
