@@ -36,9 +36,8 @@
 //               accumulators for the whole sequence.
 //   interval 2  producers: Q~, K~, K_end^T ("transposed" by a product with an identity block)
 //               and the decay of the chunk to LDS.
-//               consumer 0: T_b from the reduced Gram tiles: both diagonal 16x16 blocks of
-//               (I + A_kk)^-1 at once by forward substitution (lanes 0-15 one block, 16-31 the
-//               other), the off-diagonal block with split MFMA products.
+//               consumer 0: T_b from the reduced Gram tiles by block elimination with
+//               16x16x16 MFMA products (closed-form 4x4 diagonal blocks, then 8x8, 16x16, 32x32).
 //               consumers 1-3: one masked A_qk tile each.
 //
 // Precision: bf16 MFMA with fp32 accumulation.  Operands whose rounding would dominate the error
@@ -70,8 +69,7 @@ struct Layout {
     static constexpr int SB = 16 * 20 + 16;                   // fp32 16x16 block stride (banks +16)
     static constexpr int o_Gp = 0;                            // fp32 [NCB][6][64][4] partials
     static constexpr int o_N = o_Gp + NCB * 6 * 64 * 16;      // fp32 2 blocks [16][20]: A_kk diag
-    static constexpr int o_T = o_N + 2 * SB * 4;              // fp32 2 blocks [col][20]: T00, T11
-    static constexpr int o_Tb = o_T + 2 * SB * 4;             // bf16 planes [C][TB]
+    static constexpr int o_Tb = o_N + 2 * SB * 4;             // bf16 planes [C][TB]
     static constexpr int o_Aq = o_Tb + kNP * kC * TB * 2;     // bf16 hi, lo [C][TB]
     static constexpr int o_Kt = o_Aq + 2 * kC * TB * 2;       // bf16 planes [C][RB]: K~
     static constexpr int o_Qt = o_Kt + kNP * kC * RB * 2;     // bf16 hi, lo [C][RB]: Q~
@@ -147,21 +145,11 @@ __device__ __forceinline__ void split4(f32x4 a, bf16x4& hi, bf16x4& lo) {
     lo = bf16x4{l[0], l[1], l[2], l[3]};
 }
 
-// hi*hi + lo*hi + hi*lo of two fp32 fragments whose contraction is 16 long (elements 0-3 from
-// `a` and `b`, the rest zero).
-__device__ __forceinline__ f32x4 mma16_split(const float* a, const float* b) {
-    float xa[8], xb[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        xa[e] = e < 4 ? a[e] : 0.f;
-        xb[e] = e < 4 ? b[e] : 0.f;
-    }
-    bf16x8 ah, al, bh, bl;
-    split8(xa, ah, al);
-    split8(xb, bh, bl);
-    f32x4 r = mma(ah, bh, zero4());
-    r = mma(al, bh, r);
-    return mma(ah, bl, r);
+// 16x16x16 product, single bf16 operands: lane (i16, g4) supplies row (A) / column (B) i16 at
+// contraction positions 4 g4 .. 4 g4 + 3; the result is laid out as for mma().
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
 // Storage order of every 32-long contraction index in LDS: position pm(c) puts the elements one
@@ -725,91 +713,103 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         // ---- interval 2: the UT solve (cw = 0) and the A_qk tiles (cw = 1..3) of chunk it
         if (it < nchunks) {
             if (cw == 0) {
+                // T = (I + N)^-1, N = A_kk with rows scaled by beta (strictly lower, 32 x 32).
+                // Each diagonal 16x16 block B = L0 + L1 + L2 (L0: inside the 4x4 diagonal
+                // blocks; L1: the 4x4 blocks just below them within each 8x8 diagonal block; L2:
+                // the lower-left 8x8 block) is inverted by block elimination,
+                //     D = (I + L0)^-1 (closed form, fp32),  E = D - D L1 D,  X = E - E L2 E,
+                // each product filling blocks that are zero in the previous level (no
+                // cancellation), and T10 = -T11 N10 T00.  Products are 16x16x16 MFMAs on single
+                // bf16 operands: T_b is rounded to bf16 in any case, and the diagonal 4x4 blocks
+                // stay fp32.  Forms: row form of M in lane (i16, g4) = M[i16][4 g4 + j], column
+                // form = M[4 g4 + j][i16]; mma16(row form of X, column form of Y) is the column
+                // form of X Y, and the row form of M is the column form of M^T.
                 const float bt[2] = {f32p(Lay::o_beta)[i16], f32p(Lay::o_beta)[16 + i16]};
-                // A_kk diagonal blocks (rows scaled by beta, strictly lower part) to LDS
-                f32x4 N0 = reduce(3), N1 = reduce(4);
-                const f32x4 A10 = reduce(5);
+                // an opaque lane index: keeps the compiler from hoisting lane-constant masks out
+                // of the chunk loop into registers held across it
+                int lid = i16;
+                asm volatile("" : "+v"(lid));
+                const int rb = lid >> 2;                       // 4-row block of this lane's row / column
+                f32x4 Nr[2];
+                Nr[0] = reduce(3);
+                Nr[1] = reduce(4);
+                f32x4 N10r = reduce(5);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const bool low = 4 * g4 + j < i16;
-                    N0[j] = low ? N0[j] * bt[0] : 0.f;
-                    N1[j] = low ? N1[j] * bt[1] : 0.f;
+                    const bool low = 4 * g4 + j < lid;
+                    Nr[0][j] = low ? Nr[0][j] * bt[0] : 0.f;
+                    Nr[1][j] = low ? Nr[1][j] * bt[1] : 0.f;
+                    N10r[j] *= bt[1];
                 }
                 float* Nb = f32p(Lay::o_N);
-                st<f32x4>(Nb + i16 * 20 + 4 * g4, N0);
-                st<f32x4>(Nb + SB + i16 * 20 + 4 * g4, N1);
+                st<f32x4>(Nb + i16 * 20 + 4 * g4, Nr[0]);
+                st<f32x4>(Nb + SB + i16 * 20 + 4 * g4, Nr[1]);
                 wave_lds_order();
-                // column c = i16 of (I + N_bb)^-1, bb = g4 & 1, by forward substitution in blocks
-                // of 4 rows.  The row pieces a block needs (16-byte broadcast reads; the two
-                // matrices sit 16 banks apart) are read together and pinned, so the dependent
-                // chain waits on LDS once per block.
-                const int bb = g4 & 1;
-                const float* Nm = Nb + bb * SB;
-                f32x4 nv[16][4];
-                auto load_block = [&](int I) {
+                f32x4 Nc[2], n1[2], n2[2], n3[2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                for (int q = 0; q < 2; ++q) {
 #pragma unroll
-                        for (int K = 0; K <= I; ++K)
-                            if (K < I || i > 0) nv[4 * I + i][K] = ld<f32x4>(Nm + (4 * I + i) * 20 + 4 * K);
-                };
-                float x[16];
-                // an opaque lane index: keeps the compiler from hoisting the 16 identity entries
-                // of this lane (or their compare masks) out of the chunk loop into registers
-                int col = i16;
-                asm volatile("" : "+v"(col));
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    load_block(I);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int K = 0; K <= I; ++K)
-                            if (K < I || i > 0) pin(nv[4 * I + i][K]);
-                    float y[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        y[i] = (4 * I + i == col) ? 1.f : 0.f;
-#pragma unroll
-                        for (int K = 0; K < I; ++K) {
-                            const f32x4 nr = nv[4 * I + i][K];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) y[i] = __builtin_fmaf(-nr[e], x[4 * K + e], y[i]);
-                        }
-                    }
-                    const f32x4 n1 = nv[4 * I + 1][I], n2 = nv[4 * I + 2][I], n3 = nv[4 * I + 3][I];
-                    x[4 * I] = y[0];
-                    x[4 * I + 1] = __builtin_fmaf(-n1[0], x[4 * I], y[1]);
-                    x[4 * I + 2] = __builtin_fmaf(-n2[1], x[4 * I + 1], __builtin_fmaf(-n2[0], x[4 * I], y[2]));
-                    x[4 * I + 3] = __builtin_fmaf(-n3[2], x[4 * I + 2],
-                                                  __builtin_fmaf(-n3[1], x[4 * I + 1], __builtin_fmaf(-n3[0], x[4 * I], y[3])));
+                    for (int j = 0; j < 4; ++j) Nc[q][j] = Nb[q * SB + (4 * g4 + j) * 20 + i16];
+                    // rows 1..3 of the 4x4 diagonal block g4 (strictly lower entries)
+                    n1[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 1) * 20 + 4 * g4);
+                    n2[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 2) * 20 + 4 * g4);
+                    n3[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 3) * 20 + 4 * g4);
                 }
-                // diagonal blocks of T_b, and T_bb column-major (fp32) for the off-diagonal block
-                if (g4 < 2) {
-                    const float bc = bt[bb];
+                const bool on_diag = g4 == rb;                 // this lane's 4-block holds D entries
+                const int kk = lid & 3;
+                const float d0 = kk == 0 ? 1.f : 0.f, d1 = kk == 1 ? 1.f : 0.f;
+                const float d2 = kk == 2 ? 1.f : 0.f, d3 = kk == 3 ? 1.f : 0.f;
+                // whole-vector masks: L1 and L2 in row form (row i16, columns 4 g4 + j) and in
+                // column form (rows 4 g4 + j, column i16)
+                const bool l1r = (rb == 1 || rb == 3) && g4 == rb - 1;
+                const bool l1c = (g4 == 1 || g4 == 3) && rb == g4 - 1;
+                const bool l2r = lid >= 8 && g4 < 2;
+                const bool l2c = g4 >= 2 && lid < 8;
+                auto mask = [](f32x4 v, bool keep) { return keep ? v : zero4(); };
+                f32x4 Xc0, Xr1;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) put_tb(16 * bb + r, 16 * bb + i16, x[r] * bc);
-                    float* Tt = f32p(Lay::o_T) + bb * SB + i16 * 20;
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4)
-                        st<f32x4>(Tt + 4 * r4, f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]});
+                for (int q = 0; q < 2; ++q) {
+                    // D = (I + L0)^-1: column kk (column form) and row kk (row form) of the
+                    // inverse of the unit lower 4x4 block g4
+                    const float x1 = d1 - n1[q][0] * d0;
+                    const float x2 = d2 - n2[q][0] * d0 - n2[q][1] * x1;
+                    const float x3 = d3 - n3[q][0] * d0 - n3[q][1] * x1 - n3[q][2] * x2;
+                    const float y2 = d2 - d3 * n3[q][2];
+                    const float y1 = d1 - y2 * n2[q][1] - d3 * n3[q][1];
+                    const float y0 = d0 - y1 * n1[q][0] - y2 * n2[q][0] - d3 * n3[q][0];
+                    const f32x4 Dc = on_diag ? f32x4{d0, x1, x2, x3} : zero4();
+                    const f32x4 Dr = on_diag ? f32x4{y0, y1, y2, d3} : zero4();
+                    const bf16x4 Dcb = to_bf16x4(Dc), Drb = to_bf16x4(Dr);
+                    // E = D - D L1 D (column form), E^T = D^T - D^T L1^T D^T (row form of E)
+                    const f32x4 Ec = Dc - mma16(Drb, to_bf16x4(mma16(to_bf16x4(mask(Nr[q], l1r)), Dcb, zero4())), zero4());
+                    const f32x4 Er = Dr - mma16(Dcb, to_bf16x4(mma16(to_bf16x4(mask(Nc[q], l1c)), Drb, zero4())), zero4());
+                    const bf16x4 Ecb = to_bf16x4(Ec), Erb = to_bf16x4(Er);
+                    // X = E - E L2 E: column form for T00, row form for T11
+                    if (q == 0)
+                        Xc0 = Ec - mma16(Erb, to_bf16x4(mma16(to_bf16x4(mask(Nr[q], l2r)), Ecb, zero4())), zero4());
+                    else
+                        Xr1 = Er - mma16(Ecb, to_bf16x4(mma16(to_bf16x4(mask(Nc[q], l2c)), Erb, zero4())), zero4());
                 }
-                wave_lds_order();
-                // Y = A_kk[1,0] T00 (rows scaled by beta), then T10 = -T11 Y; contraction 16:
-                // operand element e < 4 pairs with index 4 g4 + e
-                float ya[4], yb[4], za[4];
-                const f32x4 t00 = ld<f32x4>(f32p(Lay::o_T) + i16 * 20 + 4 * g4);   // T00[4 g4 + e][i16]
+                // T10 = -T11 (N10 T00), column form
+                const f32x4 T10c = -mma16(to_bf16x4(Xr1), to_bf16x4(mma16(to_bf16x4(N10r), to_bf16x4(Xc0), zero4())), zero4());
+                // T_b = T Diag(beta): T00 and T10 from column forms (column i16), T11 from its row
+                // form (row 16 + i16, four adjacent columns)
+                const f32x4 bcol = ld<f32x4>(f32p(Lay::o_beta) + 16 + 4 * g4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ya[e] = A10[e] * bt[1];
-                    yb[e] = t00[e];
-                    za[e] = f32p(Lay::o_T)[SB + (4 * g4 + e) * 20 + i16];               // T11[i16][4 g4 + e]
+                for (int j = 0; j < 4; ++j) {
+                    put_tb(4 * g4 + j, i16, Xc0[j] * bt[0]);
+                    put_tb(16 + 4 * g4 + j, i16, T10c[j] * bt[0]);
                 }
-                const f32x4 Y = mma16_split(ya, yb);   // lane (c, g4): Y[4 g4 + j][c]
-                const float yv[4] = {Y[0], Y[1], Y[2], Y[3]};
-                const f32x4 T10 = mma16_split(za, yv);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put_tb(16 + 4 * g4 + j, i16, -T10[j] * bt[0]);
+                const f32x4 t11 = Xr1 * bcol;
+                bf16* tr = bfp(Lay::o_Tb) + (16 + i16) * TB + pm(16 + 4 * g4);
+                if constexpr (kFull) {
+                    bf16x4 hv, lv;
+                    split4(t11, hv, lv);
+                    st<bf16x4>(tr, hv);
+                    st<bf16x4>(tr + kC * TB, lv);
+                } else {
+                    st<bf16x4>(tr, to_bf16x4(t11));
+                }
             } else {
                 // A_qk tile m (masked) -> split bf16 [row][pm(col)]
                 const int m = cw - 1;   // 0: rows 0-15 x cols 0-15, 1: 16-31 x 16-31, 2: 16-31 x 0-15
