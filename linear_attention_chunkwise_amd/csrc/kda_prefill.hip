@@ -754,6 +754,9 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                     n1[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 1) * 20 + 4 * g4);
                     n2[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 2) * 20 + 4 * g4);
                     n3[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 3) * 20 + 4 * g4);
+                    pin(n1[q]);   // whole rows in separate registers, read together
+                    pin(n2[q]);
+                    pin(n3[q]);
                 }
                 const bool on_diag = g4 == rb;                 // this lane's 4-block holds D entries
                 const int kk = lid & 3;
