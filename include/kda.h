@@ -66,6 +66,26 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          kda_dtype in_dtype, kda_dtype out_dtype, float scale,
                          void* o, float* S_T, hipStream_t stream);
 
+/* kda_chunk_fwd that also emits prefix states (§5.4.1: the recurrent state of a prefix is what a
+ * prefix cache stores and reuses; a chunkwise prefill already holds it at chunk ends).
+ *
+ * Same arguments and results as kda_chunk_fwd, plus: after every `ckpt_interval` tokens of a
+ * sequence (a positive multiple of 32, the chunk length), the state after those tokens is written
+ * to ckpt[n, h, j] for the j-th interval end (j = 0, 1, ...), as long as j < ckpt_capacity.
+ * Layout: ckpt [N, H, ckpt_capacity, dk, dv] float32, caller-owned, 16-byte aligned.  Only whole
+ * intervals are emitted: a sequence of length L yields min(floor(L / ckpt_interval),
+ * ckpt_capacity) states (the last one equals S_T when L is a multiple of the interval); slots past
+ * that are left untouched.  ckpt must not overlap o, S0 or S_T.  ckpt_capacity = 0 (ckpt may then
+ * be NULL) behaves exactly as kda_chunk_fwd.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED (interval not a positive multiple
+ * of 32, or an unsupported shape) or KDA_ERR_HIP. */
+kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* g,
+                              const void* beta, const float* S0, const int32_t* cu_seqlens,
+                              int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
+                              kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
+                              float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity, float* ckpt,
+                              hipStream_t stream);
+
 /* One decode token per (sequence, head), state updated IN PLACE (§5.4.2: at decode the state is
  * advanced in place every step and its traffic dominates).  eq. (1) with T = 1:
  *

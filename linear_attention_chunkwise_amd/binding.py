@@ -19,8 +19,8 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_RANGE, KDA_ERR_HI
 KDA_BF16, KDA_F32 = 0, 1
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_chunk_fwd", "kda_recurrent_step", "kda_status_string", "kda_last_error",
-           "kda_version")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_recurrent_step", "kda_status_string",
+           "kda_last_error", "kda_version")
 
 _lib = None
 
@@ -44,6 +44,10 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_ckpt.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, i32, i32,
+                                       vp, vp]
+    lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_step.restype = ctypes.c_int
@@ -129,6 +133,50 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, scale: float = 1.0,
                            N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T), _stream(dev))
     _check(st)
     return o, S_T
+
+
+def chunk_fwd_ckpt(q, k, v, g, beta, S0=None, cu_seqlens=None, *, interval: int, capacity: int,
+                   scale: float = 1.0, out_dtype=None, output_final_state: bool = True, o=None,
+                   S_T=None, ckpt=None):
+    """chunk_fwd that also returns the prefix states after every ``interval`` tokens (a multiple
+    of 32) of each sequence: ckpt [N,H,capacity,dk,dv] float32, slot j = state after
+    (j+1)*interval tokens; slots past a sequence's last whole interval are left as allocated
+    (zeros when ckpt is created here).  Returns (o, S_T, ckpt)."""
+    lib = load()
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dev, dt)
+    _require(k, "k", dev, dt, (B, T, H, dk))
+    _require(v, "v", dev, dt, (B, T, H, dv))
+    _require(g, "g", dev, torch.float32, (B, T, H, dk))
+    _require(beta, "beta", dev, dt, (B, T, H))
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
+    out_dtype = out_dtype or dt
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _require(o, "o", dev, out_dtype, (B, T, H, dv))
+    if S_T is None and output_final_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
+    if ckpt is None:
+        ckpt = torch.zeros((N, H, capacity, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _require(ckpt, "ckpt", dev, torch.float32, (N, H, capacity, dk, dv))
+    st = lib.kda_chunk_fwd_ckpt(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(cu_seqlens), B, T,
+                                H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
+                                int(interval), int(capacity), _p(ckpt), _stream(dev))
+    _check(st)
+    return o, S_T, ckpt
 
 
 def recurrent_step(q, k, v, g, beta, S, *, scale: float = 1.0, out_dtype=None, o=None):

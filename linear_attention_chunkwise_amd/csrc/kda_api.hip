@@ -76,11 +76,12 @@ const char* kda_status_string(kda_status s) {
 
 const char* kda_last_error(void) { return g_last_error; }
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
-                         const void* beta, const float* S0, const int32_t* cu_seqlens,
-                         int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
-                         kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
-                         float* S_T, hipStream_t stream) {
+static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g,
+                                 const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                 int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
+                                 kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
+                                 float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity,
+                                 float* ckpt, hipStream_t stream) {
     KDA_TRY(check_dtype(in_dtype, "in_dtype"));
     KDA_TRY(check_dtype(out_dtype, "out_dtype"));
     if (B < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "B", B);
@@ -126,11 +127,46 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
         if (tokens > 0 && overlaps(S_T, nst, o, nv * dsize(out_dtype)))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps o%.0lld", "S_T");
     }
+    if (ckpt_capacity < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "ckpt_capacity", ckpt_capacity);
+    const size_t nck = (size_t)N * H * (size_t)ckpt_capacity * dk * dv * 4;
+    if (ckpt_capacity > 0) {
+        if (ckpt_interval < 1 || ckpt_interval % 32 != 0)
+            return fail(KDA_ERR_UNSUPPORTED, "%s = %lld: checkpoints sit on 32-token chunk ends (a positive multiple of 32)",
+                        "ckpt_interval", ckpt_interval);
+        KDA_TRY(check_ptr(ckpt, 16, "ckpt"));
+        if (tokens > 0 && overlaps(ckpt, nck, o, nv * dsize(out_dtype)))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps o%.0lld", "ckpt");
+        if (S_T && overlaps(ckpt, nck, S_T, nst))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S_T%.0lld", "ckpt");
+        if (S0 && overlaps(ckpt, nck, S0, nst))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S0%.0lld", "ckpt");
+    }
     if (N == 0) return ok();
 
     kda::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, T, H, N, dk, dv,
-                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T, stream};
+                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T,
+                       ckpt_capacity > 0 ? ckpt : nullptr, ckpt_interval / 32, ckpt_capacity, stream};
     return hip_status(kda::launch_chunk_fwd(a));
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const void* beta, const float* S0, const int32_t* cu_seqlens,
+                         int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
+                         kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
+                         float* S_T, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
+                          scale, o, S_T, 0, 0, nullptr, stream);
+}
+
+kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* g,
+                              const void* beta, const float* S0, const int32_t* cu_seqlens,
+                              int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
+                              kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
+                              float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity, float* ckpt,
+                              hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
+                          scale, o, S_T, ckpt_interval, ckpt_capacity, ckpt, stream);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,

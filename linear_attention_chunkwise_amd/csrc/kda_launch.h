@@ -20,6 +20,9 @@ struct PrefillArgs {
     float scale;
     void* o;
     float* ST;                // may be null
+    float* ckpt;              // may be null: [N, H, ckpt_cap, dk, dv] states at interval ends
+    int32_t ckpt_every;       // checkpoint interval in 32-token chunks (>= 1 when ckpt is set)
+    int32_t ckpt_cap;         // checkpoints kept per (sequence, head)
     hipStream_t stream;
 };
 

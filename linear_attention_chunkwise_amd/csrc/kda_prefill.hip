@@ -707,6 +707,18 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 if constexpr (kFull) s = mma(kr[ct][1], Vh, s);
                 Sacc[ct] = s;
             }
+            // state checkpoint after every ckpt_every full chunks (prefix states for reuse)
+            if (a.ckpt && it % a.ckpt_every == 0 && it * kC <= len) {
+                const int64_t j = it / a.ckpt_every - 1;
+                if (j < a.ckpt_cap) {
+                    float* C = a.ckpt + (((size_t)n * H + h) * a.ckpt_cap + j) * DK * a.dv;
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            C[(size_t)(16 * ct + 4 * g4 + jj) * a.dv + col0 + i16] = Sacc[ct][jj];
+                }
+            }
         }
         __syncthreads();
 

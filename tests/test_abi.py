@@ -101,3 +101,35 @@ def test_recurrent_step_rejects_on_host(lib, kw, status):
 
 def test_empty_work_is_ok_without_touching_memory(lib):
     assert _step(lib, N=0, q=None, S=None) == binding.KDA_OK
+
+
+def _ckpt(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2, N=1,
+             dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None, every=32, cap=2,
+             ck=FAKE * 256)
+    a.update(kw)
+    return lib.kda_chunk_fwd_ckpt(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"],
+                                  a["B"], a["T"], a["H"], a["N"], a["dk"], a["dv"], a["ind"],
+                                  a["outd"], ctypes.c_float(a["scale"]), a["o"], a["ST"],
+                                  a["every"], a["cap"], a["ck"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(every=48), binding.KDA_ERR_UNSUPPORTED),                 # not a multiple of 32
+    (dict(every=0), binding.KDA_ERR_UNSUPPORTED),
+    (dict(cap=-1), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(ck=None), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(ck=FAKE * 256 + 8), binding.KDA_ERR_INVALID_ARGUMENT),   # misaligned
+    (dict(ck=FAKE * 8), binding.KDA_ERR_INVALID_ARGUMENT),         # overlaps o
+    (dict(ST=FAKE * 256), binding.KDA_ERR_INVALID_ARGUMENT),       # overlaps S_T
+    (dict(q=None), binding.KDA_ERR_INVALID_ARGUMENT),              # the plain checks still run
+])
+def test_chunk_fwd_ckpt_rejects_on_host(lib, kw, status):
+    assert _ckpt(lib, **kw) == status
+    assert lib.kda_last_error() != b""
+
+
+def test_chunk_fwd_ckpt_capacity_zero_needs_no_buffer(lib):
+    # capacity 0: the checkpoint arguments are not checked (bad interval, NULL buffer); with no
+    # sequences nothing is launched either
+    assert _ckpt(lib, cap=0, every=7, ck=None, B=1, N=0, cu=FAKE, T=0) == binding.KDA_OK

@@ -216,6 +216,61 @@ def test_workload_long_t1m(gpu_lib):
     _sampled_check(cfg, [(0, 0), (0, 19)])
 
 
+# ------------------------------------------------------------------ prefix checkpoints
+
+@pytest.mark.parametrize("interval,capacity", [(32, 40), (96, 5), (512, 3)])
+def test_checkpoints_match_prefix_states(gpu_lib, interval, capacity):
+    """Every emitted checkpoint equals the oracle's state after that many tokens of the same
+    sequence (varlen batch with ragged, short and empty sequences)."""
+    from linear_attention_chunkwise_amd import binding
+    lens = [0, 31, 32, 100, 1100, 517]
+    cu = inputs.cu_from_lengths(lens)
+    x = inputs.make_prefill_inputs(1, int(cu[-1]), 3, 128, 128, seed=11, cu_seqlens=cu)
+    d = _to_dev(x)
+    o, ST, ck = binding.chunk_fwd_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                       d["cu_seqlens"], interval=interval, capacity=capacity,
+                                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ck = ck.cpu().numpy()
+    o_plain, ST_plain = run_gpu(x, torch.float32)
+    np.testing.assert_array_equal(o.cpu().numpy(), o_plain)       # same launch path, bitwise
+    np.testing.assert_array_equal(ST.cpu().numpy(), ST_plain)
+    cuh = [int(c) for c in cu]
+    checked = 0
+    for n in range(len(lens)):
+        full = min(lens[n] // interval, capacity)
+        for j in range(capacity):
+            if j >= full:
+                assert not ck[n, :, j].any(), f"slot {j} of sequence {n} written"
+                continue
+            s, e = cuh[n], cuh[n] + (j + 1) * interval
+            sel = lambda t: t[:, s:e].contiguous()
+            _, rST = c_oracle.kda_units(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["g"]),
+                                        sel(x["beta"]), x["S0"][n:n + 1], None,
+                                        [(0, h) for h in range(3)])
+            for h in range(3):
+                assert_close(f"ckpt[n={n},j={j},h={h}]", ck[n, h, j], rST[h])
+            checked += 1
+    assert checked > 0
+
+
+def test_resume_from_checkpoint(gpu_lib):
+    """A prefill resumed from checkpoint j over the remaining tokens gives the same outputs and
+    final state as the single pass (prefix reuse)."""
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_prefill_inputs(2, 700, 2, 128, 128, seed=5)
+    d = _to_dev(x)
+    o, ST, ck = binding.chunk_fwd_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                       interval=256, capacity=2, out_dtype=torch.float32)
+    cut = 512
+    sl = lambda t: t[:, cut:].contiguous()
+    o2, ST2 = binding.chunk_fwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(d["beta"]),
+                                ck[:, :, 1].contiguous(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close("o[resumed]", o2.cpu().numpy(), o[:, cut:].cpu().numpy())
+    assert_close("S_T[resumed]", ST2.cpu().numpy(), ST.cpu().numpy())
+
+
 # ------------------------------------------------------------------ decode
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128), (64, 64)])
