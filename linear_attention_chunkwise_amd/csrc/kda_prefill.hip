@@ -42,9 +42,10 @@
 //
 // Precision: bf16 MFMA with fp32 accumulation.  Operands whose rounding would dominate the error
 // are carried as hi + lo bf16 pairs (products hi*hi + lo*hi + hi*lo): the decayed operands of
-// A_qk, A_qk itself, V - K~ S, V~ in both of its uses, and both operands of (Q * exp(G)) S,
-// which dominates short sequences entered with a large state.  A_kk, T_b, K~, K_end and the
-// state as the operand of K~ S are single bf16; the state stays fp32.  Float32 inputs (kFull)
+// A_qk, A_qk itself, V - K~ S, V~ in both of its uses, K_end (its rounding would dominate the
+// state's error), and both operands of (Q * exp(G)) S, which dominates short sequences entered
+// with a large state.  A_kk, T_b, K~ and the state as the operand of K~ S are single bf16; the
+// state stays fp32.  Float32 inputs (kFull)
 // carry every operand but A_kk's as a pair.  The scale on q is applied to the outputs
 // (everything is linear in q).
 #include <type_traits>
@@ -73,8 +74,8 @@ struct Layout {
     static constexpr int o_Aq = o_Tb + kNP * kC * TB * 2;     // bf16 hi, lo [C][TB]
     static constexpr int o_Kt = o_Aq + 2 * kC * TB * 2;       // bf16 planes [C][RB]: K~
     static constexpr int o_Qt = o_Kt + kNP * kC * RB * 2;     // bf16 hi, lo [C][RB]: Q~
-    static constexpr int o_Ke = o_Qt + 2 * kC * RB * 2;       // bf16 planes [DK][TB] (K_end^T)
-    static constexpr int o_gam = o_Ke + kNP * DK * TB * 2;    // fp32 [DK]
+    static constexpr int o_Ke = o_Qt + 2 * kC * RB * 2;       // bf16 hi, lo [DK][TB] (K_end^T)
+    static constexpr int o_gam = o_Ke + 2 * DK * TB * 2;      // fp32 [DK]
     static constexpr int o_beta = o_gam + DK * 4;             // fp32 [C]
     static constexpr int total = o_beta + kC * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
@@ -439,14 +440,12 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 #pragma unroll
                 for (int e = 0; e < 8; ++e) xe[e] = t ? Kd1[e] * F1[e] : Kc[e] * F1[e];
                 bf16x8 eh, el;
-                if constexpr (kFull) split8(xe, eh, el);
-                else eh = to_bf16x8(xe);
+                split8(xe, eh, el);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const f32x4 ke = mma(eh, Id[hh], zero4());
                     bf16* dst = bfp(Lay::o_Ke) + (32 * p + 16 * hh + i16) * TB + pm(16 * t + 4 * g4);
-                    st<bf16x4>(dst, to_bf16x4(ke));
-                    if constexpr (kFull) st<bf16x4>(dst + DK * TB, to_bf16x4(mma(el, Id[hh], zero4())));
+                    st<bf16x4>(dst, to_bf16x4(mma(eh, Id[hh], zero4())));          // exact: bf16 in
+                    st<bf16x4>(dst + DK * TB, to_bf16x4(mma(el, Id[hh], zero4())));
                 }
             }
         }
@@ -666,15 +665,37 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 }
                 Oacc[ta] = acc;
             }
-            // batch 3: rows of K_end^T and the chunk decay gamma
-            bf16x8 kr[CT][Lay::kNP];
-            f32x4 gm[CT];
+            // batch 3, in two halves (registers): rows of K_end^T (hi, lo) and the chunk decay
+            // gamma for state tiles [0, CT/2), then [CT/2, CT)
+            constexpr int CH = CT / 2;
+            bf16x8 kr[CH][2];
+            f32x4 gm[CH];
+            auto load_half = [&](int c0h) {
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
+                for (int c = 0; c < CH; ++c) {
 #pragma unroll
-                for (int pl = 0; pl < Lay::kNP; ++pl) kr[ct][pl] = frag(Lay::o_Ke + pl * DK * TB * 2, 16 * ct + i16, TB, 0);
-                gm[ct] = ld<f32x4>(f32p(Lay::o_gam) + 16 * ct + 4 * g4);
-            }
+                    for (int pl = 0; pl < 2; ++pl) kr[c][pl] = frag(Lay::o_Ke + pl * DK * TB * 2, 16 * (c0h + c) + i16, TB, 0);
+                    gm[c] = ld<f32x4>(f32p(Lay::o_gam) + 16 * (c0h + c) + 4 * g4);
+                }
+            };
+            // state: S <- Diag(gamma_last) S + K_end^T V~ on tiles [c0h, c0h + CH)
+            auto update_half = [&](int c0h) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    pin(kr[c][0]);
+                    pin(kr[c][1]);
+                    pin(gm[c]);
+                }
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    f32x4 st = Sacc[c0h + c] * gm[c];
+                    st = mma(kr[c][0], Vh, st);
+                    st = mma(kr[c][0], Vl, st);
+                    st = mma(kr[c][1], Vh, st);
+                    Sacc[c0h + c] = st;
+                }
+            };
+            load_half(0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta) {
@@ -692,31 +713,22 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                                                               off_o[ta][j], 0, 0);
                 }
             }
-            // state: S <- Diag(gamma_last) S + K_end^T V~
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-                for (int pl = 0; pl < Lay::kNP; ++pl) pin(kr[ct][pl]);
-                pin(gm[ct]);
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                f32x4 s = Sacc[ct] * gm[ct];
-                s = mma(kr[ct][0], Vh, s);
-                s = mma(kr[ct][0], Vl, s);
-                if constexpr (kFull) s = mma(kr[ct][1], Vh, s);
-                Sacc[ct] = s;
-            }
+            update_half(0);
+            load_half(CH);
+            update_half(CH);
             // state checkpoint after every ckpt_every full chunks (prefix states for reuse)
             if (a.ckpt && it % a.ckpt_every == 0 && it * kC <= len) {
                 const int64_t j = it / a.ckpt_every - 1;
                 if (j < a.ckpt_cap) {
                     float* C = a.ckpt + (((size_t)n * H + h) * a.ckpt_cap + j) * DK * a.dv;
+                    // 32-bit lane offset, opaque so that the 32 store addresses are formed here
+                    // rather than hoisted out of the chunk loop into registers
+                    int lo = 4 * g4 * a.dv + col0 + i16;
+                    asm volatile("" : "+v"(lo));
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj)
-                            C[(size_t)(16 * ct + 4 * g4 + jj) * a.dv + col0 + i16] = Sacc[ct][jj];
+                        for (int jj = 0; jj < 4; ++jj) C[lo + (16 * ct + jj) * a.dv] = Sacc[ct][jj];
                 }
             }
         }
