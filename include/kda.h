@@ -86,6 +86,38 @@ kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const
                               float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity, float* ckpt,
                               hipStream_t stream);
 
+/* Bytes of workspace kda_chunk_fwd_cp needs: N * (segments - 1) * H * dk * (dv + dk) * 4 (the
+ * summaries below), 0 when segments <= 1 or a size is not positive. */
+size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                       int32_t segments);
+
+/* kda_chunk_fwd with each sequence split in time into `segments` pieces that run in parallel:
+ * the in-device context parallelism of §5.1.1 for long prefill with few heads, built on the
+ * decomposition of §5.1.2, eq. (17): the state after a segment is M S_in + S~, with M the product
+ * of the segment's per-token transitions (I - beta k k^T) Diag(exp(g)) and S~ the segment's state
+ * when entered with zero.  For few, long sequences (N * H small) this puts more of the GPU to
+ * work: two passes of T / segments tokens each instead of one pass of T.
+ *
+ * Segment length: ceil(T / segments) rounded up to a multiple of 32; with cu_seqlens each
+ * sequence is split at the same offsets from its own start (pieces past its end are empty).
+ * Pass 1 writes, for every sequence, head and segment but the last, [S~ | M] (dk x (dv + dk),
+ * float32; segment 0 is entered with S0) to `workspace`; pass 2 rebuilds each segment's entering
+ * state S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1} and produces its outputs.  Same results as
+ * kda_chunk_fwd within the operator's tolerance (the summaries are computed with the same
+ * arithmetic; the combination uses split bf16 products with float32 accumulation).
+ *
+ * workspace: device memory of at least kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments)
+ * bytes, 16-byte aligned, caller-owned, overlapping none of o, S0, S_T; ignored (may be NULL)
+ * when segments == 1, which is exactly kda_chunk_fwd.  Other arguments as kda_chunk_fwd.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT (also: segments < 1, workspace too small, misaligned
+ * or overlapping), KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
+kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const float* g,
+                            const void* beta, const float* S0, const int32_t* cu_seqlens, int32_t B,
+                            int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
+                            kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
+                            float* S_T, int32_t segments, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* One decode token per (sequence, head), state updated IN PLACE (§5.4.2: at decode the state is
  * advanced in place every step and its traffic dominates).  eq. (1) with T = 1:
  *

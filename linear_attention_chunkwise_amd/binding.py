@@ -19,8 +19,8 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_RANGE, KDA_ERR_HI
 KDA_BF16, KDA_F32 = 0, 1
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_recurrent_step", "kda_status_string",
-           "kda_last_error", "kda_version")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_cp", "kda_chunk_fwd_cp_workspace_size",
+           "kda_recurrent_step", "kda_status_string", "kda_last_error", "kda_version")
 
 _lib = None
 
@@ -48,6 +48,12 @@ def load(path: str = LIB_PATH):
                                        ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, i32, i32,
                                        vp, vp]
     lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
+    lib.kda_chunk_fwd_cp.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, i32, vp,
+                                     ctypes.c_size_t, vp]
+    lib.kda_chunk_fwd_cp.restype = ctypes.c_int
+    lib.kda_chunk_fwd_cp_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.kda_chunk_fwd_cp_workspace_size.restype = ctypes.c_size_t
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_step.restype = ctypes.c_int
@@ -177,6 +183,61 @@ def chunk_fwd_ckpt(q, k, v, g, beta, S0=None, cu_seqlens=None, *, interval: int,
                                 int(interval), int(capacity), _p(ckpt), _stream(dev))
     _check(st)
     return o, S_T, ckpt
+
+
+def cp_segments(n_units: int, dk: int, dv: int, slots: int = 256) -> int:
+    """Largest segment count whose two passes each fit ``slots`` workgroups (one per CU): pass 1
+    runs (dv + dk) / 64 column slices for every segment but the first and the last (dv / 64 for
+    the first), pass 2 runs dv / 64 slices for every segment."""
+    best = 1
+    for p in range(2, 65):
+        pass1 = n_units * (dv // 64 + (p - 2) * (dv + dk) // 64)
+        pass2 = n_units * p * (dv // 64)
+        if pass1 > slots or pass2 > slots:
+            break
+        best = p
+    return best
+
+
+def chunk_fwd_cp(q, k, v, g, beta, S0=None, cu_seqlens=None, *, segments: int, scale: float = 1.0,
+                 out_dtype=None, output_final_state: bool = True, o=None, S_T=None, workspace=None):
+    """chunk_fwd with each sequence split in time into ``segments`` pieces run in parallel
+    (workspace allocated here unless given as a uint8 device tensor).  Returns (o, S_T)."""
+    lib = load()
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dev, dt)
+    _require(k, "k", dev, dt, (B, T, H, dk))
+    _require(v, "v", dev, dt, (B, T, H, dv))
+    _require(g, "g", dev, torch.float32, (B, T, H, dk))
+    _require(beta, "beta", dev, dt, (B, T, H))
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
+    out_dtype = out_dtype or dt
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _require(o, "o", dev, out_dtype, (B, T, H, dv))
+    if S_T is None and output_final_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
+    need = lib.kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, int(segments))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_fwd_cp(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(cu_seqlens), B, T,
+                              H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
+                              int(segments), _p(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(dev))
+    _check(st)
+    return o, S_T
 
 
 def recurrent_step(q, k, v, g, beta, S, *, scale: float = 1.0, out_dtype=None, o=None):

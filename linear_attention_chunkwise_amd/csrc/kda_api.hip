@@ -81,7 +81,8 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                                  int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
                                  kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
                                  float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity,
-                                 float* ckpt, hipStream_t stream) {
+                                 float* ckpt, int32_t segments, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
     KDA_TRY(check_dtype(in_dtype, "in_dtype"));
     KDA_TRY(check_dtype(out_dtype, "out_dtype"));
     if (B < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "B", B);
@@ -142,11 +143,38 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         if (S0 && overlaps(ckpt, nck, S0, nst))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S0%.0lld", "ckpt");
     }
+    int64_t seg_len = 0;
+    if (segments < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "segments", segments);
+    if (segments > 1) {
+        if (ckpt_capacity > 0)
+            return fail(KDA_ERR_UNSUPPORTED, "%s: checkpoints are not emitted by segmented runs%.0lld", "segments");
+        // segment length: the whole row split evenly, rounded up to whole 32-token chunks
+        seg_len = ((T + segments - 1) / segments + 31) / 32 * 32;
+        if (seg_len == 0) seg_len = 32;
+        const size_t need = kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments);
+        if (workspace_bytes < need)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %lld bytes given, kda_chunk_fwd_cp_workspace_size asks for more",
+                        "workspace_bytes", (long long)workspace_bytes);
+        KDA_TRY(check_ptr(workspace, 16, "workspace"));
+        if ((tokens > 0 && overlaps(workspace, need, o, nv * dsize(out_dtype))) ||
+            (S_T && overlaps(workspace, need, S_T, nst)) || (S0 && overlaps(workspace, need, S0, nst)))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps o, S0 or S_T%.0lld", "workspace");
+    }
     if (N == 0) return ok();
 
     kda::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, T, H, N, dk, dv,
                        in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T,
-                       ckpt_capacity > 0 ? ckpt : nullptr, ckpt_interval / 32, ckpt_capacity, stream};
+                       ckpt_capacity > 0 ? ckpt : nullptr, ckpt_interval / 32, ckpt_capacity,
+                       /*mode*/ 0, /*nseg*/ 1, /*seg_len*/ 0, /*ws*/ nullptr, stream};
+    if (segments <= 1) return hip_status(kda::launch_chunk_fwd(a));
+    // segmented: summaries of all but the last segment, then every segment's outputs
+    a.nseg = segments;
+    a.seg_len = seg_len;
+    a.ws = static_cast<float*>(workspace);
+    a.mode = 1;
+    const hipError_t e = kda::launch_chunk_fwd(a);
+    if (e != hipSuccess) return hip_status(e);
+    a.mode = 2;
     return hip_status(kda::launch_chunk_fwd(a));
 }
 
@@ -156,7 +184,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
                          float* S_T, hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
-                          scale, o, S_T, 0, 0, nullptr, stream);
+                          scale, o, S_T, 0, 0, nullptr, 1, nullptr, 0, stream);
 }
 
 kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* g,
@@ -166,7 +194,22 @@ kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const
                               float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity, float* ckpt,
                               hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
-                          scale, o, S_T, ckpt_interval, ckpt_capacity, ckpt, stream);
+                          scale, o, S_T, ckpt_interval, ckpt_capacity, ckpt, 1, nullptr, 0, stream);
+}
+
+size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t segments) {
+    if (N < 1 || H < 1 || dk < 1 || dv < 1 || segments <= 1) return 0;
+    return (size_t)N * (size_t)(segments - 1) * H * dk * (size_t)(dv + dk) * 4;
+}
+
+kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const float* g,
+                            const void* beta, const float* S0, const int32_t* cu_seqlens, int32_t B,
+                            int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
+                            kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
+                            float* S_T, int32_t segments, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
+                          scale, o, S_T, 0, 0, nullptr, segments, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,

@@ -23,6 +23,17 @@ struct PrefillArgs {
     float* ckpt;              // may be null: [N, H, ckpt_cap, dk, dv] states at interval ends
     int32_t ckpt_every;       // checkpoint interval in 32-token chunks (>= 1 when ckpt is set)
     int32_t ckpt_cap;         // checkpoints kept per (sequence, head)
+    // Segmented (context-parallel) runs over nseg time segments of seg_len tokens per sequence:
+    //   mode 0: plain prefill (nseg, seg_len, ws unused);
+    //   mode 1: segment summaries: for segments j < nseg - 1 the state after the segment,
+    //           entered with S0 (j = 0) or 0, and the segment's transition (extra dk columns
+    //           entered with the identity, value 0) -> ws;
+    //   mode 2: outputs: each segment rebuilds its entering state from the summaries of the
+    //           segments before it, then runs as mode 0 (the last one writes S_T).
+    int32_t mode;
+    int32_t nseg;
+    int64_t seg_len;          // multiple of 32
+    float* ws;                // [N, nseg - 1, H, dk, dv + dk] float32 (modes 1, 2)
     hipStream_t stream;
 };
 

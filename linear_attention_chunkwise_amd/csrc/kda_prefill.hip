@@ -459,7 +459,7 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 // (cw = 0) or one A_qk tile (cw = 1..3).
 template <int DK, bool F32IN, bool OUT_F32>
 __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
-                                         int64_t row0, int64_t len, int n, int h, int slice) {
+                                         int64_t row0, int64_t len, int n, int h, int slice, int seg) {
     using Lay = Layout<DK, F32IN>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr bool kFull = Lay::kFull;
@@ -473,7 +473,9 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     const int H = a.H;
     const size_t sv = (size_t)H * a.dv;        // token stride of v, o
     const int col0 = slice * kDVT + 16 * cw;   // first value column of this wave
-    const bool vlane = g4 < 2;                 // lanes that load this wave's 16 v columns
+    // segment summaries: columns >= dv carry the segment's transition (value 0); no outputs
+    const bool tcols = a.mode == 1 && col0 >= a.dv;
+    const bool vlane = g4 < 2 && !tcols;       // lanes that load this wave's 16 v columns
 
     const IT* vh = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv + col0;
     using OT = typename std::conditional<OUT_F32, float, bf16>::type;
@@ -492,7 +494,51 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     f32x4 Sacc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();
-    if (a.S0) {
+    const int wcols = a.dv + DK;   // row length of a segment summary [dk][dv + dk]
+    auto summary = [&](int j) {    // summary of segment j of this (sequence, head)
+        return a.ws + (((size_t)n * (a.nseg - 1) + j) * H + h) * DK * wcols;
+    };
+    if (tcols) {
+        // transition columns start as the identity
+        const int c = col0 - a.dv + i16;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Sacc[ct][j] = (16 * ct + 4 * g4 + j == c) ? 1.f : 0.f;
+    } else if (a.mode == 2 && seg > 0) {
+        // entering state of segment seg: the state after segment 0 (entered with S0), carried
+        // through segments 1 .. seg-1 by S <- M_j S + S~_j (products on split bf16 operands)
+        const float* W0 = summary(0);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Sacc[ct][j] = W0[(size_t)(16 * ct + 4 * g4 + j) * wcols + col0 + i16];
+        for (int jseg = 1; jseg < seg; ++jseg) {
+            const float* Wj = summary(jseg);
+            bf16x8 Sh[KS], Sl[KS];
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) acc_pair_split(Sacc[2 * s2], Sacc[2 * s2 + 1], Sh[s2], Sl[s2]);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                f32x4 acc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = Wj[(size_t)(16 * ct + 4 * g4 + j) * wcols + col0 + i16];
+                // A operand: row 16 ct + i16 of M_j, contraction positions of the B operand
+                const float* Mr = Wj + (size_t)(16 * ct + i16) * wcols + a.dv;
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) {
+                    const f32x4 m0 = ld<f32x4>(Mr + 32 * s2 + 4 * g4);
+                    const f32x4 m1 = ld<f32x4>(Mr + 32 * s2 + 16 + 4 * g4);
+                    bf16x8 mh, ml;
+                    acc_pair_split(m0, m1, mh, ml);
+                    acc = mma(mh, Sh[s2], acc);
+                    acc = mma(ml, Sh[s2], acc);
+                    acc = mma(mh, Sl[s2], acc);
+                }
+                Sacc[ct] = acc;
+            }
+        }
+    } else if (a.S0 && !(a.mode == 1 && seg > 0)) {
         const float* S0 = a.S0 + ((size_t)n * H + h) * DK * a.dv;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -550,8 +596,9 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         // at its first use (without this each MFMA waits for its own read).
         if (it > 0) {
             const int64_t c0 = (it - 1) * kC;
-            const uint32_t nvalid = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
+            const uint32_t nvalid = a.mode == 1 ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
             // output rows of the chunk: stores at or past row nvalid fall outside the resource
+            // (summaries write no outputs)
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob + (size_t)c0 * sv, nvalid * (uint32_t)(sv * sizeof(OT)));
             // operand fragments read from [row][pm(index)] storage: elements 4 g4 + e (e < 4) and
             // 16 + 4 g4 + e - 4 (e >= 4) of each 32-long contraction step are one 16-byte read
@@ -855,7 +902,13 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         __syncthreads();
     }
 
-    if (a.ST) {
+    if (a.mode == 1) {
+        float* W = summary(seg);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) W[(size_t)(16 * ct + 4 * g4 + j) * wcols + col0 + i16] = Sacc[ct][j];
+    } else if (a.ST && (a.mode == 0 || seg == a.nseg - 1)) {
         float* ST = a.ST + ((size_t)n * H + h) * DK * a.dv;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -869,17 +922,27 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
 template <int DK, bool F32IN, bool OUT_F32>
 __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int nslices = a.dv / kDVT;
+    const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
+    const int nseg = a.mode == 0 ? 1 : a.nseg;
     int unit, slice;
     block_coords(nslices, unit, slice);
-    if (unit >= a.N * a.H) return;
-    const int n = unit / a.H, h = unit % a.H;
+    if (unit >= a.N * a.H * nseg) return;
+    const int h = unit % a.H;
+    const int seg = (unit / a.H) % nseg;
+    const int n = unit / (a.H * nseg);
+    if (a.mode == 1 && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;   // not needed
     int64_t row0, len;
     seq_bounds(a, n, row0, len);
+    if (a.mode != 0) {   // this segment's tokens
+        const int64_t lo = (int64_t)seg * a.seg_len;
+        const int64_t hi = lo + a.seg_len < len ? lo + a.seg_len : len;
+        row0 += lo;
+        len = hi > lo ? hi - lo : 0;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     if (wave < kNW) producer<DK, F32IN>(a, smem, wave, lane, row0, len, h);
-    else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice);
+    else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg);
 }
 
 template <int DK, bool F32IN, bool OUT_F32>
@@ -893,8 +956,8 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int nslices = a.dv / kDVT;
-    const int64_t units = (int64_t)a.N * a.H;
+    const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
+    const int64_t units = (int64_t)a.N * a.H * (a.mode == 0 ? 1 : a.nseg);
     const int64_t blocks = ((units + 7) / 8) * 8 * nslices;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kNT), Lay::total, a.stream, a);

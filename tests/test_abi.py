@@ -133,3 +133,41 @@ def test_chunk_fwd_ckpt_capacity_zero_needs_no_buffer(lib):
     # capacity 0: the checkpoint arguments are not checked (bad interval, NULL buffer); with no
     # sequences nothing is launched either
     assert _ckpt(lib, cap=0, every=7, ck=None, B=1, N=0, cu=FAKE, T=0) == binding.KDA_OK
+
+
+def test_cp_workspace_size(lib):
+    assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 3) == 1 * 2 * 32 * 128 * 256 * 4
+    assert lib.kda_chunk_fwd_cp_workspace_size(2, 4, 64, 128, 4) == 2 * 3 * 4 * 64 * 192 * 4
+    assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 1) == 0
+    assert lib.kda_chunk_fwd_cp_workspace_size(0, 32, 128, 128, 3) == 0
+
+
+def _cp(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2, N=1,
+             dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None, segs=2, ws=FAKE * 256,
+             wsb=1 << 30)
+    a.update(kw)
+    return lib.kda_chunk_fwd_cp(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"],
+                                a["T"], a["H"], a["N"], a["dk"], a["dv"], a["ind"], a["outd"],
+                                ctypes.c_float(a["scale"]), a["o"], a["ST"], a["segs"], a["ws"],
+                                a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(segs=0), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(wsb=1024), binding.KDA_ERR_INVALID_ARGUMENT),            # workspace too small
+    (dict(ws=None), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(ws=FAKE * 256 + 4), binding.KDA_ERR_INVALID_ARGUMENT),   # misaligned
+    (dict(ws=FAKE * 8), binding.KDA_ERR_INVALID_ARGUMENT),         # overlaps o
+    (dict(dk=96), binding.KDA_ERR_UNSUPPORTED),                    # the plain checks still run
+])
+def test_chunk_fwd_cp_rejects_on_host(lib, kw, status):
+    assert _cp(lib, **kw) == status
+    assert lib.kda_last_error() != b""
+
+
+def test_cp_segment_count_helper():
+    # 32 units of d = 128: pass 1 = 32 * (2 + 4 (p - 2)), pass 2 = 32 * 2 p, both <= 256
+    assert binding.cp_segments(32, 128, 128) == 3
+    assert binding.cp_segments(16, 128, 128) == 5
+    assert binding.cp_segments(256, 128, 128) == 1

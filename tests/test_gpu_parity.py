@@ -271,6 +271,98 @@ def test_resume_from_checkpoint(gpu_lib):
     assert_close("S_T[resumed]", ST2.cpu().numpy(), ST.cpu().numpy())
 
 
+# ------------------------------------------------------------------ segmented (context-parallel) runs
+
+@pytest.mark.parametrize("segments", [2, 3, 5])
+@pytest.mark.parametrize("with_s0", [True, False], ids=["S0", "noS0"])
+def test_segmented_matches_oracle_and_plain(gpu_lib, segments, with_s0):
+    """Outputs and final states of the segmented run against the oracle (and within a small
+    tolerance of the plain run), on a ragged length."""
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_prefill_inputs(2, 1000, 3, 128, 128, seed=21 + segments)
+    if not with_s0:
+        x["S0"] = None
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                 segments=segments, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rST = oracle_all(x)
+    assert_close("o[cp]", o.cpu().numpy(), ro)
+    assert_close("S_T[cp]", ST.cpu().numpy(), rST)
+    op, STp = run_gpu(x, torch.float32)
+    assert_close("o[cp vs plain]", o.cpu().numpy(), op)
+    assert_close("S_T[cp vs plain]", ST.cpu().numpy(), STp)
+
+
+@pytest.mark.parametrize("segments", [2, 4])
+def test_segmented_weak_decay_carries_state(gpu_lib, segments):
+    """With weak decay the entering state of a segment matters (its transition M is far from
+    zero), so the combination S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1} is exercised."""
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_prefill_inputs(1, 900, 2, 128, 128, seed=41)
+    x["g"] = x["g"] * 0.002                      # per-token log-decay ~ -0.005
+    x["beta"] = (x["beta"].float() * 0.25).to(x["beta"].dtype)
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                 segments=segments, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rST = oracle_all(x)
+    assert_close("o[cp weak decay]", o.cpu().numpy(), ro)
+    assert_close("S_T[cp weak decay]", ST.cpu().numpy(), rST)
+    op, _ = run_gpu(x, torch.float32)
+    # the combination path differs from the single pass in rounding only
+    diff = np.abs(o.cpu().numpy() - op).max()
+    print(f"  max |o_cp - o_plain| = {diff:.3e}", flush=True)
+
+
+def test_segmented_varlen_and_dk64(gpu_lib):
+    """Varlen batch (segments past a sequence's end are empty) and the d = 64 float32-input
+    kernel, segmented."""
+    from linear_attention_chunkwise_amd import binding
+    lens = [0, 33, 700, 1, 300]
+    cu = inputs.cu_from_lengths(lens)
+    x = inputs.make_prefill_inputs(1, int(cu[-1]), 2, 128, 128, seed=31, cu_seqlens=cu)
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                 d["cu_seqlens"], segments=4, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rST = oracle_all(x)
+    assert_close("o[cp varlen]", o.cpu().numpy(), ro)
+    assert_close("S_T[cp varlen]", ST.cpu().numpy(), rST)
+    cfg = inputs.CONFIGS["tiny_fp32_t256_d64"]
+    x = inputs.make_config_inputs(cfg, seed=0)
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                 segments=3, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rST = oracle_all(x)
+    assert_close("o[cp d64 f32]", o.cpu().numpy(), ro)
+    assert_close("S_T[cp d64 f32]", ST.cpu().numpy(), rST)
+
+
+@pytest.mark.slow
+def test_workload_long_t1m_segmented(gpu_lib):
+    """The 1M-token workload through the segmented path (segment count from the helper), sampled
+    units against the oracle over the whole sequence."""
+    from linear_attention_chunkwise_amd import binding
+    cfg = inputs.CONFIGS["long_b1_h32_t1m_d128"]
+    x = inputs.make_config_inputs(cfg, seed=0, device="cuda")
+    P = binding.cp_segments(cfg.B * cfg.H, cfg.dk, cfg.dv)
+    assert P > 1
+    o, ST = binding.chunk_fwd_cp(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], segments=P)
+    torch.cuda.synchronize()
+    for h in (0, 19):
+        sel = lambda t: t[0:1, :, h:h + 1].contiguous().cpu()
+        print(f"  unit n=0 h={h} tokens={cfg.T} segments={P}", flush=True)
+        outs, rST = c_oracle.kda_units(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["g"]),
+                                       sel(x["beta"]), x["S0"][0:1, h:h + 1].contiguous().cpu(), None,
+                                       [(0, 0)])
+        assert_close(f"o[cp n=0,h={h}]", o[0, :, h].float().cpu().numpy(), outs[0])
+        assert_close(f"S_T[cp n=0,h={h}]", ST[0, h].cpu().numpy(), rST[0])
+    del x, o, ST
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ decode
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128), (64, 64)])
