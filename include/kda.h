@@ -131,6 +131,24 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
                               void* o, hipStream_t stream);
 
+/* K decode tokens per (sequence, head) with one pass over the state: the decode-side variant
+ * §5.4.2 describes for speculative decoding, where K drafted tokens are verified together and
+ * the accepted ones are then replayed from their cached projected inputs.  The state is read
+ * once, advanced through tokens 0..K-1 in registers (eq. (1) per token), and written back IN
+ * PLACE after the first n_commit[n] tokens of sequence n (n_commit NULL: all K; 0: the state is
+ * left untouched, e.g. a verification pass).  o receives every token's output, computed from the
+ * states after each token whether or not they are committed; o may be NULL (outputs not wanted,
+ * e.g. a replay pass).  n_commit values are clamped to [0, K].
+ *
+ * Layouts: q, k, g [N, K, H, dk]; v, o [N, K, H, dv]; beta [N, K, H]; S [N, H, dk, dv] float32;
+ * n_commit device int32 [N] or NULL.  o must not overlap S or any input.  Supported: dk, dv in
+ * {64, 128}.  K = 0 or N = 0 does nothing.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
+kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, const float* g,
+                               const void* beta, float* S, const int32_t* n_commit, int32_t N,
+                               int32_t K, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
+                               kda_dtype out_dtype, float scale, void* o, hipStream_t stream);
+
 /* Static description of a status code.  Never NULL. */
 const char* kda_status_string(kda_status status);
 

@@ -20,7 +20,8 @@ KDA_BF16, KDA_F32 = 0, 1
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_cp", "kda_chunk_fwd_cp_workspace_size",
-           "kda_recurrent_step", "kda_status_string", "kda_last_error", "kda_version")
+           "kda_recurrent_step", "kda_recurrent_multi", "kda_status_string", "kda_last_error",
+           "kda_version")
 
 _lib = None
 
@@ -57,6 +58,9 @@ def load(path: str = LIB_PATH):
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_recurrent_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp]
+    lib.kda_recurrent_multi.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -262,5 +266,36 @@ def recurrent_step(q, k, v, g, beta, S, *, scale: float = 1.0, out_dtype=None, o
         _require(o, "o", dev, out_dtype, (N, H, dv))
     st = lib.kda_recurrent_step(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), N, H, dk, dv, _dt(q),
                                 _dt(o), float(scale), _p(o), _stream(dev))
+    _check(st)
+    return o
+
+
+def recurrent_multi(q, k, v, g, beta, S, n_commit=None, *, scale: float = 1.0, out_dtype=None,
+                    o=None, outputs: bool = True):
+    """K decode tokens per (sequence, head) in one state pass; S [N,H,dk,dv] float32 is advanced
+    IN PLACE by n_commit[n] tokens (int32 device tensor [N]; None: all K).  q, k [N,K,H,dk],
+    v [N,K,H,dv], beta [N,K,H] share a dtype; g [N,K,H,dk] float32.  Returns o [N,K,H,dv]
+    (None with outputs=False)."""
+    lib = load()
+    dev = q.device
+    N, K, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dev, dt)
+    _require(k, "k", dev, dt, (N, K, H, dk))
+    _require(v, "v", dev, dt, (N, K, H, dv))
+    _require(g, "g", dev, torch.float32, (N, K, H, dk))
+    _require(beta, "beta", dev, dt, (N, K, H))
+    _require(S, "S", dev, torch.float32, (N, H, dk, dv))
+    if n_commit is not None:
+        _require(n_commit, "n_commit", dev, torch.int32, (N,))
+    out_dtype = out_dtype or dt
+    if outputs and o is None:
+        o = torch.empty((N, K, H, dv), dtype=out_dtype, device=dev)
+    elif o is not None:
+        _require(o, "o", dev, out_dtype, (N, K, H, dv))
+    st = lib.kda_recurrent_multi(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), _p(n_commit), N, K, H,
+                                 dk, dv, _dt(q), _dt(o) if o is not None else _dt(q), float(scale),
+                                 _p(o), _stream(dev))
     _check(st)
     return o

@@ -243,4 +243,45 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     return hip_status(kda::launch_decode_step(a));
 }
 
+kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, const float* g,
+                               const void* beta, float* S, const int32_t* n_commit, int32_t N,
+                               int32_t K, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
+                               kda_dtype out_dtype, float scale, void* o, hipStream_t stream) {
+    KDA_TRY(check_dtype(in_dtype, "in_dtype"));
+    KDA_TRY(check_dtype(out_dtype, "out_dtype"));
+    if (N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "N", N);
+    if (K < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "K", K);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "H", H);
+    if (!(dk == 64 || dk == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dk", dk);
+    if (!(dv == 64 || dv == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dv", dv);
+    if ((int64_t)N * H > (int64_t)1 << 30) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "N*H", (long long)N * H);
+    if (N == 0 || K == 0) return ok();
+    const size_t es = dsize(in_dtype);
+    KDA_TRY(check_ptr(q, 16, "q"));
+    KDA_TRY(check_ptr(k, 16, "k"));
+    KDA_TRY(check_ptr(v, 16, "v"));
+    KDA_TRY(check_ptr(g, 16, "g"));
+    KDA_TRY(check_ptr(beta, es, "beta"));
+    KDA_TRY(check_ptr(S, 16, "S"));
+    if (n_commit) KDA_TRY(check_ptr(n_commit, 4, "n_commit"));
+    const size_t nh = (size_t)N * H, nt = nh * (size_t)K;
+    if (o) {
+        KDA_TRY(check_ptr(o, 16, "o"));
+        const size_t no = nt * dv * dsize(out_dtype);
+        if (overlaps(o, no, S, nh * dk * dv * 4) || overlaps(o, no, q, nt * dk * es) ||
+            overlaps(o, no, k, nt * dk * es) || overlaps(o, no, v, nt * dv * es) ||
+            overlaps(o, no, g, nt * dk * 4) || overlaps(o, no, beta, nt * es))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps the state or an input%.0lld", "o");
+    }
+    if (n_commit && overlaps(n_commit, (size_t)N * 4, S, nh * dk * dv * 4))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S%.0lld", "n_commit");
+    kda::DecodeArgs a{q, k, v, g, beta, S, (int32_t)nh, dk, dv,
+                      in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, stream};
+    a.K = K;
+    a.N = N;
+    a.H = H;
+    a.n_commit = n_commit;
+    return hip_status(kda::launch_decode_step(a));
+}
+
 }  // extern "C"

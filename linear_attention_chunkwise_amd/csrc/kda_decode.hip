@@ -96,6 +96,99 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qp
     }
 }
 
+// Several tokens per (sequence, head) with the state read once (speculative verification and
+// replay of accepted tokens, §5.4.2): the state stays in registers across the K tokens; it is
+// written back after the first `commit` tokens (commit = 0: outputs only, state untouched).
+// Tokens are laid out [N, K, H, d]; the reductions use two LDS buffers by token parity, one
+// workgroup barrier per token.
+template <int DK, int DV, bool IN_F32, bool OUT_F32>
+__global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restrict__ qp,
+                                                           const void* __restrict__ kp,
+                                                           const void* __restrict__ vp,
+                                                           const float* __restrict__ g,
+                                                           const void* __restrict__ betap,
+                                                           float* __restrict__ S,
+                                                           const int32_t* __restrict__ n_commit,
+                                                           int32_t N, int32_t H, int32_t K,
+                                                           float scale, void* __restrict__ op) {
+    constexpr int CG = DV / 4;
+    constexpr int NRG = 256 / CG;
+    constexpr int RPG = DK / NRG;
+    static_assert(RPG >= 1 && DK % NRG == 0, "decode tiling");
+    __shared__ f32x4 red_y[2][NRG][CG];
+    __shared__ f32x4 red_z[2][NRG][CG];
+    __shared__ float red_qk[2][NRG];
+
+    const int unit = blockIdx.x;        // sequence * H + head
+    if (unit >= N * H) return;
+    const int n = unit / H, h = unit % H;
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    const int r0 = rg * RPG;
+    int commit = n_commit ? n_commit[n] : K;
+    commit = commit < 0 ? 0 : (commit > K ? K : commit);
+
+    float* Su = S + (size_t)unit * DK * DV;
+    f32x4 s[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) s[i] = ld<f32x4>(Su + (size_t)(r0 + i) * DV + 4 * cg);
+
+    auto in_at = [&](const void* p, size_t idx) -> float {
+        if constexpr (IN_F32) return reinterpret_cast<const float*>(p)[idx];
+        else return bf2f(reinterpret_cast<const bf16*>(p)[idx]);
+    };
+    for (int tok = 0; tok < K; ++tok) {
+        const int pb = tok & 1;
+        const size_t row = ((size_t)n * K + tok) * H + h;   // token row of [N, K, H, *]
+        const size_t kb = row * DK;
+        f32x4 y = zero4(), z = zero4();
+        float qk = 0.f;
+        float kv[RPG];
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) {
+            const float a = __expf(g[kb + r0 + i]);
+            kv[i] = in_at(kp, kb + r0 + i);
+            const float qv = in_at(qp, kb + r0 + i);
+            s[i] *= a;
+            y += kv[i] * s[i];
+            z += qv * s[i];
+            qk += qv * kv[i];
+        }
+        red_y[pb][rg][cg] = y;
+        red_z[pb][rg][cg] = z;
+        if (cg == 0) red_qk[pb][rg] = qk;
+        __syncthreads();   // the other parity's buffers were last read before this barrier
+        f32x4 yt = zero4(), zt = zero4();
+        float qkt = 0.f;
+#pragma unroll
+        for (int j = 0; j < NRG; ++j) {
+            yt += red_y[pb][j][cg];
+            zt += red_z[pb][j][cg];
+            qkt += red_qk[pb][j];
+        }
+        const float b = in_at(betap, row);
+        const size_t vb = row * DV + 4 * cg;
+        f32x4 u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) u[c] = b * (in_at(vp, vb + c) - yt[c]);
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) s[i] += kv[i] * u;
+        if (tok + 1 == commit) {
+#pragma unroll
+            for (int i = 0; i < RPG; ++i) st<f32x4>(Su + (size_t)(r0 + i) * DV + 4 * cg, s[i]);
+        }
+        if (op && rg == 0) {
+            const f32x4 o = scale * (zt + qkt * u);
+            if constexpr (OUT_F32) {
+                st<f32x4>(reinterpret_cast<float*>(op) + vb, o);
+            } else {
+                bf16x4 ob{f2bf(o[0]), f2bf(o[1]), f2bf(o[2]), f2bf(o[3])};
+                st<bf16x4>(reinterpret_cast<bf16*>(op) + vb, ob);
+            }
+        }
+    }
+}
+
 template <int DK, int DV, bool IN_F32, bool OUT_F32>
 static hipError_t launch_decode(const DecodeArgs& a) {
     if (a.NH == 0) return hipSuccess;
@@ -104,8 +197,21 @@ static hipError_t launch_decode(const DecodeArgs& a) {
     return hipGetLastError();
 }
 
+template <int DK, int DV, bool IN_F32, bool OUT_F32>
+static hipError_t launch_multi(const DecodeArgs& a) {
+    const int64_t units = (int64_t)a.N * a.H;
+    if (units == 0 || a.K == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IN_F32, OUT_F32>), dim3((unsigned)units), dim3(256), 0,
+                       a.stream, a.q, a.k, a.v, a.g, a.beta, a.S, a.n_commit, a.N, a.H, a.K, a.scale, a.o);
+    return hipGetLastError();
+}
+
 template <int DK, int DV>
 static hipError_t dispatch_io(const DecodeArgs& a) {
+    if (a.K > 0) {
+        if (a.in_f32) return a.out_f32 ? launch_multi<DK, DV, true, true>(a) : launch_multi<DK, DV, true, false>(a);
+        return a.out_f32 ? launch_multi<DK, DV, false, true>(a) : launch_multi<DK, DV, false, false>(a);
+    }
     if (a.in_f32) return a.out_f32 ? launch_decode<DK, DV, true, true>(a)
                                    : launch_decode<DK, DV, true, false>(a);
     return a.out_f32 ? launch_decode<DK, DV, false, true>(a) : launch_decode<DK, DV, false, false>(a);

@@ -49,6 +49,10 @@ struct DecodeArgs {
     float scale;
     void* o;
     hipStream_t stream;
+    // several tokens per (sequence, head) when K > 0: inputs [N, K, H, d], o [N, K, H, dv] or
+    // null, the state written after n_commit[n] tokens (null: all K)
+    int32_t K = 0, N = 0, H = 0;
+    const int32_t* n_commit = nullptr;
 };
 
 hipError_t launch_chunk_fwd(const PrefillArgs& a);

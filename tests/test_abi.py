@@ -171,3 +171,34 @@ def test_cp_segment_count_helper():
     assert binding.cp_segments(32, 128, 128) == 3
     assert binding.cp_segments(16, 128, 128) == 5
     assert binding.cp_segments(256, 128, 128) == 1
+
+
+def _multi(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S=FAKE * 16, nc=None, N=4, K=3, H=2,
+             dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 64)
+    a.update(kw)
+    return lib.kda_recurrent_multi(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["nc"],
+                                   a["N"], a["K"], a["H"], a["dk"], a["dv"], a["ind"], a["outd"],
+                                   ctypes.c_float(a["scale"]), a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=-1), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(N=-2), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dv=96), binding.KDA_ERR_UNSUPPORTED),
+    (dict(outd=5), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(beta=None), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(nc=FAKE + 2), binding.KDA_ERR_INVALID_ARGUMENT),         # misaligned n_commit
+    (dict(nc=FAKE * 16), binding.KDA_ERR_INVALID_ARGUMENT),        # n_commit overlaps S
+    (dict(o=FAKE * 16 + 64), binding.KDA_ERR_INVALID_ARGUMENT),    # o overlaps S
+    (dict(o=FAKE + 8), binding.KDA_ERR_INVALID_ARGUMENT),          # misaligned o
+])
+def test_recurrent_multi_rejects_on_host(lib, kw, status):
+    assert _multi(lib, **kw) == status
+    assert lib.kda_last_error() != b""
+
+
+def test_recurrent_multi_empty_work_is_ok(lib):
+    assert _multi(lib, K=0, q=None, S=None) == binding.KDA_OK
+    assert _multi(lib, N=0, q=None, S=None) == binding.KDA_OK

@@ -407,3 +407,87 @@ def test_decode_matches_prefill_t1(gpu_lib):
     torch.cuda.synchronize()
     assert_close("o", o1.cpu().numpy(), o2[:, 0].cpu().numpy())
     assert_close("S", S.cpu().numpy(), S2.cpu().numpy())
+
+
+# ------------------------------------------------------------------ multi-token decode
+
+def _oracle_multi(x, S, commits, scale=1.0):
+    """Outputs of all K tokens (the full forward from S) and, per sequence, the state after its
+    first commits[n] tokens (S itself for 0)."""
+    ro, _ = c_oracle.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S, None, scale)
+    rS = S.double().numpy().copy()
+    for n, c in enumerate(commits):
+        if c > 0:
+            sl = lambda t: t[n:n + 1, :c].contiguous()
+            _, s = c_oracle.kda_forward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]),
+                                        sl(x["beta"]), S[n:n + 1].contiguous(), None, scale)
+            rS[n] = s[0]
+    return ro, rS
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128), (64, 64)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["o_f32", "o_bf16"])
+def test_decode_multi_small(gpu_lib, dk, dv, out_dtype):
+    from linear_attention_chunkwise_amd import binding
+    N, K, H = 6, 5, 3
+    x = inputs.make_prefill_inputs(N, K, H, dk, dv, seed=dk + 2 * dv)
+    commits = [5, 0, 2, 1, 3, 9]          # 9 is clamped to K
+    S = x["S0"].clone().cuda()
+    d = _to_dev(x)
+    nc = torch.tensor(commits, dtype=torch.int32, device="cuda")
+    o = binding.recurrent_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], S, nc, scale=0.7,
+                                out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rS = _oracle_multi(x, x["S0"], [min(c, K) for c in commits], scale=0.7)
+    assert_close("o", o.float().cpu().numpy(), ro)
+    assert_close("S", S.cpu().numpy(), rS)
+    assert torch.equal(S[1].cpu(), x["S0"][1])           # commit 0 leaves the state untouched
+
+
+def test_decode_multi_state_only_all_tokens(gpu_lib):
+    """o = NULL and n_commit = NULL: a replay that advances the state by all K tokens."""
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_prefill_inputs(4, 7, 2, 128, 128, seed=11)
+    d = _to_dev(x)
+    S = d["S0"].clone()
+    assert binding.recurrent_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], S,
+                                   outputs=False) is None
+    torch.cuda.synchronize()
+    _, rS = c_oracle.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    assert_close("S", S.cpu().numpy(), rS)
+
+
+def test_decode_multi_matches_repeated_steps(gpu_lib):
+    """K tokens in one state pass equal K single-token steps (same per-token arithmetic)."""
+    from linear_attention_chunkwise_amd import binding
+    N, K, H = 8, 4, 4
+    x = _to_dev(inputs.make_prefill_inputs(N, K, H, 128, 128, seed=12))
+    S1 = x["S0"].clone()
+    o1 = binding.recurrent_multi(x["q"], x["k"], x["v"], x["g"], x["beta"], S1,
+                                 out_dtype=torch.float32)
+    S2 = x["S0"].clone()
+    o2 = torch.stack([binding.recurrent_step(*(x[n][:, t].contiguous()
+                                               for n in ("q", "k", "v", "g", "beta")), S2,
+                                             out_dtype=torch.float32) for t in range(K)], 1)
+    torch.cuda.synchronize()
+    assert_close("o", o1.cpu().numpy(), o2.cpu().numpy())
+    assert_close("S", S1.cpu().numpy(), S2.cpu().numpy())
+
+
+def test_decode_multi_workload_n1024_h32_k4(gpu_lib):
+    """Speculative verification at the decode workload's size: 4 drafted tokens per sequence,
+    a random accepted prefix committed; sampled sequences against the oracle."""
+    from linear_attention_chunkwise_amd import binding
+    cfg = inputs.DECODE_CONFIG
+    K = 4
+    x = inputs.make_prefill_inputs(cfg.N, K, cfg.H, cfg.dk, cfg.dv, seed=3, device="cuda")
+    gen = torch.Generator().manual_seed(3)
+    commits = torch.randint(0, K + 1, (cfg.N,), generator=gen, dtype=torch.int32)
+    S = x["S0"].clone()
+    o = binding.recurrent_multi(x["q"], x["k"], x["v"], x["g"], x["beta"], S, commits.cuda())
+    torch.cuda.synchronize()
+    idx = torch.arange(0, cfg.N, 41)
+    sub = {k: x[k][idx].cpu() for k in ("q", "k", "v", "g", "beta", "S0")}
+    ro, rS = _oracle_multi(sub, sub["S0"], commits[idx].tolist())
+    assert_close("o", o[idx].float().cpu().numpy(), ro)
+    assert_close("S", S[idx].cpu().numpy(), rS)
