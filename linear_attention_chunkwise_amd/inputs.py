@@ -104,9 +104,12 @@ def _l2norm_last(x):
 
 def make_prefill_inputs(B, T, H, dk, dv, *, dtype=torch.bfloat16, seed=0, device="cpu",
                         A_std=0.5, S0_std=0.1, near_gmin_frac=0.0, cu_seqlens=None,
-                        beta_dtype=None):
+                        beta_dtype=None, with_logits=False):
     """Draw one prefill batch.  Returns a dict with q, k, v, g, beta, S0 (or None),
-    cu_seqlens (int32 tensor on ``device`` or None) and N (number of sequences)."""
+    cu_seqlens (int32 tensor on ``device`` or None) and N (number of sequences).  With
+    ``with_logits`` it also holds the decay logits z ([B, T, H, dk], stored in ``dtype``) and the
+    per-head log-scales A_log ([H] float32) that g was synthesised from (g itself comes from the
+    float32 logits, before z is rounded to ``dtype``)."""
     device = torch.device(device)
     gen = _gen(device, seed)
     q = _l2norm_last(_randn((B, T, H, dk), gen, device)).to(dtype)
@@ -122,12 +125,16 @@ def make_prefill_inputs(B, T, H, dk, dv, *, dtype=torch.bfloat16, seed=0, device
         mask.scatter_(1, chans, True)
         z = torch.where(mask, torch.full_like(z, 3.0), z)
     g = (G_MIN * torch.sigmoid(torch.exp(A)[None, None, :, None] * z)).float()
+    zs = z.to(dtype) if with_logits else None
     del z
     beta = torch.sigmoid(_randn((B, T, H), gen, device)).to(beta_dtype or dtype)
     N = B if cu_seqlens is None else len(cu_seqlens) - 1
     S0 = None if S0_std is None else _randn((N, H, dk, dv), gen, device) * S0_std
     cu = None if cu_seqlens is None else torch.as_tensor(cu_seqlens, dtype=torch.int32).to(device)
-    return dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, cu_seqlens=cu, N=N)
+    out = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, cu_seqlens=cu, N=N)
+    if with_logits:
+        out.update(z=zs, A_log=A.float().contiguous())
+    return out
 
 
 def make_config_inputs(cfg: PrefillConfig, seed=0, device="cpu"):

@@ -22,8 +22,10 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle (always when force, else only if the library is missing)."""
-    if force or not os.path.exists(_LIB):
+    """Compile the C oracle (always when force, else only if the library is missing or older
+    than its source)."""
+    stale = not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.run(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC,
                         "-o", tmp, "-lm"], check=True)
@@ -37,7 +39,8 @@ def _load():
         build(force=False)
         lib = ctypes.CDLL(_LIB)
         vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
-        lib.kda_oracle_units.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64,
+        lib.kda_oracle_units.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, i64,
                                          i32, i32, i32, f64, i32, vp, vp, vp, vp]
         lib.kda_oracle_units.restype = None
         lib.kda_oracle_threads.restype = ctypes.c_int
@@ -55,6 +58,8 @@ def _dtype_code(t):
         return 0
     if t.dtype == torch.float32:
         return 1
+    if t.dtype == torch.float64:
+        return 2
     raise TypeError("stored dtype must be bfloat16 or float32, got %s" % t.dtype)
 
 
@@ -66,15 +71,17 @@ def kda_units(q, k, v, g, beta, S0=None, cu_seqlens=None, units=None, scale=1.0)
     """Evaluate eq. (1) on selected (sequence, head) units.
 
     Tensors are CPU torch tensors: q, k [B, T, H, dk], v [B, T, H, dv] (bf16 or f32),
-    g [B, T, H, dk] f32, beta [B, T, H], S0 [N, H, dk, dv] f32 or None, cu_seqlens [N+1] or None.
+    g [B, T, H, dk] f32 or f64 (torch or numpy), beta [B, T, H], S0 [N, H, dk, dv] f32 or None, cu_seqlens [N+1] or None.
     ``units``: list of (n, h); default all.
     Returns (list of o arrays [len_n, dv] float64 per unit, S_T array [n_units, dk, dv])."""
     lib = _load()
+    if isinstance(g, np.ndarray):
+        g = torch.from_numpy(g)
     q, k, v, g, beta = (t.detach().cpu().contiguous() for t in (q, k, v, g, beta))
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k, v must share a dtype")
-    if g.dtype != torch.float32:
-        raise TypeError("g must be float32")
+    if g.dtype not in (torch.float32, torch.float64):
+        raise TypeError("g must be float32 or float64")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if cu_seqlens is None:
@@ -99,7 +106,7 @@ def kda_units(q, k, v, g, beta, S0=None, cu_seqlens=None, units=None, scale=1.0)
     o = np.zeros((max(off, 1), dv), np.float64)
     ST = np.zeros((len(units), dk, dv), np.float64)
     lib.kda_oracle_units(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dtype_code(q),
-                         _dtype_code(beta), T, H, dk, dv, float(scale), len(units),
+                         _dtype_code(beta), _dtype_code(g), T, H, dk, dv, float(scale), len(units),
                          desc.ctypes.data_as(ctypes.c_void_p),
                          S0u.ctypes.data_as(ctypes.c_void_p), o.ctypes.data_as(ctypes.c_void_p),
                          ST.ctypes.data_as(ctypes.c_void_p))

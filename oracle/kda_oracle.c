@@ -9,7 +9,8 @@
  * evaluated as: decay the rows of S by exp(g_t) (decay before the delta update), form
  * u = beta_t (v_t - S^T k_t) against the decayed state, add k_t u^T, read out S^T q_t after the
  * update.  All arithmetic is double precision; inputs are upcast from their stored dtype
- * (bf16 bit patterns or float32).  Only tests/ and bench.py's CPU-baseline leg load this
+ * (bf16 bit patterns or float32; g may also be float64, e.g. the decay map of eq. (5) evaluated
+ * in double).  Only tests/ and bench.py's CPU-baseline leg load this
  * library; the HIP product path never does, and the two share no code.
  *
  * Units run in parallel with OpenMP (one unit per thread at a time); within a unit the loop is
@@ -23,7 +24,9 @@
 #include <omp.h>
 #endif
 
+/* dtype codes: 0 bf16, 1 float32, 2 float64 */
 static double load_elem(const void* base, int dtype, int64_t idx) {
+    if (dtype == 2) return ((const double*)base)[idx];
     if (dtype == 0) { /* bf16: the 16 stored bits are the top half of a float32 */
         uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
         float f;
@@ -45,8 +48,9 @@ int kda_oracle_threads(void) {
  * lives at ((b * T + t) * H + h) * d + c.  beta at (b * T + t) * H + h.
  * S0_units / ST_out: [n_units, dk, dv] row-major.  o_out: unit u's outputs start at
  * o_offset[u] * dv, one row of dv per token of the unit. */
-void kda_oracle_units(const void* q, const void* k, const void* v, const float* g,
-                      const void* beta, int in_dtype, int beta_dtype, int64_t T, int32_t H,
+void kda_oracle_units(const void* q, const void* k, const void* v, const void* g,
+                      const void* beta, int in_dtype, int beta_dtype, int g_dtype, int64_t T,
+                      int32_t H,
                       int32_t dk, int32_t dv, double scale, int32_t n_units,
                       const int64_t* unit_desc, const double* S0_units, double* o_out,
                       double* ST_out) {
@@ -69,7 +73,7 @@ void kda_oracle_units(const void* q, const void* k, const void* v, const float* 
                 for (int32_t i = 0; i < dk; ++i) {
                     qt[i] = scale * load_elem(q, in_dtype, row * dk + i);
                     kt[i] = load_elem(k, in_dtype, row * dk + i);
-                    at[i] = exp((double)g[row * dk + i]);
+                    at[i] = exp(load_elem(g, g_dtype, row * dk + i));
                 }
                 const double bt = load_elem(beta, beta_dtype, row);
                 /* decay, then y = S^T k on the decayed state */

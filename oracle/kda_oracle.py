@@ -108,3 +108,19 @@ def kda_decode_step(q, k, v, g, beta, S, scale=1.0):
             o[n, h], Snew[n, h] = kda_token_step(S[n, h], q[n, h], k[n, h], v[n, h],
                                                  g[n, h], beta[n, h], scale)
     return o, Snew
+
+
+G_MIN = -5.0   # §2.1.1, eq. (5): the lower bound of the log-decay is fixed at -5
+
+
+def kda_gate(z, A_log, g_min=G_MIN):
+    """The bounded decay map of §2.1.1, eq. (5): g = g_min * Sigmoid(exp(A_h) * z), per head h
+    (A_h is the per-head log-scale) and per key channel.
+
+    z: [..., H, dk] (any leading shape); A_log: [H].  Returns g in float64, in [g_min, 0].
+    Sigmoid(x) = 1 / (1 + exp(-x)); exp(-x) overflowing to +inf for very negative x gives the
+    limit 0 exactly."""
+    z, A = _f64(z), _f64(A_log)
+    x = np.exp(A)[:, None] * z
+    with np.errstate(over="ignore"):
+        return g_min / (1.0 + np.exp(-x))

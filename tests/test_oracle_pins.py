@@ -372,3 +372,89 @@ def test_decode_step_is_one_token():
     o2, S2 = kda_oracle.kda_forward(x["q"][:, None], x["k"][:, None], x["v"][:, None],
                                     x["g"][:, None], x["beta"][:, None], x["S"])
     assert np.array_equal(o, o2[:, 0]) and np.array_equal(S, S2)
+
+
+# ----------------------------------------------------------------------------- decay map, eq. (5)
+
+def _gate_pins(gate):
+    """Errors of a gate map g(z, A_log) against what eq. (5) and the text after it fix."""
+    import scipy.special
+    rng = np.random.default_rng(5)
+    H, dk = 3, 8
+    A = np.array([0.0, 0.7, -1.3])
+    z = rng.standard_normal((2, 4, H, dk)) * 3
+    errs = {}
+    # Sigmoid(0) = 1/2: g = g_min / 2 for every head, whatever A_h is
+    errs["zero_logit"] = float(np.abs(gate(np.zeros((1, H, dk)), A) - (-2.5)).max())
+    # A_h = 0 (the initialisation the text gives): g_min times the logistic function (scipy)
+    g0 = gate(z, np.zeros(H))
+    errs["logistic_at_A0"] = float(np.abs(g0 - (-5.0) * scipy.special.expit(z)).max())
+    # Sigmoid(x) + Sigmoid(-x) = 1: g(z) + g(-z) = g_min
+    errs["reflection"] = float(np.abs(gate(z, A) + gate(-z, A) - (-5.0)).max())
+    # exp(A_h) scales the logit of head h only: head h with A_h equals A = 0 on exp(A_h) z
+    ga = gate(z, A)
+    errs["head_scale"] = max(float(np.abs(ga[..., h, :] - (-5.0) * scipy.special.expit(
+        math.exp(A[h]) * z[..., h, :])).max()) for h in range(H))
+    # range (g_min, 0) and its limits at saturated logits, without NaN
+    zs = np.array([[[-1e4] * dk, [1e4] * dk, [0.0] * dk]]).reshape(1, 3, dk)
+    gs = gate(zs, np.zeros(3))
+    errs["limits"] = float(abs(gs[0, 0]).max() + abs(gs[0, 1] + 5.0).max())
+    errs["range"] = 0.0 if (np.all(ga <= 0) and np.all(ga >= -5.0)) else 1.0
+    # monotone: a larger logit never gives a weaker decay
+    zz = np.sort(z.reshape(-1))
+    gg = gate(zz.reshape(-1, 1, 1) * np.ones((1, 1, 1)), np.array([0.4]))[:, 0, 0]
+    errs["monotone"] = 0.0 if np.all(np.diff(gg) <= 0) else 1.0
+    return errs
+
+
+def test_gate_pins():
+    for name, err in _gate_pins(kda_oracle.kda_gate).items():
+        assert err <= 1e-14, f"gate pin {name}: {err:.3e}"
+
+
+def test_gate_respects_page_bounds():
+    """α = exp(g) > exp(-5) ≈ 6.7e-3 and a 16-token window sums to more than -80 (the numbers
+    printed after eq. (5)), on the decay-heavy synthetic recipe (10% of channels at z = +3)."""
+    from linear_attention_chunkwise_amd import inputs
+    d = json.load(open(os.path.join(GOLDEN, "decay_bounds.json")))
+    x = inputs.make_prefill_inputs(1, 256, 4, 32, 8, seed=6, near_gmin_frac=0.1, with_logits=True)
+    g = kda_oracle.kda_gate(x["z"], x["A_log"])
+    assert np.exp(g).min() > math.exp(d["g_min"]) and g.max() < 0
+    win = np.lib.stride_tricks.sliding_window_view(g, 16, axis=1).sum(-1)
+    assert win.min() > d["tile_log_decay_lower_bound"]
+
+
+GATE_MUTANTS = {
+    # the unbounded map eq. (5) replaces (negative Softplus, scaled by exp(A_h))
+    "softplus_map": lambda z, A: -np.exp(_np(A))[:, None] * np.log1p(np.exp(_np(z))),
+    # A_h used as the scale itself instead of exp(A_h)
+    "no_exp_on_A": lambda z, A: -5.0 / (1.0 + np.exp(-_np(A)[:, None] * _np(z))),
+    # the logistic function mirrored
+    "mirrored_sigmoid": lambda z, A: -5.0 / (1.0 + np.exp(np.exp(_np(A))[:, None] * _np(z))),
+    # the per-head scale applied along the key channels
+    "scale_on_channels": lambda z, A: -5.0 / (1.0 + np.exp(-np.resize(np.exp(_np(A)),
+                                                                       _np(z).shape[-1]) * _np(z))),
+}
+
+
+def _np(x):
+    return np.asarray(x, np.float64)
+
+
+@pytest.mark.parametrize("name", sorted(GATE_MUTANTS))
+def test_gate_pins_catch_planted_mistake(name):
+    try:
+        errs = _gate_pins(GATE_MUTANTS[name])
+    except (ValueError, IndexError):
+        return  # a shape mistake that cannot even broadcast is caught too
+    assert max(errs.values()) > 1e-6, f"planted gate mistake {name} passes every pin"
+
+
+def test_c_oracle_takes_float64_decay():
+    """The C token loop reads float64 g (the eq. (5) map evaluated in double) like float32 g."""
+    from linear_attention_chunkwise_amd import inputs
+    x = inputs.make_prefill_inputs(2, 19, 2, 16, 8, seed=7, with_logits=True)
+    g = kda_oracle.kda_gate(x["z"], x["A_log"])
+    a = kda_oracle.kda_forward(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
+    b = c_oracle.kda_forward(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
+    assert _rel(b[0], a[0]) < 1e-13 and _rel(b[1], a[1]) < 1e-13
