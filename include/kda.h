@@ -86,6 +86,25 @@ kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const
                               float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity, float* ckpt,
                               hipStream_t stream);
 
+/* kda_chunk_fwd with the decay computed inside the kernel from its logits by the bounded map of
+ * §2.1.1, eq. (5):
+ *
+ *     g[b, t, h, c] = g_min * Sigmoid(exp(A_log[h]) * z[b, t, h, c]),   g_min = -5,
+ *
+ * so g never goes through memory (z is read in in_dtype, 2 bytes per channel for bf16, instead
+ * of float32 g).  A_log is the per-head log-scale A_h of eq. (5).
+ *
+ * z: [B, T, H, dk] in in_dtype, 16-byte aligned; A_log: device float32 [H], 4-byte aligned.  Every
+ * other argument, the layouts and the results are those of kda_chunk_fwd evaluated on that g
+ * (the map runs in float32).  o must not overlap z or A_log either.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT (also: z or A_log NULL or misaligned),
+ * KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
+kda_status kda_chunk_fwd_gate(const void* q, const void* k, const void* v, const void* z,
+                              const float* A_log, const void* beta, const float* S0,
+                              const int32_t* cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t N,
+                              int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype,
+                              float scale, void* o, float* S_T, hipStream_t stream);
+
 /* Bytes of workspace kda_chunk_fwd_cp needs: N * (segments - 1) * H * dk * (dv + dk) * 4 (the
  * summaries below), 0 when segments <= 1 or a size is not positive. */
 size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv,
@@ -130,6 +149,15 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               const void* beta, float* S, int32_t N, int32_t H, int32_t dk,
                               int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
                               void* o, hipStream_t stream);
+
+/* kda_recurrent_step with the decay computed from its logits, g = g_min Sigmoid(exp(A_log[h]) z)
+ * with g_min = -5 (§2.1.1, eq. (5)), as in kda_chunk_fwd_gate.  z: [N, H, dk] in in_dtype,
+ * 16-byte aligned; A_log: device float32 [H].  Other arguments as kda_recurrent_step.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
+kda_status kda_recurrent_step_gate(const void* q, const void* k, const void* v, const void* z,
+                                   const float* A_log, const void* beta, float* S, int32_t N,
+                                   int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
+                                   kda_dtype out_dtype, float scale, void* o, hipStream_t stream);
 
 /* K decode tokens per (sequence, head) with one pass over the state: the decode-side variant
  * §5.4.2 describes for speculative decoding, where K drafted tokens are verified together and

@@ -19,9 +19,9 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_RANGE, KDA_ERR_HI
 KDA_BF16, KDA_F32 = 0, 1
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_cp", "kda_chunk_fwd_cp_workspace_size",
-           "kda_recurrent_step", "kda_recurrent_multi", "kda_status_string", "kda_last_error",
-           "kda_version")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_gate", "kda_chunk_fwd_cp",
+           "kda_chunk_fwd_cp_workspace_size", "kda_recurrent_step", "kda_recurrent_step_gate",
+           "kda_recurrent_multi", "kda_status_string", "kda_last_error", "kda_version")
 
 _lib = None
 
@@ -61,6 +61,12 @@ def load(path: str = LIB_PATH):
     lib.kda_recurrent_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_multi.restype = ctypes.c_int
+    lib.kda_chunk_fwd_gate.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                       i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp]
+    lib.kda_chunk_fwd_gate.restype = ctypes.c_int
+    lib.kda_recurrent_step_gate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp]
+    lib.kda_recurrent_step_gate.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -297,5 +303,68 @@ def recurrent_multi(q, k, v, g, beta, S, n_commit=None, *, scale: float = 1.0, o
     st = lib.kda_recurrent_multi(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), _p(n_commit), N, K, H,
                                  dk, dv, _dt(q), _dt(o) if o is not None else _dt(q), float(scale),
                                  _p(o), _stream(dev))
+    _check(st)
+    return o
+
+
+def chunk_fwd_gate(q, k, v, z, A_log, beta, S0=None, cu_seqlens=None, *, scale: float = 1.0,
+                   out_dtype=None, output_final_state: bool = True, o=None, S_T=None):
+    """chunk_fwd with the decay map in the kernel: g = -5 Sigmoid(exp(A_log[h]) z) is formed from
+    the logits z [B,T,H,dk] (q's dtype) and A_log [H] float32 instead of being read."""
+    lib = load()
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dev, dt)
+    _require(k, "k", dev, dt, (B, T, H, dk))
+    _require(v, "v", dev, dt, (B, T, H, dv))
+    _require(z, "z", dev, dt, (B, T, H, dk))
+    _require(A_log, "A_log", dev, torch.float32, (H,))
+    _require(beta, "beta", dev, dt, (B, T, H))
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
+    out_dtype = out_dtype or dt
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _require(o, "o", dev, out_dtype, (B, T, H, dv))
+    if S_T is None and output_final_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
+    st = lib.kda_chunk_fwd_gate(_p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta), _p(S0),
+                                _p(cu_seqlens), B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale),
+                                _p(o), _p(S_T), _stream(dev))
+    _check(st)
+    return o, S_T
+
+
+def recurrent_step_gate(q, k, v, z, A_log, beta, S, *, scale: float = 1.0, out_dtype=None, o=None):
+    """recurrent_step with the decay formed from the logits z [N,H,dk] (q's dtype) and A_log [H]."""
+    lib = load()
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dev, dt)
+    _require(k, "k", dev, dt, (N, H, dk))
+    _require(v, "v", dev, dt, (N, H, dv))
+    _require(z, "z", dev, dt, (N, H, dk))
+    _require(A_log, "A_log", dev, torch.float32, (H,))
+    _require(beta, "beta", dev, dt, (N, H))
+    _require(S, "S", dev, torch.float32, (N, H, dk, dv))
+    out_dtype = out_dtype or dt
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _require(o, "o", dev, out_dtype, (N, H, dv))
+    st = lib.kda_recurrent_step_gate(_p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta), _p(S), N, H,
+                                     dk, dv, _dt(q), _dt(o), float(scale), _p(o), _stream(dev))
     _check(st)
     return o

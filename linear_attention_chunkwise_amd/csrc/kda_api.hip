@@ -77,7 +77,7 @@ const char* kda_status_string(kda_status s) {
 const char* kda_last_error(void) { return g_last_error; }
 
 static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g,
-                                 const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                 const void* z, const float* A_log, const void* beta, const float* S0, const int32_t* cu_seqlens,
                                  int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
                                  kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
                                  float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity,
@@ -109,12 +109,18 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         KDA_TRY(check_ptr(q, 16, "q"));
         KDA_TRY(check_ptr(k, 16, "k"));
         KDA_TRY(check_ptr(v, 16, "v"));
-        KDA_TRY(check_ptr(g, 16, "g"));
+        if (z) {
+            KDA_TRY(check_ptr(z, 16, "z"));
+            KDA_TRY(check_ptr(A_log, 4, "A_log"));
+        } else {
+            KDA_TRY(check_ptr(g, 16, "g"));
+        }
         KDA_TRY(check_ptr(beta, es, "beta"));
         KDA_TRY(check_ptr(o, 16, "o"));
         const size_t no = nv * dsize(out_dtype);
         if (overlaps(o, no, q, nqk * es) || overlaps(o, no, k, nqk * es) ||
-            overlaps(o, no, v, nv * es) || overlaps(o, no, g, nqk * 4) ||
+            overlaps(o, no, v, nv * es) || (!z && overlaps(o, no, g, nqk * 4)) ||
+            (z && (overlaps(o, no, z, nqk * es) || overlaps(o, no, A_log, (size_t)H * 4))) ||
             overlaps(o, no, beta, (size_t)tokens * H * es))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps an input%.0lld", "o");
     }
@@ -166,6 +172,11 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                        in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T,
                        ckpt_capacity > 0 ? ckpt : nullptr, ckpt_interval / 32, ckpt_capacity,
                        /*mode*/ 0, /*nseg*/ 1, /*seg_len*/ 0, /*ws*/ nullptr, stream};
+    if (z) {
+        a.g = nullptr;
+        a.z = z;
+        a.A_log = A_log;
+    }
     if (segments <= 1) return hip_status(kda::launch_chunk_fwd(a));
     // segmented: summaries of all but the last segment, then every segment's outputs
     a.nseg = segments;
@@ -183,7 +194,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
                          kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
                          float* S_T, hipStream_t stream) {
-    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
+    return chunk_fwd_impl(q, k, v, g, nullptr, nullptr, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
                           scale, o, S_T, 0, 0, nullptr, 1, nullptr, 0, stream);
 }
 
@@ -193,8 +204,18 @@ kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const
                               kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
                               float* S_T, int32_t ckpt_interval, int32_t ckpt_capacity, float* ckpt,
                               hipStream_t stream) {
-    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
+    return chunk_fwd_impl(q, k, v, g, nullptr, nullptr, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
                           scale, o, S_T, ckpt_interval, ckpt_capacity, ckpt, 1, nullptr, 0, stream);
+}
+
+kda_status kda_chunk_fwd_gate(const void* q, const void* k, const void* v, const void* z,
+                              const float* A_log, const void* beta, const float* S0,
+                              const int32_t* cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t N,
+                              int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype,
+                              float scale, void* o, float* S_T, hipStream_t stream) {
+    if (!z) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL%.0lld", "z");
+    return chunk_fwd_impl(q, k, v, nullptr, z, A_log, beta, S0, cu_seqlens, B, T, H, N, dk, dv,
+                          in_dtype, out_dtype, scale, o, S_T, 0, 0, nullptr, 1, nullptr, 0, stream);
 }
 
 size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t segments) {
@@ -208,14 +229,15 @@ kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const f
                             kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
                             float* S_T, int32_t segments, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-    return chunk_fwd_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
+    return chunk_fwd_impl(q, k, v, g, nullptr, nullptr, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
                           scale, o, S_T, 0, 0, nullptr, segments, workspace, workspace_bytes, stream);
 }
 
-kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
-                              const void* beta, float* S, int32_t N, int32_t H, int32_t dk,
-                              int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
-                              void* o, hipStream_t stream) {
+static kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const float* g,
+                                      const void* z, const float* A_log, const void* beta, float* S,
+                                      int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                      kda_dtype in_dtype, kda_dtype out_dtype, float scale,
+                                      void* o, hipStream_t stream) {
     KDA_TRY(check_dtype(in_dtype, "in_dtype"));
     KDA_TRY(check_dtype(out_dtype, "out_dtype"));
     if (N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "N", N);
@@ -228,7 +250,12 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     KDA_TRY(check_ptr(q, 16, "q"));
     KDA_TRY(check_ptr(k, 16, "k"));
     KDA_TRY(check_ptr(v, 16, "v"));
-    KDA_TRY(check_ptr(g, 16, "g"));
+    if (z) {
+        KDA_TRY(check_ptr(z, 16, "z"));
+        KDA_TRY(check_ptr(A_log, 4, "A_log"));
+    } else {
+        KDA_TRY(check_ptr(g, 16, "g"));
+    }
     KDA_TRY(check_ptr(beta, es, "beta"));
     KDA_TRY(check_ptr(S, 16, "S"));
     KDA_TRY(check_ptr(o, 16, "o"));
@@ -236,11 +263,33 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     const size_t no = nh * dv * dsize(out_dtype);
     if (overlaps(o, no, S, nh * dk * dv * 4) || overlaps(o, no, q, nh * dk * es) ||
         overlaps(o, no, k, nh * dk * es) || overlaps(o, no, v, nh * dv * es) ||
-        overlaps(o, no, g, nh * dk * 4) || overlaps(o, no, beta, nh * es))
+        (!z && overlaps(o, no, g, nh * dk * 4)) ||
+        (z && (overlaps(o, no, z, nh * dk * es) || overlaps(o, no, A_log, (size_t)H * 4))) ||
+        overlaps(o, no, beta, nh * es))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps the state or an input%.0lld", "o");
-    kda::DecodeArgs a{q, k, v, g, beta, S, (int32_t)nh, dk, dv,
+    kda::DecodeArgs a{q, k, v, z ? nullptr : g, beta, S, (int32_t)nh, dk, dv,
                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, stream};
+    a.H = H;
+    a.z = z;
+    a.A_log = z ? A_log : nullptr;
     return hip_status(kda::launch_decode_step(a));
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                              const void* beta, float* S, int32_t N, int32_t H, int32_t dk,
+                              int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
+                              void* o, hipStream_t stream) {
+    return recurrent_step_impl(q, k, v, g, nullptr, nullptr, beta, S, N, H, dk, dv, in_dtype,
+                               out_dtype, scale, o, stream);
+}
+
+kda_status kda_recurrent_step_gate(const void* q, const void* k, const void* v, const void* z,
+                                   const float* A_log, const void* beta, float* S, int32_t N,
+                                   int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
+                                   kda_dtype out_dtype, float scale, void* o, hipStream_t stream) {
+    if (!z) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL%.0lld", "z");
+    return recurrent_step_impl(q, k, v, nullptr, z, A_log, beta, S, N, H, dk, dv, in_dtype,
+                               out_dtype, scale, o, stream);
 }
 
 kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, const float* g,

@@ -9,6 +9,9 @@
 // Bound: HBM.  Per (sequence, head) the algorithmic traffic is the state read once and written
 // once (2 * dk * dv * 4 bytes) plus q, k, v, g, beta and o; the arithmetic is ~7 dk dv fp32 ops.
 //
+// The decay is either given (g) or computed here from the logits z and the per-head log-scales by
+// the bounded map of §2.1.1, eq. (5), g = g_min Sigmoid(exp(A_h) z) with g_min = -5.
+//
 // Mapping: one 256-thread workgroup per (sequence, head).  Thread t owns four adjacent value
 // columns (one float4 per state row) and a contiguous group of dk / (1024 / dv) state rows, so
 // every state row is read and written by full 16-byte lanes, 512 contiguous bytes per row at
@@ -19,11 +22,28 @@
 
 namespace kda {
 
-template <int DK, int DV, bool IN_F32, bool OUT_F32>
+// Per-channel decay exp(g) of element idx: g as given, or (GATE) the bounded map of the logit,
+// g = g_min Sigmoid(exp(A_h) z), with ea = exp(A_h).
+template <bool IN_F32, bool GATE>
+__device__ __forceinline__ float decay_at(const float* __restrict__ g, const void* __restrict__ z,
+                                          float ea, size_t idx) {
+    if constexpr (GATE) {
+        float zv;
+        if constexpr (IN_F32) zv = reinterpret_cast<const float*>(z)[idx];
+        else zv = bf2f(reinterpret_cast<const bf16*>(z)[idx]);
+        return __expf(kGmin * __builtin_amdgcn_rcpf(1.f + __expf(-ea * zv)));
+    } else {
+        return __expf(g[idx]);
+    }
+}
+
+template <int DK, int DV, bool IN_F32, bool OUT_F32, bool GATE>
 __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qp,
                                                      const void* __restrict__ kp,
                                                      const void* __restrict__ vp,
                                                      const float* __restrict__ g,
+                                                     const void* __restrict__ zp,
+                                                     const float* __restrict__ A_log, int32_t H,
                                                      const void* __restrict__ betap,
                                                      float* __restrict__ S, int32_t NH,
                                                      float scale, void* __restrict__ op) {
@@ -51,11 +71,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qp
         else return bf2f(reinterpret_cast<const bf16*>(p)[idx]);
     };
     const size_t kb = (size_t)unit * DK;
+    const float ea = GATE ? __expf(A_log[unit % H]) : 0.f;
     f32x4 y = zero4(), z = zero4();
     float qk = 0.f;
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
-        const float a = __expf(g[kb + r0 + i]);
+        const float a = decay_at<IN_F32, GATE>(g, zp, ea, kb + r0 + i);
         const float kv = in_at(kp, kb + r0 + i);
         const float qv = in_at(qp, kb + r0 + i);
         s[i] *= a;
@@ -101,11 +122,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qp
 // written back after the first `commit` tokens (commit = 0: outputs only, state untouched).
 // Tokens are laid out [N, K, H, d]; the reductions use two LDS buffers by token parity, one
 // workgroup barrier per token.
-template <int DK, int DV, bool IN_F32, bool OUT_F32>
+template <int DK, int DV, bool IN_F32, bool OUT_F32, bool GATE>
 __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restrict__ qp,
                                                            const void* __restrict__ kp,
                                                            const void* __restrict__ vp,
                                                            const float* __restrict__ g,
+                                                           const void* __restrict__ zp,
+                                                           const float* __restrict__ A_log,
                                                            const void* __restrict__ betap,
                                                            float* __restrict__ S,
                                                            const int32_t* __restrict__ n_commit,
@@ -127,6 +150,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
     const int r0 = rg * RPG;
     int commit = n_commit ? n_commit[n] : K;
     commit = commit < 0 ? 0 : (commit > K ? K : commit);
+    const float ea = GATE ? __expf(A_log[h]) : 0.f;
 
     float* Su = S + (size_t)unit * DK * DV;
     f32x4 s[RPG];
@@ -146,7 +170,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
         float kv[RPG];
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {
-            const float a = __expf(g[kb + r0 + i]);
+            const float a = decay_at<IN_F32, GATE>(g, zp, ea, kb + r0 + i);
             kv[i] = in_at(kp, kb + r0 + i);
             const float qv = in_at(qp, kb + r0 + i);
             s[i] *= a;
@@ -189,39 +213,47 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
     }
 }
 
-template <int DK, int DV, bool IN_F32, bool OUT_F32>
+template <int DK, int DV, bool IN_F32, bool OUT_F32, bool GATE>
 static hipError_t launch_decode(const DecodeArgs& a) {
     if (a.NH == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, IN_F32, OUT_F32>), dim3(a.NH), dim3(256), 0,
-                       a.stream, a.q, a.k, a.v, a.g, a.beta, a.S, a.NH, a.scale, a.o);
+    hipLaunchKernelGGL((decode_kernel<DK, DV, IN_F32, OUT_F32, GATE>), dim3(a.NH), dim3(256), 0,
+                       a.stream, a.q, a.k, a.v, a.g, a.z, a.A_log, a.H, a.beta, a.S, a.NH, a.scale,
+                       a.o);
     return hipGetLastError();
 }
 
-template <int DK, int DV, bool IN_F32, bool OUT_F32>
+template <int DK, int DV, bool IN_F32, bool OUT_F32, bool GATE>
 static hipError_t launch_multi(const DecodeArgs& a) {
     const int64_t units = (int64_t)a.N * a.H;
     if (units == 0 || a.K == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IN_F32, OUT_F32>), dim3((unsigned)units), dim3(256), 0,
-                       a.stream, a.q, a.k, a.v, a.g, a.beta, a.S, a.n_commit, a.N, a.H, a.K, a.scale, a.o);
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IN_F32, OUT_F32, GATE>), dim3((unsigned)units),
+                       dim3(256), 0, a.stream, a.q, a.k, a.v, a.g, a.z, a.A_log, a.beta, a.S,
+                       a.n_commit, a.N, a.H, a.K, a.scale, a.o);
     return hipGetLastError();
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool GATE>
 static hipError_t dispatch_io(const DecodeArgs& a) {
     if (a.K > 0) {
-        if (a.in_f32) return a.out_f32 ? launch_multi<DK, DV, true, true>(a) : launch_multi<DK, DV, true, false>(a);
-        return a.out_f32 ? launch_multi<DK, DV, false, true>(a) : launch_multi<DK, DV, false, false>(a);
+        if (a.in_f32)
+            return a.out_f32 ? launch_multi<DK, DV, true, true, GATE>(a) : launch_multi<DK, DV, true, false, GATE>(a);
+        return a.out_f32 ? launch_multi<DK, DV, false, true, GATE>(a) : launch_multi<DK, DV, false, false, GATE>(a);
     }
-    if (a.in_f32) return a.out_f32 ? launch_decode<DK, DV, true, true>(a)
-                                   : launch_decode<DK, DV, true, false>(a);
-    return a.out_f32 ? launch_decode<DK, DV, false, true>(a) : launch_decode<DK, DV, false, false>(a);
+    if (a.in_f32)
+        return a.out_f32 ? launch_decode<DK, DV, true, true, GATE>(a) : launch_decode<DK, DV, true, false, GATE>(a);
+    return a.out_f32 ? launch_decode<DK, DV, false, true, GATE>(a) : launch_decode<DK, DV, false, false, GATE>(a);
+}
+
+template <int DK, int DV>
+static hipError_t dispatch_gate(const DecodeArgs& a) {
+    return a.z ? dispatch_io<DK, DV, true>(a) : dispatch_io<DK, DV, false>(a);
 }
 
 hipError_t launch_decode_step(const DecodeArgs& a) {
-    if (a.dk == 128 && a.dv == 128) return dispatch_io<128, 128>(a);
-    if (a.dk == 128 && a.dv == 64) return dispatch_io<128, 64>(a);
-    if (a.dk == 64 && a.dv == 128) return dispatch_io<64, 128>(a);
-    if (a.dk == 64 && a.dv == 64) return dispatch_io<64, 64>(a);
+    if (a.dk == 128 && a.dv == 128) return dispatch_gate<128, 128>(a);
+    if (a.dk == 128 && a.dv == 64) return dispatch_gate<128, 64>(a);
+    if (a.dk == 64 && a.dv == 128) return dispatch_gate<64, 128>(a);
+    if (a.dk == 64 && a.dv == 64) return dispatch_gate<64, 64>(a);
     return hipErrorInvalidValue;
 }
 

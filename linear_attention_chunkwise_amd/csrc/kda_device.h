@@ -12,6 +12,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// g_min of the bounded decay map, g = g_min Sigmoid(exp(A_h) z), and g_min in log2 units
+constexpr float kGmin = -5.0f;
+constexpr float kGminLog2e = -7.2134752044448170f;
 
 // D = A * B + C on one 16x16x32 bf16 tile (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
 // With lane l, i16 = l % 16 and g4 = l / 16: the A operand of lane l holds row i16 and the B

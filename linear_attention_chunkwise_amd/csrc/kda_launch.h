@@ -35,6 +35,10 @@ struct PrefillArgs {
     int64_t seg_len;          // multiple of 32
     float* ws;                // [N, nseg - 1, H, dk, dv + dk] float32 (modes 1, 2)
     hipStream_t stream;
+    // decay map in the kernel (g unused): g = -5 Sigmoid(exp(A_log[h]) z), z [.., H, dk] stored
+    // like q
+    const void* z = nullptr;
+    const float* A_log = nullptr;
 };
 
 struct DecodeArgs {
@@ -53,6 +57,9 @@ struct DecodeArgs {
     // null, the state written after n_commit[n] tokens (null: all K)
     int32_t K = 0, N = 0, H = 0;
     const int32_t* n_commit = nullptr;
+    // decay map in the kernel (g unused), as in PrefillArgs; H must be set
+    const void* z = nullptr;
+    const float* A_log = nullptr;
 };
 
 hipError_t launch_chunk_fwd(const PrefillArgs& a);

@@ -241,7 +241,7 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t&
 // ==================================== producer waves =========================================
 // Wave p owns key channels [32 p, 32 p + 32) (none when p >= DK / 32).  Per chunk: the decayed
 // operands and the partial Gram tiles (interval 1); Q~, K~, K_end^T and gamma (interval 2).
-template <int DK, bool F32IN>
+template <int DK, bool F32IN, bool GATE>
 __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p, int lane,
                                          int64_t row0, int64_t len, int h) {
     using Lay = Layout<DK, F32IN>;
@@ -257,7 +257,11 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 
     const IT* qh = reinterpret_cast<const IT*>(a.q) + (size_t)row0 * sq + (size_t)h * DK;
     const IT* kh = reinterpret_cast<const IT*>(a.k) + (size_t)row0 * sq + (size_t)h * DK;
-    const float* gh = a.g + (size_t)row0 * sq + (size_t)h * DK;
+    const float* gh = GATE ? nullptr : a.g + (size_t)row0 * sq + (size_t)h * DK;
+    const IT* zh = GATE ? reinterpret_cast<const IT*>(a.z) + (size_t)row0 * sq + (size_t)h * DK : nullptr;
+    // decay map of the logits: g log2(e) = g_min log2(e) / (1 + 2^(zsc z)), zsc = -exp(A_h) log2(e)
+    float zsc = 0.f;
+    if constexpr (GATE) zsc = -__expf(a.A_log[h]) * kLog2e;
     const IT* bh = reinterpret_cast<const IT*>(a.beta) + (size_t)row0 * a.H + h;
     uint32_t off_qk[2], off_g[2], off_b[2];
 #pragma unroll
@@ -276,21 +280,25 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
         for (int e = 0; e < 8; ++e) Id[hh][e] = f2bf((8 * g4 + e == 16 * hh + i16) ? 1.f : 0.f);
 
     // prefetch registers (one chunk ahead): token 16 t + i16 of tile t
-    Raw8<F32IN> pq[2], pk[2];
+    Raw8<F32IN> pq[2], pk[2], pz[2];
     uint4 pg[2][2];
     uint32_t pb[2];
     auto prefetch = [&](int64_t c0) {
         const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT)));
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT)));
-        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gh + (size_t)c0 * sq, nv * (uint32_t)(sq * 4));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(bh + (size_t)c0 * a.H, nv * (uint32_t)(a.H * sizeof(IT)));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             pq[t].load(rq, off_qk[t]);
             pk[t].load(rk, off_qk[t]);
-            pg[t][0] = bload16(rg, off_g[t]);
-            pg[t][1] = bload16(rg, off_g[t] + 16);
+            if constexpr (GATE) {
+                pz[t].load(make_rsrc(zh + (size_t)c0 * sq, nv * (uint32_t)(sq * sizeof(IT))), off_qk[t]);
+            } else {
+                const __amdgpu_buffer_rsrc_t rg = make_rsrc(gh + (size_t)c0 * sq, nv * (uint32_t)(sq * 4));
+                pg[t][0] = bload16(rg, off_g[t]);
+                pg[t][1] = bload16(rg, off_g[t] + 16);
+            }
             if (p == 0) {
                 if constexpr (F32IN) pb[t] = __builtin_amdgcn_raw_buffer_load_b32(rb, off_b[t], 0, 0);
                 else pb[t] = __builtin_amdgcn_raw_buffer_load_b16(rb, off_b[t], 0, 0);
@@ -298,8 +306,28 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
         }
     };
 
+    // GATE: the log2 decay of a chunk is mapped from its logits one interval ahead, in interval 2
+    // of the chunk before (the producers' shorter interval), so interval 1 only reads Lg.
+    float Lg[2][8];
+    auto gate_map = [&](int64_t c0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            pz[t].pin_all();
+            // tokens past the end read z = 0, whose map is not 0: they must not decay
+            const bool valid = 16 * t + i16 < len - c0;
+            float zv[8];
+            pz[t].to_f32(zv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                Lg[t][e] = valid ? kGminLog2e * __builtin_amdgcn_rcpf(1.f + fast_exp2(zsc * zv[e])) : 0.f;
+        }
+    };
+
     const int64_t nchunks = (len + kC - 1) / kC;
-    if (intra && nchunks > 0) prefetch(0);
+    if (intra && nchunks > 0) {
+        prefetch(0);
+        if constexpr (GATE) gate_map(0);
+    }
 
     for (int64_t it = 0; it <= nchunks; ++it) {
         const bool work = intra && it < nchunks;   // wave-uniform
@@ -313,16 +341,23 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
             for (int t = 0; t < 2; ++t) {
                 pq[t].pin_all();
                 pk[t].pin_all();
-                pin(pg[t][0]);
-                pin(pg[t][1]);
+                if constexpr (!GATE) {
+                    pin(pg[t][0]);
+                    pin(pg[t][1]);
+                }
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 pq[t].to_f32(qv[t]);
                 pk[t].to_f32(kv[t]);
-                const float* gl = reinterpret_cast<const float*>(pg[t]);
+                if constexpr (GATE) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
+                    for (int e = 0; e < 8; ++e) L[t][e] = Lg[t][e];
+                } else {
+                    const float* gl = reinterpret_cast<const float*>(pg[t]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
+                }
             }
             if (p == 0) {   // beta of the chunk for the solve
 #pragma unroll
@@ -447,6 +482,9 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                     st<bf16x4>(dst, to_bf16x4(mma(eh, Id[hh], zero4())));          // exact: bf16 in
                     st<bf16x4>(dst + DK * TB, to_bf16x4(mma(el, Id[hh], zero4())));
                 }
+            }
+            if constexpr (GATE) {
+                if (it + 1 < nchunks) gate_map((it + 1) * kC);
             }
         }
         __syncthreads();
@@ -919,7 +957,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
 }
 
 // Both roles run the same number of iterations (chunks + 1) with three barriers each.
-template <int DK, bool F32IN, bool OUT_F32>
+template <int DK, bool F32IN, bool OUT_F32, bool GATE>
 __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
@@ -941,14 +979,14 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
-    if (wave < kNW) producer<DK, F32IN>(a, smem, wave, lane, row0, len, h);
+    if (wave < kNW) producer<DK, F32IN, GATE>(a, smem, wave, lane, row0, len, h);
     else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg);
 }
 
-template <int DK, bool F32IN, bool OUT_F32>
+template <int DK, bool F32IN, bool OUT_F32, bool GATE>
 static hipError_t launch_prefill(const PrefillArgs& a) {
     using Lay = Layout<DK, F32IN>;
-    auto kern = prefill_kernel<DK, F32IN, OUT_F32>;
+    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE>;
     static bool attr_set = false;   // benign race: the attribute value is idempotent
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -964,17 +1002,23 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_fwd(const PrefillArgs& a) {
+template <bool GATE>
+static hipError_t dispatch_prefill(const PrefillArgs& a) {
     if (a.dk == 128) {
         // float32 inputs are supported at dk = 64 (the ABI rejects them at dk = 128)
         if (a.in_f32) return hipErrorInvalidValue;
-        return a.out_f32 ? launch_prefill<128, false, true>(a) : launch_prefill<128, false, false>(a);
+        return a.out_f32 ? launch_prefill<128, false, true, GATE>(a) : launch_prefill<128, false, false, GATE>(a);
     }
     if (a.dk == 64) {
-        if (a.in_f32) return a.out_f32 ? launch_prefill<64, true, true>(a) : launch_prefill<64, true, false>(a);
-        return a.out_f32 ? launch_prefill<64, false, true>(a) : launch_prefill<64, false, false>(a);
+        if (a.in_f32)
+            return a.out_f32 ? launch_prefill<64, true, true, GATE>(a) : launch_prefill<64, true, false, GATE>(a);
+        return a.out_f32 ? launch_prefill<64, false, true, GATE>(a) : launch_prefill<64, false, false, GATE>(a);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_fwd(const PrefillArgs& a) {
+    return a.z ? dispatch_prefill<true>(a) : dispatch_prefill<false>(a);
 }
 
 }  // namespace kda

@@ -202,3 +202,41 @@ def test_recurrent_multi_rejects_on_host(lib, kw, status):
 def test_recurrent_multi_empty_work_is_ok(lib):
     assert _multi(lib, K=0, q=None, S=None) == binding.KDA_OK
     assert _multi(lib, N=0, q=None, S=None) == binding.KDA_OK
+
+
+def _gate(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, z=FAKE, A=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2,
+             N=1, dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_gate(a["q"], a["k"], a["v"], a["z"], a["A"], a["beta"], a["S0"],
+                                  a["cu"], a["B"], a["T"], a["H"], a["N"], a["dk"], a["dv"],
+                                  a["ind"], a["outd"], ctypes.c_float(a["scale"]), a["o"], a["ST"],
+                                  None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=None), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(z=FAKE + 4), binding.KDA_ERR_INVALID_ARGUMENT),          # misaligned
+    (dict(A=None), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(A=FAKE + 2), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(z=FAKE * 8 + 32), binding.KDA_ERR_INVALID_ARGUMENT),     # o overlaps z
+    (dict(A=FAKE * 8 + 64), binding.KDA_ERR_INVALID_ARGUMENT),     # o overlaps A_log
+    (dict(dk=96), binding.KDA_ERR_UNSUPPORTED),
+])
+def test_chunk_fwd_gate_rejects_on_host(lib, kw, status):
+    assert _gate(lib, **kw) == status
+    assert lib.kda_last_error() != b""
+
+
+def test_recurrent_step_gate_rejects_on_host(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, z=FAKE, A=FAKE, beta=FAKE, S=FAKE * 16, N=4, H=2, dk=128,
+                 dv=128, o=FAKE * 64)
+        a.update(kw)
+        return lib.kda_recurrent_step_gate(a["q"], a["k"], a["v"], a["z"], a["A"], a["beta"],
+                                           a["S"], a["N"], a["H"], a["dk"], a["dv"], 0, 0,
+                                           ctypes.c_float(1.0), a["o"], None)
+    assert call(z=None) == binding.KDA_ERR_INVALID_ARGUMENT
+    assert call(A=None) == binding.KDA_ERR_INVALID_ARGUMENT
+    assert call(o=FAKE * 16) == binding.KDA_ERR_INVALID_ARGUMENT      # o aliases S
+    assert call(N=0, q=None) == binding.KDA_OK

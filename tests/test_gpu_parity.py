@@ -491,3 +491,92 @@ def test_decode_multi_workload_n1024_h32_k4(gpu_lib):
     ro, rS = _oracle_multi(sub, sub["S0"], commits[idx].tolist())
     assert_close("o", o[idx].float().cpu().numpy(), ro)
     assert_close("S", S[idx].cpu().numpy(), rS)
+
+
+# ------------------------------------------------------------------ decay map in the kernel
+
+def _gate_oracle(x, S0, cu=None, scale=1.0, units=None):
+    """The oracle on g = kda_gate(z, A_log) (float64), the map of eq. (5)."""
+    from oracle import kda_oracle
+    g = kda_oracle.kda_gate(x["z"].cpu(), x["A_log"].cpu())
+    if units is None:
+        return c_oracle.kda_forward(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), g, x["beta"].cpu(),
+                                    S0, cu, scale)
+    return c_oracle.kda_units(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), g, x["beta"].cpu(), S0, cu,
+                              units, scale)
+
+
+GATE_CASES = [
+    # (B, T, H, dk, dv, dtype, near_gmin_frac)
+    (2, 77, 3, 128, 128, torch.bfloat16, 0.0),
+    (1, 200, 2, 128, 64, torch.bfloat16, 0.1),
+    (1, 129, 2, 64, 64, torch.bfloat16, 0.0),
+    (1, 256, 1, 64, 64, torch.float32, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[f"B{c[0]}T{c[1]}k{c[3]}v{c[4]}{str(c[5])[6:]}"
+                                                  for c in GATE_CASES])
+def test_prefill_gate_small(gpu_lib, case):
+    from linear_attention_chunkwise_amd import binding
+    B, T, H, dk, dv, dt, frac = case
+    x = inputs.make_prefill_inputs(B, T, H, dk, dv, dtype=dt, seed=T + dk, near_gmin_frac=frac,
+                                   with_logits=True, A_std=0.8)
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd_gate(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta"], d["S0"],
+                                   scale=0.9, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rST = _gate_oracle(x, x["S0"], scale=0.9)
+    assert_close("o", o.cpu().numpy(), ro)
+    assert_close("S_T", ST.cpu().numpy(), rST)
+
+
+def test_prefill_gate_varlen(gpu_lib):
+    from linear_attention_chunkwise_amd import binding
+    cu = inputs.cu_from_lengths([0, 45, 300, 1, 64])
+    x = inputs.make_prefill_inputs(1, int(cu[-1]), 2, 128, 128, seed=21, cu_seqlens=cu,
+                                   with_logits=True)
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd_gate(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta"], d["S0"],
+                                   d["cu_seqlens"])
+    torch.cuda.synchronize()
+    ro, rST = _gate_oracle(x, x["S0"], cu)
+    assert_close("o", o.float().cpu().numpy(), ro)
+    assert_close("S_T", ST.cpu().numpy(), rST)
+
+
+def test_workload_prefill_gate_b4_h32_t32k(gpu_lib):
+    """The prefill workload with the map in the kernel, sampled (sequence, head) units."""
+    from linear_attention_chunkwise_amd import binding
+    cfg = inputs.CONFIGS["prefill_b4_h32_t32k_d128"]
+    x = inputs.make_prefill_inputs(cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, seed=5, device="cuda",
+                                   A_std=cfg.A_std, with_logits=True)
+    del x["g"]
+    o, ST = binding.chunk_fwd_gate(x["q"], x["k"], x["v"], x["z"], x["A_log"], x["beta"], x["S0"])
+    torch.cuda.synchronize()
+    units = [(0, 0), (1, 13), (3, 31)]
+    for n, h in units:
+        print(f"  unit n={n} h={h} tokens={cfg.T}", flush=True)
+        sel = lambda t: t[n:n + 1, :, h:h + 1].contiguous().cpu()
+        sub = {k: sel(x[k]) for k in ("q", "k", "v", "z", "beta")}
+        sub["A_log"] = x["A_log"][h:h + 1].cpu()
+        outs, rST = _gate_oracle(sub, x["S0"][n:n + 1, h:h + 1].contiguous().cpu(), units=[(0, 0)])
+        assert_close(f"o[n={n},h={h}]", o[n, :, h].float().cpu().numpy(), outs[0])
+        assert_close(f"S_T[n={n},h={h}]", ST[n, h].cpu().numpy(), rST[0])
+    del x, o, ST
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_decode_gate(gpu_lib, dk, dv):
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_prefill_inputs(7, 1, 3, dk, dv, seed=dk + 1, with_logits=True, A_std=0.8)
+    d = {k: (v[:, 0].contiguous() if torch.is_tensor(v) and v.dim() >= 3 and v.shape[1] == 1
+             and k not in ("S0",) else v) for k, v in _to_dev(x).items()}
+    S = d["S0"].clone()
+    o = binding.recurrent_step_gate(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta"], S,
+                                    out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rS = _gate_oracle(x, x["S0"])
+    assert_close("o", o.cpu().numpy(), ro[:, 0])
+    assert_close("S", S.cpu().numpy(), rS)
