@@ -51,8 +51,31 @@ def prefill_alg_flops(B, T, H, dk, dv, C=32):
     return th * (intra + inter)
 
 
-def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2):
-    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * in_bytes + dk * 4 + in_bytes + dv * out_bytes)
+def prefill_gate_alg_bytes(B, T, H, dk, dv, N, in_bytes=2, out_bytes=2):
+    """As prefill_alg_bytes with the decay map in the kernel: the logits z (input dtype) are read
+    instead of float32 g, plus H float32 log-scales."""
+    th = B * T * H
+    per_th = (3 * dk + dv) * in_bytes + in_bytes + dv * out_bytes
+    return th * per_th + 2 * N * H * dk * dv * 4 + H * 4
+
+
+def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2, K=1):
+    """State read and written once per launch; K tokens of q, k, v, g, beta in, o out."""
+    return N * H * (2 * dk * dv * 4 + K * ((2 * dk + dv) * in_bytes + dk * 4 + in_bytes +
+                                           dv * out_bytes))
+
+
+def time_launches(fn, reps=10):
+    """Average duration of fn's launches (HIP events on the current stream), after 2 warmups."""
+    for _ in range(2):
+        fn()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for _ in range(reps):
+        fn()
+    e[1].record()
+    torch.cuda.synchronize()
+    return e[0].elapsed_time(e[1]) / reps
 
 
 def kernel_source_hash(name):
@@ -118,6 +141,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the variants timed after the steps (decay map in the kernel, "
+                         "multi-token decode)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="profile helper: run only the prefill launch per step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -136,7 +162,10 @@ def main():
     dev = torch.device("cuda:0")
     cfg = inputs.CONFIGS["prefill_b4_h32_t32k_d128"]
     dcfg = inputs.DECODE_CONFIG
-    x = inputs.make_config_inputs(cfg, seed=0, device=dev)
+    x = inputs.make_prefill_inputs(cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, dtype=cfg.dtype, seed=0,
+                                   device=dev, A_std=cfg.A_std, S0_std=cfg.S0_std,
+                                   near_gmin_frac=cfg.near_gmin_frac,
+                                   with_logits=not args.no_extras)
     d = inputs.make_decode_inputs(dcfg.N, dcfg.H, dcfg.dk, dcfg.dv, seed=0, device=dev)
     B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
@@ -201,6 +230,27 @@ def main():
                      "traffic": measured_traffic("prefill_kernel<128,bf16,bf16>", "kda_prefill.hip"),
                      "kernel": "prefill_kernel<128,bf16,bf16 out>"},
     }
+    if not args.no_extras and not args.prefill_only:
+        # variants, timed after the steps (not part of ms_per_step)
+        g_ms = time_launches(lambda: binding.chunk_fwd_gate(
+            x["q"], x["k"], x["v"], x["z"], x["A_log"], x["beta"], x["S0"], o=o, S_T=ST))
+        gbytes = prefill_gate_alg_bytes(B, T, H, dk, dv, B)
+        res["prefill_gate"] = {"ms": g_ms, "tokens_per_s": B * T / (g_ms * 1e-3),
+                               "alg_bytes": gbytes, "alg_GBps": gbytes / (g_ms * 1e-3) / 1e9,
+                               "what": "kda_chunk_fwd_gate: g = -5 Sigmoid(exp(A_h) z) formed "
+                                       "in the kernel from bf16 z"}
+        K = 4
+        m = inputs.make_prefill_inputs(dcfg.N, K, dcfg.H, dcfg.dk, dcfg.dv, seed=1, device=dev)
+        om = torch.empty((dcfg.N, K, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)
+        Sm = m["S0"]
+        m_ms = time_launches(lambda: binding.recurrent_multi(m["q"], m["k"], m["v"], m["g"],
+                                                             m["beta"], Sm, o=om))
+        mbytes = decode_alg_bytes(dcfg.N, dcfg.H, dcfg.dk, dcfg.dv, K=K)
+        res["decode_multi"] = {"K": K, "us": m_ms * 1e3, "us_per_token": m_ms * 1e3 / K,
+                               "alg_bytes": mbytes, "GBps": mbytes / (m_ms * 1e-3) / 1e9,
+                               "what": "kda_recurrent_multi: 4 tokens per (sequence, head) per "
+                                       "state pass, 1024 sequences x 32 heads"}
+        del m, om, Sm
     if not args.no_cpu_baseline:
         del o, od
         res["cpu_baseline"] = cpu_baseline(x)
