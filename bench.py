@@ -153,7 +153,7 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: every workload here fits "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: every workload here fits "
                                    "one MI355X; --gpus must be 1"}))
         sys.exit(2)
 
@@ -251,6 +251,20 @@ def main():
                                "what": "kda_recurrent_multi: 4 tokens per (sequence, head) per "
                                        "state pass, 1024 sequences x 32 heads"}
         del m, om, Sm
+        # context for the HBM fractions: what the vendor's own read+write kernels reach here
+        xb = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        yb = torch.empty_like(xb)
+        nb = 2 * xb.numel() * 4
+        c_ms = time_launches(lambda: yb.copy_(xb))
+        r_ms = time_launches(lambda: xb.mul_(1.0))
+        res["hbm_reference"] = {
+            "device_copy_GBps": nb / (c_ms * 1e-3) / 1e9,
+            "inplace_scale_GBps": nb / (r_ms * 1e-3) / 1e9,
+            "decode_vs_best": dbytes / (dec_ms * 1e-3) / 1e9 / (nb / (min(c_ms, r_ms) * 1e-3) / 1e9),
+            "what": "torch device copy and in-place multiply of a 1 GiB float32 buffer (1 GiB read "
+                    "+ 1 GiB written per launch), timed like the variants; decode_vs_best = decode "
+                    "GB/s over the faster of the two"}
+        del xb, yb
     if not args.no_cpu_baseline:
         del o, od
         res["cpu_baseline"] = cpu_baseline(x)
