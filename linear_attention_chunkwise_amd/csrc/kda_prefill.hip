@@ -79,6 +79,7 @@ struct Layout {
     static constexpr int o_beta = o_gam + DK * 4;             // fp32 [C]
     static constexpr int total = o_beta + kC * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
+    static_assert(o_N - o_Gp >= 4 * (1024 + 1), "sequence ranking scratch fits the Gram region");
 };
 
 // DPP row shift right by N lanes inside each 16-lane row, zero fill.
@@ -956,8 +957,45 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     }
 }
 
-// Both roles run the same number of iterations (chunks + 1) with three barriers each.
-template <int DK, bool F32IN, bool OUT_F32, bool GATE>
+// Packed sequences run longest first: the workgroups of rank r take the r-th longest sequence
+// (ties in index order), so a long sequence does not start only after the short ones before it
+// in the batch have been through the machine.  Every thread of the workgroup calls this; the
+// lengths are ranked in LDS (the Gram-partials region, not yet in use), 1024 sequences at most.
+constexpr int kRankMax = 1024;
+__device__ int seq_of_rank(const PrefillArgs& a, int r, char* smem) {
+    int* L = reinterpret_cast<int*>(smem);
+    int* found = L + kRankMax;
+    const int n4 = (a.N + 3) / 4;
+    for (int m = threadIdx.x; m < 4 * n4; m += kNT) {
+        int64_t row0 = 0, len = -1;       // padding ranks below every real length
+        if (m < a.N) seq_bounds(a, m, row0, len);
+        L[m] = (int)len;
+    }
+    if (threadIdx.x == 0) *found = r;     // unreachable for a valid r; keeps the result in range
+    __syncthreads();
+    for (int m = threadIdx.x; m < a.N; m += kNT) {
+        const int lm = L[m];
+        int rank = 0;
+        for (int j4 = 0; j4 < n4; ++j4) {
+            const int4 v = reinterpret_cast<const int4*>(L)[j4];
+            const int j = 4 * j4;
+            rank += (v.x > lm) | ((v.x == lm) & (j < m));
+            rank += (v.y > lm) | ((v.y == lm) & (j + 1 < m));
+            rank += (v.z > lm) | ((v.z == lm) & (j + 2 < m));
+            rank += (v.w > lm) | ((v.w == lm) & (j + 3 < m));
+        }
+        if (rank == r) *found = m;
+    }
+    __syncthreads();
+    const int n = *found;
+    __syncthreads();   // the region is reused by the pipeline
+    return n;
+}
+
+// Both roles run the same number of iterations (chunks + 1) with two barriers each.  RANK: packed
+// sequences (at most kRankMax) in longest-first order; a separate instantiation, so that the
+// fixed-length kernel's code is not changed by the ranking.
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
 __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
@@ -967,8 +1005,10 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     if (unit >= a.N * a.H * nseg) return;
     const int h = unit % a.H;
     const int seg = (unit / a.H) % nseg;
-    const int n = unit / (a.H * nseg);
+    const int rank = unit / (a.H * nseg);
     if (a.mode == 1 && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;   // not needed
+    int n = rank;
+    if constexpr (RANK) n = seq_of_rank(a, rank, smem);
     int64_t row0, len;
     seq_bounds(a, n, row0, len);
     if (a.mode != 0) {   // this segment's tokens
@@ -983,10 +1023,10 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg);
 }
 
-template <int DK, bool F32IN, bool OUT_F32, bool GATE>
-static hipError_t launch_prefill(const PrefillArgs& a) {
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
+static hipError_t launch_one(const PrefillArgs& a) {
     using Lay = Layout<DK, F32IN>;
-    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE>;
+    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE, RANK>;
     static bool attr_set = false;   // benign race: the attribute value is idempotent
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1000,6 +1040,12 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kNT), Lay::total, a.stream, a);
     return hipGetLastError();
+}
+
+template <int DK, bool F32IN, bool OUT_F32, bool GATE>
+static hipError_t launch_prefill(const PrefillArgs& a) {
+    if (a.cu && a.N > 1 && a.N <= kRankMax) return launch_one<DK, F32IN, OUT_F32, GATE, true>(a);
+    return launch_one<DK, F32IN, OUT_F32, GATE, false>(a);
 }
 
 template <bool GATE>

@@ -580,3 +580,26 @@ def test_decode_gate(gpu_lib, dk, dv):
     ro, rS = _gate_oracle(x, x["S0"])
     assert_close("o", o.cpu().numpy(), ro[:, 0])
     assert_close("S", S.cpu().numpy(), rS)
+
+
+# ------------------------------------------------------------------ packed-sequence ordering
+
+@pytest.mark.parametrize("lengths", [
+    [64, 5, 64, 300, 0, 64, 300, 1, 33],                       # ties, an empty sequence
+    [1, 2, 3] * 341 + [40],                                     # 1024 sequences: ranked order
+    [2, 1, 3] * 344,                                            # 1032 sequences: index order
+], ids=["ties", "n1024", "n1032"])
+def test_prefill_varlen_order_independent(gpu_lib, lengths):
+    """Which workgroup runs which sequence (longest first up to 1024 sequences) never changes a
+    result: every sequence against the oracle, with ties and past the ranking limit."""
+    from linear_attention_chunkwise_amd import binding
+    cu = inputs.cu_from_lengths(lengths)
+    H = 2 if len(lengths) < 100 else 1
+    x = inputs.make_prefill_inputs(1, int(cu[-1]), H, 64, 64, seed=len(lengths), cu_seqlens=cu)
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["cu_seqlens"],
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rST = oracle_all(x)
+    assert_close("o", o.cpu().numpy(), ro)
+    assert_close("S_T", ST.cpu().numpy(), rST)
