@@ -111,6 +111,42 @@ def calibrate_copy():
                       "bytes_written": x.numel() * 4, "launches": 2}), flush=True)
 
 
+def calibrate_peaks(dev):
+    """Measured ceilings on this machine (bench_calib.so, built beside this file): the issue rate
+    of v_mfma_f32_16x16x32_bf16 with independent accumulators on every SIMD, and a grid-stride
+    device copy of 1 GiB (1 GiB read + 1 GiB written).  None if the library was not built."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_calib.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.calib_mfma_flops.restype = ctypes.c_double
+    lib.calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                               ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    blocks, iters = 2048, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def mfma():
+        assert lib.calib_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, stream) == 0
+
+    m_ms = time_launches(mfma, reps=5)
+    x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+
+    def copy():
+        assert lib.calib_copy(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                              x.numel() // 4, 1024, stream) == 0
+
+    c_ms = time_launches(copy)
+    return {"mfma_bf16_TFLOPs": lib.calib_mfma_flops(blocks, iters) / (m_ms * 1e-3) / 1e12,
+            "copy_GBps": 2 * x.numel() * 4 / (c_ms * 1e-3) / 1e9,
+            "what": "bench_calib.hip: 8 independent v_mfma_f32_16x16x32_bf16 chains per wave, "
+                    "2048 x 256 threads; grid-stride float4 copy, 1024 x 256 threads"}
+
+
 def cpu_baseline(x, units_wanted=None):
     """The C float64 reference token loop on the first `units_wanted` (sequence, head) units (all
     of them by default: the whole prefill workload is a few seconds of host work)."""
@@ -251,6 +287,21 @@ def main():
                                "what": "kda_recurrent_multi: 4 tokens per (sequence, head) per "
                                        "state pass, 1024 sequences x 32 heads"}
         del m, om, Sm
+        # packed prefill: 64 sequences, lognormal lengths (median 1024, longest 65536)
+        vcfg = inputs.CONFIGS["varlen64_h32_d128"]
+        xv = inputs.make_config_inputs(vcfg, seed=0, device=dev)
+        Tv = xv["q"].shape[1]
+        ov = torch.empty((1, Tv, vcfg.H, vcfg.dv), dtype=torch.bfloat16, device=dev)
+        STv = torch.empty((xv["N"], vcfg.H, vcfg.dk, vcfg.dv), dtype=torch.float32, device=dev)
+        v_ms = time_launches(lambda: binding.chunk_fwd(xv["q"], xv["k"], xv["v"], xv["g"], xv["beta"],
+                                                       xv["S0"], xv["cu_seqlens"], o=ov, S_T=STv))
+        lens = xv["cu_seqlens"][1:] - xv["cu_seqlens"][:-1]
+        vbytes = prefill_alg_bytes(1, Tv, vcfg.H, vcfg.dk, vcfg.dv, xv["N"])
+        res["prefill_varlen64"] = {"ms": v_ms, "tokens": Tv, "tokens_per_s": Tv / (v_ms * 1e-3),
+                                   "longest": int(lens.max()), "alg_GBps": vbytes / (v_ms * 1e-3) / 1e9,
+                                   "what": "kda_chunk_fwd on 64 packed sequences (cu_seqlens), "
+                                           "H=32, d=128; the longest sequence runs first"}
+        del xv, ov, STv
         # context for the HBM fractions: what the vendor's own read+write kernels reach here
         xb = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         yb = torch.empty_like(xb)
@@ -265,6 +316,11 @@ def main():
                     "+ 1 GiB written per launch), timed like the variants; decode_vs_best = decode "
                     "GB/s over the faster of the two"}
         del xb, yb
+        cal = calibrate_peaks(dev)
+        if cal is not None:
+            cal["prefill_alg_mfma_frac_of_measured"] = pflops / (pre_ms * 1e-3) / 1e12 / cal["mfma_bf16_TFLOPs"]
+            cal["decode_frac_of_measured_copy"] = dbytes / (dec_ms * 1e-3) / 1e9 / cal["copy_GBps"]
+        res["calibration"] = cal
     if not args.no_cpu_baseline:
         del o, od
         res["cpu_baseline"] = cpu_baseline(x)
