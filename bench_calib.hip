@@ -22,16 +22,23 @@ __global__ __launch_bounds__(256) void mfma_loop(float* __restrict__ out, int it
         a[e] = (__bf16)(1.0f + 0.001f * (threadIdx.x & 7));
         b[e] = (__bf16)(0.5f - 0.001f * e);
     }
-    f32x4 acc[kChains];
-#pragma unroll
-    for (int j = 0; j < kChains; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // distinct starting values keep the eight accumulators in eight register quads
+    const float l = (float)(threadIdx.x & 3);
+    f32x4 c0{l, 0.f, 0.f, 0.f}, c1{l + 1.f, 0.f, 0.f, 0.f}, c2{l + 2.f, 0.f, 0.f, 0.f},
+        c3{l + 3.f, 0.f, 0.f, 0.f}, c4{l + 4.f, 0.f, 0.f, 0.f}, c5{l + 5.f, 0.f, 0.f, 0.f},
+        c6{l + 6.f, 0.f, 0.f, 0.f}, c7{l + 7.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < iters; ++i) {
-#pragma unroll
-        for (int j = 0; j < kChains; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c3, 0, 0, 0);
+        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c4, 0, 0, 0);
+        c5 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c5, 0, 0, 0);
+        c6 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c6, 0, 0, 0);
+        c7 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c7, 0, 0, 0);
     }
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < kChains; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    const f32x4 t = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+    const float s = t[0] + t[1] + t[2] + t[3];
     if (s == -1.0f) out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
