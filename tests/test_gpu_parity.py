@@ -603,3 +603,36 @@ def test_prefill_varlen_order_independent(gpu_lib, lengths):
     ro, rST = oracle_all(x)
     assert_close("o", o.cpu().numpy(), ro)
     assert_close("S_T", ST.cpu().numpy(), rST)
+
+
+# ------------------------------------------------------------------ decode with float32 inputs
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_decode_f32_inputs_single_and_multi(gpu_lib, dk, dv):
+    """float32 q, k, v, beta through the single-token, multi-token and decay-map decode paths."""
+    from linear_attention_chunkwise_amd import binding
+    N, K, H = 5, 3, 2
+    x = inputs.make_prefill_inputs(N, K, H, dk, dv, dtype=torch.float32, seed=dk + 7,
+                                   with_logits=True)
+    d = _to_dev(x)
+    S1 = d["S0"].clone()
+    o1 = binding.recurrent_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], S1)
+    ro, rS = c_oracle.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    S2 = d["S0"].clone()
+    o2 = binding.recurrent_step(*(d[n][:, 0].contiguous() for n in ("q", "k", "v", "g", "beta")), S2)
+    S3 = d["S0"].clone()
+    o3 = binding.recurrent_step_gate(*(d[n][:, 0].contiguous() for n in ("q", "k", "v", "z")),
+                                     d["A_log"], d["beta"][:, 0].contiguous(), S3)
+    torch.cuda.synchronize()
+    assert o1.dtype == torch.float32
+    assert_close("o multi", o1.cpu().numpy(), ro)
+    assert_close("S multi", S1.cpu().numpy(), rS)
+    r1o, r1S = c_oracle.kda_forward(*(x[n][:, :1].contiguous() for n in ("q", "k", "v", "g", "beta")),
+                                    x["S0"])
+    assert_close("o step", o2.cpu().numpy(), r1o[:, 0])
+    assert_close("S step", S2.cpu().numpy(), r1S)
+    sub = {n: x[n][:, :1].contiguous() for n in ("q", "k", "v", "z", "beta")}
+    sub["A_log"] = x["A_log"]
+    rgo, rgS = _gate_oracle(sub, x["S0"])
+    assert_close("o gate", o3.cpu().numpy(), rgo[:, 0])
+    assert_close("S gate", S3.cpu().numpy(), rgS)
