@@ -636,3 +636,33 @@ def test_decode_f32_inputs_single_and_multi(gpu_lib, dk, dv):
     rgo, rgS = _gate_oracle(sub, x["S0"])
     assert_close("o gate", o3.cpu().numpy(), rgo[:, 0])
     assert_close("S gate", S3.cpu().numpy(), rgS)
+
+
+def test_every_entry_point_is_bitwise_deterministic(gpu_lib):
+    """No atomics and fixed reduction orders: two runs of each entry point give identical bits."""
+    from linear_attention_chunkwise_amd import binding
+    cu = inputs.cu_from_lengths([70, 3, 200, 41])
+    x = _to_dev(inputs.make_prefill_inputs(1, int(cu[-1]), 3, 128, 128, seed=31, cu_seqlens=cu,
+                                           with_logits=True))
+    runs = []
+    for _ in range(2):
+        r = {}
+        r["gate"] = binding.chunk_fwd_gate(x["q"], x["k"], x["v"], x["z"], x["A_log"], x["beta"],
+                                           x["S0"], x["cu_seqlens"])
+        r["cp"] = binding.chunk_fwd_cp(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
+                                       x["cu_seqlens"], segments=3)
+        r["ckpt"] = binding.chunk_fwd_ckpt(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
+                                           x["cu_seqlens"], interval=64, capacity=3)
+        d = _to_dev(inputs.make_prefill_inputs(8, 3, 4, 128, 128, seed=32, with_logits=True))
+        S = d["S0"].clone()
+        r["multi"] = (binding.recurrent_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], S), S)
+        S1 = d["S0"].clone()
+        r["step"] = (binding.recurrent_step(*(d[n][:, 0].contiguous() for n in ("q", "k", "v", "g", "beta")), S1), S1)
+        S2 = d["S0"].clone()
+        r["step_gate"] = (binding.recurrent_step_gate(*(d[n][:, 0].contiguous() for n in ("q", "k", "v", "z")),
+                                                      d["A_log"], d["beta"][:, 0].contiguous(), S2), S2)
+        torch.cuda.synchronize()
+        runs.append(r)
+    for name in runs[0]:
+        for a, b in zip(runs[0][name], runs[1][name]):
+            assert torch.equal(a, b), name
