@@ -21,6 +21,12 @@
  *    host.  All argument checks run on the host before any launch: on error nothing is enqueued.
  *  - Results are deterministic: no atomics, fixed reduction orders.
  *  - Re-entrant; no global mutable state.
+ *  - Domain check (a debug aid, off by default): with the environment variable KDA_CHECK_RANGE=1,
+ *    every entry point that reads g first checks on `stream` that each value lies in [-5, 0]
+ *    (eq. (5) and the bound after it; NaN fails), synchronises `stream` to read the result, and
+ *    returns KDA_ERR_RANGE without launching anything else if one does not.  The prefill kernel
+ *    relies on this domain for the bf16 range of its rescale factors; outside it results are
+ *    undefined (never an out-of-bounds access).
  */
 #ifndef LIBKDA_KDA_H
 #define LIBKDA_KDA_H
@@ -38,7 +44,7 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size, aliasing, bad dtype   */
     KDA_ERR_UNSUPPORTED = 2,      /* a valid request this build does not implement (e.g. dk=96) */
-    KDA_ERR_RANGE = 3,            /* reserved: input values outside the documented domain       */
+    KDA_ERR_RANGE = 3,            /* g outside [-5, 0] (only with KDA_CHECK_RANGE=1, see below)  */
     KDA_ERR_HIP = 4               /* the HIP runtime reported an error (launch, no device)      */
 } kda_status;
 

@@ -2,6 +2,7 @@
 //
 // Every check runs before anything is enqueued, so an error return leaves the stream untouched.
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "kda.h"
@@ -48,6 +49,20 @@ kda_status check_ptr(const void* p, size_t align, const char* what) {
     if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL%.0lld", what);
     if (!aligned(p, align))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %lld-byte aligned", what, (long long)align);
+    return KDA_OK;
+}
+
+// KDA_CHECK_RANGE=1: check g against [-5, 0] before launching (synchronises the stream)
+kda_status check_g(const float* g, size_t n, hipStream_t stream) {
+    const char* env = getenv("KDA_CHECK_RANGE");
+    if (!env || env[0] != '1' || !g || n == 0) return KDA_OK;
+    bool in_range = true;
+    const hipError_t e = kda::check_range(g, n, -5.0f, 0.0f, stream, in_range);
+    if (e != hipSuccess) {
+        snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+        return KDA_ERR_HIP;
+    }
+    if (!in_range) return fail(KDA_ERR_RANGE, "%s: a value lies outside [-5, 0] or is NaN%.0lld", "g");
     return KDA_OK;
 }
 
@@ -168,6 +183,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     }
     if (N == 0) return ok();
 
+    if (!z) KDA_TRY(check_g(g, (size_t)tokens * H * dk, stream));
     kda::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, T, H, N, dk, dv,
                        in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T,
                        ckpt_capacity > 0 ? ckpt : nullptr, ckpt_interval / 32, ckpt_capacity,
@@ -267,6 +283,7 @@ static kda_status recurrent_step_impl(const void* q, const void* k, const void* 
         (z && (overlaps(o, no, z, nh * dk * es) || overlaps(o, no, A_log, (size_t)H * 4))) ||
         overlaps(o, no, beta, nh * es))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps the state or an input%.0lld", "o");
+    if (!z) KDA_TRY(check_g(g, nh * dk, stream));
     kda::DecodeArgs a{q, k, v, z ? nullptr : g, beta, S, (int32_t)nh, dk, dv,
                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, stream};
     a.H = H;
@@ -324,6 +341,7 @@ kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, cons
     }
     if (n_commit && overlaps(n_commit, (size_t)N * 4, S, nh * dk * dv * 4))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S%.0lld", "n_commit");
+    KDA_TRY(check_g(g, nt * dk, stream));
     kda::DecodeArgs a{q, k, v, g, beta, S, (int32_t)nh, dk, dv,
                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, stream};
     a.K = K;

@@ -666,3 +666,34 @@ def test_every_entry_point_is_bitwise_deterministic(gpu_lib):
     for name in runs[0]:
         for a, b in zip(runs[0][name], runs[1][name]):
             assert torch.equal(a, b), name
+
+
+def test_range_check_on_request(gpu_lib, monkeypatch):
+    """KDA_CHECK_RANGE=1: g outside [-5, 0] (or NaN) is refused with KDA_ERR_RANGE before any
+    launch; in range it runs as usual; without the variable nothing is checked."""
+    from linear_attention_chunkwise_amd import binding
+    x = _to_dev(inputs.make_prefill_inputs(1, 40, 2, 64, 64, seed=33))
+    d = _to_dev(inputs.make_decode_inputs(3, 2, 64, 64, seed=34))
+    monkeypatch.setenv("KDA_CHECK_RANGE", "1")
+    binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    binding.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S"].clone())
+    for bad in (-5.5, 0.25, float("nan")):
+        g = x["g"].clone()
+        g[0, 17, 1, 5] = bad
+        with pytest.raises(binding.KdaError) as ei:
+            binding.chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
+        assert ei.value.status == binding.KDA_ERR_RANGE
+        gd = d["g"].clone()
+        gd[2, 1, 3] = bad
+        S = d["S"].clone()
+        with pytest.raises(binding.KdaError) as ei:
+            binding.recurrent_step(d["q"], d["k"], d["v"], gd, d["beta"], S)
+        assert ei.value.status == binding.KDA_ERR_RANGE
+        assert torch.equal(S, d["S"])               # nothing was launched
+    g = x["g"].clone()
+    g[0, 0, 0, 0] = -5.0                             # the bound itself is in the domain
+    binding.chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
+    monkeypatch.delenv("KDA_CHECK_RANGE")
+    g[0, 0, 0, 0] = -5.5
+    binding.chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])   # unchecked
+    torch.cuda.synchronize()
