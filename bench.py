@@ -141,10 +141,27 @@ def calibrate_peaks(dev):
                               x.numel() // 4, 1024, stream) == 0
 
     c_ms = time_launches(copy)
-    return {"mfma_bf16_TFLOPs": lib.calib_mfma_flops(blocks, iters) / (m_ms * 1e-3) / 1e12,
+    lib.calib_contraction_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.calib_contraction_flops.restype = ctypes.c_double
+    lib.calib_contraction.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cblocks, chunks = 256, 1024
+    outc = torch.empty(cblocks * 512, dtype=torch.float32, device=dev)
+
+    def contraction():
+        assert lib.calib_contraction(ctypes.c_void_p(outc.data_ptr()), cblocks, chunks, stream) == 0
+
+    k_ms = time_launches(contraction, reps=5)
+    mfma = lib.calib_mfma_flops(blocks, iters) / (m_ms * 1e-3) / 1e12
+    contr = lib.calib_contraction_flops(cblocks, chunks) / (k_ms * 1e-3) / 1e12
+    return {"mfma_bf16_TFLOPs": mfma,
             "copy_GBps": 2 * x.numel() * 4 / (c_ms * 1e-3) / 1e9,
+            "contraction_TFLOPs": contr,
+            "contraction_frac_of_spec": contr / BF16_MFMA_PEAK_TFLOPS,
+            "contraction_frac_of_measured": contr / mfma,
             "what": "bench_calib.hip: 8 independent v_mfma_f32_16x16x32_bf16 chains per wave, "
-                    "2048 x 256 threads; grid-stride float4 copy, 1024 x 256 threads"}
+                    "2048 x 256 threads; grid-stride float4 copy, 1024 x 256 threads; the prefill "
+                    "consumer's per-chunk contraction sequence (68 MFMAs, operands from LDS, "
+                    "elementwise work left out), 256 x 512 threads, 1024 chunks"}
 
 
 def cpu_baseline(x, units_wanted=None):
