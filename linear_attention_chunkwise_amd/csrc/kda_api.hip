@@ -167,6 +167,10 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     int64_t seg_len = 0;
     if (segments < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "segments", segments);
     if (segments > 1) {
+        // one workgroup per (sequence, head, segment, 64-column slice): keep the grid and the
+        // kernel's 32-bit unit index in range
+        if ((int64_t)N * H * segments > (int64_t)1 << 28)
+            return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "N*H*segments", (long long)N * H * segments);
         if (ckpt_capacity > 0)
             return fail(KDA_ERR_UNSUPPORTED, "%s: checkpoints are not emitted by segmented runs%.0lld", "segments");
         // segment length: the whole row split evenly, rounded up to whole 32-token chunks

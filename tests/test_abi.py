@@ -154,6 +154,7 @@ def _cp(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
+    (dict(T=0, H=1 << 14, segs=1 << 15), binding.KDA_ERR_UNSUPPORTED),   # grid too large
     (dict(segs=0), binding.KDA_ERR_INVALID_ARGUMENT),
     (dict(wsb=1024), binding.KDA_ERR_INVALID_ARGUMENT),            # workspace too small
     (dict(ws=None), binding.KDA_ERR_INVALID_ARGUMENT),
