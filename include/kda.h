@@ -64,7 +64,7 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  *
  * Supported: dk in {64, 128}; dv in {64, 128}; in_dtype KDA_BF16, or KDA_F32 at dk = 64 (float32
  * inputs are carried at higher internal precision); out_dtype KDA_BF16 or KDA_F32; T >= 0;
- * B, H >= 1.
+ * B, H >= 1; N * H <= 2^30; H * max(dk, dv) <= 2^22 (KDA_ERR_UNSUPPORTED beyond).
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const void* beta, const float* S0, const int32_t* cu_seqlens,
@@ -131,6 +131,7 @@ size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t
  * kda_chunk_fwd within the operator's tolerance (the summaries are computed with the same
  * arithmetic; the combination uses split bf16 products with float32 accumulation).
  *
+ * N * H * segments <= 2^28 (KDA_ERR_UNSUPPORTED beyond).
  * workspace: device memory of at least kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments)
  * bytes, 16-byte aligned, caller-owned, overlapping none of o, S0, S_T; ignored (may be NULL)
  * when segments == 1, which is exactly kda_chunk_fwd.  Other arguments as kda_chunk_fwd.

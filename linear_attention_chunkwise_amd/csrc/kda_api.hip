@@ -114,6 +114,9 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     if (!(dk == 64 || dk == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dk", dk);
     if (!(dv == 64 || dv == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dv", dv);
     if ((int64_t)N * H > (int64_t)1 << 30) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "N*H", (long long)N * H);
+    // the kernel addresses one 32-token chunk of a head's rows with 32-bit byte offsets
+    if ((int64_t)H * (dk > dv ? dk : dv) > (int64_t)1 << 22)
+        return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "H*d", (long long)H * (dk > dv ? dk : dv));
     if (in_dtype == KDA_F32 && dk != 64)
         return fail(KDA_ERR_UNSUPPORTED, "%s: float32 inputs are supported at dk = 64 only (got %lld)", "in_dtype", dk);
 

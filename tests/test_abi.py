@@ -69,6 +69,7 @@ def _fwd(lib, **kw):
     (dict(B=2, N=2, cu=FAKE), binding.KDA_ERR_INVALID_ARGUMENT),   # packed needs B == 1
     (dict(dk=96), binding.KDA_ERR_UNSUPPORTED),
     (dict(dv=32), binding.KDA_ERR_UNSUPPORTED),
+    (dict(T=0, H=1 << 16), binding.KDA_ERR_UNSUPPORTED),           # H * d past 32-bit chunk offsets
     (dict(ind=1), binding.KDA_ERR_UNSUPPORTED),                    # f32 inputs at dk = 128
     (dict(o=FAKE), binding.KDA_ERR_INVALID_ARGUMENT),              # o aliases q
     (dict(S0=FAKE * 64, ST=FAKE * 64 + 16), binding.KDA_ERR_INVALID_ARGUMENT),  # partial alias
