@@ -124,3 +124,59 @@ def kda_gate(z, A_log, g_min=G_MIN):
     x = np.exp(A)[:, None] * z
     with np.errstate(over="ignore"):
         return g_min / (1.0 + np.exp(-x))
+
+
+# ----------------------------------------------------------------------------- around the operator
+# The weight-free steps that eq. (2) and eq. (6) of §2.1.1 apply around the recurrence, for the
+# fused decode: L2-normalised q and k, beta = Sigmoid of its logit, and the output gate
+# y = Sigmoid(G) * RMSNorm(o~) with G = W_g x given (W_o, the projections, ShortConv and Swish need
+# trained weights and stay outside).
+
+L2NORM_FLOOR = 1e-12   # the norm is floored so that a zero vector stays zero
+
+
+def l2norm(x):
+    """x / max(||x||_2, 1e-12) over the last axis, float64 (eq. (2): L2Norm of q and k)."""
+    x = _f64(x)
+    n = np.sqrt((x * x).sum(-1, keepdims=True))
+    return x / np.maximum(n, L2NORM_FLOOR)
+
+
+def sigmoid(x):
+    """1 / (1 + exp(-x)), float64 (eq. (2) for beta, eq. (6) for the output gate)."""
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def gated_rmsnorm(o, G, weight=None, eps=1e-6):
+    """Sigmoid(G) * RMSNorm(o) over the last axis (per head), eq. (6) without W_o:
+    RMSNorm(o) = o / sqrt(mean(o^2) + eps) * weight (weight None: ones).  float64."""
+    o, G = _f64(o), _f64(G)
+    r = o / np.sqrt((o * o).mean(-1, keepdims=True) + eps)
+    if weight is not None:
+        r = r * _f64(weight)
+    return sigmoid(G) * r
+
+
+def kda_fused_decode(q, k, v, z, A_log, b, S, G, weight=None, eps=1e-6, scale=1.0, n_commit=None):
+    """K decode tokens per (sequence, head) with the fused prologue and epilogue: q, k
+    L2-normalised, beta = Sigmoid(b), g = kda_gate(z, A_log), the recurrence (eq. (1)) from S,
+    outputs gated_rmsnorm(o~, G, weight, eps).  q, k, z [N, K, H, dk]; v, G [N, K, H, dv];
+    b [N, K, H]; S [N, H, dk, dv].  Returns (y [N, K, H, dv], state after n_commit[n] tokens)
+    in float64 (n_commit None: all K)."""
+    qn, kn = l2norm(q), l2norm(k)
+    beta = sigmoid(b)
+    g = kda_gate(z, A_log)
+    S = _f64(S)
+    N, K = qn.shape[:2]
+    o, _ = kda_forward(qn, kn, v, g, beta, S, scale=scale)
+    y = gated_rmsnorm(o, G, weight, eps)
+    S_out = S.copy()
+    for n in range(N):
+        c = K if n_commit is None else max(0, min(K, int(n_commit[n])))
+        if c > 0:
+            _, s = kda_forward(qn[n:n + 1, :c], kn[n:n + 1, :c], _f64(v)[n:n + 1, :c], g[n:n + 1, :c],
+                               beta[n:n + 1, :c], S[n:n + 1], scale=scale)
+            S_out[n] = s[0]
+    return y, S_out

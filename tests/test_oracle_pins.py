@@ -458,3 +458,85 @@ def test_c_oracle_takes_float64_decay():
     a = kda_oracle.kda_forward(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
     b = c_oracle.kda_forward(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
     assert _rel(b[0], a[0]) < 1e-13 and _rel(b[1], a[1]) < 1e-13
+
+
+# ----------------------------------------------------------------------------- fused decode steps
+
+def _fused_pins(l2norm, sigmoid, gated_rmsnorm):
+    import scipy.special
+    import sklearn.preprocessing
+    rng = np.random.default_rng(9)
+    errs = {}
+    x = rng.standard_normal((5, 3, 16)) * 2.0
+    # L2Norm against scikit-learn's row normalisation; unit norm; invariant to positive scale;
+    # a zero vector stays zero (the floor), never NaN
+    ref = sklearn.preprocessing.normalize(x.reshape(-1, 16)).reshape(x.shape)
+    errs["l2_sklearn"] = float(np.abs(l2norm(x) - ref).max())
+    errs["l2_scale"] = float(np.abs(l2norm(3.7 * x) - l2norm(x)).max())
+    zv = l2norm(np.zeros((2, 16)))
+    errs["l2_zero"] = 0.0 if np.all(zv == 0) else 1.0
+    # Sigmoid against scipy
+    errs["sigmoid"] = float(np.abs(sigmoid(x) - scipy.special.expit(x)).max())
+    # Sigmoid(G) * RMSNorm(o) * w against torch's rms_norm (float64)
+    o = rng.standard_normal((4, 2, 32))
+    G = rng.standard_normal((4, 2, 32))
+    w = rng.standard_normal(32)
+    t = torch.nn.functional.rms_norm(torch.from_numpy(o), (32,), torch.from_numpy(w), 1e-6).numpy()
+    errs["rms_torch"] = float(np.abs(gated_rmsnorm(o, G, w, 1e-6) - scipy.special.expit(G) * t).max())
+    # closed form: a constant vector c with G = 0 and no weight gives 0.5 c / sqrt(c^2 + eps)
+    c = np.full((1, 8), -2.5)
+    errs["rms_const"] = float(np.abs(gated_rmsnorm(c, np.zeros((1, 8)), None, 1e-6)
+                                     - 0.5 * (-2.5) / math.sqrt(6.25 + 1e-6)).max())
+    return errs
+
+
+def test_fused_decode_pins():
+    errs = _fused_pins(kda_oracle.l2norm, kda_oracle.sigmoid, kda_oracle.gated_rmsnorm)
+    for name, err in errs.items():
+        assert err <= 1e-12, f"fused pin {name}: {err:.3e}"
+
+
+FUSED_MUTANTS = {
+    "l2_no_floor": (lambda x: _np(x) / np.sqrt((_np(x) ** 2).sum(-1, keepdims=True)), None, None),
+    "rms_mean_removed": (None, None, lambda o, G, w=None, eps=1e-6: kda_oracle.sigmoid(G) * (
+        (_np(o) - _np(o).mean(-1, keepdims=True)) / np.sqrt(_np(o).var(-1, keepdims=True) + eps)
+        * (1.0 if w is None else _np(w)))),
+    "weight_inside": (None, None, lambda o, G, w=None, eps=1e-6: kda_oracle.gated_rmsnorm(
+        _np(o) * (1.0 if w is None else _np(w)), G, None, eps)),
+    "gate_mirrored": (None, lambda x: 1.0 / (1.0 + np.exp(_np(x))), None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_MUTANTS))
+def test_fused_pins_catch_planted_mistake(name):
+    import warnings
+    l2, sg, rms = FUSED_MUTANTS[name]
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        errs = _fused_pins(l2 or kda_oracle.l2norm, sg or kda_oracle.sigmoid,
+                           rms or kda_oracle.gated_rmsnorm)
+    assert any(not (e <= 1e-6) for e in errs.values()), f"planted mistake {name} passes every pin"
+
+
+def test_fused_decode_invariants():
+    """Positive rescaling of the raw q and k changes nothing (they are L2-normalised); n_commit = 0
+    leaves the state; K tokens at once equal K single-token calls."""
+    from linear_attention_chunkwise_amd import inputs
+    x = inputs.make_prefill_inputs(2, 3, 2, 16, 8, dtype=torch.float32, seed=12, with_logits=True)
+    rng = np.random.default_rng(4)
+    b = rng.standard_normal((2, 3, 2))
+    G = rng.standard_normal((2, 3, 2, 8))
+    w = rng.standard_normal(8)
+    args = (x["v"], x["z"], x["A_log"], b, x["S0"], G, w)
+    y1, s1 = kda_oracle.kda_fused_decode(x["q"], x["k"], *args)
+    y2, s2 = kda_oracle.kda_fused_decode(_np(x["q"]) * 2.5, _np(x["k"]) * 0.3, *args)
+    assert np.abs(y1 - y2).max() < 1e-12 and np.abs(s1 - s2).max() < 1e-12
+    _, s0 = kda_oracle.kda_fused_decode(x["q"], x["k"], *args, n_commit=[0, 0])
+    assert np.array_equal(s0, _np(x["S0"]))
+    S = _np(x["S0"])
+    for t in range(3):
+        sl = lambda a: _np(a)[:, t:t + 1]
+        yt, S = kda_oracle.kda_fused_decode(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["z"]),
+                                            x["A_log"], b[:, t:t + 1], S, G[:, t:t + 1], w)
+        assert np.abs(yt[:, 0] - y1[:, t]).max() < 1e-12
+    assert np.abs(S - s1).max() < 1e-12
