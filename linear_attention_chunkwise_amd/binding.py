@@ -21,7 +21,8 @@ KDA_BF16, KDA_F32 = 0, 1
 # every symbol include/kda.h declares
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_gate", "kda_chunk_fwd_cp",
            "kda_chunk_fwd_cp_workspace_size", "kda_recurrent_step", "kda_recurrent_step_gate",
-           "kda_recurrent_multi", "kda_status_string", "kda_last_error", "kda_version")
+           "kda_recurrent_multi", "kda_recurrent_multi_fused", "kda_status_string",
+           "kda_last_error", "kda_version")
 
 _lib = None
 
@@ -67,6 +68,10 @@ def load(path: str = LIB_PATH):
     lib.kda_recurrent_step_gate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_step_gate.restype = ctypes.c_int
+    lib.kda_recurrent_multi_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                              i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_float, vp, vp]
+    lib.kda_recurrent_multi_fused.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -368,3 +373,45 @@ def recurrent_step_gate(q, k, v, z, A_log, beta, S, *, scale: float = 1.0, out_d
                                      dk, dv, _dt(q), _dt(o), float(scale), _p(o), _stream(dev))
     _check(st)
     return o
+
+
+def recurrent_multi_fused(q, k, v, z, A_log, beta_logit, G, S, n_commit=None, *, norm_weight=None,
+                          eps: float = 1e-6, scale: float = 1.0, out_dtype=None, y=None,
+                          outputs: bool = True):
+    """recurrent_multi with the weight-free steps around the operator fused in: q, k
+    L2-normalised, beta = Sigmoid(beta_logit), g from the logits z and A_log, and outputs
+    y = Sigmoid(G) * RMSNorm(o~) (weight norm_weight [dv] float32 or None, eps).  q, k, z
+    [N,K,H,dk], v, G [N,K,H,dv], beta_logit [N,K,H] share a dtype; S advanced in place as in
+    recurrent_multi.  Returns y [N,K,H,dv] (None with outputs=False)."""
+    lib = load()
+    dev = q.device
+    N, K, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _require(q, "q", dev, dt)
+    _require(k, "k", dev, dt, (N, K, H, dk))
+    _require(v, "v", dev, dt, (N, K, H, dv))
+    _require(z, "z", dev, dt, (N, K, H, dk))
+    _require(A_log, "A_log", dev, torch.float32, (H,))
+    _require(beta_logit, "beta_logit", dev, dt, (N, K, H))
+    _require(S, "S", dev, torch.float32, (N, H, dk, dv))
+    if n_commit is not None:
+        _require(n_commit, "n_commit", dev, torch.int32, (N,))
+    if norm_weight is not None:
+        _require(norm_weight, "norm_weight", dev, torch.float32, (dv,))
+    out_dtype = out_dtype or dt
+    if outputs:
+        _require(G, "G", dev, dt, (N, K, H, dv))
+        if y is None:
+            y = torch.empty((N, K, H, dv), dtype=out_dtype, device=dev)
+        else:
+            _require(y, "y", dev, out_dtype, (N, K, H, dv))
+    else:
+        y = None
+    st = lib.kda_recurrent_multi_fused(_p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta_logit),
+                                       _p(G) if outputs else None, _p(norm_weight), float(eps), _p(S),
+                                       _p(n_commit), N, K, H, dk, dv, _dt(q),
+                                       _dt(y) if y is not None else _dt(q), float(scale), _p(y),
+                                       _stream(dev))
+    _check(st)
+    return y

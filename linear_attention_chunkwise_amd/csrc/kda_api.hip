@@ -358,4 +358,59 @@ kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, cons
     return hip_status(kda::launch_decode_step(a));
 }
 
+kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v, const void* z,
+                                     const float* A_log, const void* beta_logit, const void* G,
+                                     const float* norm_weight, float eps, float* S,
+                                     const int32_t* n_commit, int32_t N, int32_t K, int32_t H,
+                                     int32_t dk, int32_t dv, kda_dtype in_dtype,
+                                     kda_dtype out_dtype, float scale, void* y, hipStream_t stream) {
+    KDA_TRY(check_dtype(in_dtype, "in_dtype"));
+    KDA_TRY(check_dtype(out_dtype, "out_dtype"));
+    if (N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "N", N);
+    if (K < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "K", K);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "H", H);
+    if (!(eps >= 0.f)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0%.0lld", "eps");
+    if (!(dk == 64 || dk == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dk", dk);
+    if (!(dv == 64 || dv == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dv", dv);
+    if ((int64_t)N * H > (int64_t)1 << 30) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "N*H", (long long)N * H);
+    if (N == 0 || K == 0) return ok();
+    const size_t es = dsize(in_dtype);
+    KDA_TRY(check_ptr(q, 16, "q"));
+    KDA_TRY(check_ptr(k, 16, "k"));
+    KDA_TRY(check_ptr(v, 16, "v"));
+    KDA_TRY(check_ptr(z, 16, "z"));
+    KDA_TRY(check_ptr(A_log, 4, "A_log"));
+    KDA_TRY(check_ptr(beta_logit, es, "beta_logit"));
+    KDA_TRY(check_ptr(S, 16, "S"));
+    if (n_commit) KDA_TRY(check_ptr(n_commit, 4, "n_commit"));
+    if (norm_weight) KDA_TRY(check_ptr(norm_weight, 16, "norm_weight"));
+    const size_t nh = (size_t)N * H, nt = nh * (size_t)K;
+    if (y) {
+        KDA_TRY(check_ptr(y, 16, "y"));
+        KDA_TRY(check_ptr(G, es, "G"));
+        const size_t ny = nt * dv * dsize(out_dtype);
+        if (overlaps(y, ny, S, nh * dk * dv * 4) || overlaps(y, ny, q, nt * dk * es) ||
+            overlaps(y, ny, k, nt * dk * es) || overlaps(y, ny, v, nt * dv * es) ||
+            overlaps(y, ny, z, nt * dk * es) || overlaps(y, ny, beta_logit, nt * es) ||
+            overlaps(y, ny, G, nt * dv * es) || overlaps(y, ny, A_log, (size_t)H * 4) ||
+            (norm_weight && overlaps(y, ny, norm_weight, (size_t)dv * 4)))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps the state or an input%.0lld", "y");
+    }
+    if (n_commit && overlaps(n_commit, (size_t)N * 4, S, nh * dk * dv * 4))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S%.0lld", "n_commit");
+    kda::DecodeArgs a{q, k, v, nullptr, beta_logit, S, (int32_t)nh, dk, dv,
+                      in_dtype == KDA_F32, out_dtype == KDA_F32, scale, y, stream};
+    a.K = K;
+    a.N = N;
+    a.H = H;
+    a.n_commit = n_commit;
+    a.z = z;
+    a.A_log = A_log;
+    a.fused = true;
+    a.G = G;
+    a.norm_w = norm_weight;
+    a.eps = eps;
+    return hip_status(kda::launch_decode_step(a));
+}
+
 }  // extern "C"

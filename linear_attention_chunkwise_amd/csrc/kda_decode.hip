@@ -215,6 +215,132 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
     }
 }
 
+// The multi-token step fused with the weight-free steps around it (§2.1.1): before the recurrence,
+// eq. (2)'s L2Norm of q and k (x / max(||x||, 1e-12)), beta = Sigmoid of its logit and the bounded
+// decay map of eq. (5); after it, eq. (6) without W_o: y = Sigmoid(G) * RMSNorm(o~) per head, with
+// RMSNorm(o~) = o~ / sqrt(mean(o~^2) + eps) * w.  The normalisations need two more dk
+// reductions per token (q . q, k . k, finished with the others) and one dv reduction (o~ . o~,
+// inside each row group's lanes).  Same mapping and commit rule as decode_multi_kernel.
+template <int DK, int DV, bool IN_F32, bool OUT_F32>
+__global__ __launch_bounds__(256) void decode_fused_kernel(const void* __restrict__ qp,
+                                                           const void* __restrict__ kp,
+                                                           const void* __restrict__ vp,
+                                                           const void* __restrict__ zp,
+                                                           const float* __restrict__ A_log,
+                                                           const void* __restrict__ bp,
+                                                           const void* __restrict__ Gp,
+                                                           const float* __restrict__ norm_w, float eps,
+                                                           float* __restrict__ S,
+                                                           const int32_t* __restrict__ n_commit,
+                                                           int32_t N, int32_t H, int32_t K,
+                                                           float scale, void* __restrict__ op) {
+    constexpr int CG = DV / 4;
+    constexpr int NRG = 256 / CG;
+    constexpr int RPG = DK / NRG;
+    static_assert(RPG >= 1 && DK % NRG == 0 && 64 % CG == 0, "decode tiling");
+    __shared__ f32x4 red_y[2][NRG][CG];
+    __shared__ f32x4 red_z[2][NRG][CG];
+    __shared__ f32x4 red_s[2][NRG];   // q . k, q . q, k . k (and one spare) per row group
+
+    const int unit = blockIdx.x;        // sequence * H + head
+    if (unit >= N * H) return;
+    const int n = unit / H, h = unit % H;
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    const int r0 = rg * RPG;
+    int commit = n_commit ? n_commit[n] : K;
+    commit = commit < 0 ? 0 : (commit > K ? K : commit);
+    const float ea = __expf(A_log[h]);
+    f32x4 w = f32x4{1.f, 1.f, 1.f, 1.f};
+    if (norm_w) w = ld<f32x4>(norm_w + 4 * cg);
+
+    float* Su = S + (size_t)unit * DK * DV;
+    f32x4 s[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
+
+    auto in_at = [&](const void* p, size_t idx) -> float {
+        if constexpr (IN_F32) return reinterpret_cast<const float*>(p)[idx];
+        else return bf2f(reinterpret_cast<const bf16*>(p)[idx]);
+    };
+    auto sigm = [](float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); };
+    for (int tok = 0; tok < K; ++tok) {
+        const int pb = tok & 1;
+        const size_t row = ((size_t)n * K + tok) * H + h;   // token row of [N, K, H, *]
+        const size_t kb = row * DK;
+        f32x4 y = zero4(), z = zero4();
+        float qk = 0.f, qq = 0.f, kk = 0.f;
+        float kv[RPG];
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) {
+            const float a = decay_at<IN_F32, true>(nullptr, zp, ea, kb + r0 + i);
+            kv[i] = in_at(kp, kb + r0 + i);
+            const float qv = in_at(qp, kb + r0 + i);
+            s[i] *= a;
+            y += kv[i] * s[i];
+            z += qv * s[i];
+            qk += qv * kv[i];
+            qq += qv * qv;
+            kk += kv[i] * kv[i];
+        }
+        red_y[pb][rg][cg] = y;
+        red_z[pb][rg][cg] = z;
+        if (cg == 0) red_s[pb][rg] = f32x4{qk, qq, kk, 0.f};
+        __syncthreads();   // the other parity's buffers were last read before this barrier
+        f32x4 yt = zero4(), zt = zero4(), st4 = zero4();
+#pragma unroll
+        for (int j = 0; j < NRG; ++j) {
+            yt += red_y[pb][j][cg];
+            zt += red_z[pb][j][cg];
+            st4 += red_s[pb][j];
+        }
+        // L2Norm of q and k as scale factors on the sums (and on k in the state update)
+        const float rq = 1.f / fmaxf(sqrtf(st4[1]), 1e-12f);
+        const float rk = 1.f / fmaxf(sqrtf(st4[2]), 1e-12f);
+        const float b = sigm(in_at(bp, row));
+        const size_t vb = row * DV + 4 * cg;
+        f32x4 u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) u[c] = b * (in_at(vp, vb + c) - yt[c] * rk);
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) s[i] += (kv[i] * rk) * u;
+        if (tok + 1 == commit) {
+#pragma unroll
+            for (int i = 0; i < RPG; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
+        }
+        if (op) {
+            // o~ for this thread's 4 columns, then RMSNorm over dv across the CG lanes of the row
+            // group (one wave holds whole row groups) and the gate
+            const f32x4 o = scale * (zt * rq + (st4[0] * rq * rk) * u);
+            float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+#pragma unroll
+            for (int m = 1; m < CG; m *= 2) ss += __shfl_xor(ss, m, 64);
+            const float inv = rsqrtf(ss / DV + eps);
+            if (rg == 0) {
+                f32x4 yo;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) yo[c] = sigm(in_at(Gp, vb + c)) * (o[c] * inv * w[c]);
+                if constexpr (OUT_F32) {
+                    st<f32x4>(reinterpret_cast<float*>(op) + vb, yo);
+                } else {
+                    bf16x4 ob{f2bf(yo[0]), f2bf(yo[1]), f2bf(yo[2]), f2bf(yo[3])};
+                    st<bf16x4>(reinterpret_cast<bf16*>(op) + vb, ob);
+                }
+            }
+        }
+    }
+}
+
+template <int DK, int DV, bool IN_F32, bool OUT_F32>
+static hipError_t launch_fused(const DecodeArgs& a) {
+    const int64_t units = (int64_t)a.N * a.H;
+    if (units == 0 || a.K == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_fused_kernel<DK, DV, IN_F32, OUT_F32>), dim3((unsigned)units), dim3(256), 0,
+                       a.stream, a.q, a.k, a.v, a.z, a.A_log, a.beta, a.G, a.norm_w, a.eps, a.S,
+                       a.n_commit, a.N, a.H, a.K, a.scale, a.o);
+    return hipGetLastError();
+}
+
 template <int DK, int DV, bool IN_F32, bool OUT_F32, bool GATE>
 static hipError_t launch_decode(const DecodeArgs& a) {
     if (a.NH == 0) return hipSuccess;
@@ -248,6 +374,10 @@ static hipError_t dispatch_io(const DecodeArgs& a) {
 
 template <int DK, int DV>
 static hipError_t dispatch_gate(const DecodeArgs& a) {
+    if (a.fused) {
+        if (a.in_f32) return a.out_f32 ? launch_fused<DK, DV, true, true>(a) : launch_fused<DK, DV, true, false>(a);
+        return a.out_f32 ? launch_fused<DK, DV, false, true>(a) : launch_fused<DK, DV, false, false>(a);
+    }
     return a.z ? dispatch_io<DK, DV, true>(a) : dispatch_io<DK, DV, false>(a);
 }
 

@@ -60,6 +60,12 @@ struct DecodeArgs {
     // decay map in the kernel (g unused), as in PrefillArgs; H must be set
     const void* z = nullptr;
     const float* A_log = nullptr;
+    // fused prologue/epilogue (K > 0, z set): q, k L2-normalised, beta holds logits, outputs
+    // Sigmoid(G) * RMSNorm(o~) with weight norm_w (null: ones) and eps
+    bool fused = false;
+    const void* G = nullptr;
+    const float* norm_w = nullptr;
+    float eps = 0.f;
 };
 
 hipError_t launch_chunk_fwd(const PrefillArgs& a);

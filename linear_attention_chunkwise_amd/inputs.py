@@ -164,3 +164,23 @@ def make_decode_inputs(N, H, dk, dv, *, dtype=torch.bfloat16, seed=0, device="cp
     beta = torch.sigmoid(_randn((N, H), gen, device)).to(dtype)
     S = _randn((N, H, dk, dv), gen, device) * S_std
     return dict(q=q, k=k, v=v, g=g, beta=beta, S=S)
+
+
+def make_fused_decode_inputs(N, K, H, dk, dv, *, dtype=torch.bfloat16, seed=0, device="cpu",
+                             A_std=0.5, S_std=0.1):
+    """K decode tokens per (sequence, head) as the fused decode takes them: the raw projections
+    q, k, v ~ N(0, 1) (not normalised), decay logits z ~ N(0, 1) and per-head log-scales
+    A_log ~ N(0, A_std), beta logits ~ N(0, 1), output-gate pre-activations G ~ N(0, 1), an RMSNorm
+    weight 1 + 0.1 N(0, 1) (float32 [dv]) and states S ~ N(0, S_std)."""
+    device = torch.device(device)
+    gen = _gen(device, seed)
+    q = _randn((N, K, H, dk), gen, device).to(dtype)
+    k = _randn((N, K, H, dk), gen, device).to(dtype)
+    v = _randn((N, K, H, dv), gen, device).to(dtype)
+    z = _randn((N, K, H, dk), gen, device).to(dtype)
+    A_log = (_randn((H,), gen, device) * A_std).float()
+    b = _randn((N, K, H), gen, device).to(dtype)
+    G = _randn((N, K, H, dv), gen, device).to(dtype)
+    w = (1.0 + 0.1 * _randn((dv,), gen, device)).float()
+    S = _randn((N, H, dk, dv), gen, device) * S_std
+    return dict(q=q, k=k, v=v, z=z, A_log=A_log, beta_logit=b, G=G, norm_weight=w, S=S)

@@ -242,3 +242,32 @@ def test_recurrent_step_gate_rejects_on_host(lib):
     assert call(A=None) == binding.KDA_ERR_INVALID_ARGUMENT
     assert call(o=FAKE * 16) == binding.KDA_ERR_INVALID_ARGUMENT      # o aliases S
     assert call(N=0, q=None) == binding.KDA_OK
+
+
+def _fused(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, z=FAKE, A=FAKE, b=FAKE, G=FAKE, w=None, eps=1e-6, S=FAKE * 16,
+             nc=None, N=4, K=3, H=2, dk=128, dv=128, ind=0, outd=0, y=FAKE * 64)
+    a.update(kw)
+    return lib.kda_recurrent_multi_fused(a["q"], a["k"], a["v"], a["z"], a["A"], a["b"], a["G"],
+                                         a["w"], ctypes.c_float(a["eps"]), a["S"], a["nc"], a["N"],
+                                         a["K"], a["H"], a["dk"], a["dv"], a["ind"], a["outd"],
+                                         ctypes.c_float(1.0), a["y"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(eps=-1.0), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(eps=float("nan")), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(z=None), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(G=None), binding.KDA_ERR_INVALID_ARGUMENT),              # outputs asked, no gate input
+    (dict(w=FAKE + 4), binding.KDA_ERR_INVALID_ARGUMENT),          # misaligned weight
+    (dict(y=FAKE * 16 + 128), binding.KDA_ERR_INVALID_ARGUMENT),   # y overlaps S
+    (dict(dk=32), binding.KDA_ERR_UNSUPPORTED),
+])
+def test_recurrent_multi_fused_rejects_on_host(lib, kw, status):
+    assert _fused(lib, **kw) == status
+    assert lib.kda_last_error() != b""
+
+
+def test_recurrent_multi_fused_empty_and_state_only_checks(lib):
+    assert _fused(lib, K=0, q=None) == binding.KDA_OK
+    assert _fused(lib, y=None, G=None, z=None) == binding.KDA_ERR_INVALID_ARGUMENT   # z still needed

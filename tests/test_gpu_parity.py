@@ -697,3 +697,66 @@ def test_range_check_on_request(gpu_lib, monkeypatch):
     g[0, 0, 0, 0] = -5.5
     binding.chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])   # unchecked
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ fused decode
+
+def _fused_oracle(x, S, commits, weight=True, eps=1e-6, scale=1.0):
+    from oracle import kda_oracle
+    c = lambda t: t.detach().cpu()
+    return kda_oracle.kda_fused_decode(c(x["q"]), c(x["k"]), c(x["v"]), c(x["z"]), c(x["A_log"]),
+                                       c(x["beta_logit"]), c(S), c(x["G"]),
+                                       c(x["norm_weight"]) if weight else None, eps, scale, commits)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128), (64, 64)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["o_f32", "o_bf16"])
+def test_fused_decode_small(gpu_lib, dk, dv, out_dtype):
+    from linear_attention_chunkwise_amd import binding
+    N, K, H = 6, 3, 2
+    x = _to_dev(inputs.make_fused_decode_inputs(N, K, H, dk, dv, seed=dk + dv))
+    commits = [3, 0, 1, 2, 3, 7]
+    S = x["S"].clone()
+    y = binding.recurrent_multi_fused(x["q"], x["k"], x["v"], x["z"], x["A_log"], x["beta_logit"],
+                                      x["G"], S, torch.tensor(commits, dtype=torch.int32, device="cuda"),
+                                      norm_weight=x["norm_weight"], eps=1e-5, scale=0.8,
+                                      out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ry, rS = _fused_oracle(x, x["S"], [min(c, K) for c in commits], eps=1e-5, scale=0.8)
+    assert_close("y", y.float().cpu().numpy(), ry)
+    assert_close("S", S.cpu().numpy(), rS)
+
+
+def test_fused_decode_unit_weight_state_only_and_f32(gpu_lib):
+    from linear_attention_chunkwise_amd import binding
+    x = _to_dev(inputs.make_fused_decode_inputs(4, 5, 3, 64, 64, dtype=torch.float32, seed=40))
+    S = x["S"].clone()
+    y = binding.recurrent_multi_fused(x["q"], x["k"], x["v"], x["z"], x["A_log"], x["beta_logit"],
+                                      x["G"], S)
+    torch.cuda.synchronize()
+    ry, rS = _fused_oracle(x, x["S"], None, weight=False)
+    assert_close("y", y.cpu().numpy(), ry)
+    assert_close("S", S.cpu().numpy(), rS)
+    S2 = x["S"].clone()
+    assert binding.recurrent_multi_fused(x["q"], x["k"], x["v"], x["z"], x["A_log"], x["beta_logit"],
+                                         None, S2, outputs=False) is None
+    torch.cuda.synchronize()
+    assert_close("S state-only", S2.cpu().numpy(), rS)
+
+
+def test_fused_decode_workload_n1024_h32_k4(gpu_lib):
+    from linear_attention_chunkwise_amd import binding
+    cfg = inputs.DECODE_CONFIG
+    K = 4
+    x = inputs.make_fused_decode_inputs(cfg.N, K, cfg.H, cfg.dk, cfg.dv, seed=41, device="cuda")
+    gen = torch.Generator().manual_seed(41)
+    commits = torch.randint(0, K + 1, (cfg.N,), generator=gen, dtype=torch.int32)
+    S = x["S"].clone()
+    y = binding.recurrent_multi_fused(x["q"], x["k"], x["v"], x["z"], x["A_log"], x["beta_logit"],
+                                      x["G"], S, commits.cuda(), norm_weight=x["norm_weight"])
+    torch.cuda.synchronize()
+    idx = torch.arange(0, cfg.N, 97)
+    sub = {k: (x[k][idx] if k not in ("A_log", "norm_weight") else x[k]) for k in x}
+    ry, rS = _fused_oracle(sub, sub["S"], commits[idx].tolist())
+    assert_close("y", y[idx].float().cpu().numpy(), ry)
+    assert_close("S", S[idx].cpu().numpy(), rS)
