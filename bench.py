@@ -304,6 +304,20 @@ def main():
                                "what": "kda_recurrent_multi: 4 tokens per (sequence, head) per "
                                        "state pass, 1024 sequences x 32 heads"}
         del m, om, Sm
+        f = inputs.make_fused_decode_inputs(dcfg.N, K, dcfg.H, dcfg.dk, dcfg.dv, seed=2, device=dev)
+        yf = torch.empty((dcfg.N, K, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)
+        f_ms = time_launches(lambda: binding.recurrent_multi_fused(
+            f["q"], f["k"], f["v"], f["z"], f["A_log"], f["beta_logit"], f["G"], f["S"],
+            norm_weight=f["norm_weight"], y=yf))
+        # per token-head: q, k, z, v, G, beta logit in, y out (bf16); state read + written once
+        fbytes = dcfg.N * dcfg.H * (2 * dcfg.dk * dcfg.dv * 4 +
+                                    K * ((3 * dcfg.dk + 2 * dcfg.dv) * 2 + 2 + dcfg.dv * 2))
+        res["decode_multi_fused"] = {"K": K, "us": f_ms * 1e3, "us_per_token": f_ms * 1e3 / K,
+                                     "alg_bytes": fbytes, "GBps": fbytes / (f_ms * 1e-3) / 1e9,
+                                     "what": "kda_recurrent_multi_fused: the 4-token pass with q/k "
+                                             "L2Norm, beta = Sigmoid(logit), decay map, "
+                                             "Sigmoid(G) * RMSNorm(o~) fused in"}
+        del f, yf
         # packed prefill: 64 sequences, lognormal lengths (median 1024, longest 65536)
         vcfg = inputs.CONFIGS["varlen64_h32_d128"]
         xv = inputs.make_config_inputs(vcfg, seed=0, device=dev)
