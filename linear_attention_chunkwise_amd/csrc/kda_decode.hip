@@ -73,12 +73,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qp
         else return bf2f(reinterpret_cast<const bf16*>(p)[idx]);
     };
     const size_t kb = (size_t)unit * DK;
-    const float ea = GATE ? __expf(A_log[unit % H]) : 0.f;
+    // decay map (GATE): once per channel through LDS rather than in each of the CG threads that
+    // hold the channel's row (the state loads above are already in flight)
+    __shared__ float dec[GATE ? DK : 1];
+    if constexpr (GATE) {
+        if (t < DK) dec[t] = decay_at<IN_F32, true>(g, zp, __expf(A_log[unit % H]), kb + t);
+        __syncthreads();
+    }
     f32x4 y = zero4(), z = zero4();
     float qk = 0.f;
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
-        const float a = decay_at<IN_F32, GATE>(g, zp, ea, kb + r0 + i);
+        const float a = GATE ? dec[r0 + i] : __expf(g[kb + r0 + i]);
         const float kv = in_at(kp, kb + r0 + i);
         const float qv = in_at(qp, kb + r0 + i);
         s[i] *= a;
