@@ -65,17 +65,22 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2, K=1):
                                            dv * out_bytes))
 
 
-def time_launches(fn, reps=10):
-    """Average duration of fn's launches (HIP events on the current stream), after 2 warmups."""
-    for _ in range(2):
+def time_launches(fn, reps=10, groups=3, warmup=5):
+    """Duration of one of fn's launches in ms (HIP events on the current stream): the median over
+    `groups` groups of `reps` back-to-back launches, after `warmup` launches."""
+    import statistics
+    for _ in range(warmup):
         fn()
     e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    e[0].record()
-    for _ in range(reps):
-        fn()
-    e[1].record()
-    torch.cuda.synchronize()
-    return e[0].elapsed_time(e[1]) / reps
+    out = []
+    for _ in range(groups):
+        e[0].record()
+        for _ in range(reps):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        out.append(e[0].elapsed_time(e[1]) / reps)
+    return statistics.median(out)
 
 
 def kernel_source_hash(name):
