@@ -760,3 +760,30 @@ def test_fused_decode_workload_n1024_h32_k4(gpu_lib):
     ry, rS = _fused_oracle(sub, sub["S"], commits[idx].tolist())
     assert_close("y", y[idx].float().cpu().numpy(), ry)
     assert_close("S", S[idx].cpu().numpy(), rS)
+
+
+def test_multi_and_fused_decode_long_replay(gpu_lib):
+    """K = 33 tokens in one state pass (the LDS buffers alternate by token parity many times),
+    plain and fused, with commit points at both ends and in the middle."""
+    from linear_attention_chunkwise_amd import binding
+    N, K, H = 4, 33, 2
+    x = inputs.make_prefill_inputs(N, K, H, 128, 64, seed=50)
+    d = _to_dev(x)
+    commits = [33, 0, 17, 1]
+    S = d["S0"].clone()
+    o = binding.recurrent_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], S,
+                                torch.tensor(commits, dtype=torch.int32, device="cuda"),
+                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rS = _oracle_multi(x, x["S0"], commits)
+    assert_close("o", o.cpu().numpy(), ro)
+    assert_close("S", S.cpu().numpy(), rS)
+    f = _to_dev(inputs.make_fused_decode_inputs(N, K, H, 64, 128, seed=51))
+    S2 = f["S"].clone()
+    y = binding.recurrent_multi_fused(f["q"], f["k"], f["v"], f["z"], f["A_log"], f["beta_logit"],
+                                      f["G"], S2, torch.tensor(commits, dtype=torch.int32, device="cuda"),
+                                      norm_weight=f["norm_weight"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ry, rS2 = _fused_oracle(f, f["S"], commits)
+    assert_close("y", y.cpu().numpy(), ry)
+    assert_close("S fused", S2.cpu().numpy(), rS2)
