@@ -129,7 +129,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qp
 // replay of accepted tokens, §5.4.2): the state stays in registers across the K tokens; it is
 // written back after the first `commit` tokens (commit = 0: outputs only, state untouched).
 // Tokens are laid out [N, K, H, d]; the reductions use two LDS buffers by token parity, one
-// workgroup barrier per token.
+// workgroup barrier per token.  The per-channel decay of token tok + 1 is computed once per
+// channel into LDS while token tok is processed (the barrier of token tok publishes it), instead
+// of in each of the CG threads holding the channel's row: 822 -> 765 us for 4 tokens at
+// 1024 x 32 heads.
 template <int DK, int DV, bool IN_F32, bool OUT_F32, bool GATE>
 __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restrict__ qp,
                                                            const void* __restrict__ kp,
@@ -149,6 +152,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
     __shared__ f32x4 red_y[2][NRG][CG];
     __shared__ f32x4 red_z[2][NRG][CG];
     __shared__ float red_qk[2][NRG];
+    __shared__ float dec[2][DK];
 
     const int unit = blockIdx.x;        // sequence * H + head
     if (unit >= N * H) return;
@@ -169,16 +173,23 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
         if constexpr (IN_F32) return reinterpret_cast<const float*>(p)[idx];
         else return bf2f(reinterpret_cast<const bf16*>(p)[idx]);
     };
+    // the buffer a token writes was last read before the previous token's barrier
+    auto decay_into = [&](int tok, int buf) {
+        if (t < DK) dec[buf][t] = decay_at<IN_F32, GATE>(g, zp, ea, (((size_t)n * K + tok) * H + h) * DK + t);
+    };
+    decay_into(0, 0);
+    __syncthreads();
     for (int tok = 0; tok < K; ++tok) {
         const int pb = tok & 1;
         const size_t row = ((size_t)n * K + tok) * H + h;   // token row of [N, K, H, *]
         const size_t kb = row * DK;
+        if (tok + 1 < K) decay_into(tok + 1, pb ^ 1);
         f32x4 y = zero4(), z = zero4();
         float qk = 0.f;
         float kv[RPG];
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {
-            const float a = decay_at<IN_F32, GATE>(g, zp, ea, kb + r0 + i);
+            const float a = dec[pb][r0 + i];
             kv[i] = in_at(kp, kb + r0 + i);
             const float qv = in_at(qp, kb + r0 + i);
             s[i] *= a;
