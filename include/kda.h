@@ -43,7 +43,7 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size, aliasing, bad dtype   */
-    KDA_ERR_UNSUPPORTED = 2,      /* a valid request this build does not implement (e.g. dk=96) */
+    KDA_ERR_UNSUPPORTED = 2,      /* a valid request the library does not implement (e.g. dk=96) */
     KDA_ERR_RANGE = 3,            /* g outside [-5, 0] (only with KDA_CHECK_RANGE=1, see below)  */
     KDA_ERR_HIP = 4               /* the HIP runtime reported an error (launch, no device)      */
 } kda_status;
