@@ -190,7 +190,19 @@ def cpu_baseline(x, units_wanted=None):
     return {"value": token_heads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(units)} of {B * H} (sequence, head) units x {T} tokens of the prefill "
                       f"workload ({token_heads} token-heads, float64 C token loop, OpenMP over units, "
-                      f"{dt:.1f} s wall); tokens/s = token-heads/s / H"}
+                      f"{dt:.1f} s wall, {cpu_model()}); tokens/s = token-heads/s / H"}
+
+
+def cpu_model():
+    """The host CPU's model name as the kernel reports it (unknown if it does not)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "CPU model unknown"
 
 
 def main():
