@@ -48,6 +48,7 @@
 // state stays fp32.  Float32 inputs (kFull)
 // carry every operand but A_kk's as a pair.  The scale on q is applied to the outputs
 // (everything is linear in q).
+#include <atomic>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -1027,12 +1028,19 @@ template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
 static hipError_t launch_one(const PrefillArgs& a) {
     using Lay = Layout<DK, F32IN>;
     auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE, RANK>;
-    static bool attr_set = false;   // benign race: the attribute value is idempotent
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, Lay::total);
+    // The LDS limit is a per-device attribute of the kernel: set it once on each device this
+    // instantiation launches on (devices past 63 set it on every launch).  Concurrent first calls
+    // may both set it; the value is the same.
+    static std::atomic<uint64_t> attr_set{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (!(attr_set.load(std::memory_order_relaxed) & bit) || !bit) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                Lay::total);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set.fetch_or(bit, std::memory_order_relaxed);
     }
     const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
     const int64_t units = (int64_t)a.N * a.H * (a.mode == 0 ? 1 : a.nseg);
