@@ -17,10 +17,13 @@
  *      beta  [B, T, H]         S0, S_T [N, H, dk, dv] (float32)
  *    q, k, v and beta share `in_dtype`; o has `out_dtype`.
  *  - Every pointer must be 16-byte aligned (beta: 4-byte aligned is enough).
- *  - Work is enqueued asynchronously on `stream` (0 = the null stream); nothing synchronises the
+ *  - Work runs on the calling thread's current HIP device and is enqueued asynchronously on
+ *    `stream` (0 = the null stream), which must belong to that device; nothing synchronises the
  *    host.  All argument checks run on the host before any launch: on error nothing is enqueued.
  *  - Results are deterministic: no atomics, fixed reduction orders.
- *  - Re-entrant; no global mutable state.
+ *  - Thread-safe and re-entrant.  The only process-wide state is a per-device record of which
+ *    prefill kernels have had their LDS limit raised (set once, idempotent) and the flag of the
+ *    optional domain check below (used under a lock); error text is per thread.
  *  - Domain check (a debug aid, off by default): with the environment variable KDA_CHECK_RANGE=1,
  *    every entry point that reads g first checks on `stream` that each value lies in [-5, 0]
  *    (eq. (5) and the bound after it; NaN fails), synchronises `stream` to read the result, and

@@ -105,6 +105,13 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _on(device, fn, *args):
+    """Calls the library with the tensors' device current: it launches on the current HIP
+    device, on the stream it is given (that device's current stream here)."""
+    with torch.cuda.device(device):
+        return fn(*args)
+
+
 def _require(t, name, device, dtype=None, shape=None):
     if not t.is_cuda or t.device != device:
         raise ValueError(f"{name} must be on {device}")
@@ -150,8 +157,8 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, scale: float = 1.0,
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif S_T is not None:
         _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
-    st = lib.kda_chunk_fwd(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(cu_seqlens), B, T, H,
-                           N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T), _stream(dev))
+    st = _on(dev, lib.kda_chunk_fwd, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(cu_seqlens),
+             B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T), _stream(dev))
     _check(st)
     return o, S_T
 
@@ -193,9 +200,9 @@ def chunk_fwd_ckpt(q, k, v, g, beta, S0=None, cu_seqlens=None, *, interval: int,
         ckpt = torch.zeros((N, H, capacity, dk, dv), dtype=torch.float32, device=dev)
     else:
         _require(ckpt, "ckpt", dev, torch.float32, (N, H, capacity, dk, dv))
-    st = lib.kda_chunk_fwd_ckpt(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(cu_seqlens), B, T,
-                                H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
-                                int(interval), int(capacity), _p(ckpt), _stream(dev))
+    st = _on(dev, lib.kda_chunk_fwd_ckpt, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
+             _p(cu_seqlens), B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
+             int(interval), int(capacity), _p(ckpt), _stream(dev))
     _check(st)
     return o, S_T, ckpt
 
@@ -247,10 +254,10 @@ def chunk_fwd_cp(q, k, v, g, beta, S0=None, cu_seqlens=None, *, segments: int, s
     need = lib.kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, int(segments))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    st = lib.kda_chunk_fwd_cp(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(cu_seqlens), B, T,
-                              H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
-                              int(segments), _p(workspace), workspace.numel() * workspace.element_size(),
-                              _stream(dev))
+    st = _on(dev, lib.kda_chunk_fwd_cp, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
+             _p(cu_seqlens), B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
+             int(segments), _p(workspace), workspace.numel() * workspace.element_size(),
+             _stream(dev))
     _check(st)
     return o, S_T
 
@@ -275,8 +282,8 @@ def recurrent_step(q, k, v, g, beta, S, *, scale: float = 1.0, out_dtype=None, o
         o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     else:
         _require(o, "o", dev, out_dtype, (N, H, dv))
-    st = lib.kda_recurrent_step(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), N, H, dk, dv, _dt(q),
-                                _dt(o), float(scale), _p(o), _stream(dev))
+    st = _on(dev, lib.kda_recurrent_step, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), N, H, dk, dv,
+             _dt(q), _dt(o), float(scale), _p(o), _stream(dev))
     _check(st)
     return o
 
@@ -305,9 +312,9 @@ def recurrent_multi(q, k, v, g, beta, S, n_commit=None, *, scale: float = 1.0, o
         o = torch.empty((N, K, H, dv), dtype=out_dtype, device=dev)
     elif o is not None:
         _require(o, "o", dev, out_dtype, (N, K, H, dv))
-    st = lib.kda_recurrent_multi(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), _p(n_commit), N, K, H,
-                                 dk, dv, _dt(q), _dt(o) if o is not None else _dt(q), float(scale),
-                                 _p(o), _stream(dev))
+    st = _on(dev, lib.kda_recurrent_multi, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S),
+             _p(n_commit), N, K, H, dk, dv, _dt(q), _dt(o) if o is not None else _dt(q),
+             float(scale), _p(o), _stream(dev))
     _check(st)
     return o
 
@@ -343,9 +350,9 @@ def chunk_fwd_gate(q, k, v, z, A_log, beta, S0=None, cu_seqlens=None, *, scale: 
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif S_T is not None:
         _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
-    st = lib.kda_chunk_fwd_gate(_p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta), _p(S0),
-                                _p(cu_seqlens), B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale),
-                                _p(o), _p(S_T), _stream(dev))
+    st = _on(dev, lib.kda_chunk_fwd_gate, _p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta), _p(S0),
+             _p(cu_seqlens), B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
+             _stream(dev))
     _check(st)
     return o, S_T
 
@@ -369,8 +376,8 @@ def recurrent_step_gate(q, k, v, z, A_log, beta, S, *, scale: float = 1.0, out_d
         o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     else:
         _require(o, "o", dev, out_dtype, (N, H, dv))
-    st = lib.kda_recurrent_step_gate(_p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta), _p(S), N, H,
-                                     dk, dv, _dt(q), _dt(o), float(scale), _p(o), _stream(dev))
+    st = _on(dev, lib.kda_recurrent_step_gate, _p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta),
+             _p(S), N, H, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _stream(dev))
     _check(st)
     return o
 
@@ -408,10 +415,9 @@ def recurrent_multi_fused(q, k, v, z, A_log, beta_logit, G, S, n_commit=None, *,
             _require(y, "y", dev, out_dtype, (N, K, H, dv))
     else:
         y = None
-    st = lib.kda_recurrent_multi_fused(_p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta_logit),
-                                       _p(G) if outputs else None, _p(norm_weight), float(eps), _p(S),
-                                       _p(n_commit), N, K, H, dk, dv, _dt(q),
-                                       _dt(y) if y is not None else _dt(q), float(scale), _p(y),
-                                       _stream(dev))
+    st = _on(dev, lib.kda_recurrent_multi_fused, _p(q), _p(k), _p(v), _p(z), _p(A_log),
+             _p(beta_logit), _p(G) if outputs else None, _p(norm_weight), float(eps), _p(S),
+             _p(n_commit), N, K, H, dk, dv, _dt(q), _dt(y) if y is not None else _dt(q),
+             float(scale), _p(y), _stream(dev))
     _check(st)
     return y

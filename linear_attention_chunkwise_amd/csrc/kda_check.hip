@@ -4,11 +4,15 @@
 // 16-token rescale factors.  A debug aid: the check synchronises the stream to read its result.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda_launch.h"
 
 namespace kda {
 
-__device__ uint32_t g_range_violations;   // per device; cleared before each check
+// One flag per device, cleared before each check.  Checks in one process take turns (the lock
+// below), so concurrent checked calls from several host threads do not see each other's flag.
+__device__ uint32_t g_range_violations;
 
 __global__ __launch_bounds__(256) void range_kernel(const float* __restrict__ g, size_t n, float lo, float hi) {
     uint32_t bad = 0;
@@ -23,6 +27,8 @@ __global__ __launch_bounds__(256) void range_kernel(const float* __restrict__ g,
 hipError_t check_range(const float* g, size_t n, float lo, float hi, hipStream_t stream, bool& ok) {
     ok = true;
     if (n == 0) return hipSuccess;
+    static std::mutex lock;
+    const std::lock_guard<std::mutex> hold(lock);
     static const uint32_t zero = 0;
     hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_range_violations), &zero, sizeof zero, 0,
                                           hipMemcpyHostToDevice, stream);

@@ -699,6 +699,40 @@ def test_range_check_on_request(gpu_lib, monkeypatch):
     torch.cuda.synchronize()
 
 
+def test_range_check_from_concurrent_threads(gpu_lib, monkeypatch):
+    """The domain check's flag is one per device: checked calls from two host threads on their own
+    streams, one with g in range and one with a value outside it, each get their own verdict."""
+    import threading
+    from linear_attention_chunkwise_amd import binding
+    d = _to_dev(inputs.make_decode_inputs(64, 8, 64, 64, seed=35))
+    g_bad = d["g"].clone()
+    g_bad[5, 3, 7] = 0.5
+    monkeypatch.setenv("KDA_CHECK_RANGE", "1")
+    errors = []
+
+    def worker(g, expect_refusal):
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            S = d["S"].clone()
+            for i in range(40):
+                try:
+                    binding.recurrent_step(d["q"], d["k"], d["v"], g, d["beta"], S)
+                    if expect_refusal:
+                        errors.append(f"call {i}: out-of-range g accepted")
+                except binding.KdaError as e:
+                    if not expect_refusal or e.status != binding.KDA_ERR_RANGE:
+                        errors.append(f"call {i}: {e}")
+        stream.synchronize()
+
+    threads = [threading.Thread(target=worker, args=(d["g"], False)),
+               threading.Thread(target=worker, args=(g_bad, True))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
+
+
 # ------------------------------------------------------------------ fused decode
 
 def _fused_oracle(x, S, commits, weight=True, eps=1e-6, scale=1.0):
