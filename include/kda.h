@@ -115,7 +115,8 @@ kda_status kda_chunk_fwd_gate(const void* q, const void* k, const void* v, const
                               float scale, void* o, float* S_T, hipStream_t stream);
 
 /* Bytes of workspace kda_chunk_fwd_cp needs: N * (segments - 1) * H * dk * (dv + dk) * 4 (the
- * summaries below), 0 when segments <= 1 or a size is not positive. */
+ * summaries below), 0 when segments <= 1 or a size is not positive, SIZE_MAX when the product
+ * does not fit in size_t. */
 size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv,
                                        int32_t segments);
 

@@ -243,7 +243,12 @@ kda_status kda_chunk_fwd_gate(const void* q, const void* k, const void* v, const
 
 size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t segments) {
     if (N < 1 || H < 1 || dk < 1 || dv < 1 || segments <= 1) return 0;
-    return (size_t)N * (size_t)(segments - 1) * H * dk * (size_t)(dv + dk) * 4;
+    // saturate rather than wrap for sizes no device could hold
+    size_t n = 4;
+    const size_t factors[5] = {(size_t)N, (size_t)(segments - 1), (size_t)H, (size_t)dk, (size_t)dv + (size_t)dk};
+    for (size_t f : factors)
+        if (__builtin_mul_overflow(n, f, &n)) return SIZE_MAX;
+    return n;
 }
 
 kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const float* g,

@@ -141,6 +141,8 @@ def test_cp_workspace_size(lib):
     assert lib.kda_chunk_fwd_cp_workspace_size(2, 4, 64, 128, 4) == 2 * 3 * 4 * 64 * 192 * 4
     assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 1) == 0
     assert lib.kda_chunk_fwd_cp_workspace_size(0, 32, 128, 128, 3) == 0
+    big = 2**31 - 1                        # saturates instead of wrapping
+    assert lib.kda_chunk_fwd_cp_workspace_size(big, big, big, big, big) == 2**64 - 1
 
 
 def _cp(lib, **kw):
