@@ -17,6 +17,10 @@
  *      beta  [B, T, H]         S0, S_T [N, H, dk, dv] (float32)
  *    q, k, v and beta share `in_dtype`; o has `out_dtype`.
  *  - Every pointer must be 16-byte aligned (beta: 4-byte aligned is enough).
+ *  - Outputs (o, y, S_T, checkpoints, workspace, and a state updated in place) may overlap no
+ *    input and no other output; read-only inputs may alias one another.  The one exception is
+ *    S_T aliasing S0 exactly in an unsegmented prefill.  Any other overlap returns
+ *    KDA_ERR_INVALID_ARGUMENT.
  *  - Work runs on the calling thread's current HIP device and is enqueued asynchronously on
  *    `stream` (0 = the null stream), which must belong to that device; nothing synchronises the
  *    host.  All argument checks run on the host before any launch: on error nothing is enqueued.
@@ -63,7 +67,8 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * results.
  *
  * S0 may be NULL (zero entering state).  S_T may be NULL (final state not wanted) and may alias
- * S0 exactly (in-place state advance).  o must not overlap any input.
+ * S0 exactly (in-place state advance).  o and S_T must not overlap any input (cu_seqlens
+ * included) or each other.
  *
  * Supported: dk in {64, 128}; dv in {64, 128}; in_dtype KDA_BF16, or KDA_F32 at dk = 64 (float32
  * inputs are carried at higher internal precision); out_dtype KDA_BF16 or KDA_F32; T >= 0;
@@ -84,7 +89,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * Layout: ckpt [N, H, ckpt_capacity, dk, dv] float32, caller-owned, 16-byte aligned.  Only whole
  * intervals are emitted: a sequence of length L yields min(floor(L / ckpt_interval),
  * ckpt_capacity) states (the last one equals S_T when L is a multiple of the interval); slots past
- * that are left untouched.  ckpt must not overlap o, S0 or S_T.  ckpt_capacity = 0 (ckpt may then
+ * that are left untouched.  ckpt must not overlap an input, o or S_T.  ckpt_capacity = 0 (ckpt may then
  * be NULL) behaves exactly as kda_chunk_fwd.
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED (interval not a positive multiple
  * of 32, or an unsupported shape) or KDA_ERR_HIP. */
@@ -137,8 +142,10 @@ size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t
  *
  * N * H * segments <= 2^28 (KDA_ERR_UNSUPPORTED beyond).
  * workspace: device memory of at least kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments)
- * bytes, 16-byte aligned, caller-owned, overlapping none of o, S0, S_T; ignored (may be NULL)
- * when segments == 1, which is exactly kda_chunk_fwd.  Other arguments as kda_chunk_fwd.
+ * bytes, 16-byte aligned, caller-owned, overlapping no input, o or S_T; ignored (may be NULL)
+ * when segments == 1, which is exactly kda_chunk_fwd.  With segments > 1, S_T may not alias S0
+ * (the first segment reads S0 while the last one writes S_T, in the same launch).  Other
+ * arguments as kda_chunk_fwd.
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT (also: segments < 1, workspace too small, misaligned
  * or overlapping), KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const float* g,
@@ -154,7 +161,7 @@ kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const f
  *     S <- Diag(exp(g)) S;  u = beta (v - S^T k);  S <- S + k u^T;  o = S^T (scale q).
  *
  * Layouts: q, k, g [N, H, dk]; v, o [N, H, dv]; beta [N, H]; S [N, H, dk, dv] float32.
- * o must not overlap S or any input.  Supported: dk, dv in {64, 128}.
+ * Neither S nor o may overlap an input, nor each other.  Supported: dk, dv in {64, 128}.
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                               const void* beta, float* S, int32_t N, int32_t H, int32_t dk,
@@ -180,8 +187,8 @@ kda_status kda_recurrent_step_gate(const void* q, const void* k, const void* v, 
  * e.g. a replay pass).  n_commit values are clamped to [0, K].
  *
  * Layouts: q, k, g [N, K, H, dk]; v, o [N, K, H, dv]; beta [N, K, H]; S [N, H, dk, dv] float32;
- * n_commit device int32 [N] or NULL.  o must not overlap S or any input.  Supported: dk, dv in
- * {64, 128}.  K = 0 or N = 0 does nothing.
+ * n_commit device int32 [N] or NULL.  Neither S nor o may overlap an input (n_commit included),
+ * nor each other.  Supported: dk, dv in {64, 128}.  K = 0 or N = 0 does nothing.
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, const float* g,
                                const void* beta, float* S, const int32_t* n_commit, int32_t N,
@@ -200,7 +207,7 @@ kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, cons
  * Layouts: q, k, z [N, K, H, dk]; v, G, y [N, K, H, dv]; beta_logit [N, K, H], all in in_dtype;
  * A_log [H] float32; norm_weight [dv] float32, 16-byte aligned, or NULL (ones); eps >= 0;
  * S [N, H, dk, dv] float32; n_commit device int32 [N] or NULL.  y may be NULL (no outputs; G is
- * then not read).  y must not overlap S or any input.  Supported: dk, dv in {64, 128}.
+ * then not read).  Neither S nor y may overlap an input, nor each other.  Supported: dk, dv in {64, 128}.
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v, const void* z,
                                      const float* A_log, const void* beta_logit, const void* G,

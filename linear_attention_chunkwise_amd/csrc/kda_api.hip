@@ -31,6 +31,31 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// A byte range of one argument.  A null pointer or an empty range takes part in no overlap.
+struct Span {
+    const void* p;
+    size_t n;
+    const char* name;
+};
+
+// Outputs may overlap no input and no other output: workgroups read inputs while others write
+// outputs.  Read-only inputs may alias one another.
+template <size_t NO, size_t NI>
+kda_status check_disjoint(const Span (&outs)[NO], const Span (&ins)[NI]) {
+    for (size_t i = 0; i < NO; ++i) {
+        const Span* hit = nullptr;
+        for (size_t j = 0; j < NI && !hit; ++j)
+            if (overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) hit = &ins[j];
+        for (size_t j = i + 1; j < NO && !hit; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) hit = &outs[j];
+        if (hit) {
+            snprintf(g_last_error, sizeof g_last_error, "%s overlaps %s", outs[i].name, hit->name);
+            return KDA_ERR_INVALID_ARGUMENT;
+        }
+    }
+    return KDA_OK;
+}
+
 kda_status hip_status(hipError_t e) {
     if (e == hipSuccess) return ok();
     snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
@@ -135,12 +160,6 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         }
         KDA_TRY(check_ptr(beta, es, "beta"));
         KDA_TRY(check_ptr(o, 16, "o"));
-        const size_t no = nv * dsize(out_dtype);
-        if (overlaps(o, no, q, nqk * es) || overlaps(o, no, k, nqk * es) ||
-            overlaps(o, no, v, nv * es) || (!z && overlaps(o, no, g, nqk * 4)) ||
-            (z && (overlaps(o, no, z, nqk * es) || overlaps(o, no, A_log, (size_t)H * 4))) ||
-            overlaps(o, no, beta, (size_t)tokens * H * es))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps an input%.0lld", "o");
     }
     if (cu_seqlens == nullptr && N == 0) return ok();
     const size_t nst = (size_t)N * H * dk * dv * 4;
@@ -149,8 +168,6 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         KDA_TRY(check_ptr(S_T, 16, "S_T"));
         if (S_T != S0 && overlaps(S_T, nst, S0, nst))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s partially overlaps S0 (only exact aliasing is allowed)%.0lld", "S_T");
-        if (tokens > 0 && overlaps(S_T, nst, o, nv * dsize(out_dtype)))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps o%.0lld", "S_T");
     }
     if (ckpt_capacity < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 0 (got %lld)", "ckpt_capacity", ckpt_capacity);
@@ -160,14 +177,9 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
             return fail(KDA_ERR_UNSUPPORTED, "%s = %lld: checkpoints sit on 32-token chunk ends (a positive multiple of 32)",
                         "ckpt_interval", ckpt_interval);
         KDA_TRY(check_ptr(ckpt, 16, "ckpt"));
-        if (tokens > 0 && overlaps(ckpt, nck, o, nv * dsize(out_dtype)))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps o%.0lld", "ckpt");
-        if (S_T && overlaps(ckpt, nck, S_T, nst))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S_T%.0lld", "ckpt");
-        if (S0 && overlaps(ckpt, nck, S0, nst))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S0%.0lld", "ckpt");
     }
     int64_t seg_len = 0;
+    size_t need = 0;
     if (segments < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "segments", segments);
     if (segments > 1) {
         // one workgroup per (sequence, head, segment, 64-column slice): keep the grid and the
@@ -179,14 +191,31 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         // segment length: the whole row split evenly, rounded up to whole 32-token chunks
         seg_len = ((T + segments - 1) / segments + 31) / 32 * 32;
         if (seg_len == 0) seg_len = 32;
-        const size_t need = kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments);
+        // the first segment reads S0 while the last one writes S_T, in the same launch
+        if (S_T && S_T == S0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s may not alias S0 in a segmented run%.0lld", "S_T");
+        need = kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments);
         if (workspace_bytes < need)
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %lld bytes given, kda_chunk_fwd_cp_workspace_size asks for more",
                         "workspace_bytes", (long long)workspace_bytes);
         KDA_TRY(check_ptr(workspace, 16, "workspace"));
-        if ((tokens > 0 && overlaps(workspace, need, o, nv * dsize(out_dtype))) ||
-            (S_T && overlaps(workspace, need, S_T, nst)) || (S0 && overlaps(workspace, need, S0, nst)))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps o, S0 or S_T%.0lld", "workspace");
+    }
+    {
+        // S_T may be S0 itself (in place: each workgroup reads its S0 block before writing it)
+        const Span outs[] = {{tokens > 0 ? o : nullptr, nv * dsize(out_dtype), "o"},
+                             {S_T, nst, "S_T"},
+                             {ckpt_capacity > 0 ? ckpt : nullptr, nck, "ckpt"},
+                             {segments > 1 ? workspace : nullptr, need, "workspace"}};
+        const Span ins[] = {{q, nqk * es, "q"},
+                            {k, nqk * es, "k"},
+                            {v, nv * es, "v"},
+                            {z ? nullptr : g, nqk * 4, "g"},
+                            {z, nqk * es, "z"},
+                            {z ? A_log : nullptr, (size_t)H * 4, "A_log"},
+                            {beta, (size_t)tokens * H * es, "beta"},
+                            {cu_seqlens, cu_seqlens ? ((size_t)N + 1) * 4 : 0, "cu_seqlens"},
+                            {S_T == S0 ? nullptr : S0, nst, "S0"}};
+        KDA_TRY(check_disjoint(outs, ins));
     }
     if (N == 0) return ok();
 
@@ -288,13 +317,17 @@ static kda_status recurrent_step_impl(const void* q, const void* k, const void* 
     KDA_TRY(check_ptr(S, 16, "S"));
     KDA_TRY(check_ptr(o, 16, "o"));
     const size_t nh = (size_t)N * H;
-    const size_t no = nh * dv * dsize(out_dtype);
-    if (overlaps(o, no, S, nh * dk * dv * 4) || overlaps(o, no, q, nh * dk * es) ||
-        overlaps(o, no, k, nh * dk * es) || overlaps(o, no, v, nh * dv * es) ||
-        (!z && overlaps(o, no, g, nh * dk * 4)) ||
-        (z && (overlaps(o, no, z, nh * dk * es) || overlaps(o, no, A_log, (size_t)H * 4))) ||
-        overlaps(o, no, beta, nh * es))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps the state or an input%.0lld", "o");
+    {
+        const Span outs[] = {{S, nh * dk * dv * 4, "S"}, {o, nh * dv * dsize(out_dtype), "o"}};
+        const Span ins[] = {{q, nh * dk * es, "q"},
+                            {k, nh * dk * es, "k"},
+                            {v, nh * dv * es, "v"},
+                            {z ? nullptr : g, nh * dk * 4, "g"},
+                            {z, nh * dk * es, "z"},
+                            {z ? A_log : nullptr, (size_t)H * 4, "A_log"},
+                            {beta, nh * es, "beta"}};
+        KDA_TRY(check_disjoint(outs, ins));
+    }
     if (!z) KDA_TRY(check_g(g, nh * dk, stream));
     kda::DecodeArgs a{q, k, v, z ? nullptr : g, beta, S, (int32_t)nh, dk, dv,
                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, stream};
@@ -343,16 +376,13 @@ kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, cons
     KDA_TRY(check_ptr(S, 16, "S"));
     if (n_commit) KDA_TRY(check_ptr(n_commit, 4, "n_commit"));
     const size_t nh = (size_t)N * H, nt = nh * (size_t)K;
-    if (o) {
-        KDA_TRY(check_ptr(o, 16, "o"));
-        const size_t no = nt * dv * dsize(out_dtype);
-        if (overlaps(o, no, S, nh * dk * dv * 4) || overlaps(o, no, q, nt * dk * es) ||
-            overlaps(o, no, k, nt * dk * es) || overlaps(o, no, v, nt * dv * es) ||
-            overlaps(o, no, g, nt * dk * 4) || overlaps(o, no, beta, nt * es))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps the state or an input%.0lld", "o");
+    if (o) KDA_TRY(check_ptr(o, 16, "o"));
+    {
+        const Span outs[] = {{S, nh * dk * dv * 4, "S"}, {o, nt * dv * dsize(out_dtype), "o"}};
+        const Span ins[] = {{q, nt * dk * es, "q"}, {k, nt * dk * es, "k"},    {v, nt * dv * es, "v"},
+                            {g, nt * dk * 4, "g"},  {beta, nt * es, "beta"}, {n_commit, (size_t)N * 4, "n_commit"}};
+        KDA_TRY(check_disjoint(outs, ins));
     }
-    if (n_commit && overlaps(n_commit, (size_t)N * 4, S, nh * dk * dv * 4))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S%.0lld", "n_commit");
     KDA_TRY(check_g(g, nt * dk, stream));
     kda::DecodeArgs a{q, k, v, g, beta, S, (int32_t)nh, dk, dv,
                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, stream};
@@ -393,16 +423,20 @@ kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v
     if (y) {
         KDA_TRY(check_ptr(y, 16, "y"));
         KDA_TRY(check_ptr(G, es, "G"));
-        const size_t ny = nt * dv * dsize(out_dtype);
-        if (overlaps(y, ny, S, nh * dk * dv * 4) || overlaps(y, ny, q, nt * dk * es) ||
-            overlaps(y, ny, k, nt * dk * es) || overlaps(y, ny, v, nt * dv * es) ||
-            overlaps(y, ny, z, nt * dk * es) || overlaps(y, ny, beta_logit, nt * es) ||
-            overlaps(y, ny, G, nt * dv * es) || overlaps(y, ny, A_log, (size_t)H * 4) ||
-            (norm_weight && overlaps(y, ny, norm_weight, (size_t)dv * 4)))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps the state or an input%.0lld", "y");
     }
-    if (n_commit && overlaps(n_commit, (size_t)N * 4, S, nh * dk * dv * 4))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps S%.0lld", "n_commit");
+    {
+        const Span outs[] = {{S, nh * dk * dv * 4, "S"}, {y, nt * dv * dsize(out_dtype), "y"}};
+        const Span ins[] = {{q, nt * dk * es, "q"},
+                            {k, nt * dk * es, "k"},
+                            {v, nt * dv * es, "v"},
+                            {z, nt * dk * es, "z"},
+                            {A_log, (size_t)H * 4, "A_log"},
+                            {beta_logit, nt * es, "beta_logit"},
+                            {y ? G : nullptr, nt * dv * es, "G"},
+                            {norm_weight, (size_t)dv * 4, "norm_weight"},
+                            {n_commit, (size_t)N * 4, "n_commit"}};
+        KDA_TRY(check_disjoint(outs, ins));
+    }
     kda::DecodeArgs a{q, k, v, nullptr, beta_logit, S, (int32_t)nh, dk, dv,
                       in_dtype == KDA_F32, out_dtype == KDA_F32, scale, y, stream};
     a.K = K;

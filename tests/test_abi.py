@@ -273,3 +273,22 @@ def test_recurrent_multi_fused_rejects_on_host(lib, kw, status):
 def test_recurrent_multi_fused_empty_and_state_only_checks(lib):
     assert _fused(lib, K=0, q=None) == binding.KDA_OK
     assert _fused(lib, y=None, G=None, z=None) == binding.KDA_ERR_INVALID_ARGUMENT   # z still needed
+
+
+@pytest.mark.parametrize("call,kw,names", [
+    (_fwd, dict(ST=FAKE), (b"S_T", b"q")),                          # final state over an input
+    (_fwd, dict(cu=FAKE * 8), (b"o", b"cu_seqlens")),
+    (_fwd, dict(S0=FAKE * 8), (b"o", b"S0")),
+    (_ckpt, dict(ck=FAKE), (b"ckpt", b"q")),
+    (_cp, dict(ws=FAKE), (b"workspace", b"q")),
+    (_cp, dict(S0=FAKE * 64, ST=FAKE * 64), (b"S_T", b"S0")),       # in place only unsegmented
+    (_step, dict(S=FAKE), (b"S", b"q")),                            # state updated over an input
+    (_multi, dict(S=FAKE), (b"S", b"q")),
+    (_fused, dict(S=FAKE), (b"S", b"q")),
+    (_fused, dict(nc=FAKE * 64), (b"y", b"n_commit")),
+    (_gate, dict(ST=FAKE * 8 + 4096), (b"o", b"S_T")),               # two outputs
+])
+def test_outputs_may_not_overlap_inputs_or_each_other(lib, call, kw, names):
+    assert call(lib, **kw) == binding.KDA_ERR_INVALID_ARGUMENT
+    err = lib.kda_last_error()
+    assert all(n in err for n in names), err
