@@ -216,6 +216,29 @@ def test_workload_long_t1m(gpu_lib):
     _sampled_check(cfg, [(0, 0), (0, 19)])
 
 
+@pytest.mark.parametrize("dk,dtype,H", [(128, torch.bfloat16, 32768), (64, torch.float32, 65536)],
+                         ids=["d128_bf16_h32768", "d64_f32_h65536"])
+def test_prefill_at_the_head_count_limit(gpu_lib, dk, dtype, H):
+    """H * d at the largest value the library accepts (2^22: the kernel addresses one 32-token chunk
+    of a head's rows with 32-bit byte offsets), one ragged 40-token sequence; sampled heads, the
+    last one (largest offsets) included, against the oracle."""
+    from linear_attention_chunkwise_amd import binding
+    assert H * dk == 1 << 22
+    x = inputs.make_prefill_inputs(1, 40, H, dk, dk, dtype=dtype, seed=41, device="cuda")
+    o, ST = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for h in (0, 1, H // 2 + 3, H - 2, H - 1):
+        sel = lambda t: t[:, :, h:h + 1].contiguous().cpu()
+        outs, rST = c_oracle.kda_units(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["g"]),
+                                       sel(x["beta"]), x["S0"][:, h:h + 1].contiguous().cpu(), None,
+                                       [(0, 0)])
+        assert_close(f"o[h={h}]", o[0, :, h].cpu().numpy(), outs[0])
+        assert_close(f"S_T[h={h}]", ST[0, h].cpu().numpy(), rST[0])
+    del x, o, ST
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ prefix checkpoints
 
 @pytest.mark.parametrize("interval,capacity", [(32, 40), (96, 5), (512, 3)])
