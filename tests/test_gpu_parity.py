@@ -418,6 +418,26 @@ def test_decode_workload_n1024_h32(gpu_lib):
     assert_close("S", S[idx].cpu().numpy(), rS)
 
 
+def test_decode_with_states_past_4gib(gpu_lib):
+    """2^20 (sequence, head) units of 64 x 64 float32 states (16 GiB): state offsets past 2^32
+    bytes and a grid of 2^20 workgroups; sampled sequences, the last one included, every head."""
+    from linear_attention_chunkwise_amd import binding
+    N, H, d = 32768, 32, 64
+    x = inputs.make_decode_inputs(N, H, d, d, seed=43, device="cuda")
+    idx = torch.tensor([0, 1, N // 2 + 5, N - 2, N - 1])
+    sub = {k: x[k][idx.to(x[k].device)].cpu() for k in ("q", "k", "v", "g", "beta", "S")}
+    S = x["S"]                                   # advanced in place
+    o = binding.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], S)
+    torch.cuda.synchronize()
+    ro, rS = c_oracle.kda_forward(sub["q"][:, None], sub["k"][:, None], sub["v"][:, None],
+                                  sub["g"][:, None], sub["beta"][:, None], sub["S"])
+    dev_idx = idx.to(S.device)
+    assert_close("o", o[dev_idx].float().cpu().numpy(), ro[:, 0])
+    assert_close("S", S[dev_idx].cpu().numpy(), rS)
+    del x, S, o
+    torch.cuda.empty_cache()
+
+
 def test_decode_matches_prefill_t1(gpu_lib):
     """Decode is eq. (1) with T = 1: the two entry points agree."""
     from linear_attention_chunkwise_amd import binding
