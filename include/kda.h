@@ -125,6 +125,13 @@ kda_status kda_chunk_fwd_gate(const void* q, const void* k, const void* v, const
 size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv,
                                        int32_t segments);
 
+/* The segment count for kda_chunk_fwd_cp that suits a GPU with `slots` concurrent prefill
+ * workgroups (one per CU: 256 on MI355X): the largest P <= 64 for which both passes below fit in
+ * one round, pass 1 with N*H*(dv/64 + (P-2)*(dv+dk)/64) working workgroups and pass 2 with
+ * N*H*P*dv/64; 1 when P = 2 does not fit either (then kda_chunk_fwd is as fast).  Host arithmetic
+ * only (no device call); 1 for non-positive arguments. */
+int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t slots);
+
 /* kda_chunk_fwd with each sequence split in time into `segments` pieces that run in parallel:
  * the in-device context parallelism of §5.1.1 for long prefill with few heads, built on the
  * decomposition of §5.1.2, eq. (17): the state after a segment is M S_in + S~, with M the product

@@ -20,7 +20,8 @@ KDA_BF16, KDA_F32 = 0, 1
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_gate", "kda_chunk_fwd_cp",
-           "kda_chunk_fwd_cp_workspace_size", "kda_recurrent_step", "kda_recurrent_step_gate",
+           "kda_chunk_fwd_cp_workspace_size", "kda_chunk_fwd_cp_segments", "kda_recurrent_step",
+           "kda_recurrent_step_gate",
            "kda_recurrent_multi", "kda_recurrent_multi_fused", "kda_status_string",
            "kda_last_error", "kda_version")
 
@@ -56,6 +57,8 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_fwd_cp.restype = ctypes.c_int
     lib.kda_chunk_fwd_cp_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.kda_chunk_fwd_cp_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_fwd_cp_segments.argtypes = [i32, i32, i32, i32, i32]
+    lib.kda_chunk_fwd_cp_segments.restype = i32
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_step.restype = ctypes.c_int
@@ -208,17 +211,9 @@ def chunk_fwd_ckpt(q, k, v, g, beta, S0=None, cu_seqlens=None, *, interval: int,
 
 
 def cp_segments(n_units: int, dk: int, dv: int, slots: int = 256) -> int:
-    """Largest segment count whose two passes each fit ``slots`` workgroups (one per CU): pass 1
-    runs (dv + dk) / 64 column slices for every segment but the first and the last (dv / 64 for
-    the first), pass 2 runs dv / 64 slices for every segment."""
-    best = 1
-    for p in range(2, 65):
-        pass1 = n_units * (dv // 64 + (p - 2) * (dv + dk) // 64)
-        pass2 = n_units * p * (dv // 64)
-        if pass1 > slots or pass2 > slots:
-            break
-        best = p
-    return best
+    """The library's segment count for chunk_fwd_cp over ``n_units`` (sequence, head) units on a
+    GPU with ``slots`` concurrent prefill workgroups (kda_chunk_fwd_cp_segments)."""
+    return int(load().kda_chunk_fwd_cp_segments(int(n_units), 1, int(dk), int(dv), int(slots)))
 
 
 def chunk_fwd_cp(q, k, v, g, beta, S0=None, cu_seqlens=None, *, segments: int, scale: float = 1.0,

@@ -280,6 +280,19 @@ size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t
     return n;
 }
 
+int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t slots) {
+    if (N < 1 || H < 1 || dk < 1 || dv < 1 || slots < 1) return 1;
+    const int64_t units = (int64_t)N * H;
+    int32_t best = 1;
+    for (int32_t p = 2; p <= 64; ++p) {
+        const int64_t pass1 = units * (dv / 64 + (int64_t)(p - 2) * ((dv + dk) / 64));
+        const int64_t pass2 = units * p * (dv / 64);
+        if (pass1 > slots || pass2 > slots) break;
+        best = p;
+    }
+    return best;
+}
+
 kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const float* g,
                             const void* beta, const float* S0, const int32_t* cu_seqlens, int32_t B,
                             int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,

@@ -170,11 +170,15 @@ def test_chunk_fwd_cp_rejects_on_host(lib, kw, status):
     assert lib.kda_last_error() != b""
 
 
-def test_cp_segment_count_helper():
+def test_cp_segment_count_helper(lib):
     # 32 units of d = 128: pass 1 = 32 * (2 + 4 (p - 2)), pass 2 = 32 * 2 p, both <= 256
     assert binding.cp_segments(32, 128, 128) == 3
     assert binding.cp_segments(16, 128, 128) == 5
     assert binding.cp_segments(256, 128, 128) == 1
+    assert lib.kda_chunk_fwd_cp_segments(1, 32, 128, 128, 256) == 3    # the same through the ABI
+    assert lib.kda_chunk_fwd_cp_segments(1, 8, 64, 64, 256) == 17      # pass 1: 8 (1 + 2 (p - 2)) <= 256
+    assert lib.kda_chunk_fwd_cp_segments(1, 32, 128, 128, 0) == 1
+    assert lib.kda_chunk_fwd_cp_segments(0, 32, 128, 128, 256) == 1
 
 
 def _multi(lib, **kw):
