@@ -226,6 +226,21 @@ def pin_varlen_independence(fwd):
     return err
 
 
+def pin_column_independence(fwd, col_sets=([5, 1, 3, 0, 4, 2], [4, 0])):
+    """Value columns evolve independently: column j of S, v and o forms its own recurrence with the
+    shared keys, decays and betas (eq. (1) acts on S from the left only).  A run with the columns
+    of V and S0 permuted gives the same permutation of the full run's columns, and a run on a
+    subset gives exactly those columns; this is what allows the state to be split over dv.  The
+    permuted run keeps dk = dv, where a transposed state would still be well-formed."""
+    q, k, v, g, beta, S0 = _rand_inputs(T=24, H=2, dk=6, dv=6, seed=29)
+    o, ST = fwd(q, k, v, g, beta, S0)
+    err = 0.0
+    for cols in col_sets:
+        oc, STc = fwd(q, k, v[..., cols].contiguous(), g, beta, S0[..., cols].contiguous())
+        err = max(err, _rel(oc, o[..., cols]), _rel(STc, ST[..., cols]))
+    return err
+
+
 PINS = {
     "beta_zero": (pin_beta_zero, 1e-13),
     "single_token_dense": (pin_single_token_dense, 1e-13),
@@ -236,6 +251,7 @@ PINS = {
     "affine_transition": (pin_affine_transition, 1e-12),
     "resume": (pin_resume, 1e-8),
     "varlen_independence": (pin_varlen_independence, 0.0),
+    "column_independence": (pin_column_independence, 1e-13),
 }
 
 
@@ -304,8 +320,15 @@ def _base2_decay(S, q, k, v, g, beta, scale=1.0):
     return S.T @ q, S
 
 
+def _transposed_state(S, q, k, v, g, beta, scale=1.0):
+    S = np.exp(g)[:, None] * S
+    S = S + np.outer(k, beta * (v - S @ k))   # S k in place of S^T k (well-formed when dk = dv)
+    return S.T @ q, S
+
+
 MUTANTS = {
     "read_before_update": _read_before_update,
+    "transposed_state": _transposed_state,
     "decay_after_delta": _decay_after_delta,
     "decay_on_columns": _decay_on_columns,
     "sign_flip": _sign_flip,
@@ -325,15 +348,25 @@ def test_pins_catch_planted_mistake(name):
         try:
             if fn(fwd) > max(tol, 1e-9):
                 failed.append(pin)
-        except AssertionError:
+        except (AssertionError, ValueError):   # ValueError: a shape the mistake cannot take
             failed.append(pin)
     assert failed, f"planted mistake {name} passes every pin"
+
+
+def test_column_pin_catches_a_transposed_state_numerically():
+    """With dk = dv the transposed-state mistake is well-formed; the permuted-column run alone
+    rejects it by value, not by shape."""
+    assert pin_column_independence(_mutant(_transposed_state), col_sets=([5, 1, 3, 0, 4, 2],)) > 1e-3
 
 
 def test_chunkwise_catches_planted_mistakes():
     """The chunkwise cross-check alone also rejects each planted mistake."""
     for name, step in MUTANTS.items():
-        assert pin_chunkwise(_mutant(step), chunks=(16,)) > 1e-6, name
+        try:
+            err = pin_chunkwise(_mutant(step), chunks=(16,))
+        except ValueError:   # the mistake cannot take this shape (dk != dv): rejected as well
+            continue
+        assert err > 1e-6, name
 
 
 # ----------------------------------------------------------------------------- page constants
