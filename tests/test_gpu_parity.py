@@ -151,6 +151,65 @@ def test_prefill_resume_matches_one_pass(gpu_lib):
     assert_close("S_T", Sb.cpu().numpy(), ST.cpu().numpy())
 
 
+# ------------------------------------------------------------------ seeded sweep of small shapes
+
+def _sweep_cases(n=40, seed=2024):
+    """Seeded random combinations of the prefill arguments: entry point (plain, decay map in the
+    kernel, segmented), batch or packed lengths (empty sequences included), heads, dk and dv, input
+    dtype (float32 at dk = 64), S0 present or not, output dtype and scale."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+        f32_in = dk == 64 and rng.random() < 0.3
+        entry = str(rng.choice(["plain", "gate", "cp"]))
+        if rng.random() < 0.35:
+            lens = [int(L) for L in rng.integers(0, 200, size=int(rng.integers(1, 6)))]
+            lens[0] = max(lens[0], 1)
+            B, T = 1, sum(lens)
+        else:
+            lens, B, T = None, int(rng.integers(1, 4)), int(rng.integers(1, 260))
+        cases.append(dict(entry=entry, B=B, T=T, lens=lens, H=int(rng.integers(1, 5)), dk=dk, dv=dv,
+                          f32_in=f32_in, s0=bool(rng.random() < 0.7),
+                          out_f32=bool(rng.random() < 0.5), scale=float(rng.choice([1.0, 0.5])),
+                          segments=int(rng.integers(2, 5)) if entry == "cp" else 1))
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("i", range(len(SWEEP)))
+def test_prefill_sweep(gpu_lib, i):
+    from linear_attention_chunkwise_amd import binding
+    c = SWEEP[i]
+    print(f"  case {i}: {c}", flush=True)
+    cu = None if c["lens"] is None else inputs.cu_from_lengths(c["lens"])
+    x = inputs.make_prefill_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"],
+                                   dtype=torch.float32 if c["f32_in"] else torch.bfloat16,
+                                   seed=100 + i, S0_std=0.1 if c["s0"] else None, cu_seqlens=cu,
+                                   with_logits=c["entry"] == "gate")
+    d = _to_dev(x)
+    od = torch.float32 if c["out_f32"] else torch.bfloat16
+    if c["entry"] == "gate":
+        o, ST = binding.chunk_fwd_gate(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta"],
+                                       d["S0"], d["cu_seqlens"], scale=c["scale"], out_dtype=od)
+    elif c["entry"] == "cp":
+        o, ST = binding.chunk_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                     d["cu_seqlens"], segments=c["segments"], scale=c["scale"],
+                                     out_dtype=od)
+    else:
+        o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                  d["cu_seqlens"], scale=c["scale"], out_dtype=od)
+    torch.cuda.synchronize()
+    if c["entry"] == "gate":
+        ro, rST = _gate_oracle(x, x["S0"], None if cu is None else cu.cpu(), scale=c["scale"])
+    else:
+        ro, rST = oracle_all(x, scale=c["scale"])
+    assert_close("o", o.float().cpu().numpy(), ro)
+    assert_close("S_T", ST.cpu().numpy(), rST)
+
+
 # ------------------------------------------------------------------ the named workloads
 
 def test_workload_tiny_fp32_t256_d64(gpu_lib):
