@@ -707,6 +707,83 @@ def test_prefill_varlen_order_independent(gpu_lib, lengths):
     assert_close("S_T", ST.cpu().numpy(), rST)
 
 
+# ------------------------------------------------------------------ seeded sweep of decode calls
+
+def _decode_sweep_cases(n=32, seed=4242):
+    """Seeded random decode calls: entry point (single step, single step with the decay map,
+    K-token pass, fused K-token pass), sequences, heads, dk and dv, input and output dtype, scale,
+    accepted-prefix lengths (0 and past K included), and for the fused pass the norm weight and
+    eps."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        entry = str(rng.choice(["step", "step_gate", "multi", "fused"]))
+        N = int(rng.integers(1, 40))
+        K = int(rng.integers(1, 7)) if entry in ("multi", "fused") else 1
+        cases.append(dict(entry=entry, N=N, K=K, H=int(rng.integers(1, 5)),
+                          dk=int(rng.choice([64, 128])), dv=int(rng.choice([64, 128])),
+                          f32_in=bool(rng.random() < 0.3), out_f32=bool(rng.random() < 0.5),
+                          scale=float(rng.choice([1.0, 0.6])),
+                          commits=[int(c) for c in rng.integers(0, K + 2, size=N)],
+                          weight=bool(rng.random() < 0.7), eps=float(rng.choice([1e-6, 1e-5]))))
+    return cases
+
+
+DECODE_SWEEP = _decode_sweep_cases()
+
+
+@pytest.mark.parametrize("i", range(len(DECODE_SWEEP)))
+def test_decode_sweep(gpu_lib, i):
+    from linear_attention_chunkwise_amd import binding
+    c = DECODE_SWEEP[i]
+    print(f"  case {i}: {c}", flush=True)
+    N, K, H, dk, dv = c["N"], c["K"], c["H"], c["dk"], c["dv"]
+    dt = torch.float32 if c["f32_in"] else torch.bfloat16
+    od = torch.float32 if c["out_f32"] else torch.bfloat16
+    commits = [min(v, K) for v in c["commits"]]
+    nc = torch.tensor(c["commits"], dtype=torch.int32, device="cuda")
+    if c["entry"] == "fused":
+        x = _to_dev(inputs.make_fused_decode_inputs(N, K, H, dk, dv, dtype=dt, seed=200 + i))
+        S = x["S"].clone()
+        w = x["norm_weight"] if c["weight"] else None
+        y = binding.recurrent_multi_fused(x["q"], x["k"], x["v"], x["z"], x["A_log"],
+                                          x["beta_logit"], x["G"], S, nc, norm_weight=w,
+                                          eps=c["eps"], scale=c["scale"], out_dtype=od)
+        torch.cuda.synchronize()
+        ry, rS = _fused_oracle(x, x["S"], commits, weight=c["weight"], eps=c["eps"],
+                               scale=c["scale"])
+        assert_close("y", y.float().cpu().numpy(), ry)
+        assert_close("S", S.cpu().numpy(), rS)
+        return
+    x = inputs.make_prefill_inputs(N, K, H, dk, dv, dtype=dt, seed=200 + i,
+                                   with_logits=c["entry"] == "step_gate")
+    d = _to_dev(x)
+    S = d["S0"].clone()
+    if c["entry"] == "multi":
+        o = binding.recurrent_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], S, nc,
+                                    scale=c["scale"], out_dtype=od)
+        torch.cuda.synchronize()
+        ro, rS = _oracle_multi(x, x["S0"], commits, scale=c["scale"])
+        assert_close("o", o.float().cpu().numpy(), ro)
+        assert_close("S", S.cpu().numpy(), rS)
+        return
+    one = lambda t: t[:, 0].contiguous()
+    if c["entry"] == "step_gate":
+        o = binding.recurrent_step_gate(one(d["q"]), one(d["k"]), one(d["v"]), one(d["z"]),
+                                        d["A_log"], one(d["beta"]), S, scale=c["scale"],
+                                        out_dtype=od)
+        torch.cuda.synchronize()
+        ro, rS = _gate_oracle(x, x["S0"], scale=c["scale"])
+    else:
+        o = binding.recurrent_step(one(d["q"]), one(d["k"]), one(d["v"]), one(d["g"]),
+                                   one(d["beta"]), S, scale=c["scale"], out_dtype=od)
+        torch.cuda.synchronize()
+        ro, rS = c_oracle.kda_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], None,
+                                      c["scale"])
+    assert_close("o", o.float().cpu().numpy(), ro[:, 0])
+    assert_close("S", S.cpu().numpy(), rS)
+
+
 # ------------------------------------------------------------------ decode with float32 inputs
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
