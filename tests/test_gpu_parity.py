@@ -847,6 +847,44 @@ def test_every_entry_point_is_bitwise_deterministic(gpu_lib):
             assert torch.equal(a, b), name
 
 
+def test_prefill_and_decode_replay_in_a_hip_graph(gpu_lib):
+    """The entry points only enqueue kernels (no allocation, no host synchronisation), so a caller
+    can capture them in a HIP graph: a prefill whose final state a decode step then advances in
+    place, captured once and replayed with eager work and synchronisation between replays, matches
+    the eager results bitwise on every replay."""
+    from linear_attention_chunkwise_amd import binding
+    x = _to_dev(inputs.make_prefill_inputs(2, 100, 2, 128, 128, seed=51))
+    d = _to_dev(inputs.make_decode_inputs(2, 2, 128, 128, seed=52))
+    o_ref, ST_ref = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    S_ref = ST_ref.clone()
+    od_ref = binding.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], S_ref)
+    torch.cuda.synchronize()
+    o, ST, od = torch.empty_like(o_ref), torch.empty_like(ST_ref), torch.empty_like(od_ref)
+
+    def work():
+        binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], o=o, S_T=ST)
+        binding.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], ST, o=od)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # one eager pass on the capturing stream first
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for r in range(4):
+        for t in (o, ST, od):               # eager work between the replays
+            t.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {r}: o"
+        assert torch.equal(ST, S_ref), f"replay {r}: state"
+        assert torch.equal(od, od_ref), f"replay {r}: decode output"
+
+
 def test_range_check_on_request(gpu_lib, monkeypatch):
     """KDA_CHECK_RANGE=1: g outside [-5, 0] (or NaN) is refused with KDA_ERR_RANGE before any
     launch; in range it runs as usual; without the variable nothing is checked."""
