@@ -45,9 +45,8 @@
 // A_qk, A_qk itself, V - K~ S, V~ in both of its uses, K_end (its rounding would dominate the
 // state's error), and both operands of (Q * exp(G)) S, which dominates short sequences entered
 // with a large state.  A_kk, T_b, K~ and the state as the operand of K~ S are single bf16; the
-// state stays fp32.  Float32 inputs (kFull)
-// carry every operand but A_kk's as a pair.  The scale on q is applied to the outputs
-// (everything is linear in q).
+// state stays fp32.  Float32 inputs (kFull) carry every operand but A_kk's as a pair.  The scale
+// on q is applied to the outputs (everything is linear in q).
 #include <atomic>
 #include <type_traits>
 
