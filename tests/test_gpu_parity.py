@@ -336,6 +336,33 @@ def test_checkpoints_match_prefix_states(gpu_lib, interval, capacity):
     assert checked > 0
 
 
+@pytest.mark.parametrize("dk,dv,dtype,s0", [(64, 64, torch.float32, True), (64, 128, torch.bfloat16, False),
+                                           (128, 64, torch.bfloat16, True)],
+                         ids=["k64v64_f32", "k64v128_bf16_noS0", "k128v64_bf16"])
+def test_checkpoints_other_shapes_and_dtypes(gpu_lib, dk, dv, dtype, s0):
+    """Checkpoints at every 64 tokens of two ragged fixed-length sequences, for the remaining
+    dk/dv combinations and float32 inputs, against the oracle's prefix states."""
+    from linear_attention_chunkwise_amd import binding
+    B, T, H, interval, capacity = 2, 300, 2, 64, 5
+    x = inputs.make_prefill_inputs(B, T, H, dk, dv, dtype=dtype, seed=dk + dv,
+                                   S0_std=0.1 if s0 else None)
+    d = _to_dev(x)
+    _, _, ck = binding.chunk_fwd_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                      interval=interval, capacity=capacity, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ck = ck.cpu().numpy()
+    full = T // interval
+    for j in range(capacity):
+        if j >= full:
+            assert not ck[:, :, j].any(), f"slot {j} written"
+            continue
+        e = (j + 1) * interval
+        sel = lambda t: t[:, :e].contiguous()
+        _, rST = c_oracle.kda_forward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["g"]),
+                                      sel(x["beta"]), x["S0"], None)
+        assert_close(f"ckpt[j={j}]", ck[:, :, j], rST)
+
+
 def test_resume_from_checkpoint(gpu_lib):
     """A prefill resumed from checkpoint j over the remaining tokens gives the same outputs and
     final state as the single pass (prefix reuse)."""
