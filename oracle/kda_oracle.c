@@ -10,8 +10,8 @@
  * u = beta_t (v_t - S^T k_t) against the decayed state, add k_t u^T, read out S^T q_t after the
  * update.  All arithmetic is double precision; inputs are upcast from their stored dtype
  * (bf16 bit patterns or float32; g may also be float64, e.g. the decay map of eq. (5) evaluated
- * in double).  Only tests/ and bench.py's CPU-baseline leg load this
- * library; the HIP product path never does, and the two share no code.
+ * in double).  Only tests/, the smoke check in __graft_entry__.py and bench.py's CPU-baseline
+ * leg load this library; the HIP product path never does, and the two share no code.
  *
  * Units run in parallel with OpenMP (one unit per thread at a time); within a unit the loop is
  * sequential and unblocked.
