@@ -76,6 +76,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qp
     // decay map (GATE): once per channel through LDS rather than in each of the CG threads that
     // hold the channel's row (the state loads above are already in flight)
     __shared__ float dec[GATE ? DK : 1];
+    KDA_POISON(red_y, sizeof red_y);
+    KDA_POISON(red_z, sizeof red_z);
+    KDA_POISON(red_qk, sizeof red_qk);
+    KDA_POISON(dec, sizeof dec);
+    KDA_POISON_DONE();
     if constexpr (GATE) {
         if (t < DK) dec[t] = decay_at<IN_F32, true>(g, zp, __expf(A_log[unit % H]), kb + t);
         __syncthreads();
@@ -156,6 +161,11 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
 
     const int unit = blockIdx.x;        // sequence * H + head
     if (unit >= N * H) return;
+    KDA_POISON(red_y, sizeof red_y);
+    KDA_POISON(red_z, sizeof red_z);
+    KDA_POISON(red_qk, sizeof red_qk);
+    KDA_POISON(dec, sizeof dec);
+    KDA_POISON_DONE();
     const int n = unit / H, h = unit % H;
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;
@@ -265,6 +275,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
     const int unit = blockIdx.x;        // sequence * H + head
     if (unit >= N * H) return;
+    KDA_POISON(red_y, sizeof red_y);
+    KDA_POISON(red_z, sizeof red_z);
+    KDA_POISON(red_s, sizeof red_s);
+    KDA_POISON(dec, sizeof dec);
+    KDA_POISON_DONE();
     const int n = unit / H, h = unit % H;
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;

@@ -28,6 +28,21 @@ __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Debug builds only (-DKDA_POISON_LDS): every kernel first fills its LDS with 0x7FC07FC0, a
+// float32 NaN whose two 16-bit halves are bf16 NaNs, so a value read before any wave wrote it
+// reaches the results as NaN.  The library build compiles both macros to nothing.
+#ifdef KDA_POISON_LDS
+__device__ __forceinline__ void poison_lds(void* p, size_t bytes) {
+    uint32_t* w = static_cast<uint32_t*>(p);
+    for (size_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0x7FC07FC0u;
+}
+#define KDA_POISON(p, bytes) ::kda::poison_lds((p), (bytes))
+#define KDA_POISON_DONE() __syncthreads()
+#else
+#define KDA_POISON(p, bytes) ((void)0)
+#define KDA_POISON_DONE() ((void)0)
+#endif
+
 __device__ __forceinline__ float bf2f(bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ bf16 f2bf(float x) { return static_cast<bf16>(x); }  // round to nearest even
 

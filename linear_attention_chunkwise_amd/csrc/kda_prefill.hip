@@ -1007,6 +1007,8 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     const int seg = (unit / a.H) % nseg;
     const int rank = unit / (a.H * nseg);
     if (a.mode == 1 && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;   // not needed
+    KDA_POISON(smem, (Layout<DK, F32IN>::total));
+    KDA_POISON_DONE();
     int n = rank;
     if constexpr (RANK) n = seq_of_rank(a, rank, smem);
     int64_t row0, len;

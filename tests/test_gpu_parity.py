@@ -912,6 +912,68 @@ def test_prefill_and_decode_replay_in_a_hip_graph(gpu_lib):
         assert torch.equal(od, od_ref), f"replay {r}: decode output"
 
 
+def _every_entry_point():
+    """Small runs of every entry point on fixed seeded inputs; the results as CPU tensors."""
+    from linear_attention_chunkwise_amd import binding
+    r = {}
+    cu = inputs.cu_from_lengths([0, 40, 1, 100, 33])
+    xv = _to_dev(inputs.make_prefill_inputs(1, int(cu[-1]), 2, 128, 128, seed=61, cu_seqlens=cu,
+                                            with_logits=True))
+    r["varlen"] = binding.chunk_fwd(xv["q"], xv["k"], xv["v"], xv["g"], xv["beta"], xv["S0"],
+                                    xv["cu_seqlens"], out_dtype=torch.float32)
+    r["gate"] = binding.chunk_fwd_gate(xv["q"], xv["k"], xv["v"], xv["z"], xv["A_log"], xv["beta"],
+                                       xv["S0"], xv["cu_seqlens"])
+    x = _to_dev(inputs.make_prefill_inputs(2, 150, 2, 128, 64, seed=62))
+    r["plain"] = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    r["cp"] = binding.chunk_fwd_cp(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], segments=3)
+    r["ckpt"] = binding.chunk_fwd_ckpt(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
+                                       interval=32, capacity=5)
+    xf = _to_dev(inputs.make_prefill_inputs(1, 70, 2, 64, 64, dtype=torch.float32, seed=63))
+    r["f32"] = binding.chunk_fwd(xf["q"], xf["k"], xf["v"], xf["g"], xf["beta"], xf["S0"])
+    d = _to_dev(inputs.make_prefill_inputs(6, 3, 2, 128, 128, seed=64, with_logits=True))
+    one = lambda t: t[:, 0].contiguous()
+    S = d["S0"].clone()
+    r["step"] = (binding.recurrent_step(one(d["q"]), one(d["k"]), one(d["v"]), one(d["g"]),
+                                        one(d["beta"]), S), S)
+    S = d["S0"].clone()
+    r["step_gate"] = (binding.recurrent_step_gate(one(d["q"]), one(d["k"]), one(d["v"]), one(d["z"]),
+                                                  d["A_log"], one(d["beta"]), S), S)
+    S = d["S0"].clone()
+    nc = torch.tensor([3, 0, 1, 2, 3, 5], dtype=torch.int32, device="cuda")
+    r["multi"] = (binding.recurrent_multi(d["q"], d["k"], d["v"], d["g"], d["beta"], S, nc), S)
+    f = _to_dev(inputs.make_fused_decode_inputs(6, 3, 2, 128, 128, seed=65))
+    S = f["S"].clone()
+    r["fused"] = (binding.recurrent_multi_fused(f["q"], f["k"], f["v"], f["z"], f["A_log"],
+                                                f["beta_logit"], f["G"], S, nc,
+                                                norm_weight=f["norm_weight"]), S)
+    torch.cuda.synchronize()
+    return {k: [t.cpu() for t in v if t is not None] for k, v in r.items()}
+
+
+def test_no_kernel_reads_lds_nothing_wrote(gpu_lib):
+    """The debug build in which every kernel first fills its LDS with NaN (libkda_poison.so) gives,
+    for every entry point, finite results bitwise equal to the library's: no kernel reads LDS that
+    no wave of its launch has written."""
+    import os
+    from linear_attention_chunkwise_amd import binding
+    from linear_attention_chunkwise_amd import build as kbuild
+    if not os.path.exists(kbuild.POISON_LIB):
+        pytest.fail(f"{kbuild.POISON_LIB} is missing: run the build step")
+    saved = binding._lib
+    try:
+        out = {}
+        for name, path in (("library", kbuild.LIB), ("poisoned", kbuild.POISON_LIB)):
+            binding._lib = None
+            binding.load(path)
+            out[name] = _every_entry_point()
+    finally:
+        binding._lib = saved
+    for entry, tensors in out["poisoned"].items():
+        for i, (p, q) in enumerate(zip(tensors, out["library"][entry])):
+            assert torch.isfinite(p.float()).all(), f"{entry}[{i}]: NaN or inf with poisoned LDS"
+            assert torch.equal(p, q), f"{entry}[{i}]: differs with poisoned LDS"
+
+
 def test_range_check_on_request(gpu_lib, monkeypatch):
     """KDA_CHECK_RANGE=1: g outside [-5, 0] (or NaN) is refused with KDA_ERR_RANGE before any
     launch; in range it runs as usual; without the variable nothing is checked."""
