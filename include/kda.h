@@ -33,7 +33,9 @@
  *    (eq. (5) and the bound after it; NaN fails), synchronises `stream` to read the result, and
  *    returns KDA_ERR_RANGE without launching anything else if one does not.  The prefill kernel
  *    relies on this domain for the bf16 range of its rescale factors; outside it results are
- *    undefined (never an out-of-bounds access).
+ *    undefined (never an out-of-bounds access).  With the same variable, every entry point that
+ *    takes cu_seqlens first checks on `stream` that the offsets run from 0 to T without
+ *    decreasing, and returns KDA_ERR_INVALID_ARGUMENT if they do not.
  */
 #ifndef LIBKDA_KDA_H
 #define LIBKDA_KDA_H

@@ -91,6 +91,22 @@ kda_status check_g(const float* g, size_t n, hipStream_t stream) {
     return KDA_OK;
 }
 
+// KDA_CHECK_RANGE=1: check the packed-sequence offsets before launching (synchronises the stream)
+kda_status check_cu(const int32_t* cu, int32_t N, int64_t T, hipStream_t stream) {
+    const char* env = getenv("KDA_CHECK_RANGE");
+    if (!env || env[0] != '1' || !cu) return KDA_OK;
+    bool fine = true;
+    const hipError_t e = kda::check_offsets(cu, N, T, stream, fine);
+    if (e != hipSuccess) {
+        snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+        return KDA_ERR_HIP;
+    }
+    if (!fine)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: the offsets do not run from 0 to T without decreasing%.0lld",
+                    "cu_seqlens");
+    return KDA_OK;
+}
+
 #define KDA_TRY(expr)                      \
     do {                                   \
         kda_status _s = (expr);            \
@@ -219,6 +235,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     }
     if (N == 0) return ok();
 
+    KDA_TRY(check_cu(cu_seqlens, N, T, stream));
     if (!z) KDA_TRY(check_g(g, (size_t)tokens * H * dk, stream));
     kda::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, T, H, N, dk, dv,
                        in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T,

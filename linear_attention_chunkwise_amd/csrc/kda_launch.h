@@ -71,6 +71,8 @@ struct DecodeArgs {
 hipError_t launch_chunk_fwd(const PrefillArgs& a);
 // ok = every g[i], i < n, lies in [lo, hi] (NaN does not); synchronises `stream`
 hipError_t check_range(const float* g, size_t n, float lo, float hi, hipStream_t stream, bool& ok);
+// ok = cu[0] == 0, cu non-decreasing, cu[N] == T (the N + 1 packed-sequence offsets); synchronises
+hipError_t check_offsets(const int32_t* cu, int32_t N, int64_t T, hipStream_t stream, bool& ok);
 hipError_t launch_decode_step(const DecodeArgs& a);
 
 }  // namespace kda

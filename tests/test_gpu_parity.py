@@ -1005,6 +1005,30 @@ def test_range_check_on_request(gpu_lib, monkeypatch):
     torch.cuda.synchronize()
 
 
+def test_offsets_check_on_request(gpu_lib, monkeypatch):
+    """KDA_CHECK_RANGE=1: packed-sequence offsets that do not run from 0 to T without decreasing
+    are refused with KDA_ERR_INVALID_ARGUMENT before anything is launched; valid ones run as usual
+    and give the unchecked results."""
+    from linear_attention_chunkwise_amd import binding
+    cu = inputs.cu_from_lengths([5, 0, 40, 19])                       # [0, 5, 5, 45, 64]
+    x = _to_dev(inputs.make_prefill_inputs(1, int(cu[-1]), 2, 64, 64, seed=71, cu_seqlens=cu))
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    o_ref, S_ref = binding.chunk_fwd(*args, x["cu_seqlens"])
+    monkeypatch.setenv("KDA_CHECK_RANGE", "1")
+    o, S = binding.chunk_fwd(*args, x["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    for bad in ([1, 5, 5, 45, 64], [0, 5, 4, 45, 64], [0, 5, 5, 45, 63], [0, 5, 5, 45, 65]):
+        cub = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        with pytest.raises(binding.KdaError) as ei:
+            binding.chunk_fwd(*args, cub)
+        assert ei.value.status == binding.KDA_ERR_INVALID_ARGUMENT, bad
+        with pytest.raises(binding.KdaError) as ei:
+            binding.chunk_fwd_cp(*args, cub, segments=2)
+        assert ei.value.status == binding.KDA_ERR_INVALID_ARGUMENT, bad
+    torch.cuda.synchronize()
+
+
 def test_range_check_from_concurrent_threads(gpu_lib, monkeypatch):
     """The domain check's flag is one per device: checked calls from two host threads on their own
     streams, one with g in range and one with a value outside it, each get their own verdict."""
