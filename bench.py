@@ -372,6 +372,10 @@ def main():
     if not args.no_cpu_baseline:
         del o, od
         res["cpu_baseline"] = cpu_baseline(x)
+    props = torch.cuda.get_device_properties(dev)
+    res["env"] = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+                  "compute_units": props.multi_processor_count, "hip": torch.version.hip,
+                  "torch": torch.__version__}
     print(json.dumps(res), flush=True)
 
 
