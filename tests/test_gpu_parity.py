@@ -133,6 +133,34 @@ def test_prefill_deterministic(gpu_lib):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def test_results_do_not_depend_on_the_rest_of_the_batch(gpu_lib):
+    """Batch invariance: a sequence's outputs and final state are bitwise the same whether it runs
+    alone, in a fixed-length batch, or packed with sequences of other lengths (the longest-first
+    instantiation); a decode unit's result is the same alone or in a batch."""
+    from linear_attention_chunkwise_amd import binding
+    x = _to_dev(inputs.make_prefill_inputs(3, 130, 2, 128, 128, seed=81))
+    o_b, S_b = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    one = lambda t, n: t[n:n + 1].contiguous()
+    for n in range(3):
+        o_1, S_1 = binding.chunk_fwd(*(one(x[k], n) for k in ("q", "k", "v", "g", "beta", "S0")))
+        assert torch.equal(o_1, o_b[n:n + 1]) and torch.equal(S_1, S_b[n:n + 1]), f"alone {n}"
+    # packed: a 57-token sequence, batch row 1 (130 tokens), a 3-token sequence
+    xp = _to_dev(inputs.make_prefill_inputs(1, 57 + 3, 2, 128, 128, seed=82))
+    cat = lambda k: torch.cat([xp[k][:, :57], x[k][1:2], xp[k][:, 57:]], dim=1).contiguous()
+    S0p = torch.cat([xp["S0"], x["S0"][1:2], xp["S0"]], dim=0).contiguous()
+    cu = torch.tensor([0, 57, 187, 190], dtype=torch.int32, device="cuda")
+    o_p, S_p = binding.chunk_fwd(*(cat(k) for k in ("q", "k", "v", "g", "beta")), S0p, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p[:, 57:187], o_b[1:2]) and torch.equal(S_p[1:2], S_b[1:2]), "packed"
+    d = _to_dev(inputs.make_decode_inputs(9, 2, 128, 128, seed=83))
+    S_all = d["S"].clone()
+    o_all = binding.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], S_all)
+    S_5 = one(d["S"], 5).clone()
+    o_5 = binding.recurrent_step(*(one(d[k], 5) for k in ("q", "k", "v", "g", "beta")), S_5)
+    torch.cuda.synchronize()
+    assert torch.equal(o_5, o_all[5:6]) and torch.equal(S_5, S_all[5:6]), "decode"
+
+
 def test_prefill_resume_matches_one_pass(gpu_lib):
     """Splitting a sequence and re-entering with the first part's final state (eq. (17) with two
     segments) agrees with the single pass within the parity tolerance."""
