@@ -555,6 +555,44 @@ def test_decode_with_states_past_4gib(gpu_lib):
     torch.cuda.empty_cache()
 
 
+def test_prefill_then_decode_steps_match_one_long_prefill(gpu_lib):
+    """The serving flow: a prefill over T tokens whose final state is then advanced by single-token
+    decode steps and by one 3-token pass gives the outputs and final state of one prefill over
+    all the tokens (and of the oracle).  Weak decay and small beta (g x 0.002, beta x 0.25), so the
+    prefill's state still carries the result after the decode tokens."""
+    from linear_attention_chunkwise_amd import binding
+    T, extra = 200, 8
+    x = inputs.make_prefill_inputs(3, T + extra, 2, 128, 128, seed=85)
+    x["g"] = x["g"] * 0.002
+    x["beta"] = (x["beta"].float() * 0.25).to(x["beta"].dtype)
+    x = _to_dev(x)
+    head = lambda t: t[:, :T].contiguous()
+    _, S = binding.chunk_fwd(head(x["q"]), head(x["k"]), head(x["v"]), head(x["g"]), head(x["beta"]),
+                             x["S0"], out_dtype=torch.float32)
+    outs = []
+    for t in range(T, T + 5):                                        # five single steps
+        at = lambda a: a[:, t].contiguous()
+        outs.append(binding.recurrent_step(at(x["q"]), at(x["k"]), at(x["v"]), at(x["g"]),
+                                           at(x["beta"]), S, out_dtype=torch.float32)[:, None])
+    tail = lambda a: a[:, T + 5:].contiguous()                       # then one 3-token pass
+    outs.append(binding.recurrent_multi(tail(x["q"]), tail(x["k"]), tail(x["v"]), tail(x["g"]),
+                                        tail(x["beta"]), S, out_dtype=torch.float32))
+    o_dec = torch.cat(outs, dim=1)
+    o_all, S_all = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close("o[decoded vs one prefill]", o_dec.cpu().numpy(), o_all[:, T:].cpu().numpy())
+    assert_close("S[decoded vs one prefill]", S.cpu().numpy(), S_all.cpu().numpy())
+    c = {k: v.cpu() if torch.is_tensor(v) else v for k, v in x.items()}
+    ro, rS = c_oracle.kda_forward(c["q"], c["k"], c["v"], c["g"], c["beta"], c["S0"])
+    assert_close("o[decoded vs oracle]", o_dec.cpu().numpy(), ro[:, T:])
+    assert_close("S[decoded vs oracle]", S.cpu().numpy(), rS)
+    # the entering state matters: dropping it changes the decoded outputs well beyond tolerance
+    ro0, _ = c_oracle.kda_forward(c["q"][:, T:], c["k"][:, T:], c["v"][:, T:], c["g"][:, T:],
+                                  c["beta"][:, T:], None)
+    assert _rel(ro0, ro[:, T:]) > 0.1
+
+
 def test_decode_matches_prefill_t1(gpu_lib):
     """Decode is eq. (1) with T = 1: the two entry points agree."""
     from linear_attention_chunkwise_amd import binding
