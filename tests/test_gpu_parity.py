@@ -110,6 +110,25 @@ def test_prefill_varlen_with_empty_and_ragged(gpu_lib):
             assert np.array_equal(ST[n], x["S0"][n].numpy())
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["o_f32", "o_bf16"])
+def test_prefill_weak_decay_long_memory(gpu_lib, out_dtype):
+    """Very weak decay and small beta (g x 0.0002, beta x 0.25) over 2000 tokens: the first half of
+    the sequence still shapes the outputs at its end, so errors in the chunk-to-chunk propagation
+    accumulate over ~60 chunks instead of decaying away within a few tokens as they do under the
+    workload's decay."""
+    x = inputs.make_prefill_inputs(2, 2000, 2, 128, 128, seed=87)
+    x["g"] = x["g"] * 0.0002
+    x["beta"] = (x["beta"].float() * 0.25).to(x["beta"].dtype)
+    ro, rST = oracle_all(x)
+    v0 = x["v"].clone()
+    v0[:, :1000] = 0
+    ro0, _ = c_oracle.kda_forward(x["q"], x["k"], v0, x["g"], x["beta"], x["S0"])
+    assert _rel(ro0[:, -32:], ro[:, -32:]) > 0.01          # long memory holds in this regime
+    o, ST = run_gpu(x, out_dtype)
+    assert_close("o", o, ro)
+    assert_close("S_T", ST, rST)
+
+
 def test_prefill_no_final_state_and_inplace(gpu_lib):
     from linear_attention_chunkwise_amd import binding
     x = _to_dev(inputs.make_prefill_inputs(2, 77, 2, 128, 128, seed=5))
