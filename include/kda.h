@@ -225,6 +225,21 @@ kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v
                                      int32_t dk, int32_t dv, kda_dtype in_dtype,
                                      kda_dtype out_dtype, float scale, void* y, hipStream_t stream);
 
+/* Process-wide choice of the precision of the UT transform's inverse (§2.1.1: the WY / UT
+ * representation of the chunk's accumulated Householder-like products), for every prefill entry
+ * point (kda_chunk_fwd, _ckpt, _gate, _cp).
+ *
+ * on = 0 (the default): the inverse's block products and T_b = T Diag(beta) use single bf16
+ * operands.  on = 1: hi + lo bf16 pairs there (separate kernel instantiations), about 24 % more
+ * prefill time.  The single form is accurate to about 1e-4 relative for independent random keys;
+ * with beta near 1 and keys bunched around one direction (entries of A_kk near 1) its output
+ * error grows to about 6e-3 relative, which the pairs bring to 7e-4 .. 1e-3.
+ *
+ * Applies to calls made after it returns, on every host thread and device; work already enqueued
+ * is unaffected.  `previous` (may be NULL) receives the setting before the call.
+ * Returns KDA_OK, or KDA_ERR_INVALID_ARGUMENT when `on` is neither 0 nor 1. */
+kda_status kda_set_precise_solve(int32_t on, int32_t* previous);
+
 /* Static description of a status code.  Never NULL. */
 const char* kda_status_string(kda_status status);
 

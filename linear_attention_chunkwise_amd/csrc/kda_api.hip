@@ -5,12 +5,15 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kda.h"
 #include "kda_launch.h"
 
 namespace {
 
 thread_local char g_last_error[512] = "";
+std::atomic<int32_t> g_precise_solve{0};   // kda_set_precise_solve
 
 kda_status fail(kda_status s, const char* fmt, const char* what, long long x = 0) {
     snprintf(g_last_error, sizeof g_last_error, fmt, what, x);
@@ -117,7 +120,14 @@ kda_status check_cu(const int32_t* cu, int32_t N, int64_t T, hipStream_t stream)
 
 extern "C" {
 
-int32_t kda_version(void) { return (1 << 16) | 0; }
+int32_t kda_version(void) { return (1 << 16) | 1; }
+
+kda_status kda_set_precise_solve(int32_t on, int32_t* previous) {
+    if (on != 0 && on != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be 0 or 1, got %lld", "on", on);
+    const int32_t was = g_precise_solve.exchange(on, std::memory_order_relaxed);
+    if (previous) *previous = was;
+    return ok();
+}
 
 const char* kda_status_string(kda_status s) {
     switch (s) {
@@ -241,6 +251,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                        in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T,
                        ckpt_capacity > 0 ? ckpt : nullptr, ckpt_interval / 32, ckpt_capacity,
                        /*mode*/ 0, /*nseg*/ 1, /*seg_len*/ 0, /*ws*/ nullptr, stream};
+    a.precise = g_precise_solve.load(std::memory_order_relaxed) != 0;
     if (z) {
         a.g = nullptr;
         a.z = z;

@@ -43,10 +43,17 @@
 // Precision: bf16 MFMA with fp32 accumulation.  Operands whose rounding would dominate the error
 // are carried as hi + lo bf16 pairs (products hi*hi + lo*hi + hi*lo): the decayed operands of
 // A_qk, A_qk itself, V - K~ S, V~ in both of its uses, K_end (its rounding would dominate the
-// state's error), and both operands of (Q * exp(G)) S, which dominates short sequences entered
-// with a large state.  A_kk, T_b, K~ and the state as the operand of K~ S are single bf16; the
-// state stays fp32.  Float32 inputs (kFull) carry every operand but A_kk's as a pair.  The scale
-// on q is applied to the outputs (everything is linear in q).
+// state's error), both operands of (Q * exp(G)) S, which dominates short sequences entered with a
+// large state.  A_kk, T_b, K~ and the state as the operand of K~ S are single bf16; the state
+// stays fp32.  Float32 inputs (kFull) carry T_b and K~ as pairs too.  The scale on q is applied to
+// the outputs (everything is linear in q).
+//
+// Precise-solve instantiation (PREC): T_b as a pair, and both operands of every product inside the
+// UT solve as pairs.  With beta near 1 and keys close to one direction, A_kk's entries are near 1,
+// the inverse's entries are of order one, and the single-bf16 rounding of the solve's operands
+// then dominates the output's error (about 6e-3 relative instead of 1e-4 for random keys); the
+// pairs bring it to 7e-4 .. 1e-3 at about 24 % more time, as the solve lies on the critical path
+// of its pipeline interval.
 #include <atomic>
 #include <type_traits>
 
@@ -60,10 +67,12 @@ constexpr int kDVT = 64;   // value columns per workgroup
 constexpr int kNW = 4;     // producer waves = consumer waves
 constexpr int kNT = 128 * kNW;
 
-template <int DK, bool F32IN>
+template <int DK, bool F32IN, bool PREC>
 struct Layout {
     static constexpr bool kFull = F32IN;
-    static constexpr int kNP = kFull ? 2 : 1;               // bf16 planes of "single" operands
+    static constexpr bool kPrec = PREC;
+    static constexpr int kNP = kFull ? 2 : 1;               // bf16 planes of K~
+    static constexpr int kTP = kFull || kPrec ? 2 : 1;      // bf16 planes of T_b
     static constexpr int NCB = DK / 32;                       // 32-channel blocks = intra waves
     static constexpr int RB = DK + 8;                         // bf16 [token][DK] row stride
     static constexpr int TB = kC + 8;                         // bf16 [*][token] row stride
@@ -71,7 +80,7 @@ struct Layout {
     static constexpr int o_Gp = 0;                            // fp32 [NCB][6][64][4] partials
     static constexpr int o_N = o_Gp + NCB * 6 * 64 * 16;      // fp32 2 blocks [16][20]: A_kk diag
     static constexpr int o_Tb = o_N + 2 * SB * 4;             // bf16 planes [C][TB]
-    static constexpr int o_Aq = o_Tb + kNP * kC * TB * 2;     // bf16 hi, lo [C][TB]
+    static constexpr int o_Aq = o_Tb + kTP * kC * TB * 2;     // bf16 hi, lo [C][TB]
     static constexpr int o_Kt = o_Aq + 2 * kC * TB * 2;       // bf16 planes [C][RB]: K~
     static constexpr int o_Qt = o_Kt + kNP * kC * RB * 2;     // bf16 hi, lo [C][RB]: Q~
     static constexpr int o_Ke = o_Qt + 2 * kC * RB * 2;       // bf16 hi, lo [DK][TB] (K_end^T)
@@ -152,6 +161,16 @@ __device__ __forceinline__ void split4(f32x4 a, bf16x4& hi, bf16x4& lo) {
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// The same product on fp32 operands carried as hi + lo bf16 pairs (hi*hi + lo*hi + hi*lo).
+__device__ __forceinline__ f32x4 mma16x(f32x4 a, f32x4 b) {
+    bf16x4 ah, al, bh, bl;
+    split4(a, ah, al);
+    split4(b, bh, bl);
+    f32x4 c = mma16(ah, bh, zero4());
+    c = mma16(al, bh, c);
+    return mma16(ah, bl, c);
 }
 
 // Storage order of every 32-long contraction index in LDS: position pm(c) puts the elements one
@@ -242,10 +261,10 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t&
 // ==================================== producer waves =========================================
 // Wave p owns key channels [32 p, 32 p + 32) (none when p >= DK / 32).  Per chunk: the decayed
 // operands and the partial Gram tiles (interval 1); Q~, K~, K_end^T and gamma (interval 2).
-template <int DK, bool F32IN, bool GATE>
+template <int DK, bool F32IN, bool GATE, bool PREC>
 __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p, int lane,
                                          int64_t row0, int64_t len, int h) {
-    using Lay = Layout<DK, F32IN>;
+    using Lay = Layout<DK, F32IN, PREC>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr bool kFull = Lay::kFull;
     constexpr int RB = Lay::RB, TB = Lay::TB;
@@ -496,10 +515,10 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 // Wave 4 + cw owns value columns [16 cw, 16 cw + 16) of the slice and its dk x 16 state slice.
 // Interval 1 of iteration i: the inter-chunk step of chunk i - 1.  Interval 2: chunk i's T_b
 // (cw = 0) or one A_qk tile (cw = 1..3).
-template <int DK, bool F32IN, bool OUT_F32>
+template <int DK, bool F32IN, bool OUT_F32, bool PREC>
 __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
                                          int64_t row0, int64_t len, int n, int h, int slice, int seg) {
-    using Lay = Layout<DK, F32IN>;
+    using Lay = Layout<DK, F32IN, PREC>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr bool kFull = Lay::kFull;
     constexpr int KS = DK / 32;          // 32-channel contraction steps
@@ -594,7 +613,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         st<bf16x4>(ad + kC * TB, z);
         bf16* td = bfp(Lay::o_Tb) + i16 * TB + pm(16 + 4 * g4);
 #pragma unroll
-        for (int pl = 0; pl < Lay::kNP; ++pl) st<bf16x4>(td + pl * kC * TB, z);
+        for (int pl = 0; pl < Lay::kTP; ++pl) st<bf16x4>(td + pl * kC * TB, z);
     }
 
     bf16x8 Id0;   // identity block: B operand selecting columns 0..15 of a 32-long step
@@ -616,7 +635,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     };
     auto put_tb = [&](int r, int c, float v) {   // T_b[r][c] (one or two bf16 planes)
         bf16* Tb = bfp(Lay::o_Tb);
-        if constexpr (kFull) {
+        if constexpr (Lay::kTP == 2) {
             bf16 hh, ll;
             split_bf16(v, hh, ll);
             Tb[r * TB + pm(c)] = hh;
@@ -645,14 +664,16 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 return ld<bf16x8>(bfp(off) + row * stride + col + 8 * g4);
             };
             // batch 1: rows of K~ (for K~ S) and of T_b
-            bf16x8 tbr[2][Lay::kNP], kt[2][KS][Lay::kNP];
+            constexpr int kPL = Lay::kTP > Lay::kNP ? Lay::kTP : Lay::kNP;
+            bf16x8 tbr[2][Lay::kTP], kt[2][KS][Lay::kNP];
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
-                for (int pl = 0; pl < Lay::kNP; ++pl) {
-                    tbr[ta][pl] = frag(Lay::o_Tb + pl * kC * TB * 2, 16 * ta + i16, TB, 0);
+                for (int pl = 0; pl < kPL; ++pl) {
+                    if (pl < Lay::kTP) tbr[ta][pl] = frag(Lay::o_Tb + pl * kC * TB * 2, 16 * ta + i16, TB, 0);
+                    if (pl < Lay::kNP)
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) kt[ta][s][pl] = frag(Lay::o_Kt + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
+                        for (int s = 0; s < KS; ++s) kt[ta][s][pl] = frag(Lay::o_Kt + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
                 }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -683,10 +704,11 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
-                for (int pl = 0; pl < Lay::kNP; ++pl) {
-                    pin(tbr[ta][pl]);
+                for (int pl = 0; pl < kPL; ++pl) {
+                    if (pl < Lay::kTP) pin(tbr[ta][pl]);
+                    if (pl < Lay::kNP)
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) pin(kt[ta][s][pl]);
+                        for (int s = 0; s < KS; ++s) pin(kt[ta][s][pl]);
                 }
             // batch 2: rows of Q~ (hi, lo) and of A_qk (hi, lo)
             bf16x8 qr[2][KS][2], ar[2][2];
@@ -700,7 +722,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 }
             __builtin_amdgcn_sched_barrier(0);
             // V~ = T_b (V - K~ S): the residual R = V - K~ S in fp32, then one product with T_b
-            // (R split, so only T_b is rounded)
+            // (R split, so only T_b's own planes are rounded)
             f32x4 Vt[2];
             {
                 f32x4 R[2];
@@ -723,7 +745,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 for (int ta = 0; ta < 2; ++ta) {
                     f32x4 v = mma(tbr[ta][0], Rh, zero4());
                     v = mma(tbr[ta][0], Rl, v);
-                    if constexpr (kFull) v = mma(tbr[ta][1], Rh, v);
+                    if constexpr (Lay::kTP == 2) v = mma(tbr[ta][1], Rh, v);
                     Vt[ta] = v;
                 }
             }
@@ -830,8 +852,8 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 //     D = (I + L0)^-1 (closed form, fp32),  E = D - D L1 D,  X = E - E L2 E,
                 // each product filling blocks that are zero in the previous level (no
                 // cancellation), and T10 = -T11 N10 T00.  Products are 16x16x16 MFMAs on single
-                // bf16 operands: T_b is rounded to bf16 in any case, and the diagonal 4x4 blocks
-                // stay fp32.  Forms: row form of M in lane (i16, g4) = M[i16][4 g4 + j], column
+                // bf16 operands (on hi + lo pairs in the precise-solve instantiation), and the
+                // diagonal 4x4 blocks stay fp32.  Forms: row form of M in lane (i16, g4) = M[i16][4 g4 + j], column
                 // form = M[4 g4 + j][i16]; mma16(row form of X, column form of Y) is the column
                 // form of X Y, and the row form of M is the column form of M^T.
                 const float bt[2] = {f32p(Lay::o_beta)[i16], f32p(Lay::o_beta)[16 + i16]};
@@ -892,19 +914,32 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                     const float y0 = d0 - y1 * n1[q][0] - y2 * n2[q][0] - d3 * n3[q][0];
                     const f32x4 Dc = on_diag ? f32x4{d0, x1, x2, x3} : zero4();
                     const f32x4 Dr = on_diag ? f32x4{y0, y1, y2, d3} : zero4();
-                    const bf16x4 Dcb = to_bf16x4(Dc), Drb = to_bf16x4(Dr);
-                    // E = D - D L1 D (column form), E^T = D^T - D^T L1^T D^T (row form of E)
-                    const f32x4 Ec = Dc - mma16(Drb, to_bf16x4(mma16(to_bf16x4(mask(Nr[q], l1r)), Dcb, zero4())), zero4());
-                    const f32x4 Er = Dr - mma16(Dcb, to_bf16x4(mma16(to_bf16x4(mask(Nc[q], l1c)), Drb, zero4())), zero4());
-                    const bf16x4 Ecb = to_bf16x4(Ec), Erb = to_bf16x4(Er);
-                    // X = E - E L2 E: column form for T00, row form for T11
-                    if (q == 0)
-                        Xc0 = Ec - mma16(Erb, to_bf16x4(mma16(to_bf16x4(mask(Nr[q], l2r)), Ecb, zero4())), zero4());
-                    else
-                        Xr1 = Er - mma16(Ecb, to_bf16x4(mma16(to_bf16x4(mask(Nc[q], l2c)), Erb, zero4())), zero4());
+                    if constexpr (Lay::kPrec) {
+                        // E = D - D L1 D (column form), E^T = D^T - D^T L1^T D^T (row form of E)
+                        const f32x4 Ec = Dc - mma16x(Dr, mma16x(mask(Nr[q], l1r), Dc));
+                        const f32x4 Er = Dr - mma16x(Dc, mma16x(mask(Nc[q], l1c), Dr));
+                        // X = E - E L2 E: column form for T00, row form for T11
+                        if (q == 0)
+                            Xc0 = Ec - mma16x(Er, mma16x(mask(Nr[q], l2r), Ec));
+                        else
+                            Xr1 = Er - mma16x(Ec, mma16x(mask(Nc[q], l2c), Er));
+                    } else {
+                        const bf16x4 Dcb = to_bf16x4(Dc), Drb = to_bf16x4(Dr);
+                        const f32x4 Ec = Dc - mma16(Drb, to_bf16x4(mma16(to_bf16x4(mask(Nr[q], l1r)), Dcb, zero4())), zero4());
+                        const f32x4 Er = Dr - mma16(Dcb, to_bf16x4(mma16(to_bf16x4(mask(Nc[q], l1c)), Drb, zero4())), zero4());
+                        const bf16x4 Ecb = to_bf16x4(Ec), Erb = to_bf16x4(Er);
+                        if (q == 0)
+                            Xc0 = Ec - mma16(Erb, to_bf16x4(mma16(to_bf16x4(mask(Nr[q], l2r)), Ecb, zero4())), zero4());
+                        else
+                            Xr1 = Er - mma16(Ecb, to_bf16x4(mma16(to_bf16x4(mask(Nc[q], l2c)), Erb, zero4())), zero4());
+                    }
                 }
                 // T10 = -T11 (N10 T00), column form
-                const f32x4 T10c = -mma16(to_bf16x4(Xr1), to_bf16x4(mma16(to_bf16x4(N10r), to_bf16x4(Xc0), zero4())), zero4());
+                f32x4 T10c;
+                if constexpr (Lay::kPrec)
+                    T10c = -mma16x(Xr1, mma16x(N10r, Xc0));
+                else
+                    T10c = -mma16(to_bf16x4(Xr1), to_bf16x4(mma16(to_bf16x4(N10r), to_bf16x4(Xc0), zero4())), zero4());
                 // T_b = T Diag(beta): T00 and T10 from column forms (column i16), T11 from its row
                 // form (row 16 + i16, four adjacent columns)
                 const f32x4 bcol = ld<f32x4>(f32p(Lay::o_beta) + 16 + 4 * g4);
@@ -915,7 +950,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 }
                 const f32x4 t11 = Xr1 * bcol;
                 bf16* tr = bfp(Lay::o_Tb) + (16 + i16) * TB + pm(16 + 4 * g4);
-                if constexpr (kFull) {
+                if constexpr (Lay::kTP == 2) {
                     bf16x4 hv, lv;
                     split4(t11, hv, lv);
                     st<bf16x4>(tr, hv);
@@ -994,8 +1029,8 @@ __device__ int seq_of_rank(const PrefillArgs& a, int r, char* smem) {
 
 // Both roles run the same number of iterations (chunks + 1) with two barriers each.  RANK: packed
 // sequences (at most kRankMax) in longest-first order; a separate instantiation, so that the
-// fixed-length kernel's code is not changed by the ranking.
-template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
+// fixed-length kernel's code is not changed by the ranking.  PREC: the precise solve.
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, bool PREC>
 __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
@@ -1007,7 +1042,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     const int seg = (unit / a.H) % nseg;
     const int rank = unit / (a.H * nseg);
     if (a.mode == 1 && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;   // not needed
-    KDA_POISON(smem, (Layout<DK, F32IN>::total));
+    KDA_POISON(smem, (Layout<DK, F32IN, PREC>::total));
     KDA_POISON_DONE();
     int n = rank;
     if constexpr (RANK) n = seq_of_rank(a, rank, smem);
@@ -1021,14 +1056,14 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
-    if (wave < kNW) producer<DK, F32IN, GATE>(a, smem, wave, lane, row0, len, h);
-    else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg);
+    if (wave < kNW) producer<DK, F32IN, GATE, PREC>(a, smem, wave, lane, row0, len, h);
+    else consumer<DK, F32IN, OUT_F32, PREC>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg);
 }
 
-template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, bool PREC>
 static hipError_t launch_one(const PrefillArgs& a) {
-    using Lay = Layout<DK, F32IN>;
-    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE, RANK>;
+    using Lay = Layout<DK, F32IN, PREC>;
+    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE, RANK, PREC>;
     // The LDS limit is a per-device attribute of the kernel: set it once on each device this
     // instantiation launches on (devices past 63 set it on every launch).  Concurrent first calls
     // may both set it; the value is the same.
@@ -1051,10 +1086,16 @@ static hipError_t launch_one(const PrefillArgs& a) {
     return hipGetLastError();
 }
 
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool PREC>
+static hipError_t launch_ranked(const PrefillArgs& a) {
+    if (a.cu && a.N > 1 && a.N <= kRankMax) return launch_one<DK, F32IN, OUT_F32, GATE, true, PREC>(a);
+    return launch_one<DK, F32IN, OUT_F32, GATE, false, PREC>(a);
+}
+
 template <int DK, bool F32IN, bool OUT_F32, bool GATE>
 static hipError_t launch_prefill(const PrefillArgs& a) {
-    if (a.cu && a.N > 1 && a.N <= kRankMax) return launch_one<DK, F32IN, OUT_F32, GATE, true>(a);
-    return launch_one<DK, F32IN, OUT_F32, GATE, false>(a);
+    return a.precise ? launch_ranked<DK, F32IN, OUT_F32, GATE, true>(a)
+                     : launch_ranked<DK, F32IN, OUT_F32, GATE, false>(a);
 }
 
 template <bool GATE>

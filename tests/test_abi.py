@@ -38,6 +38,18 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_precise_solve_switch(lib):
+    """Host-only: the setting round-trips, reports the previous value and rejects values other
+    than 0 and 1 without changing the setting."""
+    prev = ctypes.c_int32(-1)
+    assert lib.kda_set_precise_solve(1, ctypes.byref(prev)) == 0 and prev.value == 0
+    assert lib.kda_set_precise_solve(2, ctypes.byref(prev)) == 1
+    assert b"0 or 1" in lib.kda_last_error()
+    assert lib.kda_set_precise_solve(0, ctypes.byref(prev)) == 0 and prev.value == 1
+    assert lib.kda_set_precise_solve(0, None) == 0
+    assert binding.set_precise_solve(True) is False and binding.set_precise_solve(False) is True
+
+
 def test_status_strings(lib):
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARGUMENT"
