@@ -1131,6 +1131,18 @@ def _every_entry_point():
                                        interval=32, capacity=5)
     xf = _to_dev(inputs.make_prefill_inputs(1, 70, 2, 64, 64, dtype=torch.float32, seed=63))
     r["f32"] = binding.chunk_fwd(xf["q"], xf["k"], xf["v"], xf["g"], xf["beta"], xf["S0"])
+    prev = binding.set_precise_solve(True)   # the precise-solve instantiations (own LDS layout)
+    try:
+        r["precise_varlen"] = binding.chunk_fwd(xv["q"], xv["k"], xv["v"], xv["g"], xv["beta"],
+                                                xv["S0"], xv["cu_seqlens"], out_dtype=torch.float32)
+        r["precise_gate"] = binding.chunk_fwd_gate(xv["q"], xv["k"], xv["v"], xv["z"], xv["A_log"],
+                                                   xv["beta"], xv["S0"], xv["cu_seqlens"])
+        r["precise_plain"] = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+        r["precise_cp"] = binding.chunk_fwd_cp(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
+                                               segments=3)
+        r["precise_f32"] = binding.chunk_fwd(xf["q"], xf["k"], xf["v"], xf["g"], xf["beta"], xf["S0"])
+    finally:
+        binding.set_precise_solve(prev)
     d = _to_dev(inputs.make_prefill_inputs(6, 3, 2, 128, 128, seed=64, with_logits=True))
     one = lambda t: t[:, 0].contiguous()
     S = d["S0"].clone()
