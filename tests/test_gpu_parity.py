@@ -804,6 +804,31 @@ def test_decode_multi_matches_repeated_steps(gpu_lib):
     assert_close("S", S1.cpu().numpy(), S2.cpu().numpy())
 
 
+def test_decode_steps_with_correlated_keys(gpu_lib):
+    """Decode has no triangular solve: in the beta = 1, bunched-keys regime its token-by-token
+    float32 update meets the bar without any precision switch (64 steps, then 4-token passes)."""
+    from linear_attention_chunkwise_amd import binding
+    x = _correlated_keys_case(0.05)
+    n = 64
+    for kk in ("q", "k", "v", "g", "beta"):
+        x[kk] = x[kk][:, :n].contiguous()
+    ro, rST = oracle_all(x)
+    d = _to_dev(x)
+    S = d["S0"].clone()
+    o = torch.stack([binding.recurrent_step(*(d[kk][:, t].contiguous()
+                                              for kk in ("q", "k", "v", "g", "beta")), S,
+                                            out_dtype=torch.float32) for t in range(n)], 1)
+    S2 = d["S0"].clone()
+    o2 = torch.cat([binding.recurrent_multi(*(d[kk][:, t:t + 4].contiguous()
+                                              for kk in ("q", "k", "v", "g", "beta")), S2,
+                                            out_dtype=torch.float32) for t in range(0, n, 4)], 1)
+    torch.cuda.synchronize()
+    assert_close("o[step]", o.cpu().numpy(), ro)
+    assert_close("S[step]", S.cpu().numpy(), rST)
+    assert_close("o[multi]", o2.cpu().numpy(), ro)
+    assert_close("S[multi]", S2.cpu().numpy(), rST)
+
+
 def test_decode_multi_workload_n1024_h32_k4(gpu_lib):
     """Speculative verification at the decode workload's size: 4 drafted tokens per sequence,
     a random accepted prefix committed; sampled sequences against the oracle."""
