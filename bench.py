@@ -309,15 +309,6 @@ def main():
                                "alg_bytes": gbytes, "alg_GBps": gbytes / (g_ms * 1e-3) / 1e9,
                                "what": "kda_chunk_fwd_gate: g = -5 Sigmoid(exp(A_h) z) formed "
                                        "in the kernel from bf16 z"}
-        binding.set_precise_solve(True)
-        try:
-            p_ms = time_launches(lambda: binding.chunk_fwd(
-                x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], o=o, S_T=ST))
-        finally:
-            binding.set_precise_solve(False)
-        res["prefill_precise_solve"] = {"ms": p_ms, "tokens_per_s": B * T / (p_ms * 1e-3),
-                                        "what": "kda_set_precise_solve(1): hi + lo bf16 pairs in "
-                                                "the UT solve's products and T_b"}
         K = 4
         m = inputs.make_prefill_inputs(dcfg.N, K, dcfg.H, dcfg.dk, dcfg.dv, seed=1, device=dev)
         om = torch.empty((dcfg.N, K, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)

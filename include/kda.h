@@ -72,9 +72,16 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * S0 exactly (in-place state advance).  o and S_T must not overlap any input (cu_seqlens
  * included) or each other.
  *
- * Supported: dk in {64, 128}; dv in {64, 128}; in_dtype KDA_BF16, or KDA_F32 at dk = 64 (float32
- * inputs are carried at higher internal precision); out_dtype KDA_BF16 or KDA_F32; T >= 0;
- * B, H >= 1; N * H <= 2^30; H * max(dk, dv) <= 2^22 (KDA_ERR_UNSUPPORTED beyond).
+ * Supported: dk in {64, 128}; dv in {64, 128}; in_dtype KDA_BF16 or KDA_F32; out_dtype KDA_BF16
+ * or KDA_F32; T >= 0; B, H >= 1; N * H <= 2^30; H * max(dk, dv) <= 2^22 (KDA_ERR_UNSUPPORTED
+ * beyond).
+ *
+ * Accuracy: relative L2 error of o and S_T against a float64 evaluation of eq. (1) on the same
+ * stored inputs is about 2e-4 for random unit keys and stays below 5e-4 in the hardest regime
+ * tested (beta = 1, weak decay, keys bunched around one direction); a bf16 o adds its own
+ * rounding (1.66e-3 relative).  q and k are expected to be L2-normalised as eq. (2) produces them
+ * (|q|, |k| <= 1 per entry): the kernel carries decayed q and k as float16.  v and S0 may have any
+ * finite magnitude: the value path is rescaled by powers of two inside the kernel.
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const void* beta, const float* S0, const int32_t* cu_seqlens,
@@ -224,21 +231,6 @@ kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v
                                      const int32_t* n_commit, int32_t N, int32_t K, int32_t H,
                                      int32_t dk, int32_t dv, kda_dtype in_dtype,
                                      kda_dtype out_dtype, float scale, void* y, hipStream_t stream);
-
-/* Process-wide choice of the precision of the UT transform's inverse (§2.1.1: the WY / UT
- * representation of the chunk's accumulated Householder-like products), for every prefill entry
- * point (kda_chunk_fwd, _ckpt, _gate, _cp).
- *
- * on = 0 (the default): the inverse's block products and T_b = T Diag(beta) use single bf16
- * operands.  on = 1: hi + lo bf16 pairs there (separate kernel instantiations), about 24 % more
- * prefill time.  The single form is accurate to about 1e-4 relative for independent random keys;
- * with beta near 1 and keys bunched around one direction (entries of A_kk near 1) its output
- * error grows to about 6e-3 relative, which the pairs bring to 7e-4 .. 1e-3.
- *
- * Applies to calls made after it returns, on every host thread and device; work already enqueued
- * is unaffected.  `previous` (may be NULL) receives the setting before the call.
- * Returns KDA_OK, or KDA_ERR_INVALID_ARGUMENT when `on` is neither 0 nor 1. */
-kda_status kda_set_precise_solve(int32_t on, int32_t* previous);
 
 /* Static description of a status code.  Never NULL. */
 const char* kda_status_string(kda_status status);

@@ -23,7 +23,7 @@ EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_gate", "kda_chu
            "kda_chunk_fwd_cp_workspace_size", "kda_chunk_fwd_cp_segments", "kda_recurrent_step",
            "kda_recurrent_step_gate",
            "kda_recurrent_multi", "kda_recurrent_multi_fused", "kda_status_string",
-           "kda_last_error", "kda_version", "kda_set_precise_solve")
+           "kda_last_error", "kda_version")
 
 _lib = None
 
@@ -81,8 +81,6 @@ def load(path: str = LIB_PATH):
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
     lib.kda_version.restype = ctypes.c_int32
-    lib.kda_set_precise_solve.argtypes = [i32, ctypes.POINTER(ctypes.c_int32)]
-    lib.kda_set_precise_solve.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -210,14 +208,6 @@ def chunk_fwd_ckpt(q, k, v, g, beta, S0=None, cu_seqlens=None, *, interval: int,
              int(interval), int(capacity), _p(ckpt), _stream(dev))
     _check(st)
     return o, S_T, ckpt
-
-
-def set_precise_solve(on: bool) -> bool:
-    """Select the precise UT solve for later prefill calls (kda_set_precise_solve); returns the
-    previous setting."""
-    prev = ctypes.c_int32(0)
-    _check(load().kda_set_precise_solve(int(bool(on)), ctypes.byref(prev)))
-    return bool(prev.value)
 
 
 def cp_segments(n_units: int, dk: int, dv: int, slots: int = 256) -> int:

@@ -5,15 +5,12 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <atomic>
-
 #include "kda.h"
 #include "kda_launch.h"
 
 namespace {
 
 thread_local char g_last_error[512] = "";
-std::atomic<int32_t> g_precise_solve{0};   // kda_set_precise_solve
 
 kda_status fail(kda_status s, const char* fmt, const char* what, long long x = 0) {
     snprintf(g_last_error, sizeof g_last_error, fmt, what, x);
@@ -122,13 +119,6 @@ extern "C" {
 
 int32_t kda_version(void) { return (1 << 16) | 1; }
 
-kda_status kda_set_precise_solve(int32_t on, int32_t* previous) {
-    if (on != 0 && on != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be 0 or 1, got %lld", "on", on);
-    const int32_t was = g_precise_solve.exchange(on, std::memory_order_relaxed);
-    if (previous) *previous = was;
-    return ok();
-}
-
 const char* kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";
@@ -168,8 +158,6 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     // the kernel addresses one 32-token chunk of a head's rows with 32-bit byte offsets
     if ((int64_t)H * (dk > dv ? dk : dv) > (int64_t)1 << 22)
         return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "H*d", (long long)H * (dk > dv ? dk : dv));
-    if (in_dtype == KDA_F32 && dk != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: float32 inputs are supported at dk = 64 only (got %lld)", "in_dtype", dk);
 
     const int64_t tokens = (int64_t)B * T;
     const size_t es = dsize(in_dtype);
@@ -251,7 +239,6 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
                        in_dtype == KDA_F32, out_dtype == KDA_F32, scale, o, S_T,
                        ckpt_capacity > 0 ? ckpt : nullptr, ckpt_interval / 32, ckpt_capacity,
                        /*mode*/ 0, /*nseg*/ 1, /*seg_len*/ 0, /*ws*/ nullptr, stream};
-    a.precise = g_precise_solve.load(std::memory_order_relaxed) != 0;
     if (z) {
         a.g = nullptr;
         a.z = z;

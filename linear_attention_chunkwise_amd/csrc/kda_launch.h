@@ -39,8 +39,6 @@ struct PrefillArgs {
     // like q
     const void* z = nullptr;
     const float* A_log = nullptr;
-    // UT solve and T_b on hi + lo bf16 pairs (the precise-solve instantiations)
-    bool precise = false;
 };
 
 struct DecodeArgs {

@@ -4,14 +4,21 @@
 // inside a chunk.  For a chunk entered with state S (positions r = 0..C-1), G_r is the running
 // sum of g inside the chunk (log of the cumulative decay gamma of eq. (3)), and unrolling eq. (1)
 // over the chunk gives (the UT transform the pages defer to Kimi Linear):
-//     A_kk[r,i] = beta_r sum_c k_rc k_ic exp(G_rc - G_ic)        i < r   (strictly lower)
-//     T = (I + A_kk)^-1,  T_b = T Diag(beta),  K~ = K * exp(G)
-//     V~ = T_b (V - K~ S)            (pseudo-values; the same as U - W S with U = T_b V and
-//                                     W = T_b K~, computed without forming W)
-//     A_qk[r,i] = sum_c q_rc k_ic exp(G_rc - G_ic)             i <= r  (eq. (4): Tril keeps
-//                                                                        the diagonal)
-//     O = (Q * exp(G)) S + A_qk V~                                        (eq. (4))
+//     A_kk[r,i] = sum_c k_rc k_ic exp(G_rc - G_ic)                 i < r   (strictly lower)
+//     T = (I + Diag(beta) A_kk)^-1,  T_b = T Diag(beta),  K~ = K * exp(G)
+//     V~ = T_b (V - K~ S)            (pseudo-values, the U - W S of §2.1.1)
+//     A_qk[r,i] = sum_c q_rc k_ic exp(G_rc - G_ic)                 i <= r  (eq. (4): Tril keeps
+//                                                                            the diagonal)
+//     O = (Q * exp(G)) S + A_qk V~                                            (eq. (4))
 //     S <- Diag(exp(G_last)) S + (K * exp(G_last - G))^T V~.
+// The kernel never forms V~: with R = V - K~ S, M = A_qk T_b (C x C) and W = K_end^T T_b
+// (dk x C, K_end = K * exp(G_last - G)), associativity gives
+//     O = Q~ S + M R,      S <- Diag(gamma) S + W R.
+// M and W depend on the chunk only, not on the state, so they are formed a pipeline stage ahead
+// of the state step and shared by every value column.  This is also what keeps the rounding
+// small: with keys bunched around one direction and beta near 1, V~ is a sequence of
+// differences whose running sums (A_qk V~, K_end^T V~) cancel almost completely, while M and W
+// are formed once from accurate factors and the state step multiplies well-scaled R.
 //
 // Decayed products inside a chunk use 16-token sub-tiles (§2.1.1, "lower-bounded decay"): for the
 // row tile a with reference E = G at the end of tile a-1 (0 for a = 0),
@@ -21,39 +28,32 @@
 // is a dense MFMA product.
 //
 // Grid: one 512-thread workgroup per (sequence, head, 64-column slice of dv); the slices of one
-// head go to the same XCD so their reads of q, k, g share L2.  Only the last of the steps below
-// depends on the state, so the workgroup is a two-stage pipeline: four producer waves prepare
-// chunk i while four consumer waves advance the state through chunk i - 1.  Each SIMD runs one
-// wave of each kind, so one kind's latency hides behind the other's issue.  Two workgroup
-// barriers per iteration; every hand-off buffer is written after the barrier that ends its last
-// read, so one copy of each suffices.
-//   interval 1  producers: inputs of chunk i (prefetched one chunk ahead), in-tile decay prefix
-//               (DPP scan over the 16 token lanes of a row), decayed operands in registers and the
-//               partial Gram tiles of A_kk and A_qk over each wave's 32 key channels.
-//               consumers: the inter-chunk step of chunk i - 1 on their 16 value columns:
-//               V~ = T_b (V - K~ S), O = Q~ S + A_qk V~ (written out),
-//               S <- Diag(gamma) S + K_end^T V~.  The state slice (dk x 16, fp32) stays in MFMA
-//               accumulators for the whole sequence.
-//   interval 2  producers: Q~, K~, K_end^T ("transposed" by a product with an identity block)
-//               and the decay of the chunk to LDS.
-//               consumer 0: T_b from the reduced Gram tiles by block elimination with
-//               16x16x16 MFMA products (closed-form 4x4 diagonal blocks, then 8x8, 16x16, 32x32).
-//               consumers 1-3: one masked A_qk tile each.
+// head go to the same XCD so their reads of q, k, g share L2.  Four producer waves (channel
+// slices) and four consumer waves (16 value columns each), one of each per SIMD.  Iteration it
+// has two intervals separated by workgroup barriers and works on three chunks at once:
+//   interval 1  producers, chunk it: decay prefix (DPP scan over the 16 token lanes of a row),
+//                   decayed operands, partial Gram tiles of A_kk and A_qk over the wave's 32 key
+//                   channels.
+//               consumers, chunk it - 2: the state step on their 16 columns: R = V - K~ S,
+//                   O = Q~ S + M R (written out), S <- gamma S + W R; consumer 2 also completes
+//                   T_b of chunk it - 1 with its off-diagonal block T10 = -T11 N10 T00.
+//   interval 2  producers: the rows of W over the wave's channels (and M) for chunk it - 1, from
+//                   the K_end fragments they kept; Q~, K~, gamma and K_end of chunk it.
+//               consumers, chunk it: the diagonal blocks T00 (consumer 0) and T11 (consumer 1) of
+//                   the UT transform, beta N10 and the A_qk tiles (consumers 2, 3); every
+//                   consumer sets the scale of its value path for chunk it - 1.
+// The state slice (dk x 16, fp32) stays in MFMA accumulators for the whole sequence.  Every
+// hand-off buffer is read at least one barrier after it was written and written again only after
+// its last read; buffers whose writer runs ahead of the reader are doubled.
 //
-// Precision: bf16 MFMA with fp32 accumulation.  Operands whose rounding would dominate the error
-// are carried as hi + lo bf16 pairs (products hi*hi + lo*hi + hi*lo): the decayed operands of
-// A_qk, A_qk itself, V - K~ S, V~ in both of its uses, K_end (its rounding would dominate the
-// state's error), both operands of (Q * exp(G)) S, which dominates short sequences entered with a
-// large state.  A_kk, T_b, K~ and the state as the operand of K~ S are single bf16; the state
-// stays fp32.  Float32 inputs (kFull) carry T_b and K~ as pairs too.  The scale on q is applied to
+// Precision: Gram tiles on bf16 hi + lo pairs (products hi*hi + lo*hi + hi*lo, fp32
+// accumulation: the column factors reach exp(80), beyond float16); the UT solve on the fp32
+// MFMA; M and W from float16 hi + lo pairs of A_qk, T_b and K_end; the state step on single
+// float16 operands (Q~, K~, S, M, W, R).  To keep the value path inside float16's range each
+// consumer wave carries its state as S 2^-e with a power-of-two exponent e chosen, per chunk,
+// from the largest |S| and |V| alone (history-free, so a run resumed from a checkpoint repeats
+// the same arithmetic); V is scaled by 2^-e and the outputs by 2^e.  The scale on q is applied to
 // the outputs (everything is linear in q).
-//
-// Precise-solve instantiation (PREC): T_b as a pair, and both operands of every product inside the
-// UT solve as pairs.  With beta near 1 and keys close to one direction, A_kk's entries are near 1,
-// the inverse's entries are of order one, and the single-bf16 rounding of the solve's operands
-// then dominates the output's error (about 6e-3 relative instead of 1e-4 for random keys); the
-// pairs bring it to 7e-4 .. 1e-3 at about 24 % more time, as the solve lies on the critical path
-// of its pipeline interval.
 #include <atomic>
 #include <type_traits>
 
@@ -67,28 +67,29 @@ constexpr int kDVT = 64;   // value columns per workgroup
 constexpr int kNW = 4;     // producer waves = consumer waves
 constexpr int kNT = 128 * kNW;
 
-template <int DK, bool F32IN, bool PREC>
+template <int DK>
 struct Layout {
-    static constexpr bool kFull = F32IN;
-    static constexpr bool kPrec = PREC;
-    static constexpr int kNP = kFull ? 2 : 1;               // bf16 planes of K~
-    static constexpr int kTP = kFull || kPrec ? 2 : 1;      // bf16 planes of T_b
-    static constexpr int NCB = DK / 32;                       // 32-channel blocks = intra waves
-    static constexpr int RB = DK + 8;                         // bf16 [token][DK] row stride
-    static constexpr int TB = kC + 8;                         // bf16 [*][token] row stride
-    static constexpr int SB = 16 * 20 + 16;                   // fp32 16x16 block stride (banks +16)
-    static constexpr int o_Gp = 0;                            // fp32 [NCB][6][64][4] partials
-    static constexpr int o_N = o_Gp + NCB * 6 * 64 * 16;      // fp32 2 blocks [16][20]: A_kk diag
-    static constexpr int o_Tb = o_N + 2 * SB * 4;             // bf16 planes [C][TB]
-    static constexpr int o_Aq = o_Tb + kTP * kC * TB * 2;     // bf16 hi, lo [C][TB]
-    static constexpr int o_Kt = o_Aq + 2 * kC * TB * 2;       // bf16 planes [C][RB]: K~
-    static constexpr int o_Qt = o_Kt + kNP * kC * RB * 2;     // bf16 hi, lo [C][RB]: Q~
-    static constexpr int o_Ke = o_Qt + 2 * kC * RB * 2;       // bf16 hi, lo [DK][TB] (K_end^T)
-    static constexpr int o_gam = o_Ke + 2 * DK * TB * 2;      // fp32 [DK]
-    static constexpr int o_beta = o_gam + DK * 4;             // fp32 [C]
-    static constexpr int total = o_beta + kC * 4;
+    static constexpr int NCB = DK / 32;                     // 32-channel blocks = producer waves
+    static constexpr int RB = DK + 8;                       // f16 [token][DK] row stride
+    static constexpr int TB = kC + 8;                       // f16 [*][token] row stride
+    static constexpr int SB = 16 * 20 + 16;                 // fp32 16x16 block stride (banks +16)
+    static constexpr int GPB = NCB * 6 * 64 * 16;           // one set of partial Gram tiles
+    static constexpr int QKB = 2 * kC * RB * 2 + DK * 4;    // Q~, K~ rows, gamma
+    static constexpr int CPL = kC * TB * 2;                 // one C x C plane
+    static constexpr int o_Gp = 0;                          // fp32 [NCB][6][64][4]
+    static constexpr int o_beta = o_Gp + GPB;               // fp32 [2][C]
+    static constexpr int o_QK = o_beta + 2 * kC * 4;        // [2] x {Q~ [C][RB], K~ [C][RB] f16, gamma [DK]}
+    static constexpr int o_Tb = o_QK + 2 * QKB;             // [2] x T_b^T hi, lo [C][TB] f16
+    static constexpr int o_Aq = o_Tb + 2 * 2 * CPL;         // [2] x A_qk hi, lo [C][TB] f16
+    static constexpr int o_M = o_Aq + 2 * 2 * CPL;          // M [C][TB] f16
+    static constexpr int o_W = o_M + CPL;                   // W [DK][TB] f16
+    static constexpr int o_N = o_W + DK * TB * 2;           // fp32 2 blocks [16][20]: solve scratch
+    static constexpr int o_Pub = o_N + 2 * SB * 4;          // fp32 3 blocks [16][20]: T00, T11, N10
+    static constexpr int total = o_Pub + 3 * SB * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
-    static_assert(o_N - o_Gp >= 4 * (1024 + 1), "sequence ranking scratch fits the Gram region");
+    static_assert(GPB >= 4 * (1024 + 1), "sequence ranking scratch fits the Gram region");
+    static_assert(o_QK % 16 == 0 && QKB % 16 == 0 && o_Tb % 16 == 0 && o_W % 16 == 0 && o_N % 16 == 0,
+                  "16-byte aligned regions");
 };
 
 // DPP row shift right by N lanes inside each 16-lane row, zero fill.
@@ -106,6 +107,26 @@ __device__ __forceinline__ float row_scan16(float x) {   // inclusive prefix sum
     return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
+// Maximum over the 64 lanes of a wave (wave-uniform result): quad swaps, half-row and row
+// mirrors inside each 16-lane row, then the four rows.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));    // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f<0x4E>(x));    // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f<0x141>(x));   // row_half_mirror
+    x = fmaxf(x, dpp_f<0x140>(x));   // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, as a packed word.
@@ -114,10 +135,23 @@ __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
+// Two floats to two float16 (round to nearest even) in one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_h(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
     const uint4 w{cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3]), cvt_pk(x[4], x[5]), cvt_pk(x[6], x[7])};
     return __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ f16x8 to_f16x8(const float* x) {
+    const uint4 w{cvt_pk_h(x[0], x[1]), cvt_pk_h(x[2], x[3]), cvt_pk_h(x[4], x[5]), cvt_pk_h(x[6], x[7])};
+    return __builtin_bit_cast(f16x8, w);
+}
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 a) {
+    return __builtin_bit_cast(f16x4, uint2{cvt_pk_h(a[0], a[1]), cvt_pk_h(a[2], a[3])});
 }
 
 // x = hi + lo, hi = bf16(x), lo = bf16(x - hi): pairs are converted together and hi is widened
@@ -135,6 +169,20 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
     lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
 }
 
+// The same split on float16 halves (22 significant bits for values of order one).
+__device__ __forceinline__ void split_h4(f32x4 a, f16x4& hi, f16x4& lo) {
+    hi = to_f16x4(a);
+    const f32x4 r{a[0] - (float)hi[0], a[1] - (float)hi[1], a[2] - (float)hi[2], a[3] - (float)hi[3]};
+    lo = to_f16x4(r);
+}
+__device__ __forceinline__ void split_h8(const float* x, f16x8& hi, f16x8& lo) {
+    f16x4 h0, l0, h1, l1;
+    split_h4(f32x4{x[0], x[1], x[2], x[3]}, h0, l0);
+    split_h4(f32x4{x[4], x[5], x[6], x[7]}, h1, l1);
+    hi = f16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    lo = f16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+}
+
 // Fragment of an f32x4 accumulator pair as an operand with the accumulator-compatible contraction
 // order (element e < 4 from `a`, e >= 4 from `b`).
 __device__ __forceinline__ bf16x8 acc_pair(f32x4 a, f32x4 b) {
@@ -145,32 +193,32 @@ __device__ __forceinline__ void acc_pair_split(f32x4 a, f32x4 b, bf16x8& hi, bf1
     const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     split8(x, hi, lo);
 }
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 a) {
-    return __builtin_bit_cast(bf16x4, uint2{cvt_pk(a[0], a[1]), cvt_pk(a[2], a[3])});
-}
-__device__ __forceinline__ void split4(f32x4 a, bf16x4& hi, bf16x4& lo) {
-    const float x[8] = {a[0], a[1], a[2], a[3], 0.f, 0.f, 0.f, 0.f};
-    bf16x8 h, l;
-    split8(x, h, l);
-    hi = bf16x4{h[0], h[1], h[2], h[3]};
-    lo = bf16x4{l[0], l[1], l[2], l[3]};
+__device__ __forceinline__ f16x8 acc_pair_h(f32x4 a, f32x4 b) {
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return to_f16x8(x);
 }
 
-// 16x16x16 product, single bf16 operands: lane (i16, g4) supplies row (A) / column (B) i16 at
-// contraction positions 4 g4 .. 4 g4 + 3; the result is laid out as for mma().
-__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+// 16x16x16 product on fp32 operands with the fp32 MFMA (four v_mfma_f32_16x16x4_f32): `xr` is
+// the row form of X (lane (i16, g4) holds X[i16][4 g4 + e]), `yc` the column form of Y (lane
+// (j16, g4) holds Y[4 g4 + e][j16]); MFMA e contracts over the positions 4 g4 + e, and the
+// result is the column form of X Y.
+__device__ __forceinline__ f32x4 mm16(f32x4 xr, f32x4 yc, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[0], yc[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[1], yc[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[2], yc[2], c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(xr[3], yc[3], c, 0, 0, 0);
 }
 
-// The same product on fp32 operands carried as hi + lo bf16 pairs (hi*hi + lo*hi + hi*lo).
-__device__ __forceinline__ f32x4 mma16x(f32x4 a, f32x4 b) {
-    bf16x4 ah, al, bh, bl;
-    split4(a, ah, al);
-    split4(b, bh, bl);
-    f32x4 c = mma16(ah, bh, zero4());
-    c = mma16(al, bh, c);
-    return mma16(ah, bl, c);
+// hi*hi + lo*hi + hi*lo on float16 pairs
+__device__ __forceinline__ f32x4 mma_h3(f16x8 ah, f16x8 al, f16x8 bh, f16x8 bl, f32x4 c) {
+    c = mma_h(ah, bh, c);
+    c = mma_h(al, bh, c);
+    return mma_h(ah, bl, c);
+}
+__device__ __forceinline__ f32x4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+    c = mma(ah, bh, c);
+    c = mma(al, bh, c);
+    return mma(ah, bl, c);
 }
 
 // Storage order of every 32-long contraction index in LDS: position pm(c) puts the elements one
@@ -210,6 +258,7 @@ __device__ __forceinline__ void pin(uint32_t& u) { asm volatile("" : "+v"(u)); }
 // instead of each right before its first use.
 __device__ __forceinline__ void pin(f32x4& u) { asm volatile("" : "+v"(u)); }
 __device__ __forceinline__ void pin(bf16x8& u) { asm volatile("" : "+v"(u)); }
+__device__ __forceinline__ void pin(f16x8& u) { asm volatile("" : "+v"(u)); }
 
 // Keeps the compiler from moving LDS accesses across this point; the hardware executes one
 // wave's LDS instructions in order, so lanes of a wave then see each other's earlier writes.
@@ -259,16 +308,17 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t&
 }
 
 // ==================================== producer waves =========================================
-// Wave p owns key channels [32 p, 32 p + 32) (none when p >= DK / 32).  Per chunk: the decayed
-// operands and the partial Gram tiles (interval 1); Q~, K~, K_end^T and gamma (interval 2).
-template <int DK, bool F32IN, bool GATE, bool PREC>
+// Wave p owns key channels [32 p, 32 p + 32) (none when p >= DK / 32).  Iteration it: the decayed
+// operands and the partial Gram tiles of chunk it (interval 1); the rows of W over the wave's
+// channels and a row tile of M for chunk it - 1, then Q~, K~, gamma and K_end of chunk it
+// (interval 2).
+template <int DK, bool F32IN, bool GATE>
 __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p, int lane,
                                          int64_t row0, int64_t len, int h) {
-    using Lay = Layout<DK, F32IN, PREC>;
+    using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
-    constexpr bool kFull = Lay::kFull;
     constexpr int RB = Lay::RB, TB = Lay::TB;
-    auto bfp = [&](int off) { return reinterpret_cast<bf16*>(smem + off); };
+    auto hp = [&](int off) { return reinterpret_cast<f16*>(smem + off); };
     auto f32p = [&](int off) { return reinterpret_cast<float*>(smem + off); };
     const int i16 = lane & 15, g4 = lane >> 4;
     const bool intra = p < Lay::NCB;
@@ -293,11 +343,11 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
     }
 
     // identity blocks: B operand selecting channel half hh of a 32-long contraction step
-    bf16x8 Id[2];
+    f16x8 Id[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Id[hh][e] = f2bf((8 * g4 + e == 16 * hh + i16) ? 1.f : 0.f);
+        for (int e = 0; e < 8; ++e) Id[hh][e] = (f16)((8 * g4 + e == 16 * hh + i16) ? 1.f : 0.f);
 
     // prefetch registers (one chunk ahead): token 16 t + i16 of tile t
     Raw8<F32IN> pq[2], pk[2], pz[2];
@@ -343,16 +393,25 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
         }
     };
 
+    // K_end of the last chunk as B operands (channel half hh, plane hi / lo), kept for one
+    // iteration until M and W of that chunk are formed
+    f16x8 Ke[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) Ke[hh][pl] = f16x8{};
+
     const int64_t nchunks = (len + kC - 1) / kC;
     if (intra && nchunks > 0) {
         prefetch(0);
         if constexpr (GATE) gate_map(0);
     }
 
-    for (int64_t it = 0; it <= nchunks; ++it) {
+    for (int64_t it = 0; it <= nchunks + 1; ++it) {
         const bool work = intra && it < nchunks;   // wave-uniform
+        const int buf = (int)(it & 1);
         float F0[8], F1[8], Qs1[8], Kr[2][8], Kd1[8], Kc[8];
-        bf16x8 Qh0, Ql0;
+        f16x8 Qt0;
 
         // ---- interval 1: decay prefix, decayed operands, partial Gram tiles
         if (work) {
@@ -384,7 +443,7 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                 for (int t = 0; t < 2; ++t) {
                     pin(pb[t]);
                     if (g4 == 0)
-                        f32p(Lay::o_beta)[16 * t + i16] =
+                        f32p(Lay::o_beta)[buf * kC + 16 * t + i16] =
                             F32IN ? __builtin_bit_cast(float, pb[t]) : __builtin_bit_cast(float, pb[t] << 16);
                 }
             }
@@ -420,87 +479,107 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                 Kc[e] = Kd0[e] * F0[e];                  // tile 0 seen from tile 1
                 Qs1[e] = Qs[1][e];
             }
-            bf16x8 Qh1, Ql1, Krh[2], Kdh[2], Kdl[2], Kch, Kcl;
-            split8(Qs[0], Qh0, Ql0);
-            split8(Qs[1], Qh1, Ql1);
-            Krh[0] = to_bf16x8(Kr[0]);
-            Krh[1] = to_bf16x8(Kr[1]);
+            Qt0 = to_f16x8(Qs[0]);
+            bf16x8 Qh[2], Ql[2], Krh[2], Krl[2], Kdh[2], Kdl[2], Kch, Kcl;
+            split8(Qs[0], Qh[0], Ql[0]);
+            split8(Qs[1], Qh[1], Ql[1]);
+            split8(Kr[0], Krh[0], Krl[0]);
+            split8(Kr[1], Krh[1], Krl[1]);
             split8(Kd0, Kdh[0], Kdl[0]);
             split8(Kd1, Kdh[1], Kdl[1]);
             split8(Kc, Kch, Kcl);
             // Gram tiles transposed (column side as the A operand): the accumulator of lane
             // (row r = i16, g4) holds A[r][16 b + 4 g4 + j].  m: 0 qk00, 1 qk11, 2 qk10,
-            // 3 kk00, 4 kk11, 5 kk10.  A_qk with split operands (3 products); A_kk feeds only the
-            // triangular inverse, where single bf16 operands cost no measurable accuracy.
+            // 3 kk00, 4 kk11, 5 kk10; every tile on split operands (3 products).
 #pragma unroll
             for (int m = 0; m < 6; ++m) {
                 const int ta = (m % 3 == 0) ? 0 : 1;
                 const bf16x8 ch = (m % 3 == 2) ? Kch : Kdh[ta];
                 const bf16x8 cl = (m % 3 == 2) ? Kcl : Kdl[ta];
-                f32x4 acc;
-                if (m < 3) {
-                    const bf16x8 rh = ta ? Qh1 : Qh0, rl = ta ? Ql1 : Ql0;
-                    acc = mma(ch, rh, zero4());
-                    acc = mma(cl, rh, acc);
-                    acc = mma(ch, rl, acc);
-                } else {
-                    acc = mma(ch, Krh[ta], zero4());
-                }
+                const bf16x8 rh = m < 3 ? Qh[ta] : Krh[ta];
+                const bf16x8 rl = m < 3 ? Ql[ta] : Krl[ta];
+                const f32x4 acc = mma3(ch, cl, rh, rl, zero4());
                 st<f32x4>(smem + Lay::o_Gp + ((p * 6 + m) * 64 + lane) * 16, acc);
             }
         }
         __syncthreads();
 
-        // ---- interval 2: Q~ (split), K~ and K_end^T to LDS, and the decay of the chunk
+        // ---- interval 2: M and W of chunk it - 1 (formed from the K_end fragments held since
+        // interval 2 of the previous iteration and T_b, A_qk from LDS), then Q~, K~, gamma and the
+        // K_end fragments of chunk it.
+        if (it >= 1 && it <= nchunks) {
+            // W = K_end^T T_b and M = A_qk T_b on float16 pairs, formed transposed:
+            // D[i][x] = sum_j T_b[j][i] X[x][j], whose accumulator (lane (column x, g4) holding
+            // tokens i = 4 g4 + j) is the row fragment of W or M.
+            const int tbuf = (int)((it - 1) & 1);
+            f16x8 tA[2][2];   // rows of T_b^T for token tiles 0, 1, planes hi, lo
+#pragma unroll
+            for (int ai = 0; ai < 2; ++ai)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+                    tA[ai][pl] = ld<f16x8>(hp(Lay::o_Tb + (2 * tbuf + pl) * Lay::CPL) + (16 * ai + i16) * TB + 8 * g4);
+            if (intra) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const f32x4 d0 = mma_h3(tA[0][0], tA[0][1], Ke[hh][0], Ke[hh][1], zero4());
+                    const f32x4 d1 = mma_h3(tA[1][0], tA[1][1], Ke[hh][0], Ke[hh][1], zero4());
+                    st<f16x8>(hp(Lay::o_W) + (32 * p + 16 * hh + i16) * TB + 8 * g4, acc_pair_h(d0, d1));
+                }
+            }
+            // M: row tile 0 by producer wave 2, row tile 1 by producer wave 3
+            const int b = p - (kNW - 2);
+            if (b >= 0) {
+                const f16x8 ah = ld<f16x8>(hp(Lay::o_Aq + (2 * tbuf) * Lay::CPL) + (16 * b + i16) * TB + 8 * g4);
+                const f16x8 al = ld<f16x8>(hp(Lay::o_Aq + (2 * tbuf + 1) * Lay::CPL) + (16 * b + i16) * TB + 8 * g4);
+                const f32x4 d0 = mma_h3(tA[0][0], tA[0][1], ah, al, zero4());
+                const f32x4 d1 = b ? mma_h3(tA[1][0], tA[1][1], ah, al, zero4()) : zero4();
+                st<f16x8>(hp(Lay::o_M) + (16 * b + i16) * TB + 8 * g4, acc_pair_h(d0, d1));
+            }
+        }
         if (work) {
+            char* qk = smem + Lay::o_QK + buf * Lay::QKB;
             if (i16 == 0) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) f32p(Lay::o_gam)[ch0 + e] = F0[e] * F1[e];
+                for (int e = 0; e < 8; ++e) reinterpret_cast<float*>(qk + 2 * kC * RB * 2)[ch0 + e] = F0[e] * F1[e];
             }
             // 8 channels of token 16 t + i16 into [token][pm(channel)] storage
-            auto put_row = [&](int off, int t, bf16x8 v) {
-                bf16* d = bfp(off) + (16 * t + i16) * RB + 32 * p;
-                st<bf16x4>(d + pm(8 * g4), bf16x4{v[0], v[1], v[2], v[3]});
-                st<bf16x4>(d + pm(8 * g4 + 4), bf16x4{v[4], v[5], v[6], v[7]});
+            auto put_row = [&](char* base, int t, f16x8 v) {
+                f16* d = reinterpret_cast<f16*>(base) + (16 * t + i16) * RB + 32 * p;
+                st<f16x4>(d + pm(8 * g4), f16x4{v[0], v[1], v[2], v[3]});
+                st<f16x4>(d + pm(8 * g4 + 4), f16x4{v[4], v[5], v[6], v[7]});
             };
             // Q~ = Q exp(G), K~ = K exp(G) from the chunk start; tile 1 carries the tile-0 decay
+            {
+                float x[8], y[8];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x8 hh = Qh0, ll = Ql0;
-                float xt[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xt[e] = t ? Kr[1][e] * F0[e] : Kr[0][e];
-                if (t == 1) {
-                    float x[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = Qs1[e] * F0[e];
-                    split8(x, hh, ll);
+                for (int e = 0; e < 8; ++e) {
+                    x[e] = Qs1[e] * F0[e];
+                    y[e] = Kr[1][e] * F0[e];
                 }
-                put_row(Lay::o_Qt, t, hh);
-                put_row(Lay::o_Qt + kC * RB * 2, t, ll);
-                if constexpr (kFull) {
-                    bf16x8 th, tl;
-                    split8(xt, th, tl);
-                    put_row(Lay::o_Kt, t, th);
-                    put_row(Lay::o_Kt + kC * RB * 2, t, tl);
-                } else {
-                    put_row(Lay::o_Kt, t, to_bf16x8(xt));
-                }
+                put_row(qk, 0, Qt0);
+                put_row(qk, 1, to_f16x8(x));
+                put_row(qk + kC * RB * 2, 0, to_f16x8(Kr[0]));
+                put_row(qk + kC * RB * 2, 1, to_f16x8(y));
             }
-            // K_end = K exp(G_last - G), transposed through the identity: the accumulator of lane
-            // (channel i16 of half hh, g4) holds tokens 16 t + 4 g4 + j.
+            // K_end = K exp(G_last - G), split and transposed through the identity: lane (channel
+            // i16 of half hh, g4) gets tokens 16 t + 4 g4 + j of tile t, i.e. the B operand of a
+            // contraction over the chunk's tokens in pm order
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 float xe[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) xe[e] = t ? Kd1[e] * F1[e] : Kc[e] * F1[e];
-                bf16x8 eh, el;
-                split8(xe, eh, el);
+                f16x8 eh, el;
+                split_h8(xe, eh, el);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    bf16* dst = bfp(Lay::o_Ke) + (32 * p + 16 * hh + i16) * TB + pm(16 * t + 4 * g4);
-                    st<bf16x4>(dst, to_bf16x4(mma(eh, Id[hh], zero4())));          // exact: bf16 in
-                    st<bf16x4>(dst + DK * TB, to_bf16x4(mma(el, Id[hh], zero4())));
+                    const f16x4 vh = to_f16x4(mma_h(eh, Id[hh], zero4()));   // exact: f16 in
+                    const f16x4 vl = to_f16x4(mma_h(el, Id[hh], zero4()));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        Ke[hh][0][4 * t + j] = vh[j];
+                        Ke[hh][1][4 * t + j] = vl[j];
+                    }
                 }
             }
             if constexpr (GATE) {
@@ -513,19 +592,20 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 
 // ==================================== consumer waves =========================================
 // Wave 4 + cw owns value columns [16 cw, 16 cw + 16) of the slice and its dk x 16 state slice.
-// Interval 1 of iteration i: the inter-chunk step of chunk i - 1.  Interval 2: chunk i's T_b
-// (cw = 0) or one A_qk tile (cw = 1..3).
-template <int DK, bool F32IN, bool OUT_F32, bool PREC>
+// Iteration it: the state step of chunk it - 2 (interval 1; wave 2 also completes T_b of chunk
+// it - 1 with its off-diagonal block); for chunk it the diagonal blocks of the UT transform
+// (cw = 0, 1), beta N10 and the A_qk tiles (cw = 2, 3), and the scale of the value path for
+// chunk it - 1 (interval 2).
+template <int DK, bool F32IN, bool OUT_F32>
 __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
                                          int64_t row0, int64_t len, int n, int h, int slice, int seg) {
-    using Lay = Layout<DK, F32IN, PREC>;
+    using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
-    constexpr bool kFull = Lay::kFull;
     constexpr int KS = DK / 32;          // 32-channel contraction steps
     constexpr int CT = DK / 16;          // 16-channel tiles of the state
     constexpr int NCB = Lay::NCB;
     constexpr int RB = Lay::RB, TB = Lay::TB, SB = Lay::SB;
-    auto bfp = [&](int off) { return reinterpret_cast<bf16*>(smem + off); };
+    auto hp = [&](int off) { return reinterpret_cast<f16*>(smem + off); };
     auto f32p = [&](int off) { return reinterpret_cast<float*>(smem + off); };
     const int i16 = lane & 15, g4 = lane >> 4;
     const int H = a.H;
@@ -548,7 +628,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
             off_o[t][j] = (uint32_t)(((16 * t + 4 * g4 + j) * sv + i16) * sizeof(OT));
     }
 
-    // ---- state slice in accumulators: Sacc[ct][j] = S[16 ct + 4 g4 + j][col0 + i16]
+    // ---- state slice in accumulators: Sacc[ct][j] = S[16 ct + 4 g4 + j][col0 + i16] 2^-esc
     f32x4 Sacc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();
@@ -589,9 +669,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                     const f32x4 m1 = ld<f32x4>(Mr + 32 * s2 + 16 + 4 * g4);
                     bf16x8 mh, ml;
                     acc_pair_split(m0, m1, mh, ml);
-                    acc = mma(mh, Sh[s2], acc);
-                    acc = mma(ml, Sh[s2], acc);
-                    acc = mma(mh, Sl[s2], acc);
+                    acc = mma3(mh, ml, Sh[s2], Sl[s2], acc);
                 }
                 Sacc[ct] = acc;
             }
@@ -604,391 +682,358 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
             for (int j = 0; j < 4; ++j)
                 Sacc[ct][j] = S0[(size_t)(16 * ct + 4 * g4 + j) * a.dv + col0 + i16];
     }
+    // power-of-two scale of the value path: Sacc = S 2^-esc, V enters as V 2^-esc
+    int esc = 0;
+    float vsc = 1.f, osc = a.scale;
 
-    // the upper-right 16x16 blocks of T_b and A_qk are zero for every chunk
+    // blocks that are zero for every chunk (both buffers): rows 16..31 x columns 0..15 of T_b^T
+    // (T_b is lower triangular) and rows 0..15 x columns 16..31 of A_qk
     if (cw == 1) {
-        const bf16x4 z{f2bf(0.f), f2bf(0.f), f2bf(0.f), f2bf(0.f)};
-        bf16* ad = bfp(Lay::o_Aq) + i16 * TB + pm(16 + 4 * g4);
-        st<bf16x4>(ad, z);
-        st<bf16x4>(ad + kC * TB, z);
-        bf16* td = bfp(Lay::o_Tb) + i16 * TB + pm(16 + 4 * g4);
+        const f16x4 z{(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
 #pragma unroll
-        for (int pl = 0; pl < Lay::kTP; ++pl) st<bf16x4>(td + pl * kC * TB, z);
+        for (int pl = 0; pl < 4; ++pl) {
+            st<f16x4>(hp(Lay::o_Aq + pl * Lay::CPL) + i16 * TB + pm(16 + 4 * g4), z);
+            st<f16x4>(hp(Lay::o_Tb + pl * Lay::CPL) + (16 + i16) * TB + pm(4 * g4), z);
+        }
     }
 
     bf16x8 Id0;   // identity block: B operand selecting columns 0..15 of a 32-long step
 #pragma unroll
     for (int e = 0; e < 8; ++e) Id0[e] = f2bf((8 * g4 + e == i16) ? 1.f : 0.f);
 
-    Raw8<F32IN> pv[2];
-    auto prefetch_v = [&](int64_t c0) {
+    // v fetched two chunks ahead: pa holds the chunk of the next state step, pb the one after;
+    // the sets rotate after each step (named registers: an indexed pair would live in scratch)
+    const IT* vhc = vh;   // rows of the next chunk to fetch
+    OT* obc = ob;         // rows of the next chunk to write
+    Raw8<F32IN> pa[2], pb[2];
+    auto prefetch_v = [&](Raw8<F32IN>* pv, int64_t c0) {
         const uint32_t nv = (uint32_t)((len - c0) < kC ? (len - c0) : kC);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (size_t)c0 * sv, nv * (uint32_t)(sv * sizeof(IT)));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vhc, nv * (uint32_t)(sv * sizeof(IT)));
+        vhc += (size_t)kC * sv;
 #pragma unroll
         for (int t = 0; t < 2; ++t) pv[t].load(rv, off_v[t]);
     };
     auto reduce = [&](int m) -> f32x4 {   // sum of the producers' partial Gram tiles
-        f32x4 acc = ld<f32x4>(smem + Lay::o_Gp + (m * 64 + lane) * 16);
+        const char* base = smem + Lay::o_Gp;
+        f32x4 acc = ld<f32x4>(base + (m * 64 + lane) * 16);
 #pragma unroll
-        for (int w = 1; w < NCB; ++w) acc += ld<f32x4>(smem + Lay::o_Gp + ((w * 6 + m) * 64 + lane) * 16);
+        for (int w = 1; w < NCB; ++w) acc += ld<f32x4>(base + ((w * 6 + m) * 64 + lane) * 16);
         return acc;
     };
-    auto put_tb = [&](int r, int c, float v) {   // T_b[r][c] (one or two bf16 planes)
-        bf16* Tb = bfp(Lay::o_Tb);
-        if constexpr (Lay::kTP == 2) {
-            bf16 hh, ll;
-            split_bf16(v, hh, ll);
-            Tb[r * TB + pm(c)] = hh;
-            Tb[kC * TB + r * TB + pm(c)] = ll;
-        } else {
-            Tb[r * TB + pm(c)] = f2bf(v);
-        }
+    auto frag = [&](int off, int row, int stride) -> f16x8 {   // 8 contraction positions of a row
+        return ld<f16x8>(hp(off) + row * stride + 8 * g4);
     };
 
     const int64_t nchunks = (len + kC - 1) / kC;
-    if (nchunks > 0) prefetch_v(0);
+    if (nchunks > 0) prefetch_v(pa, 0);
+    if (nchunks > 1) prefetch_v(pb, kC);
 
-    for (int64_t it = 0; it <= nchunks; ++it) {
-        // ---- interval 1: inter-chunk step of chunk it - 1 on this wave's 16 state columns.
-        // LDS operands come in three batches, each issued ahead of independent work and pinned
-        // at its first use (without this each MFMA waits for its own read).
-        if (it > 0) {
-            const int64_t c0 = (it - 1) * kC;
+    for (int64_t it = 0; it <= nchunks + 1; ++it) {
+        // ---- interval 1: state step of chunk it - 2 on this wave's 16 state columns.
+        if (it >= 2) {
+            const int64_t c = it - 2, c0 = c * kC;
+            const char* qk = smem + Lay::o_QK + (int)(c & 1) * Lay::QKB;
             const uint32_t nvalid = a.mode == 1 ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
             // output rows of the chunk: stores at or past row nvalid fall outside the resource
             // (summaries write no outputs)
-            const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob + (size_t)c0 * sv, nvalid * (uint32_t)(sv * sizeof(OT)));
-            // operand fragments read from [row][pm(index)] storage: elements 4 g4 + e (e < 4) and
-            // 16 + 4 g4 + e - 4 (e >= 4) of each 32-long contraction step are one 16-byte read
-            auto frag = [&](int off, int row, int stride, int col) -> bf16x8 {
-                return ld<bf16x8>(bfp(off) + row * stride + col + 8 * g4);
-            };
-            // batch 1: rows of K~ (for K~ S) and of T_b
-            constexpr int kPL = Lay::kTP > Lay::kNP ? Lay::kTP : Lay::kNP;
-            bf16x8 tbr[2][Lay::kTP], kt[2][KS][Lay::kNP];
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(obc, nvalid * (uint32_t)(sv * sizeof(OT)));
+            obc += (size_t)kC * sv;
+            // batch 1: rows of K~, Q~ and M
+            f16x8 kt[2][KS], qr[2][KS], mr[2];
 #pragma unroll
-            for (int ta = 0; ta < 2; ++ta)
+            for (int ta = 0; ta < 2; ++ta) {
 #pragma unroll
-                for (int pl = 0; pl < kPL; ++pl) {
-                    if (pl < Lay::kTP) tbr[ta][pl] = frag(Lay::o_Tb + pl * kC * TB * 2, 16 * ta + i16, TB, 0);
-                    if (pl < Lay::kNP)
-#pragma unroll
-                        for (int s = 0; s < KS; ++s) kt[ta][s][pl] = frag(Lay::o_Kt + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
+                for (int s = 0; s < KS; ++s) {
+                    kt[ta][s] = ld<f16x8>(reinterpret_cast<const f16*>(qk + kC * RB * 2) + (16 * ta + i16) * RB + 32 * s + 8 * g4);
+                    qr[ta][s] = ld<f16x8>(reinterpret_cast<const f16*>(qk) + (16 * ta + i16) * RB + 32 * s + 8 * g4);
                 }
+                mr[ta] = frag(Lay::o_M, 16 * ta + i16, TB);
+            }
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) pv[t].pin_all();
-            Raw8<F32IN> vr[2] = {pv[0], pv[1]};
-            if (it < nchunks) prefetch_v(it * kC);
-
             // V: token-per-lane -> column-per-lane through a product with the identity; the
             // accumulator of lane (column i16, g4) holds tokens 16 t + 4 g4 + j
             f32x4 Vf[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                if constexpr (kFull) {
+                pa[t].pin_all();
+                if constexpr (F32IN) {
                     float vv[8];
-                    vr[t].to_f32(vv);
+                    pa[t].to_f32(vv);
                     bf16x8 vh, vl;
                     split8(vv, vh, vl);
                     Vf[t] = mma(vl, Id0, mma(vh, Id0, zero4()));
                 } else {
-                    Vf[t] = mma(__builtin_bit_cast(bf16x8, vr[t].p[0]), Id0, zero4());   // bf16 as stored
+                    Vf[t] = mma(__builtin_bit_cast(bf16x8, pa[t].p[0]), Id0, zero4());   // bf16 as stored
                 }
             }
+            // rotate: the next chunk's v (fetched one step ago) moves up, the one after is fetched
+#pragma unroll
+            for (int t = 0; t < 2; ++t) pa[t] = pb[t];
+            if (c + 2 < nchunks) prefetch_v(pb, (c + 2) * kC);
             // state as B operand: contraction index (32-channel step s, g4, e) ->
             // channel 32 s + 4 g4 + e (e < 4), 32 s + 16 + 4 g4 + (e - 4) (e >= 4)
-            bf16x8 Sh[KS], Sl[KS];
+            f16x8 Sh[KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) acc_pair_split(Sacc[2 * s], Sacc[2 * s + 1], Sh[s], Sl[s]);
-#pragma unroll
-            for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-                for (int pl = 0; pl < kPL; ++pl) {
-                    if (pl < Lay::kTP) pin(tbr[ta][pl]);
-                    if (pl < Lay::kNP)
-#pragma unroll
-                        for (int s = 0; s < KS; ++s) pin(kt[ta][s][pl]);
-                }
-            // batch 2: rows of Q~ (hi, lo) and of A_qk (hi, lo)
-            bf16x8 qr[2][KS][2], ar[2][2];
-#pragma unroll
-            for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-                for (int pl = 0; pl < 2; ++pl) {
-                    ar[ta][pl] = frag(Lay::o_Aq + pl * kC * TB * 2, 16 * ta + i16, TB, 0);
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) qr[ta][s][pl] = frag(Lay::o_Qt + pl * kC * RB * 2, 16 * ta + i16, RB, 32 * s);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            // V~ = T_b (V - K~ S): the residual R = V - K~ S in fp32, then one product with T_b
-            // (R split, so only T_b's own planes are rounded)
-            f32x4 Vt[2];
-            {
-                f32x4 R[2];
-#pragma unroll
-                for (int ta = 0; ta < 2; ++ta) {
-                    f32x4 acc = zero4();
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) {
-                        acc = mma(kt[ta][s][0], Sh[s], acc);
-                        if constexpr (kFull) {
-                            acc = mma(kt[ta][s][1], Sh[s], acc);
-                            acc = mma(kt[ta][s][0], Sl[s], acc);
-                        }
-                    }
-                    R[ta] = Vf[ta] - acc;
-                }
-                bf16x8 Rh, Rl;   // R as B operand: token index (g4, e) as for V~ below
-                acc_pair_split(R[0], R[1], Rh, Rl);
-#pragma unroll
-                for (int ta = 0; ta < 2; ++ta) {
-                    f32x4 v = mma(tbr[ta][0], Rh, zero4());
-                    v = mma(tbr[ta][0], Rl, v);
-                    if constexpr (Lay::kTP == 2) v = mma(tbr[ta][1], Rh, v);
-                    Vt[ta] = v;
-                }
-            }
-            // V~ as B operand: token index (g4, e) -> 4 g4 + e (e < 4), 16 + 4 g4 + (e - 4)
-            bf16x8 Vh, Vl;
-            acc_pair_split(Vt[0], Vt[1], Vh, Vl);
-#pragma unroll
-            for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-                for (int pl = 0; pl < 2; ++pl) {
-                    pin(ar[ta][pl]);
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) pin(qr[ta][s][pl]);
-                }
-            // outputs O = Q~ S + A_qk V~
-            f32x4 Oacc[2];
+            for (int s = 0; s < KS; ++s) Sh[s] = acc_pair_h(Sacc[2 * s], Sacc[2 * s + 1]);
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta) {
-                f32x4 acc = zero4();
+                pin(mr[ta]);
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    acc = mma(qr[ta][s][0], Sh[s], acc);
-                    acc = mma(qr[ta][s][1], Sh[s], acc);
-                    acc = mma(qr[ta][s][0], Sl[s], acc);
+                    pin(kt[ta][s]);
+                    pin(qr[ta][s]);
                 }
-                Oacc[ta] = acc;
             }
-            // batch 3, in two halves (registers): rows of K_end^T (hi, lo) and the chunk decay
-            // gamma for state tiles [0, CT/2), then [CT/2, CT)
+            // K~ S and Q~ S, four independent chains
+            f32x4 KSa[2] = {zero4(), zero4()}, QSa[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                KSa[0] = mma_h(kt[0][s], Sh[s], KSa[0]);
+                KSa[1] = mma_h(kt[1][s], Sh[s], KSa[1]);
+                QSa[0] = mma_h(qr[0][s], Sh[s], QSa[0]);
+                QSa[1] = mma_h(qr[1][s], Sh[s], QSa[1]);
+            }
+            // batch 2, in two halves (registers): rows of W and the chunk decay gamma for state
+            // tiles [0, CT/2), then [CT/2, CT)
             constexpr int CH = CT / 2;
-            bf16x8 kr[CH][2];
+            f16x8 wr[CH];
             f32x4 gm[CH];
             auto load_half = [&](int c0h) {
 #pragma unroll
-                for (int c = 0; c < CH; ++c) {
-#pragma unroll
-                    for (int pl = 0; pl < 2; ++pl) kr[c][pl] = frag(Lay::o_Ke + pl * DK * TB * 2, 16 * (c0h + c) + i16, TB, 0);
-                    gm[c] = ld<f32x4>(f32p(Lay::o_gam) + 16 * (c0h + c) + 4 * g4);
-                }
-            };
-            // state: S <- Diag(gamma_last) S + K_end^T V~ on tiles [c0h, c0h + CH)
-            auto update_half = [&](int c0h) {
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    pin(kr[c][0]);
-                    pin(kr[c][1]);
-                    pin(gm[c]);
-                }
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    f32x4 st = Sacc[c0h + c] * gm[c];
-                    st = mma(kr[c][0], Vh, st);
-                    st = mma(kr[c][0], Vl, st);
-                    st = mma(kr[c][1], Vh, st);
-                    Sacc[c0h + c] = st;
+                for (int cc = 0; cc < CH; ++cc) {
+                    wr[cc] = frag(Lay::o_W, 16 * (c0h + cc) + i16, TB);
+                    gm[cc] = ld<f32x4>(reinterpret_cast<const float*>(qk + 2 * kC * RB * 2) + 16 * (c0h + cc) + 4 * g4);
                 }
             };
             load_half(0);
             __builtin_amdgcn_sched_barrier(0);
+            // R = V 2^-esc - K~ S, as the B operand of M R and W R
+            f32x4 R[2];
+#pragma unroll
+            for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) R[ta][j] = __builtin_fmaf(Vf[ta][j], vsc, -KSa[ta][j]);
+            const f16x8 Rh = acc_pair_h(R[0], R[1]);
+            // outputs O = Q~ S + M R
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta) {
-                f32x4 acc = Oacc[ta];
-                acc = mma(ar[ta][0], Vh, acc);
-                acc = mma(ar[ta][1], Vh, acc);
-                acc = mma(ar[ta][0], Vl, acc);
+                const f32x4 acc = mma_h(mr[ta], Rh, QSa[ta]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if constexpr (OUT_F32)
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, a.scale * acc[j]), ro,
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, osc * acc[j]), ro,
                                                               off_o[ta][j], 0, 0);
                     else
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, f2bf(a.scale * acc[j])), ro,
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, f2bf(osc * acc[j])), ro,
                                                               off_o[ta][j], 0, 0);
                 }
             }
+            // state: S <- Diag(gamma_last) S + W R on tiles [c0h, c0h + CH)
+            auto update_half = [&](int c0h) {
+#pragma unroll
+                for (int cc = 0; cc < CH; ++cc) {
+                    pin(wr[cc]);
+                    pin(gm[cc]);
+                }
+#pragma unroll
+                for (int cc = 0; cc < CH; ++cc) Sacc[c0h + cc] = mma_h(wr[cc], Rh, Sacc[c0h + cc] * gm[cc]);
+            };
             update_half(0);
             load_half(CH);
             update_half(CH);
             // state checkpoint after every ckpt_every full chunks (prefix states for reuse)
-            if (a.ckpt && it % a.ckpt_every == 0 && it * kC <= len) {
-                const int64_t j = it / a.ckpt_every - 1;
+            const int64_t done = c + 1;   // chunks folded into the state
+            if (a.ckpt && done % a.ckpt_every == 0 && done * kC <= len) {
+                const int64_t j = done / a.ckpt_every - 1;
                 if (j < a.ckpt_cap) {
-                    float* C = a.ckpt + (((size_t)n * H + h) * a.ckpt_cap + j) * DK * a.dv;
+                    float* Cp = a.ckpt + (((size_t)n * H + h) * a.ckpt_cap + j) * DK * a.dv;
                     // 32-bit lane offset, opaque so that the 32 store addresses are formed here
                     // rather than hoisted out of the chunk loop into registers
                     int lo = 4 * g4 * a.dv + col0 + i16;
                     asm volatile("" : "+v"(lo));
+                    const float un = __builtin_ldexpf(1.f, esc);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) C[lo + (16 * ct + jj) * a.dv] = Sacc[ct][jj];
+                        for (int jj = 0; jj < 4; ++jj) Cp[lo + (16 * ct + jj) * a.dv] = Sacc[ct][jj] * un;
                 }
             }
         }
+        // ---- interval 1, wave 2: T10 = -T11 (beta N10) T00 of chunk it - 1 (column form, times
+        // beta of its columns) completes T_b^T in the buffer of that chunk
+        if (cw == 2 && it >= 1 && it <= nchunks) {
+            const int tb = (int)((it - 1) & 1);
+            const float* pub = f32p(Lay::o_Pub);
+            const f32x4 T00c = ld<f32x4>(pub + i16 * 20 + 4 * g4);
+            const f32x4 T11r = ld<f32x4>(pub + SB + i16 * 20 + 4 * g4);
+            const f32x4 N10r = ld<f32x4>(pub + 2 * SB + i16 * 20 + 4 * g4);
+            const float b0 = f32p(Lay::o_beta)[tb * kC + i16];
+            const f32x4 T10c = mm16(T11r, mm16(N10r, T00c, zero4()), zero4()) * (-b0);
+            f16x4 hv, lv;
+            split_h4(T10c, hv, lv);
+            f16* t = hp(Lay::o_Tb + 2 * tb * Lay::CPL) + i16 * TB + pm(16 + 4 * g4);
+            st<f16x4>(t, hv);
+            st<f16x4>(t + Lay::CPL / 2, lv);
+        }
         __syncthreads();
 
-        // ---- interval 2: the UT solve (cw = 0) and the A_qk tiles (cw = 1..3) of chunk it
+        // ---- interval 2, chunk it: diagonal blocks of the UT transform (cw = 0: T00, cw = 1:
+        // T11), beta N10 and the A_qk tiles (cw = 2, 3), from the Gram tiles of interval 1
         if (it < nchunks) {
-            if (cw == 0) {
-                // T = (I + N)^-1, N = A_kk with rows scaled by beta (strictly lower, 32 x 32).
-                // Each diagonal 16x16 block B = L0 + L1 + L2 (L0: inside the 4x4 diagonal
-                // blocks; L1: the 4x4 blocks just below them within each 8x8 diagonal block; L2:
-                // the lower-left 8x8 block) is inverted by block elimination,
-                //     D = (I + L0)^-1 (closed form, fp32),  E = D - D L1 D,  X = E - E L2 E,
+            const int tb = (int)(it & 1);
+            const float* bet = f32p(Lay::o_beta) + tb * kC;
+            float* pub = f32p(Lay::o_Pub);   // [0] T00 (column form rows), [1] T11 (rows), [2] beta N10 (rows)
+            if (cw < 2) {
+                // T_qq = (I + N_qq)^-1 for the diagonal 16x16 block q of N = Diag(beta) A_kk
+                // (strictly lower) by block elimination: B = L0 + L1 + L2 (L0: inside the 4x4
+                // diagonal blocks; L1: the 4x4 blocks just below them within each 8x8 diagonal
+                // block; L2: the lower-left 8x8 block),
+                //     D = (I + L0)^-1 (closed form),  E = D - D L1 D,  X = E - E L2 E,
                 // each product filling blocks that are zero in the previous level (no
-                // cancellation), and T10 = -T11 N10 T00.  Products are 16x16x16 MFMAs on single
-                // bf16 operands (on hi + lo pairs in the precise-solve instantiation), and the
-                // diagonal 4x4 blocks stay fp32.  Forms: row form of M in lane (i16, g4) = M[i16][4 g4 + j], column
-                // form = M[4 g4 + j][i16]; mma16(row form of X, column form of Y) is the column
-                // form of X Y, and the row form of M is the column form of M^T.
-                const float bt[2] = {f32p(Lay::o_beta)[i16], f32p(Lay::o_beta)[16 + i16]};
+                // cancellation).  Products on the fp32 MFMA.  Forms: row form of M in lane
+                // (i16, g4) = M[i16][4 g4 + j], column form = M[4 g4 + j][i16]; mm16(row form of
+                // X, column form of Y) is the column form of X Y; a row form is read back from LDS
+                // where a column form was stored.
+                const int q = cw;
+                const float bq = bet[16 * q + i16];
                 // an opaque lane index: keeps the compiler from hoisting lane-constant masks out
                 // of the chunk loop into registers held across it
                 int lid = i16;
                 asm volatile("" : "+v"(lid));
                 const int rb = lid >> 2;                       // 4-row block of this lane's row / column
-                f32x4 Nr[2];
-                Nr[0] = reduce(3);
-                Nr[1] = reduce(4);
-                f32x4 N10r = reduce(5);
+                f32x4 Nr = reduce(3 + q);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool low = 4 * g4 + j < lid;
-                    Nr[0][j] = low ? Nr[0][j] * bt[0] : 0.f;
-                    Nr[1][j] = low ? Nr[1][j] * bt[1] : 0.f;
-                    N10r[j] *= bt[1];
-                }
-                float* Nb = f32p(Lay::o_N);
-                st<f32x4>(Nb + i16 * 20 + 4 * g4, Nr[0]);
-                st<f32x4>(Nb + SB + i16 * 20 + 4 * g4, Nr[1]);
+                for (int j = 0; j < 4; ++j) Nr[j] = 4 * g4 + j < lid ? Nr[j] * bq : 0.f;
+                float* Nb = f32p(Lay::o_N) + q * SB;
+                st<f32x4>(Nb + i16 * 20 + 4 * g4, Nr);
                 wave_lds_order();
-                f32x4 Nc[2], n1[2], n2[2], n3[2];
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) Nc[q][j] = Nb[q * SB + (4 * g4 + j) * 20 + i16];
-                    // rows 1..3 of the 4x4 diagonal block g4 (strictly lower entries)
-                    n1[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 1) * 20 + 4 * g4);
-                    n2[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 2) * 20 + 4 * g4);
-                    n3[q] = ld<f32x4>(Nb + q * SB + (4 * g4 + 3) * 20 + 4 * g4);
-                    pin(n1[q]);   // whole rows in separate registers, read together
-                    pin(n2[q]);
-                    pin(n3[q]);
-                }
+                // rows 1..3 of the 4x4 diagonal block g4 (strictly lower entries)
+                f32x4 n1 = ld<f32x4>(Nb + (4 * g4 + 1) * 20 + 4 * g4);
+                f32x4 n2 = ld<f32x4>(Nb + (4 * g4 + 2) * 20 + 4 * g4);
+                f32x4 n3 = ld<f32x4>(Nb + (4 * g4 + 3) * 20 + 4 * g4);
+                pin(n1);   // whole rows in separate registers, read together
+                pin(n2);
+                pin(n3);
+                wave_lds_order();
                 const bool on_diag = g4 == rb;                 // this lane's 4-block holds D entries
                 const int kk = lid & 3;
                 const float d0 = kk == 0 ? 1.f : 0.f, d1 = kk == 1 ? 1.f : 0.f;
                 const float d2 = kk == 2 ? 1.f : 0.f, d3 = kk == 3 ? 1.f : 0.f;
-                // whole-vector masks: L1 and L2 in row form (row i16, columns 4 g4 + j) and in
-                // column form (rows 4 g4 + j, column i16)
+                // whole-vector masks of L1 and L2 in row form (row i16, columns 4 g4 + j)
                 const bool l1r = (rb == 1 || rb == 3) && g4 == rb - 1;
-                const bool l1c = (g4 == 1 || g4 == 3) && rb == g4 - 1;
                 const bool l2r = lid >= 8 && g4 < 2;
-                const bool l2c = g4 >= 2 && lid < 8;
                 auto mask = [](f32x4 v, bool keep) { return keep ? v : zero4(); };
-                f32x4 Xc0, Xr1;
+                // D = (I + L0)^-1: column kk (column form) and row kk (row form) of the inverse of
+                // the unit lower 4x4 block g4
+                const float x1 = d1 - n1[0] * d0;
+                const float x2 = d2 - n2[0] * d0 - n2[1] * x1;
+                const float x3 = d3 - n3[0] * d0 - n3[1] * x1 - n3[2] * x2;
+                const float y2 = d2 - d3 * n3[2];
+                const float y1 = d1 - y2 * n2[1] - d3 * n3[1];
+                const float y0 = d0 - y1 * n1[0] - y2 * n2[0] - d3 * n3[0];
+                const f32x4 Dc = on_diag ? f32x4{d0, x1, x2, x3} : zero4();
+                const f32x4 Dr = on_diag ? f32x4{y0, y1, y2, d3} : zero4();
+                // E = D - D L1 D (column form); its row form through LDS (Nb is free again)
+                const f32x4 Ec = Dc - mm16(Dr, mm16(mask(Nr, l1r), Dc, zero4()), zero4());
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    // D = (I + L0)^-1: column kk (column form) and row kk (row form) of the
-                    // inverse of the unit lower 4x4 block g4
-                    const float x1 = d1 - n1[q][0] * d0;
-                    const float x2 = d2 - n2[q][0] * d0 - n2[q][1] * x1;
-                    const float x3 = d3 - n3[q][0] * d0 - n3[q][1] * x1 - n3[q][2] * x2;
-                    const float y2 = d2 - d3 * n3[q][2];
-                    const float y1 = d1 - y2 * n2[q][1] - d3 * n3[q][1];
-                    const float y0 = d0 - y1 * n1[q][0] - y2 * n2[q][0] - d3 * n3[q][0];
-                    const f32x4 Dc = on_diag ? f32x4{d0, x1, x2, x3} : zero4();
-                    const f32x4 Dr = on_diag ? f32x4{y0, y1, y2, d3} : zero4();
-                    if constexpr (Lay::kPrec) {
-                        // E = D - D L1 D (column form), E^T = D^T - D^T L1^T D^T (row form of E)
-                        const f32x4 Ec = Dc - mma16x(Dr, mma16x(mask(Nr[q], l1r), Dc));
-                        const f32x4 Er = Dr - mma16x(Dc, mma16x(mask(Nc[q], l1c), Dr));
-                        // X = E - E L2 E: column form for T00, row form for T11
-                        if (q == 0)
-                            Xc0 = Ec - mma16x(Er, mma16x(mask(Nr[q], l2r), Ec));
-                        else
-                            Xr1 = Er - mma16x(Ec, mma16x(mask(Nc[q], l2c), Er));
-                    } else {
-                        const bf16x4 Dcb = to_bf16x4(Dc), Drb = to_bf16x4(Dr);
-                        const f32x4 Ec = Dc - mma16(Drb, to_bf16x4(mma16(to_bf16x4(mask(Nr[q], l1r)), Dcb, zero4())), zero4());
-                        const f32x4 Er = Dr - mma16(Dcb, to_bf16x4(mma16(to_bf16x4(mask(Nc[q], l1c)), Drb, zero4())), zero4());
-                        const bf16x4 Ecb = to_bf16x4(Ec), Erb = to_bf16x4(Er);
-                        if (q == 0)
-                            Xc0 = Ec - mma16(Erb, to_bf16x4(mma16(to_bf16x4(mask(Nr[q], l2r)), Ecb, zero4())), zero4());
-                        else
-                            Xr1 = Er - mma16(Ecb, to_bf16x4(mma16(to_bf16x4(mask(Nc[q], l2c)), Erb, zero4())), zero4());
-                    }
-                }
-                // T10 = -T11 (N10 T00), column form
-                f32x4 T10c;
-                if constexpr (Lay::kPrec)
-                    T10c = -mma16x(Xr1, mma16x(N10r, Xc0));
-                else
-                    T10c = -mma16(to_bf16x4(Xr1), to_bf16x4(mma16(to_bf16x4(N10r), to_bf16x4(Xc0), zero4())), zero4());
-                // T_b = T Diag(beta): T00 and T10 from column forms (column i16), T11 from its row
-                // form (row 16 + i16, four adjacent columns)
-                const f32x4 bcol = ld<f32x4>(f32p(Lay::o_beta) + 16 + 4 * g4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    put_tb(4 * g4 + j, i16, Xc0[j] * bt[0]);
-                    put_tb(16 + 4 * g4 + j, i16, T10c[j] * bt[0]);
-                }
-                const f32x4 t11 = Xr1 * bcol;
-                bf16* tr = bfp(Lay::o_Tb) + (16 + i16) * TB + pm(16 + 4 * g4);
-                if constexpr (Lay::kTP == 2) {
-                    bf16x4 hv, lv;
-                    split4(t11, hv, lv);
-                    st<bf16x4>(tr, hv);
-                    st<bf16x4>(tr + kC * TB, lv);
+                for (int j = 0; j < 4; ++j) Nb[(4 * g4 + j) * 20 + i16] = Ec[j];
+                wave_lds_order();
+                f32x4 Er = ld<f32x4>(Nb + i16 * 20 + 4 * g4);
+                pin(Er);
+                // X = E - E L2 E, column form
+                const f32x4 Xc = Ec - mm16(Er, mm16(mask(Nr, l2r), Ec, zero4()), zero4());
+                // T_b^T [i][pm(j)] = T[j][i] beta_i (float16 hi, lo) for this block: lane
+                // (column i16, g4) holds T[16 q + 4 g4 + j][16 q + i16]
+                f16x4 hv, lv;
+                split_h4(Xc * bq, hv, lv);
+                f16* t = hp(Lay::o_Tb + 2 * tb * Lay::CPL) + (16 * q + i16) * TB + pm(16 * q + 4 * g4);
+                st<f16x4>(t, hv);
+                st<f16x4>(t + Lay::CPL / 2, lv);
+                // for T10: T00 in column form, T11 in row form
+                if (q == 0) {
+                    st<f32x4>(pub + i16 * 20 + 4 * g4, Xc);
                 } else {
-                    st<bf16x4>(tr, to_bf16x4(t11));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pub[SB + (4 * g4 + j) * 20 + i16] = Xc[j];
                 }
             } else {
-                // A_qk tile m (masked) -> split bf16 [row][pm(col)]
-                const int m = cw - 1;   // 0: rows 0-15 x cols 0-15, 1: 16-31 x 16-31, 2: 16-31 x 0-15
-                f32x4 acc = reduce(m);
-                const int ta = (m == 0) ? 0 : 1, tb = (m == 1) ? 1 : 0;
-                const int r = 16 * ta + i16;
+                // A_qk tiles (masked) -> float16 hi, lo [row][pm(col)]; m: 0 rows 0-15 x cols
+                // 0-15, 1: 16-31 x 16-31, 2: 16-31 x 0-15.  cw = 2 also forms beta N10 (row form).
+                auto aqk_tile = [&](int m) {
+                    f32x4 acc = reduce(m);
+                    const int ta = (m == 0) ? 0 : 1, tbb = (m == 1) ? 1 : 0;
+                    const int r = 16 * ta + i16;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = (16 * tb + 4 * g4 + j <= r) ? acc[j] : 0.f;
-                bf16x4 hv, lv;
-                split4(acc, hv, lv);
-                bf16* ad = bfp(Lay::o_Aq) + r * TB + pm(16 * tb + 4 * g4);
-                st<bf16x4>(ad, hv);
-                st<bf16x4>(ad + kC * TB, lv);
+                    for (int j = 0; j < 4; ++j) acc[j] = (16 * tbb + 4 * g4 + j <= r) ? acc[j] : 0.f;
+                    f16x4 hv, lv;
+                    split_h4(acc, hv, lv);
+                    f16* ad = hp(Lay::o_Aq + 2 * tb * Lay::CPL) + r * TB + pm(16 * tbb + 4 * g4);
+                    st<f16x4>(ad, hv);
+                    st<f16x4>(ad + Lay::CPL / 2, lv);
+                };
+                if (cw == 2) {
+                    const f32x4 N10r = reduce(5) * bet[16 + i16];
+                    st<f32x4>(pub + 2 * SB + i16 * 20 + 4 * g4, N10r);
+                    aqk_tile(2);
+                } else {
+                    aqk_tile(0);
+                    aqk_tile(1);
+                }
+            }
+        }
+        // ---- interval 2: scale of the value path for the state step of chunk it - 1, from the
+        // largest |S| and |V| only, in steps of 2^4, so that the scaled values lie in [2^6, 2^10)
+        if (it >= 1 && it <= nchunks) {
+            float mV = 0.f;   // pa holds v of chunk it - 1
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                pa[t].pin_all();
+                float vv[8];
+                pa[t].to_f32(vv);
+                mV = fmaxf(mV, fmaxf(fmaxf(fmaxf(fabsf(vv[0]), fabsf(vv[1])), fmaxf(fabsf(vv[2]), fabsf(vv[3]))),
+                                     fmaxf(fmaxf(fabsf(vv[4]), fabsf(vv[5])), fmaxf(fabsf(vv[6]), fabsf(vv[7])))));
+            }
+            float mS0 = 0.f, mS1 = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < CT; ct += 2) {
+                mS0 = fmaxf(fmaxf(mS0, fabsf(Sacc[ct][0])), fabsf(Sacc[ct][1]));
+                mS0 = fmaxf(fmaxf(mS0, fabsf(Sacc[ct][2])), fabsf(Sacc[ct][3]));
+                mS1 = fmaxf(fmaxf(mS1, fabsf(Sacc[ct + 1][0])), fabsf(Sacc[ct + 1][1]));
+                mS1 = fmaxf(fmaxf(mS1, fabsf(Sacc[ct + 1][2])), fabsf(Sacc[ct + 1][3]));
+            }
+            const float m = wave_max(fmaxf(mV * vsc, fmaxf(mS0, mS1)));
+            if (m > 0.f && m < 3.0e38f) {
+                // m in [2^(ex-1), 2^ex) in scaled units; the unscaled exponent is ex + esc
+                const int ex = __builtin_amdgcn_frexp_expf(m) + esc;
+                int want = ((ex - 7) >> 2) << 2;                 // floor to a multiple of 4
+                want = want < -120 ? -120 : (want > 120 ? 120 : want);
+                if (want != esc) {
+                    const float f = __builtin_ldexpf(1.f, esc - want);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) Sacc[ct] *= f;
+                    esc = want;
+                    vsc = __builtin_ldexpf(1.f, -esc);
+                    osc = a.scale * __builtin_ldexpf(1.f, esc);
+                }
             }
         }
         __syncthreads();
     }
 
+    const float un = __builtin_ldexpf(1.f, esc);
     if (a.mode == 1) {
-        float* W = summary(seg);
+        float* Wsum = summary(seg);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) W[(size_t)(16 * ct + 4 * g4 + j) * wcols + col0 + i16] = Sacc[ct][j];
+            for (int j = 0; j < 4; ++j) Wsum[(size_t)(16 * ct + 4 * g4 + j) * wcols + col0 + i16] = Sacc[ct][j] * un;
     } else if (a.ST && (a.mode == 0 || seg == a.nseg - 1)) {
         float* ST = a.ST + ((size_t)n * H + h) * DK * a.dv;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                ST[(size_t)(16 * ct + 4 * g4 + j) * a.dv + col0 + i16] = Sacc[ct][j];
+                ST[(size_t)(16 * ct + 4 * g4 + j) * a.dv + col0 + i16] = Sacc[ct][j] * un;
     }
 }
 
@@ -1027,10 +1072,10 @@ __device__ int seq_of_rank(const PrefillArgs& a, int r, char* smem) {
     return n;
 }
 
-// Both roles run the same number of iterations (chunks + 1) with two barriers each.  RANK: packed
+// Both roles run the same number of iterations (chunks + 2) with two barriers each.  RANK: packed
 // sequences (at most kRankMax) in longest-first order; a separate instantiation, so that the
-// fixed-length kernel's code is not changed by the ranking.  PREC: the precise solve.
-template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, bool PREC>
+// fixed-length kernel's code is not changed by the ranking.
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
 __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
@@ -1042,7 +1087,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     const int seg = (unit / a.H) % nseg;
     const int rank = unit / (a.H * nseg);
     if (a.mode == 1 && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;   // not needed
-    KDA_POISON(smem, (Layout<DK, F32IN, PREC>::total));
+    KDA_POISON(smem, (Layout<DK>::total));
     KDA_POISON_DONE();
     int n = rank;
     if constexpr (RANK) n = seq_of_rank(a, rank, smem);
@@ -1056,14 +1101,14 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
-    if (wave < kNW) producer<DK, F32IN, GATE, PREC>(a, smem, wave, lane, row0, len, h);
-    else consumer<DK, F32IN, OUT_F32, PREC>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg);
+    if (wave < kNW) producer<DK, F32IN, GATE>(a, smem, wave, lane, row0, len, h);
+    else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg);
 }
 
-template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, bool PREC>
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
 static hipError_t launch_one(const PrefillArgs& a) {
-    using Lay = Layout<DK, F32IN, PREC>;
-    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE, RANK, PREC>;
+    using Lay = Layout<DK>;
+    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE, RANK>;
     // The LDS limit is a per-device attribute of the kernel: set it once on each device this
     // instantiation launches on (devices past 63 set it on every launch).  Concurrent first calls
     // may both set it; the value is the same.
@@ -1086,23 +1131,17 @@ static hipError_t launch_one(const PrefillArgs& a) {
     return hipGetLastError();
 }
 
-template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool PREC>
-static hipError_t launch_ranked(const PrefillArgs& a) {
-    if (a.cu && a.N > 1 && a.N <= kRankMax) return launch_one<DK, F32IN, OUT_F32, GATE, true, PREC>(a);
-    return launch_one<DK, F32IN, OUT_F32, GATE, false, PREC>(a);
-}
-
 template <int DK, bool F32IN, bool OUT_F32, bool GATE>
 static hipError_t launch_prefill(const PrefillArgs& a) {
-    return a.precise ? launch_ranked<DK, F32IN, OUT_F32, GATE, true>(a)
-                     : launch_ranked<DK, F32IN, OUT_F32, GATE, false>(a);
+    if (a.cu && a.N > 1 && a.N <= kRankMax) return launch_one<DK, F32IN, OUT_F32, GATE, true>(a);
+    return launch_one<DK, F32IN, OUT_F32, GATE, false>(a);
 }
 
 template <bool GATE>
 static hipError_t dispatch_prefill(const PrefillArgs& a) {
     if (a.dk == 128) {
-        // float32 inputs are supported at dk = 64 (the ABI rejects them at dk = 128)
-        if (a.in_f32) return hipErrorInvalidValue;
+        if (a.in_f32)
+            return a.out_f32 ? launch_prefill<128, true, true, GATE>(a) : launch_prefill<128, true, false, GATE>(a);
         return a.out_f32 ? launch_prefill<128, false, true, GATE>(a) : launch_prefill<128, false, false, GATE>(a);
     }
     if (a.dk == 64) {

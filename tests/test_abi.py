@@ -38,18 +38,6 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
-def test_precise_solve_switch(lib):
-    """Host-only: the setting round-trips, reports the previous value and rejects values other
-    than 0 and 1 without changing the setting."""
-    prev = ctypes.c_int32(-1)
-    assert lib.kda_set_precise_solve(1, ctypes.byref(prev)) == 0 and prev.value == 0
-    assert lib.kda_set_precise_solve(2, ctypes.byref(prev)) == 1
-    assert b"0 or 1" in lib.kda_last_error()
-    assert lib.kda_set_precise_solve(0, ctypes.byref(prev)) == 0 and prev.value == 1
-    assert lib.kda_set_precise_solve(0, None) == 0
-    assert binding.set_precise_solve(True) is False and binding.set_precise_solve(False) is True
-
-
 def test_status_strings(lib):
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARGUMENT"
@@ -82,7 +70,6 @@ def _fwd(lib, **kw):
     (dict(dk=96), binding.KDA_ERR_UNSUPPORTED),
     (dict(dv=32), binding.KDA_ERR_UNSUPPORTED),
     (dict(T=0, H=1 << 16), binding.KDA_ERR_UNSUPPORTED),           # H * d past 32-bit chunk offsets
-    (dict(ind=1), binding.KDA_ERR_UNSUPPORTED),                    # f32 inputs at dk = 128
     (dict(o=FAKE), binding.KDA_ERR_INVALID_ARGUMENT),              # o aliases q
     (dict(S0=FAKE * 64, ST=FAKE * 64 + 16), binding.KDA_ERR_INVALID_ARGUMENT),  # partial alias
 ])
