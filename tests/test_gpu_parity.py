@@ -6,9 +6,10 @@ output rounded from the exact value already sits at a relative L2 of about 1.66e
 significand), so bf16-output cases pass only if the kernel itself adds little error; the float32
 output cases show the kernel's own error.
 
-Small cases are compared element by element on every unit; the full-size workloads are run in the
-benchmark's launch configuration and compared on sampled (sequence, head) units, each evaluated by
-the oracle over its whole sequence.
+Small cases are compared element by element on every unit; the benchmark, packed and decode
+workloads are run at full size in the benchmark's launch configuration and compared element by
+element on every (sequence, head) unit too; the 1M-token sequence and the largest shapes are
+compared on sampled units, each evaluated by the oracle over its whole sequence.
 """
 import math
 
@@ -404,17 +405,54 @@ def _sampled_check(cfg, units, out_dtype=torch.bfloat16, seed=0):
     torch.cuda.empty_cache()
 
 
+def _all_units_check(cfg, out_dtype=torch.bfloat16, seed=0, batch=64):
+    """Full-size run on the GPU (inputs generated on the GPU) against the oracle on every
+    (sequence, head) unit, element by element: the units are evaluated in batches and the
+    whole-tensor relative L2 and max-abs errors accumulated over all of them."""
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_config_inputs(cfg, seed=seed, device="cuda")
+    o, ST = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["cu_seqlens"],
+                              out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    h = {k: (None if x[k] is None else x[k].cpu()) for k in ("q", "k", "v", "g", "beta", "S0")}
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu().tolist()
+    o_h, ST_h = o.float().cpu().numpy(), ST.cpu().numpy()
+    del x, o, ST
+    torch.cuda.empty_cache()
+    B, T, H = h["q"].shape[:3]
+    N = B if cu is None else len(cu) - 1
+    units = [(n, hh) for n in range(N) for hh in range(H)]
+    acc = {"o": [0.0, 0.0, 0.0], "S_T": [0.0, 0.0, 0.0]}   # sum (x-y)^2, sum y^2, max |x-y|
+
+    def add(name, got, ref):
+        d = np.asarray(got, np.float64) - ref
+        a = acc[name]
+        a[0] += float((d * d).sum())
+        a[1] += float((ref * ref).sum())
+        a[2] = max(a[2], float(np.abs(d).max()) if d.size else 0.0)
+
+    for i in range(0, len(units), batch):
+        part = units[i:i + batch]
+        outs, rST = c_oracle.kda_units(h["q"], h["k"], h["v"], h["g"], h["beta"], h["S0"],
+                                       None if cu is None else torch.tensor(cu), part)
+        for (n, hh), ou, sr in zip(part, outs, rST):
+            b, s0, e = (n, 0, T) if cu is None else (0, cu[n], cu[n + 1])
+            add("o", o_h[b, s0:e, hh], ou)
+            add("S_T", ST_h[n, hh], sr)
+    for name, (e2, r2, m) in acc.items():
+        r = math.sqrt(e2 / r2) if r2 > 0 else math.sqrt(e2)
+        print(f"  {name} over {len(units)} units: rel_l2={r:.3e} max_abs={m:.3e}", flush=True)
+        assert r <= REL_L2 and m <= MAX_ABS, f"{name}: rel_l2 {r:.3e} max_abs {m:.3e}"
+
+
 def test_workload_prefill_b4_h32_t32k(gpu_lib):
-    cfg = inputs.CONFIGS["prefill_b4_h32_t32k_d128"]
-    _sampled_check(cfg, [(0, 0), (1, 17), (2, 31), (3, 5)])
+    """The benchmark workload, every one of its 128 (sequence, head) units."""
+    _all_units_check(inputs.CONFIGS["prefill_b4_h32_t32k_d128"])
 
 
 def test_workload_varlen64(gpu_lib):
-    cfg = inputs.CONFIGS["varlen64_h32_d128"]
-    lens = inputs.varlen_lengths(cfg.n_varlen, 0)
-    longest = int(np.argmax(lens))
-    shortest = int(np.argmin(lens))
-    _sampled_check(cfg, [(longest, 3), (shortest, 30), (10, 0), (40, 21)])
+    """64 packed lognormal-length sequences x 32 heads: every one of the 2048 units."""
+    _all_units_check(inputs.CONFIGS["varlen64_h32_d128"])
 
 
 @pytest.mark.slow
@@ -647,12 +685,11 @@ def test_decode_workload_n1024_h32(gpu_lib):
     S = x["S"].clone()
     o = binding.recurrent_step(x["q"], x["k"], x["v"], x["g"], x["beta"], S)
     torch.cuda.synchronize()
-    idx = torch.arange(0, cfg.N, 37)
-    sub = {k: x[k][idx].cpu() for k in ("q", "k", "v", "g", "beta", "S")}
+    sub = {k: x[k].cpu() for k in ("q", "k", "v", "g", "beta", "S")}   # every (sequence, head)
     ro, rS = c_oracle.kda_forward(sub["q"][:, None], sub["k"][:, None], sub["v"][:, None],
                                   sub["g"][:, None], sub["beta"][:, None], sub["S"])
-    assert_close("o", o[idx].float().cpu().numpy(), ro[:, 0])
-    assert_close("S", S[idx].cpu().numpy(), rS)
+    assert_close("o", o.float().cpu().numpy(), ro[:, 0])
+    assert_close("S", S.cpu().numpy(), rS)
 
 
 def test_decode_with_states_past_4gib(gpu_lib):
