@@ -127,10 +127,10 @@ def kda_gate(z, A_log, g_min=G_MIN):
 
 
 # ----------------------------------------------------------------------------- around the operator
-# The weight-free steps that eq. (2) and eq. (6) of §2.1.1 apply around the recurrence, for the
-# fused decode: L2-normalised q and k, beta = Sigmoid of its logit, and the output gate
-# y = Sigmoid(G) * RMSNorm(o~) with G = W_g x given (W_o, the projections, ShortConv and Swish need
-# trained weights and stay outside).
+# The steps that eq. (2) and eq. (6) of §2.1.1 apply around the recurrence, for the fused decode:
+# the short convolution (caller taps) and Swish of the projections, L2-normalised q and k,
+# beta = Sigmoid of its logit, and the output gate y = Sigmoid(G) * RMSNorm(o~) with G = W_g x
+# given (the projections themselves and W_o need trained weights and stay outside).
 
 L2NORM_FLOOR = 1e-12   # the norm is floored so that a zero vector stays zero
 
@@ -159,12 +159,66 @@ def gated_rmsnorm(o, G, weight=None, eps=1e-6):
     return sigmoid(G) * r
 
 
-def kda_fused_decode(q, k, v, z, A_log, b, S, G, weight=None, eps=1e-6, scale=1.0, n_commit=None):
+def swish(x):
+    """x * Sigmoid(x), float64 (eq. (2): the activation after the short convolution)."""
+    x = _f64(x)
+    return x * sigmoid(x)
+
+
+def short_conv(x, w, state=None):
+    """Causal depthwise convolution along the token axis (eq. (2): ShortConv of a projection).
+
+    x: [N, K, H, C], K consecutive tokens per sequence; w: [H, C, W] taps per (head, channel),
+    w[..., W-1] weighting the current token and w[..., 0] the token W-1 steps back; state:
+    [N, H, C, W-1], the W-1 inputs that precede token 0, oldest first (None: zeros).  With xx the
+    state followed by x along the tokens,
+
+        y[n, t, h, c] = sum_j w[h, c, j] * xx[n, h, c, t + j].
+
+    Returns (y [N, K, H, C], xx [N, H, C, W - 1 + K]) in float64; the window after the first m
+    tokens is xx[..., m : m + W - 1]."""
+    x, w = _f64(x), _f64(w)
+    N, K, H, C = x.shape
+    W = w.shape[-1]
+    st = np.zeros((N, H, C, W - 1)) if state is None else _f64(state)
+    xx = np.concatenate([st, np.transpose(x, (0, 2, 3, 1))], axis=-1)
+    y = np.zeros((N, K, H, C))
+    for t in range(K):
+        y[:, t] = (xx[..., t:t + W] * w[None]).sum(-1)
+    return y, xx
+
+
+def kda_fused_decode(q, k, v, z, A_log, b, S, G, weight=None, eps=1e-6, scale=1.0, n_commit=None,
+                     conv_w=None, conv_state=None):
     """K decode tokens per (sequence, head) with the fused prologue and epilogue: q, k
     L2-normalised, beta = Sigmoid(b), g = kda_gate(z, A_log), the recurrence (eq. (1)) from S,
     outputs gated_rmsnorm(o~, G, weight, eps).  q, k, z [N, K, H, dk]; v, G [N, K, H, dv];
     b [N, K, H]; S [N, H, dk, dv].  Returns (y [N, K, H, dv], state after n_commit[n] tokens)
-    in float64 (n_commit None: all K)."""
+    in float64 (n_commit None: all K).
+
+    With conv_w ([H, 2 dk + dv, W]: the taps of q's channels, then k's, then v's) q, k, v are the
+    projections before eq. (2)'s ShortConv, and the operator's inputs are
+    L2Norm(Swish(ShortConv(q))), L2Norm(Swish(ShortConv(k))), Swish(ShortConv(v)), the window
+    entering from conv_state ([N, H, 2 dk + dv, W - 1], oldest first; None: zeros).  The result
+    then also holds the window after the n_commit[n] committed tokens."""
+    conv_out = None
+    if conv_w is not None:
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        dk, dv = q.shape[-1], v.shape[-1]
+        cw = _f64(conv_w)
+        st = None if conv_state is None else _f64(conv_state)
+        parts = []
+        for x, lo, hi in ((q, 0, dk), (k, dk, 2 * dk), (v, 2 * dk, 2 * dk + dv)):
+            y, xx = short_conv(x, cw[:, lo:hi], None if st is None else st[:, :, lo:hi])
+            parts.append((swish(y), xx))
+        (q, xq), (k, xk), (v, xv) = parts
+        W = cw.shape[-1]
+        N, K = q.shape[:2]
+        xx = np.concatenate([xq, xk, xv], axis=2)
+        conv_out = np.zeros(xx.shape[:3] + (W - 1,))
+        for n in range(N):
+            c = K if n_commit is None else max(0, min(K, int(n_commit[n])))
+            conv_out[n] = xx[n, :, :, c:c + W - 1]
     qn, kn = l2norm(q), l2norm(k)
     beta = sigmoid(b)
     g = kda_gate(z, A_log)
@@ -179,4 +233,6 @@ def kda_fused_decode(q, k, v, z, A_log, b, S, G, weight=None, eps=1e-6, scale=1.
             _, s = kda_forward(qn[n:n + 1, :c], kn[n:n + 1, :c], _f64(v)[n:n + 1, :c], g[n:n + 1, :c],
                                beta[n:n + 1, :c], S[n:n + 1], scale=scale)
             S_out[n] = s[0]
+    if conv_out is not None:
+        return y, S_out, conv_out
     return y, S_out

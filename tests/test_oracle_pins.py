@@ -573,3 +573,122 @@ def test_fused_decode_invariants():
                                             x["A_log"], b[:, t:t + 1], S, G[:, t:t + 1], w)
         assert np.abs(yt[:, 0] - y1[:, t]).max() < 1e-12
     assert np.abs(S - s1).max() < 1e-12
+
+
+# ------------------------------------------------------------------ short convolution (eq. (2))
+
+def _conv_pins(conv, sw):
+    """Errors of a short-convolution / Swish pair against library routines and closed forms."""
+    import scipy.signal
+    rng = np.random.default_rng(21)
+    errs = {}
+    N, K, H, C, W = 2, 7, 3, 5, 4
+    x = rng.standard_normal((N, K, H, C))
+    w = rng.standard_normal((H, C, W))
+    st = rng.standard_normal((N, H, C, W - 1))
+    y, xx = conv(x, w, st)
+    ref_np = np.zeros_like(y)
+    ref_lf = np.zeros_like(y)
+    for n in range(N):
+        for h in range(H):
+            for c in range(C):
+                series = np.concatenate([st[n, h, c], x[n, :, h, c]])
+                # numpy.convolve flips its second argument: reversed taps give sum_j w_j xx_{t+j}
+                ref_np[n, :, h, c] = np.convolve(series, w[h, c][::-1], mode="valid")
+                # an FIR filter y[m] = sum_k b_k s[m - k] with b = reversed taps, from m = W - 1 on
+                ref_lf[n, :, h, c] = scipy.signal.lfilter(w[h, c][::-1], [1.0], series)[W - 1:]
+    errs["conv_numpy"] = float(np.abs(y - ref_np).max())
+    errs["conv_lfilter"] = float(np.abs(y - ref_lf).max())
+    # the returned history: state, then the inputs
+    errs["history"] = float(np.abs(xx[..., W - 1:] - np.transpose(x, (0, 2, 3, 1))).max()
+                            + np.abs(xx[..., :W - 1] - st).max())
+    # a one-tap filter scales each input; a delta tap at position 0 returns the input W-1 back
+    y1, _ = conv(x, w[..., -1:], None)
+    errs["one_tap"] = float(np.abs(y1 - x * w[None, None, :, :, -1]).max())
+    d = np.zeros((H, C, W))
+    d[..., 0] = 1.0
+    yd, _ = conv(x, d, st)
+    errs["delta_back"] = float(np.abs(yd[:, W - 1:] - x[:, :K - W + 1]).max()
+                               + np.abs(yd[:, 0] - np.transpose(st[..., 0], (0, 1, 2))).max())
+    # resume: the first m tokens, then the rest entered with the window after m
+    m = 3
+    ya, xa = conv(x[:, :m], w, st)
+    yb, _ = conv(x[:, m:], w, xa[..., m:m + W - 1])
+    errs["resume"] = float(np.abs(np.concatenate([ya, yb], 1) - y).max())
+    # Swish against torch's silu and the definition with scipy's logistic
+    import scipy.special
+    z = rng.standard_normal(50) * 4
+    errs["swish_torch"] = float(np.abs(sw(z) - torch.nn.functional.silu(torch.from_numpy(z)).numpy()).max())
+    errs["swish_expit"] = float(np.abs(sw(z) - z * scipy.special.expit(z)).max())
+    return errs
+
+
+def test_short_conv_pins():
+    errs = _conv_pins(kda_oracle.short_conv, kda_oracle.swish)
+    for name, err in errs.items():
+        assert err <= 1e-12, f"short-conv pin {name}: {err:.3e}"
+
+
+def _conv_off_by_one(x, w, state=None):
+    y, xx = kda_oracle.short_conv(x, w, state)
+    W = _np(w).shape[-1]
+    yy = np.zeros_like(y)
+    for t in range(y.shape[1]):          # window one token late: drops the current input
+        lo = max(0, t - 1)
+        yy[:, t] = (xx[..., lo:lo + W] * _np(w)[None]).sum(-1)
+    return yy, xx
+
+
+def _conv_taps_unreversed(x, w, state=None):
+    return kda_oracle.short_conv(x, _np(w)[..., ::-1], state)
+
+
+CONV_MUTANTS = {
+    "window_off_by_one": (_conv_off_by_one, None),
+    "taps_reversed": (_conv_taps_unreversed, None),
+    "swish_is_sigmoid": (None, kda_oracle.sigmoid),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_pins_catch_planted_mistake(name):
+    conv, sw = CONV_MUTANTS[name]
+    errs = _conv_pins(conv or kda_oracle.short_conv, sw or kda_oracle.swish)
+    assert any(not (e <= 1e-6) for e in errs.values()), f"planted mistake {name} passes every pin"
+
+
+def test_fused_decode_with_conv_composes():
+    """The fused decode with the short convolution equals the fused decode without it on the
+    convolved, Swish-activated projections; the window it returns is the inputs around the
+    committed prefix; K tokens at once equal token-by-token calls that carry state and window."""
+    rng = np.random.default_rng(31)
+    N, K, H, dk, dv, W = 2, 4, 2, 8, 6, 4
+    C = 2 * dk + dv
+    pq, pk = rng.standard_normal((N, K, H, dk)), rng.standard_normal((N, K, H, dk))
+    pv = rng.standard_normal((N, K, H, dv))
+    z = rng.standard_normal((N, K, H, dk))
+    A = rng.standard_normal(H) * 0.5
+    b = rng.standard_normal((N, K, H))
+    G = rng.standard_normal((N, K, H, dv))
+    S = rng.standard_normal((N, H, dk, dv)) * 0.1
+    cw = rng.standard_normal((H, C, W)) * 0.5
+    cs = rng.standard_normal((N, H, C, W - 1))
+    nc = [2, 4]
+    y, s1, win = kda_oracle.kda_fused_decode(pq, pk, pv, z, A, b, S, G, None, 1e-6, 1.0, nc, cw, cs)
+    cq, _ = kda_oracle.short_conv(pq, cw[:, :dk], cs[:, :, :dk])
+    ck, _ = kda_oracle.short_conv(pk, cw[:, dk:2 * dk], cs[:, :, dk:2 * dk])
+    cv, _ = kda_oracle.short_conv(pv, cw[:, 2 * dk:], cs[:, :, 2 * dk:])
+    y2, s2 = kda_oracle.kda_fused_decode(kda_oracle.swish(cq), kda_oracle.swish(ck), kda_oracle.swish(cv),
+                                         z, A, b, S, G, None, 1e-6, 1.0, nc)
+    assert np.abs(y - y2).max() < 1e-12 and np.abs(s1 - s2).max() < 1e-12
+    for n, c in enumerate(nc):
+        series = np.concatenate([cs[n], np.concatenate([np.transpose(a[n], (1, 2, 0)) for a in (pq, pk, pv)], 1)], -1)
+        assert np.array_equal(win[n], series[..., c:c + W - 1])
+    Sc, Wc = S, cs
+    for t in range(K):
+        sl = lambda a: a[:, t:t + 1]
+        yt, Sc, Wc = kda_oracle.kda_fused_decode(sl(pq), sl(pk), sl(pv), sl(z), A, sl(b), Sc, sl(G),
+                                                 None, 1e-6, 1.0, None, cw, Wc)
+        assert np.abs(yt[:, 0] - y[:, t]).max() < 1e-12
+    _, s_all, w_all = kda_oracle.kda_fused_decode(pq, pk, pv, z, A, b, S, G, None, 1e-6, 1.0, None, cw, cs)
+    assert np.abs(Sc - s_all).max() < 1e-12 and np.abs(Wc - w_all).max() < 1e-12
