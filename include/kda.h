@@ -211,23 +211,35 @@ kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, cons
                                int32_t K, int32_t H, int32_t dk, int32_t dv, kda_dtype in_dtype,
                                kda_dtype out_dtype, float scale, void* o, hipStream_t stream);
 
-/* kda_recurrent_multi fused with the weight-free steps the model applies around the operator
- * (§2.1.1), for serving and speculative decoding:
- *   before (eq. (2)): q and k are L2-normalised per (token, head), x / max(||x||_2, 1e-12);
+/* kda_recurrent_multi fused with the steps the model applies around the operator (§2.1.1),
+ * for serving and speculative decoding (§5.4.2: one kernel covers short convolution, input
+ * norm, gating, the recurrence and the output norm, for the replayed and drafted tokens):
+ *   before (eq. (2)): with conv_weight given, q, k and v are the projections before the short
+ *     convolution and become Swish(ShortConv(.)) first, ShortConv being causal and depthwise per
+ *     (head, channel):  x'_t = sum_{j < W} conv_weight[h, c, j] x_{t - W + 1 + j},  with the W - 1
+ *     inputs before the first token taken from conv_state, Swish(x) = x Sigmoid(x);
+ *     then q and k are L2-normalised per (token, head), x / max(||x||_2, 1e-12);
  *     beta = Sigmoid(beta_logit); g = -5 Sigmoid(exp(A_log[h]) z) (eq. (5));
  *   after (eq. (6) without W_o): y = Sigmoid(G) * RMSNorm(o~) per (token, head), with
  *     RMSNorm(o~) = o~ / sqrt(mean over dv of o~^2 + eps) * norm_weight.
  * The projections that produce q, k, v, z, beta_logit and G (and W_o after) need model weights
- * and stay with the caller.  State update, commit rule and o~ are those of kda_recurrent_multi.
+ * and stay with the caller.  State update, commit rule and o~ are those of kda_recurrent_multi;
+ * the convolution window is committed with the state: conv_state receives, IN PLACE, the last
+ * W - 1 inputs of each channel up to and including token n_commit[n] - 1 (0: untouched).
  *
  * Layouts: q, k, z [N, K, H, dk]; v, G, y [N, K, H, dv]; beta_logit [N, K, H], all in in_dtype;
  * A_log [H] float32; norm_weight [dv] float32, 16-byte aligned, or NULL (ones); eps >= 0;
- * S [N, H, dk, dv] float32; n_commit device int32 [N] or NULL.  y may be NULL (no outputs; G is
- * then not read).  Neither S nor y may overlap an input, nor each other.  Supported: dk, dv in {64, 128}.
+ * conv_weight [H, 2 dk + dv, W] float32 (channels of q, then k, then v; tap W - 1 weights the
+ * current token) or NULL (no convolution and no Swish: q, k, v are used as given);
+ * conv_state [N, H, 2 dk + dv, W - 1] in in_dtype, oldest input first (may be NULL when W = 1);
+ * conv_width W in [1, 4] (ignored without conv_weight); S [N, H, dk, dv] float32; n_commit device
+ * int32 [N] or NULL.  y may be NULL (no outputs; G is then not read).  None of S, conv_state and y
+ * may overlap an input or each other.  Supported: dk, dv in {64, 128}.
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v, const void* z,
                                      const float* A_log, const void* beta_logit, const void* G,
-                                     const float* norm_weight, float eps, float* S,
+                                     const float* norm_weight, float eps, const float* conv_weight,
+                                     void* conv_state, int32_t conv_width, float* S,
                                      const int32_t* n_commit, int32_t N, int32_t K, int32_t H,
                                      int32_t dk, int32_t dv, kda_dtype in_dtype,
                                      kda_dtype out_dtype, float scale, void* y, hipStream_t stream);

@@ -72,8 +72,8 @@ def load(path: str = LIB_PATH):
                                             ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_step_gate.restype = ctypes.c_int
     lib.kda_recurrent_multi_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
-                                              i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
-                                              ctypes.c_float, vp, vp]
+                                              i32, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_multi_fused.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -379,12 +379,14 @@ def recurrent_step_gate(q, k, v, z, A_log, beta, S, *, scale: float = 1.0, out_d
 
 def recurrent_multi_fused(q, k, v, z, A_log, beta_logit, G, S, n_commit=None, *, norm_weight=None,
                           eps: float = 1e-6, scale: float = 1.0, out_dtype=None, y=None,
-                          outputs: bool = True):
-    """recurrent_multi with the weight-free steps around the operator fused in: q, k
-    L2-normalised, beta = Sigmoid(beta_logit), g from the logits z and A_log, and outputs
-    y = Sigmoid(G) * RMSNorm(o~) (weight norm_weight [dv] float32 or None, eps).  q, k, z
-    [N,K,H,dk], v, G [N,K,H,dv], beta_logit [N,K,H] share a dtype; S advanced in place as in
-    recurrent_multi.  Returns y [N,K,H,dv] (None with outputs=False)."""
+                          outputs: bool = True, conv_weight=None, conv_state=None):
+    """recurrent_multi with the steps around the operator fused in: optionally the short
+    convolution and Swish on q, k, v (conv_weight [H, 2dk+dv, W] float32, conv_state
+    [N, H, 2dk+dv, W-1] in the input dtype, oldest first, advanced in place to the committed
+    token), then q, k L2-normalised, beta = Sigmoid(beta_logit), g from the logits z and A_log,
+    and outputs y = Sigmoid(G) * RMSNorm(o~) (weight norm_weight [dv] float32 or None, eps).
+    q, k, z [N,K,H,dk], v, G [N,K,H,dv], beta_logit [N,K,H] share a dtype; S advanced in place
+    as in recurrent_multi.  Returns y [N,K,H,dv] (None with outputs=False)."""
     lib = load()
     dev = q.device
     N, K, H, dk = q.shape
@@ -401,6 +403,12 @@ def recurrent_multi_fused(q, k, v, z, A_log, beta_logit, G, S, n_commit=None, *,
         _require(n_commit, "n_commit", dev, torch.int32, (N,))
     if norm_weight is not None:
         _require(norm_weight, "norm_weight", dev, torch.float32, (dv,))
+    width = 1
+    if conv_weight is not None:
+        width = conv_weight.shape[-1]
+        _require(conv_weight, "conv_weight", dev, torch.float32, (H, 2 * dk + dv, width))
+        if width > 1:
+            _require(conv_state, "conv_state", dev, dt, (N, H, 2 * dk + dv, width - 1))
     out_dtype = out_dtype or dt
     if outputs:
         _require(G, "G", dev, dt, (N, K, H, dv))
@@ -411,7 +419,8 @@ def recurrent_multi_fused(q, k, v, z, A_log, beta_logit, G, S, n_commit=None, *,
     else:
         y = None
     st = _on(dev, lib.kda_recurrent_multi_fused, _p(q), _p(k), _p(v), _p(z), _p(A_log),
-             _p(beta_logit), _p(G) if outputs else None, _p(norm_weight), float(eps), _p(S),
+             _p(beta_logit), _p(G) if outputs else None, _p(norm_weight), float(eps),
+             _p(conv_weight), _p(conv_state) if width > 1 else None, width, _p(S),
              _p(n_commit), N, K, H, dk, dv, _dt(q), _dt(y) if y is not None else _dt(q),
              float(scale), _p(y), _stream(dev))
     _check(st)

@@ -117,7 +117,7 @@ kda_status check_cu(const int32_t* cu, int32_t N, int64_t T, hipStream_t stream)
 
 extern "C" {
 
-int32_t kda_version(void) { return (1 << 16) | 1; }
+int32_t kda_version(void) { return (1 << 16) | 2; }
 
 const char* kda_status_string(kda_status s) {
     switch (s) {
@@ -423,7 +423,8 @@ kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, cons
 
 kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v, const void* z,
                                      const float* A_log, const void* beta_logit, const void* G,
-                                     const float* norm_weight, float eps, float* S,
+                                     const float* norm_weight, float eps, const float* conv_weight,
+                                     void* conv_state, int32_t conv_width, float* S,
                                      const int32_t* n_commit, int32_t N, int32_t K, int32_t H,
                                      int32_t dk, int32_t dv, kda_dtype in_dtype,
                                      kda_dtype out_dtype, float scale, void* y, hipStream_t stream) {
@@ -436,6 +437,8 @@ kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v
     if (!(dk == 64 || dk == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dk", dk);
     if (!(dv == 64 || dv == 128)) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld is not supported (64 or 128)", "dv", dv);
     if ((int64_t)N * H > (int64_t)1 << 30) return fail(KDA_ERR_UNSUPPORTED, "%s = %lld too large", "N*H", (long long)N * H);
+    if (conv_weight && (conv_width < 1 || conv_width > 4))
+        return fail(KDA_ERR_UNSUPPORTED, "%s = %lld: the short convolution is 1 to 4 taps wide", "conv_width", conv_width);
     if (N == 0 || K == 0) return ok();
     const size_t es = dsize(in_dtype);
     KDA_TRY(check_ptr(q, 16, "q"));
@@ -452,8 +455,19 @@ kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v
         KDA_TRY(check_ptr(y, 16, "y"));
         KDA_TRY(check_ptr(G, es, "G"));
     }
+    const size_t nch = (size_t)(2 * dk + dv);
+    size_t ncw = 0, ncs = 0;
+    if (conv_weight) {
+        KDA_TRY(check_ptr(conv_weight, 4, "conv_weight"));
+        ncw = (size_t)H * nch * conv_width * 4;
+        if (conv_width > 1) {
+            KDA_TRY(check_ptr(conv_state, es, "conv_state"));
+            ncs = nh * nch * (conv_width - 1) * es;
+        }
+    }
     {
-        const Span outs[] = {{S, nh * dk * dv * 4, "S"}, {y, nt * dv * dsize(out_dtype), "y"}};
+        const Span outs[] = {{S, nh * dk * dv * 4, "S"}, {y, nt * dv * dsize(out_dtype), "y"},
+                             {ncs ? conv_state : nullptr, ncs, "conv_state"}};
         const Span ins[] = {{q, nt * dk * es, "q"},
                             {k, nt * dk * es, "k"},
                             {v, nt * dv * es, "v"},
@@ -462,7 +476,8 @@ kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v
                             {beta_logit, nt * es, "beta_logit"},
                             {y ? G : nullptr, nt * dv * es, "G"},
                             {norm_weight, (size_t)dv * 4, "norm_weight"},
-                            {n_commit, (size_t)N * 4, "n_commit"}};
+                            {n_commit, (size_t)N * 4, "n_commit"},
+                            {conv_weight, ncw, "conv_weight"}};
         KDA_TRY(check_disjoint(outs, ins));
     }
     kda::DecodeArgs a{q, k, v, nullptr, beta_logit, S, (int32_t)nh, dk, dv,
@@ -477,6 +492,9 @@ kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v
     a.G = G;
     a.norm_w = norm_weight;
     a.eps = eps;
+    a.conv_w = conv_weight;
+    a.conv_state = conv_state;
+    a.conv_width = conv_weight ? conv_width : 1;
     return hip_status(kda::launch_decode_step(a));
 }
 

@@ -251,7 +251,13 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
 // decay map runs once per (token, channel) into LDS instead of in every thread that holds the
 // channel's row, and k is read again for the state update rather than held across the barrier:
 // with those, three waves per SIMD fit (1194 -> 882 us for 4 tokens at 1024 x 32 heads).
-template <int DK, int DV, bool IN_F32, bool OUT_F32>
+//
+// CONV: q, k, v are the projections before eq. (2)'s short convolution.  Each of the 2 dk + dv
+// channels (q's, then k's, then v's) is owned by one thread, which keeps the channel's last
+// W - 1 inputs in registers, forms Swish(sum_j w_j x_{t-W+1+j}) a token ahead into LDS (read there
+// by the recurrence in place of q, k, v) and writes its window back to conv_state after the
+// committed prefix, together with S.
+template <int DK, int DV, bool IN_F32, bool OUT_F32, bool CONV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_fused_kernel(const void* __restrict__ qp,
                                                            const void* __restrict__ kp,
                                                            const void* __restrict__ vp,
@@ -263,15 +269,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                                                            float* __restrict__ S,
                                                            const int32_t* __restrict__ n_commit,
                                                            int32_t N, int32_t H, int32_t K,
-                                                           float scale, void* __restrict__ op) {
+                                                           float scale, void* __restrict__ op,
+                                                           const float* __restrict__ conv_w,
+                                                           void* __restrict__ conv_state, int32_t W) {
     constexpr int CG = DV / 4;
     constexpr int NRG = 256 / CG;
     constexpr int RPG = DK / NRG;
+    constexpr int NCH = 2 * DK + DV;  // convolved channels
     static_assert(RPG >= 1 && DK % NRG == 0 && 64 % CG == 0, "decode tiling");
+    static_assert(NCH <= 512, "two convolved channels per thread at most");
     __shared__ f32x4 red_y[2][NRG][CG];
     __shared__ f32x4 red_z[2][NRG][CG];
     __shared__ f32x4 red_s[2][NRG];   // q . k, q . q, k . k (and one spare) per row group
     __shared__ float dec[2][DK];      // per-channel decay exp(g) of a token, by token parity
+    __shared__ float cin[CONV ? 3 : 1][CONV ? NCH : 1];   // convolved q, k, v of a token, rotating
+    __shared__ __align__(16) float cwt[CONV ? NCH : 1][8];  // taps and window per channel
 
     const int unit = blockIdx.x;        // sequence * H + head
     if (unit >= N * H) return;
@@ -279,6 +291,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     KDA_POISON(red_z, sizeof red_z);
     KDA_POISON(red_s, sizeof red_s);
     KDA_POISON(dec, sizeof dec);
+    KDA_POISON(cin, sizeof cin);
+    KDA_POISON(cwt, sizeof cwt);
     KDA_POISON_DONE();
     const int n = unit / H, h = unit % H;
     const int t = threadIdx.x;
@@ -305,20 +319,93 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     auto decay_into = [&](int tok, int buf) {
         if (t < DK) dec[buf][t] = decay_at<IN_F32, true>(nullptr, zp, ea, (((size_t)n * K + tok) * H + h) * DK + t);
     };
+    // CONV: thread t owns channels t and t + 256 (when < NCH).  A channel's taps and window sit in
+    // its own row of cwt, read and written by its owner only (no barrier needed), right-aligned
+    // (zeros on the left when W < 4) so that y = w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3}
+    // with fixed offsets: cwt[c] = {w0, w1, w2, w3, x_{t-3}, x_{t-2}, x_{t-1}, unused}.
+    auto chan = [&](int c, const void*& src, size_t& at, size_t& stride) {
+        // q channels [0, DK), k channels [DK, 2 DK), v channels [2 DK, NCH); [N, K, H, d] layout
+        const int part = c < DK ? 0 : (c < 2 * DK ? 1 : 2);
+        const int d = part < 2 ? DK : DV;
+        src = part == 0 ? qp : (part == 1 ? kp : vp);
+        stride = (size_t)H * d;
+        at = ((size_t)n * K * H + h) * d + (c - part * DK);
+    };
+    if constexpr (CONV) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int c = t + 256 * e;
+            if (c < NCH) {
+                const float* wrow = conv_w + ((size_t)h * NCH + c) * W;
+                const size_t so = (((size_t)n * H + h) * NCH + c) * (W - 1);
+                f32x4 tp = zero4(), wn = zero4();
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j >= 4 - W) tp[j] = wrow[j - (4 - W)];
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    if (j >= 4 - W) wn[j] = in_at(conv_state, so + (j - (4 - W)));
+                *reinterpret_cast<f32x4*>(&cwt[c][0]) = tp;
+                *reinterpret_cast<f32x4*>(&cwt[c][4]) = wn;
+            }
+        }
+    }
+    // convolved inputs of token tok into cin[buf]; the window is stored once the committed tokens
+    // are in it
+    auto conv_into = [&](int tok, int buf) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int c = t + 256 * e;
+            if (c < NCH) {
+                const void* src;
+                size_t at, stride;
+                chan(c, src, at, stride);
+                const float x = in_at(src, at + (size_t)tok * stride);
+                const f32x4 tp = *reinterpret_cast<const f32x4*>(&cwt[c][0]);
+                f32x4 wn = *reinterpret_cast<const f32x4*>(&cwt[c][4]);
+                const float y = tp[3] * x + tp[2] * wn[2] + tp[1] * wn[1] + tp[0] * wn[0];
+                cin[buf][c] = y * sigm(y);                  // Swish
+                wn = f32x4{wn[1], wn[2], x, 0.f};
+                *reinterpret_cast<f32x4*>(&cwt[c][4]) = wn;
+                if (tok + 1 == commit) {
+                    const size_t so = (((size_t)n * H + h) * NCH + c) * (W - 1);
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) {
+                        if (j >= 4 - W) {
+                            const size_t o = so + (j - (4 - W));
+                            if constexpr (IN_F32) reinterpret_cast<float*>(conv_state)[o] = wn[j];
+                            else reinterpret_cast<bf16*>(conv_state)[o] = f2bf(wn[j]);
+                        }
+                    }
+                }
+            }
+        }
+    };
+    // cin rotates over three buffers: a token's convolved k and v are read after the barrier too,
+    // so the buffer written a token ahead must be the one read two tokens back (a barrier between)
+    int cb = 0;
     decay_into(0, 0);
+    if constexpr (CONV) conv_into(0, 0);
     __syncthreads();
     for (int tok = 0; tok < K; ++tok) {
         const int pb = tok & 1;
+        const int cn = cb == 2 ? 0 : cb + 1;
         const size_t row = ((size_t)n * K + tok) * H + h;   // token row of [N, K, H, *]
         const size_t kb = row * DK;
-        if (tok + 1 < K) decay_into(tok + 1, pb ^ 1);
+        if (tok + 1 < K) {
+            decay_into(tok + 1, pb ^ 1);
+            if constexpr (CONV) conv_into(tok + 1, cn);
+        }
+        // q, k, v of the token: as given, or (CONV) convolved, from LDS
+        auto q_at = [&](int r) { if constexpr (CONV) return cin[cb][r]; else return in_at(qp, kb + r); };
+        auto k_at = [&](int r) { if constexpr (CONV) return cin[cb][DK + r]; else return in_at(kp, kb + r); };
         f32x4 y = zero4(), z = zero4();
         float qk = 0.f, qq = 0.f, kk = 0.f;
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {
             const float a = dec[pb][r0 + i];
-            const float kvi = in_at(kp, kb + r0 + i);
-            const float qv = in_at(qp, kb + r0 + i);
+            const float kvi = k_at(r0 + i);
+            const float qv = q_at(r0 + i);
             s[i] *= a;
             y += kvi * s[i];
             z += qv * s[i];
@@ -344,9 +431,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         const size_t vb = row * DV + 4 * cg;
         f32x4 u;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) u[c] = b * (in_at(vp, vb + c) - yt[c] * rk);
+        for (int c = 0; c < 4; ++c) {
+            float vv;
+            if constexpr (CONV) vv = cin[cb][2 * DK + 4 * cg + c];
+            else vv = in_at(vp, vb + c);
+            u[c] = b * (vv - yt[c] * rk);
+        }
 #pragma unroll
-        for (int i = 0; i < RPG; ++i) s[i] += (in_at(kp, kb + r0 + i) * rk) * u;   // k re-read (cached)
+        for (int i = 0; i < RPG; ++i) s[i] += (k_at(r0 + i) * rk) * u;   // k re-read (cached)
         if (tok + 1 == commit) {
 #pragma unroll
             for (int i = 0; i < RPG; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
@@ -371,6 +463,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                 }
             }
         }
+        cb = cn;
     }
 }
 
@@ -378,9 +471,14 @@ template <int DK, int DV, bool IN_F32, bool OUT_F32>
 static hipError_t launch_fused(const DecodeArgs& a) {
     const int64_t units = (int64_t)a.N * a.H;
     if (units == 0 || a.K == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_fused_kernel<DK, DV, IN_F32, OUT_F32>), dim3((unsigned)units), dim3(256), 0,
-                       a.stream, a.q, a.k, a.v, a.z, a.A_log, a.beta, a.G, a.norm_w, a.eps, a.S,
-                       a.n_commit, a.N, a.H, a.K, a.scale, a.o);
+    if (a.conv_w)
+        hipLaunchKernelGGL((decode_fused_kernel<DK, DV, IN_F32, OUT_F32, true>), dim3((unsigned)units), dim3(256), 0,
+                           a.stream, a.q, a.k, a.v, a.z, a.A_log, a.beta, a.G, a.norm_w, a.eps, a.S,
+                           a.n_commit, a.N, a.H, a.K, a.scale, a.o, a.conv_w, a.conv_state, a.conv_width);
+    else
+        hipLaunchKernelGGL((decode_fused_kernel<DK, DV, IN_F32, OUT_F32, false>), dim3((unsigned)units), dim3(256), 0,
+                           a.stream, a.q, a.k, a.v, a.z, a.A_log, a.beta, a.G, a.norm_w, a.eps, a.S,
+                           a.n_commit, a.N, a.H, a.K, a.scale, a.o, nullptr, nullptr, 1);
     return hipGetLastError();
 }
 

@@ -66,6 +66,11 @@ struct DecodeArgs {
     const void* G = nullptr;
     const float* norm_w = nullptr;
     float eps = 0.f;
+    // eq. (2)'s short convolution before Swish (fused only): taps [H, 2 dk + dv, conv_width]
+    // float32, window [N, H, 2 dk + dv, conv_width - 1] in the input dtype, updated at the commit
+    const float* conv_w = nullptr;
+    void* conv_state = nullptr;
+    int32_t conv_width = 1;
 };
 
 hipError_t launch_chunk_fwd(const PrefillArgs& a);

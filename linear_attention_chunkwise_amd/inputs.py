@@ -184,3 +184,16 @@ def make_fused_decode_inputs(N, K, H, dk, dv, *, dtype=torch.bfloat16, seed=0, d
     w = (1.0 + 0.1 * _randn((dv,), gen, device)).float()
     S = _randn((N, H, dk, dv), gen, device) * S_std
     return dict(q=q, k=k, v=v, z=z, A_log=A_log, beta_logit=b, G=G, norm_weight=w, S=S)
+
+
+def make_conv_inputs(N, H, dk, dv, W, *, dtype=torch.bfloat16, seed=0, device="cpu"):
+    """Taps and entering windows for the short convolution in front of the fused decode: weights
+    [H, 2 dk + dv, W] float32 ~ N(0, 1 / W) (channels of q, then k, then v; the last tap weights
+    the current token) and windows [N, H, 2 dk + dv, W - 1] ~ N(0, 1) in dtype, oldest first,
+    standing for the previous projections."""
+    device = torch.device(device)
+    gen = _gen(device, seed)
+    C = 2 * dk + dv
+    w = (_randn((H, C, W), gen, device) / W ** 0.5).float()
+    st = _randn((N, H, C, max(W - 1, 0)), gen, device).to(dtype)
+    return dict(conv_weight=w, conv_state=st)

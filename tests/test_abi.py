@@ -251,12 +251,13 @@ def test_recurrent_step_gate_rejects_on_host(lib):
 
 def _fused(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, z=FAKE, A=FAKE, b=FAKE, G=FAKE, w=None, eps=1e-6, S=FAKE * 16,
-             nc=None, N=4, K=3, H=2, dk=128, dv=128, ind=0, outd=0, y=FAKE * 64)
+             nc=None, N=4, K=3, H=2, dk=128, dv=128, ind=0, outd=0, y=FAKE * 64, cw=None,
+             cs=None, W=4)
     a.update(kw)
     return lib.kda_recurrent_multi_fused(a["q"], a["k"], a["v"], a["z"], a["A"], a["b"], a["G"],
-                                         a["w"], ctypes.c_float(a["eps"]), a["S"], a["nc"], a["N"],
-                                         a["K"], a["H"], a["dk"], a["dv"], a["ind"], a["outd"],
-                                         ctypes.c_float(1.0), a["y"], None)
+                                         a["w"], ctypes.c_float(a["eps"]), a["cw"], a["cs"], a["W"],
+                                         a["S"], a["nc"], a["N"], a["K"], a["H"], a["dk"], a["dv"],
+                                         a["ind"], a["outd"], ctypes.c_float(1.0), a["y"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -267,6 +268,11 @@ def _fused(lib, **kw):
     (dict(w=FAKE + 4), binding.KDA_ERR_INVALID_ARGUMENT),          # misaligned weight
     (dict(y=FAKE * 16 + 128), binding.KDA_ERR_INVALID_ARGUMENT),   # y overlaps S
     (dict(dk=32), binding.KDA_ERR_UNSUPPORTED),
+    (dict(cw=FAKE * 128, cs=FAKE * 256, W=5), binding.KDA_ERR_UNSUPPORTED),   # conv too wide
+    (dict(cw=FAKE * 128, cs=FAKE * 256, W=0), binding.KDA_ERR_UNSUPPORTED),
+    (dict(cw=FAKE * 128, cs=None), binding.KDA_ERR_INVALID_ARGUMENT),         # window needed
+    (dict(cw=FAKE * 128 + 2, cs=FAKE * 256), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(cw=FAKE * 128, cs=FAKE * 16 + 64), binding.KDA_ERR_INVALID_ARGUMENT),  # window over S
 ])
 def test_recurrent_multi_fused_rejects_on_host(lib, kw, status):
     assert _fused(lib, **kw) == status
@@ -276,6 +282,7 @@ def test_recurrent_multi_fused_rejects_on_host(lib, kw, status):
 def test_recurrent_multi_fused_empty_and_state_only_checks(lib):
     assert _fused(lib, K=0, q=None) == binding.KDA_OK
     assert _fused(lib, y=None, G=None, z=None) == binding.KDA_ERR_INVALID_ARGUMENT   # z still needed
+    assert _fused(lib, K=0, q=None, cw=FAKE * 128, cs=None, W=1) == binding.KDA_OK  # no window at W 1
 
 
 @pytest.mark.parametrize("call,kw,names", [
@@ -289,6 +296,7 @@ def test_recurrent_multi_fused_empty_and_state_only_checks(lib):
     (_multi, dict(S=FAKE), (b"S", b"q")),
     (_fused, dict(S=FAKE), (b"S", b"q")),
     (_fused, dict(nc=FAKE * 64), (b"y", b"n_commit")),
+    (_fused, dict(cw=FAKE * 128, cs=FAKE), (b"conv_state", b"q")),   # window written over q
     (_gate, dict(ST=FAKE * 8 + 4096), (b"o", b"S_T")),               # two outputs
 ])
 def test_outputs_may_not_overlap_inputs_or_each_other(lib, call, kw, names):
