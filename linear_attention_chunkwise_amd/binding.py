@@ -116,6 +116,8 @@ def _on(device, fn, *args):
 
 
 def _require(t, name, device, dtype=None, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
     if not t.is_cuda or t.device != device:
         raise ValueError(f"{name} must be on {device}")
     if not t.is_contiguous():
@@ -126,44 +128,63 @@ def _require(t, name, device, dtype=None, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+class _Prefill:
+    """The checks and output allocation every prefill entry point shares: q, k [B,T,H,dk],
+    v [B,T,H,dv], beta [B,T,H] in q's dtype, the decay input (g float32, or the logits z in q's
+    dtype with A_log [H] float32), S0, cu_seqlens, and o / S_T made here unless given."""
+
+    def __init__(self, q, k, v, beta, S0, cu_seqlens, out_dtype, output_final_state, o, S_T,
+                 g=None, z=None, A_log=None):
+        self.dev = dev = q.device
+        self.B, self.T, self.H, self.dk = B, T, H, dk = q.shape
+        self.dv = dv = v.shape[-1]
+        dt = q.dtype
+        _require(q, "q", dev, dt)
+        _require(k, "k", dev, dt, (B, T, H, dk))
+        _require(v, "v", dev, dt, (B, T, H, dv))
+        if z is None:
+            _require(g, "g", dev, torch.float32, (B, T, H, dk))
+        else:
+            _require(z, "z", dev, dt, (B, T, H, dk))
+            _require(A_log, "A_log", dev, torch.float32, (H,))
+        _require(beta, "beta", dev, dt, (B, T, H))
+        if cu_seqlens is not None:
+            _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+            self.N = N = cu_seqlens.numel() - 1
+        else:
+            self.N = N = B
+        if S0 is not None:
+            _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
+        out_dtype = out_dtype or dt
+        if o is None:
+            o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+        else:
+            _require(o, "o", dev, out_dtype, (B, T, H, dv))
+        if S_T is None and output_final_state:
+            S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        elif S_T is not None:
+            _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
+        self.o, self.S_T = o, S_T
+
+    def sizes(self, q):
+        """B, T, H, N, dk, dv, in_dtype, out_dtype as the C calls take them."""
+        return (self.B, self.T, self.H, self.N, self.dk, self.dv, _dt(q), _dt(self.o))
+
+
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, scale: float = 1.0,
               out_dtype=None, output_final_state: bool = True, o=None, S_T=None):
     """KDA chunkwise prefill: returns (o [B,T,H,dv], S_T [N,H,dk,dv] float32 or None).
 
-    q, k [B,T,H,dk], v [B,T,H,dv], beta [B,T,H] share a dtype (bf16, or f32 at dk = 64);
-    g [B,T,H,dk] float32; S0 [N,H,dk,dv] float32 or None; cu_seqlens int32 [N+1] (device) with
-    B = 1 for packed sequences.  ``S_T`` may be passed as S0 itself to advance the state in
-    place.  ``out_dtype`` defaults to q's dtype."""
+    q, k [B,T,H,dk], v [B,T,H,dv], beta [B,T,H] share a dtype (bf16 or f32); g [B,T,H,dk]
+    float32; S0 [N,H,dk,dv] float32 or None; cu_seqlens int32 [N+1] (device) with B = 1 for
+    packed sequences.  ``S_T`` may be passed as S0 itself to advance the state in place.
+    ``out_dtype`` defaults to q's dtype."""
     lib = load()
-    dev = q.device
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _require(q, "q", dev, dt)
-    _require(k, "k", dev, dt, (B, T, H, dk))
-    _require(v, "v", dev, dt, (B, T, H, dv))
-    _require(g, "g", dev, torch.float32, (B, T, H, dk))
-    _require(beta, "beta", dev, dt, (B, T, H))
-    if cu_seqlens is not None:
-        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
-    if S0 is not None:
-        _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
-    out_dtype = out_dtype or dt
-    if o is None:
-        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
-    else:
-        _require(o, "o", dev, out_dtype, (B, T, H, dv))
-    if S_T is None and output_final_state:
-        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    elif S_T is not None:
-        _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
-    st = _on(dev, lib.kda_chunk_fwd, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(cu_seqlens),
-             B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T), _stream(dev))
+    a = _Prefill(q, k, v, beta, S0, cu_seqlens, out_dtype, output_final_state, o, S_T, g=g)
+    st = _on(a.dev, lib.kda_chunk_fwd, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
+             _p(cu_seqlens), *a.sizes(q), float(scale), _p(a.o), _p(a.S_T), _stream(a.dev))
     _check(st)
-    return o, S_T
+    return a.o, a.S_T
 
 
 def chunk_fwd_ckpt(q, k, v, g, beta, S0=None, cu_seqlens=None, *, interval: int, capacity: int,
@@ -174,40 +195,17 @@ def chunk_fwd_ckpt(q, k, v, g, beta, S0=None, cu_seqlens=None, *, interval: int,
     (j+1)*interval tokens; slots past a sequence's last whole interval are left as allocated
     (zeros when ckpt is created here).  Returns (o, S_T, ckpt)."""
     lib = load()
-    dev = q.device
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _require(q, "q", dev, dt)
-    _require(k, "k", dev, dt, (B, T, H, dk))
-    _require(v, "v", dev, dt, (B, T, H, dv))
-    _require(g, "g", dev, torch.float32, (B, T, H, dk))
-    _require(beta, "beta", dev, dt, (B, T, H))
-    if cu_seqlens is not None:
-        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
-    if S0 is not None:
-        _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
-    out_dtype = out_dtype or dt
-    if o is None:
-        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
-    else:
-        _require(o, "o", dev, out_dtype, (B, T, H, dv))
-    if S_T is None and output_final_state:
-        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    elif S_T is not None:
-        _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
+    a = _Prefill(q, k, v, beta, S0, cu_seqlens, out_dtype, output_final_state, o, S_T, g=g)
+    shape = (a.N, a.H, capacity, a.dk, a.dv)
     if ckpt is None:
-        ckpt = torch.zeros((N, H, capacity, dk, dv), dtype=torch.float32, device=dev)
+        ckpt = torch.zeros(shape, dtype=torch.float32, device=a.dev)
     else:
-        _require(ckpt, "ckpt", dev, torch.float32, (N, H, capacity, dk, dv))
-    st = _on(dev, lib.kda_chunk_fwd_ckpt, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
-             _p(cu_seqlens), B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
-             int(interval), int(capacity), _p(ckpt), _stream(dev))
+        _require(ckpt, "ckpt", a.dev, torch.float32, shape)
+    st = _on(a.dev, lib.kda_chunk_fwd_ckpt, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
+             _p(cu_seqlens), *a.sizes(q), float(scale), _p(a.o), _p(a.S_T), int(interval),
+             int(capacity), _p(ckpt), _stream(a.dev))
     _check(st)
-    return o, S_T, ckpt
+    return a.o, a.S_T, ckpt
 
 
 def cp_segments(n_units: int, dk: int, dv: int, slots: int = 256) -> int:
@@ -221,40 +219,15 @@ def chunk_fwd_cp(q, k, v, g, beta, S0=None, cu_seqlens=None, *, segments: int, s
     """chunk_fwd with each sequence split in time into ``segments`` pieces run in parallel
     (workspace allocated here unless given as a uint8 device tensor).  Returns (o, S_T)."""
     lib = load()
-    dev = q.device
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _require(q, "q", dev, dt)
-    _require(k, "k", dev, dt, (B, T, H, dk))
-    _require(v, "v", dev, dt, (B, T, H, dv))
-    _require(g, "g", dev, torch.float32, (B, T, H, dk))
-    _require(beta, "beta", dev, dt, (B, T, H))
-    if cu_seqlens is not None:
-        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
-    if S0 is not None:
-        _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
-    out_dtype = out_dtype or dt
-    if o is None:
-        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
-    else:
-        _require(o, "o", dev, out_dtype, (B, T, H, dv))
-    if S_T is None and output_final_state:
-        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    elif S_T is not None:
-        _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
-    need = lib.kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, int(segments))
+    a = _Prefill(q, k, v, beta, S0, cu_seqlens, out_dtype, output_final_state, o, S_T, g=g)
+    need = lib.kda_chunk_fwd_cp_workspace_size(a.N, a.H, a.dk, a.dv, int(segments))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    st = _on(dev, lib.kda_chunk_fwd_cp, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
-             _p(cu_seqlens), B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
-             int(segments), _p(workspace), workspace.numel() * workspace.element_size(),
-             _stream(dev))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.dev)
+    st = _on(a.dev, lib.kda_chunk_fwd_cp, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
+             _p(cu_seqlens), *a.sizes(q), float(scale), _p(a.o), _p(a.S_T), int(segments),
+             _p(workspace), workspace.numel() * workspace.element_size(), _stream(a.dev))
     _check(st)
-    return o, S_T
+    return a.o, a.S_T
 
 
 def recurrent_step(q, k, v, g, beta, S, *, scale: float = 1.0, out_dtype=None, o=None):
@@ -319,37 +292,13 @@ def chunk_fwd_gate(q, k, v, z, A_log, beta, S0=None, cu_seqlens=None, *, scale: 
     """chunk_fwd with the decay map in the kernel: g = -5 Sigmoid(exp(A_log[h]) z) is formed from
     the logits z [B,T,H,dk] (q's dtype) and A_log [H] float32 instead of being read."""
     lib = load()
-    dev = q.device
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dt = q.dtype
-    _require(q, "q", dev, dt)
-    _require(k, "k", dev, dt, (B, T, H, dk))
-    _require(v, "v", dev, dt, (B, T, H, dv))
-    _require(z, "z", dev, dt, (B, T, H, dk))
-    _require(A_log, "A_log", dev, torch.float32, (H,))
-    _require(beta, "beta", dev, dt, (B, T, H))
-    if cu_seqlens is not None:
-        _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
-        N = cu_seqlens.numel() - 1
-    else:
-        N = B
-    if S0 is not None:
-        _require(S0, "S0", dev, torch.float32, (N, H, dk, dv))
-    out_dtype = out_dtype or dt
-    if o is None:
-        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
-    else:
-        _require(o, "o", dev, out_dtype, (B, T, H, dv))
-    if S_T is None and output_final_state:
-        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    elif S_T is not None:
-        _require(S_T, "S_T", dev, torch.float32, (N, H, dk, dv))
-    st = _on(dev, lib.kda_chunk_fwd_gate, _p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta), _p(S0),
-             _p(cu_seqlens), B, T, H, N, dk, dv, _dt(q), _dt(o), float(scale), _p(o), _p(S_T),
-             _stream(dev))
+    a = _Prefill(q, k, v, beta, S0, cu_seqlens, out_dtype, output_final_state, o, S_T, z=z,
+                 A_log=A_log)
+    st = _on(a.dev, lib.kda_chunk_fwd_gate, _p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta),
+             _p(S0), _p(cu_seqlens), *a.sizes(q), float(scale), _p(a.o), _p(a.S_T),
+             _stream(a.dev))
     _check(st)
-    return o, S_T
+    return a.o, a.S_T
 
 
 def recurrent_step_gate(q, k, v, z, A_log, beta, S, *, scale: float = 1.0, out_dtype=None, o=None):
