@@ -11,7 +11,8 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library allocates no
- *    device memory and keeps no pointer after the call's work has run on `stream`.
+ *    device memory and keeps no pointer after the call's work has run on `stream`.  (The one
+ *    fixed array it owns, behind kda_chunk_fwd_cp_noalloc, is part of its code object.)
  *  - Dense row-major layouts, token-major with heads interleaved ("B, T, H, d"):
  *      q, k  [B, T, H, dk]     v, o  [B, T, H, dv]     g [B, T, H, dk] (float32)
  *      beta  [B, T, H]         S0, S_T [N, H, dk, dv] (float32)
@@ -26,8 +27,10 @@
  *    host.  All argument checks run on the host before any launch: on error nothing is enqueued.
  *  - Results are deterministic: no atomics, fixed reduction orders.
  *  - Thread-safe and re-entrant.  The only process-wide state is a per-device record of which
- *    prefill kernels have had their LDS limit raised (set once, idempotent) and the flag of the
- *    optional domain check below (used under a lock); error text is per thread.
+ *    prefill kernels have had their LDS limit raised (set once, idempotent), the flag of the
+ *    optional domain check below (used under a lock) and the per-device address of the fixed
+ *    array of kda_chunk_fwd_cp_noalloc (looked up once, under a lock; the array's contents are
+ *    shared by that entry point's calls, see there); error text is per thread.
  *  - Domain check (a debug aid, off by default): with the environment variable KDA_CHECK_RANGE=1,
  *    every entry point that reads g first checks on `stream` that each value lies in [-5, 0]
  *    (eq. (5) and the bound after it; NaN fails), synchronises `stream` to read the result, and
@@ -170,6 +173,26 @@ kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const f
                             kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
                             float* S_T, int32_t segments, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/* Bytes of the fixed device array behind kda_chunk_fwd_cp_noalloc (32 MiB). */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* kda_chunk_fwd_cp for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and results
+ * bit for bit, with the segment summaries kept in a fixed array of KDA_NOALLOC_SCRATCH_BYTES that
+ * each device's copy of the library holds from its first use there until the process ends.  The
+ * call allocates nothing (no hipMalloc, no hipFree); the caller still passes inputs and outputs.
+ * The array is written by pass 1 before pass 2 reads it, so nothing needs clearing between calls.
+ * All calls on one device share that device's array: calls that may overlap in time on one
+ * device (different streams, or other host threads) race on it and must be serialised by the
+ * caller.  kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments) must not exceed
+ * KDA_NOALLOC_SCRATCH_BYTES (KDA_ERR_UNSUPPORTED otherwise, checked before anything runs).
+ * Other arguments, checks and results as kda_chunk_fwd_cp. */
+kda_status kda_chunk_fwd_cp_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                    int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk,
+                                    int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
+                                    void* o, float* S_T, int32_t segments, hipStream_t stream);
 
 /* One decode token per (sequence, head), state updated IN PLACE (§5.4.2: at decode the state is
  * advanced in place every step and its traffic dominates).  eq. (1) with T = 1:

@@ -20,6 +20,7 @@ KDA_BF16, KDA_F32 = 0, 1
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_gate", "kda_chunk_fwd_cp",
+           "kda_chunk_fwd_cp_noalloc",
            "kda_chunk_fwd_cp_workspace_size", "kda_chunk_fwd_cp_segments", "kda_recurrent_step",
            "kda_recurrent_step_gate",
            "kda_recurrent_multi", "kda_recurrent_multi_fused", "kda_status_string",
@@ -55,6 +56,10 @@ def load(path: str = LIB_PATH):
                                      ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, i32, vp,
                                      ctypes.c_size_t, vp]
     lib.kda_chunk_fwd_cp.restype = ctypes.c_int
+    lib.kda_chunk_fwd_cp_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                             i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, vp,
+                                             vp, i32, vp]
+    lib.kda_chunk_fwd_cp_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_cp_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.kda_chunk_fwd_cp_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_cp_segments.argtypes = [i32, i32, i32, i32, i32]
@@ -285,6 +290,21 @@ def recurrent_multi(q, k, v, g, beta, S, n_commit=None, *, scale: float = 1.0, o
              float(scale), _p(o), _stream(dev))
     _check(st)
     return o
+
+
+def chunk_fwd_cp_noalloc(q, k, v, g, beta, S0=None, cu_seqlens=None, *, segments: int,
+                         scale: float = 1.0, out_dtype=None, output_final_state: bool = True, o=None,
+                         S_T=None):
+    """chunk_fwd_cp with the segment summaries in the library's fixed per-device array instead of
+    a workspace: the C call allocates nothing (o and S_T are made here unless given).  Calls
+    that overlap in time on one device race on that array.  Returns (o, S_T)."""
+    lib = load()
+    a = _Prefill(q, k, v, beta, S0, cu_seqlens, out_dtype, output_final_state, o, S_T, g=g)
+    st = _on(a.dev, lib.kda_chunk_fwd_cp_noalloc, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
+             _p(cu_seqlens), *a.sizes(q), float(scale), _p(a.o), _p(a.S_T), int(segments),
+             _stream(a.dev))
+    _check(st)
+    return a.o, a.S_T
 
 
 def chunk_fwd_gate(q, k, v, z, A_log, beta, S0=None, cu_seqlens=None, *, scale: float = 1.0,

@@ -5,10 +5,22 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kda.h"
 #include "kda_launch.h"
 
 namespace {
+
+// Segment summaries of kda_chunk_fwd_cp_noalloc: a fixed array in each device's copy of the code
+// object, so that the call itself allocates nothing.  Host code never uses the name as an
+// address (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, looked up once per device and kept in g_scratch_dev.
+constexpr size_t kScratchBytes = KDA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_lock;
+void* g_scratch_dev[kMaxDevices] = {};
 
 thread_local char g_last_error[512] = "";
 
@@ -316,6 +328,45 @@ kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const f
                             hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, g, nullptr, nullptr, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
                           scale, o, S_T, 0, 0, nullptr, segments, workspace, workspace_bytes, stream);
+}
+
+// The scratch array's address on the current device (looked up on the first call there).
+static kda_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KDA_ERR_UNSUPPORTED, "%s = %lld: beyond the devices this library tracks", "device", dev);
+    const std::lock_guard<std::mutex> hold(g_scratch_lock);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return fail(KDA_ERR_HIP, "%s: hipGetSymbolAddress gave no address%.0lld", "scratch");
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_cp_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                    int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk,
+                                    int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
+                                    void* o, float* S_T, int32_t segments, hipStream_t stream) {
+    void* ws = nullptr;
+    if (segments > 1) {
+        const size_t need = kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments);
+        if (need > kScratchBytes)
+            return fail(KDA_ERR_UNSUPPORTED,
+                        "%s: the summaries need %lld bytes, beyond the fixed 32 MiB of the no-allocation "
+                        "variant (use kda_chunk_fwd_cp with a workspace, or fewer segments)",
+                        "segments", need == SIZE_MAX ? -1LL : (long long)need);
+        if (need > 0) KDA_TRY(scratch_on_current_device(&ws));
+    }
+    return chunk_fwd_impl(q, k, v, g, nullptr, nullptr, beta, S0, cu_seqlens, B, T, H, N, dk, dv,
+                          in_dtype, out_dtype, scale, o, S_T, 0, 0, nullptr, segments, ws,
+                          ws ? kScratchBytes : 0, stream);
 }
 
 static kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const float* g,

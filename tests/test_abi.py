@@ -155,6 +155,37 @@ def _cp(lib, **kw):
                                 a["wsb"], None)
 
 
+def _cp_noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2, N=1,
+             dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None, segs=2)
+    a.update(kw)
+    return lib.kda_chunk_fwd_cp_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"],
+                                        a["B"], a["T"], a["H"], a["N"], a["dk"], a["dv"], a["ind"],
+                                        a["outd"], ctypes.c_float(a["scale"]), a["o"], a["ST"],
+                                        a["segs"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=256, segs=8), binding.KDA_ERR_UNSUPPORTED),       # 235 MiB of summaries > 32 MiB
+    (dict(H=1 << 14, segs=1 << 14), binding.KDA_ERR_UNSUPPORTED),  # size saturates
+    (dict(segs=0), binding.KDA_ERR_INVALID_ARGUMENT),
+    (dict(segs=1, o=FAKE), binding.KDA_ERR_INVALID_ARGUMENT),  # o over q: checked as for _cp
+    (dict(segs=1, dk=96), binding.KDA_ERR_UNSUPPORTED),
+])
+def test_cp_noalloc_rejects_on_host(lib, kw, status):
+    """Checked before the fixed array is looked up or anything is enqueued."""
+    assert _cp_noalloc(lib, **kw) == status
+    assert lib.kda_last_error() != b""
+
+
+def test_cp_noalloc_limit_is_the_header_constant(lib):
+    fit = lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 9)      # 8 x 32 x 128 KiB
+    assert fit == 32 << 20
+    assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 10) > 32 << 20
+    assert _cp_noalloc(lib, H=32, segs=10) == binding.KDA_ERR_UNSUPPORTED
+    assert b"32 MiB" in lib.kda_last_error()
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(T=0, H=1 << 14, segs=1 << 15), binding.KDA_ERR_UNSUPPORTED),   # grid too large
     (dict(segs=0), binding.KDA_ERR_INVALID_ARGUMENT),
