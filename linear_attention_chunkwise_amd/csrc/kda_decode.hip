@@ -242,21 +242,26 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(const void* __restric
     }
 }
 
-// The multi-token step fused with the weight-free steps around it (§2.1.1): before the recurrence,
-// eq. (2)'s L2Norm of q and k (x / max(||x||, 1e-12)), beta = Sigmoid of its logit and the bounded
-// decay map of eq. (5); after it, eq. (6) without W_o: y = Sigmoid(G) * RMSNorm(o~) per head, with
-// RMSNorm(o~) = o~ / sqrt(mean(o~^2) + eps) * w.  The normalisations need two more dk
-// reductions per token (q . q, k . k, finished with the others) and one dv reduction (o~ . o~,
-// inside each row group's lanes).  Same mapping and commit rule as decode_multi_kernel.  The
-// decay map runs once per (token, channel) into LDS instead of in every thread that holds the
-// channel's row, and k is read again for the state update rather than held across the barrier:
-// with those, three waves per SIMD fit (1194 -> 882 us for 4 tokens at 1024 x 32 heads).
+// The multi-token step fused with the steps the model applies around it (§2.1.1): before the
+// recurrence, optionally eq. (2)'s short convolution and Swish on q, k, v (CONV), then its L2Norm
+// of q and k (x / max(||x||, 1e-12)), beta = Sigmoid of its logit and the bounded decay map of
+// eq. (5); after it, eq. (6) without W_o: y = Sigmoid(G) * RMSNorm(o~) per head, with
+// RMSNorm(o~) = o~ / sqrt(mean(o~^2) + eps) * w.  Same mapping and commit rule as
+// decode_multi_kernel.
 //
-// CONV: q, k, v are the projections before eq. (2)'s short convolution.  Each of the 2 dk + dv
-// channels (q's, then k's, then v's) is owned by one thread, which keeps the channel's last
-// W - 1 inputs in registers, forms Swish(sum_j w_j x_{t-W+1+j}) a token ahead into LDS (read there
-// by the recurrence in place of q, k, v) and writes its window back to conv_state after the
-// committed prefix, together with S.
+// None of the steps before the recurrence depend on the state, so they run for a group of KB
+// tokens at once, ahead of the serial token loop, and leave LDS holding the recurrence's inputs
+// ready to use (normalised q and k, v, exp(g), beta, q . k, Sigmoid(G)).  For the first group
+// the input loads are issued before the state's, and the preparation runs while the state is
+// still arriving from HBM (vector loads complete in issue order, so loads issued after the
+// state's would wait for it).  The token loop is then the plain multi-token loop plus the
+// output norm.
+//
+// CONV: thread t owns channels t and t + 256 (when < 2 dk + dv; q's channels, then k's, then
+// v's).  A channel's taps and window sit in its own row of cwt, used by its owner only, kept
+// right-aligned (zeros on the left when W < 4): y = w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3},
+// cwt[c] = {w0, w1, w2, w3, x_{t-3}, x_{t-2}, x_{t-1}, unused}.  The window is written back to
+// conv_state after the committed prefix, together with S.
 template <int DK, int DV, bool IN_F32, bool OUT_F32, bool CONV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_fused_kernel(const void* __restrict__ qp,
                                                            const void* __restrict__ kp,
@@ -275,62 +280,156 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     constexpr int CG = DV / 4;
     constexpr int NRG = 256 / CG;
     constexpr int RPG = DK / NRG;
-    constexpr int NCH = 2 * DK + DV;  // convolved channels
-    static_assert(RPG >= 1 && DK % NRG == 0 && 64 % CG == 0, "decode tiling");
-    static_assert(NCH <= 512, "two convolved channels per thread at most");
+    constexpr int NCH = 2 * DK + DV;   // q, k, v channels
+    constexpr int KB = 4;              // tokens prepared per group: one wave each for the norms
+    constexpr int ZPT = KB * DK / 256; // decay logits per thread in a group
+    constexpr int GPT = KB * DV / 256; // gate inputs per thread in a group
+    static_assert(RPG >= 4 && RPG % 4 == 0 && DK % NRG == 0 && 64 % CG == 0, "decode tiling");
+    static_assert(NCH <= 512 && ZPT >= 1 && GPT >= 1, "two channels per thread at most");
     __shared__ f32x4 red_y[2][NRG][CG];
     __shared__ f32x4 red_z[2][NRG][CG];
-    __shared__ f32x4 red_s[2][NRG];   // q . k, q . q, k . k (and one spare) per row group
-    __shared__ float dec[2][DK];      // per-channel decay exp(g) of a token, by token parity
-    __shared__ float cin[CONV ? 3 : 1][CONV ? NCH : 1];   // convolved q, k, v of a token, rotating
-    __shared__ __align__(16) float cwt[CONV ? NCH : 1][8];  // taps and window per channel
+    __shared__ __align__(16) float xin[KB][NCH];   // q^, k^ (normalised) and v of the group
+    __shared__ __align__(16) float dec[KB][DK];    // exp(g)
+    __shared__ __align__(16) float sgate[KB][DV];  // Sigmoid(G)
+    __shared__ float tb[KB][2];                    // beta, q^ . k^
+    __shared__ __align__(16) float cwt[CONV ? NCH : 1][8];
 
     const int unit = blockIdx.x;        // sequence * H + head
     if (unit >= N * H) return;
     KDA_POISON(red_y, sizeof red_y);
     KDA_POISON(red_z, sizeof red_z);
-    KDA_POISON(red_s, sizeof red_s);
+    KDA_POISON(xin, sizeof xin);
     KDA_POISON(dec, sizeof dec);
-    KDA_POISON(cin, sizeof cin);
+    KDA_POISON(sgate, sizeof sgate);
+    KDA_POISON(tb, sizeof tb);
     KDA_POISON(cwt, sizeof cwt);
     KDA_POISON_DONE();
     const int n = unit / H, h = unit % H;
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;
     const int r0 = rg * RPG;
+    const int wv = t / 64, lane = t % 64;
     int commit = n_commit ? n_commit[n] : K;
     commit = commit < 0 ? 0 : (commit > K ? K : commit);
     const float ea = __expf(A_log[h]);
-    f32x4 w = f32x4{1.f, 1.f, 1.f, 1.f};
-    if (norm_w) w = ld<f32x4>(norm_w + 4 * cg);
-
-    float* Su = S + (size_t)unit * DK * DV;
-    f32x4 s[RPG];
-#pragma unroll
-    for (int i = 0; i < RPG; ++i) s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
 
     auto in_at = [&](const void* p, size_t idx) -> float {
         if constexpr (IN_F32) return reinterpret_cast<const float*>(p)[idx];
         else return bf2f(reinterpret_cast<const bf16*>(p)[idx]);
     };
     auto sigm = [](float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); };
-    // the decay map once per (token, channel), a token ahead: written before the barrier that
-    // precedes its use; the buffer it overwrites was last read before the previous barrier
-    auto decay_into = [&](int tok, int buf) {
-        if (t < DK) dec[buf][t] = decay_at<IN_F32, true>(nullptr, zp, ea, (((size_t)n * K + tok) * H + h) * DK + t);
-    };
-    // CONV: thread t owns channels t and t + 256 (when < NCH).  A channel's taps and window sit in
-    // its own row of cwt, read and written by its owner only (no barrier needed), right-aligned
-    // (zeros on the left when W < 4) so that y = w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3}
-    // with fixed offsets: cwt[c] = {w0, w1, w2, w3, x_{t-3}, x_{t-2}, x_{t-1}, unused}.
+    auto row_of = [&](int tok) { return ((size_t)n * K + tok) * H + h; };   // token row of [N, K, H, *]
+    // channel c of the [N, K, H, d] inputs: where token 0 sits and the token stride
     auto chan = [&](int c, const void*& src, size_t& at, size_t& stride) {
-        // q channels [0, DK), k channels [DK, 2 DK), v channels [2 DK, NCH); [N, K, H, d] layout
         const int part = c < DK ? 0 : (c < 2 * DK ? 1 : 2);
         const int d = part < 2 ? DK : DV;
         src = part == 0 ? qp : (part == 1 ? kp : vp);
         stride = (size_t)H * d;
         at = ((size_t)n * K * H + h) * d + (c - part * DK);
     };
+
+    // a group's inputs, loaded to registers
+    float xr[2][KB], zr[ZPT], gr[GPT], br = 0.f;
+    auto load_group = [&](int t0, int kb) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int c = t + 256 * e;
+            const void* src;
+            size_t at, stride;
+            chan(c < NCH ? c : 0, src, at, stride);
+#pragma unroll
+            for (int j = 0; j < KB; ++j) xr[e][j] = (c < NCH && j < kb) ? in_at(src, at + (size_t)(t0 + j) * stride) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < ZPT; ++i) {
+            const int idx = t + 256 * i, j = idx / DK, c = idx % DK;
+            zr[i] = j < kb ? in_at(zp, row_of(t0 + j) * DK + c) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int idx = t + 256 * i, j = idx / DV, c = idx % DV;
+            gr[i] = (op && j < kb) ? in_at(Gp, row_of(t0 + j) * DV + c) : 0.f;
+        }
+        br = t < kb ? in_at(bp, row_of(t0 + t)) : 0.f;
+    };
+    // everything before the recurrence for the group's tokens, into LDS
+    auto prep_group = [&](int t0, int kb) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int c = t + 256 * e;
+            if (c >= NCH) continue;
+            if constexpr (CONV) {
+                const f32x4 tp = *reinterpret_cast<const f32x4*>(&cwt[c][0]);
+                f32x4 wn = *reinterpret_cast<const f32x4*>(&cwt[c][4]);
+                const size_t so = (((size_t)n * H + h) * NCH + c) * (W - 1);
+#pragma unroll
+                for (int j = 0; j < KB; ++j) {
+                    if (j < kb) {
+                        const float x = xr[e][j];
+                        const float y = tp[3] * x + tp[2] * wn[2] + tp[1] * wn[1] + tp[0] * wn[0];
+                        xin[j][c] = y * sigm(y);   // Swish
+                        wn = f32x4{wn[1], wn[2], x, 0.f};
+                        if (t0 + j + 1 == commit) {
+#pragma unroll
+                            for (int m = 0; m < 3; ++m) {
+                                if (m >= 4 - W) {
+                                    const size_t o = so + (m - (4 - W));
+                                    if constexpr (IN_F32) reinterpret_cast<float*>(conv_state)[o] = wn[m];
+                                    else reinterpret_cast<bf16*>(conv_state)[o] = f2bf(wn[m]);
+                                }
+                            }
+                        }
+                    }
+                }
+                *reinterpret_cast<f32x4*>(&cwt[c][4]) = wn;
+            } else {
+#pragma unroll
+                for (int j = 0; j < KB; ++j)
+                    if (j < kb) xin[j][c] = xr[e][j];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < ZPT; ++i) {
+            const int idx = t + 256 * i, j = idx / DK, c = idx % DK;
+            if (j < kb) dec[j][c] = __expf(kGmin * sigm(ea * zr[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int idx = t + 256 * i, j = idx / DV, c = idx % DV;
+            if (op && j < kb) sgate[j][c] = sigm(gr[i]);
+        }
+        if (t < kb) tb[t][0] = sigm(br);
+        __syncthreads();
+        // L2Norm of q and k: wave wv normalises token wv of the group in place
+        if (wv < kb) {
+            float qq = 0.f, kk = 0.f, qk = 0.f;
+#pragma unroll
+            for (int c = lane; c < DK; c += 64) {
+                const float qv = xin[wv][c], kv = xin[wv][DK + c];
+                qq += qv * qv;
+                kk += kv * kv;
+                qk += qv * kv;
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m /= 2) {
+                qq += __shfl_xor(qq, m, 64);
+                kk += __shfl_xor(kk, m, 64);
+                qk += __shfl_xor(qk, m, 64);
+            }
+            const float rq = 1.f / fmaxf(sqrtf(qq), 1e-12f);
+            const float rk = 1.f / fmaxf(sqrtf(kk), 1e-12f);
+#pragma unroll
+            for (int c = lane; c < DK; c += 64) {
+                xin[wv][c] *= rq;
+                xin[wv][DK + c] *= rk;
+            }
+            if (lane == 0) tb[wv][1] = qk * rq * rk;
+        }
+        __syncthreads();
+    };
+
+    f32x4 w = f32x4{1.f, 1.f, 1.f, 1.f};
+    if (norm_w) w = ld<f32x4>(norm_w + 4 * cg);
     if constexpr (CONV) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -350,111 +449,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             }
         }
     }
-    // convolved inputs of token tok into cin[buf]; the window is stored once the committed tokens
-    // are in it
-    auto conv_into = [&](int tok, int buf) {
+    load_group(0, K < KB ? K : KB);
+    // the state, after the first group's inputs (see above)
+    float* Su = S + (size_t)unit * DK * DV;
+    f32x4 s[RPG];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int c = t + 256 * e;
-            if (c < NCH) {
-                const void* src;
-                size_t at, stride;
-                chan(c, src, at, stride);
-                const float x = in_at(src, at + (size_t)tok * stride);
-                const f32x4 tp = *reinterpret_cast<const f32x4*>(&cwt[c][0]);
-                f32x4 wn = *reinterpret_cast<const f32x4*>(&cwt[c][4]);
-                const float y = tp[3] * x + tp[2] * wn[2] + tp[1] * wn[1] + tp[0] * wn[0];
-                cin[buf][c] = y * sigm(y);                  // Swish
-                wn = f32x4{wn[1], wn[2], x, 0.f};
-                *reinterpret_cast<f32x4*>(&cwt[c][4]) = wn;
-                if (tok + 1 == commit) {
-                    const size_t so = (((size_t)n * H + h) * NCH + c) * (W - 1);
+    for (int i = 0; i < RPG; ++i) s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
+
+    for (int t0 = 0;;) {
+        const int kb = K - t0 < KB ? K - t0 : KB;
+        prep_group(t0, kb);
+        for (int j = 0; j < kb; ++j) {
+            const int tok = t0 + j;
+            const int pb = tok & 1;
+            f32x4 y = zero4(), z = zero4();
 #pragma unroll
-                    for (int j = 0; j < 3; ++j) {
-                        if (j >= 4 - W) {
-                            const size_t o = so + (j - (4 - W));
-                            if constexpr (IN_F32) reinterpret_cast<float*>(conv_state)[o] = wn[j];
-                            else reinterpret_cast<bf16*>(conv_state)[o] = f2bf(wn[j]);
-                        }
-                    }
+            for (int i4 = 0; i4 < RPG; i4 += 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(&dec[j][r0 + i4]);
+                const f32x4 kv = *reinterpret_cast<const f32x4*>(&xin[j][DK + r0 + i4]);
+                const f32x4 qv = *reinterpret_cast<const f32x4*>(&xin[j][r0 + i4]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    s[i4 + m] *= a[m];
+                    y += kv[m] * s[i4 + m];
+                    z += qv[m] * s[i4 + m];
                 }
             }
-        }
-    };
-    // cin rotates over three buffers: a token's convolved k and v are read after the barrier too,
-    // so the buffer written a token ahead must be the one read two tokens back (a barrier between)
-    int cb = 0;
-    decay_into(0, 0);
-    if constexpr (CONV) conv_into(0, 0);
-    __syncthreads();
-    for (int tok = 0; tok < K; ++tok) {
-        const int pb = tok & 1;
-        const int cn = cb == 2 ? 0 : cb + 1;
-        const size_t row = ((size_t)n * K + tok) * H + h;   // token row of [N, K, H, *]
-        const size_t kb = row * DK;
-        if (tok + 1 < K) {
-            decay_into(tok + 1, pb ^ 1);
-            if constexpr (CONV) conv_into(tok + 1, cn);
-        }
-        // q, k, v of the token: as given, or (CONV) convolved, from LDS
-        auto q_at = [&](int r) { if constexpr (CONV) return cin[cb][r]; else return in_at(qp, kb + r); };
-        auto k_at = [&](int r) { if constexpr (CONV) return cin[cb][DK + r]; else return in_at(kp, kb + r); };
-        f32x4 y = zero4(), z = zero4();
-        float qk = 0.f, qq = 0.f, kk = 0.f;
+            red_y[pb][rg][cg] = y;
+            red_z[pb][rg][cg] = z;
+            __syncthreads();   // the other parity's buffers were last read before this barrier
+            f32x4 yt = zero4(), zt = zero4();
 #pragma unroll
-        for (int i = 0; i < RPG; ++i) {
-            const float a = dec[pb][r0 + i];
-            const float kvi = k_at(r0 + i);
-            const float qv = q_at(r0 + i);
-            s[i] *= a;
-            y += kvi * s[i];
-            z += qv * s[i];
-            qk += qv * kvi;
-            qq += qv * qv;
-            kk += kvi * kvi;
-        }
-        red_y[pb][rg][cg] = y;
-        red_z[pb][rg][cg] = z;
-        if (cg == 0) red_s[pb][rg] = f32x4{qk, qq, kk, 0.f};
-        __syncthreads();   // the other parity's buffers were last read before this barrier
-        f32x4 yt = zero4(), zt = zero4(), st4 = zero4();
+            for (int m = 0; m < NRG; ++m) {
+                yt += red_y[pb][m][cg];
+                zt += red_z[pb][m][cg];
+            }
+            const f32x4 vv = *reinterpret_cast<const f32x4*>(&xin[j][2 * DK + 4 * cg]);
+            const f32x4 u = tb[j][0] * (vv - yt);
 #pragma unroll
-        for (int j = 0; j < NRG; ++j) {
-            yt += red_y[pb][j][cg];
-            zt += red_z[pb][j][cg];
-            st4 += red_s[pb][j];
-        }
-        // L2Norm of q and k as scale factors on the sums (and on k in the state update)
-        const float rq = 1.f / fmaxf(sqrtf(st4[1]), 1e-12f);
-        const float rk = 1.f / fmaxf(sqrtf(st4[2]), 1e-12f);
-        const float b = sigm(in_at(bp, row));
-        const size_t vb = row * DV + 4 * cg;
-        f32x4 u;
+            for (int i4 = 0; i4 < RPG; i4 += 4) {
+                const f32x4 kv = *reinterpret_cast<const f32x4*>(&xin[j][DK + r0 + i4]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float vv;
-            if constexpr (CONV) vv = cin[cb][2 * DK + 4 * cg + c];
-            else vv = in_at(vp, vb + c);
-            u[c] = b * (vv - yt[c] * rk);
-        }
+                for (int m = 0; m < 4; ++m) s[i4 + m] += kv[m] * u;
+            }
+            if (tok + 1 == commit) {
 #pragma unroll
-        for (int i = 0; i < RPG; ++i) s[i] += (k_at(r0 + i) * rk) * u;   // k re-read (cached)
-        if (tok + 1 == commit) {
+                for (int i = 0; i < RPG; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
+            }
+            if (op && rg == 0) {
+                // o~ for this thread's 4 columns, then RMSNorm over dv across the CG lanes of row
+                // group 0 (within one wave) and the gate
+                const f32x4 o = scale * (zt + tb[j][1] * u);
+                float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
 #pragma unroll
-            for (int i = 0; i < RPG; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
-        }
-        if (op) {
-            // o~ for this thread's 4 columns, then RMSNorm over dv across the CG lanes of the row
-            // group (one wave holds whole row groups) and the gate
-            const f32x4 o = scale * (zt * rq + (st4[0] * rq * rk) * u);
-            float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-#pragma unroll
-            for (int m = 1; m < CG; m *= 2) ss += __shfl_xor(ss, m, 64);
-            const float inv = rsqrtf(ss / DV + eps);
-            if (rg == 0) {
-                f32x4 yo;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) yo[c] = sigm(in_at(Gp, vb + c)) * (o[c] * inv * w[c]);
+                for (int m = 1; m < CG; m *= 2) ss += __shfl_xor(ss, m, 64);
+                const float inv = rsqrtf(ss / DV + eps);
+                const f32x4 gt = *reinterpret_cast<const f32x4*>(&sgate[j][4 * cg]);
+                const f32x4 yo = gt * (o * inv * w);
+                const size_t vb = row_of(tok) * DV + 4 * cg;
                 if constexpr (OUT_F32) {
                     st<f32x4>(reinterpret_cast<float*>(op) + vb, yo);
                 } else {
@@ -463,7 +515,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                 }
             }
         }
-        cb = cn;
+        t0 += KB;
+        if (t0 >= K) break;
+        load_group(t0, K - t0 < KB ? K - t0 : KB);
+        __syncthreads();   // the group's LDS is rewritten next
     }
 }
 
