@@ -288,11 +288,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     static_assert(NCH <= 512 && ZPT >= 1 && GPT >= 1, "two channels per thread at most");
     __shared__ f32x4 red_y[2][NRG][CG];
     __shared__ f32x4 red_z[2][NRG][CG];
-    __shared__ __align__(16) float xin[KB][NCH];   // q^, k^ (normalised) and v of the group
+    // Rows are padded to the 512 channels two per thread can name, and tb to one beta slot per
+    // thread, so that the preparation stores unconditionally: a loaded value used only under a
+    // per-thread condition gets sunk past the state's loads, and waiting for it would then wait
+    // for the state as well.
+    constexpr int XS = 512;
+    __shared__ __align__(16) float xin[KB][XS];    // q^, k^ (normalised) and v of the group
     __shared__ __align__(16) float dec[KB][DK];    // exp(g)
     __shared__ __align__(16) float sgate[KB][DV];  // Sigmoid(G)
-    __shared__ float tb[KB][2];                    // beta, q^ . k^
-    __shared__ __align__(16) float cwt[CONV ? NCH : 1][8];
+    __shared__ float bsig[256];                    // beta of the group's tokens (first KB)
+    __shared__ float tqk[KB];                      // q^ . k^
+    __shared__ __align__(16) float cwt[CONV ? XS : 1][8];
 
     const int unit = blockIdx.x;        // sequence * H + head
     if (unit >= N * H) return;
@@ -301,7 +307,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     KDA_POISON(xin, sizeof xin);
     KDA_POISON(dec, sizeof dec);
     KDA_POISON(sgate, sizeof sgate);
-    KDA_POISON(tb, sizeof tb);
+    KDA_POISON(bsig, sizeof bsig);
+    KDA_POISON(tqk, sizeof tqk);
     KDA_POISON(cwt, sizeof cwt);
     KDA_POISON_DONE();
     const int n = unit / H, h = unit % H;
@@ -313,70 +320,88 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     commit = commit < 0 ? 0 : (commit > K ? K : commit);
     const float ea = __expf(A_log[h]);
 
-    auto in_at = [&](const void* p, size_t idx) -> float {
-        if constexpr (IN_F32) return reinterpret_cast<const float*>(p)[idx];
-        else return bf2f(reinterpret_cast<const bf16*>(p)[idx]);
+    // Addressing: every tensor is reached from a workgroup-uniform base (the unit's token 0,
+    // head h) plus a 32-bit per-thread offset, so that addresses live in scalar registers and
+    // the loads take the base + 32-bit offset form; the vector registers go to the state.
+    constexpr int ES = IN_F32 ? 4 : 2;
+    const size_t tok0 = (size_t)n * K * H + h;            // row of (n, token 0, h) in [N, K, H]
+    const uint32_t HDK = (uint32_t)H * DK, HDV = (uint32_t)H * DV;
+    const char* const qb = static_cast<const char*>(qp) + tok0 * DK * ES;
+    const char* const kbp = static_cast<const char*>(kp) + tok0 * DK * ES;
+    const char* const vbp = static_cast<const char*>(vp) + tok0 * DV * ES;
+    const char* const zb = static_cast<const char*>(zp) + tok0 * DK * ES;
+    const char* const bb = static_cast<const char*>(bp) + tok0 * ES;
+    // without outputs G may be absent: z stands in (read, never used)
+    const char* const gb = op ? static_cast<const char*>(Gp) + tok0 * DV * ES : zb;
+    // element i past a uniform base; the byte offset is formed in 32 bits (the host keeps a
+    // unit's K tokens under 2^30 elements)
+    auto ldx = [&](const char* base, uint32_t i) -> float {
+        const char* p = base + i * (uint32_t)ES;
+        if constexpr (IN_F32) return *reinterpret_cast<const float*>(p);
+        else return bf2f(*reinterpret_cast<const bf16*>(p));
     };
     auto sigm = [](float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); };
-    auto row_of = [&](int tok) { return ((size_t)n * K + tok) * H + h; };   // token row of [N, K, H, *]
-    // channel c of the [N, K, H, d] inputs: where token 0 sits and the token stride
-    auto chan = [&](int c, const void*& src, size_t& at, size_t& stride) {
-        const int part = c < DK ? 0 : (c < 2 * DK ? 1 : 2);
-        const int d = part < 2 ? DK : DV;
-        src = part == 0 ? qp : (part == 1 ? kp : vp);
-        stride = (size_t)H * d;
-        at = ((size_t)n * K * H + h) * d + (c - part * DK);
+    // channel c of q | k | v: its base (uniform across a wave, as the three ranges are whole
+    // waves: dk and dv are multiples of 64), its offset within a token and the token stride
+    auto chan = [&](int c, const char*& src, uint32_t& off, uint32_t& stride) {
+        const int part = __builtin_amdgcn_readfirstlane(c < DK ? 0 : (c < 2 * DK ? 1 : 2));
+        src = part == 0 ? qb : (part == 1 ? kbp : vbp);
+        stride = part < 2 ? HDK : HDV;
+        off = (uint32_t)(c - part * DK);
     };
 
-    // a group's inputs, loaded to registers
+    // a group's inputs, loaded to registers.  Every load is unconditional, at an index clamped
+    // into range (values past the group or the channels are never used): a load under a
+    // per-thread condition is waited for where the branches join, one at a time.
     float xr[2][KB], zr[ZPT], gr[GPT], br = 0.f;
     auto load_group = [&](int t0, int kb) {
+        const int last = t0 + kb - 1;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int c = t + 256 * e;
-            const void* src;
-            size_t at, stride;
-            chan(c < NCH ? c : 0, src, at, stride);
+            const char* src;
+            uint32_t off, stride;
+            chan(c < NCH ? c : NCH - 1, src, off, stride);
 #pragma unroll
-            for (int j = 0; j < KB; ++j) xr[e][j] = (c < NCH && j < kb) ? in_at(src, at + (size_t)(t0 + j) * stride) : 0.f;
+            for (int j = 0; j < KB; ++j) xr[e][j] = ldx(src, (uint32_t)(t0 + j < last ? t0 + j : last) * stride + off);
         }
 #pragma unroll
         for (int i = 0; i < ZPT; ++i) {
             const int idx = t + 256 * i, j = idx / DK, c = idx % DK;
-            zr[i] = j < kb ? in_at(zp, row_of(t0 + j) * DK + c) : 0.f;
+            zr[i] = ldx(zb, (uint32_t)(t0 + j < last ? t0 + j : last) * HDK + c);
         }
 #pragma unroll
         for (int i = 0; i < GPT; ++i) {
             const int idx = t + 256 * i, j = idx / DV, c = idx % DV;
-            gr[i] = (op && j < kb) ? in_at(Gp, row_of(t0 + j) * DV + c) : 0.f;
+            gr[i] = ldx(gb, op ? (uint32_t)(t0 + j < last ? t0 + j : last) * HDV + c : 0u);
         }
-        br = t < kb ? in_at(bp, row_of(t0 + t)) : 0.f;
+        br = ldx(bb, (uint32_t)(t0 + t < last ? t0 + t : last) * H);
     };
-    // everything before the recurrence for the group's tokens, into LDS
+    // the unit's conv window rows: [N, H, NCH, W - 1]
+    char* const csb = CONV && W > 1 ? static_cast<char*>(conv_state) + ((size_t)n * H + h) * NCH * (W - 1) * ES : nullptr;
+    // everything before the recurrence for the group's tokens, into LDS (rows past the group
+    // and channels past NCH receive values that are never read)
     auto prep_group = [&](int t0, int kb) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int c = t + 256 * e;
-            if (c >= NCH) continue;
             if constexpr (CONV) {
                 const f32x4 tp = *reinterpret_cast<const f32x4*>(&cwt[c][0]);
                 f32x4 wn = *reinterpret_cast<const f32x4*>(&cwt[c][4]);
-                const size_t so = (((size_t)n * H + h) * NCH + c) * (W - 1);
 #pragma unroll
                 for (int j = 0; j < KB; ++j) {
-                    if (j < kb) {
-                        const float x = xr[e][j];
-                        const float y = tp[3] * x + tp[2] * wn[2] + tp[1] * wn[1] + tp[0] * wn[0];
-                        xin[j][c] = y * sigm(y);   // Swish
-                        wn = f32x4{wn[1], wn[2], x, 0.f};
-                        if (t0 + j + 1 == commit) {
+                    const float x = xr[e][j];
+                    const float y = tp[3] * x + tp[2] * wn[2] + tp[1] * wn[1] + tp[0] * wn[0];
+                    xin[j][c] = y * sigm(y);   // Swish
+                    const f32x4 rolled = f32x4{wn[1], wn[2], x, 0.f};
+                    wn = j < kb ? rolled : wn;
+                    if (c < NCH && t0 + j + 1 == commit) {
 #pragma unroll
-                            for (int m = 0; m < 3; ++m) {
-                                if (m >= 4 - W) {
-                                    const size_t o = so + (m - (4 - W));
-                                    if constexpr (IN_F32) reinterpret_cast<float*>(conv_state)[o] = wn[m];
-                                    else reinterpret_cast<bf16*>(conv_state)[o] = f2bf(wn[m]);
-                                }
+                        for (int m = 0; m < 3; ++m) {
+                            if (m >= 4 - W) {
+                                char* const o = csb + ((uint32_t)c * (W - 1) + (m - (4 - W))) * (uint32_t)ES;
+                                if constexpr (IN_F32) *reinterpret_cast<float*>(o) = wn[m];
+                                else *reinterpret_cast<bf16*>(o) = f2bf(wn[m]);
                             }
                         }
                     }
@@ -384,21 +409,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                 *reinterpret_cast<f32x4*>(&cwt[c][4]) = wn;
             } else {
 #pragma unroll
-                for (int j = 0; j < KB; ++j)
-                    if (j < kb) xin[j][c] = xr[e][j];
+                for (int j = 0; j < KB; ++j) xin[j][c] = xr[e][j];
             }
         }
 #pragma unroll
         for (int i = 0; i < ZPT; ++i) {
             const int idx = t + 256 * i, j = idx / DK, c = idx % DK;
-            if (j < kb) dec[j][c] = __expf(kGmin * sigm(ea * zr[i]));
+            dec[j][c] = __expf(kGmin * sigm(ea * zr[i]));
         }
 #pragma unroll
         for (int i = 0; i < GPT; ++i) {
             const int idx = t + 256 * i, j = idx / DV, c = idx % DV;
-            if (op && j < kb) sgate[j][c] = sigm(gr[i]);
+            sgate[j][c] = sigm(gr[i]);
         }
-        if (t < kb) tb[t][0] = sigm(br);
+        bsig[t] = sigm(br);
         __syncthreads();
         // L2Norm of q and k: wave wv normalises token wv of the group in place
         if (wv < kb) {
@@ -423,42 +447,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                 xin[wv][c] *= rq;
                 xin[wv][DK + c] *= rk;
             }
-            if (lane == 0) tb[wv][1] = qk * rq * rk;
+            if (lane == 0) tqk[wv] = qk * rq * rk;
         }
         __syncthreads();
     };
 
-    f32x4 w = f32x4{1.f, 1.f, 1.f, 1.f};
-    if (norm_w) w = ld<f32x4>(norm_w + 4 * cg);
+    // CONV: taps and entering window to registers (stored to cwt only after the state's loads
+    // are issued, so that nothing waits for them before); unconditional loads at clamped
+    // indices, as in load_group; with W = 1 there is no window (conv_state may be absent) and a
+    // tap stands in (read, never used)
+    f32x4 tp0[2], wn0[2];
     if constexpr (CONV) {
+        const float* const cwb = conv_w + (size_t)h * NCH * W;
+        const char* const wsb = W > 1 ? csb : reinterpret_cast<const char*>(cwb);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int c = t + 256 * e;
-            if (c < NCH) {
-                const float* wrow = conv_w + ((size_t)h * NCH + c) * W;
-                const size_t so = (((size_t)n * H + h) * NCH + c) * (W - 1);
-                f32x4 tp = zero4(), wn = zero4();
+            const uint32_t c = t + 256 * e < NCH ? t + 256 * e : NCH - 1;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (j >= 4 - W) tp[j] = wrow[j - (4 - W)];
-#pragma unroll
-                for (int j = 0; j < 3; ++j)
-                    if (j >= 4 - W) wn[j] = in_at(conv_state, so + (j - (4 - W)));
-                *reinterpret_cast<f32x4*>(&cwt[c][0]) = tp;
-                *reinterpret_cast<f32x4*>(&cwt[c][4]) = wn;
+            for (int j = 0; j < 4; ++j) {
+                const int m = j - (4 - W);
+                const float x = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(cwb) + (c * W + (m > 0 ? m : 0)) * 4u);
+                tp0[e][j] = m >= 0 ? x : 0.f;
             }
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int m = j - (4 - W);
+                const float x = ldx(wsb, W > 1 ? c * (W - 1) + (m > 0 ? m : 0) : 0u);
+                wn0[e][j] = m >= 0 ? x : 0.f;
+            }
+            wn0[e][3] = 0.f;
         }
     }
     load_group(0, K < KB ? K : KB);
     // the state, after the first group's inputs (see above)
-    float* Su = S + (size_t)unit * DK * DV;
+    float* const Su = S + (size_t)unit * DK * DV;
+    const uint32_t so0 = (uint32_t)r0 * DV + 4 * cg;
     f32x4 s[RPG];
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
+    for (int i = 0; i < RPG; ++i) s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + so0 + i * DV));
+    if constexpr (CONV) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            *reinterpret_cast<f32x4*>(&cwt[t + 256 * e][0]) = tp0[e];
+            *reinterpret_cast<f32x4*>(&cwt[t + 256 * e][4]) = wn0[e];
+        }
+    }
 
+    char* const yb = op ? static_cast<char*>(op) + tok0 * DV * (OUT_F32 ? 4 : 2) : nullptr;
+    // the first group is prepared outside the loop: its waits then count only the loads issued
+    // before the state's, where inside the loop they would be merged with the later groups'
+    prep_group(0, K < KB ? K : KB);
     for (int t0 = 0;;) {
         const int kb = K - t0 < KB ? K - t0 : KB;
-        prep_group(t0, kb);
         for (int j = 0; j < kb; ++j) {
             const int tok = t0 + j;
             const int pb = tok & 1;
@@ -485,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                 zt += red_z[pb][m][cg];
             }
             const f32x4 vv = *reinterpret_cast<const f32x4*>(&xin[j][2 * DK + 4 * cg]);
-            const f32x4 u = tb[j][0] * (vv - yt);
+            const f32x4 u = bsig[j] * (vv - yt);
 #pragma unroll
             for (int i4 = 0; i4 < RPG; i4 += 4) {
                 const f32x4 kv = *reinterpret_cast<const f32x4*>(&xin[j][DK + r0 + i4]);
@@ -494,24 +534,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             }
             if (tok + 1 == commit) {
 #pragma unroll
-                for (int i = 0; i < RPG; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Su + (size_t)(r0 + i) * DV + 4 * cg));
+                for (int i = 0; i < RPG; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Su + so0 + i * DV));
             }
-            if (op && rg == 0) {
-                // o~ for this thread's 4 columns, then RMSNorm over dv across the CG lanes of row
-                // group 0 (within one wave) and the gate
-                const f32x4 o = scale * (zt + tb[j][1] * u);
+            if (op && rg == (tok * (64 / CG)) % NRG) {
+                // o~ for this thread's 4 columns, then RMSNorm over dv across the CG lanes of one
+                // row group (within one wave) and the gate; the waves take turns by token, so
+                // that no wave carries this on every token's critical path
+                const f32x4 o = scale * (zt + tqk[j] * u);
                 float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
 #pragma unroll
                 for (int m = 1; m < CG; m *= 2) ss += __shfl_xor(ss, m, 64);
                 const float inv = rsqrtf(ss / DV + eps);
                 const f32x4 gt = *reinterpret_cast<const f32x4*>(&sgate[j][4 * cg]);
+                const f32x4 w = norm_w ? ld<f32x4>(norm_w + 4 * cg) : f32x4{1.f, 1.f, 1.f, 1.f};
                 const f32x4 yo = gt * (o * inv * w);
-                const size_t vb = row_of(tok) * DV + 4 * cg;
+                const uint32_t yo_at = (uint32_t)tok * HDV + 4 * cg;
                 if constexpr (OUT_F32) {
-                    st<f32x4>(reinterpret_cast<float*>(op) + vb, yo);
+                    st<f32x4>(reinterpret_cast<float*>(yb) + yo_at, yo);
                 } else {
                     bf16x4 ob{f2bf(yo[0]), f2bf(yo[1]), f2bf(yo[2]), f2bf(yo[3])};
-                    st<bf16x4>(reinterpret_cast<bf16*>(op) + vb, ob);
+                    st<bf16x4>(reinterpret_cast<bf16*>(yb) + yo_at, ob);
                 }
             }
         }
@@ -519,6 +561,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         if (t0 >= K) break;
         load_group(t0, K - t0 < KB ? K - t0 : KB);
         __syncthreads();   // the group's LDS is rewritten next
+        prep_group(t0, K - t0 < KB ? K - t0 : KB);
     }
 }
 
