@@ -7,11 +7,17 @@ One step = one pass of the whole hot path over one synthetic batch:
     updated in place, one token each).
 Inputs are generated on the GPU before the timed region (seeded; see inputs.py for the recipe).
 
-Prints one JSON line.  ``value`` is prefill tokens per second of the whole step (B*T tokens per
-step / step time, decode included).  ``roofline`` is for the prefill kernel (the dominant one):
-algorithmic HBM bytes per launch / its average launch time measured with HIP events on the
-launch stream.  ``decode`` reports the decode kernel against HBM the same way.  ``cpu_baseline``
-times the C float64 reference token loop on a bounded sample of the same prefill workload.
+Prints one JSON line.  ``value`` is prefill tokens per second: B*T tokens over the prefill
+launch's own time (HIP events on its stream, averaged over the timed steps); ``ms_per_step`` is
+the whole step, decode included, and ``decode`` reports the decode launch separately.
+``roofline`` is for the prefill kernel (the dominant one): algorithmic HBM bytes per launch / its
+average launch time.  ``mfma_busy`` is the prefill kernel's MFMA-busy fraction from the
+committed counter summary (profiles/kernel_counters.json), when it was taken on the current
+kernel source.  The variants after the steps cover the other workloads: the decay map in the
+kernel, multi-token and fused decode (with and without the short convolution), the packed
+64-sequence prefill, and the one-million-token prefill, plain and split in time.
+``cpu_baseline`` times the C float64 reference token loop on a bounded sample of the prefill
+workload.
 """
 from __future__ import annotations
 
@@ -88,18 +94,33 @@ def kernel_source_hash(name):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, source_name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE and
-    WRITE_SIZE per dispatch, each scaled by what the counter reads for a plain device copy of
-    known size).  None when the summary is missing or was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+def _counters(kernel_key, source_name):
+    """The kernel's record in the committed rocprofv3 counter summary, or None when it is missing
+    or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "kernel_counters.json")
     try:
         rec = json.load(open(path))[kernel_key]
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("source_sha256_16") != kernel_source_hash(source_name):
         return None
+    return rec
+
+
+def measured_traffic(kernel_key, source_name):
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+    counter reads for a plain device copy of known size), or None."""
+    rec = _counters(kernel_key, source_name)
+    if rec is None or "fetch_kib" not in rec:
+        return None
     return (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024
+
+
+def measured_mfma_busy(kernel_key, source_name):
+    """Fraction of SIMD cycles with the MFMA unit busy during the kernel
+    (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4 SIMDs) per dispatch), or None."""
+    rec = _counters(kernel_key, source_name)
+    return None if rec is None else rec.get("mfma_busy_frac")
 
 
 def calibrate_copy():
@@ -146,27 +167,11 @@ def calibrate_peaks(dev):
                               x.numel() // 4, 1024, stream) == 0
 
     c_ms = time_launches(copy)
-    lib.calib_contraction_flops.argtypes = [ctypes.c_int, ctypes.c_int]
-    lib.calib_contraction_flops.restype = ctypes.c_double
-    lib.calib_contraction.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    cblocks, chunks = 256, 1024
-    outc = torch.empty(cblocks * 512, dtype=torch.float32, device=dev)
-
-    def contraction():
-        assert lib.calib_contraction(ctypes.c_void_p(outc.data_ptr()), cblocks, chunks, stream) == 0
-
-    k_ms = time_launches(contraction, reps=5)
     mfma = lib.calib_mfma_flops(blocks, iters) / (m_ms * 1e-3) / 1e12
-    contr = lib.calib_contraction_flops(cblocks, chunks) / (k_ms * 1e-3) / 1e12
     return {"mfma_bf16_TFLOPs": mfma,
             "copy_GBps": 2 * x.numel() * 4 / (c_ms * 1e-3) / 1e9,
-            "contraction_TFLOPs": contr,
-            "contraction_frac_of_spec": contr / BF16_MFMA_PEAK_TFLOPS,
-            "contraction_frac_of_measured": contr / mfma,
             "what": "bench_calib.hip: 8 independent v_mfma_f32_16x16x32_bf16 chains per wave, "
-                    "2048 x 256 threads; grid-stride float4 copy, 1024 x 256 threads; the prefill "
-                    "consumer's per-chunk contraction sequence (68 MFMAs, operands from LDS, "
-                    "elementwise work left out), 256 x 512 threads, 1024 chunks"}
+                    "2048 x 256 threads; grid-stride float4 copy, 1024 x 256 threads"}
 
 
 def cpu_baseline(x, units_wanted=None):
@@ -193,6 +198,10 @@ def cpu_baseline(x, units_wanted=None):
                       f"{dt:.1f} s wall, {cpu_model()}); tokens/s = token-heads/s / H"}
 
 
+def props_cu(dev):
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
 def cpu_model():
     """The host CPU's model name as the kernel reports it (unknown if it does not)."""
     try:
@@ -213,7 +222,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the variants timed after the steps (decay map in the kernel, "
-                         "precise solve, multi-token decode, packed prefill)")
+                         "multi-token and fused decode, packed and long prefill)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="profile helper: run only the prefill launch per step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -271,7 +280,7 @@ def main():
     achieved = pbytes / (pre_ms * 1e-3) / 1e9
     res = {
         "metric": "KDA prefill tokens/s (H=32,d=128,T=32K) + %MFMA peak; decode GB/s vs HBM",
-        "value": B * T / (ms_per_step * 1e-3),
+        "value": B * T / (pre_ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -290,11 +299,18 @@ def main():
         "prefill": {"ms": pre_ms, "tokens_per_s": B * T / (pre_ms * 1e-3),
                     "alg_bytes": pbytes, "alg_GBps": achieved,
                     "alg_mfma_tflops": pflops / (pre_ms * 1e-3) / 1e12,
-                    "mfma_frac": pflops / (pre_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+                    "mfma_frac": pflops / (pre_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                    "mfma_busy": measured_mfma_busy("prefill_kernel<128,bf16,bf16>",
+                                                    "kda_prefill.hip"),
+                    "what": "mfma_frac: the chunkwise form's algorithmic MFMA flops (causal tiles "
+                            "only) per second over the dense bf16 peak; mfma_busy: the kernel's "
+                            "measured MFMA-busy fraction of SIMD cycles (rocprofv3 counters)"},
         "decode": None if args.prefill_only else {
             "us": dec_ms * 1e3, "alg_bytes": dbytes, "GBps": dbytes / (dec_ms * 1e-3) / 1e9,
             "frac_hbm": dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": measured_traffic("decode_kernel<128,128,bf16,bf16>", "kda_decode.hip")},
+            "traffic": measured_traffic("decode_kernel<128,128,bf16,bf16>", "kda_decode.hip"),
+            "what": "kda_recurrent_step: one token per (sequence, head), 1024 sequences x 32 heads, "
+                    "float32 128x128 states updated in place"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic("prefill_kernel<128,bf16,bf16>", "kda_prefill.hip"),
@@ -331,10 +347,26 @@ def main():
                                     K * ((3 * dcfg.dk + 2 * dcfg.dv) * 2 + 2 + dcfg.dv * 2))
         res["decode_multi_fused"] = {"K": K, "us": f_ms * 1e3, "us_per_token": f_ms * 1e3 / K,
                                      "alg_bytes": fbytes, "GBps": fbytes / (f_ms * 1e-3) / 1e9,
+                                     "frac_hbm": fbytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                      "what": "kda_recurrent_multi_fused: the 4-token pass with q/k "
                                              "L2Norm, beta = Sigmoid(logit), decay map, "
                                              "Sigmoid(G) * RMSNorm(o~) fused in"}
-        del f, yf
+        W = 4
+        cv = inputs.make_conv_inputs(dcfg.N, dcfg.H, dcfg.dk, dcfg.dv, W, seed=3, device=dev)
+        fc_ms = time_launches(lambda: binding.recurrent_multi_fused(
+            f["q"], f["k"], f["v"], f["z"], f["A_log"], f["beta_logit"], f["G"], f["S"],
+            norm_weight=f["norm_weight"], y=yf, conv_weight=cv["conv_weight"],
+            conv_state=cv["conv_state"]))
+        # plus the window read and written once (bf16) and the taps (float32, per head)
+        nch = 2 * dcfg.dk + dcfg.dv
+        fcbytes = fbytes + dcfg.N * dcfg.H * nch * (W - 1) * 2 * 2 + dcfg.H * nch * W * 4
+        res["decode_multi_fused_conv"] = {
+            "K": K, "W": W, "us": fc_ms * 1e3, "us_per_token": fc_ms * 1e3 / K,
+            "alg_bytes": fcbytes, "GBps": fcbytes / (fc_ms * 1e-3) / 1e9,
+            "frac_hbm": fcbytes / (fc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "what": "the fused 4-token pass with the 4-tap short convolution and Swish on q, k, v "
+                    "in front, its window committed with the state"}
+        del f, yf, cv
         # packed prefill: 64 sequences, lognormal lengths (median 1024, longest 65536)
         vcfg = inputs.CONFIGS["varlen64_h32_d128"]
         xv = inputs.make_config_inputs(vcfg, seed=0, device=dev)
@@ -350,6 +382,30 @@ def main():
                                    "what": "kda_chunk_fwd on 64 packed sequences (cu_seqlens), "
                                            "H=32, d=128; the longest sequence runs first"}
         del xv, ov, STv
+        # long prefill: one sequence of 2^20 tokens, 32 heads: plain (64 workgroups) and split in
+        # time with the library's segment count for this GPU (kda_chunk_fwd_cp_segments)
+        lcfg = inputs.CONFIGS["long_b1_h32_t1m_d128"]
+        xl = inputs.make_config_inputs(lcfg, seed=0, device=dev)
+        ol = torch.empty((1, lcfg.T, lcfg.H, lcfg.dv), dtype=torch.bfloat16, device=dev)
+        STl = torch.empty((1, lcfg.H, lcfg.dk, lcfg.dv), dtype=torch.float32, device=dev)
+        lbytes = prefill_alg_bytes(1, lcfg.T, lcfg.H, lcfg.dk, lcfg.dv, 1)
+        l_ms = time_launches(lambda: binding.chunk_fwd(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"],
+                                                       xl["S0"], o=ol, S_T=STl),
+                             reps=2, groups=1, warmup=1)
+        P = binding.cp_segments(lcfg.H, lcfg.dk, lcfg.dv, props_cu(dev))
+        ws = torch.empty(max(binding.load().kda_chunk_fwd_cp_workspace_size(1, lcfg.H, lcfg.dk, lcfg.dv, P), 16),
+                         dtype=torch.uint8, device=dev)
+        lc_ms = time_launches(lambda: binding.chunk_fwd_cp(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"],
+                                                           xl["S0"], segments=P, o=ol, S_T=STl,
+                                                           workspace=ws),
+                              reps=2, groups=1, warmup=1)
+        res["prefill_long_t1m"] = {
+            "tokens": lcfg.T, "plain_ms": l_ms, "segmented_ms": lc_ms, "segments": P,
+            "tokens_per_s": lcfg.T / (min(l_ms, lc_ms) * 1e-3),
+            "alg_GBps": lbytes / (min(l_ms, lc_ms) * 1e-3) / 1e9,
+            "what": "B=1, H=32, T=1048576, d=128 (13 of 128 key channels per head near g_min): "
+                    "kda_chunk_fwd, and kda_chunk_fwd_cp with the library's segment count"}
+        del xl, ol, STl, ws
         # context for the HBM fractions: what the vendor's own read+write kernels reach here
         xb = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         yb = torch.empty_like(xb)

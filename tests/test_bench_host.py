@@ -41,7 +41,7 @@ def test_prefill_algorithmic_flops_per_token_head():
 
 def test_recorded_traffic_is_gated_by_the_kernel_source():
     assert bench.measured_traffic("no such kernel", "kda_prefill.hip") is None
-    rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))
+    rec = json.load(open(os.path.join(ROOT, "profiles", "kernel_counters.json")))
     for key, src in (("prefill_kernel<128,bf16,bf16>", "kda_prefill.hip"),
                      ("decode_kernel<128,128,bf16,bf16>", "kda_decode.hip")):
         t = bench.measured_traffic(key, src)
@@ -52,6 +52,7 @@ def test_recorded_traffic_is_gated_by_the_kernel_source():
         # the other kernel's source never validates this record
         other = "kda_decode.hip" if src == "kda_prefill.hip" else "kda_prefill.hip"
         assert bench.measured_traffic(key, other) is None
+        assert bench.measured_mfma_busy(key, other) is None
 
 
 def test_more_than_one_gpu_is_refused_before_any_device_use():
