@@ -30,18 +30,25 @@
 // Grid: one 512-thread workgroup per (sequence, head, 64-column slice of dv); the slices of one
 // head go to the same XCD so their reads of q, k, g share L2.  Four producer waves (channel
 // slices) and four consumer waves (16 value columns each), one of each per SIMD.  Iteration it
-// has two intervals separated by workgroup barriers and works on three chunks at once:
-//   interval 1  producers, chunk it: decay prefix (DPP scan over the 16 token lanes of a row),
-//                   decayed operands, partial Gram tiles of A_kk and A_qk over the wave's 32 key
-//                   channels.
+// has two intervals separated by workgroup barriers and works on four chunks at once:
+//   interval 1  producers, chunk it: the decayed operands (prepared in the interval before)
+//                   split into bf16 pairs, partial Gram tiles of A_kk and A_qk over the wave's
+//                   32 key channels, the rows of Q~ and K~ and gamma (into one of three LDS
+//                   buffers), K_end.
 //               consumers, chunk it - 2: the state step on their 16 columns: R = V - K~ S,
 //                   O = Q~ S + M R (written out), S <- gamma S + W R; consumer 2 also completes
 //                   T_b of chunk it - 1 with its off-diagonal block T10 = -T11 N10 T00.
 //   interval 2  producers: the rows of W over the wave's channels (and M) for chunk it - 1, from
-//                   the K_end fragments they kept; Q~, K~, gamma and K_end of chunk it.
+//                   the K_end fragments they kept; the K_end fragments of chunk it; then the
+//                   decay prefix (DPP scan over the 16 token lanes of a row) and the decayed
+//                   operands of chunk it + 1 (kept in registers).
 //               consumers, chunk it: the diagonal blocks T00 (consumer 0) and T11 (consumer 1) of
 //                   the UT transform, beta N10 and the A_qk tiles (consumers 2, 3); every
 //                   consumer sets the scale of its value path for chunk it - 1.
+// A wave issues at most one instruction every four cycles, so each interval lasts about as long
+// as its busiest wave's instruction stream: the producers' elementwise work (several hundred
+// instructions per chunk) is split between the two intervals so that each producer interval
+// stays within the consumers' (the state step in interval 1, the UT solve in interval 2).
 // The state slice (dk x 16, fp32) stays in MFMA accumulators for the whole sequence.  Every
 // hand-off buffer is read at least one barrier after it was written and written again only after
 // its last read; buffers whose writer runs ahead of the reader are doubled.
@@ -78,8 +85,8 @@ struct Layout {
     static constexpr int CPL = kC * TB * 2;                 // one C x C plane
     static constexpr int o_Gp = 0;                          // fp32 [NCB][6][64][4]
     static constexpr int o_beta = o_Gp + GPB;               // fp32 [2][C]
-    static constexpr int o_QK = o_beta + 2 * kC * 4;        // [2] x {Q~ [C][RB], K~ [C][RB] f16, gamma [DK]}
-    static constexpr int o_Tb = o_QK + 2 * QKB;             // [2] x T_b^T hi, lo [C][TB] f16
+    static constexpr int o_QK = o_beta + 2 * kC * 4;        // [3] x {Q~ [C][RB], K~ [C][RB] f16, gamma [DK]}
+    static constexpr int o_Tb = o_QK + 3 * QKB;             // [2] x T_b^T hi, lo [C][TB] f16
     static constexpr int o_Aq = o_Tb + 2 * 2 * CPL;         // [2] x A_qk hi, lo [C][TB] f16
     static constexpr int o_M = o_Aq + 2 * 2 * CPL;          // M [C][TB] f16
     static constexpr int o_W = o_M + CPL;                   // W [DK][TB] f16
@@ -376,20 +383,123 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
         }
     };
 
-    // GATE: the log2 decay of a chunk is mapped from its logits one interval ahead, in interval 2
-    // of the chunk before (the producers' shorter interval), so interval 1 only reads Lg.
-    float Lg[2][8];
-    auto gate_map = [&](int64_t c0) {
+    const int64_t nchunks = (len + kC - 1) / kC;
+
+    // Decayed operands of the next chunk (float), held from their preparation in interval 2 to
+    // interval 1, where they are split for its Gram tiles and turned into its rows and K_end.
+    float Qs[2][8], Kr[2][8], Kd0[8], Kd1[8], Kc[8], F0[8], F1[8];
+    // K_end of the chunk of this iteration (float, before its split)
+    float Xe[2][8];
+
+    // The part of chunk c that comes first: the decay prefix and the decayed operands; beta into
+    // o_beta[c & 1] (wave 0); and the fetch of chunk c + 1.
+    auto prep = [&](int64_t c) {
+        const int64_t c0 = c * kC;
+        float qv[2][8], kv[2][8], L[2][8];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            pz[t].pin_all();
-            // tokens past the end read z = 0, whose map is not 0: they must not decay
-            const bool valid = 16 * t + i16 < len - c0;
-            float zv[8];
-            pz[t].to_f32(zv);
+            pq[t].pin_all();
+            pk[t].pin_all();
+            if constexpr (GATE) {
+                pz[t].pin_all();
+            } else {
+                pin(pg[t][0]);
+                pin(pg[t][1]);
+            }
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                Lg[t][e] = valid ? kGminLog2e * __builtin_amdgcn_rcpf(1.f + fast_exp2(zsc * zv[e])) : 0.f;
+        for (int t = 0; t < 2; ++t) {
+            pq[t].to_f32(qv[t]);
+            pk[t].to_f32(kv[t]);
+            if constexpr (GATE) {
+                // decay map of the logits; tokens past the end read z = 0, whose map is not 0:
+                // they must not decay
+                const bool valid = 16 * t + i16 < len - c0;
+                float zv[8];
+                pz[t].to_f32(zv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    L[t][e] = valid ? kGminLog2e * __builtin_amdgcn_rcpf(1.f + fast_exp2(zsc * zv[e])) : 0.f;
+            } else {
+                const float* gl = reinterpret_cast<const float*>(pg[t]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
+            }
+        }
+        if (p == 0) {   // beta of the chunk for the solve
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                pin(pb[t]);
+                if (g4 == 0)
+                    f32p(Lay::o_beta)[(int)(c & 1) * kC + 16 * t + i16] =
+                        F32IN ? __builtin_bit_cast(float, pb[t]) : __builtin_bit_cast(float, pb[t] << 16);
+            }
+        }
+        // the raw registers are consumed: fetch the next chunk while this one is computed
+        if (c + 1 < nchunks) prefetch(c0 + kC);
+
+        float P[2][8], Pi[2][8];
+        // in-tile prefix of the log2 decay (DPP scan across the 16 token lanes of a row)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                L[t][e] = row_scan16(L[t][e]);
+                P[t][e] = fast_exp2(L[t][e]);        // tile start -> token, <= 1
+                Pi[t][e] = fast_exp2(-L[t][e]);      // token -> tile start, >= 1
+            }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            F0[e] = __shfl(P[0][e], (lane & ~15) | 15, 64);   // decay over tile 0
+            F1[e] = __shfl(P[1][e], (lane & ~15) | 15, 64);   // decay over tile 1
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                Qs[t][e] = qv[t][e] * P[t][e];
+                Kr[t][e] = kv[t][e] * P[t][e];
+            }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            Kd0[e] = kv[0][e] * Pi[0][e];
+            Kd1[e] = kv[1][e] * Pi[1][e];
+            Kc[e] = Kd0[e] * F0[e];                  // tile 0 seen from tile 1
+        }
+    };
+
+    // The rest of chunk c before its products, from the operands above: the rows of Q~ and K~
+    // and the chunk decay gamma into QK[c % 3], K_end.
+    auto rows = [&](int64_t c) {
+        char* qk = smem + Lay::o_QK + (int)(c % 3) * Lay::QKB;
+        if (i16 == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) reinterpret_cast<float*>(qk + 2 * kC * RB * 2)[ch0 + e] = F0[e] * F1[e];
+        }
+        // 8 channels of token 16 t + i16 into [token][pm(channel)] storage
+        auto put_row = [&](char* base, int t, f16x8 v) {
+            f16* d = reinterpret_cast<f16*>(base) + (16 * t + i16) * RB + 32 * p;
+            st<f16x4>(d + pm(8 * g4), f16x4{v[0], v[1], v[2], v[3]});
+            st<f16x4>(d + pm(8 * g4 + 4), f16x4{v[4], v[5], v[6], v[7]});
+        };
+        // Q~ = Q exp(G), K~ = K exp(G) from the chunk start; tile 1 carries the tile-0 decay
+        {
+            float x[8], y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[e] = Qs[1][e] * F0[e];
+                y[e] = Kr[1][e] * F0[e];
+            }
+            put_row(qk, 0, to_f16x8(Qs[0]));
+            put_row(qk, 1, to_f16x8(x));
+            put_row(qk + kC * RB * 2, 0, to_f16x8(Kr[0]));
+            put_row(qk + kC * RB * 2, 1, to_f16x8(y));
+        }
+        // K_end = K exp(G_last - G)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            Xe[0][e] = Kc[e] * F1[e];
+            Xe[1][e] = Kd1[e] * F1[e];
         }
     };
 
@@ -401,85 +511,20 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) Ke[hh][pl] = f16x8{};
 
-    const int64_t nchunks = (len + kC - 1) / kC;
     if (intra && nchunks > 0) {
         prefetch(0);
-        if constexpr (GATE) gate_map(0);
+        prep(0);
     }
 
     for (int64_t it = 0; it <= nchunks + 1; ++it) {
         const bool work = intra && it < nchunks;   // wave-uniform
-        const int buf = (int)(it & 1);
-        float F0[8], F1[8], Qs1[8], Kr[2][8], Kd1[8], Kc[8];
-        f16x8 Qt0;
 
-        // ---- interval 1: decay prefix, decayed operands, partial Gram tiles
+        // ---- interval 1: partial Gram tiles of chunk it, from the operands prepared in the
+        // previous interval 2, split here.  Transposed (column side as the A operand): the
+        // accumulator of lane (row r = i16, g4) holds A[r][16 b + 4 g4 + j].  m: 0 qk00,
+        // 1 qk11, 2 qk10, 3 kk00, 4 kk11, 5 kk10; every tile on split operands (3 products).
+        // Then the rows, gamma and K_end of the chunk.
         if (work) {
-            float qv[2][8], kv[2][8], L[2][8];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                pq[t].pin_all();
-                pk[t].pin_all();
-                if constexpr (!GATE) {
-                    pin(pg[t][0]);
-                    pin(pg[t][1]);
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                pq[t].to_f32(qv[t]);
-                pk[t].to_f32(kv[t]);
-                if constexpr (GATE) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) L[t][e] = Lg[t][e];
-                } else {
-                    const float* gl = reinterpret_cast<const float*>(pg[t]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) L[t][e] = gl[e] * kLog2e;
-                }
-            }
-            if (p == 0) {   // beta of the chunk for the solve
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    pin(pb[t]);
-                    if (g4 == 0)
-                        f32p(Lay::o_beta)[buf * kC + 16 * t + i16] =
-                            F32IN ? __builtin_bit_cast(float, pb[t]) : __builtin_bit_cast(float, pb[t] << 16);
-                }
-            }
-            // the raw registers are consumed: fetch the next chunk while this one is computed
-            if (it + 1 < nchunks) prefetch((it + 1) * kC);
-
-            float P[2][8], Pi[2][8], Qs[2][8], Kd0[8];
-            // in-tile prefix of the log2 decay (DPP scan across the 16 token lanes of a row)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    L[t][e] = row_scan16(L[t][e]);
-                    P[t][e] = fast_exp2(L[t][e]);        // tile start -> token, <= 1
-                    Pi[t][e] = fast_exp2(-L[t][e]);      // token -> tile start, >= 1
-                }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                F0[e] = __shfl(P[0][e], (lane & ~15) | 15, 64);   // decay over tile 0
-                F1[e] = __shfl(P[1][e], (lane & ~15) | 15, 64);   // decay over tile 1
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    Qs[t][e] = qv[t][e] * P[t][e];
-                    Kr[t][e] = kv[t][e] * P[t][e];
-                }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                Kd0[e] = kv[0][e] * Pi[0][e];
-                Kd1[e] = kv[1][e] * Pi[1][e];
-                Kc[e] = Kd0[e] * F0[e];                  // tile 0 seen from tile 1
-                Qs1[e] = Qs[1][e];
-            }
-            Qt0 = to_f16x8(Qs[0]);
             bf16x8 Qh[2], Ql[2], Krh[2], Krl[2], Kdh[2], Kdl[2], Kch, Kcl;
             split8(Qs[0], Qh[0], Ql[0]);
             split8(Qs[1], Qh[1], Ql[1]);
@@ -488,9 +533,6 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
             split8(Kd0, Kdh[0], Kdl[0]);
             split8(Kd1, Kdh[1], Kdl[1]);
             split8(Kc, Kch, Kcl);
-            // Gram tiles transposed (column side as the A operand): the accumulator of lane
-            // (row r = i16, g4) holds A[r][16 b + 4 g4 + j].  m: 0 qk00, 1 qk11, 2 qk10,
-            // 3 kk00, 4 kk11, 5 kk10; every tile on split operands (3 products).
 #pragma unroll
             for (int m = 0; m < 6; ++m) {
                 const int ta = (m % 3 == 0) ? 0 : 1;
@@ -501,12 +543,13 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                 const f32x4 acc = mma3(ch, cl, rh, rl, zero4());
                 st<f32x4>(smem + Lay::o_Gp + ((p * 6 + m) * 64 + lane) * 16, acc);
             }
+            rows(it);
         }
         __syncthreads();
 
         // ---- interval 2: M and W of chunk it - 1 (formed from the K_end fragments held since
-        // interval 2 of the previous iteration and T_b, A_qk from LDS), then Q~, K~, gamma and the
-        // K_end fragments of chunk it.
+        // the previous interval 2 and T_b, A_qk from LDS), the K_end fragments of chunk it, then
+        // the preparation of chunk it + 1.
         if (it >= 1 && it <= nchunks) {
             // W = K_end^T T_b and M = A_qk T_b on float16 pairs, formed transposed:
             // D[i][x] = sum_j T_b[j][i] X[x][j], whose accumulator (lane (column x, g4) holding
@@ -537,40 +580,13 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
             }
         }
         if (work) {
-            char* qk = smem + Lay::o_QK + buf * Lay::QKB;
-            if (i16 == 0) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) reinterpret_cast<float*>(qk + 2 * kC * RB * 2)[ch0 + e] = F0[e] * F1[e];
-            }
-            // 8 channels of token 16 t + i16 into [token][pm(channel)] storage
-            auto put_row = [&](char* base, int t, f16x8 v) {
-                f16* d = reinterpret_cast<f16*>(base) + (16 * t + i16) * RB + 32 * p;
-                st<f16x4>(d + pm(8 * g4), f16x4{v[0], v[1], v[2], v[3]});
-                st<f16x4>(d + pm(8 * g4 + 4), f16x4{v[4], v[5], v[6], v[7]});
-            };
-            // Q~ = Q exp(G), K~ = K exp(G) from the chunk start; tile 1 carries the tile-0 decay
-            {
-                float x[8], y[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    x[e] = Qs1[e] * F0[e];
-                    y[e] = Kr[1][e] * F0[e];
-                }
-                put_row(qk, 0, Qt0);
-                put_row(qk, 1, to_f16x8(x));
-                put_row(qk + kC * RB * 2, 0, to_f16x8(Kr[0]));
-                put_row(qk + kC * RB * 2, 1, to_f16x8(y));
-            }
-            // K_end = K exp(G_last - G), split and transposed through the identity: lane (channel
-            // i16 of half hh, g4) gets tokens 16 t + 4 g4 + j of tile t, i.e. the B operand of a
-            // contraction over the chunk's tokens in pm order
+            // K_end split and transposed through the identity: lane (channel i16 of half hh, g4)
+            // gets tokens 16 t + 4 g4 + j of tile t, i.e. the B operand of a contraction over
+            // the chunk's tokens in pm order
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                float xe[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xe[e] = t ? Kd1[e] * F1[e] : Kc[e] * F1[e];
                 f16x8 eh, el;
-                split_h8(xe, eh, el);
+                split_h8(Xe[t], eh, el);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const f16x4 vh = to_f16x4(mma_h(eh, Id[hh], zero4()));   // exact: f16 in
@@ -582,10 +598,8 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                     }
                 }
             }
-            if constexpr (GATE) {
-                if (it + 1 < nchunks) gate_map((it + 1) * kC);
-            }
         }
+        if (intra && it + 1 < nchunks) prep(it + 1);
         __syncthreads();
     }
 }
@@ -732,7 +746,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         // ---- interval 1: state step of chunk it - 2 on this wave's 16 state columns.
         if (it >= 2) {
             const int64_t c = it - 2, c0 = c * kC;
-            const char* qk = smem + Lay::o_QK + (int)(c & 1) * Lay::QKB;
+            const char* qk = smem + Lay::o_QK + (int)(c % 3) * Lay::QKB;
             const uint32_t nvalid = a.mode == 1 ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
             // output rows of the chunk: stores at or past row nvalid fall outside the resource
             // (summaries write no outputs)
