@@ -35,9 +35,10 @@
 //                   split into bf16 pairs, partial Gram tiles of A_kk and A_qk over the wave's
 //                   32 key channels, the rows of Q~ and K~ and gamma (into one of three LDS
 //                   buffers), K_end.
+//                   Producer 1 also completes T_b of chunk it - 1 with its off-diagonal block
+//                   T10 = -T11 N10 T00.
 //               consumers, chunk it - 2: the state step on their 16 columns: R = V - K~ S,
-//                   O = Q~ S + M R (written out), S <- gamma S + W R; consumer 2 also completes
-//                   T_b of chunk it - 1 with its off-diagonal block T10 = -T11 N10 T00.
+//                   O = Q~ S + M R (written out), S <- gamma S + W R.
 //   interval 2  producers: the rows of W over the wave's channels (and M) for chunk it - 1, from
 //                   the K_end fragments they kept; the K_end fragments of chunk it; then the
 //                   decay prefix (DPP scan over the 16 token lanes of a row) and the decayed
@@ -545,6 +546,22 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
             }
             rows(it);
         }
+        // ---- interval 1, producer wave 1: T10 = -T11 (beta N10) T00 of chunk it - 1 (column
+        // form, times beta of its columns) completes T_b^T in the buffer of that chunk
+        if (p == 1 && it >= 1 && it <= nchunks) {
+            const int tb = (int)((it - 1) & 1);
+            const float* pub = f32p(Lay::o_Pub);
+            const f32x4 T00c = ld<f32x4>(pub + i16 * 20 + 4 * g4);
+            const f32x4 T11r = ld<f32x4>(pub + Lay::SB + i16 * 20 + 4 * g4);
+            const f32x4 N10r = ld<f32x4>(pub + 2 * Lay::SB + i16 * 20 + 4 * g4);
+            const float b0 = f32p(Lay::o_beta)[tb * kC + i16];
+            const f32x4 T10c = mm16(T11r, mm16(N10r, T00c, zero4()), zero4()) * (-b0);
+            f16x4 hv, lv;
+            split_h4(T10c, hv, lv);
+            f16* t = hp(Lay::o_Tb + 2 * tb * Lay::CPL) + i16 * TB + pm(16 + 4 * g4);
+            st<f16x4>(t, hv);
+            st<f16x4>(t + Lay::CPL / 2, lv);
+        }
         __syncthreads();
 
         // ---- interval 2: M and W of chunk it - 1 (formed from the K_end fragments held since
@@ -872,22 +889,6 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                         for (int jj = 0; jj < 4; ++jj) Cp[lo + (16 * ct + jj) * a.dv] = Sacc[ct][jj] * un;
                 }
             }
-        }
-        // ---- interval 1, wave 2: T10 = -T11 (beta N10) T00 of chunk it - 1 (column form, times
-        // beta of its columns) completes T_b^T in the buffer of that chunk
-        if (cw == 2 && it >= 1 && it <= nchunks) {
-            const int tb = (int)((it - 1) & 1);
-            const float* pub = f32p(Lay::o_Pub);
-            const f32x4 T00c = ld<f32x4>(pub + i16 * 20 + 4 * g4);
-            const f32x4 T11r = ld<f32x4>(pub + SB + i16 * 20 + 4 * g4);
-            const f32x4 N10r = ld<f32x4>(pub + 2 * SB + i16 * 20 + 4 * g4);
-            const float b0 = f32p(Lay::o_beta)[tb * kC + i16];
-            const f32x4 T10c = mm16(T11r, mm16(N10r, T00c, zero4()), zero4()) * (-b0);
-            f16x4 hv, lv;
-            split_h4(T10c, hv, lv);
-            f16* t = hp(Lay::o_Tb + 2 * tb * Lay::CPL) + i16 * TB + pm(16 + 4 * g4);
-            st<f16x4>(t, hv);
-            st<f16x4>(t + Lay::CPL / 2, lv);
         }
         __syncthreads();
 
