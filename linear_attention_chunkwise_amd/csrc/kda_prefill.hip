@@ -505,12 +505,35 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
     };
 
     // K_end of the last chunk as B operands (channel half hh, plane hi / lo), kept for one
-    // iteration until M and W of that chunk are formed
-    f16x8 Ke[2][2];
+    // iteration until M and W of that chunk are formed.  With bf16 inputs the fragments of a
+    // chunk are formed in interval 1 (KeN), beside its products, and move to Ke after W; with
+    // float32 inputs (more registers in flight) they are formed in interval 2 directly into Ke.
+    constexpr bool KE_EARLY = !F32IN;
+    f16x8 Ke[2][2], KeN[2][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl) Ke[hh][pl] = f16x8{};
+        for (int pl = 0; pl < 2; ++pl) Ke[hh][pl] = KeN[hh][pl] = f16x8{};
+    // K_end split and transposed through the identity: lane (channel i16 of half hh, g4) gets
+    // tokens 16 t + 4 g4 + j of tile t, i.e. the B operand of a contraction over the chunk's
+    // tokens in pm order
+    auto ke_frags = [&](f16x8 (&K)[2][2]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f16x8 eh, el;
+            split_h8(Xe[t], eh, el);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const f16x4 vh = to_f16x4(mma_h(eh, Id[hh], zero4()));   // exact: f16 in
+                const f16x4 vl = to_f16x4(mma_h(el, Id[hh], zero4()));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    K[hh][0][4 * t + j] = vh[j];
+                    K[hh][1][4 * t + j] = vl[j];
+                }
+            }
+        }
+    };
 
     if (intra && nchunks > 0) {
         prefetch(0);
@@ -545,6 +568,7 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
                 st<f32x4>(smem + Lay::o_Gp + ((p * 6 + m) * 64 + lane) * 16, acc);
             }
             rows(it);
+            if constexpr (KE_EARLY) ke_frags(KeN);
         }
         // ---- interval 1, producer wave 1: T10 = -T11 (beta N10) T00 of chunk it - 1 (column
         // form, times beta of its columns) completes T_b^T in the buffer of that chunk
@@ -597,23 +621,13 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
             }
         }
         if (work) {
-            // K_end split and transposed through the identity: lane (channel i16 of half hh, g4)
-            // gets tokens 16 t + 4 g4 + j of tile t, i.e. the B operand of a contraction over
-            // the chunk's tokens in pm order
+            if constexpr (KE_EARLY) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                f16x8 eh, el;
-                split_h8(Xe[t], eh, el);
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const f16x4 vh = to_f16x4(mma_h(eh, Id[hh], zero4()));   // exact: f16 in
-                    const f16x4 vl = to_f16x4(mma_h(el, Id[hh], zero4()));
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        Ke[hh][0][4 * t + j] = vh[j];
-                        Ke[hh][1][4 * t + j] = vl[j];
-                    }
-                }
+                    for (int pl = 0; pl < 2; ++pl) Ke[hh][pl] = KeN[hh][pl];
+            } else {
+                ke_frags(Ke);
             }
         }
         if (intra && it + 1 < nchunks) prep(it + 1);
