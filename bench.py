@@ -373,15 +373,27 @@ def main():
         Tv = xv["q"].shape[1]
         ov = torch.empty((1, Tv, vcfg.H, vcfg.dv), dtype=torch.bfloat16, device=dev)
         STv = torch.empty((xv["N"], vcfg.H, vcfg.dk, vcfg.dv), dtype=torch.float32, device=dev)
+        vneed = binding.chunk_fwd_workspace_size(xv["N"], Tv, vcfg.H, vcfg.dk, vcfg.dv, True)
+        wsv = torch.empty(vneed, dtype=torch.uint8, device=dev) if vneed else None
         v_ms = time_launches(lambda: binding.chunk_fwd(xv["q"], xv["k"], xv["v"], xv["g"], xv["beta"],
-                                                       xv["S0"], xv["cu_seqlens"], o=ov, S_T=STv))
+                                                       xv["S0"], xv["cu_seqlens"], o=ov, S_T=STv,
+                                                       workspace=wsv))
+        plan = wsv[:4].cpu().view(torch.int32).tolist()[0] if vneed else 0
+        vw_ms = time_launches(lambda: binding.chunk_fwd(xv["q"], xv["k"], xv["v"], xv["g"], xv["beta"],
+                                                        xv["S0"], xv["cu_seqlens"], o=ov, S_T=STv,
+                                                        workspace=None))
         lens = xv["cu_seqlens"][1:] - xv["cu_seqlens"][:-1]
         vbytes = prefill_alg_bytes(1, Tv, vcfg.H, vcfg.dk, vcfg.dv, xv["N"])
-        res["prefill_varlen64"] = {"ms": v_ms, "tokens": Tv, "tokens_per_s": Tv / (v_ms * 1e-3),
+        res["prefill_varlen64"] = {"ms": v_ms, "whole_ms": vw_ms, "planned_segment_len": plan,
+                                   "tokens": Tv, "tokens_per_s": Tv / (v_ms * 1e-3),
                                    "longest": int(lens.max()), "alg_GBps": vbytes / (v_ms * 1e-3) / 1e9,
                                    "what": "kda_chunk_fwd on 64 packed sequences (cu_seqlens), "
-                                           "H=32, d=128; the longest sequence runs first"}
-        del xv, ov, STv
+                                           "H=32, d=128, as kda_chunk_fwd plans it (ms; 4096 "
+                                           "workgroups already fill the GPU, so it asks for no "
+                                           "workspace and runs every sequence whole: "
+                                           "planned_segment_len 0) and with no workspace "
+                                           "(whole_ms); the longest sequence runs first"}
+        del xv, ov, STv, wsv
         # long prefill: one sequence of 2^20 tokens, 32 heads: plain (64 workgroups) and split in
         # time with the library's segment count for this GPU (kda_chunk_fwd_cp_segments)
         lcfg = inputs.CONFIGS["long_b1_h32_t1m_d128"]
@@ -390,21 +402,20 @@ def main():
         STl = torch.empty((1, lcfg.H, lcfg.dk, lcfg.dv), dtype=torch.float32, device=dev)
         lbytes = prefill_alg_bytes(1, lcfg.T, lcfg.H, lcfg.dk, lcfg.dv, 1)
         l_ms = time_launches(lambda: binding.chunk_fwd(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"],
-                                                       xl["S0"], o=ol, S_T=STl),
+                                                       xl["S0"], o=ol, S_T=STl, workspace=None),
                              reps=2, groups=1, warmup=1)
-        P = binding.cp_segments(lcfg.H, lcfg.dk, lcfg.dv, props_cu(dev))
-        ws = torch.empty(max(binding.load().kda_chunk_fwd_cp_workspace_size(1, lcfg.H, lcfg.dk, lcfg.dv, P), 16),
-                         dtype=torch.uint8, device=dev)
-        lc_ms = time_launches(lambda: binding.chunk_fwd_cp(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"],
-                                                           xl["S0"], segments=P, o=ol, S_T=STl,
-                                                           workspace=ws),
+        need = binding.chunk_fwd_workspace_size(1, lcfg.T, lcfg.H, lcfg.dk, lcfg.dv, False)
+        summary = lcfg.H * lcfg.dk * (lcfg.dk + lcfg.dv) * 4
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        la_ms = time_launches(lambda: binding.chunk_fwd(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"],
+                                                        xl["S0"], o=ol, S_T=STl, workspace=ws),
                               reps=2, groups=1, warmup=1)
         res["prefill_long_t1m"] = {
-            "tokens": lcfg.T, "plain_ms": l_ms, "segmented_ms": lc_ms, "segments": P,
-            "tokens_per_s": lcfg.T / (min(l_ms, lc_ms) * 1e-3),
-            "alg_GBps": lbytes / (min(l_ms, lc_ms) * 1e-3) / 1e9,
+            "tokens": lcfg.T, "ms": la_ms, "whole_ms": l_ms, "segments": need // summary + 1,
+            "tokens_per_s": lcfg.T / (la_ms * 1e-3), "alg_GBps": lbytes / (la_ms * 1e-3) / 1e9,
             "what": "B=1, H=32, T=1048576, d=128 (13 of 128 key channels per head near g_min): "
-                    "kda_chunk_fwd, and kda_chunk_fwd_cp with the library's segment count"}
+                    "kda_chunk_fwd with the workspace of its automatic split (ms; segments as "
+                    "planned) and without (whole_ms, 64 workgroups)"}
         del xl, ol, STl, ws
         # context for the HBM fractions: what the vendor's own read+write kernels reach here
         xb = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)

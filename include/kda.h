@@ -85,12 +85,42 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * rounding (1.66e-3 relative).  q and k are expected to be L2-normalised as eq. (2) produces them
  * (|q|, |k| <= 1 per entry): the kernel carries decayed q and k as float16.  v and S0 may have any
  * finite magnitude: the value path is rescaled by powers of two inside the kernel.
+ *
+ * Splitting in time (the in-device context parallelism of §5.1.1, on the decomposition of
+ * §5.1.2, eq. (17); see kda_chunk_fwd_cp): with a workspace of at least
+ * kda_chunk_fwd_workspace_size(N, B * T, H, dk, dv, cu_seqlens != NULL) bytes (16-byte aligned,
+ * caller-owned, overlapping no input or output), the call plans by itself whether and how to
+ * split sequences in time.  It prices each candidate segment length with a model of the two
+ * passes on this GPU's compute units (a pass lasts at least its longest workgroup and at least
+ * its total work over the units) and splits only when that beats the whole-sequence schedule.
+ * Fixed-length rows are planned on the host (all rows alike); packed batches of few sequences
+ * (fewer than two whole-sequence workgroups per compute unit) are planned on the device from
+ * cu_seqlens (no host synchronisation), each sequence by its own length: longer sequences get
+ * more segments, sequences no longer than the segment length stay whole and run beside the
+ * first pass.  Larger packed batches run whole.  Results agree with the whole-sequence run within the operator's
+ * tolerance (not bit for bit).  With workspace NULL or too small, or S_T aliasing S0, every
+ * sequence runs whole (workspace_bytes is then not checked).
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const void* beta, const float* S0, const int32_t* cu_seqlens,
                          int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
                          kda_dtype in_dtype, kda_dtype out_dtype, float scale,
-                         void* o, float* S_T, hipStream_t stream);
+                         void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Bytes of workspace kda_chunk_fwd needs to plan a split in time for n_seq sequences holding
+ * total_tokens tokens in all, on the current device (the plan depends on its compute units):
+ * packed = 0 for fixed-length rows (n_seq rows of total_tokens / n_seq tokens: the exact need of
+ * the plan, 0 when the rows are better left whole), packed = 1 for cu_seqlens batches (an upper
+ * bound for any mix of lengths: the plan, 4 + 5 n_seq + 6 Smax int32 rounded up to 256 bytes,
+ * then Smax = min(n_seq (Pmax - 1), total_tokens / Lmin) summaries of H x dk x (dv + dk)
+ * float32, with Pmax
+ * = min(16, ceil(2 CUs / (H dv / 64))) segments per sequence and Lmin = max(1024, ceil(
+ * total_tokens / 64) rounded up to 32) tokens per segment; 0 beyond 65536 sequences and when
+ * the whole-sequence grid, n_seq H dv / 64 workgroups, already reaches two per compute unit:
+ * such batches run whole).  0 for unsupported sizes. */
+size_t kda_chunk_fwd_workspace_size(int32_t n_seq, int64_t total_tokens, int32_t H, int32_t dk,
+                                    int32_t dv, int32_t packed);
 
 /* kda_chunk_fwd that also emits prefix states (§5.4.1: the recurrent state of a prefix is what a
  * prefix cache stores and reuses; a chunkwise prefill already holds it at chunk ends).
@@ -151,8 +181,8 @@ int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, 
  * when entered with zero.  For few, long sequences (N * H small) this puts more of the GPU to
  * work: two passes of T / segments tokens each instead of one pass of T.
  *
- * Segment length: ceil(T / segments) rounded up to a multiple of 32; with cu_seqlens each
- * sequence is split at the same offsets from its own start (pieces past its end are empty).
+ * Segment length: each sequence's own ceil(len / segments) rounded up to a multiple of 32 (pieces
+ * past its end are empty).
  * Pass 1 writes, for every sequence, head and segment but the last, [S~ | M] (dk x (dv + dk),
  * float32; segment 0 is entered with S0) to `workspace`; pass 2 rebuilds each segment's entering
  * state S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1} and produces its outputs.  Same results as

@@ -19,7 +19,8 @@ def __getattr__(name):
     if name in ("binding", "inputs", "build"):
         import importlib
         return importlib.import_module("." + name, __name__)
-    if name in ("chunk_fwd", "chunk_fwd_cp", "recurrent_step", "recurrent_multi_fused"):
+    if name in ("chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_cp", "recurrent_step",
+                "recurrent_multi_fused"):
         from . import binding
         return getattr(binding, name)
     raise AttributeError(name)

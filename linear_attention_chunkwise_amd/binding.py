@@ -19,7 +19,7 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_RANGE, KDA_ERR_HI
 KDA_BF16, KDA_F32 = 0, 1
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_gate", "kda_chunk_fwd_cp",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_ckpt", "kda_chunk_fwd_gate", "kda_chunk_fwd_cp",
            "kda_chunk_fwd_cp_noalloc",
            "kda_chunk_fwd_cp_workspace_size", "kda_chunk_fwd_cp_segments", "kda_recurrent_step",
            "kda_recurrent_step_gate",
@@ -46,8 +46,11 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
-                                  ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp]
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_ckpt.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, i32, i32,
                                        vp, vp]
@@ -176,18 +179,39 @@ class _Prefill:
         return (self.B, self.T, self.H, self.N, self.dk, self.dv, _dt(q), _dt(self.o))
 
 
+def chunk_fwd_workspace_size(n_seq: int, total_tokens: int, H: int, dk: int, dv: int,
+                             packed: bool, device=None) -> int:
+    """Bytes of workspace kda_chunk_fwd needs to plan a split in time on ``device``."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    return int(_on(dev, load().kda_chunk_fwd_workspace_size, int(n_seq), int(total_tokens), int(H),
+                   int(dk), int(dv), int(bool(packed))))
+
+
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, *, scale: float = 1.0,
-              out_dtype=None, output_final_state: bool = True, o=None, S_T=None):
+              out_dtype=None, output_final_state: bool = True, o=None, S_T=None,
+              workspace="auto"):
     """KDA chunkwise prefill: returns (o [B,T,H,dv], S_T [N,H,dk,dv] float32 or None).
 
     q, k [B,T,H,dk], v [B,T,H,dv], beta [B,T,H] share a dtype (bf16 or f32); g [B,T,H,dk]
     float32; S0 [N,H,dk,dv] float32 or None; cu_seqlens int32 [N+1] (device) with B = 1 for
     packed sequences.  ``S_T`` may be passed as S0 itself to advance the state in place.
-    ``out_dtype`` defaults to q's dtype."""
+    ``out_dtype`` defaults to q's dtype.  ``workspace``: "auto" allocates what the library asks
+    for its automatic split in time (kda_chunk_fwd_workspace_size), None runs every sequence
+    whole, or a uint8 device tensor."""
     lib = load()
     a = _Prefill(q, k, v, beta, S0, cu_seqlens, out_dtype, output_final_state, o, S_T, g=g)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        need = chunk_fwd_workspace_size(a.N, a.B * a.T, a.H, a.dk, a.dv, cu_seqlens is not None,
+                                        a.dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.dev) if need else None
+    if workspace is not None:
+        _require(workspace, "workspace", a.dev, torch.uint8)
+    nbytes = 0 if workspace is None else workspace.numel()
     st = _on(a.dev, lib.kda_chunk_fwd, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
-             _p(cu_seqlens), *a.sizes(q), float(scale), _p(a.o), _p(a.S_T), _stream(a.dev))
+             _p(cu_seqlens), *a.sizes(q), float(scale), _p(a.o), _p(a.S_T), _p(workspace),
+             nbytes, _stream(a.dev))
     _check(st)
     return a.o, a.S_T
 

@@ -68,6 +68,19 @@ kda_status check_disjoint(const Span (&outs)[NO], const Span (&ins)[NI]) {
     return KDA_OK;
 }
 
+// Concurrent prefill workgroups on the current device: one per compute unit.
+int device_slots() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 256;
+    return cus;
+}
+
+// Bytes of the plan in front of the summaries in an automatic split, 256-aligned.
+size_t plan_bytes(int32_t N, int64_t Smax) {
+    return ((size_t)kda::PlanLayout{N, (int32_t)Smax}.ints() * 4 + 255) / 256 * 256;
+}
+
 kda_status hip_status(hipError_t e) {
     if (e == hipSuccess) return ok();
     snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
@@ -206,6 +219,29 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     }
     int64_t seg_len = 0;
     size_t need = 0;
+    // automatic split (segments == 0, kda_chunk_fwd with a workspace): the plan for fixed-length
+    // rows is made here; packed sequences are planned on the device
+    bool device_plan = false;
+    kda::SplitLimits lim;
+    int slots = 0;
+    if (segments == 0) {
+        segments = 1;
+        if (workspace && workspace_bytes > 0 && ckpt_capacity == 0 && N > 0 && !(S_T && S_T == S0)) {
+            slots = device_slots();
+            const size_t want = kda_chunk_fwd_workspace_size(N, tokens, H, dk, dv, cu_seqlens ? 1 : 0);
+            if (want > 0 && workspace_bytes >= want) {
+                if (cu_seqlens) {
+                    lim = kda::split_limits(N, tokens, H, dv, slots);
+                    if (lim.Smax > 0 && kda::plan_packed(N, H, dv, slots)) {
+                        device_plan = true;
+                        segments = lim.Pmax;
+                    }
+                } else {
+                    segments = kda::plan_fixed_segments(N, T, H, dk, dv, slots);
+                }
+            }
+        }
+    }
     if (segments < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "segments", segments);
     if (segments > 1) {
         // one workgroup per (sequence, head, segment, 64-column slice): keep the grid and the
@@ -220,9 +256,10 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         // the first segment reads S0 while the last one writes S_T, in the same launch
         if (S_T && S_T == S0)
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s may not alias S0 in a segmented run%.0lld", "S_T");
-        need = kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments);
+        need = device_plan ? plan_bytes(N, lim.Smax) + (size_t)lim.Smax * H * dk * (dv + dk) * 4
+                           : kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments);
         if (workspace_bytes < need)
-            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %lld bytes given, kda_chunk_fwd_cp_workspace_size asks for more",
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %lld bytes given, the workspace size asks for more",
                         "workspace_bytes", (long long)workspace_bytes);
         KDA_TRY(check_ptr(workspace, 16, "workspace"));
     }
@@ -261,10 +298,21 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     a.nseg = segments;
     a.seg_len = seg_len;
     a.ws = static_cast<float*>(workspace);
+    const kda::PlanLayout lay{N, (int32_t)lim.Smax};
+    if (device_plan) {
+        int32_t* plan = static_cast<int32_t*>(workspace);
+        a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan_bytes(N, lim.Smax));
+        const hipError_t e = kda::launch_plan(a, plan, slots, lim);
+        if (e != hipSuccess) return hip_status(e);
+        a.plan = plan;
+        a.plan_smax = (int32_t)lim.Smax;
+    }
     a.mode = 1;
+    a.plan_items = lay.max_items1();
     const hipError_t e = kda::launch_chunk_fwd(a);
     if (e != hipSuccess) return hip_status(e);
     a.mode = 2;
+    a.plan_items = lay.max_items2();
     return hip_status(kda::launch_chunk_fwd(a));
 }
 
@@ -272,9 +320,23 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          const void* beta, const float* S0, const int32_t* cu_seqlens,
                          int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk, int32_t dv,
                          kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
-                         float* S_T, hipStream_t stream) {
+                         float* S_T, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, g, nullptr, nullptr, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
-                          scale, o, S_T, 0, 0, nullptr, 1, nullptr, 0, stream);
+                          scale, o, S_T, 0, 0, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+size_t kda_chunk_fwd_workspace_size(int32_t n_seq, int64_t total_tokens, int32_t H, int32_t dk, int32_t dv,
+                                    int32_t packed) {
+    if (n_seq < 1 || total_tokens <= 0 || H < 1 || !(dk == 64 || dk == 128) || !(dv == 64 || dv == 128)) return 0;
+    const int slots = device_slots();
+    if (packed) {
+        const kda::SplitLimits lim = kda::split_limits(n_seq, total_tokens, H, dv, slots);
+        if (lim.Smax <= 0 || !kda::plan_packed(n_seq, H, dv, slots)) return 0;
+        return plan_bytes(n_seq, lim.Smax) + (size_t)lim.Smax * H * dk * (dv + dk) * 4;
+    }
+    if (total_tokens % n_seq) return 0;
+    const int32_t P = kda::plan_fixed_segments(n_seq, total_tokens / n_seq, H, dk, dv, slots);
+    return P > 1 ? kda_chunk_fwd_cp_workspace_size(n_seq, H, dk, dv, P) : 0;
 }
 
 kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* g,
@@ -326,6 +388,7 @@ kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const f
                             kda_dtype in_dtype, kda_dtype out_dtype, float scale, void* o,
                             float* S_T, int32_t segments, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
+    if (segments < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "segments", segments);
     return chunk_fwd_impl(q, k, v, g, nullptr, nullptr, beta, S0, cu_seqlens, B, T, H, N, dk, dv, in_dtype, out_dtype,
                           scale, o, S_T, 0, 0, nullptr, segments, workspace, workspace_bytes, stream);
 }
@@ -354,6 +417,7 @@ kda_status kda_chunk_fwd_cp_noalloc(const void* q, const void* k, const void* v,
                                     int32_t B, int64_t T, int32_t H, int32_t N, int32_t dk,
                                     int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
                                     void* o, float* S_T, int32_t segments, hipStream_t stream) {
+    if (segments < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "%s must be >= 1 (got %lld)", "segments", segments);
     void* ws = nullptr;
     if (segments > 1) {
         const size_t need = kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments);

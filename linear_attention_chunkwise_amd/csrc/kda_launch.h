@@ -30,15 +30,40 @@ struct PrefillArgs {
     //           entered with the identity, value 0) -> ws;
     //   mode 2: outputs: each segment rebuilds its entering state from the summaries of the
     //           segments before it, then runs as mode 0 (the last one writes S_T).
+    //   Without a plan every sequence has nseg segments of ceil(len / nseg) tokens rounded up
+    //   to whole chunks.  With one (plan != null, from launch_plan), sequence n has
+    //   plan[1 + n] <= nseg segments of plan[1 + 2N + n] tokens, its summaries start at index
+    //   plan[1 + N + n], and a sequence with one segment runs whole in mode 1 (outputs and S_T).
     int32_t mode;
     int32_t nseg;
-    int64_t seg_len;          // multiple of 32
-    float* ws;                // [N, nseg - 1, H, dk, dv + dk] float32 (modes 1, 2)
+    int64_t seg_len;          // unused (kept for the layout of this record)
+    float* ws;                // summaries [index, H, dk, dv + dk] float32 (modes 1, 2)
     hipStream_t stream;
     // decay map in the kernel (g unused): g = -5 Sigmoid(exp(A_log[h]) z), z [.., H, dk] stored
     // like q
     const void* z = nullptr;
     const float* A_log = nullptr;
+    const int32_t* plan = nullptr;   // see PlanLayout
+    int32_t plan_smax = 0;           // summaries the plan may use (per head)
+    int32_t plan_items = 0;          // grid bound of this pass: work items of the plan
+};
+
+// Layout of a device plan (int32), for N sequences and at most Smax summaries:
+//   [0] segment length (0: no split), [1] items of pass 1, [2] items of pass 2, [3] unused,
+//   segs[N], first summary[N], segment length[N] per sequence,
+//   pass-1 items [N + Smax] x {sequence, segment}: the summaries of the split sequences and the
+//   whole runs of the others, longest sequences first,
+//   pass-2 items [2 Smax] x {sequence, segment}: the segments of the split sequences.
+struct PlanLayout {
+    int32_t N, Smax;
+    __host__ __device__ int64_t segs() const { return 4; }
+    __host__ __device__ int64_t first() const { return 4 + (int64_t)N; }
+    __host__ __device__ int64_t seglen() const { return 4 + 2 * (int64_t)N; }
+    __host__ __device__ int64_t items1() const { return 4 + 3 * (int64_t)N; }
+    __host__ __device__ int64_t items2() const { return items1() + 2 * ((int64_t)N + Smax); }
+    __host__ __device__ int64_t ints() const { return items2() + 4 * (int64_t)Smax; }
+    __host__ __device__ int32_t max_items1() const { return N + Smax; }
+    __host__ __device__ int32_t max_items2() const { return 2 * Smax; }
 };
 
 struct DecodeArgs {
@@ -74,6 +99,91 @@ struct DecodeArgs {
 };
 
 hipError_t launch_chunk_fwd(const PrefillArgs& a);
+
+// ---- Splitting sequences in time (in-device context parallelism).  Costs are in chunk steps
+// of one workgroup (one 32-token chunk of one 64-column slice).  A sequence of len tokens left
+// whole costs nsl workgroups x ceil(len / 32) steps, all in pass 1 (beside the summaries).  Split
+// into P segments of Ls tokens it costs, in pass 1, nsl x ceil(Ls / 32) for the summary of its
+// first segment (value columns) and nslt x ceil(Ls / 32) for each of the next P - 2 (value and
+// transition columns), and in pass 2 nsl x (ceil(Ls_j / 32) + j) for segment j (its tokens and
+// the j summaries it composes).  A pass on `slots` concurrent workgroups takes at least its
+// longest workgroup and at least its total work / slots; a plan is priced at the sum of the two
+// passes' bounds.
+struct SplitCost {
+    double work1 = 0, work2 = 0;   // per head
+    int64_t crit1 = 0, crit2 = 0;
+    int64_t summaries = 0;         // per head
+};
+__host__ __device__ inline int64_t chunks_of(int64_t x) { return (x + 31) / 32; }
+// segments of one sequence for the segment length L (L <= 0: whole), at most Pmax of them
+__host__ __device__ inline void split_of(int64_t len, int64_t L, int Pmax, int& P, int64_t& Ls) {
+    if (L <= 0 || len <= L) {
+        P = 1;
+        Ls = len;
+        return;
+    }
+    int64_t p = (len + L - 1) / L;
+    Ls = L;
+    if (p > Pmax) {
+        p = Pmax;
+        Ls = ((len + p - 1) / p + 31) / 32 * 32;
+    }
+    P = (int)p;
+}
+__host__ __device__ inline void split_add(SplitCost& c, int64_t len, int P, int64_t Ls, int nsl, int nslt) {
+    if (P <= 1) {
+        c.work1 += (double)nsl * chunks_of(len);
+        c.crit1 = c.crit1 > chunks_of(len) ? c.crit1 : chunks_of(len);
+        return;
+    }
+    const int64_t ch = chunks_of(Ls);
+    c.work1 += (double)ch * (nsl + (double)nslt * (P - 2));
+    c.crit1 = c.crit1 > ch ? c.crit1 : ch;
+    c.work2 += (double)nsl * ((double)chunks_of(len) + (double)P * (P - 1) / 2);
+    c.crit2 = c.crit2 > ch + P - 1 ? c.crit2 : ch + P - 1;
+    c.summaries += P - 1;
+}
+__host__ __device__ inline double split_makespan(const SplitCost& c, int H, int slots) {
+    const double w1 = c.work1 * H / slots, w2 = c.work2 * H / slots;
+    const double m1 = (double)c.crit1 > w1 ? (double)c.crit1 : w1;
+    const double m2 = c.summaries ? ((double)c.crit2 > w2 ? (double)c.crit2 : w2) : 0.0;
+    return m1 + m2;
+}
+// A split must beat the whole-sequence schedule by this factor (extra launch, rough chain cost).
+constexpr double kSplitGain = 0.95;
+// Packed batches are planned on the device up to this many sequences (one workgroup prices them).
+constexpr int32_t kPlanMaxSeqs = 65536;
+// ... and only when their whole-sequence grid (N H dv / 64 workgroups) is under two per compute
+// unit: a larger batch already fills the GPU, and its planned launches would carry that many
+// idle workgroups through the dispatcher for a gain the model rarely finds (a packed batch of 64
+// sequences of 32 heads priced no split, and the idle grid cost about 1 ms of 6).
+__host__ __device__ inline bool plan_packed(int32_t N, int32_t H, int32_t dv, int slots) {
+    return N <= kPlanMaxSeqs && (int64_t)N * H * (dv / 64) < 2 * (int64_t)slots;
+}
+// Limits of the automatic plan on a GPU with `slots` concurrent workgroups: segments per
+// sequence, the shortest segment, and the number of summaries the workspace holds per head.
+struct SplitLimits {
+    int Pmax = 1;
+    int64_t Lmin = 0;
+    int64_t Smax = 0;
+};
+__host__ __device__ inline SplitLimits split_limits(int32_t N, int64_t total, int32_t H, int32_t dv, int slots) {
+    SplitLimits l;
+    const int64_t units = (int64_t)H * (dv / 64);
+    int64_t p = (2 * (int64_t)slots + units - 1) / units;
+    l.Pmax = (int)(p < 1 ? 1 : (p > 16 ? 16 : p));
+    int64_t lm = ((total + 63) / 64 + 31) / 32 * 32;
+    l.Lmin = lm < 1024 ? 1024 : lm;
+    const int64_t s1 = (int64_t)N * (l.Pmax - 1), s2 = total / l.Lmin;
+    l.Smax = s1 < s2 ? s1 : s2;
+    if (l.Pmax <= 1 || total >= ((int64_t)1 << 31)) l.Smax = 0;
+    return l;
+}
+// The whole-sequence plan for N sequences of T tokens: the segment count (1: no split).
+int32_t plan_fixed_segments(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int slots);
+// The device planner for packed sequences (one workgroup), writing the plan laid out as
+// PlanLayout{N, lim.Smax}.  a supplies cu, N, T, H, dk, dv and the stream.
+hipError_t launch_plan(const PrefillArgs& a, int32_t* plan, int slots, SplitLimits lim);
 // ok = every g[i], i < n, lies in [lo, hi] (NaN does not); synchronises `stream`
 hipError_t check_range(const float* g, size_t n, float lo, float hi, hipStream_t stream, bool& ok);
 // ok = cu[0] == 0, cu non-decreasing, cu[N] == T (the N + 1 packed-sequence offsets); synchronises

@@ -643,7 +643,8 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 // chunk it - 1 (interval 2).
 template <int DK, bool F32IN, bool OUT_F32>
 __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
-                                         int64_t row0, int64_t len, int n, int h, int slice, int seg) {
+                                         int64_t row0, int64_t len, int n, int h, int slice, int seg,
+                                         int mode, int nseg_n, int64_t sbase) {
     using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr int KS = DK / 32;          // 32-channel contraction steps
@@ -657,7 +658,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     const size_t sv = (size_t)H * a.dv;        // token stride of v, o
     const int col0 = slice * kDVT + 16 * cw;   // first value column of this wave
     // segment summaries: columns >= dv carry the segment's transition (value 0); no outputs
-    const bool tcols = a.mode == 1 && col0 >= a.dv;
+    const bool tcols = mode == 1 && col0 >= a.dv;
     const bool vlane = g4 < 2 && !tcols;       // lanes that load this wave's 16 v columns
 
     const IT* vh = reinterpret_cast<const IT*>(a.v) + (size_t)row0 * sv + (size_t)h * a.dv + col0;
@@ -679,7 +680,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();
     const int wcols = a.dv + DK;   // row length of a segment summary [dk][dv + dk]
     auto summary = [&](int j) {    // summary of segment j of this (sequence, head)
-        return a.ws + (((size_t)n * (a.nseg - 1) + j) * H + h) * DK * wcols;
+        return a.ws + ((size_t)(sbase + j) * H + h) * DK * wcols;
     };
     if (tcols) {
         // transition columns start as the identity
@@ -688,7 +689,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) Sacc[ct][j] = (16 * ct + 4 * g4 + j == c) ? 1.f : 0.f;
-    } else if (a.mode == 2 && seg > 0) {
+    } else if (mode == 2 && seg > 0) {
         // entering state of segment seg: the state after segment 0 (entered with S0), carried
         // through segments 1 .. seg-1 by S <- M_j S + S~_j (products on split bf16 operands)
         const float* W0 = summary(0);
@@ -719,7 +720,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 Sacc[ct] = acc;
             }
         }
-    } else if (a.S0 && !(a.mode == 1 && seg > 0)) {
+    } else if (a.S0 && !(mode == 1 && seg > 0)) {
         const float* S0 = a.S0 + ((size_t)n * H + h) * DK * a.dv;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -778,7 +779,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         if (it >= 2) {
             const int64_t c = it - 2, c0 = c * kC;
             const char* qk = smem + Lay::o_QK + (int)(c % 3) * Lay::QKB;
-            const uint32_t nvalid = a.mode == 1 ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
+            const uint32_t nvalid = mode == 1 ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
             // output rows of the chunk: stores at or past row nvalid fall outside the resource
             // (summaries write no outputs)
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(obc, nvalid * (uint32_t)(sv * sizeof(OT)));
@@ -1050,13 +1051,13 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     }
 
     const float un = __builtin_ldexpf(1.f, esc);
-    if (a.mode == 1) {
+    if (mode == 1) {
         float* Wsum = summary(seg);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) Wsum[(size_t)(16 * ct + 4 * g4 + j) * wcols + col0 + i16] = Sacc[ct][j] * un;
-    } else if (a.ST && (a.mode == 0 || seg == a.nseg - 1)) {
+    } else if (a.ST && (mode == 0 || seg == nseg_n - 1)) {
         float* ST = a.ST + ((size_t)n * H + h) * DK * a.dv;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -1108,30 +1109,67 @@ template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
 __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
-    const int nseg = a.mode == 0 ? 1 : a.nseg;
+    const int nseg = a.mode == 0 ? 1 : a.nseg;   // segments per sequence in the grid (at most)
     int unit, slice;
     block_coords(nslices, unit, slice);
-    if (unit >= a.N * a.H * nseg) return;
+    int n, seg, mode = a.mode, nseg_n = 1;
+    int64_t sbase = 0, row0, len;
     const int h = unit % a.H;
-    const int seg = (unit / a.H) % nseg;
-    const int rank = unit / (a.H * nseg);
-    if (a.mode == 1 && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;   // not needed
-    KDA_POISON(smem, (Layout<DK>::total));
-    KDA_POISON_DONE();
-    int n = rank;
-    if constexpr (RANK) n = seq_of_rank(a, rank, smem);
-    int64_t row0, len;
-    seq_bounds(a, n, row0, len);
-    if (a.mode != 0) {   // this segment's tokens
-        const int64_t lo = (int64_t)seg * a.seg_len;
-        const int64_t hi = lo + a.seg_len < len ? lo + a.seg_len : len;
-        row0 += lo;
-        len = hi > lo ? hi - lo : 0;
+    if (a.plan) {
+        // a planned split: the workgroup's item of this pass's list
+        const PlanLayout lay{a.N, a.plan_smax};
+        const int item = unit / a.H;
+        if (item >= a.plan[a.mode]) return;
+        const int32_t* it = a.plan + (a.mode == 1 ? lay.items1() : lay.items2()) + 2 * (int64_t)item;
+        n = it[0];
+        seg = it[1];
+        nseg_n = a.plan[lay.segs() + n];
+        sbase = a.plan[lay.first() + n];
+        const int64_t L = a.plan[lay.seglen() + n];
+        if (nseg_n <= 1) {
+            // a sequence the plan leaves whole runs here completely, beside the summaries
+            if (slice * kDVT >= a.dv) return;
+            mode = 0;
+        } else if (a.mode == 1 && seg == 0 && slice * kDVT >= a.dv) {
+            return;   // the first segment is entered with S0: no transition columns
+        }
+        KDA_POISON(smem, (Layout<DK>::total));
+        KDA_POISON_DONE();
+        seq_bounds(a, n, row0, len);
+        if (mode != 0) {   // this segment's tokens
+            const int64_t lo = (int64_t)seg * L;
+            const int64_t hi = lo + L < len ? lo + L : len;
+            row0 += lo;
+            len = hi > lo ? hi - lo : 0;
+        }
+    } else {
+        if (unit >= a.N * a.H * nseg) return;
+        seg = (unit / a.H) % nseg;
+        const int rank = unit / (a.H * nseg);
+        // every sequence has nseg segments: summaries are needed for all but the last, and on
+        // value columns only for the first
+        if (a.mode == 1 && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;
+        KDA_POISON(smem, (Layout<DK>::total));
+        KDA_POISON_DONE();
+        n = rank;
+        if constexpr (RANK) n = seq_of_rank(a, rank, smem);
+        seq_bounds(a, n, row0, len);
+        if (a.mode != 0) {
+            // nseg segments of ceil(len / nseg) tokens rounded up to whole chunks
+            nseg_n = nseg;
+            sbase = (int64_t)n * (nseg - 1);
+            int64_t L = ((len + nseg - 1) / nseg + kC - 1) / kC * kC;
+            if (L == 0) L = kC;
+            const int64_t lo = (int64_t)seg * L;
+            const int64_t hi = lo + L < len ? lo + L : len;
+            row0 += lo;
+            len = hi > lo ? hi - lo : 0;
+        }
     }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     if (wave < kNW) producer<DK, F32IN, GATE>(a, smem, wave, lane, row0, len, h);
-    else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg);
+    else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg, mode, nseg_n, sbase);
 }
 
 template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
@@ -1153,7 +1191,7 @@ static hipError_t launch_one(const PrefillArgs& a) {
         attr_set.fetch_or(bit, std::memory_order_relaxed);
     }
     const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
-    const int64_t units = (int64_t)a.N * a.H * (a.mode == 0 ? 1 : a.nseg);
+    const int64_t units = a.plan ? (int64_t)a.plan_items * a.H : (int64_t)a.N * a.H * (a.mode == 0 ? 1 : a.nseg);
     const int64_t blocks = ((units + 7) / 8) * 8 * nslices;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kNT), Lay::total, a.stream, a);
@@ -1162,7 +1200,7 @@ static hipError_t launch_one(const PrefillArgs& a) {
 
 template <int DK, bool F32IN, bool OUT_F32, bool GATE>
 static hipError_t launch_prefill(const PrefillArgs& a) {
-    if (a.cu && a.N > 1 && a.N <= kRankMax) return launch_one<DK, F32IN, OUT_F32, GATE, true>(a);
+    if (a.cu && !a.plan && a.N > 1 && a.N <= kRankMax) return launch_one<DK, F32IN, OUT_F32, GATE, true>(a);
     return launch_one<DK, F32IN, OUT_F32, GATE, false>(a);
 }
 
@@ -1183,6 +1221,179 @@ static hipError_t dispatch_prefill(const PrefillArgs& a) {
 
 hipError_t launch_chunk_fwd(const PrefillArgs& a) {
     return a.z ? dispatch_prefill<true>(a) : dispatch_prefill<false>(a);
+}
+
+int32_t plan_fixed_segments(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int slots) {
+    const SplitLimits lim = split_limits(N, (int64_t)N * T, H, dv, slots);
+    const int nsl = dv / kDVT, nslt = (dv + dk) / kDVT;
+    if (lim.Smax <= 0 || N < 1 || T <= 0) return 1;
+    SplitCost whole;
+    split_add(whole, T, 1, T, nsl, nslt);
+    whole.work1 *= N;
+    const double base = split_makespan(whole, H, slots);
+    double best = base * kSplitGain;
+    int32_t bestP = 1;
+    for (int64_t L = lim.Lmin; L < T; L *= 2) {
+        int P;
+        int64_t Ls;
+        split_of(T, L, lim.Pmax, P, Ls);
+        if ((int64_t)N * (P - 1) > lim.Smax) continue;
+        SplitCost c;
+        split_add(c, T, P, Ls, nsl, nslt);
+        c.work1 *= N;
+        c.work2 *= N;
+        c.summaries *= N;
+        const double m = split_makespan(c, H, slots);
+        if (m < best) {
+            best = m;
+            bestP = P;
+        }
+    }
+    return bestP;
+}
+
+// One workgroup of 256 threads prices every candidate segment length (the minimum doubled
+// until it covers the longest sequence) with the model above and writes the plan of the best.
+__global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __restrict__ plan, int slots,
+                                                   SplitLimits lim) {
+    __shared__ double rd[2][256];
+    __shared__ int64_t ri[3][256];
+    const int t = threadIdx.x;
+    const int N = a.N, H = a.H, nsl = a.dv / kDVT, nslt = (a.dv + a.dk) / kDVT;
+    auto reduce = [&](double& w1, double& w2, int64_t& c1, int64_t& c2, int64_t& ns) {
+        rd[0][t] = w1;
+        rd[1][t] = w2;
+        ri[0][t] = c1;
+        ri[1][t] = c2;
+        ri[2][t] = ns;
+        __syncthreads();
+        for (int k = 128; k > 0; k >>= 1) {
+            if (t < k) {
+                rd[0][t] += rd[0][t + k];
+                rd[1][t] += rd[1][t + k];
+                ri[0][t] = ri[0][t] > ri[0][t + k] ? ri[0][t] : ri[0][t + k];
+                ri[1][t] = ri[1][t] > ri[1][t + k] ? ri[1][t] : ri[1][t + k];
+                ri[2][t] += ri[2][t + k];
+            }
+            __syncthreads();
+        }
+        w1 = rd[0][0];
+        w2 = rd[1][0];
+        c1 = ri[0][0];
+        c2 = ri[1][0];
+        ns = ri[2][0];
+        __syncthreads();
+    };
+    auto price = [&](int64_t L, SplitCost& c) {
+        SplitCost mine;
+        for (int n = t; n < N; n += 256) {
+            int64_t row0, len;
+            seq_bounds(a, n, row0, len);
+            int P;
+            int64_t Ls;
+            split_of(len, L, lim.Pmax, P, Ls);
+            split_add(mine, len, P, Ls, nsl, nslt);
+        }
+        reduce(mine.work1, mine.work2, mine.crit1, mine.crit2, mine.summaries);
+        c = mine;
+    };
+    SplitCost whole;
+    price(0, whole);
+    const int64_t longest = whole.crit1 * 32;   // in tokens, rounded up to whole chunks
+    double best = split_makespan(whole, H, slots) * kSplitGain;
+    int64_t bestL = 0;
+    for (int64_t L = lim.Lmin; L < longest; L *= 2) {
+        SplitCost c;
+        price(L, c);
+        if (c.summaries > lim.Smax) continue;
+        const double m = split_makespan(c, H, slots);
+        if (m < best) {
+            best = m;
+            bestL = L;
+        }
+    }
+    // The plan of bestL.  Sequences are taken longest first (ranked here for up to kRankMax of
+    // them, in index order beyond): their summaries' first index and their pass-1 and pass-2
+    // items follow from exclusive prefix sums in that order.
+    const PlanLayout lay{N, (int32_t)lim.Smax};
+    __shared__ int32_t order[kRankMax];
+    __shared__ int64_t lens[kRankMax];
+    const bool ranked = N <= kRankMax;
+    if (ranked) {
+        for (int n = t; n < N; n += 256) {
+            int64_t row0, len;
+            seq_bounds(a, n, row0, len);
+            lens[n] = len;
+        }
+        __syncthreads();
+        for (int n = t; n < N; n += 256) {
+            int r = 0;
+            for (int m = 0; m < N; ++m) r += (lens[m] > lens[n]) | ((lens[m] == lens[n]) & (m < n));
+            order[r] = n;
+        }
+        __syncthreads();
+    }
+    int32_t c_sum = 0, c_a = 0, c_b = 0;
+    __shared__ int32_t sc[3][256];
+    for (int base = 0; base < N; base += 256) {
+        const int r = base + t;
+        int P = 0;
+        int64_t Ls = 0;
+        int n = 0;
+        if (r < N) {
+            n = ranked ? order[r] : r;
+            int64_t row0, len;
+            seq_bounds(a, n, row0, len);
+            split_of(len, bestL, lim.Pmax, P, Ls);
+            plan[lay.segs() + n] = P;
+            plan[lay.seglen() + n] = (int32_t)(P > 1 ? Ls : (Ls > 0 ? Ls : kC));
+        }
+        const int na = r < N ? (P > 1 ? P - 1 : 1) : 0;   // pass-1 items
+        const int nb = r < N && P > 1 ? P : 0;             // pass-2 items
+        const int ns = r < N ? P - 1 : 0;                  // summaries
+        sc[0][t] = ns;
+        sc[1][t] = na;
+        sc[2][t] = nb;
+        __syncthreads();
+        for (int k = 1; k < 256; k <<= 1) {
+            const int32_t x0 = t >= k ? sc[0][t - k] : 0, x1 = t >= k ? sc[1][t - k] : 0,
+                          x2 = t >= k ? sc[2][t - k] : 0;
+            __syncthreads();
+            sc[0][t] += x0;
+            sc[1][t] += x1;
+            sc[2][t] += x2;
+            __syncthreads();
+        }
+        if (r < N) {
+            plan[lay.first() + n] = c_sum + sc[0][t] - ns;
+            int32_t ia = c_a + sc[1][t] - na, ib = c_b + sc[2][t] - nb;
+            int32_t* A = plan + lay.items1();
+            int32_t* B = plan + lay.items2();
+            for (int j = 0; j < na; ++j) {
+                A[2 * (ia + j)] = n;
+                A[2 * (ia + j) + 1] = j;
+            }
+            for (int j = 0; j < nb; ++j) {
+                B[2 * (ib + j)] = n;
+                B[2 * (ib + j) + 1] = j;
+            }
+        }
+        c_sum += sc[0][255];
+        c_a += sc[1][255];
+        c_b += sc[2][255];
+        __syncthreads();
+    }
+    if (t == 0) {
+        plan[0] = (int32_t)bestL;
+        plan[1] = c_a;
+        plan[2] = c_b;
+        plan[3] = 0;
+    }
+}
+
+hipError_t launch_plan(const PrefillArgs& a, int32_t* plan, int slots, SplitLimits lim) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, a.stream, a, plan, slots, lim);
+    return hipGetLastError();
 }
 
 }  // namespace kda

@@ -52,11 +52,11 @@ FAKE = 1 << 20   # an aligned, never-dereferenced address: every case below fail
 
 def _fwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2, N=1,
-             dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None)
+             dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None, ws=None, wsb=0)
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"],
                              a["T"], a["H"], a["N"], a["dk"], a["dv"], a["ind"], a["outd"],
-                             ctypes.c_float(a["scale"]), a["o"], a["ST"], None)
+                             ctypes.c_float(a["scale"]), a["o"], a["ST"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -334,3 +334,37 @@ def test_outputs_may_not_overlap_inputs_or_each_other(lib, call, kw, names):
     assert call(lib, **kw) == binding.KDA_ERR_INVALID_ARGUMENT
     err = lib.kda_last_error()
     assert all(n in err for n in names), err
+
+
+def test_chunk_fwd_workspace_size_plans_on_the_host(lib):
+    """Without a GPU the planner assumes 256 compute units (one prefill workgroup each)."""
+    size = lib.kda_chunk_fwd_workspace_size
+    assert size(0, 1 << 20, 32, 128, 128, 0) == 0
+    assert size(1, 1 << 20, 32, 96, 128, 0) == 0
+    # B=4, T=32768, H=32: 256 workgroups already fill the GPU, rows stay whole
+    assert size(4, 4 * 32768, 32, 128, 128, 0) == 0
+    # one sequence of 2^20 tokens, 32 heads: split; the need is P - 1 summaries of the fixed path
+    one = size(1, 1 << 20, 32, 128, 128, 0)
+    summary = 32 * 128 * (128 + 128) * 4
+    assert one > 0 and one % summary == 0
+    P = one // summary + 1
+    assert one == lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, P) and 2 <= P <= 16
+    # packed: an upper bound for any mix of lengths, plan first (few sequences only)
+    assert size(64, 158485, 32, 128, 128, 1) == 0            # 4096 workgroups: runs whole
+    N, total = 3, 158485
+    pmax = min(16, -(-2 * 256 // (32 * 2)))
+    lmin = max(1024, -(-(-(-total // 64)) // 32) * 32)
+    smax = min(N * (pmax - 1), total // lmin)
+    plan = ((4 + 5 * N + 6 * smax) * 4 + 255) // 256 * 256
+    assert size(N, total, 32, 128, 128, 1) == plan + smax * summary
+    assert size(1 << 17, 1 << 24, 1, 64, 64, 1) == 0            # beyond the device planner
+
+
+def test_chunk_fwd_workspace_is_checked_when_a_split_is_planned(lib):
+    # a packed batch long enough to split: the workspace then may not overlap an input
+    kw = dict(cu=FAKE * 8192, N=2, B=1, T=1 << 20, H=2, dk=64, dv=64, o=FAKE * 4096)
+    need = lib.kda_chunk_fwd_workspace_size(2, 1 << 20, 2, 64, 64, 1)
+    assert need > 0
+    assert _fwd(lib, ws=FAKE, wsb=need, **kw) == binding.KDA_ERR_INVALID_ARGUMENT   # over q
+    assert b"workspace" in lib.kda_last_error()
+    assert _fwd(lib, ws=FAKE * 16384 + 8, wsb=need, **kw) == binding.KDA_ERR_INVALID_ARGUMENT  # misaligned

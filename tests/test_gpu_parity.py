@@ -66,11 +66,13 @@ def _to_dev(x, dev="cuda"):
     return {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in x.items()}
 
 
-def run_gpu(x, out_dtype, scale=1.0):
+def run_gpu(x, out_dtype, scale=1.0, workspace="auto"):
+    """kda_chunk_fwd as a caller gets it by default (its automatic split in time when it pays),
+    or with workspace=None every sequence whole."""
     from linear_attention_chunkwise_amd import binding
     d = _to_dev(x)
     o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["cu_seqlens"],
-                              scale=scale, out_dtype=out_dtype)
+                              scale=scale, out_dtype=out_dtype, workspace=workspace)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), ST.cpu().numpy()
 
@@ -252,9 +254,9 @@ def test_prefill_value_path_range(gpu_lib):
 def test_prefill_no_final_state_and_inplace(gpu_lib):
     from linear_attention_chunkwise_amd import binding
     x = _to_dev(inputs.make_prefill_inputs(2, 77, 2, 128, 128, seed=5))
-    o1, ST1 = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    o1, ST1 = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], workspace=None)
     o2, none = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
-                                 output_final_state=False)
+                                 output_final_state=False, workspace=None)
     assert none is None and torch.equal(o1, o2)
     S = x["S0"].clone()
     o3, S_out = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], S, S_T=S)
@@ -275,20 +277,23 @@ def test_prefill_deterministic(gpu_lib):
 def test_results_do_not_depend_on_the_rest_of_the_batch(gpu_lib):
     """Batch invariance: a sequence's outputs and final state are bitwise the same whether it runs
     alone, in a fixed-length batch, or packed with sequences of other lengths (the longest-first
-    instantiation); a decode unit's result is the same alone or in a batch."""
+    instantiation); a decode unit's result is the same alone or in a batch.  Whole sequences
+    only (workspace=None): a split in time follows a plan made for the whole batch."""
     from linear_attention_chunkwise_amd import binding
     x = _to_dev(inputs.make_prefill_inputs(3, 130, 2, 128, 128, seed=81))
-    o_b, S_b = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    o_b, S_b = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], workspace=None)
     one = lambda t, n: t[n:n + 1].contiguous()
     for n in range(3):
-        o_1, S_1 = binding.chunk_fwd(*(one(x[k], n) for k in ("q", "k", "v", "g", "beta", "S0")))
+        o_1, S_1 = binding.chunk_fwd(*(one(x[k], n) for k in ("q", "k", "v", "g", "beta", "S0")),
+                                     workspace=None)
         assert torch.equal(o_1, o_b[n:n + 1]) and torch.equal(S_1, S_b[n:n + 1]), f"alone {n}"
     # packed: a 57-token sequence, batch row 1 (130 tokens), a 3-token sequence
     xp = _to_dev(inputs.make_prefill_inputs(1, 57 + 3, 2, 128, 128, seed=82))
     cat = lambda k: torch.cat([xp[k][:, :57], x[k][1:2], xp[k][:, 57:]], dim=1).contiguous()
     S0p = torch.cat([xp["S0"], x["S0"][1:2], xp["S0"]], dim=0).contiguous()
     cu = torch.tensor([0, 57, 187, 190], dtype=torch.int32, device="cuda")
-    o_p, S_p = binding.chunk_fwd(*(cat(k) for k in ("q", "k", "v", "g", "beta")), S0p, cu)
+    o_p, S_p = binding.chunk_fwd(*(cat(k) for k in ("q", "k", "v", "g", "beta")), S0p, cu,
+                                 workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(o_p[:, 57:187], o_b[1:2]) and torch.equal(S_p[1:2], S_b[1:2]), "packed"
     d = _to_dev(inputs.make_decode_inputs(9, 2, 128, 128, seed=83))
@@ -518,7 +523,7 @@ def test_checkpoints_match_prefix_states(gpu_lib, interval, capacity):
                                        out_dtype=torch.float32)
     torch.cuda.synchronize()
     ck = ck.cpu().numpy()
-    o_plain, ST_plain = run_gpu(x, torch.float32)
+    o_plain, ST_plain = run_gpu(x, torch.float32, workspace=None)
     np.testing.assert_array_equal(o.cpu().numpy(), o_plain)       # same launch path, bitwise
     np.testing.assert_array_equal(ST.cpu().numpy(), ST_plain)
     cuh = [int(c) for c in cu]
@@ -580,7 +585,7 @@ def test_resume_from_checkpoint(gpu_lib):
     cut = 512
     sl = lambda t: t[:, cut:].contiguous()
     o2, ST2 = binding.chunk_fwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(d["beta"]),
-                                ck[:, :, 1].contiguous(), out_dtype=torch.float32)
+                                ck[:, :, 1].contiguous(), out_dtype=torch.float32, workspace=None)
     torch.cuda.synchronize()
     assert_close("o[resumed]", o2.cpu().numpy(), o[:, cut:].cpu().numpy())
     assert_close("S_T[resumed]", ST2.cpu().numpy(), ST.cpu().numpy())
@@ -654,6 +659,92 @@ def test_segmented_varlen_and_dk64(gpu_lib):
     ro, rST = oracle_all(x)
     assert_close("o[cp d64 f32]", o.cpu().numpy(), ro)
     assert_close("S_T[cp d64 f32]", ST.cpu().numpy(), rST)
+
+
+def _plan(ws, N):
+    """The plan kda_chunk_fwd left at the head of its workspace: (segment length, per-sequence
+    segment counts, first summaries, segment lengths, pass-1 items, pass-2 items)."""
+    head = ws[:16].cpu().view(torch.int32).tolist()
+    n1, n2 = head[1], head[2]
+    p = ws[: (4 + 3 * N) * 4].cpu().view(torch.int32).tolist()
+    # item lists: pass 1 right after the per-sequence arrays; pass 2 after room for N + Smax
+    return p[0], p[4:4 + N], p[4 + N:4 + 2 * N], p[4 + 2 * N:4 + 3 * N], n1, n2
+
+
+def test_auto_split_long_sequence(gpu_lib):
+    """kda_chunk_fwd with a workspace on one long sequence of few heads: the host plan splits it
+    (the workspace it asks for is the segmented run's), and the result matches the oracle."""
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_prefill_inputs(1, 12000, 2, 64, 64, seed=91)
+    need = binding.chunk_fwd_workspace_size(1, 12000, 2, 64, 64, False)
+    summary = 2 * 64 * 128 * 4
+    assert need > 0 and need % summary == 0, need
+    print(f"  planned segments: {need // summary + 1}", flush=True)
+    o, ST = run_gpu(x, torch.float32)
+    ro, rST = oracle_all(x)
+    assert_close("o[auto split]", o, ro)
+    assert_close("S_T[auto split]", ST, rST)
+    op, STp = run_gpu(x, torch.float32, workspace=None)
+    assert_close("o[auto vs whole]", o, op)
+    assert_close("S_T[auto vs whole]", ST, STp)
+
+
+def test_auto_split_packed_by_length(gpu_lib):
+    """Packed sequences planned on the device: the longest get the most segments, the short ones
+    stay whole and run beside the first pass, summaries are indexed compactly; every sequence
+    matches the oracle (empty and one-token sequences included)."""
+    from linear_attention_chunkwise_amd import binding
+    lens = [9000, 300, 0, 45, 1500, 3000, 1, 20000]
+    cu = inputs.cu_from_lengths(lens)
+    N, H = len(lens), 2
+    x = inputs.make_prefill_inputs(1, int(cu[-1]), H, 128, 128, seed=92, cu_seqlens=cu)
+    need = binding.chunk_fwd_workspace_size(N, int(cu[-1]), H, 128, 128, True)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["cu_seqlens"],
+                              out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    L, P, first, seg, n1, n2 = _plan(ws, N)
+    print(f"  plan: L={L} P={P} first={first} seg={seg} items {n1} + {n2}", flush=True)
+    assert n1 == sum(p - 1 if p > 1 else 1 for p in P) and n2 == sum(p for p in P if p > 1)
+    assert L > 0 and L % 32 == 0
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pmax = min(16, -(-2 * cus // (H * 2)))
+    for n, ln in enumerate(lens):          # each sequence by its own length, at most pmax pieces
+        want = 1 if ln <= L else -(-ln // L)
+        if want > pmax:
+            assert P[n] == pmax and seg[n] == -(-(-(-ln // pmax)) // 32) * 32, (n, P[n], seg[n])
+        else:
+            assert P[n] == want, (n, P[n], want)
+            assert want == 1 or seg[n] == L
+    assert P[7] >= P[0] >= P[5] > 1
+    # the summaries of the split sequences tile [0, sum(P - 1)) without overlap
+    spans = sorted((first[n], P[n] - 1) for n in range(N) if P[n] > 1)
+    acc = 0
+    for f, c in spans:
+        assert f == acc, spans
+        acc += c
+    assert acc == sum(p - 1 for p in P)
+    ro, rST = oracle_all(x)
+    assert_close("o[auto packed]", o.cpu().numpy(), ro)
+    assert_close("S_T[auto packed]", ST.cpu().numpy(), rST)
+    assert np.array_equal(ST[2].cpu().numpy(), x["S0"][2].numpy())   # empty: S_T = S0
+
+
+def test_auto_split_leaves_full_batches_whole(gpu_lib):
+    """When the whole-sequence schedule already fills the GPU (B=4, H=32: 256 workgroups) the
+    workspace asked for is 0, and an in-place state (S_T = S0) never splits."""
+    from linear_attention_chunkwise_amd import binding
+    assert binding.chunk_fwd_workspace_size(4, 4 * 32768, 32, 128, 128, False) == 0
+    x = _to_dev(inputs.make_prefill_inputs(1, 5000, 2, 64, 64, seed=93))
+    ws = torch.empty(binding.chunk_fwd_workspace_size(1, 5000, 2, 64, 64, False), dtype=torch.uint8,
+                     device="cuda")
+    S = x["S0"].clone()
+    o1, _ = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], S, S_T=S, workspace=ws)
+    o2, S2 = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S, S2)
 
 
 @pytest.mark.slow
