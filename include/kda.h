@@ -284,7 +284,8 @@ kda_status kda_recurrent_multi(const void* q, const void* k, const void* v, cons
  * A_log [H] float32; norm_weight [dv] float32, 16-byte aligned, or NULL (ones); eps >= 0;
  * conv_weight [H, 2 dk + dv, W] float32 (channels of q, then k, then v; tap W - 1 weights the
  * current token) or NULL (no convolution and no Swish: q, k, v are used as given);
- * conv_state [N, H, 2 dk + dv, W - 1] in in_dtype, oldest input first (may be NULL when W = 1);
+ * conv_state [N, H, 2 dk + dv, W - 1] in in_dtype, oldest input first, 16-byte aligned (may be
+ * NULL when W = 1);
  * conv_width W in [1, 4] (ignored without conv_weight); S [N, H, dk, dv] float32; n_commit device
  * int32 [N] or NULL.  y may be NULL (no outputs; G is then not read).  None of S, conv_state and y
  * may overlap an input or each other.  Supported: dk, dv in {64, 128}.

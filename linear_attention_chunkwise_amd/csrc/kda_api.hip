@@ -576,7 +576,7 @@ kda_status kda_recurrent_multi_fused(const void* q, const void* k, const void* v
         KDA_TRY(check_ptr(conv_weight, 4, "conv_weight"));
         ncw = (size_t)H * nch * conv_width * 4;
         if (conv_width > 1) {
-            KDA_TRY(check_ptr(conv_state, es, "conv_state"));
+            KDA_TRY(check_ptr(conv_state, 16, "conv_state"));
             ncs = nh * nch * (conv_width - 1) * es;
         }
     }

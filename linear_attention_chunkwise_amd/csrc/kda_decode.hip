@@ -299,6 +299,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     __shared__ float bsig[256];                    // beta of the group's tokens (first KB)
     __shared__ float tqk[KB];                      // q^ . k^
     __shared__ __align__(16) float cwt[CONV ? XS : 1][8];
+    // the committed windows of the unit, staged in conv_state's own layout [NCH][W - 1] so that
+    // they leave as whole 16-byte stores instead of scattered 2- or 4-byte ones
+    __shared__ __align__(16) char cst[CONV ? NCH * 3 * (IN_F32 ? 4 : 2) : 16];
 
     const int unit = blockIdx.x;        // sequence * H + head
     if (unit >= N * H) return;
@@ -310,6 +313,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     KDA_POISON(bsig, sizeof bsig);
     KDA_POISON(tqk, sizeof tqk);
     KDA_POISON(cwt, sizeof cwt);
+    KDA_POISON(cst, sizeof cst);
     KDA_POISON_DONE();
     const int n = unit / H, h = unit % H;
     const int t = threadIdx.x;
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 #pragma unroll
                         for (int m = 0; m < 3; ++m) {
                             if (m >= 4 - W) {
-                                char* const o = csb + ((uint32_t)c * (W - 1) + (m - (4 - W))) * (uint32_t)ES;
+                                char* const o = cst + ((uint32_t)c * (W - 1) + (m - (4 - W))) * (uint32_t)ES;
                                 if constexpr (IN_F32) *reinterpret_cast<float*>(o) = wn[m];
                                 else *reinterpret_cast<bf16*>(o) = f2bf(wn[m]);
                             }
@@ -424,6 +428,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         }
         bsig[t] = sigm(br);
         __syncthreads();
+        if constexpr (CONV) {
+            // the group holds the commit (block-uniform): the staged windows go out whole
+            if (W > 1 && t0 < commit && commit <= t0 + kb) {
+                const uint32_t bytes = (uint32_t)NCH * (W - 1) * ES;
+                for (uint32_t i = 16 * t; i + 16 <= bytes; i += 16 * 256)
+                    *reinterpret_cast<uint4*>(csb + i) = *reinterpret_cast<const uint4*>(cst + i);
+                for (uint32_t i = bytes / 16 * 16 + ES * t; i < bytes; i += ES * 256) {
+                    if constexpr (IN_F32) *reinterpret_cast<float*>(csb + i) = *reinterpret_cast<const float*>(cst + i);
+                    else *reinterpret_cast<bf16*>(csb + i) = *reinterpret_cast<const bf16*>(cst + i);
+                }
+            }
+        }
         // L2Norm of q and k: wave wv normalises token wv of the group in place
         if (wv < kb) {
             float qq = 0.f, kk = 0.f, qk = 0.f;
