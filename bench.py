@@ -117,8 +117,10 @@ def measured_traffic(kernel_key, source_name):
 
 
 def measured_mfma_busy(kernel_key, source_name):
-    """Fraction of SIMD cycles with the MFMA unit busy during the kernel
-    (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4 SIMDs) per dispatch), or None."""
+    """Fraction of SIMD cycles with the MFMA unit busy during the kernel, or None:
+    SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES / 32 shader engines x 1024 SIMDs) per dispatch
+    (SQ_BUSY_CYCLES sums the shader engines, SQ_VALU_MFMA_BUSY_CYCLES every SIMD; the same
+    expression reads 0.985 for a loop of independent MFMAs)."""
     rec = _counters(kernel_key, source_name)
     return None if rec is None else rec.get("mfma_busy_frac")
 
