@@ -316,7 +316,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic("prefill_kernel<128,bf16,bf16>", "kda_prefill.hip"),
-                     "kernel": "prefill_kernel<128,bf16,bf16 out>"},
+                     "kernel": "prefill_kernel<128,bf16,bf16 out>",
+                     "limiter": "instruction issue and dependent-chain latency inside a workgroup "
+                                "(about 905 VALU and 90 MFMA instructions per SIMD per 32-token "
+                                "chunk); neither HBM (frac above) nor the MFMA pipes (prefill."
+                                "mfma_busy) is saturated"},
     }
     if not args.no_extras and not args.prefill_only:
         # variants, timed after the steps (not part of ms_per_step)
