@@ -112,7 +112,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * total_tokens tokens in all, on the current device (the plan depends on its compute units):
  * packed = 0 for fixed-length rows (n_seq rows of total_tokens / n_seq tokens: the exact need of
  * the plan, 0 when the rows are better left whole), packed = 1 for cu_seqlens batches (an upper
- * bound for any mix of lengths: the plan, 4 + 5 n_seq + 6 Smax int32 rounded up to 256 bytes,
+ * bound for any mix of lengths: the plan, 4 + 5 n_seq + 4 Smax int32 rounded up to 256 bytes,
  * then Smax = min(n_seq (Pmax - 1), total_tokens / Lmin) summaries of H x dk x (dv + dk)
  * float32, with Pmax
  * = min(16, ceil(2 CUs / (H dv / 64))) segments per sequence and Lmin = max(1024, ceil(
@@ -170,7 +170,7 @@ size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t
 /* The segment count for kda_chunk_fwd_cp that suits a GPU with `slots` concurrent prefill
  * workgroups (one per CU: 256 on MI355X): the largest P <= 64 for which both passes below fit in
  * one round, pass 1 with N*H*(dv/64 + (P-2)*(dv+dk)/64) working workgroups and pass 2 with
- * N*H*P*dv/64; 1 when P = 2 does not fit either (then kda_chunk_fwd is as fast).  Host arithmetic
+ * N*H*(P-1)*dv/64; 1 when P = 2 does not fit either (then kda_chunk_fwd is as fast).  Host arithmetic
  * only (no device call); 1 for non-positive arguments. */
 int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t slots);
 
@@ -184,9 +184,11 @@ int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, 
  * Segment length: each sequence's own ceil(len / segments) rounded up to a multiple of 32 (pieces
  * past its end are empty).
  * Pass 1 writes, for every sequence, head and segment but the last, [S~ | M] (dk x (dv + dk),
- * float32; segment 0 is entered with S0) to `workspace`; pass 2 rebuilds each segment's entering
- * state S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1} and produces its outputs.  Same results as
- * kda_chunk_fwd within the operator's tolerance (the summaries are computed with the same
+ * float32; segment 0 is entered with S0 and writes its outputs too) to `workspace`; the
+ * workgroups of the transition columns M stop as soon as those columns are exactly zero (they
+ * stay zero: the result is the same bit for bit).  Pass 2 rebuilds the entering state of each
+ * later segment, S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1}, and produces its outputs.  Same results
+ * as kda_chunk_fwd within the operator's tolerance (the summaries are computed with the same
  * arithmetic; the combination uses split bf16 products with float32 accumulation).
  *
  * N * H * segments <= 2^28 (KDA_ERR_UNSUPPORTED beyond).

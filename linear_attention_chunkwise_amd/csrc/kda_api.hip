@@ -375,7 +375,7 @@ int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, 
     int32_t best = 1;
     for (int32_t p = 2; p <= 64; ++p) {
         const int64_t pass1 = units * (dv / 64 + (int64_t)(p - 2) * ((dv + dk) / 64));
-        const int64_t pass2 = units * p * (dv / 64);
+        const int64_t pass2 = units * (p - 1) * (dv / 64);
         if (pass1 > slots || pass2 > slots) break;
         best = p;
     }

@@ -53,7 +53,8 @@ struct PrefillArgs {
 //   segs[N], first summary[N], segment length[N] per sequence,
 //   pass-1 items [N + Smax] x {sequence, segment}: the summaries of the split sequences and the
 //   whole runs of the others, longest sequences first,
-//   pass-2 items [2 Smax] x {sequence, segment}: the segments of the split sequences.
+//   pass-2 items [Smax] x {sequence, segment}: the segments after the first of the split
+//   sequences (the first segment writes its outputs in pass 1).
 struct PlanLayout {
     int32_t N, Smax;
     __host__ __device__ int64_t segs() const { return 4; }
@@ -61,9 +62,9 @@ struct PlanLayout {
     __host__ __device__ int64_t seglen() const { return 4 + 2 * (int64_t)N; }
     __host__ __device__ int64_t items1() const { return 4 + 3 * (int64_t)N; }
     __host__ __device__ int64_t items2() const { return items1() + 2 * ((int64_t)N + Smax); }
-    __host__ __device__ int64_t ints() const { return items2() + 4 * (int64_t)Smax; }
+    __host__ __device__ int64_t ints() const { return items2() + 2 * (int64_t)Smax; }
     __host__ __device__ int32_t max_items1() const { return N + Smax; }
-    __host__ __device__ int32_t max_items2() const { return 2 * Smax; }
+    __host__ __device__ int32_t max_items2() const { return Smax; }
 };
 
 struct DecodeArgs {
@@ -103,12 +104,13 @@ hipError_t launch_chunk_fwd(const PrefillArgs& a);
 // ---- Splitting sequences in time (in-device context parallelism).  Costs are in chunk steps
 // of one workgroup (one 32-token chunk of one 64-column slice).  A sequence of len tokens left
 // whole costs nsl workgroups x ceil(len / 32) steps, all in pass 1 (beside the summaries).  Split
-// into P segments of Ls tokens it costs, in pass 1, nsl x ceil(Ls / 32) for the summary of its
-// first segment (value columns) and nslt x ceil(Ls / 32) for each of the next P - 2 (value and
-// transition columns), and in pass 2 nsl x (ceil(Ls_j / 32) + j) for segment j (its tokens and
-// the j summaries it composes).  A pass on `slots` concurrent workgroups takes at least its
-// longest workgroup and at least its total work / slots; a plan is priced at the sum of the two
-// passes' bounds.
+// into P segments of Ls tokens it costs, in pass 1, nsl x ceil(Ls / 32) for its first segment
+// (its outputs and the summary of its value columns) and nslt x ceil(Ls / 32) for each of the
+// next P - 2 (value and transition columns; the transition workgroups stop early once their
+// columns are exactly zero, which the model does not count on), and in pass 2
+// nsl x (ceil(Ls_j / 32) + j) for segment j >= 1 (its tokens and the j summaries it composes).
+// A pass on `slots` concurrent workgroups takes at least its longest workgroup and at least its
+// total work / slots; a plan is priced at the sum of the two passes' bounds.
 struct SplitCost {
     double work1 = 0, work2 = 0;   // per head
     int64_t crit1 = 0, crit2 = 0;
@@ -139,7 +141,7 @@ __host__ __device__ inline void split_add(SplitCost& c, int64_t len, int P, int6
     const int64_t ch = chunks_of(Ls);
     c.work1 += (double)ch * (nsl + (double)nslt * (P - 2));
     c.crit1 = c.crit1 > ch ? c.crit1 : ch;
-    c.work2 += (double)nsl * ((double)chunks_of(len) + (double)P * (P - 1) / 2);
+    c.work2 += (double)nsl * ((double)(chunks_of(len) - ch) + (double)P * (P - 1) / 2);
     c.crit2 = c.crit2 > ch + P - 1 ? c.crit2 : ch + P - 1;
     c.summaries += P - 1;
 }
@@ -148,6 +150,11 @@ __host__ __device__ inline double split_makespan(const SplitCost& c, int H, int 
     const double m1 = (double)c.crit1 > w1 ? (double)c.crit1 : w1;
     const double m2 = c.summaries ? ((double)c.crit2 > w2 ? (double)c.crit2 : w2) : 0.0;
     return m1 + m2;
+}
+// The candidate segment length that cuts a sequence of `longest` tokens into P pieces (whole
+// chunks); the planners try P = 2 .. Pmax for the longest sequence of the batch.
+__host__ __device__ inline int64_t split_candidate(int64_t longest, int P) {
+    return ((longest + P - 1) / P + 31) / 32 * 32;
 }
 // A split must beat the whole-sequence schedule by this factor (extra launch, rough chain cost).
 constexpr double kSplitGain = 0.95;

@@ -94,7 +94,9 @@ struct Layout {
     static constexpr int o_N = o_W + DK * TB * 2;           // fp32 2 blocks [16][20]: solve scratch
     static constexpr int o_Pub = o_N + 2 * SB * 4;          // fp32 3 blocks [16][20]: T00, T11, N10
     static constexpr int total = o_Pub + 3 * SB * 4;
-    static_assert(total <= 160 * 1024, "LDS budget");
+    static constexpr int o_stop = total;                    // int [4]: consumer votes to stop early
+    static constexpr int total_summ = total + 16;           // (first pass of a split in time)
+    static_assert(total + 16 <= 160 * 1024, "LDS budget");
     static_assert(GPB >= 4 * (1024 + 1), "sequence ranking scratch fits the Gram region");
     static_assert(o_QK % 16 == 0 && QKB % 16 == 0 && o_Tb % 16 == 0 && o_W % 16 == 0 && o_N % 16 == 0,
                   "16-byte aligned regions");
@@ -238,15 +240,35 @@ __device__ __forceinline__ constexpr int pm(int c) {
 
 // One block of the grid -> (unit, column slice), slices of a unit on one XCD (the dispatcher
 // places consecutive workgroups on consecutive XCDs, 8 of them).
-__device__ __forceinline__ void block_coords(int nslices, int& unit, int& slice) {
+// Workgroups are dispatched in order, round-robin over the 8 XCDs (block b to XCD b mod 8); the
+// slices of one unit stay on one XCD so that their reads of q, k, g share its L2.  SUMM (the first
+// pass of a split in time, nv value slices and nslices - nv transition slices per unit): all
+// transition slices come first.  Their workgroups are short (a sequence's first and last
+// segments have none; the others stop once the transition is zero), and an XCD dispatches in
+// order, waiting while the shader engine a workgroup is bound for is full: placed after the
+// long-running value slices, a short workgroup would hold back every later value slice until a
+// long one ends.
+template <bool SUMM>
+__device__ __forceinline__ void block_coords(int nslices, int nv, int& unit, int& slice) {
     const int b = blockIdx.x;
     const int xcd = b & 7, slot = b >> 3;
+    if (SUMM && nslices > nv) {
+        const int per_xcd = gridDim.x / (8 * nslices);   // units per XCD (the grid is a multiple)
+        const int nt = nslices - nv;
+        if (slot < per_xcd * nt) {
+            unit = (slot / nt) * 8 + xcd;
+            slice = nv + slot % nt;
+        } else {
+            const int s2 = slot - per_xcd * nt;
+            unit = (s2 / nv) * 8 + xcd;
+            slice = s2 % nv;
+        }
+        return;
+    }
     unit = (slot / nslices) * 8 + xcd;
     slice = slot % nslices;
 }
 
-// Buffer resource over [base, base + bytes): loads at or past `bytes` return zero, so the ragged
-// tail of a sequence needs neither branches nor clamped addresses.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
@@ -302,6 +324,13 @@ struct Raw8 {
 };
 
 // Sequence bounds (clamped: malformed cu_seqlens never produce out-of-bounds accesses).
+// Every consumer wave of the workgroup voted to stop (read after the barrier that ends the
+// interval in which the votes were written; a scalar result).
+__device__ __forceinline__ bool stop_voted(const char* votes) {
+    const int4 f = *reinterpret_cast<const int4*>(votes);
+    return __builtin_amdgcn_readfirstlane(f.x & f.y & f.z & f.w) != 0;
+}
+
 __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t& row0, int64_t& len) {
     if (a.cu) {
         int64_t s0 = a.cu[n], s1 = a.cu[n + 1];
@@ -320,9 +349,9 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t&
 // operands and the partial Gram tiles of chunk it (interval 1); the rows of W over the wave's
 // channels and a row tile of M for chunk it - 1, then Q~, K~, gamma and K_end of chunk it
 // (interval 2).
-template <int DK, bool F32IN, bool GATE>
+template <int DK, bool F32IN, bool GATE, bool SUMM>
 __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p, int lane,
-                                         int64_t row0, int64_t len, int h) {
+                                         int64_t row0, int64_t len, int h, bool tslice) {
     using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr int RB = Lay::RB, TB = Lay::TB;
@@ -632,6 +661,12 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
         }
         if (intra && it + 1 < nchunks) prep(it + 1);
         __syncthreads();
+        if constexpr (SUMM) {
+            if (tslice && stop_voted(smem + Lay::o_stop)) {
+                __builtin_amdgcn_s_waitcnt(0);   // the next chunk's loads are abandoned
+                return;
+            }
+        }
     }
 }
 
@@ -641,10 +676,10 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 // it - 1 with its off-diagonal block); for chunk it the diagonal blocks of the UT transform
 // (cw = 0, 1), beta N10 and the A_qk tiles (cw = 2, 3), and the scale of the value path for
 // chunk it - 1 (interval 2).
-template <int DK, bool F32IN, bool OUT_F32>
+template <int DK, bool F32IN, bool OUT_F32, bool SUMM>
 __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
                                          int64_t row0, int64_t len, int n, int h, int slice, int seg,
-                                         int mode, int nseg_n, int64_t sbase) {
+                                         int mode, int nseg_n, int64_t sbase, bool tslice) {
     using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr int KS = DK / 32;          // 32-channel contraction steps
@@ -779,9 +814,9 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         if (it >= 2) {
             const int64_t c = it - 2, c0 = c * kC;
             const char* qk = smem + Lay::o_QK + (int)(c % 3) * Lay::QKB;
-            const uint32_t nvalid = mode == 1 ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
+            const uint32_t nvalid = (mode == 1 && (!SUMM || seg > 0)) ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
             // output rows of the chunk: stores at or past row nvalid fall outside the resource
-            // (summaries write no outputs)
+            // (summaries write no outputs, except those of a first segment, entered with S0)
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(obc, nvalid * (uint32_t)(sv * sizeof(OT)));
             obc += (size_t)kC * sv;
             // batch 1: rows of K~, Q~ and M
@@ -1047,7 +1082,25 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 }
             }
         }
+        if (SUMM && tslice) {
+            // transition columns: V is 0, so once every entry is exactly zero every later step
+            // leaves them zero (R = 0 - K~ 0, S <- gamma 0 + W 0); this wave's vote to stop
+            uint32_t nz = 0;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) nz |= __builtin_bit_cast(uint32_t, Sacc[ct][j]) & 0x7fffffffu;
+            const bool zero = __builtin_amdgcn_ballot_w64(nz != 0) == 0;
+            if (lane == 0) reinterpret_cast<int*>(smem + Lay::o_stop)[cw] = zero ? 1 : 0;
+        }
         __syncthreads();
+        if constexpr (SUMM) {
+            if (tslice && stop_voted(smem + Lay::o_stop)) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();   // +0, as the remaining steps give
+                break;
+            }
+        }
     }
 
     const float un = __builtin_ldexpf(1.f, esc);
@@ -1102,38 +1155,41 @@ __device__ int seq_of_rank(const PrefillArgs& a, int r, char* smem) {
     return n;
 }
 
-// Both roles run the same number of iterations (chunks + 2) with two barriers each.  RANK: packed
-// sequences (at most kRankMax) in longest-first order; a separate instantiation, so that the
-// fixed-length kernel's code is not changed by the ranking.
-template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
+// Both roles run the same number of iterations (chunks + 2) with two barriers each.  PASS: 0 a
+// whole-sequence run, 1 the first pass of a split in time (segment summaries; first segments
+// also write their outputs; transition workgroups may stop early), 2 its second pass (the later
+// segments); a.mode equals PASS.  RANK: packed sequences (at most kRankMax) in longest-first
+// order.  Separate instantiations, so that the plain kernel carries none of the split's code.
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, int PASS>
 __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int nslices = (a.mode == 1 ? a.dv + a.dk : a.dv) / kDVT;
-    const int nseg = a.mode == 0 ? 1 : a.nseg;   // segments per sequence in the grid (at most)
+    constexpr bool SUMM = PASS == 1;
+    const int nslices = (SUMM ? a.dv + a.dk : a.dv) / kDVT;
+    const int nseg = PASS == 0 ? 1 : a.nseg;   // segments per sequence in the grid (at most)
     int unit, slice;
-    block_coords(nslices, unit, slice);
-    int n, seg, mode = a.mode, nseg_n = 1;
+    block_coords<SUMM>(nslices, a.dv / kDVT, unit, slice);
+    int n, seg, mode = PASS, nseg_n = 1;
     int64_t sbase = 0, row0, len;
     const int h = unit % a.H;
-    if (a.plan) {
+    if (PASS != 0 && a.plan) {
         // a planned split: the workgroup's item of this pass's list
         const PlanLayout lay{a.N, a.plan_smax};
         const int item = unit / a.H;
-        if (item >= a.plan[a.mode]) return;
-        const int32_t* it = a.plan + (a.mode == 1 ? lay.items1() : lay.items2()) + 2 * (int64_t)item;
+        if (item >= a.plan[PASS]) return;
+        const int32_t* it = a.plan + (SUMM ? lay.items1() : lay.items2()) + 2 * (int64_t)item;
         n = it[0];
         seg = it[1];
         nseg_n = a.plan[lay.segs() + n];
         sbase = a.plan[lay.first() + n];
         const int64_t L = a.plan[lay.seglen() + n];
-        if (nseg_n <= 1) {
+        if (SUMM && nseg_n <= 1) {
             // a sequence the plan leaves whole runs here completely, beside the summaries
             if (slice * kDVT >= a.dv) return;
             mode = 0;
-        } else if (a.mode == 1 && seg == 0 && slice * kDVT >= a.dv) {
+        } else if (SUMM && seg == 0 && slice * kDVT >= a.dv) {
             return;   // the first segment is entered with S0: no transition columns
         }
-        KDA_POISON(smem, (Layout<DK>::total));
+        KDA_POISON(smem, (SUMM ? Layout<DK>::total_summ : Layout<DK>::total));
         KDA_POISON_DONE();
         seq_bounds(a, n, row0, len);
         if (mode != 0) {   // this segment's tokens
@@ -1148,13 +1204,14 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         const int rank = unit / (a.H * nseg);
         // every sequence has nseg segments: summaries are needed for all but the last, and on
         // value columns only for the first
-        if (a.mode == 1 && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;
-        KDA_POISON(smem, (Layout<DK>::total));
+        if (SUMM && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;
+        if (PASS == 2 && seg == 0) return;   // the first segment wrote its outputs in pass 1
+        KDA_POISON(smem, (SUMM ? Layout<DK>::total_summ : Layout<DK>::total));
         KDA_POISON_DONE();
         n = rank;
         if constexpr (RANK) n = seq_of_rank(a, rank, smem);
         seq_bounds(a, n, row0, len);
-        if (a.mode != 0) {
+        if (PASS != 0) {
             // nseg segments of ceil(len / nseg) tokens rounded up to whole chunks
             nseg_n = nseg;
             sbase = (int64_t)n * (nseg - 1);
@@ -1168,14 +1225,18 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
-    if (wave < kNW) producer<DK, F32IN, GATE>(a, smem, wave, lane, row0, len, h);
-    else consumer<DK, F32IN, OUT_F32>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg, mode, nseg_n, sbase);
+    // a workgroup of transition columns (segment summaries) may stop once they are all zero
+    const bool tslice = SUMM && mode == 1 && slice * kDVT >= a.dv;
+    if (wave < kNW) producer<DK, F32IN, GATE, SUMM>(a, smem, wave, lane, row0, len, h, tslice);
+    else consumer<DK, F32IN, OUT_F32, SUMM>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg, mode, nseg_n,
+                                            sbase, tslice);
 }
 
-template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK>
+template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, int PASS>
 static hipError_t launch_one(const PrefillArgs& a) {
     using Lay = Layout<DK>;
-    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE, RANK>;
+    constexpr bool SUMM = PASS == 1;
+    auto kern = prefill_kernel<DK, F32IN, OUT_F32, GATE, RANK, PASS>;
     // The LDS limit is a per-device attribute of the kernel: set it once on each device this
     // instantiation launches on (devices past 63 set it on every launch).  Concurrent first calls
     // may both set it; the value is the same.
@@ -1186,7 +1247,7 @@ static hipError_t launch_one(const PrefillArgs& a) {
     const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
     if (!(attr_set.load(std::memory_order_relaxed) & bit) || !bit) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                Lay::total);
+                                SUMM ? Lay::total_summ : Lay::total);
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit, std::memory_order_relaxed);
     }
@@ -1194,14 +1255,27 @@ static hipError_t launch_one(const PrefillArgs& a) {
     const int64_t units = a.plan ? (int64_t)a.plan_items * a.H : (int64_t)a.N * a.H * (a.mode == 0 ? 1 : a.nseg);
     const int64_t blocks = ((units + 7) / 8) * 8 * nslices;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kNT), Lay::total, a.stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kNT), SUMM ? Lay::total_summ : Lay::total, a.stream, a);
     return hipGetLastError();
 }
 
 template <int DK, bool F32IN, bool OUT_F32, bool GATE>
 static hipError_t launch_prefill(const PrefillArgs& a) {
-    if (a.cu && !a.plan && a.N > 1 && a.N <= kRankMax) return launch_one<DK, F32IN, OUT_F32, GATE, true>(a);
-    return launch_one<DK, F32IN, OUT_F32, GATE, false>(a);
+    const bool rank = a.cu && !a.plan && a.N > 1 && a.N <= kRankMax;
+    if (a.mode == 1 || a.mode == 2) {
+        // the passes of a split in time (the decay map is not offered there)
+        if constexpr (GATE) {
+            return hipErrorInvalidValue;
+        } else {
+            if (a.mode == 1)
+                return rank ? launch_one<DK, F32IN, OUT_F32, GATE, true, 1>(a)
+                            : launch_one<DK, F32IN, OUT_F32, GATE, false, 1>(a);
+            return rank ? launch_one<DK, F32IN, OUT_F32, GATE, true, 2>(a)
+                        : launch_one<DK, F32IN, OUT_F32, GATE, false, 2>(a);
+        }
+    }
+    if (rank) return launch_one<DK, F32IN, OUT_F32, GATE, true, 0>(a);
+    return launch_one<DK, F32IN, OUT_F32, GATE, false, 0>(a);
 }
 
 template <bool GATE>
@@ -1233,7 +1307,9 @@ int32_t plan_fixed_segments(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t
     const double base = split_makespan(whole, H, slots);
     double best = base * kSplitGain;
     int32_t bestP = 1;
-    for (int64_t L = lim.Lmin; L < T; L *= 2) {
+    for (int p = 2; p <= lim.Pmax; ++p) {
+        const int64_t L = split_candidate(T, p);
+        if (L < lim.Lmin) break;
         int P;
         int64_t Ls;
         split_of(T, L, lim.Pmax, P, Ls);
@@ -1252,8 +1328,8 @@ int32_t plan_fixed_segments(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t
     return bestP;
 }
 
-// One workgroup of 256 threads prices every candidate segment length (the minimum doubled
-// until it covers the longest sequence) with the model above and writes the plan of the best.
+// One workgroup of 256 threads prices every candidate segment length (the longest sequence cut
+// into 2 .. Pmax pieces) with the model above and writes the plan of the best.
 __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __restrict__ plan, int slots,
                                                    SplitLimits lim) {
     __shared__ double rd[2][256];
@@ -1302,7 +1378,9 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
     const int64_t longest = whole.crit1 * 32;   // in tokens, rounded up to whole chunks
     double best = split_makespan(whole, H, slots) * kSplitGain;
     int64_t bestL = 0;
-    for (int64_t L = lim.Lmin; L < longest; L *= 2) {
+    for (int p = 2; p <= lim.Pmax; ++p) {
+        const int64_t L = split_candidate(longest, p);
+        if (L < lim.Lmin) break;
         SplitCost c;
         price(L, c);
         if (c.summaries > lim.Smax) continue;
@@ -1349,7 +1427,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             plan[lay.seglen() + n] = (int32_t)(P > 1 ? Ls : (Ls > 0 ? Ls : kC));
         }
         const int na = r < N ? (P > 1 ? P - 1 : 1) : 0;   // pass-1 items
-        const int nb = r < N && P > 1 ? P : 0;             // pass-2 items
+        const int nb = r < N && P > 1 ? P - 1 : 0;         // pass-2 items (segments 1 .. P - 1)
         const int ns = r < N ? P - 1 : 0;                  // summaries
         sc[0][t] = ns;
         sc[1][t] = na;
@@ -1375,7 +1453,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             }
             for (int j = 0; j < nb; ++j) {
                 B[2 * (ib + j)] = n;
-                B[2 * (ib + j) + 1] = j;
+                B[2 * (ib + j) + 1] = j + 1;
             }
         }
         c_sum += sc[0][255];

@@ -636,6 +636,34 @@ def test_segmented_weak_decay_carries_state(gpu_lib, segments):
     print(f"  max |o_cp - o_plain| = {diff:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("weak", [False, True], ids=["decay_vanishes", "weak_decay"])
+def test_segmented_transitions_stop_once_zero(gpu_lib, weak):
+    """The workgroups of a segment's transition columns stop as soon as those columns are exactly
+    zero (they stay zero).  With the workload's decay every transition a summary holds is +0.0 bit
+    for bit (the workspace is filled with 0xFF first, so the zeros were written); with weak decay
+    the transitions are carried in full.  Both runs match the oracle."""
+    from linear_attention_chunkwise_amd import binding
+    H, dk, dv, P = 2, 128, 128, 4
+    x = inputs.make_prefill_inputs(1, 4096, H, dk, dv, seed=43)
+    if weak:
+        x["g"] = x["g"] * 0.002
+    d = _to_dev(x)
+    need = binding.load().kda_chunk_fwd_cp_workspace_size(1, H, dk, dv, P)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    o, ST = binding.chunk_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], segments=P,
+                                 out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    summ = ws.view(torch.int32).view(P - 1, H, dk, dv + dk).cpu()   # [S~ | M] per segment, head
+    trans = summ[1:, :, :, dv:]                  # segment 0 is entered with S0: no transition
+    if weak:
+        assert (trans != 0).any()
+    else:
+        assert (trans == 0).all(), "a transition that vanished was not written as +0.0"
+    ro, rST = oracle_all(x)
+    assert_close("o[cp transitions]", o.cpu().numpy(), ro)
+    assert_close("S_T[cp transitions]", ST.cpu().numpy(), rST)
+
+
 def test_segmented_varlen_and_dk64(gpu_lib):
     """Varlen batch (segments past a sequence's end are empty) and the d = 64 float32-input
     kernel, segmented."""
@@ -707,7 +735,7 @@ def test_auto_split_packed_by_length(gpu_lib):
     torch.cuda.synchronize()
     L, P, first, seg, n1, n2 = _plan(ws, N)
     print(f"  plan: L={L} P={P} first={first} seg={seg} items {n1} + {n2}", flush=True)
-    assert n1 == sum(p - 1 if p > 1 else 1 for p in P) and n2 == sum(p for p in P if p > 1)
+    assert n1 == sum(p - 1 if p > 1 else 1 for p in P) and n2 == sum(p - 1 for p in P if p > 1)
     assert L > 0 and L % 32 == 0
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     pmax = min(16, -(-2 * cus // (H * 2)))
