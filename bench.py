@@ -394,11 +394,10 @@ def main():
                                    "tokens": Tv, "tokens_per_s": Tv / (v_ms * 1e-3),
                                    "longest": int(lens.max()), "alg_GBps": vbytes / (v_ms * 1e-3) / 1e9,
                                    "what": "kda_chunk_fwd on 64 packed sequences (cu_seqlens), "
-                                           "H=32, d=128, as kda_chunk_fwd plans it (ms; 4096 "
-                                           "workgroups already fill the GPU, so it asks for no "
-                                           "workspace and runs every sequence whole: "
-                                           "planned_segment_len 0) and with no workspace "
-                                           "(whole_ms); the longest sequence runs first"}
+                                           "H=32, d=128, with the workspace of its automatic plan "
+                                           "(ms; planned_segment_len: the plan's segment length, "
+                                           "0 for no split) and with no workspace (whole_ms: "
+                                           "every sequence whole, the longest first)"}
         del xv, ov, STv, wsv
         # long prefill: one sequence of 2^20 tokens, 32 heads: plain (64 workgroups) and split in
         # time with the library's segment count for this GPU (kda_chunk_fwd_cp_segments)

@@ -93,8 +93,8 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * split sequences in time.  It prices each candidate segment length with a model of the two
  * passes on this GPU's compute units (a pass lasts at least its longest workgroup and at least
  * its total work over the units) and splits only when that beats the whole-sequence schedule.
- * Fixed-length rows are planned on the host (all rows alike); packed batches of few sequences
- * (fewer than two whole-sequence workgroups per compute unit) are planned on the device from
+ * Fixed-length rows are planned on the host (all rows alike); packed batches (at most 16
+ * whole-sequence workgroups, n_seq H dv / 64, per compute unit) are planned on the device from
  * cu_seqlens (no host synchronisation), each sequence by its own length: longer sequences get
  * more segments, sequences no longer than the segment length stay whole and run beside the
  * first pass.  Larger packed batches run whole.  Results agree with the whole-sequence run within the operator's
@@ -117,7 +117,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * float32, with Pmax
  * = min(16, ceil(2 CUs / (H dv / 64))) segments per sequence and Lmin = max(1024, ceil(
  * total_tokens / 64) rounded up to 32) tokens per segment; 0 beyond 65536 sequences and when
- * the whole-sequence grid, n_seq H dv / 64 workgroups, already reaches two per compute unit:
+ * the whole-sequence grid, n_seq H dv / 64 workgroups, exceeds 16 per compute unit:
  * such batches run whole).  0 for unsupported sizes. */
 size_t kda_chunk_fwd_workspace_size(int32_t n_seq, int64_t total_tokens, int32_t H, int32_t dk,
                                     int32_t dv, int32_t packed);

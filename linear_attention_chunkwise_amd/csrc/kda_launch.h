@@ -160,12 +160,13 @@ __host__ __device__ inline int64_t split_candidate(int64_t longest, int P) {
 constexpr double kSplitGain = 0.95;
 // Packed batches are planned on the device up to this many sequences (one workgroup prices them).
 constexpr int32_t kPlanMaxSeqs = 65536;
-// ... and only when their whole-sequence grid (N H dv / 64 workgroups) is under two per compute
-// unit: a larger batch already fills the GPU, and its planned launches would carry that many
-// idle workgroups through the dispatcher for a gain the model rarely finds (a packed batch of 64
-// sequences of 32 heads priced no split, and the idle grid cost about 1 ms of 6).
+// ... and only when their whole-sequence grid (N H dv / 64 workgroups) is at most kPlanWgsPerCu
+// per compute unit: the planned launches carry a grid sized for the largest plan, whose unused
+// workgroups pass through the dispatcher, while a batch that many times the GPU's size is rarely
+// bound by one sequence's chain.
+constexpr int32_t kPlanWgsPerCu = 16;
 __host__ __device__ inline bool plan_packed(int32_t N, int32_t H, int32_t dv, int slots) {
-    return N <= kPlanMaxSeqs && (int64_t)N * H * (dv / 64) < 2 * (int64_t)slots;
+    return N <= kPlanMaxSeqs && (int64_t)N * H * (dv / 64) <= (int64_t)kPlanWgsPerCu * slots;
 }
 // Limits of the automatic plan on a GPU with `slots` concurrent workgroups: segments per
 // sequence, the shortest segment, and the number of summaries the workspace holds per head.
