@@ -1421,7 +1421,7 @@ def test_offsets_check_on_request(gpu_lib, monkeypatch):
 
 def test_range_check_from_concurrent_threads(gpu_lib, monkeypatch):
     """The domain check's flag is one per device: checked calls from two host threads on their own
-    streams, one with g in range and one with a value outside it, each get their own verdict."""
+    streams, one with g in range and one with a value outside it, each get their own result."""
     import threading
     from linear_attention_chunkwise_amd import binding
     d = _to_dev(inputs.make_decode_inputs(64, 8, 64, 64, seed=35))
