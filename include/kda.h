@@ -97,9 +97,9 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * whole-sequence workgroups, n_seq H dv / 64, per compute unit) are planned on the device from
  * cu_seqlens (no host synchronisation), each sequence by its own length: longer sequences get
  * more segments, sequences no longer than the segment length stay whole and run beside the
- * first pass.  Larger packed batches run whole.  Results agree with the whole-sequence run within the operator's
- * tolerance (not bit for bit).  With workspace NULL or too small, or S_T aliasing S0, every
- * sequence runs whole (workspace_bytes is then not checked).
+ * first pass.  Larger packed batches run whole.  Results agree with the whole-sequence run
+ * within the operator's tolerance (not bit for bit).  With workspace NULL or too small, or S_T
+ * aliasing S0, every sequence runs whole (workspace_bytes is then not checked).
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const void* beta, const float* S0, const int32_t* cu_seqlens,
