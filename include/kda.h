@@ -96,8 +96,9 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * Fixed-length rows are planned on the host (all rows alike); packed batches (at most 16
  * whole-sequence workgroups, n_seq H dv / 64, per compute unit) are planned on the device from
  * cu_seqlens (no host synchronisation), each sequence by its own length: longer sequences get
- * more segments, sequences no longer than the segment length stay whole and run beside the
- * first pass.  Larger packed batches run whole.  Results agree with the whole-sequence run
+ * more segments, sequences no longer than the segment length stay whole and run in the second
+ * pass while its idle capacity (compute units x its longest workgroup, less its work) lasts,
+ * longest first, the rest beside the first pass.  Larger packed batches run whole.  Results agree with the whole-sequence run
  * within the operator's tolerance (not bit for bit).  With workspace NULL or too small, or S_T
  * aliasing S0, every sequence runs whole (workspace_bytes is then not checked).
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
@@ -112,7 +113,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * total_tokens tokens in all, on the current device (the plan depends on its compute units):
  * packed = 0 for fixed-length rows (n_seq rows of total_tokens / n_seq tokens: the exact need of
  * the plan, 0 when the rows are better left whole), packed = 1 for cu_seqlens batches (an upper
- * bound for any mix of lengths: the plan, 4 + 5 n_seq + 4 Smax int32 rounded up to 256 bytes,
+ * bound for any mix of lengths: the plan, 4 + 7 n_seq + 4 Smax int32 rounded up to 256 bytes,
  * then Smax = min(n_seq (Pmax - 1), total_tokens / Lmin) summaries of H x dk x (dv + dk)
  * float32, with Pmax
  * = min(16, ceil(2 CUs / (H dv / 64))) segments per sequence and Lmin = max(1024, ceil(

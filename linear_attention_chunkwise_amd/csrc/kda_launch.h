@@ -53,8 +53,9 @@ struct PrefillArgs {
 //   segs[N], first summary[N], segment length[N] per sequence,
 //   pass-1 items [N + Smax] x {sequence, segment}: the summaries of the split sequences and the
 //   whole runs of the others, longest sequences first,
-//   pass-2 items [Smax] x {sequence, segment}: the segments after the first of the split
-//   sequences (the first segment writes its outputs in pass 1).
+//   pass-2 items [N + Smax] x {sequence, segment}: the segments after the first of the split
+//   sequences (the first segment writes its outputs in pass 1), then the whole runs moved into
+//   the second pass's idle slots.
 struct PlanLayout {
     int32_t N, Smax;
     __host__ __device__ int64_t segs() const { return 4; }
@@ -62,9 +63,9 @@ struct PlanLayout {
     __host__ __device__ int64_t seglen() const { return 4 + 2 * (int64_t)N; }
     __host__ __device__ int64_t items1() const { return 4 + 3 * (int64_t)N; }
     __host__ __device__ int64_t items2() const { return items1() + 2 * ((int64_t)N + Smax); }
-    __host__ __device__ int64_t ints() const { return items2() + 2 * (int64_t)Smax; }
+    __host__ __device__ int64_t ints() const { return items2() + 2 * ((int64_t)N + Smax); }
     __host__ __device__ int32_t max_items1() const { return N + Smax; }
-    __host__ __device__ int32_t max_items2() const { return Smax; }
+    __host__ __device__ int32_t max_items2() const { return N + Smax; }
 };
 
 struct DecodeArgs {
@@ -110,9 +111,13 @@ hipError_t launch_chunk_fwd(const PrefillArgs& a);
 // columns are exactly zero, which the model does not count on), and in pass 2
 // nsl x (ceil(Ls_j / 32) + j) for segment j >= 1 (its tokens and the j summaries it composes).
 // A pass on `slots` concurrent workgroups takes at least its longest workgroup and at least its
-// total work / slots; a plan is priced at the sum of the two passes' bounds.
+// total work / slots; a plan is priced at the sum of the two passes' bounds.  Where the second
+// pass leaves slots idle (slots x its longest workgroup above its work), sequences left whole
+// run there instead of in the first pass, up to the idle capacity: each is no longer than the
+// segment length, so it fits under the second pass's longest workgroup.
 struct SplitCost {
     double work1 = 0, work2 = 0;   // per head
+    double whole = 0;              // per head: the part of work1 in sequences left whole
     int64_t crit1 = 0, crit2 = 0;
     int64_t summaries = 0;         // per head
 };
@@ -135,6 +140,7 @@ __host__ __device__ inline void split_of(int64_t len, int64_t L, int Pmax, int& 
 __host__ __device__ inline void split_add(SplitCost& c, int64_t len, int P, int64_t Ls, int nsl, int nslt) {
     if (P <= 1) {
         c.work1 += (double)nsl * chunks_of(len);
+        c.whole += (double)nsl * chunks_of(len);
         c.crit1 = c.crit1 > chunks_of(len) ? c.crit1 : chunks_of(len);
         return;
     }
@@ -145,8 +151,16 @@ __host__ __device__ inline void split_add(SplitCost& c, int64_t len, int P, int6
     c.crit2 = c.crit2 > ch + P - 1 ? c.crit2 : ch + P - 1;
     c.summaries += P - 1;
 }
+// The idle capacity of the second pass, in work per head (0 without a split).
+__host__ __device__ inline double split_idle2(const SplitCost& c, int H, int slots) {
+    if (!c.summaries) return 0.0;
+    const double idle = (double)slots * (double)c.crit2 / H - c.work2;
+    return idle > 0.0 ? idle : 0.0;
+}
 __host__ __device__ inline double split_makespan(const SplitCost& c, int H, int slots) {
-    const double w1 = c.work1 * H / slots, w2 = c.work2 * H / slots;
+    const double idle = split_idle2(c, H, slots);
+    const double x = c.whole < idle ? c.whole : idle;
+    const double w1 = (c.work1 - x) * H / slots, w2 = (c.work2 + x) * H / slots;
     const double m1 = (double)c.crit1 > w1 ? (double)c.crit1 : w1;
     const double m2 = c.summaries ? ((double)c.crit2 > w2 ? (double)c.crit2 : w2) : 0.0;
     return m1 + m2;

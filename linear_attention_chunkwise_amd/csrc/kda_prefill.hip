@@ -1159,8 +1159,9 @@ __device__ int seq_of_rank(const PrefillArgs& a, int r, char* smem) {
 // Both roles run the same number of iterations (chunks + 2) with two barriers each.  PASS: 0 a
 // whole-sequence run, 1 the first pass of a split in time (segment summaries; first segments
 // also write their outputs; transition workgroups may stop early), 2 its second pass (the later
-// segments); a.mode equals PASS.  RANK: packed sequences (at most kRankMax) in longest-first
-// order.  Separate instantiations, so that the plain kernel carries none of the split's code.
+// segments, and whole runs a plan moves there); a.mode equals PASS.  RANK: packed sequences (at
+// most kRankMax) in longest-first order.  Separate instantiations, so that the plain kernel
+// carries none of the split's code.
 template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, int PASS>
 __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1183,9 +1184,9 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         nseg_n = a.plan[lay.segs() + n];
         sbase = a.plan[lay.first() + n];
         const int64_t L = a.plan[lay.seglen() + n];
-        if (SUMM && nseg_n <= 1) {
-            // a sequence the plan leaves whole runs here completely, beside the summaries
-            if (slice * kDVT >= a.dv) return;
+        if (nseg_n <= 1) {
+            // a sequence the plan leaves whole runs completely, in either pass
+            if (SUMM && slice * kDVT >= a.dv) return;
             mode = 0;
         } else if (SUMM && seg == 0 && slice * kDVT >= a.dv) {
             return;   // the first segment is entered with S0: no transition columns
@@ -1333,13 +1334,14 @@ int32_t plan_fixed_segments(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t
 // into 2 .. Pmax pieces) with the model above and writes the plan of the best.
 __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __restrict__ plan, int slots,
                                                    SplitLimits lim) {
-    __shared__ double rd[2][256];
+    __shared__ double rd[3][256];
     __shared__ int64_t ri[3][256];
     const int t = threadIdx.x;
     const int N = a.N, H = a.H, nsl = a.dv / kDVT, nslt = (a.dv + a.dk) / kDVT;
-    auto reduce = [&](double& w1, double& w2, int64_t& c1, int64_t& c2, int64_t& ns) {
+    auto reduce = [&](double& w1, double& w2, double& wh, int64_t& c1, int64_t& c2, int64_t& ns) {
         rd[0][t] = w1;
         rd[1][t] = w2;
+        rd[2][t] = wh;
         ri[0][t] = c1;
         ri[1][t] = c2;
         ri[2][t] = ns;
@@ -1348,6 +1350,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             if (t < k) {
                 rd[0][t] += rd[0][t + k];
                 rd[1][t] += rd[1][t + k];
+                rd[2][t] += rd[2][t + k];
                 ri[0][t] = ri[0][t] > ri[0][t + k] ? ri[0][t] : ri[0][t + k];
                 ri[1][t] = ri[1][t] > ri[1][t + k] ? ri[1][t] : ri[1][t + k];
                 ri[2][t] += ri[2][t + k];
@@ -1356,6 +1359,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
         }
         w1 = rd[0][0];
         w2 = rd[1][0];
+        wh = rd[2][0];
         c1 = ri[0][0];
         c2 = ri[1][0];
         ns = ri[2][0];
@@ -1371,7 +1375,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             split_of(len, L, lim.Pmax, P, Ls);
             split_add(mine, len, P, Ls, nsl, nslt);
         }
-        reduce(mine.work1, mine.work2, mine.crit1, mine.crit2, mine.summaries);
+        reduce(mine.work1, mine.work2, mine.whole, mine.crit1, mine.crit2, mine.summaries);
         c = mine;
     };
     SplitCost whole;
@@ -1379,6 +1383,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
     const int64_t longest = whole.crit1 * 32;   // in tokens, rounded up to whole chunks
     double best = split_makespan(whole, H, slots) * kSplitGain;
     int64_t bestL = 0;
+    double idle2 = 0.0;
     for (int p = 2; p <= lim.Pmax; ++p) {
         const int64_t L = split_candidate(longest, p);
         if (L < lim.Lmin) break;
@@ -1389,11 +1394,13 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
         if (m < best) {
             best = m;
             bestL = L;
+            idle2 = split_idle2(c, H, slots);
         }
     }
     // The plan of bestL.  Sequences are taken longest first (ranked here for up to kRankMax of
     // them, in index order beyond): their summaries' first index and their pass-1 and pass-2
-    // items follow from exclusive prefix sums in that order.
+    // items follow from exclusive prefix sums in that order.  Sequences left whole move to the
+    // second pass while the running sum of their work stays within its idle capacity.
     const PlanLayout lay{N, (int32_t)lim.Smax};
     __shared__ int32_t order[kRankMax];
     __shared__ int64_t lens[kRankMax];
@@ -1413,7 +1420,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
         __syncthreads();
     }
     int32_t c_sum = 0, c_a = 0, c_b = 0;
-    __shared__ int32_t sc[3][256];
+    int64_t c_w = 0;
+    __shared__ int32_t sc[4][256];
     for (int base = 0; base < N; base += 256) {
         const int r = base + t;
         int P = 0;
@@ -1427,9 +1435,22 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             plan[lay.segs() + n] = P;
             plan[lay.seglen() + n] = (int32_t)(P > 1 ? Ls : (Ls > 0 ? Ls : kC));
         }
-        const int na = r < N ? (P > 1 ? P - 1 : 1) : 0;   // pass-1 items
-        const int nb = r < N && P > 1 ? P - 1 : 0;         // pass-2 items (segments 1 .. P - 1)
-        const int ns = r < N ? P - 1 : 0;                  // summaries
+        // work of a whole sequence per head, in chunk steps (below 2^31: T < 2^31, dv <= 256)
+        const int32_t w = r < N && P == 1 ? nsl * (int32_t)chunks_of(Ls) : 0;
+        sc[3][t] = w;
+        __syncthreads();
+        for (int k = 1; k < 256; k <<= 1) {
+            const int32_t x3 = t >= k ? sc[3][t - k] : 0;
+            __syncthreads();
+            sc[3][t] += x3;
+            __syncthreads();
+        }
+        const bool moved = r < N && P == 1 && (double)(c_w + sc[3][t]) <= idle2;
+        const int na = r < N ? (P > 1 ? P - 1 : (moved ? 0 : 1)) : 0;   // pass-1 items
+        // pass-2 items: segments 1 .. P - 1, or the whole run of a moved sequence
+        const int nb = r < N ? (P > 1 ? P - 1 : (moved ? 1 : 0)) : 0;
+        const int ns = r < N ? P - 1 : 0;   // summaries
+        __syncthreads();
         sc[0][t] = ns;
         sc[1][t] = na;
         sc[2][t] = nb;
@@ -1454,12 +1475,13 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             }
             for (int j = 0; j < nb; ++j) {
                 B[2 * (ib + j)] = n;
-                B[2 * (ib + j) + 1] = j + 1;
+                B[2 * (ib + j) + 1] = P > 1 ? j + 1 : 0;
             }
         }
         c_sum += sc[0][255];
         c_a += sc[1][255];
         c_b += sc[2][255];
+        c_w += sc[3][255];
         __syncthreads();
     }
     if (t == 0) {

@@ -356,7 +356,7 @@ def test_chunk_fwd_workspace_size_plans_on_the_host(lib):
     pmax = min(16, -(-2 * 256 // (32 * 2)))
     lmin = max(1024, -(-(-(-total // 64)) // 32) * 32)
     smax = min(N * (pmax - 1), total // lmin)
-    plan = ((4 + 5 * N + 4 * smax) * 4 + 255) // 256 * 256
+    plan = ((4 + 7 * N + 4 * smax) * 4 + 255) // 256 * 256
     assert size(N, total, 32, 128, 128, 1) == plan + smax * summary
     assert size(1 << 17, 1 << 24, 1, 64, 64, 1) == 0            # beyond the device planner
 

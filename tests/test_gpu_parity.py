@@ -689,14 +689,17 @@ def test_segmented_varlen_and_dk64(gpu_lib):
     assert_close("S_T[cp d64 f32]", ST.cpu().numpy(), rST)
 
 
-def _plan(ws, N):
+def _plan(ws, N, smax):
     """The plan kda_chunk_fwd left at the head of its workspace: (segment length, per-sequence
-    segment counts, first summaries, segment lengths, pass-1 items, pass-2 items)."""
-    head = ws[:16].cpu().view(torch.int32).tolist()
-    n1, n2 = head[1], head[2]
-    p = ws[: (4 + 3 * N) * 4].cpu().view(torch.int32).tolist()
-    # item lists: pass 1 right after the per-sequence arrays; pass 2 after room for N + Smax
-    return p[0], p[4:4 + N], p[4 + N:4 + 2 * N], p[4 + 2 * N:4 + 3 * N], n1, n2
+    segment counts, first summaries, segment lengths, pass-1 items, pass-2 items), each item a
+    (sequence, segment) pair.  The item lists follow the per-sequence arrays, N + smax each."""
+    p = ws[: (4 + 7 * N + 4 * smax) * 4].cpu().view(torch.int32).tolist()
+    n1, n2 = p[1], p[2]
+    i1 = 4 + 3 * N
+    i2 = i1 + 2 * (N + smax)
+    items1 = [(p[i1 + 2 * j], p[i1 + 2 * j + 1]) for j in range(n1)]
+    items2 = [(p[i2 + 2 * j], p[i2 + 2 * j + 1]) for j in range(n2)]
+    return p[0], p[4:4 + N], p[4 + N:4 + 2 * N], p[4 + 2 * N:4 + 3 * N], items1, items2
 
 
 def test_auto_split_long_sequence(gpu_lib):
@@ -719,26 +722,28 @@ def test_auto_split_long_sequence(gpu_lib):
 
 def test_auto_split_packed_by_length(gpu_lib):
     """Packed sequences planned on the device: the longest get the most segments, the short ones
-    stay whole and run beside the first pass, summaries are indexed compactly; every sequence
-    matches the oracle (empty and one-token sequences included)."""
+    stay whole and run in the pass with room for them (the second pass's idle slots here),
+    summaries are indexed compactly; every sequence matches the oracle (empty and one-token
+    sequences included)."""
     from linear_attention_chunkwise_amd import binding
     lens = [9000, 300, 0, 45, 1500, 3000, 1, 20000]
     cu = inputs.cu_from_lengths(lens)
-    N, H = len(lens), 2
-    x = inputs.make_prefill_inputs(1, int(cu[-1]), H, 128, 128, seed=92, cu_seqlens=cu)
-    need = binding.chunk_fwd_workspace_size(N, int(cu[-1]), H, 128, 128, True)
+    N, H, total = len(lens), 2, int(cu[-1])
+    x = inputs.make_prefill_inputs(1, total, H, 128, 128, seed=92, cu_seqlens=cu)
+    need = binding.chunk_fwd_workspace_size(N, total, H, 128, 128, True)
     assert need > 0
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     d = _to_dev(x)
     o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["cu_seqlens"],
                               out_dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
-    L, P, first, seg, n1, n2 = _plan(ws, N)
-    print(f"  plan: L={L} P={P} first={first} seg={seg} items {n1} + {n2}", flush=True)
-    assert n1 == sum(p - 1 if p > 1 else 1 for p in P) and n2 == sum(p - 1 for p in P if p > 1)
-    assert L > 0 and L % 32 == 0
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     pmax = min(16, -(-2 * cus // (H * 2)))
+    lmin = max(1024, (-(-total // 64) + 31) // 32 * 32)
+    smax = min(N * (pmax - 1), total // lmin)
+    L, P, first, seg, items1, items2 = _plan(ws, N, smax)
+    print(f"  plan: L={L} P={P} first={first} seg={seg} items {items1} + {items2}", flush=True)
+    assert L > 0 and L % 32 == 0
     for n, ln in enumerate(lens):          # each sequence by its own length, at most pmax pieces
         want = 1 if ln <= L else -(-ln // L)
         if want > pmax:
@@ -754,6 +759,20 @@ def test_auto_split_packed_by_length(gpu_lib):
         assert f == acc, spans
         acc += c
     assert acc == sum(p - 1 for p in P)
+    # items: segments 0 .. P - 2 of a split sequence in pass 1, 1 .. P - 1 in pass 2; a whole
+    # sequence in exactly one pass; those moved to pass 2 come first in longest-first order
+    assert len(set(items1)) == len(items1) and len(set(items2)) == len(items2)
+    whole = sorted((n for n in range(N) if P[n] == 1), key=lambda n: (-lens[n], n))
+    for n in range(N):
+        if P[n] > 1:
+            assert all((n, j) in items1 for j in range(P[n] - 1)), (n, items1)
+            assert all((n, j) in items2 for j in range(1, P[n])), (n, items2)
+    assert all((n, 0) in items1 or (n, 0) in items2 for n in whole)
+    assert not any((n, 0) in items1 and (n, 0) in items2 for n in whole)
+    assert len(items1) + len(items2) == 2 * sum(p - 1 for p in P if p > 1) + len(whole)
+    moved = [(n, 0) in items2 for n in whole]
+    assert moved == sorted(moved, reverse=True), moved
+    assert all(moved), "the second pass has room for every whole sequence of this batch"
     ro, rST = oracle_all(x)
     assert_close("o[auto packed]", o.cpu().numpy(), ro)
     assert_close("S_T[auto packed]", ST.cpu().numpy(), rST)
