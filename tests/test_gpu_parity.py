@@ -779,6 +779,49 @@ def test_auto_split_packed_by_length(gpu_lib):
     assert np.array_equal(ST[2].cpu().numpy(), x["S0"][2].numpy())   # empty: S_T = S0
 
 
+def test_auto_split_packed_beyond_the_ranked_count(gpu_lib):
+    """1500 packed sequences (past the 1024 the planner ranks by length; H=1, d=64, so the batch
+    is still planned): three long ones among short ones.  Beyond the ranked count the planner
+    takes sequences in index order: the split ones get their segments in both passes, every
+    whole sequence runs in exactly one pass, those moved to the second pass come first in index
+    order; every sequence matches the oracle."""
+    from linear_attention_chunkwise_amd import binding
+    rng = np.random.default_rng(95)
+    lens = [int(x) for x in rng.integers(0, 65, size=1500)]
+    lens[100], lens[700], lens[1400] = 20000, 9000, 5000
+    cu = inputs.cu_from_lengths(lens)
+    N, H, total = len(lens), 1, int(cu[-1])
+    x = inputs.make_prefill_inputs(1, total, H, 64, 64, seed=95, cu_seqlens=cu)
+    need = binding.chunk_fwd_workspace_size(N, total, H, 64, 64, True)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["cu_seqlens"],
+                              out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pmax = min(16, -(-2 * cus // H))
+    lmin = max(1024, (-(-total // 64) + 31) // 32 * 32)
+    smax = min(N * (pmax - 1), total // lmin)
+    L, P, first, seg, items1, items2 = _plan(ws, N, smax)
+    split = [n for n in range(N) if P[n] > 1]
+    print(f"  plan: L={L} split={[(n, P[n]) for n in split]} items {len(items1)} + {len(items2)}", flush=True)
+    assert L > 0 and split == [100, 700, 1400][:len(split)] and 100 in split
+    assert len(set(items1)) == len(items1) and len(set(items2)) == len(items2)
+    for n in split:
+        assert all((n, j) in items1 for j in range(P[n] - 1))
+        assert all((n, j) in items2 for j in range(1, P[n]))
+    one1 = {n for n, j in items1 if P[n] == 1}
+    one2 = {n for n, j in items2 if P[n] == 1}
+    whole = [n for n in range(N) if P[n] == 1]
+    assert one1 | one2 == set(whole) and not (one1 & one2)
+    moved = [n in one2 for n in whole]
+    assert moved == sorted(moved, reverse=True), "moved sequences are a prefix in index order"
+    ro, rST = oracle_all(x)
+    assert_close("o[auto packed 1500]", o.cpu().numpy(), ro)
+    assert_close("S_T[auto packed 1500]", ST.cpu().numpy(), rST)
+
+
 def test_auto_split_leaves_full_batches_whole(gpu_lib):
     """When the whole-sequence schedule already fills the GPU (B=4, H=32: 256 workgroups) the
     workspace asked for is 0, and an in-place state (S_T = S0) never splits."""
