@@ -98,8 +98,8 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * cu_seqlens (no host synchronisation), each sequence by its own length: longer sequences get
  * more segments, sequences no longer than the segment length stay whole and run in the second
  * pass while its idle capacity (compute units x its longest workgroup, less its work) lasts,
- * longest first, the rest beside the first pass.  Larger packed batches run whole.  Results agree with the whole-sequence run
- * within the operator's tolerance (not bit for bit).  With workspace NULL or too small, or S_T
+ * longest first, the rest beside the first pass.  Larger packed batches run whole.  Results
+ * agree with the whole-sequence run within the operator's tolerance (not bit for bit).  With workspace NULL or too small, or S_T
  * aliasing S0, every sequence runs whole (workspace_bytes is then not checked).
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,

@@ -104,9 +104,10 @@ hipError_t launch_chunk_fwd(const PrefillArgs& a);
 
 // ---- Splitting sequences in time (in-device context parallelism).  Costs are in chunk steps
 // of one workgroup (one 32-token chunk of one 64-column slice).  A sequence of len tokens left
-// whole costs nsl workgroups x ceil(len / 32) steps, all in pass 1 (beside the summaries).  Split
-// into P segments of Ls tokens it costs, in pass 1, nsl x ceil(Ls / 32) for its first segment
-// (its outputs and the summary of its value columns) and nslt x ceil(Ls / 32) for each of the
+// whole costs nsl workgroups x ceil(len / 32) steps, in pass 1 (beside the summaries) unless the
+// plan moves it into pass 2 (below).  Split into P segments of Ls tokens it costs, in pass 1,
+// nsl x ceil(Ls / 32) for its first segment (its outputs and the summary of its value columns)
+// and nslt x ceil(Ls / 32) for each of the
 // next P - 2 (value and transition columns; the transition workgroups stop early once their
 // columns are exactly zero, which the model does not count on), and in pass 2
 // nsl x (ceil(Ls_j / 32) + j) for segment j >= 1 (its tokens and the j summaries it composes).
