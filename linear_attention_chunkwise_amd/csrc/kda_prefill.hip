@@ -350,10 +350,11 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t&
 // Wave p owns key channels [32 p, 32 p + 32) (none when p >= DK / 32).  Iteration it: the decayed
 // operands and the partial Gram tiles of chunk it (interval 1); the rows of W over the wave's
 // channels and a row tile of M for chunk it - 1, then Q~, K~, gamma and K_end of chunk it
-// (interval 2).
-template <int DK, bool F32IN, bool GATE, bool SUMM>
+// (interval 2).  TSL: a workgroup of transition columns (first pass of a split in time), which
+// stops when its consumers vote that the transition is zero.
+template <int DK, bool F32IN, bool GATE, bool TSL>
 __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p, int lane,
-                                         int64_t row0, int64_t len, int h, bool tslice) {
+                                         int64_t row0, int64_t len, int h) {
     using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr int RB = Lay::RB, TB = Lay::TB;
@@ -663,8 +664,8 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
         }
         if (intra && it + 1 < nchunks) prep(it + 1);
         __syncthreads();
-        if constexpr (SUMM) {
-            if (tslice && stop_voted(smem + Lay::o_stop)) {
+        if constexpr (TSL) {
+            if (stop_voted(smem + Lay::o_stop)) {
                 __builtin_amdgcn_s_waitcnt(0);   // the next chunk's loads are abandoned
                 return;
             }
@@ -676,11 +677,13 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 // Wave 4 + cw owns value columns [16 cw, 16 cw + 16) of the slice and its dk x 16 state slice.
 // Iteration it: the state step of chunk it - 2 (interval 1); for chunk it the diagonal blocks of
 // the UT transform (cw = 0, 1), beta N10 and the A_qk tiles (cw = 2, 3), and the scale of the
-// value path for chunk it - 1 (interval 2).
-template <int DK, bool F32IN, bool OUT_F32, bool SUMM>
+// value path for chunk it - 1 (interval 2).  SUMM: the first pass of a split in time (a first
+// segment writes its outputs, later ones none); TSL: a workgroup of its transition columns,
+// whose waves vote each iteration whether their columns are all zero and stop together.
+template <int DK, bool F32IN, bool OUT_F32, bool SUMM, bool TSL>
 __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
                                          int64_t row0, int64_t len, int n, int h, int slice, int seg,
-                                         int mode, int nseg_n, int64_t sbase, bool tslice) {
+                                         int mode, int nseg_n, int64_t sbase) {
     using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr int KS = DK / 32;          // 32-channel contraction steps
@@ -1083,7 +1086,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
                 }
             }
         }
-        if (SUMM && tslice) {
+        if (TSL) {
             // transition columns: V is 0, so once every entry is exactly zero every later step
             // leaves them zero (R = 0 - K~ 0, S <- gamma 0 + W 0); this wave's vote to stop
             uint32_t nz = 0;
@@ -1095,8 +1098,8 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
             if (lane == 0) reinterpret_cast<int*>(smem + Lay::o_stop)[cw] = zero ? 1 : 0;
         }
         __syncthreads();
-        if constexpr (SUMM) {
-            if (tslice && stop_voted(smem + Lay::o_stop)) {
+        if constexpr (TSL) {
+            if (stop_voted(smem + Lay::o_stop)) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();   // +0, as the remaining steps give
                 break;
@@ -1229,9 +1232,17 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     // a workgroup of transition columns (segment summaries) may stop once they are all zero
     const bool tslice = SUMM && mode == 1 && slice * kDVT >= a.dv;
-    if (wave < kNW) producer<DK, F32IN, GATE, SUMM>(a, smem, wave, lane, row0, len, h, tslice);
-    else consumer<DK, F32IN, OUT_F32, SUMM>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg, mode, nseg_n,
-                                            sbase, tslice);
+    if constexpr (SUMM) {
+        if (tslice) {   // its own code: the vote and the stop stay out of the value workgroups
+            if (wave < kNW) producer<DK, F32IN, GATE, true>(a, smem, wave, lane, row0, len, h);
+            else consumer<DK, F32IN, OUT_F32, true, true>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg,
+                                                           mode, nseg_n, sbase);
+            return;
+        }
+    }
+    if (wave < kNW) producer<DK, F32IN, GATE, false>(a, smem, wave, lane, row0, len, h);
+    else consumer<DK, F32IN, OUT_F32, SUMM, false>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg, mode,
+                                                   nseg_n, sbase);
 }
 
 template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, int PASS>
