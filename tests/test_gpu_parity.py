@@ -822,6 +822,73 @@ def test_auto_split_packed_beyond_the_ranked_count(gpu_lib):
     assert_close("S_T[auto packed 1500]", ST.cpu().numpy(), rST)
 
 
+def _plan_sweep_cases(n=10, seed=2027):
+    """Packed batches for the device planner: lognormal lengths (median 200), some empty, one or
+    two long sequences; heads, head sizes and dtypes drawn at random."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        N = int(rng.integers(2, 41))
+        lens = [int(x) for x in np.clip(np.round(np.exp(rng.normal(np.log(200), 1.0, size=N))), 0, 3000)]
+        for j in rng.choice(N, size=min(N, int(rng.integers(0, 4))), replace=False):
+            lens[j] = 0
+        for j in rng.choice(N, size=int(rng.integers(1, 3)), replace=False):
+            lens[j] = int(rng.integers(2000, 12001))
+        dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+        cases.append(dict(lens=lens, H=int(rng.integers(1, 5)), dk=dk, dv=dv,
+                          f32_in=bool(rng.random() < 0.25), out_f32=bool(rng.random() < 0.5)))
+    return cases
+
+
+PLAN_SWEEP = _plan_sweep_cases()
+
+
+@pytest.mark.parametrize("i", range(len(PLAN_SWEEP)))
+def test_auto_split_packed_sweep(gpu_lib, i):
+    """kda_chunk_fwd with its automatic plan on random packed batches: the plan's item lists
+    hold every segment of a split sequence in its pass and every whole sequence in exactly one
+    pass, those in the second pass forming a longest-first prefix of the whole sequences; every
+    sequence matches the oracle."""
+    from linear_attention_chunkwise_amd import binding
+    c = PLAN_SWEEP[i]
+    lens, H, dk, dv = c["lens"], c["H"], c["dk"], c["dv"]
+    cu = inputs.cu_from_lengths(lens)
+    N, total = len(lens), int(cu[-1])
+    dtype = torch.float32 if c["f32_in"] else torch.bfloat16
+    print(f"  case {i}: N={N} tokens={total} longest={max(lens)} H={H} dk={dk} dv={dv} "
+          f"in={'f32' if c['f32_in'] else 'bf16'} out={'f32' if c['out_f32'] else 'bf16'}", flush=True)
+    x = inputs.make_prefill_inputs(1, total, H, dk, dv, dtype=dtype, seed=300 + i, cu_seqlens=cu)
+    need = binding.chunk_fwd_workspace_size(N, total, H, dk, dv, True)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    d = _to_dev(x)
+    out_dtype = torch.float32 if c["out_f32"] else torch.bfloat16
+    o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["cu_seqlens"],
+                              out_dtype=out_dtype, workspace=ws)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pmax = min(16, -(-2 * cus // (H * dv // 64)))
+    lmin = max(1024, (-(-total // 64) + 31) // 32 * 32)
+    smax = min(N * (pmax - 1), total // lmin)
+    L, P, first, seg, items1, items2 = _plan(ws, N, smax)
+    print(f"  plan: L={L} split={[(n, P[n]) for n in range(N) if P[n] > 1]} "
+          f"items {len(items1)} + {len(items2)}", flush=True)
+    assert len(set(items1)) == len(items1) and len(set(items2)) == len(items2)
+    for n in range(N):
+        if P[n] > 1:
+            assert L > 0 and lens[n] > L
+            assert all((n, j) in items1 for j in range(P[n] - 1))
+            assert all((n, j) in items2 for j in range(1, P[n]))
+        else:
+            assert ((n, 0) in items1) != ((n, 0) in items2), n
+    whole = sorted((n for n in range(N) if P[n] == 1), key=lambda n: (-lens[n], n))
+    moved = [(n, 0) in items2 for n in whole]
+    assert moved == sorted(moved, reverse=True), moved
+    ro, rST = oracle_all(x)
+    assert_close(f"o[plan sweep {i}]", o.float().cpu().numpy(), ro, stored_bf16=not c["out_f32"])
+    assert_close(f"S_T[plan sweep {i}]", ST.cpu().numpy(), rST)
+
+
 def test_auto_split_leaves_full_batches_whole(gpu_lib):
     """When the whole-sequence schedule already fills the GPU (B=4, H=32: 256 workgroups) the
     workspace asked for is 0, and an in-place state (S_T = S0) never splits."""
