@@ -824,7 +824,8 @@ def test_auto_split_packed_beyond_the_ranked_count(gpu_lib):
 
 def _plan_sweep_cases(n=10, seed=2027):
     """Packed batches for the device planner: lognormal lengths (median 200), some empty, one or
-    two long sequences; heads, head sizes and dtypes drawn at random."""
+    two long sequences; heads, head sizes, dtypes and whether an initial state is given drawn at
+    random."""
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(n):
@@ -836,7 +837,8 @@ def _plan_sweep_cases(n=10, seed=2027):
             lens[j] = int(rng.integers(2000, 12001))
         dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
         cases.append(dict(lens=lens, H=int(rng.integers(1, 5)), dk=dk, dv=dv,
-                          f32_in=bool(rng.random() < 0.25), out_f32=bool(rng.random() < 0.5)))
+                          f32_in=bool(rng.random() < 0.25), out_f32=bool(rng.random() < 0.5),
+                          s0=bool(rng.random() < 0.7)))
     return cases
 
 
@@ -856,8 +858,9 @@ def test_auto_split_packed_sweep(gpu_lib, i):
     N, total = len(lens), int(cu[-1])
     dtype = torch.float32 if c["f32_in"] else torch.bfloat16
     print(f"  case {i}: N={N} tokens={total} longest={max(lens)} H={H} dk={dk} dv={dv} "
-          f"in={'f32' if c['f32_in'] else 'bf16'} out={'f32' if c['out_f32'] else 'bf16'}", flush=True)
-    x = inputs.make_prefill_inputs(1, total, H, dk, dv, dtype=dtype, seed=300 + i, cu_seqlens=cu)
+          f"in={'f32' if c['f32_in'] else 'bf16'} out={'f32' if c['out_f32'] else 'bf16'} S0={c['s0']}", flush=True)
+    x = inputs.make_prefill_inputs(1, total, H, dk, dv, dtype=dtype, seed=300 + i, cu_seqlens=cu,
+                                   S0_std=0.1 if c["s0"] else None)
     need = binding.chunk_fwd_workspace_size(N, total, H, dk, dv, True)
     assert need > 0
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
