@@ -724,7 +724,7 @@ def test_auto_split_packed_by_length(gpu_lib):
     """Packed sequences planned on the device: the longest get the most segments, the short ones
     stay whole and run in the pass with room for them (the second pass's idle slots here),
     summaries are indexed compactly; every sequence matches the oracle (empty and one-token
-    sequences included)."""
+    sequences included), and the same plan without a final state gives the same outputs."""
     from linear_attention_chunkwise_amd import binding
     lens = [9000, 300, 0, 45, 1500, 3000, 1, 20000]
     cu = inputs.cu_from_lengths(lens)
@@ -777,6 +777,11 @@ def test_auto_split_packed_by_length(gpu_lib):
     assert_close("o[auto packed]", o.cpu().numpy(), ro)
     assert_close("S_T[auto packed]", ST.cpu().numpy(), rST)
     assert np.array_equal(ST[2].cpu().numpy(), x["S0"][2].numpy())   # empty: S_T = S0
+    # the same plan without a final state: the outputs are unchanged, bit for bit
+    o2, ST2 = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], d["cu_seqlens"],
+                                out_dtype=torch.float32, output_final_state=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert ST2 is None and torch.equal(o2, o)
 
 
 def test_auto_split_packed_beyond_the_ranked_count(gpu_lib):
