@@ -71,6 +71,16 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2, K=1):
                                            dv * out_bytes))
 
 
+def plan_summary(ws, N):
+    """What the automatic split planned, read from the head of its workspace: the segment length
+    (0: no split), the layout (eager: every segment in the first pass) and the segment count of
+    the longest sequence."""
+    if ws is None:
+        return {"segment_len": 0}
+    p = ws[: (4 + N) * 4].cpu().view(torch.int32).tolist()
+    return {"segment_len": p[0], "layout": "eager" if p[3] else "deferred", "segments_of_longest": max(p[4:4 + N])}
+
+
 def time_launches(fn, reps=10, groups=3, warmup=5):
     """Duration of one of fn's launches in ms (HIP events on the current stream): the median over
     `groups` groups of `reps` back-to-back launches, after `warmup` launches."""
@@ -384,20 +394,21 @@ def main():
         v_ms = time_launches(lambda: binding.chunk_fwd(xv["q"], xv["k"], xv["v"], xv["g"], xv["beta"],
                                                        xv["S0"], xv["cu_seqlens"], o=ov, S_T=STv,
                                                        workspace=wsv))
-        plan = wsv[:4].cpu().view(torch.int32).tolist()[0] if vneed else 0
+        plan = plan_summary(wsv, xv["N"])
         vw_ms = time_launches(lambda: binding.chunk_fwd(xv["q"], xv["k"], xv["v"], xv["g"], xv["beta"],
                                                         xv["S0"], xv["cu_seqlens"], o=ov, S_T=STv,
                                                         workspace=None))
         lens = xv["cu_seqlens"][1:] - xv["cu_seqlens"][:-1]
         vbytes = prefill_alg_bytes(1, Tv, vcfg.H, vcfg.dk, vcfg.dv, xv["N"])
-        res["prefill_varlen64"] = {"ms": v_ms, "whole_ms": vw_ms, "planned_segment_len": plan,
+        res["prefill_varlen64"] = {"ms": v_ms, "whole_ms": vw_ms, "plan": plan,
                                    "tokens": Tv, "tokens_per_s": Tv / (v_ms * 1e-3),
                                    "longest": int(lens.max()), "alg_GBps": vbytes / (v_ms * 1e-3) / 1e9,
                                    "what": "kda_chunk_fwd on 64 packed sequences (cu_seqlens), "
                                            "H=32, d=128, with the workspace of its automatic plan "
-                                           "(ms; planned_segment_len: the plan's segment length, "
-                                           "0 for no split) and with no workspace (whole_ms: "
-                                           "every sequence whole, the longest first)"}
+                                           "(ms; plan: its segment length, 0 for no split, its "
+                                           "layout and the longest sequence's segments) and with "
+                                           "no workspace (whole_ms: every sequence whole, the "
+                                           "longest first)"}
         del xv, ov, STv, wsv
         # long prefill: one sequence of 2^20 tokens, 32 heads: plain (64 workgroups) and split in
         # time with the library's segment count for this GPU (kda_chunk_fwd_cp_segments)
@@ -410,17 +421,16 @@ def main():
                                                        xl["S0"], o=ol, S_T=STl, workspace=None),
                              reps=2, groups=1, warmup=1)
         need = binding.chunk_fwd_workspace_size(1, lcfg.T, lcfg.H, lcfg.dk, lcfg.dv, False)
-        summary = lcfg.H * lcfg.dk * (lcfg.dk + lcfg.dv) * 4
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         la_ms = time_launches(lambda: binding.chunk_fwd(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"],
                                                         xl["S0"], o=ol, S_T=STl, workspace=ws),
                               reps=2, groups=1, warmup=1)
         res["prefill_long_t1m"] = {
-            "tokens": lcfg.T, "ms": la_ms, "whole_ms": l_ms, "segments": need // summary + 1,
+            "tokens": lcfg.T, "ms": la_ms, "whole_ms": l_ms, "plan": plan_summary(ws if need else None, 1),
             "tokens_per_s": lcfg.T / (la_ms * 1e-3), "alg_GBps": lbytes / (la_ms * 1e-3) / 1e9,
             "what": "B=1, H=32, T=1048576, d=128 (13 of 128 key channels per head near g_min): "
-                    "kda_chunk_fwd with the workspace of its automatic split (ms; segments as "
-                    "planned) and without (whole_ms, 64 workgroups)"}
+                    "kda_chunk_fwd with the workspace of its automatic split (ms; plan as for "
+                    "varlen64) and without (whole_ms, 64 workgroups)"}
         del xl, ol, STl, ws
         # context for the HBM fractions: what the vendor's own read+write kernels reach here
         xb = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)

@@ -90,16 +90,26 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * §5.1.2, eq. (17); see kda_chunk_fwd_cp): with a workspace of at least
  * kda_chunk_fwd_workspace_size(N, B * T, H, dk, dv, cu_seqlens != NULL) bytes (16-byte aligned,
  * caller-owned, overlapping no input or output), the call plans by itself whether and how to
- * split sequences in time.  It prices each candidate segment length with a model of the two
- * passes on this GPU's compute units (a pass lasts at least its longest workgroup and at least
- * its total work over the units) and splits only when that beats the whole-sequence schedule.
- * Fixed-length rows are planned on the host (all rows alike); packed batches (at most 16
- * whole-sequence workgroups, n_seq H dv / 64, per compute unit) are planned on the device from
- * cu_seqlens (no host synchronisation), each sequence by its own length: longer sequences get
- * more segments, sequences no longer than the segment length stay whole and run in the second
- * pass while its idle capacity (compute units x its longest workgroup, less its work) lasts,
- * longest first, the rest beside the first pass.  Larger packed batches run whole.  Results
- * agree with the whole-sequence run within the operator's tolerance (not bit for bit).  With workspace NULL or too small, or S_T
+ * split sequences in time, on the device (no host synchronisation): a probe reads g over the
+ * first 256 tokens of the batch, then one planning workgroup reads the sequence lengths
+ * (cu_seqlens, or the rows of a fixed-length batch), chooses a layout and a segment length and
+ * writes the plan into the workspace.  Each sequence is cut by its own length: longer sequences
+ * get more segments, those no longer than the segment length stay whole and run beside the
+ * first pass.  Layouts: where every probed key channel decays by a factor e^-25 or more per
+ * 32-token chunk, pass 1 runs every segment with its outputs (the later ones entered with 0) and
+ * pass 2 runs each later segment again from its true entering state only over the chunks before
+ * its transition is exactly zero, after which its outputs no longer depend on that state (eq.
+ * (17): the state is M S_in + S~ with M = 0); otherwise the last segment is left to pass 2,
+ * which runs it whole.  The planner prices each candidate segment length with a model of the
+ * two passes on this GPU's compute units (a pass lasts at least its longest workgroup and at
+ * least its total work over the units) and splits only when that is expected to beat the
+ * whole-sequence schedule by 5 % (with weak decay: pricing every transition in full; with decay:
+ * expecting them to stop early, and taking at most 1.25 times the whole schedule should none
+ * stop).  Batches
+ * with more than 16 whole-sequence workgroups (n_seq H dv / 64) per compute unit run whole.
+ * Results agree with the whole-sequence run within the operator's tolerance (not bit for bit);
+ * the plan, and with it the result, is a deterministic function of the inputs.  With workspace
+ * NULL or too small, or S_T
  * aliasing S0, every sequence runs whole (workspace_bytes is then not checked).
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -111,15 +121,14 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
 
 /* Bytes of workspace kda_chunk_fwd needs to plan a split in time for n_seq sequences holding
  * total_tokens tokens in all, on the current device (the plan depends on its compute units):
- * packed = 0 for fixed-length rows (n_seq rows of total_tokens / n_seq tokens: the exact need of
- * the plan, 0 when the rows are better left whole), packed = 1 for cu_seqlens batches (an upper
- * bound for any mix of lengths: the plan, 4 + 7 n_seq + 4 Smax int32 rounded up to 256 bytes,
- * then Smax = min(n_seq (Pmax - 1), total_tokens / Lmin) summaries of H x dk x (dv + dk)
- * float32, with Pmax
- * = min(16, ceil(2 CUs / (H dv / 64))) segments per sequence and Lmin = max(1024, ceil(
- * total_tokens / 64) rounded up to 32) tokens per segment; 0 beyond 65536 sequences and when
- * the whole-sequence grid, n_seq H dv / 64 workgroups, exceeds 16 per compute unit:
- * such batches run whole).  0 for unsupported sizes. */
+ * packed = 0 for fixed-length rows (n_seq rows of total_tokens / n_seq tokens; 0 when no split
+ * can pay), packed = 1 for cu_seqlens batches.  Either is an upper bound for what the plan uses:
+ * the plan, 4 + 7 n_seq + 4 Smax + 64 int32 rounded up to 256 bytes, then Smax = min(n_seq (Pmax
+ * - 1), total_tokens / Lmin) summaries of H x dk x (dv + dk) float32 and their H x dk / 64 int32
+ * stop counts, with Pmax = min(16, ceil(2 CUs / (H dv / 64))) segments per sequence and Lmin =
+ * max(1024, ceil(total_tokens / 64) rounded up to 32) tokens per segment; 0 beyond 65536
+ * sequences and when the whole-sequence grid, n_seq H dv / 64 workgroups, exceeds 16 per
+ * compute unit: such batches run whole.  0 for unsupported sizes. */
 size_t kda_chunk_fwd_workspace_size(int32_t n_seq, int64_t total_tokens, int32_t H, int32_t dk,
                                     int32_t dv, int32_t packed);
 
@@ -162,17 +171,17 @@ kda_status kda_chunk_fwd_gate(const void* q, const void* k, const void* v, const
                               int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype,
                               float scale, void* o, float* S_T, hipStream_t stream);
 
-/* Bytes of workspace kda_chunk_fwd_cp needs: N * (segments - 1) * H * dk * (dv + dk) * 4 (the
- * summaries below), 0 when segments <= 1 or a size is not positive, SIZE_MAX when the product
- * does not fit in size_t. */
+/* Bytes of workspace kda_chunk_fwd_cp needs: N * (segments - 1) * H * (dk * (dv + dk) + dk / 64)
+ * * 4 (the summaries and stop counts below), 0 when segments <= 1 or a size is not positive,
+ * SIZE_MAX when the product does not fit in size_t. */
 size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv,
                                        int32_t segments);
 
 /* The segment count for kda_chunk_fwd_cp that suits a GPU with `slots` concurrent prefill
- * workgroups (one per CU: 256 on MI355X): the largest P <= 64 for which both passes below fit in
- * one round, pass 1 with N*H*(dv/64 + (P-2)*(dv+dk)/64) working workgroups and pass 2 with
- * N*H*(P-1)*dv/64; 1 when P = 2 does not fit either (then kda_chunk_fwd is as fast).  Host arithmetic
- * only (no device call); 1 for non-positive arguments. */
+ * workgroups (one per CU: 256 on MI355X): the largest P <= 64 whose pass-1 value workgroups,
+ * N*H*P*dv/64, fit in one round (its transition workgroups stop within a few chunks where the
+ * keys' channels decay); 1 when P = 2 does not fit (then kda_chunk_fwd is as fast).  Host
+ * arithmetic only (no device call); 1 for non-positive arguments. */
 int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t slots);
 
 /* kda_chunk_fwd with each sequence split in time into `segments` pieces that run in parallel:
@@ -180,17 +189,21 @@ int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, 
  * decomposition of §5.1.2, eq. (17): the state after a segment is M S_in + S~, with M the product
  * of the segment's per-token transitions (I - beta k k^T) Diag(exp(g)) and S~ the segment's state
  * when entered with zero.  For few, long sequences (N * H small) this puts more of the GPU to
- * work: two passes of T / segments tokens each instead of one pass of T.
+ * work: one pass of T / segments tokens instead of one of T, plus a short second pass.
  *
  * Segment length: each sequence's own ceil(len / segments) rounded up to a multiple of 32 (pieces
  * past its end are empty).
- * Pass 1 writes, for every sequence, head and segment but the last, [S~ | M] (dk x (dv + dk),
- * float32; segment 0 is entered with S0 and writes its outputs too) to `workspace`; the
- * workgroups of the transition columns M stop as soon as those columns are exactly zero (they
- * stay zero: the result is the same bit for bit).  Pass 2 rebuilds the entering state of each
- * later segment, S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1}, and produces its outputs.  Same results
- * as kda_chunk_fwd within the operator's tolerance (the summaries are computed with the same
- * arithmetic; the combination uses split bf16 products with float32 accumulation).
+ * Pass 1 runs every segment of every sequence and head with its outputs, the first entered with
+ * S0 and the others with 0, and writes [S~ | M] (dk x (dv + dk), float32) for all but the last
+ * to `workspace`, with, for every segment after the first, the number of its chunks before its
+ * transition M is exactly zero.  The workgroups of the transition columns stop at that point
+ * (the columns stay zero: the result is the same bit for bit).  Pass 2 rebuilds the entering
+ * state of each later segment, S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1}, and runs the segment
+ * again over those chunks, whose outputs depend on S_in(j) (all of them, and S_T for the last,
+ * where the transition never reaches zero); the outputs after them are those of pass 1, since
+ * there the state M S_in + S~ is S~.  Same results as kda_chunk_fwd within the operator's
+ * tolerance (the summaries are computed with the same arithmetic; the combination uses split
+ * bf16 products with float32 accumulation).
  *
  * N * H * segments <= 2^28 (KDA_ERR_UNSUPPORTED beyond).
  * workspace: device memory of at least kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments)

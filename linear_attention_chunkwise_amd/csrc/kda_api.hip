@@ -76,6 +76,12 @@ int device_slots() {
     return cus;
 }
 
+// Bytes of `count` segment summaries per head ([dk][dv + dk] float32 each) and of their stop
+// counts (one int32 per 64 transition columns), which follow them in a workspace.
+size_t summary_bytes(int64_t count, int32_t H, int32_t dk, int32_t dv) {
+    return (size_t)count * H * ((size_t)dk * (dv + dk) + dk / 64) * 4;
+}
+
 // Bytes of the plan in front of the summaries in an automatic split, 256-aligned.
 size_t plan_bytes(int32_t N, int64_t Smax) {
     return ((size_t)kda::PlanLayout{N, (int32_t)Smax}.ints() * 4 + 255) / 256 * 256;
@@ -219,8 +225,9 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
     }
     int64_t seg_len = 0;
     size_t need = 0;
-    // automatic split (segments == 0, kda_chunk_fwd with a workspace): the plan for fixed-length
-    // rows is made here; packed sequences are planned on the device
+    // automatic split (segments == 0, kda_chunk_fwd with a workspace): planned on the device (a
+    // decay probe, then one planning workgroup), fixed-length rows and packed sequences alike;
+    // the host checks only that a split can pay (the workspace size is 0 otherwise)
     bool device_plan = false;
     kda::SplitLimits lim;
     int slots = 0;
@@ -230,14 +237,11 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
             slots = device_slots();
             const size_t want = kda_chunk_fwd_workspace_size(N, tokens, H, dk, dv, cu_seqlens ? 1 : 0);
             if (want > 0 && workspace_bytes >= want) {
-                if (cu_seqlens) {
-                    lim = kda::split_limits(N, tokens, H, dv, slots);
-                    if (lim.Smax > 0 && kda::plan_packed(N, H, dv, slots)) {
-                        device_plan = true;
-                        segments = lim.Pmax;
-                    }
-                } else {
-                    segments = kda::plan_fixed_segments(N, T, H, dk, dv, slots);
+                // the device planner (fixed rows too: its decay probe chooses the layout)
+                lim = kda::split_limits(N, tokens, H, dv, slots);
+                if (lim.Smax > 0 && kda::plan_packed(N, H, dv, slots)) {
+                    device_plan = true;
+                    segments = lim.Pmax;
                 }
             }
         }
@@ -256,7 +260,7 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         // the first segment reads S0 while the last one writes S_T, in the same launch
         if (S_T && S_T == S0)
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s may not alias S0 in a segmented run%.0lld", "S_T");
-        need = device_plan ? plan_bytes(N, lim.Smax) + (size_t)lim.Smax * H * dk * (dv + dk) * 4
+        need = device_plan ? plan_bytes(N, lim.Smax) + summary_bytes(lim.Smax, H, dk, dv)
                            : kda_chunk_fwd_cp_workspace_size(N, H, dk, dv, segments);
         if (workspace_bytes < need)
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %lld bytes given, the workspace size asks for more",
@@ -294,10 +298,12 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         a.A_log = A_log;
     }
     if (segments <= 1) return hip_status(kda::launch_chunk_fwd(a));
-    // segmented: summaries of all but the last segment, then every segment's outputs
+    // segmented: every segment with its outputs and the summaries of all but the last, then the
+    // later segments again over the chunks whose outputs depend on their entering state
     a.nseg = segments;
     a.seg_len = seg_len;
     a.ws = static_cast<float*>(workspace);
+    int64_t nsum = (int64_t)N * (segments - 1);
     const kda::PlanLayout lay{N, (int32_t)lim.Smax};
     if (device_plan) {
         int32_t* plan = static_cast<int32_t*>(workspace);
@@ -306,7 +312,9 @@ static kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, co
         if (e != hipSuccess) return hip_status(e);
         a.plan = plan;
         a.plan_smax = (int32_t)lim.Smax;
+        nsum = lim.Smax;
     }
+    a.stops = reinterpret_cast<int32_t*>(a.ws + (size_t)nsum * H * dk * (dv + dk));
     a.mode = 1;
     a.plan_items = lay.max_items1();
     const hipError_t e = kda::launch_chunk_fwd(a);
@@ -329,14 +337,11 @@ size_t kda_chunk_fwd_workspace_size(int32_t n_seq, int64_t total_tokens, int32_t
                                     int32_t packed) {
     if (n_seq < 1 || total_tokens <= 0 || H < 1 || !(dk == 64 || dk == 128) || !(dv == 64 || dv == 128)) return 0;
     const int slots = device_slots();
-    if (packed) {
-        const kda::SplitLimits lim = kda::split_limits(n_seq, total_tokens, H, dv, slots);
-        if (lim.Smax <= 0 || !kda::plan_packed(n_seq, H, dv, slots)) return 0;
-        return plan_bytes(n_seq, lim.Smax) + (size_t)lim.Smax * H * dk * (dv + dk) * 4;
-    }
-    if (total_tokens % n_seq) return 0;
-    const int32_t P = kda::plan_fixed_segments(n_seq, total_tokens / n_seq, H, dk, dv, slots);
-    return P > 1 ? kda_chunk_fwd_cp_workspace_size(n_seq, H, dk, dv, P) : 0;
+    if (!packed && (total_tokens % n_seq || !kda::split_may_pay(n_seq, total_tokens / n_seq, H, dk, dv, slots)))
+        return 0;
+    const kda::SplitLimits lim = kda::split_limits(n_seq, total_tokens, H, dv, slots);
+    if (lim.Smax <= 0 || !kda::plan_packed(n_seq, H, dv, slots)) return 0;
+    return plan_bytes(n_seq, lim.Smax) + summary_bytes(lim.Smax, H, dk, dv);
 }
 
 kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* g,
@@ -363,7 +368,8 @@ size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t
     if (N < 1 || H < 1 || dk < 1 || dv < 1 || segments <= 1) return 0;
     // saturate rather than wrap for sizes no device could hold
     size_t n = 4;
-    const size_t factors[5] = {(size_t)N, (size_t)(segments - 1), (size_t)H, (size_t)dk, (size_t)dv + (size_t)dk};
+    const size_t per = (size_t)dk * ((size_t)dv + (size_t)dk) + (size_t)dk / 64;   // summary, stop counts
+    const size_t factors[4] = {(size_t)N, (size_t)(segments - 1), (size_t)H, per};
     for (size_t f : factors)
         if (__builtin_mul_overflow(n, f, &n)) return SIZE_MAX;
     return n;
@@ -371,15 +377,11 @@ size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t
 
 int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t slots) {
     if (N < 1 || H < 1 || dk < 1 || dv < 1 || slots < 1) return 1;
-    const int64_t units = (int64_t)N * H;
-    int32_t best = 1;
-    for (int32_t p = 2; p <= 64; ++p) {
-        const int64_t pass1 = units * (dv / 64 + (int64_t)(p - 2) * ((dv + dk) / 64));
-        const int64_t pass2 = units * (p - 1) * (dv / 64);
-        if (pass1 > slots || pass2 > slots) break;
-        best = p;
-    }
-    return best;
+    // the value workgroups of pass 1 (every segment) in one round; its transition workgroups
+    // stop early where the keys' channels decay
+    const int64_t units = (int64_t)N * H * (dv / 64);
+    const int64_t p = units > 0 ? slots / units : 0;
+    return (int32_t)(p < 1 ? 1 : (p > 64 ? 64 : p));
 }
 
 kda_status kda_chunk_fwd_cp(const void* q, const void* k, const void* v, const float* g,

@@ -23,13 +23,16 @@ struct PrefillArgs {
     float* ckpt;              // may be null: [N, H, ckpt_cap, dk, dv] states at interval ends
     int32_t ckpt_every;       // checkpoint interval in 32-token chunks (>= 1 when ckpt is set)
     int32_t ckpt_cap;         // checkpoints kept per (sequence, head)
-    // Segmented (context-parallel) runs over nseg time segments of seg_len tokens per sequence:
-    //   mode 0: plain prefill (nseg, seg_len, ws unused);
-    //   mode 1: segment summaries: for segments j < nseg - 1 the state after the segment,
-    //           entered with S0 (j = 0) or 0, and the segment's transition (extra dk columns
-    //           entered with the identity, value 0) -> ws;
-    //   mode 2: outputs: each segment rebuilds its entering state from the summaries of the
-    //           segments before it, then runs as mode 0 (the last one writes S_T).
+    // Segmented (context-parallel) runs over nseg time segments per sequence:
+    //   mode 0: plain prefill (nseg, ws, stops unused);
+    //   mode 1: every segment from its entering state (S0 for the first, 0 for the others) with
+    //           its outputs; the state after segments j < nseg - 1 -> ws (the last writes S_T),
+    //           and for segments j >= 1 the transition (extra dk columns entered with the
+    //           identity, value 0) -> ws for j < nseg - 1, with the number of its chunks before it
+    //           is exactly zero -> stops;
+    //   mode 2: segments j >= 1 rebuild their entering state from the summaries of the segments
+    //           before them and run again over the chunks whose outputs depend on it (all of
+    //           them, and S_T for the last, where the transition never reaches zero).
     //   Without a plan every sequence has nseg segments of ceil(len / nseg) tokens rounded up
     //   to whole chunks.  With one (plan != null, from launch_plan), sequence n has
     //   plan[1 + n] <= nseg segments of plan[1 + 2N + n] tokens, its summaries start at index
@@ -46,16 +49,23 @@ struct PrefillArgs {
     const int32_t* plan = nullptr;   // see PlanLayout
     int32_t plan_smax = 0;           // summaries the plan may use (per head)
     int32_t plan_items = 0;          // grid bound of this pass: work items of the plan
+    // modes 1, 2: per (summary index, head, transition slice of 64 columns) the chunks of segment
+    // j >= 1 (summary index of segment j - 1) whose outputs depend on its entering state
+    int32_t* stops = nullptr;
 };
 
 // Layout of a device plan (int32), for N sequences and at most Smax summaries:
-//   [0] segment length (0: no split), [1] items of pass 1, [2] items of pass 2, [3] unused,
+//   [0] segment length (0: no split), [1] items of pass 1, [2] items of pass 2, [3] 1 for the
+//   eager layout, 0 for the deferred one (below, at the split cost model),
 //   segs[N], first summary[N], segment length[N] per sequence,
-//   pass-1 items [N + Smax] x {sequence, segment}: the summaries of the split sequences and the
-//   whole runs of the others, longest sequences first,
+//   pass-1 items [N + Smax] x {sequence, segment}: the segments of the split sequences that pass
+//   1 runs and the whole runs of the others, longest sequences first,
 //   pass-2 items [N + Smax] x {sequence, segment}: the segments after the first of the split
-//   sequences (the first segment writes its outputs in pass 1), then the whole runs moved into
-//   the second pass's idle slots.
+//   sequences,
+//   probe[kProbeBlocks]: per workgroup of the decay probe, 1 where a key channel decayed by less
+//   than e^-25 over one of the first kProbeChunks chunks of the batch.
+constexpr int kProbeChunks = 8, kProbeGroups = 8, kProbeBlocks = kProbeChunks * kProbeGroups;
+constexpr float kProbeDecay = -25.f;
 struct PlanLayout {
     int32_t N, Smax;
     __host__ __device__ int64_t segs() const { return 4; }
@@ -63,7 +73,8 @@ struct PlanLayout {
     __host__ __device__ int64_t seglen() const { return 4 + 2 * (int64_t)N; }
     __host__ __device__ int64_t items1() const { return 4 + 3 * (int64_t)N; }
     __host__ __device__ int64_t items2() const { return items1() + 2 * ((int64_t)N + Smax); }
-    __host__ __device__ int64_t ints() const { return items2() + 2 * ((int64_t)N + Smax); }
+    __host__ __device__ int64_t probe() const { return items2() + 2 * ((int64_t)N + Smax); }
+    __host__ __device__ int64_t ints() const { return probe() + kProbeBlocks; }
     __host__ __device__ int32_t max_items1() const { return N + Smax; }
     __host__ __device__ int32_t max_items2() const { return N + Smax; }
 };
@@ -104,25 +115,32 @@ hipError_t launch_chunk_fwd(const PrefillArgs& a);
 
 // ---- Splitting sequences in time (in-device context parallelism).  Costs are in chunk steps
 // of one workgroup (one 32-token chunk of one 64-column slice).  A sequence of len tokens left
-// whole costs nsl workgroups x ceil(len / 32) steps, in pass 1 (beside the summaries) unless the
-// plan moves it into pass 2 (below).  Split into P segments of Ls tokens it costs, in pass 1,
-// nsl x ceil(Ls / 32) for its first segment (its outputs and the summary of its value columns)
-// and nslt x ceil(Ls / 32) for each of the
-// next P - 2 (value and transition columns; the transition workgroups stop early once their
-// columns are exactly zero, which the model does not count on), and in pass 2
-// nsl x (ceil(Ls_j / 32) + j) for segment j >= 1 (its tokens and the j summaries it composes).
-// A pass on `slots` concurrent workgroups takes at least its longest workgroup and at least its
-// total work / slots; a plan is priced at the sum of the two passes' bounds.  Where the second
-// pass leaves slots idle (slots x its longest workgroup above its work), sequences left whole
-// run there instead of in the first pass, up to the idle capacity: each is no longer than the
-// segment length, so it fits under the second pass's longest workgroup.
+// whole costs nsl workgroups x ceil(len / 32) steps, in pass 1.  A sequence split into P
+// segments of Ls tokens (the last one shorter or equal) runs, in pass 1, its first segment from
+// S0 and later ones from 0, each with its outputs (nsl x ceil(Ls_j / 32)), and the transitions
+// of the segments j >= 1 it runs (nslt - nsl workgroups x ceil(Ls_j / 32)); in pass 2 each
+// segment j >= 1 again from its true entering state, over c_j + j steps: c_j chunks whose outputs
+// depend on that state (the chunks until the segment's transition is exactly zero) and the j
+// summaries it composes.  Two layouts:
+//   eager:    pass 1 runs every segment, so pass 2 runs only the c_j chunks of each;
+//   deferred: pass 1 runs all but the last, which pass 2 runs whole (c = its length).
+// Transitions stop, and c_j ends, once the transition's columns are exactly zero, which a decay
+// of every key channel by e^-25 or more per chunk brings about within kTransSteps chunks: the
+// expected cost counts kTransSteps chunks for both, the full cost (no transition reaches zero)
+// the whole segment.  A pass on `slots` concurrent workgroups takes at least its longest
+// workgroup, at least its total work / slots and, where more than `slots` segment workgroups of
+// about the candidate length run in pass 1, at least two of them in a row.
+constexpr int64_t kTransSteps = 8;
 struct SplitCost {
-    double work1 = 0, work2 = 0;   // per head
-    double whole = 0;              // per head: the part of work1 in sequences left whole
-    int64_t crit1 = 0, crit2 = 0;
-    int64_t summaries = 0;         // per head
+    double work1 = 0, work2 = 0;     // per head, expected
+    double work1f = 0, work2f = 0;   // per head, if no transition reaches zero
+    double big = 0;                  // per head: pass-1 segment workgroups of >= 0.9 of the candidate
+    int64_t crit1 = 0, crit2 = 0, crit2f = 0;
+    int64_t summaries = 0;           // per head
 };
 __host__ __device__ inline int64_t chunks_of(int64_t x) { return (x + 31) / 32; }
+__host__ __device__ inline int64_t min_i64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ inline int64_t max_i64(int64_t a, int64_t b) { return a > b ? a : b; }
 // segments of one sequence for the segment length L (L <= 0: whole), at most Pmax of them
 __host__ __device__ inline void split_of(int64_t len, int64_t L, int Pmax, int& P, int64_t& Ls) {
     if (L <= 0 || len <= L) {
@@ -138,32 +156,66 @@ __host__ __device__ inline void split_of(int64_t len, int64_t L, int Pmax, int& 
     }
     P = (int)p;
 }
-__host__ __device__ inline void split_add(SplitCost& c, int64_t len, int P, int64_t Ls, int nsl, int nslt) {
+// Adds one sequence of len tokens cut into P segments of Ls tokens (candidate length L).
+__host__ __device__ inline void split_add(SplitCost& c, int64_t len, int P, int64_t Ls, int64_t L, int nsl,
+                                          int nslt, bool eager) {
     if (P <= 1) {
-        c.work1 += (double)nsl * chunks_of(len);
-        c.whole += (double)nsl * chunks_of(len);
-        c.crit1 = c.crit1 > chunks_of(len) ? c.crit1 : chunks_of(len);
+        const double w = (double)nsl * chunks_of(len);
+        c.work1 += w;
+        c.work1f += w;
+        c.crit1 = max_i64(c.crit1, chunks_of(len));
         return;
     }
-    const int64_t ch = chunks_of(Ls);
-    c.work1 += (double)ch * (nsl + (double)nslt * (P - 2));
-    c.crit1 = c.crit1 > ch ? c.crit1 : ch;
-    c.work2 += (double)nsl * ((double)(chunks_of(len) - ch) + (double)P * (P - 1) / 2);
-    c.crit2 = c.crit2 > ch + P - 1 ? c.crit2 : ch + P - 1;
+    const int64_t ch = chunks_of(Ls), chl = chunks_of(max_i64(0, len - (int64_t)(P - 1) * Ls));   // full, last
+    const int ntsl = nslt - nsl;
+    const int64_t e = min_i64(ch, kTransSteps), el = min_i64(chl, kTransSteps);
+    const double comp = (double)P * (P - 1) / 2;   // summaries composed by segments 1 .. P - 1
+    const int64_t tall = chunks_of(L) * 9 / 10;
+    c.crit1 = max_i64(c.crit1, ch);
     c.summaries += P - 1;
+    if (eager) {
+        const double value = (double)nsl * ((double)(P - 1) * ch + chl);
+        c.work1 += value + (double)ntsl * ((double)(P - 2) * e + el);
+        c.work1f += value + (double)ntsl * ((double)(P - 2) * ch + chl);
+        c.work2 += (double)nsl * ((double)(P - 2) * e + el + comp);
+        c.work2f += (double)nsl * ((double)(P - 2) * ch + chl + comp);
+        c.crit2 = max_i64(c.crit2, e + P - 1);
+        c.big += (double)nsl * ((ch >= tall ? P - 1 : 0) + (chl >= tall ? 1 : 0));
+    } else {
+        const double value = (double)nsl * (P - 1) * ch;
+        c.work1 += value + (double)ntsl * (P - 2) * e;
+        c.work1f += value + (double)ntsl * (P - 2) * ch;
+        c.work2 += (double)nsl * ((double)(P - 2) * e + chl + comp);
+        c.work2f += (double)nsl * ((double)(P - 2) * ch + chl + comp);
+        c.crit2 = max_i64(c.crit2, max_i64(e + P - 2, chl + P - 1));
+        c.big += (double)nsl * (ch >= tall ? P - 1 : 0);
+    }
+    c.crit2f = max_i64(c.crit2f, ch + P - 1);
 }
-// The idle capacity of the second pass, in work per head (0 without a split).
-__host__ __device__ inline double split_idle2(const SplitCost& c, int H, int slots) {
-    if (!c.summaries) return 0.0;
-    const double idle = (double)slots * (double)c.crit2 / H - c.work2;
-    return idle > 0.0 ? idle : 0.0;
+// The same for n sequences alike.
+__host__ __device__ inline void split_times(SplitCost& c, double n) {
+    c.work1 *= n;
+    c.work2 *= n;
+    c.work1f *= n;
+    c.work2f *= n;
+    c.big *= n;
+    c.summaries = (int64_t)(c.summaries * n);
 }
-__host__ __device__ inline double split_makespan(const SplitCost& c, int H, int slots) {
-    const double idle = split_idle2(c, H, slots);
-    const double x = c.whole < idle ? c.whole : idle;
-    const double w1 = (c.work1 - x) * H / slots, w2 = (c.work2 + x) * H / slots;
-    const double m1 = (double)c.crit1 > w1 ? (double)c.crit1 : w1;
-    const double m2 = c.summaries ? ((double)c.crit2 > w2 ? (double)c.crit2 : w2) : 0.0;
+__host__ __device__ inline double split_pass(double crit, double work, int H, int slots) {
+    const double w = work * H / slots;
+    return crit > w ? crit : w;
+}
+// Expected (full = false) or worst-case (full = true) time of a plan, for the candidate L.
+__host__ __device__ inline double split_makespan(const SplitCost& c, int64_t L, int H, int slots, bool full) {
+    double m1 = split_pass((double)c.crit1, full ? c.work1f : c.work1, H, slots);
+    if (c.summaries) {
+        const double rounds = (double)(int64_t)((c.big * H + slots - 1) / slots);
+        const double r = rounds * (double)(chunks_of(L) * 9 / 10);
+        m1 = m1 > r ? m1 : r;
+    }
+    const double m2 = c.summaries ? (full ? split_pass((double)c.crit2f, c.work2f, H, slots)
+                                          : split_pass((double)c.crit2, c.work2, H, slots))
+                                  : 0.0;
     return m1 + m2;
 }
 // The candidate segment length that cuts a sequence of `longest` tokens into P pieces (whole
@@ -202,10 +254,12 @@ __host__ __device__ inline SplitLimits split_limits(int32_t N, int64_t total, in
     if (l.Pmax <= 1 || total >= ((int64_t)1 << 31)) l.Smax = 0;
     return l;
 }
-// The whole-sequence plan for N sequences of T tokens: the segment count (1: no split).
-int32_t plan_fixed_segments(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int slots);
-// The device planner for packed sequences (one workgroup), writing the plan laid out as
-// PlanLayout{N, lim.Smax}.  a supplies cu, N, T, H, dk, dv and the stream.
+// Whether a split in time can pay for N sequences of T tokens in either layout (the device
+// planner makes the choice).
+bool split_may_pay(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int slots);
+// The device planner (a decay probe over the first chunks, then one workgroup), writing the plan
+// laid out as PlanLayout{N, lim.Smax}.  a supplies g, cu (or fixed rows of T tokens), N, T, H,
+// dk, dv and the stream.
 hipError_t launch_plan(const PrefillArgs& a, int32_t* plan, int slots, SplitLimits lim);
 // ok = every g[i], i < n, lies in [lo, hi] (NaN does not); synchronises `stream`
 hipError_t check_range(const float* g, size_t n, float lo, float hi, hipStream_t stream, bool& ok);

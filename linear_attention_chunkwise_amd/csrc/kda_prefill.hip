@@ -677,13 +677,15 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 // Wave 4 + cw owns value columns [16 cw, 16 cw + 16) of the slice and its dk x 16 state slice.
 // Iteration it: the state step of chunk it - 2 (interval 1); for chunk it the diagonal blocks of
 // the UT transform (cw = 0, 1), beta N10 and the A_qk tiles (cw = 2, 3), and the scale of the
-// value path for chunk it - 1 (interval 2).  SUMM: the first pass of a split in time (a first
-// segment writes its outputs, later ones none); TSL: a workgroup of its transition columns,
-// whose waves vote each iteration whether their columns are all zero and stop together.
+// value path for chunk it - 1 (interval 2).  SUMM: the first pass of a split in time (every
+// segment writes its outputs, from S0 or 0); TSL: a workgroup of its transition columns, whose
+// waves vote each iteration whether their columns are all zero and stop together.  full: false
+// where a second pass runs a segment only over the chunks whose outputs depend on its entering
+// state (the first pass wrote the rest and, for the last segment, S_T).
 template <int DK, bool F32IN, bool OUT_F32, bool SUMM, bool TSL>
 __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
                                          int64_t row0, int64_t len, int n, int h, int slice, int seg,
-                                         int mode, int nseg_n, int64_t sbase) {
+                                         int mode, int nseg_n, int64_t sbase, bool full) {
     using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr int KS = DK / 32;          // 32-channel contraction steps
@@ -810,6 +812,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     };
 
     const int64_t nchunks = (len + kC - 1) / kC;
+    int64_t dep = nchunks;   // transition columns: chunks before they are exactly zero
     if (nchunks > 0) prefetch_v(pa, 0);
     if (nchunks > 1) prefetch_v(pb, kC);
 
@@ -818,9 +821,9 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         if (it >= 2) {
             const int64_t c = it - 2, c0 = c * kC;
             const char* qk = smem + Lay::o_QK + (int)(c % 3) * Lay::QKB;
-            const uint32_t nvalid = (mode == 1 && (!SUMM || seg > 0)) ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
+            const uint32_t nvalid = (TSL || tcols) ? 0u : (uint32_t)((len - c0) < kC ? (len - c0) : kC);
             // output rows of the chunk: stores at or past row nvalid fall outside the resource
-            // (summaries write no outputs, except those of a first segment, entered with S0)
+            // (transition columns write no outputs)
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(obc, nvalid * (uint32_t)(sv * sizeof(OT)));
             obc += (size_t)kC * sv;
             // batch 1: rows of K~, Q~ and M
@@ -1102,19 +1105,28 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
             if (stop_voted(smem + Lay::o_stop)) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();   // +0, as the remaining steps give
+                // the state after chunks 0 .. it - 2 is zero: from chunk it - 1 on, the outputs of
+                // the segment do not depend on the state it is entered with
+                dep = it - 1 < nchunks ? it - 1 : nchunks;
                 break;
             }
         }
     }
 
     const float un = __builtin_ldexpf(1.f, esc);
-    if (mode == 1) {
+    if (mode == 1 && seg < nseg_n - 1) {
         float* Wsum = summary(seg);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) Wsum[(size_t)(16 * ct + 4 * g4 + j) * wcols + col0 + i16] = Sacc[ct][j] * un;
-    } else if (a.ST && (mode == 0 || seg == nseg_n - 1)) {
+    }
+    if (tcols) {
+        // chunks of this segment whose outputs depend on its entering state (all of them unless
+        // the transition reached zero), per 64-column transition slice
+        if (cw == 0 && lane == 0)
+            a.stops[((size_t)(sbase + seg - 1) * H + h) * (DK / kDVT) + (col0 - a.dv) / kDVT] = (int32_t)dep;
+    } else if (a.ST && full && (mode == 0 || seg == nseg_n - 1)) {
         float* ST = a.ST + ((size_t)n * H + h) * DK * a.dv;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -1160,9 +1172,10 @@ __device__ int seq_of_rank(const PrefillArgs& a, int r, char* smem) {
 }
 
 // Both roles run the same number of iterations (chunks + 2) with two barriers each.  PASS: 0 a
-// whole-sequence run, 1 the first pass of a split in time (segment summaries; first segments
-// also write their outputs; transition workgroups may stop early), 2 its second pass (the later
-// segments, and whole runs a plan moves there); a.mode equals PASS.  RANK: packed sequences (at
+// whole-sequence run, 1 the first pass of a split in time (every segment with its outputs, the
+// later ones entered with 0; segment summaries; transition workgroups may stop early), 2 its
+// second pass (the later segments again from their true entering state, over the chunks whose
+// outputs depend on it); a.mode equals PASS.  RANK: packed sequences (at
 // most kRankMax) in longest-first order.  Separate instantiations, so that the plain kernel
 // carries none of the split's code.
 template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, int PASS>
@@ -1207,9 +1220,9 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         if (unit >= a.N * a.H * nseg) return;
         seg = (unit / a.H) % nseg;
         const int rank = unit / (a.H * nseg);
-        // every sequence has nseg segments: summaries are needed for all but the last, and on
-        // value columns only for the first
-        if (SUMM && (seg == nseg - 1 || (seg == 0 && slice * kDVT >= a.dv))) return;
+        // every sequence has nseg segments, each run in pass 1 with the transition columns of all
+        // but the first
+        if (SUMM && seg == 0 && slice * kDVT >= a.dv) return;   // entered with S0: no transition
         if (PASS == 2 && seg == 0) return;   // the first segment wrote its outputs in pass 1
         KDA_POISON(smem, (SUMM ? Layout<DK>::total_summ : Layout<DK>::total));
         KDA_POISON_DONE();
@@ -1228,6 +1241,21 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
             len = hi > lo ? hi - lo : 0;
         }
     }
+    // Second pass: eq. (17) gives the state of segment seg at each chunk as M S_in + S~, M the
+    // transition from the segment's start.  Once M is exactly zero (both of its 64-column slices
+    // stopped in the first pass), the outputs from there on are those of the first pass, run
+    // from 0: only the chunks before it run again.
+    bool full = true;
+    // (a deferred plan's last segment has no transition: it runs whole)
+    if (PASS == 2 && mode == 2 && !(a.plan && !a.plan[3] && seg == nseg_n - 1)) {
+        const int32_t* st = a.stops + ((size_t)(sbase + seg - 1) * a.H + h) * (DK / kDVT);
+        int64_t dep = 0;
+        for (int ts = 0; ts < DK / kDVT; ++ts) dep = dep > st[ts] ? dep : st[ts];
+        if (dep * kC < len) {
+            len = dep * kC;
+            full = false;
+        }
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     // a workgroup of transition columns (segment summaries) may stop once they are all zero
@@ -1236,13 +1264,13 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         if (tslice) {   // its own code: the vote and the stop stay out of the value workgroups
             if (wave < kNW) producer<DK, F32IN, GATE, true>(a, smem, wave, lane, row0, len, h);
             else consumer<DK, F32IN, OUT_F32, true, true>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg,
-                                                           mode, nseg_n, sbase);
+                                                           mode, nseg_n, sbase, full);
             return;
         }
     }
     if (wave < kNW) producer<DK, F32IN, GATE, false>(a, smem, wave, lane, row0, len, h);
     else consumer<DK, F32IN, OUT_F32, SUMM, false>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg, mode,
-                                                   nseg_n, sbase);
+                                                   nseg_n, sbase, full);
 }
 
 template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, int PASS>
@@ -1310,109 +1338,131 @@ hipError_t launch_chunk_fwd(const PrefillArgs& a) {
     return a.z ? dispatch_prefill<true>(a) : dispatch_prefill<false>(a);
 }
 
-int32_t plan_fixed_segments(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int slots) {
+// The best candidate of one layout: its segment length (0: none qualifies).  price(L, eager, c)
+// fills c with the batch's cost for segment length L.  Eager (the probe saw every channel decay):
+// a candidate must be expected to beat the whole schedule by kSplitGain and, should no transition
+// reach zero after all, take at most kSplitRisk times as long as it; the lowest expected time
+// wins, near ties going to the lower worst case.  Deferred (weak decay seen): the transitions are
+// priced in full, which must beat the whole schedule by kSplitGain; the lowest wins.
+constexpr double kSplitRisk = 1.25, kSplitTie = 0.05;
+template <class Price>
+__host__ __device__ inline int64_t split_best(Price&& price, int64_t longest, const SplitLimits& lim,
+                                              double base, int H, int slots, bool eager) {
+    double best = 0.0;
+    int64_t bestL = 0;
+    for (int p = 2; p <= lim.Pmax; ++p) {
+        const int64_t L = split_candidate(longest, p);
+        if (L < lim.Lmin) break;
+        SplitCost c;
+        price(L, eager, c);
+        if (c.summaries > lim.Smax) continue;
+        const double m = split_makespan(c, L, H, slots, false), f = split_makespan(c, L, H, slots, true);
+        const bool ok = eager ? (m < base * kSplitGain && f <= base * kSplitRisk) : f < base * kSplitGain;
+        const double score = eager ? m + kSplitTie * f : f;
+        if (ok && (bestL == 0 || score < best)) {
+            best = score;
+            bestL = L;
+        }
+    }
+    return bestL;
+}
+
+bool split_may_pay(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int slots) {
     const SplitLimits lim = split_limits(N, (int64_t)N * T, H, dv, slots);
     const int nsl = dv / kDVT, nslt = (dv + dk) / kDVT;
-    if (lim.Smax <= 0 || N < 1 || T <= 0) return 1;
-    SplitCost whole;
-    split_add(whole, T, 1, T, nsl, nslt);
-    whole.work1 *= N;
-    const double base = split_makespan(whole, H, slots);
-    double best = base * kSplitGain;
-    int32_t bestP = 1;
-    for (int p = 2; p <= lim.Pmax; ++p) {
-        const int64_t L = split_candidate(T, p);
-        if (L < lim.Lmin) break;
+    if (lim.Smax <= 0 || N < 1 || T <= 0) return false;
+    auto price = [&](int64_t L, bool eager, SplitCost& c) {
         int P;
         int64_t Ls;
         split_of(T, L, lim.Pmax, P, Ls);
-        if ((int64_t)N * (P - 1) > lim.Smax) continue;
-        SplitCost c;
-        split_add(c, T, P, Ls, nsl, nslt);
-        c.work1 *= N;
-        c.work2 *= N;
-        c.summaries *= N;
-        const double m = split_makespan(c, H, slots);
-        if (m < best) {
-            best = m;
-            bestP = P;
-        }
-    }
-    return bestP;
+        split_add(c, T, P, Ls, L, nsl, nslt, eager);
+        split_times(c, N);
+    };
+    SplitCost whole;
+    price(0, false, whole);
+    const double base = split_makespan(whole, 0, H, slots, false);
+    return split_best(price, T, lim, base, H, slots, true) > 0 || split_best(price, T, lim, base, H, slots, false) > 0;
 }
 
-// One workgroup of 256 threads prices every candidate segment length (the longest sequence cut
-// into 2 .. Pmax pieces) with the model above and writes the plan of the best.
+// Decay probe: workgroup (chunk j, channel group) sums g over the 32 tokens of chunk j of the
+// batch for its channels and records whether any decayed by less than e^-25 (or is NaN).
+__global__ __launch_bounds__(256) void probe_kernel(PrefillArgs a, int32_t* __restrict__ probe, int64_t tokens) {
+    const int j = blockIdx.x / kProbeGroups, grp = blockIdx.x % kProbeGroups;
+    const int64_t nch = (int64_t)a.H * a.dk;
+    const int64_t t0 = (int64_t)j * 32, t1 = t0 + 32 < tokens ? t0 + 32 : tokens;
+    int weak = 0;
+    for (int64_t c = (int64_t)grp * 256 + threadIdx.x; c < nch && t0 < t1; c += 256 * kProbeGroups) {
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = t0 + i < t1 ? a.g[(t0 + i) * nch + c] : 0.f;   // loads in flight together
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sum += x[i];
+        weak |= !(sum <= kProbeDecay);
+    }
+    weak = __syncthreads_or(weak);
+    if (threadIdx.x == 0) probe[blockIdx.x] = weak;
+}
+
+// One workgroup of 256 threads chooses the layout from the probe (eager where every probed
+// channel decays by e^-25 per chunk or more), prices every candidate segment length (the longest
+// sequence cut into 2 .. Pmax pieces) with the model above and writes the plan of the best.
 __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __restrict__ plan, int slots,
                                                    SplitLimits lim) {
-    __shared__ double rd[3][256];
-    __shared__ int64_t ri[3][256];
+    __shared__ double rd[5][256];
+    __shared__ int64_t ri[4][256];
     const int t = threadIdx.x;
     const int N = a.N, H = a.H, nsl = a.dv / kDVT, nslt = (a.dv + a.dk) / kDVT;
-    auto reduce = [&](double& w1, double& w2, double& wh, int64_t& c1, int64_t& c2, int64_t& ns) {
-        rd[0][t] = w1;
-        rd[1][t] = w2;
-        rd[2][t] = wh;
-        ri[0][t] = c1;
-        ri[1][t] = c2;
-        ri[2][t] = ns;
-        __syncthreads();
-        for (int k = 128; k > 0; k >>= 1) {
-            if (t < k) {
-                rd[0][t] += rd[0][t + k];
-                rd[1][t] += rd[1][t + k];
-                rd[2][t] += rd[2][t + k];
-                ri[0][t] = ri[0][t] > ri[0][t + k] ? ri[0][t] : ri[0][t + k];
-                ri[1][t] = ri[1][t] > ri[1][t + k] ? ri[1][t] : ri[1][t + k];
-                ri[2][t] += ri[2][t + k];
-            }
-            __syncthreads();
-        }
-        w1 = rd[0][0];
-        w2 = rd[1][0];
-        wh = rd[2][0];
-        c1 = ri[0][0];
-        c2 = ri[1][0];
-        ns = ri[2][0];
-        __syncthreads();
-    };
-    auto price = [&](int64_t L, SplitCost& c) {
-        SplitCost mine;
+    const PlanLayout lay{N, (int32_t)lim.Smax};
+    const bool eager = !__syncthreads_or(t < kProbeBlocks ? plan[lay.probe() + t] : 0);
+    // the cost of every sequence for the candidate L, summed (maxima for the critical paths)
+    auto price = [&](int64_t L, bool eg, SplitCost& c) {
+        SplitCost m;
         for (int n = t; n < N; n += 256) {
             int64_t row0, len;
             seq_bounds(a, n, row0, len);
             int P;
             int64_t Ls;
             split_of(len, L, lim.Pmax, P, Ls);
-            split_add(mine, len, P, Ls, nsl, nslt);
+            split_add(m, len, P, Ls, L, nsl, nslt, eg);
         }
-        reduce(mine.work1, mine.work2, mine.whole, mine.crit1, mine.crit2, mine.summaries);
-        c = mine;
+        rd[0][t] = m.work1;
+        rd[1][t] = m.work2;
+        rd[2][t] = m.work1f;
+        rd[3][t] = m.work2f;
+        rd[4][t] = m.big;
+        ri[0][t] = m.crit1;
+        ri[1][t] = m.crit2;
+        ri[2][t] = m.crit2f;
+        ri[3][t] = m.summaries;
+        __syncthreads();
+        for (int k = 128; k > 0; k >>= 1) {
+            if (t < k) {
+                for (int i = 0; i < 5; ++i) rd[i][t] += rd[i][t + k];
+                for (int i = 0; i < 3; ++i) ri[i][t] = max_i64(ri[i][t], ri[i][t + k]);
+                ri[3][t] += ri[3][t + k];
+            }
+            __syncthreads();
+        }
+        c.work1 = rd[0][0];
+        c.work2 = rd[1][0];
+        c.work1f = rd[2][0];
+        c.work2f = rd[3][0];
+        c.big = rd[4][0];
+        c.crit1 = ri[0][0];
+        c.crit2 = ri[1][0];
+        c.crit2f = ri[2][0];
+        c.summaries = ri[3][0];
+        __syncthreads();
     };
     SplitCost whole;
-    price(0, whole);
+    price(0, eager, whole);
     const int64_t longest = whole.crit1 * 32;   // in tokens, rounded up to whole chunks
-    double best = split_makespan(whole, H, slots) * kSplitGain;
-    int64_t bestL = 0;
-    double idle2 = 0.0;
-    for (int p = 2; p <= lim.Pmax; ++p) {
-        const int64_t L = split_candidate(longest, p);
-        if (L < lim.Lmin) break;
-        SplitCost c;
-        price(L, c);
-        if (c.summaries > lim.Smax) continue;
-        const double m = split_makespan(c, H, slots);
-        if (m < best) {
-            best = m;
-            bestL = L;
-            idle2 = split_idle2(c, H, slots);
-        }
-    }
+    const int64_t bestL = split_best(price, longest, lim, split_makespan(whole, 0, H, slots, false), H, slots,
+                                     eager);
     // The plan of bestL.  Sequences are taken longest first (ranked here for up to kRankMax of
     // them, in index order beyond): their summaries' first index and their pass-1 and pass-2
-    // items follow from exclusive prefix sums in that order.  Sequences left whole move to the
-    // second pass while the running sum of their work stays within its idle capacity.
-    const PlanLayout lay{N, (int32_t)lim.Smax};
+    // items follow from exclusive prefix sums in that order.
     __shared__ int32_t order[kRankMax];
     __shared__ int64_t lens[kRankMax];
     const bool ranked = N <= kRankMax;
@@ -1431,8 +1481,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
         __syncthreads();
     }
     int32_t c_sum = 0, c_a = 0, c_b = 0;
-    int64_t c_w = 0;
-    __shared__ int32_t sc[4][256];
+    __shared__ int32_t sc[3][256];
     for (int base = 0; base < N; base += 256) {
         const int r = base + t;
         int P = 0;
@@ -1446,22 +1495,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             plan[lay.segs() + n] = P;
             plan[lay.seglen() + n] = (int32_t)(P > 1 ? Ls : (Ls > 0 ? Ls : kC));
         }
-        // work of a whole sequence per head, in chunk steps (below 2^31: T < 2^31, dv <= 256)
-        const int32_t w = r < N && P == 1 ? nsl * (int32_t)chunks_of(Ls) : 0;
-        sc[3][t] = w;
-        __syncthreads();
-        for (int k = 1; k < 256; k <<= 1) {
-            const int32_t x3 = t >= k ? sc[3][t - k] : 0;
-            __syncthreads();
-            sc[3][t] += x3;
-            __syncthreads();
-        }
-        const bool moved = r < N && P == 1 && (double)(c_w + sc[3][t]) <= idle2;
-        const int na = r < N ? (P > 1 ? P - 1 : (moved ? 0 : 1)) : 0;   // pass-1 items
-        // pass-2 items: segments 1 .. P - 1, or the whole run of a moved sequence
-        const int nb = r < N ? (P > 1 ? P - 1 : (moved ? 1 : 0)) : 0;
+        // pass-1 items: every segment (deferred: all but the last; a whole run: one)
+        const int na = r < N ? (P > 1 && !eager ? P - 1 : P) : 0;
+        const int nb = r < N ? P - 1 : 0;   // pass-2 items: segments 1 .. P - 1
         const int ns = r < N ? P - 1 : 0;   // summaries
-        __syncthreads();
         sc[0][t] = ns;
         sc[1][t] = na;
         sc[2][t] = nb;
@@ -1477,7 +1514,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
         }
         if (r < N) {
             plan[lay.first() + n] = c_sum + sc[0][t] - ns;
-            int32_t ia = c_a + sc[1][t] - na, ib = c_b + sc[2][t] - nb;
+            const int32_t ia = c_a + sc[1][t] - na, ib = c_b + sc[2][t] - nb;
             int32_t* A = plan + lay.items1();
             int32_t* B = plan + lay.items2();
             for (int j = 0; j < na; ++j) {
@@ -1486,24 +1523,28 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             }
             for (int j = 0; j < nb; ++j) {
                 B[2 * (ib + j)] = n;
-                B[2 * (ib + j) + 1] = P > 1 ? j + 1 : 0;
+                B[2 * (ib + j) + 1] = j + 1;
             }
         }
         c_sum += sc[0][255];
         c_a += sc[1][255];
         c_b += sc[2][255];
-        c_w += sc[3][255];
         __syncthreads();
     }
     if (t == 0) {
         plan[0] = (int32_t)bestL;
         plan[1] = c_a;
         plan[2] = c_b;
-        plan[3] = 0;
+        plan[3] = eager ? 1 : 0;
     }
 }
 
 hipError_t launch_plan(const PrefillArgs& a, int32_t* plan, int slots, SplitLimits lim) {
+    const PlanLayout lay{a.N, (int32_t)lim.Smax};
+    const int64_t tokens = a.cu ? a.T : (int64_t)a.N * a.T;
+    hipLaunchKernelGGL(probe_kernel, dim3(kProbeBlocks), dim3(256), 0, a.stream, a, plan + lay.probe(), tokens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, a.stream, a, plan, slots, lim);
     return hipGetLastError();
 }

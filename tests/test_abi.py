@@ -136,8 +136,9 @@ def test_chunk_fwd_ckpt_capacity_zero_needs_no_buffer(lib):
 
 
 def test_cp_workspace_size(lib):
-    assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 3) == 1 * 2 * 32 * 128 * 256 * 4
-    assert lib.kda_chunk_fwd_cp_workspace_size(2, 4, 64, 128, 4) == 2 * 3 * 4 * 64 * 192 * 4
+    # summaries [dk][dv + dk] float32 and one int32 stop count per 64 transition columns
+    assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 3) == 1 * 2 * 32 * (128 * 256 + 2) * 4
+    assert lib.kda_chunk_fwd_cp_workspace_size(2, 4, 64, 128, 4) == 2 * 3 * 4 * (64 * 192 + 1) * 4
     assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 1) == 0
     assert lib.kda_chunk_fwd_cp_workspace_size(0, 32, 128, 128, 3) == 0
     big = 2**31 - 1                        # saturates instead of wrapping
@@ -179,10 +180,10 @@ def test_cp_noalloc_rejects_on_host(lib, kw, status):
 
 
 def test_cp_noalloc_limit_is_the_header_constant(lib):
-    fit = lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 9)      # 8 x 32 x 128 KiB
-    assert fit == 32 << 20
-    assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 10) > 32 << 20
-    assert _cp_noalloc(lib, H=32, segs=10) == binding.KDA_ERR_UNSUPPORTED
+    fit = lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 8)      # 7 x 32 x (128 KiB + 8 B)
+    assert fit <= 32 << 20
+    assert lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, 9) > 32 << 20
+    assert _cp_noalloc(lib, H=32, segs=9) == binding.KDA_ERR_UNSUPPORTED
     assert b"32 MiB" in lib.kda_last_error()
 
 
@@ -201,12 +202,13 @@ def test_chunk_fwd_cp_rejects_on_host(lib, kw, status):
 
 
 def test_cp_segment_count_helper(lib):
-    # 32 units of d = 128: pass 1 = 32 * (2 + 4 (p - 2)), pass 2 = 32 * 2 p, both <= 256
-    assert binding.cp_segments(32, 128, 128) == 3
-    assert binding.cp_segments(16, 128, 128) == 5
+    # 32 units of dv = 128: pass 1 runs 32 * 2 p value workgroups, <= 256
+    assert binding.cp_segments(32, 128, 128) == 4
+    assert binding.cp_segments(16, 128, 128) == 8
     assert binding.cp_segments(256, 128, 128) == 1
-    assert lib.kda_chunk_fwd_cp_segments(1, 32, 128, 128, 256) == 3    # the same through the ABI
-    assert lib.kda_chunk_fwd_cp_segments(1, 8, 64, 64, 256) == 17      # pass 1: 8 (1 + 2 (p - 2)) <= 256
+    assert lib.kda_chunk_fwd_cp_segments(1, 32, 128, 128, 256) == 4    # the same through the ABI
+    assert lib.kda_chunk_fwd_cp_segments(1, 8, 64, 64, 256) == 32      # 8 p <= 256
+    assert lib.kda_chunk_fwd_cp_segments(1, 1, 64, 64, 256) == 64      # at most 64
     assert lib.kda_chunk_fwd_cp_segments(1, 32, 128, 128, 0) == 1
     assert lib.kda_chunk_fwd_cp_segments(0, 32, 128, 128, 256) == 1
 
@@ -343,21 +345,22 @@ def test_chunk_fwd_workspace_size_plans_on_the_host(lib):
     assert size(1, 1 << 20, 32, 96, 128, 0) == 0
     # B=4, T=32768, H=32: 256 workgroups already fill the GPU, rows stay whole
     assert size(4, 4 * 32768, 32, 128, 128, 0) == 0
-    # one sequence of 2^20 tokens, 32 heads: split; the need is P - 1 summaries of the fixed path
-    one = size(1, 1 << 20, 32, 128, 128, 0)
-    summary = 32 * 128 * (128 + 128) * 4
-    assert one > 0 and one % summary == 0
-    P = one // summary + 1
-    assert one == lib.kda_chunk_fwd_cp_workspace_size(1, 32, 128, 128, P) and 2 <= P <= 16
+    summary = 32 * (128 * (128 + 128) + 2) * 4   # H x ([dk][dv + dk] float32 + dk / 64 int32)
+
+    def bound(N, total, H=32, d=128):
+        pmax = min(16, -(-2 * 256 // (H * d // 64)))
+        lmin = max(1024, -(-(-(-total // 64)) // 32) * 32)
+        smax = min(N * (pmax - 1), total // lmin)
+        return ((4 + 7 * N + 4 * smax + 64) * 4 + 255) // 256 * 256 + smax * summary
+
+    # one sequence of 2^20 tokens, 32 heads: a split pays; fixed rows and packed batches are
+    # planned alike on the device, so both ask for the same bound
+    assert size(1, 1 << 20, 32, 128, 128, 0) == bound(1, 1 << 20) > 0
+    assert size(1, 1 << 20, 32, 128, 128, 1) == bound(1, 1 << 20)
     # packed: an upper bound for any mix of lengths, plan first (few sequences only)
     assert size(64, 158485, 32, 128, 128, 1) > 0             # 4096 workgroups: planned
     assert size(65, 158485, 32, 128, 128, 1) == 0            # past 16 per CU: runs whole
-    N, total = 3, 158485
-    pmax = min(16, -(-2 * 256 // (32 * 2)))
-    lmin = max(1024, -(-(-(-total // 64)) // 32) * 32)
-    smax = min(N * (pmax - 1), total // lmin)
-    plan = ((4 + 7 * N + 4 * smax) * 4 + 255) // 256 * 256
-    assert size(N, total, 32, 128, 128, 1) == plan + smax * summary
+    assert size(3, 158485, 32, 128, 128, 1) == bound(3, 158485)
     assert size(1 << 17, 1 << 24, 1, 64, 64, 1) == 0            # beyond the device planner
 
 

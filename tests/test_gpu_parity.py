@@ -653,12 +653,19 @@ def test_segmented_transitions_stop_once_zero(gpu_lib, weak):
     o, ST = binding.chunk_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], segments=P,
                                  out_dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
-    summ = ws.view(torch.int32).view(P - 1, H, dk, dv + dk).cpu()   # [S~ | M] per segment, head
+    nsum = (P - 1) * H * dk * (dv + dk)
+    wsi = ws.view(torch.int32).cpu()
+    summ = wsi[:nsum].view(P - 1, H, dk, dv + dk)   # [S~ | M] per segment, head
     trans = summ[1:, :, :, dv:]                  # segment 0 is entered with S0: no transition
+    # per segment j >= 1, head and 64 transition columns: the chunks before the transition is zero
+    stops = wsi[nsum:nsum + (P - 1) * H * (dk // 64)].view(P - 1, H, dk // 64)
+    print(f"  stop counts per segment: {stops.amax(dim=(1, 2)).tolist()} of 32 chunks", flush=True)
     if weak:
         assert (trans != 0).any()
+        assert (stops == 32).all(), "a transition that never reaches zero runs its whole segment"
     else:
         assert (trans == 0).all(), "a transition that vanished was not written as +0.0"
+        assert ((stops >= 1) & (stops < 32)).all(), stops
     ro, rST = oracle_all(x)
     assert_close("o[cp transitions]", o.cpu().numpy(), ro)
     assert_close("S_T[cp transitions]", ST.cpu().numpy(), rST)
@@ -691,27 +698,58 @@ def test_segmented_varlen_and_dk64(gpu_lib):
 
 def _plan(ws, N, smax):
     """The plan kda_chunk_fwd left at the head of its workspace: (segment length, per-sequence
-    segment counts, first summaries, segment lengths, pass-1 items, pass-2 items), each item a
-    (sequence, segment) pair.  The item lists follow the per-sequence arrays, N + smax each."""
+    segment counts, first summaries, segment lengths, pass-1 items, pass-2 items, eager layout),
+    each item a (sequence, segment) pair.  The item lists follow the per-sequence arrays, N + smax
+    each."""
     p = ws[: (4 + 7 * N + 4 * smax) * 4].cpu().view(torch.int32).tolist()
     n1, n2 = p[1], p[2]
     i1 = 4 + 3 * N
     i2 = i1 + 2 * (N + smax)
     items1 = [(p[i1 + 2 * j], p[i1 + 2 * j + 1]) for j in range(n1)]
     items2 = [(p[i2 + 2 * j], p[i2 + 2 * j + 1]) for j in range(n2)]
-    return p[0], p[4:4 + N], p[4 + N:4 + 2 * N], p[4 + 2 * N:4 + 3 * N], items1, items2
+    return p[0], p[4:4 + N], p[4 + N:4 + 2 * N], p[4 + 2 * N:4 + 3 * N], items1, items2, p[3]
 
 
-def test_auto_split_long_sequence(gpu_lib):
-    """kda_chunk_fwd with a workspace on one long sequence of few heads: the host plan splits it
-    (the workspace it asks for is the segmented run's), and the result matches the oracle."""
+def _check_items(P, items1, items2, eager):
+    """Pass 1 holds every segment of a split sequence (deferred layout: all but the last) and the
+    whole sequences, pass 2 the segments after the first; nothing twice."""
+    N = len(P)
+    assert len(set(items1)) == len(items1) and len(set(items2)) == len(items2)
+    for n in range(N):
+        if P[n] > 1:
+            first_pass = P[n] if eager else P[n] - 1
+            assert sorted(j for m, j in items1 if m == n) == list(range(first_pass)), (n, items1)
+            assert sorted(j for m, j in items2 if m == n) == list(range(1, P[n])), (n, items2)
+        else:
+            assert (n, 0) in items1 and all(m != n for m, _ in items2), n
+    assert len(items1) == sum((p if eager else p - 1) if p > 1 else 1 for p in P)
+    assert len(items2) == sum(p - 1 for p in P)
+
+
+@pytest.mark.parametrize("weak", [False, True], ids=["decay", "weak_decay"])
+def test_auto_split_long_sequence(gpu_lib, weak):
+    """kda_chunk_fwd with a workspace on one long sequence of few heads: the plan splits it, in
+    the eager layout with the workload's decay and in the deferred one (the last segment run
+    whole in the second pass) with weak decay, and the result matches the oracle."""
     from linear_attention_chunkwise_amd import binding
     x = inputs.make_prefill_inputs(1, 12000, 2, 64, 64, seed=91)
+    if weak:
+        x["g"] = x["g"] * 0.002
     need = binding.chunk_fwd_workspace_size(1, 12000, 2, 64, 64, False)
-    summary = 2 * 64 * 128 * 4
-    assert need > 0 and need % summary == 0, need
-    print(f"  planned segments: {need // summary + 1}", flush=True)
-    o, ST = run_gpu(x, torch.float32)
+    assert need > 0, need
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                              out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    o, ST = o.cpu().numpy(), ST.cpu().numpy()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pmax = min(16, -(-2 * cus // 2))
+    smax = min(pmax - 1, 12000 // 1024)
+    L, P, first, seg, items1, items2, eager = _plan(ws, 1, smax)
+    print(f"  plan: L={L} P={P} eager={eager} items {items1} + {items2}", flush=True)
+    assert L > 0 and P[0] > 1 and eager == (0 if weak else 1)
+    _check_items(P, items1, items2, eager)
     ro, rST = oracle_all(x)
     assert_close("o[auto split]", o, ro)
     assert_close("S_T[auto split]", ST, rST)
@@ -722,9 +760,9 @@ def test_auto_split_long_sequence(gpu_lib):
 
 def test_auto_split_packed_by_length(gpu_lib):
     """Packed sequences planned on the device: the longest get the most segments, the short ones
-    stay whole and run in the pass with room for them (the second pass's idle slots here),
-    summaries are indexed compactly; every sequence matches the oracle (empty and one-token
-    sequences included), and the same plan without a final state gives the same outputs."""
+    stay whole and run in the first pass, summaries are indexed compactly; every sequence matches
+    the oracle (empty and one-token sequences included), and the same plan without a final state
+    gives the same outputs."""
     from linear_attention_chunkwise_amd import binding
     lens = [9000, 300, 0, 45, 1500, 3000, 1, 20000]
     cu = inputs.cu_from_lengths(lens)
@@ -741,8 +779,9 @@ def test_auto_split_packed_by_length(gpu_lib):
     pmax = min(16, -(-2 * cus // (H * 2)))
     lmin = max(1024, (-(-total // 64) + 31) // 32 * 32)
     smax = min(N * (pmax - 1), total // lmin)
-    L, P, first, seg, items1, items2 = _plan(ws, N, smax)
-    print(f"  plan: L={L} P={P} first={first} seg={seg} items {items1} + {items2}", flush=True)
+    L, P, first, seg, items1, items2, eager = _plan(ws, N, smax)
+    print(f"  plan: L={L} P={P} eager={eager} first={first} seg={seg} items {items1} + {items2}", flush=True)
+    assert eager == 1   # the generator's decay: every chunk decays every channel by far more than e^-25
     assert L > 0 and L % 32 == 0
     for n, ln in enumerate(lens):          # each sequence by its own length, at most pmax pieces
         want = 1 if ln <= L else -(-ln // L)
@@ -759,20 +798,7 @@ def test_auto_split_packed_by_length(gpu_lib):
         assert f == acc, spans
         acc += c
     assert acc == sum(p - 1 for p in P)
-    # items: segments 0 .. P - 2 of a split sequence in pass 1, 1 .. P - 1 in pass 2; a whole
-    # sequence in exactly one pass; those moved to pass 2 come first in longest-first order
-    assert len(set(items1)) == len(items1) and len(set(items2)) == len(items2)
-    whole = sorted((n for n in range(N) if P[n] == 1), key=lambda n: (-lens[n], n))
-    for n in range(N):
-        if P[n] > 1:
-            assert all((n, j) in items1 for j in range(P[n] - 1)), (n, items1)
-            assert all((n, j) in items2 for j in range(1, P[n])), (n, items2)
-    assert all((n, 0) in items1 or (n, 0) in items2 for n in whole)
-    assert not any((n, 0) in items1 and (n, 0) in items2 for n in whole)
-    assert len(items1) + len(items2) == 2 * sum(p - 1 for p in P if p > 1) + len(whole)
-    moved = [(n, 0) in items2 for n in whole]
-    assert moved == sorted(moved, reverse=True), moved
-    assert all(moved), "the second pass has room for every whole sequence of this batch"
+    _check_items(P, items1, items2, eager)
     ro, rST = oracle_all(x)
     assert_close("o[auto packed]", o.cpu().numpy(), ro)
     assert_close("S_T[auto packed]", ST.cpu().numpy(), rST)
@@ -788,8 +814,7 @@ def test_auto_split_packed_beyond_the_ranked_count(gpu_lib):
     """1500 packed sequences (past the 1024 the planner ranks by length; H=1, d=64, so the batch
     is still planned): three long ones among short ones.  Beyond the ranked count the planner
     takes sequences in index order: the split ones get their segments in both passes, every
-    whole sequence runs in exactly one pass, those moved to the second pass come first in index
-    order; every sequence matches the oracle."""
+    whole sequence runs in the first pass; every sequence matches the oracle."""
     from linear_attention_chunkwise_amd import binding
     rng = np.random.default_rng(95)
     lens = [int(x) for x in rng.integers(0, 65, size=1500)]
@@ -808,20 +833,12 @@ def test_auto_split_packed_beyond_the_ranked_count(gpu_lib):
     pmax = min(16, -(-2 * cus // H))
     lmin = max(1024, (-(-total // 64) + 31) // 32 * 32)
     smax = min(N * (pmax - 1), total // lmin)
-    L, P, first, seg, items1, items2 = _plan(ws, N, smax)
+    L, P, first, seg, items1, items2, eager = _plan(ws, N, smax)
     split = [n for n in range(N) if P[n] > 1]
-    print(f"  plan: L={L} split={[(n, P[n]) for n in split]} items {len(items1)} + {len(items2)}", flush=True)
+    print(f"  plan: L={L} eager={eager} split={[(n, P[n]) for n in split]} "
+          f"items {len(items1)} + {len(items2)}", flush=True)
     assert L > 0 and split == [100, 700, 1400][:len(split)] and 100 in split
-    assert len(set(items1)) == len(items1) and len(set(items2)) == len(items2)
-    for n in split:
-        assert all((n, j) in items1 for j in range(P[n] - 1))
-        assert all((n, j) in items2 for j in range(1, P[n]))
-    one1 = {n for n, j in items1 if P[n] == 1}
-    one2 = {n for n, j in items2 if P[n] == 1}
-    whole = [n for n in range(N) if P[n] == 1]
-    assert one1 | one2 == set(whole) and not (one1 & one2)
-    moved = [n in one2 for n in whole]
-    assert moved == sorted(moved, reverse=True), "moved sequences are a prefix in index order"
+    _check_items(P, items1, items2, eager)
     ro, rST = oracle_all(x)
     assert_close("o[auto packed 1500]", o.cpu().numpy(), ro)
     assert_close("S_T[auto packed 1500]", ST.cpu().numpy(), rST)
@@ -852,9 +869,9 @@ PLAN_SWEEP = _plan_sweep_cases()
 
 @pytest.mark.parametrize("i", range(len(PLAN_SWEEP)))
 def test_auto_split_packed_sweep(gpu_lib, i):
-    """kda_chunk_fwd with its automatic plan on random packed batches: the plan's item lists
-    hold every segment of a split sequence in its pass and every whole sequence in exactly one
-    pass, those in the second pass forming a longest-first prefix of the whole sequences; every
+    """kda_chunk_fwd with its automatic plan on random packed batches (every other case with weak
+    decay, which the plan's probe sees: the deferred layout): the plan's item lists hold every
+    segment of a split sequence in its pass and every whole sequence in the first pass; every
     sequence matches the oracle."""
     from linear_attention_chunkwise_amd import binding
     c = PLAN_SWEEP[i]
@@ -866,6 +883,9 @@ def test_auto_split_packed_sweep(gpu_lib, i):
           f"in={'f32' if c['f32_in'] else 'bf16'} out={'f32' if c['out_f32'] else 'bf16'} S0={c['s0']}", flush=True)
     x = inputs.make_prefill_inputs(1, total, H, dk, dv, dtype=dtype, seed=300 + i, cu_seqlens=cu,
                                    S0_std=0.1 if c["s0"] else None)
+    weak = i % 2 == 1
+    if weak:
+        x["g"] = x["g"] * 0.002
     need = binding.chunk_fwd_workspace_size(N, total, H, dk, dv, True)
     assert need > 0
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
@@ -878,20 +898,12 @@ def test_auto_split_packed_sweep(gpu_lib, i):
     pmax = min(16, -(-2 * cus // (H * dv // 64)))
     lmin = max(1024, (-(-total // 64) + 31) // 32 * 32)
     smax = min(N * (pmax - 1), total // lmin)
-    L, P, first, seg, items1, items2 = _plan(ws, N, smax)
-    print(f"  plan: L={L} split={[(n, P[n]) for n in range(N) if P[n] > 1]} "
+    L, P, first, seg, items1, items2, eager = _plan(ws, N, smax)
+    print(f"  plan: L={L} eager={eager} split={[(n, P[n]) for n in range(N) if P[n] > 1]} "
           f"items {len(items1)} + {len(items2)}", flush=True)
-    assert len(set(items1)) == len(items1) and len(set(items2)) == len(items2)
-    for n in range(N):
-        if P[n] > 1:
-            assert L > 0 and lens[n] > L
-            assert all((n, j) in items1 for j in range(P[n] - 1))
-            assert all((n, j) in items2 for j in range(1, P[n]))
-        else:
-            assert ((n, 0) in items1) != ((n, 0) in items2), n
-    whole = sorted((n for n in range(N) if P[n] == 1), key=lambda n: (-lens[n], n))
-    moved = [(n, 0) in items2 for n in whole]
-    assert moved == sorted(moved, reverse=True), moved
+    assert eager == (0 if weak else 1)
+    assert all(lens[n] > L > 0 for n in range(N) if P[n] > 1)
+    _check_items(P, items1, items2, eager)
     ro, rST = oracle_all(x)
     assert_close(f"o[plan sweep {i}]", o.float().cpu().numpy(), ro, stored_bf16=not c["out_f32"])
     assert_close(f"S_T[plan sweep {i}]", ST.cpu().numpy(), rST)
