@@ -76,7 +76,7 @@ struct PlanLayout {
     __host__ __device__ int64_t probe() const { return items2() + 2 * ((int64_t)N + Smax); }
     __host__ __device__ int64_t ints() const { return probe() + kProbeBlocks; }
     __host__ __device__ int32_t max_items1() const { return N + Smax; }
-    __host__ __device__ int32_t max_items2() const { return N + Smax; }
+    __host__ __device__ int32_t max_items2() const { return Smax; }   // one per summary
 };
 
 struct DecodeArgs {

@@ -726,15 +726,20 @@ def _check_items(P, items1, items2, eager):
     assert len(items2) == sum(p - 1 for p in P)
 
 
-@pytest.mark.parametrize("weak", [False, True], ids=["decay", "weak_decay"])
-def test_auto_split_long_sequence(gpu_lib, weak):
+@pytest.mark.parametrize("gates", ["decay", "weak_decay", "decay_then_weak"])
+def test_auto_split_long_sequence(gpu_lib, gates):
     """kda_chunk_fwd with a workspace on one long sequence of few heads: the plan splits it, in
     the eager layout with the workload's decay and in the deferred one (the last segment run
-    whole in the second pass) with weak decay, and the result matches the oracle."""
+    whole in the second pass) with weak decay.  With decay over the first 256 tokens only, the
+    probe picks the eager layout, no later transition reaches zero, and the second pass reruns
+    every later segment whole.  The result matches the oracle in each case."""
     from linear_attention_chunkwise_amd import binding
     x = inputs.make_prefill_inputs(1, 12000, 2, 64, 64, seed=91)
+    weak = gates == "weak_decay"
     if weak:
         x["g"] = x["g"] * 0.002
+    elif gates == "decay_then_weak":
+        x["g"][:, 256:] = x["g"][:, 256:] * 0.002
     need = binding.chunk_fwd_workspace_size(1, 12000, 2, 64, 64, False)
     assert need > 0, need
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
@@ -750,6 +755,17 @@ def test_auto_split_long_sequence(gpu_lib, weak):
     print(f"  plan: L={L} P={P} eager={eager} items {items1} + {items2}", flush=True)
     assert L > 0 and P[0] > 1 and eager == (0 if weak else 1)
     _check_items(P, items1, items2, eager)
+    # stop counts (after the plan and the summaries): chunks of each later segment that depend
+    # on its entering state, per head and 64 transition columns
+    pl = ((4 + 7 + 4 * smax + 64) * 4 + 255) // 256 * 256
+    nsum = smax * 2 * 64 * 128
+    stops = ws[pl:].view(torch.int32)[nsum:nsum + (P[0] - 1) * 2].cpu().view(P[0] - 1, 2)
+    seg_chunks = [-(-min(L, 12000 - j * L) // 32) for j in range(1, P[0])]
+    print(f"  stop counts {stops.amax(dim=1).tolist()} of {seg_chunks} chunks", flush=True)
+    if gates == "decay":
+        assert (stops.amax(dim=1) < torch.tensor(seg_chunks)).all()
+    elif gates == "decay_then_weak":
+        assert stops.amax(dim=1).tolist() == seg_chunks
     ro, rST = oracle_all(x)
     assert_close("o[auto split]", o, ro)
     assert_close("S_T[auto split]", ST, rST)
