@@ -1414,13 +1414,29 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
     const int t = threadIdx.x;
     const int N = a.N, H = a.H, nsl = a.dv / kDVT, nslt = (a.dv + a.dk) / kDVT;
     const PlanLayout lay{N, (int32_t)lim.Smax};
+    // the lengths, staged once in LDS (up to kRankMax sequences; read from memory beyond)
+    __shared__ int32_t order[kRankMax];
+    __shared__ int64_t lens[kRankMax];
+    const bool ranked = N <= kRankMax;
+    if (ranked) {
+        for (int n = t; n < N; n += 256) {
+            int64_t row0, len;
+            seq_bounds(a, n, row0, len);
+            lens[n] = len;
+        }
+    }
     const bool eager = !__syncthreads_or(t < kProbeBlocks ? plan[lay.probe() + t] : 0);
+    auto length = [&](int n) {
+        int64_t row0, len;
+        if (ranked) return lens[n];
+        seq_bounds(a, n, row0, len);
+        return len;
+    };
     // the cost of every sequence for the candidate L, summed (maxima for the critical paths)
     auto price = [&](int64_t L, bool eg, SplitCost& c) {
         SplitCost m;
         for (int n = t; n < N; n += 256) {
-            int64_t row0, len;
-            seq_bounds(a, n, row0, len);
+            const int64_t len = length(n);
             int P;
             int64_t Ls;
             split_of(len, L, lim.Pmax, P, Ls);
@@ -1463,16 +1479,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
     // The plan of bestL.  Sequences are taken longest first (ranked here for up to kRankMax of
     // them, in index order beyond): their summaries' first index and their pass-1 and pass-2
     // items follow from exclusive prefix sums in that order.
-    __shared__ int32_t order[kRankMax];
-    __shared__ int64_t lens[kRankMax];
-    const bool ranked = N <= kRankMax;
     if (ranked) {
-        for (int n = t; n < N; n += 256) {
-            int64_t row0, len;
-            seq_bounds(a, n, row0, len);
-            lens[n] = len;
-        }
-        __syncthreads();
         for (int n = t; n < N; n += 256) {
             int r = 0;
             for (int m = 0; m < N; ++m) r += (lens[m] > lens[n]) | ((lens[m] == lens[n]) & (m < n));
@@ -1489,9 +1496,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
         int n = 0;
         if (r < N) {
             n = ranked ? order[r] : r;
-            int64_t row0, len;
-            seq_bounds(a, n, row0, len);
-            split_of(len, bestL, lim.Pmax, P, Ls);
+            split_of(length(n), bestL, lim.Pmax, P, Ls);
             plan[lay.segs() + n] = P;
             plan[lay.seglen() + n] = (int32_t)(P > 1 ? Ls : (Ls > 0 ? Ls : kC));
         }
