@@ -1465,6 +1465,46 @@ def test_prefill_and_decode_replay_in_a_hip_graph(gpu_lib):
         assert torch.equal(od, od_ref), f"replay {r}: decode output"
 
 
+def test_auto_split_replays_in_a_hip_graph(gpu_lib):
+    """The automatic split (decay probe, planner and both passes) only enqueues kernels on the
+    caller's workspace: captured once, replayed with eager work between the replays, it matches the
+    eager run bitwise on every replay."""
+    from linear_attention_chunkwise_amd import binding
+    cu = inputs.cu_from_lengths([5000, 300, 0, 2100])
+    x = _to_dev(inputs.make_prefill_inputs(1, int(cu[-1]), 2, 64, 64, seed=53, cu_seqlens=cu))
+    need = binding.chunk_fwd_workspace_size(4, int(cu[-1]), 2, 64, 64, True)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o_ref, ST_ref = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["cu_seqlens"],
+                                      out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    assert ws[:4].view(torch.int32).item() > 0, "the batch is split"
+    o, ST = torch.empty_like(o_ref), torch.empty_like(ST_ref)
+
+    def work():
+        binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], x["cu_seqlens"],
+                          out_dtype=torch.float32, o=o, S_T=ST, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # one eager pass on the capturing stream first
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for r in range(4):
+        for t in (o, ST):                   # eager work between the replays
+            t.fill_(7.0)
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {r}: o"
+        assert torch.equal(ST, ST_ref), f"replay {r}: S_T"
+
+
 def _every_entry_point():
     """Small runs of every entry point on fixed seeded inputs; the results as CPU tensors."""
     from linear_attention_chunkwise_amd import binding
@@ -1479,6 +1519,13 @@ def _every_entry_point():
     x = _to_dev(inputs.make_prefill_inputs(2, 150, 2, 128, 64, seed=62))
     r["plain"] = binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
     r["cp"] = binding.chunk_fwd_cp(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], segments=3)
+    # the automatic split of a packed batch, eager (the generator's decay) and deferred (weak)
+    cs = inputs.cu_from_lengths([3000, 50, 0, 1500])
+    xs = _to_dev(inputs.make_prefill_inputs(1, int(cs[-1]), 1, 64, 64, seed=67, cu_seqlens=cs))
+    r["split_eager"] = binding.chunk_fwd(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["S0"],
+                                         xs["cu_seqlens"], out_dtype=torch.float32)
+    r["split_deferred"] = binding.chunk_fwd(xs["q"], xs["k"], xs["v"], xs["g"] * 0.002, xs["beta"],
+                                            xs["S0"], xs["cu_seqlens"], out_dtype=torch.float32)
     r["ckpt"] = binding.chunk_fwd_ckpt(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"],
                                        interval=32, capacity=5)
     xf = _to_dev(inputs.make_prefill_inputs(1, 70, 2, 64, 64, dtype=torch.float32, seed=63))
