@@ -90,13 +90,14 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * §5.1.2, eq. (17); see kda_chunk_fwd_cp): with a workspace of at least
  * kda_chunk_fwd_workspace_size(N, B * T, H, dk, dv, cu_seqlens != NULL) bytes (16-byte aligned,
  * caller-owned, overlapping no input or output), the call plans by itself whether and how to
- * split sequences in time, on the device (no host synchronisation): a probe reads g over the
- * first 256 tokens of the batch, then one planning workgroup reads the sequence lengths
+ * split sequences in time, on the device (no host synchronisation): a probe reads g over 8
+ * chunks of 32 tokens spread evenly over the batch, then one planning workgroup reads the
+ * sequence lengths
  * (cu_seqlens, or the rows of a fixed-length batch), chooses a layout and a segment length and
  * writes the plan into the workspace.  Each sequence is cut by its own length: longer sequences
  * get more segments, those no longer than the segment length stay whole and run beside the
- * first pass.  Layouts: where every probed key channel decays by a factor e^-25 or more per
- * 32-token chunk, pass 1 runs every segment with its outputs (the later ones entered with 0) and
+ * first pass.  Layouts: where every probed key channel decays by a factor e^-25 or more over
+ * each probed chunk, pass 1 runs every segment with its outputs (the later ones entered with 0) and
  * pass 2 runs each later segment again from its true entering state only over the chunks before
  * its transition is exactly zero, after which its outputs no longer depend on that state (eq.
  * (17): the state is M S_in + S~ with M = 0); otherwise the last segment is left to pass 2,

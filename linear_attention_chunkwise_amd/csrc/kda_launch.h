@@ -63,7 +63,7 @@ struct PrefillArgs {
 //   pass-2 items [N + Smax] x {sequence, segment}: the segments after the first of the split
 //   sequences,
 //   probe[kProbeBlocks]: per workgroup of the decay probe, 1 where a key channel decayed by less
-//   than e^-25 over one of the first kProbeChunks chunks of the batch.
+//   than e^-25 over one of kProbeChunks 32-token samples spread evenly over the batch.
 constexpr int kProbeChunks = 8, kProbeGroups = 8, kProbeBlocks = kProbeChunks * kProbeGroups;
 constexpr float kProbeDecay = -25.f;
 struct PlanLayout {

@@ -1384,12 +1384,13 @@ bool split_may_pay(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int 
     return split_best(price, T, lim, base, H, slots, true) > 0 || split_best(price, T, lim, base, H, slots, false) > 0;
 }
 
-// Decay probe: workgroup (chunk j, channel group) sums g over the 32 tokens of chunk j of the
-// batch for its channels and records whether any decayed by less than e^-25 (or is NaN).
+// Decay probe: workgroup (sample j, channel group) sums g over the 32 tokens that start at
+// j / kProbeChunks of the batch (rounded down to a multiple of 32) for its channels and records
+// whether any decayed by less than e^-25 (or is NaN).
 __global__ __launch_bounds__(256) void probe_kernel(PrefillArgs a, int32_t* __restrict__ probe, int64_t tokens) {
     const int j = blockIdx.x / kProbeGroups, grp = blockIdx.x % kProbeGroups;
     const int64_t nch = (int64_t)a.H * a.dk;
-    const int64_t t0 = (int64_t)j * 32, t1 = t0 + 32 < tokens ? t0 + 32 : tokens;
+    const int64_t t0 = tokens * j / kProbeChunks / 32 * 32, t1 = t0 + 32 < tokens ? t0 + 32 : tokens;
     int weak = 0;
     for (int64_t c = (int64_t)grp * 256 + threadIdx.x; c < nch && t0 < t1; c += 256 * kProbeGroups) {
         float x[32];

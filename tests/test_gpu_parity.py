@@ -726,20 +726,25 @@ def _check_items(P, items1, items2, eager):
     assert len(items2) == sum(p - 1 for p in P)
 
 
-@pytest.mark.parametrize("gates", ["decay", "weak_decay", "decay_then_weak"])
+@pytest.mark.parametrize("gates", ["decay", "weak_decay", "decay_where_probed"])
 def test_auto_split_long_sequence(gpu_lib, gates):
     """kda_chunk_fwd with a workspace on one long sequence of few heads: the plan splits it, in
     the eager layout with the workload's decay and in the deferred one (the last segment run
-    whole in the second pass) with weak decay.  With decay over the first 256 tokens only, the
-    probe picks the eager layout, no later transition reaches zero, and the second pass reruns
-    every later segment whole.  The result matches the oracle in each case."""
+    whole in the second pass) with weak decay.  With decay only in the 8 chunks the planner's probe
+    samples (32 tokens at j/8 of the batch, j = 0 .. 7), the probe picks the eager layout, no
+    later transition reaches zero, and the second pass reruns every later segment whole.  The
+    result matches the oracle in each case."""
     from linear_attention_chunkwise_amd import binding
     x = inputs.make_prefill_inputs(1, 12000, 2, 64, 64, seed=91)
     weak = gates == "weak_decay"
     if weak:
         x["g"] = x["g"] * 0.002
-    elif gates == "decay_then_weak":
-        x["g"][:, 256:] = x["g"][:, 256:] * 0.002
+    elif gates == "decay_where_probed":
+        probed = torch.zeros(12000, dtype=torch.bool)
+        for j in range(8):
+            t0 = 12000 * j // 8 // 32 * 32
+            probed[t0:t0 + 32] = True
+        x["g"][:, ~probed] = x["g"][:, ~probed] * 0.002
     need = binding.chunk_fwd_workspace_size(1, 12000, 2, 64, 64, False)
     assert need > 0, need
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
@@ -764,7 +769,7 @@ def test_auto_split_long_sequence(gpu_lib, gates):
     print(f"  stop counts {stops.amax(dim=1).tolist()} of {seg_chunks} chunks", flush=True)
     if gates == "decay":
         assert (stops.amax(dim=1) < torch.tensor(seg_chunks)).all()
-    elif gates == "decay_then_weak":
+    elif gates == "decay_where_probed":
         assert stops.amax(dim=1).tolist() == seg_chunks
     ro, rST = oracle_all(x)
     assert_close("o[auto split]", o, ro)
