@@ -685,7 +685,7 @@ __device__ __forceinline__ void producer(const PrefillArgs& a, char* smem, int p
 template <int DK, bool F32IN, bool OUT_F32, bool SUMM, bool TSL>
 __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int cw, int lane,
                                          int64_t row0, int64_t len, int n, int h, int slice, int seg,
-                                         int mode, int nseg_n, int64_t sbase, bool full) {
+                                         int mode, int nseg_n, int64_t sbase, bool full, int jfrom) {
     using Lay = Layout<DK>;
     using IT = typename std::conditional<F32IN, float, bf16>::type;
     constexpr int KS = DK / 32;          // 32-channel contraction steps
@@ -731,14 +731,15 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
 #pragma unroll
             for (int j = 0; j < 4; ++j) Sacc[ct][j] = (16 * ct + 4 * g4 + j == c) ? 1.f : 0.f;
     } else if (mode == 2 && seg > 0) {
-        // entering state of segment seg: the state after segment 0 (entered with S0), carried
-        // through segments 1 .. seg-1 by S <- M_j S + S~_j (products on split bf16 operands)
-        const float* W0 = summary(0);
+        // entering state of segment seg: the state after segment jfrom (after segment 0, entered
+        // with S0, or S~ of a segment whose transition is zero), carried through segments
+        // jfrom + 1 .. seg-1 by S <- M_j S + S~_j (products on split bf16 operands)
+        const float* W0 = summary(jfrom);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) Sacc[ct][j] = W0[(size_t)(16 * ct + 4 * g4 + j) * wcols + col0 + i16];
-        for (int jseg = 1; jseg < seg; ++jseg) {
+        for (int jseg = jfrom + 1; jseg < seg; ++jseg) {
             const float* Wj = summary(jseg);
             bf16x8 Sh[KS], Sl[KS];
 #pragma unroll
@@ -1188,6 +1189,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
     block_coords<SUMM>(nslices, a.dv / kDVT, unit, slice);
     int n, seg, mode = PASS, nseg_n = 1;
     int64_t sbase = 0, row0, len;
+    int64_t seqlen = 0, segL = 0;   // split runs: the sequence's tokens and its segment length
     const int h = unit % a.H;
     if (PASS != 0 && a.plan) {
         // a planned split: the workgroup's item of this pass's list
@@ -1210,6 +1212,8 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         KDA_POISON(smem, (SUMM ? Layout<DK>::total_summ : Layout<DK>::total));
         KDA_POISON_DONE();
         seq_bounds(a, n, row0, len);
+        seqlen = len;
+        segL = L;
         if (mode != 0) {   // this segment's tokens
             const int64_t lo = (int64_t)seg * L;
             const int64_t hi = lo + L < len ? lo + L : len;
@@ -1235,6 +1239,8 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
             sbase = (int64_t)n * (nseg - 1);
             int64_t L = ((len + nseg - 1) / nseg + kC - 1) / kC * kC;
             if (L == 0) L = kC;
+            seqlen = len;
+            segL = L;
             const int64_t lo = (int64_t)seg * L;
             const int64_t hi = lo + L < len ? lo + L : len;
             row0 += lo;
@@ -1256,6 +1262,23 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
             full = false;
         }
     }
+    // The entering state S_in(seg) = M_{seg-1} S_in(seg-1) + S~_{seg-1} is rebuilt from the last
+    // earlier segment whose transition is exactly zero (its chunks before zero are fewer than its
+    // chunks): the state after it is its S~, and the products with the earlier ones are +-0.
+    int jfrom = 0;
+    if (PASS == 2 && mode == 2) {
+        for (int jj = seg - 1; jj >= 1; --jj) {
+            const int64_t lo = (int64_t)jj * segL, rest = seqlen - lo;
+            const int64_t chunks = ((rest < segL ? (rest > 0 ? rest : 0) : segL) + kC - 1) / kC;
+            const int32_t* st = a.stops + ((size_t)(sbase + jj - 1) * a.H + h) * (DK / kDVT);
+            int64_t dep = 0;
+            for (int ts = 0; ts < DK / kDVT; ++ts) dep = dep > st[ts] ? dep : st[ts];
+            if (dep < chunks) {
+                jfrom = jj;
+                break;
+            }
+        }
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     // a workgroup of transition columns (segment summaries) may stop once they are all zero
@@ -1264,13 +1287,13 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         if (tslice) {   // its own code: the vote and the stop stay out of the value workgroups
             if (wave < kNW) producer<DK, F32IN, GATE, true>(a, smem, wave, lane, row0, len, h);
             else consumer<DK, F32IN, OUT_F32, true, true>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg,
-                                                           mode, nseg_n, sbase, full);
+                                                           mode, nseg_n, sbase, full, jfrom);
             return;
         }
     }
     if (wave < kNW) producer<DK, F32IN, GATE, false>(a, smem, wave, lane, row0, len, h);
     else consumer<DK, F32IN, OUT_F32, SUMM, false>(a, smem, wave - kNW, lane, row0, len, n, h, slice, seg, mode,
-                                                   nseg_n, sbase, full);
+                                                   nseg_n, sbase, full, jfrom);
 }
 
 template <int DK, bool F32IN, bool OUT_F32, bool GATE, bool RANK, int PASS>

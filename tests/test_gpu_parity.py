@@ -671,6 +671,33 @@ def test_segmented_transitions_stop_once_zero(gpu_lib, weak):
     assert_close("S_T[cp transitions]", ST.cpu().numpy(), rST)
 
 
+def test_segmented_entering_state_from_a_vanished_transition(gpu_lib):
+    """Four segments of 1024 tokens: weak decay in segment 0 (its state carries S0), the
+    workload's decay in segment 1 (its transition reaches zero), weak decay in segments 2 and 3.
+    Segment 3 then rebuilds its entering state from segment 1's S~ through M_2 (the products with
+    segment 0's state are zero) and segment 2 starts from S~_1; both carry state far into their
+    segment, so a wrong starting summary shows against the oracle."""
+    from linear_attention_chunkwise_amd import binding
+    H, dk, dv, P = 2, 128, 128, 4
+    x = inputs.make_prefill_inputs(1, 4096, H, dk, dv, seed=47)
+    x["g"][:, :1024] = x["g"][:, :1024] * 0.002
+    x["g"][:, 2048:] = x["g"][:, 2048:] * 0.002
+    x["beta"] = (x["beta"].float() * 0.25).to(x["beta"].dtype)
+    d = _to_dev(x)
+    need = binding.load().kda_chunk_fwd_cp_workspace_size(1, H, dk, dv, P)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    o, ST = binding.chunk_fwd_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], segments=P,
+                                 out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    nsum = (P - 1) * H * dk * (dv + dk)
+    stops = ws.view(torch.int32)[nsum:nsum + (P - 1) * H * (dk // 64)].cpu().view(P - 1, H, dk // 64)
+    print(f"  stop counts of segments 1..3: {stops.amax(dim=(1, 2)).tolist()} of 32 chunks", flush=True)
+    assert stops[0].amax() < 32 and (stops[1:] == 32).all()
+    ro, rST = oracle_all(x)
+    assert_close("o[cp from S~_1]", o.cpu().numpy(), ro)
+    assert_close("S_T[cp from S~_1]", ST.cpu().numpy(), rST)
+
+
 def test_segmented_varlen_and_dk64(gpu_lib):
     """Varlen batch (segments past a sequence's end are empty) and the d = 64 float32-input
     kernel, segmented."""
