@@ -62,10 +62,9 @@ struct PrefillArgs {
 //   1 runs and the whole runs of the others, longest sequences first,
 //   pass-2 items [N + Smax] x {sequence, segment}: the segments after the first of the split
 //   sequences,
-//   probe[kProbeBlocks]: per workgroup of the decay probe, 1 where a key channel decayed by less
-//   than e^-25 over one of kProbeChunks 32-token samples spread evenly over the batch.
+//   probe[kProbeBlocks]: per workgroup of the decay probe, the smallest decay (nats, float bits)
+//   of a key channel over one of kProbeChunks 32-token samples spread evenly over the batch.
 constexpr int kProbeChunks = 8, kProbeGroups = 8, kProbeBlocks = kProbeChunks * kProbeGroups;
-constexpr float kProbeDecay = -25.f;
 struct PlanLayout {
     int32_t N, Smax;
     __host__ __device__ int64_t segs() const { return 4; }
@@ -120,17 +119,19 @@ hipError_t launch_chunk_fwd(const PrefillArgs& a);
 // S0 and later ones from 0, each with its outputs (nsl x ceil(Ls_j / 32)), and the transitions
 // of the segments j >= 1 it runs (nslt - nsl workgroups x ceil(Ls_j / 32)); in pass 2 each
 // segment j >= 1 again from its true entering state, over c_j + j steps: c_j chunks whose outputs
-// depend on that state (the chunks until the segment's transition is exactly zero) and the j
+// depend on that state (the chunks until the segment's transition is negligible) and the j
 // summaries it composes.  Two layouts:
 //   eager:    pass 1 runs every segment, so pass 2 runs only the c_j chunks of each;
 //   deferred: pass 1 runs all but the last, which pass 2 runs whole (c = its length).
-// Transitions stop, and c_j ends, once the transition's columns are exactly zero, which a decay
-// of every key channel by e^-25 or more per chunk brings about within kTransSteps chunks: the
-// expected cost counts kTransSteps chunks for both, the full cost (no transition reaches zero)
-// the whole segment.  A pass on `slots` concurrent workgroups takes at least its longest
-// workgroup, at least its total work / slots and, where more than `slots` segment workgroups of
-// about the candidate length run in pass 1, at least two of them in a row.
-constexpr int64_t kTransSteps = 8;
+// Transitions stop, and c_j ends, once every entry of the transition is below 2^-140 of the
+// identity it starts from, which a decay of every key channel by d nats per chunk brings about
+// within about kZeroNats / d chunks: the expected cost counts `trans` chunks for both (the
+// planner's estimate from the decay probe), the full cost (no transition vanishes) the whole
+// segment.  A pass on `slots` concurrent workgroups takes at least its longest workgroup, at least
+// its total work / slots and, where more than `slots` segment workgroups of about the candidate
+// length run in pass 1, at least two of them in a row.
+constexpr int64_t kTransSteps = 8;          // the host's estimate (it cannot see g)
+constexpr double kZeroNats = 140 * 0.6931471805599453;   // ln 2^140
 struct SplitCost {
     double work1 = 0, work2 = 0;     // per head, expected
     double work1f = 0, work2f = 0;   // per head, if no transition reaches zero
@@ -158,7 +159,7 @@ __host__ __device__ inline void split_of(int64_t len, int64_t L, int Pmax, int& 
 }
 // Adds one sequence of len tokens cut into P segments of Ls tokens (candidate length L).
 __host__ __device__ inline void split_add(SplitCost& c, int64_t len, int P, int64_t Ls, int64_t L, int nsl,
-                                          int nslt, bool eager) {
+                                          int nslt, bool eager, int64_t trans) {
     if (P <= 1) {
         const double w = (double)nsl * chunks_of(len);
         c.work1 += w;
@@ -168,7 +169,7 @@ __host__ __device__ inline void split_add(SplitCost& c, int64_t len, int P, int6
     }
     const int64_t ch = chunks_of(Ls), chl = chunks_of(max_i64(0, len - (int64_t)(P - 1) * Ls));   // full, last
     const int ntsl = nslt - nsl;
-    const int64_t e = min_i64(ch, kTransSteps), el = min_i64(chl, kTransSteps);
+    const int64_t e = min_i64(ch, trans), el = min_i64(chl, trans);
     const double comp = (double)P * (P - 1) / 2;   // summaries composed by segments 1 .. P - 1
     const int64_t tall = chunks_of(L) * 9 / 10;
     c.crit1 = max_i64(c.crit1, ch);

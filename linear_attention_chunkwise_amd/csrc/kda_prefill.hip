@@ -1092,20 +1092,29 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
         }
         if (TSL) {
             // transition columns: V is 0, so once every entry is exactly zero every later step
-            // leaves them zero (R = 0 - K~ 0, S <- gamma 0 + W 0); this wave's vote to stop
+            // leaves them zero (R = 0 - K~ 0, S <- gamma 0 + W 0).  Entries that small in value
+            // need not reach zero: with the scale at its floor (2^-120) their float16 operands sit
+            // on the subnormal grid, where the rounded update can hold them near 2^-24 instead of
+            // letting them decay.  So below 2^-20 there (2^-140 of the identity the transition
+            // starts from) they count as zero too.  This wave's vote to stop (NaN never votes).
             uint32_t nz = 0;
+            bool tiny = true;
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) nz |= __builtin_bit_cast(uint32_t, Sacc[ct][j]) & 0x7fffffffu;
-            const bool zero = __builtin_amdgcn_ballot_w64(nz != 0) == 0;
+                for (int j = 0; j < 4; ++j) {
+                    nz |= __builtin_bit_cast(uint32_t, Sacc[ct][j]) & 0x7fffffffu;
+                    tiny = tiny && fabsf(Sacc[ct][j]) < 0x1p-20f;
+                }
+            const bool zero = __builtin_amdgcn_ballot_w64(nz != 0) == 0 ||
+                              (esc <= -120 && __builtin_amdgcn_ballot_w64(!tiny) == 0);
             if (lane == 0) reinterpret_cast<int*>(smem + Lay::o_stop)[cw] = zero ? 1 : 0;
         }
         __syncthreads();
         if constexpr (TSL) {
             if (stop_voted(smem + Lay::o_stop)) {
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();   // +0, as the remaining steps give
+                for (int ct = 0; ct < CT; ++ct) Sacc[ct] = zero4();   // +0
                 // the state after chunks 0 .. it - 2 is zero: from chunk it - 1 on, the outputs of
                 // the segment do not depend on the state it is entered with
                 dep = it - 1 < nchunks ? it - 1 : nchunks;
@@ -1361,17 +1370,16 @@ hipError_t launch_chunk_fwd(const PrefillArgs& a) {
     return a.z ? dispatch_prefill<true>(a) : dispatch_prefill<false>(a);
 }
 
-// The best candidate of one layout: its segment length (0: none qualifies).  price(L, eager, c)
-// fills c with the batch's cost for segment length L.  Eager (the probe saw every channel decay):
-// a candidate must be expected to beat the whole schedule by kSplitGain and, should no transition
-// reach zero after all, take at most kSplitRisk times as long as it; the lowest expected time
-// wins, near ties going to the lower worst case.  Deferred (weak decay seen): the transitions are
-// priced in full, which must beat the whole schedule by kSplitGain; the lowest wins.
+// The best candidate of one layout: its segment length (0: none qualifies) and its score.
+// price(L, eager, c) fills c with the batch's cost for segment length L.  A candidate must be
+// expected to beat the whole schedule by kSplitGain and, should no transition vanish after all,
+// take at most kSplitRisk times as long as it; the lowest expected time wins, near ties going to
+// the lower worst case.
 constexpr double kSplitRisk = 1.25, kSplitTie = 0.05;
 template <class Price>
 __host__ __device__ inline int64_t split_best(Price&& price, int64_t longest, const SplitLimits& lim,
-                                              double base, int H, int slots, bool eager) {
-    double best = 0.0;
+                                              double base, int H, int slots, bool eager, double& best) {
+    best = 0.0;
     int64_t bestL = 0;
     for (int p = 2; p <= lim.Pmax; ++p) {
         const int64_t L = split_candidate(longest, p);
@@ -1380,9 +1388,8 @@ __host__ __device__ inline int64_t split_best(Price&& price, int64_t longest, co
         price(L, eager, c);
         if (c.summaries > lim.Smax) continue;
         const double m = split_makespan(c, L, H, slots, false), f = split_makespan(c, L, H, slots, true);
-        const bool ok = eager ? (m < base * kSplitGain && f <= base * kSplitRisk) : f < base * kSplitGain;
-        const double score = eager ? m + kSplitTie * f : f;
-        if (ok && (bestL == 0 || score < best)) {
+        const double score = m + kSplitTie * f;
+        if (m < base * kSplitGain && f <= base * kSplitRisk && (bestL == 0 || score < best)) {
             best = score;
             bestL = L;
         }
@@ -1398,23 +1405,26 @@ bool split_may_pay(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int 
         int P;
         int64_t Ls;
         split_of(T, L, lim.Pmax, P, Ls);
-        split_add(c, T, P, Ls, L, nsl, nslt, eager);
+        split_add(c, T, P, Ls, L, nsl, nslt, eager, kTransSteps);
         split_times(c, N);
     };
     SplitCost whole;
     price(0, false, whole);
     const double base = split_makespan(whole, 0, H, slots, false);
-    return split_best(price, T, lim, base, H, slots, true) > 0 || split_best(price, T, lim, base, H, slots, false) > 0;
+    double score;
+    return split_best(price, T, lim, base, H, slots, true, score) > 0 ||
+           split_best(price, T, lim, base, H, slots, false, score) > 0;
 }
 
 // Decay probe: workgroup (sample j, channel group) sums g over the 32 tokens that start at
 // j / kProbeChunks of the batch (rounded down to a multiple of 32) for its channels and records
-// whether any decayed by less than e^-25 (or is NaN).
+// the smallest decay among them (nats; 0 for a NaN sum, +inf for an empty sample).
 __global__ __launch_bounds__(256) void probe_kernel(PrefillArgs a, int32_t* __restrict__ probe, int64_t tokens) {
+    __shared__ float red[256];
     const int j = blockIdx.x / kProbeGroups, grp = blockIdx.x % kProbeGroups;
     const int64_t nch = (int64_t)a.H * a.dk;
     const int64_t t0 = tokens * j / kProbeChunks / 32 * 32, t1 = t0 + 32 < tokens ? t0 + 32 : tokens;
-    int weak = 0;
+    float dmin = __builtin_inff();
     for (int64_t c = (int64_t)grp * 256 + threadIdx.x; c < nch && t0 < t1; c += 256 * kProbeGroups) {
         float x[32];
 #pragma unroll
@@ -1422,15 +1432,21 @@ __global__ __launch_bounds__(256) void probe_kernel(PrefillArgs a, int32_t* __re
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; ++i) sum += x[i];
-        weak |= !(sum <= kProbeDecay);
+        const float d = -sum;
+        dmin = d >= 0.f ? (d < dmin ? d : dmin) : 0.f;   // NaN or growth: no decay
     }
-    weak = __syncthreads_or(weak);
-    if (threadIdx.x == 0) probe[blockIdx.x] = weak;
+    red[threadIdx.x] = dmin;
+    __syncthreads();
+    for (int k = 128; k > 0; k >>= 1) {
+        if (threadIdx.x < k) red[threadIdx.x] = red[threadIdx.x + k] < red[threadIdx.x] ? red[threadIdx.x + k] : red[threadIdx.x];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) probe[blockIdx.x] = __builtin_bit_cast(int32_t, red[0]);
 }
 
-// One workgroup of 256 threads chooses the layout from the probe (eager where every probed
-// channel decays by e^-25 per chunk or more), prices every candidate segment length (the longest
-// sequence cut into 2 .. Pmax pieces) with the model above and writes the plan of the best.
+// One workgroup of 256 threads estimates from the probe how many chunks a transition runs
+// before it vanishes, prices every candidate segment length (the longest sequence cut into
+// 2 .. Pmax pieces) in both layouts with the model above and writes the plan of the best.
 __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __restrict__ plan, int slots,
                                                    SplitLimits lim) {
     __shared__ double rd[5][256];
@@ -1449,7 +1465,15 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             lens[n] = len;
         }
     }
-    const bool eager = !__syncthreads_or(t < kProbeBlocks ? plan[lay.probe() + t] : 0);
+    // the weakest decay per chunk the probe saw: transitions fall below 2^-140 of the identity
+    // within about kZeroNats / d chunks (the delta rule's own contraction only shortens that)
+    __shared__ float pd[kProbeBlocks];
+    if (t < kProbeBlocks) pd[t] = __builtin_bit_cast(float, plan[lay.probe() + t]);
+    __syncthreads();
+    float dmin = __builtin_inff();
+    for (int i = 0; i < kProbeBlocks; ++i) dmin = pd[i] < dmin ? pd[i] : dmin;
+    const double tr = dmin > 0.f ? kZeroNats / dmin + 2.0 : 1e18;
+    const int64_t trans = tr < 1e9 ? (int64_t)tr : (int64_t)1000000000;
     auto length = [&](int n) {
         int64_t row0, len;
         if (ranked) return lens[n];
@@ -1464,7 +1488,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
             int P;
             int64_t Ls;
             split_of(len, L, lim.Pmax, P, Ls);
-            split_add(m, len, P, Ls, L, nsl, nslt, eg);
+            split_add(m, len, P, Ls, L, nsl, nslt, eg, trans);
         }
         rd[0][t] = m.work1;
         rd[1][t] = m.work2;
@@ -1496,10 +1520,14 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
         __syncthreads();
     };
     SplitCost whole;
-    price(0, eager, whole);
+    price(0, false, whole);
     const int64_t longest = whole.crit1 * 32;   // in tokens, rounded up to whole chunks
-    const int64_t bestL = split_best(price, longest, lim, split_makespan(whole, 0, H, slots, false), H, slots,
-                                     eager);
+    const double base = split_makespan(whole, 0, H, slots, false);
+    double se, sd;   // the better of the two layouts' best candidates
+    const int64_t Le = split_best(price, longest, lim, base, H, slots, true, se);
+    const int64_t Ld = split_best(price, longest, lim, base, H, slots, false, sd);
+    const bool eager = Le > 0 && (Ld == 0 || se <= sd);
+    const int64_t bestL = eager ? Le : Ld;
     // The plan of bestL.  Sequences are taken longest first (ranked here for up to kRankMax of
     // them, in index order beyond): their summaries' first index and their pass-1 and pass-2
     // items follow from exclusive prefix sums in that order.

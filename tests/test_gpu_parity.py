@@ -756,11 +756,11 @@ def _check_items(P, items1, items2, eager):
 @pytest.mark.parametrize("gates", ["decay", "weak_decay", "decay_where_probed"])
 def test_auto_split_long_sequence(gpu_lib, gates):
     """kda_chunk_fwd with a workspace on one long sequence of few heads: the plan splits it, in
-    the eager layout with the workload's decay and in the deferred one (the last segment run
-    whole in the second pass) with weak decay.  With decay only in the 8 chunks the planner's probe
-    samples (32 tokens at j/8 of the batch, j = 0 .. 7), the probe picks the eager layout, no
-    later transition reaches zero, and the second pass reruns every later segment whole.  The
-    result matches the oracle in each case."""
+    the eager layout with the workload's decay and in either layout with weak decay (whose
+    transitions run whole).  With decay only in the 8 chunks the planner's probe samples (32
+    tokens at j/8 of the batch, j = 0 .. 7), the plan takes the eager layout, no later
+    transition vanishes, and the second pass reruns every later segment whole.  The result
+    matches the oracle in each case."""
     from linear_attention_chunkwise_amd import binding
     x = inputs.make_prefill_inputs(1, 12000, 2, 64, 64, seed=91)
     weak = gates == "weak_decay"
@@ -785,7 +785,8 @@ def test_auto_split_long_sequence(gpu_lib, gates):
     smax = min(pmax - 1, 12000 // 1024)
     L, P, first, seg, items1, items2, eager = _plan(ws, 1, smax)
     print(f"  plan: L={L} P={P} eager={eager} items {items1} + {items2}", flush=True)
-    assert L > 0 and P[0] > 1 and eager == (0 if weak else 1)
+    # with weak decay the transitions run whole in either layout and the two price alike
+    assert L > 0 and P[0] > 1 and (weak or eager == 1)
     _check_items(P, items1, items2, eager)
     # stop counts (after the plan and the summaries): chunks of each later segment that depend
     # on its entering state, per head and 64 transition columns
@@ -918,9 +919,9 @@ PLAN_SWEEP = _plan_sweep_cases()
 @pytest.mark.parametrize("i", range(len(PLAN_SWEEP)))
 def test_auto_split_packed_sweep(gpu_lib, i):
     """kda_chunk_fwd with its automatic plan on random packed batches (every other case with weak
-    decay, which the plan's probe sees: the deferred layout): the plan's item lists hold every
-    segment of a split sequence in its pass and every whole sequence in the first pass; every
-    sequence matches the oracle."""
+    decay, which the plan's probe sees): the eager layout with the generator's decay, either
+    layout with weak decay; the plan's item lists hold every segment of a split sequence in its
+    pass and every whole sequence in the first pass; every sequence matches the oracle."""
     from linear_attention_chunkwise_amd import binding
     c = PLAN_SWEEP[i]
     lens, H, dk, dv = c["lens"], c["H"], c["dk"], c["dv"]
@@ -949,7 +950,7 @@ def test_auto_split_packed_sweep(gpu_lib, i):
     L, P, first, seg, items1, items2, eager = _plan(ws, N, smax)
     print(f"  plan: L={L} eager={eager} split={[(n, P[n]) for n in range(N) if P[n] > 1]} "
           f"items {len(items1)} + {len(items2)}", flush=True)
-    assert eager == (0 if weak else 1)
+    assert weak or eager == 1
     assert all(lens[n] > L > 0 for n in range(N) if P[n] > 1)
     _check_items(P, items1, items2, eager)
     ro, rST = oracle_all(x)
