@@ -92,21 +92,20 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * caller-owned, overlapping no input or output), the call plans by itself whether and how to
  * split sequences in time, on the device (no host synchronisation): a probe reads g over 8
  * chunks of 32 tokens spread evenly over the batch, then one planning workgroup reads the
- * sequence lengths
- * (cu_seqlens, or the rows of a fixed-length batch), chooses a layout and a segment length and
- * writes the plan into the workspace.  Each sequence is cut by its own length: longer sequences
- * get more segments, those no longer than the segment length stay whole and run beside the
- * first pass.  Layouts: where every probed key channel decays by a factor e^-25 or more over
- * each probed chunk, pass 1 runs every segment with its outputs (the later ones entered with 0) and
- * pass 2 runs each later segment again from its true entering state only over the chunks before
- * its transition is exactly zero, after which its outputs no longer depend on that state (eq.
- * (17): the state is M S_in + S~ with M = 0); otherwise the last segment is left to pass 2,
- * which runs it whole.  The planner prices each candidate segment length with a model of the
- * two passes on this GPU's compute units (a pass lasts at least its longest workgroup and at
- * least its total work over the units) and splits only when that is expected to beat the
- * whole-sequence schedule by 5 % (with weak decay: pricing every transition in full; with decay:
- * expecting them to stop early, and taking at most 1.25 times the whole schedule should none
- * stop).  Batches
+ * sequence lengths (cu_seqlens, or the rows of a fixed-length batch), chooses a layout and a
+ * segment length and writes the plan into the workspace.  Each sequence is cut by its own
+ * length: longer sequences get more segments, those no longer than the segment length stay whole
+ * and run beside the first pass.  A segment's transition M (eq. (17): its state is M S_in + S~)
+ * vanishes once every entry is below 2^-140 of the identity it starts from; from there on its
+ * outputs no longer depend on the state it is entered with.  Layouts: eager, where pass 1 runs
+ * every segment with its outputs (the later ones entered with 0) and pass 2 runs each later
+ * segment again from its true entering state only over the chunks before its transition
+ * vanished; deferred, where the last segment is left to pass 2, which runs it whole.  From the
+ * weakest decay per chunk the probe saw, the planner estimates the chunks a transition needs to
+ * vanish, prices each candidate segment length in both layouts with a model of the two passes on
+ * this GPU's compute units (a pass lasts at least its longest workgroup and at least its total
+ * work over the units) and splits only when the best is expected to beat the whole-sequence
+ * schedule by 5 % and to take at most 1.25 times it should no transition vanish.  Batches
  * with more than 16 whole-sequence workgroups (n_seq H dv / 64) per compute unit run whole.
  * Results agree with the whole-sequence run within the operator's tolerance (not bit for bit);
  * the plan, and with it the result, is a deterministic function of the inputs.  With workspace
@@ -197,12 +196,14 @@ int32_t kda_chunk_fwd_cp_segments(int32_t N, int32_t H, int32_t dk, int32_t dv, 
  * Pass 1 runs every segment of every sequence and head with its outputs, the first entered with
  * S0 and the others with 0, and writes [S~ | M] (dk x (dv + dk), float32) for all but the last
  * to `workspace`, with, for every segment after the first, the number of its chunks before its
- * transition M is exactly zero.  The workgroups of the transition columns stop at that point
- * (the columns stay zero: the result is the same bit for bit).  Pass 2 rebuilds the entering
- * state of each later segment, S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1}, and runs the segment
- * again over those chunks, whose outputs depend on S_in(j) (all of them, and S_T for the last,
- * where the transition never reaches zero); the outputs after them are those of pass 1, since
- * there the state M S_in + S~ is S~.  Same results as kda_chunk_fwd within the operator's
+ * transition M vanishes (every entry zero, or below 2^-140 of the identity it starts from).
+ * The workgroups of the transition columns stop at that point and store M as +0.0, which changes
+ * no result by more than 2^-140 relative to the state carried in.  Pass 2 rebuilds the entering
+ * state of each later segment, S_in(j) = M_{j-1} S_in(j-1) + S~_{j-1} (from the last earlier
+ * segment whose M vanished), and runs the segment again over those chunks, whose outputs depend
+ * on S_in(j) (all of them, and S_T for the last, where the transition never vanishes); the
+ * outputs after them are those of pass 1, since there the state M S_in + S~ is S~ to that
+ * precision.  Same results as kda_chunk_fwd within the operator's
  * tolerance (the summaries are computed with the same arithmetic; the combination uses split
  * bf16 products with float32 accumulation).
  *

@@ -29,7 +29,7 @@ struct PrefillArgs {
     //           its outputs; the state after segments j < nseg - 1 -> ws (the last writes S_T),
     //           and for segments j >= 1 the transition (extra dk columns entered with the
     //           identity, value 0) -> ws for j < nseg - 1, with the number of its chunks before it
-    //           is exactly zero -> stops;
+    //           vanishes -> stops;
     //   mode 2: segments j >= 1 rebuild their entering state from the summaries of the segments
     //           before them and run again over the chunks whose outputs depend on it (all of
     //           them, and S_T for the last, where the transition never reaches zero).
@@ -258,8 +258,8 @@ __host__ __device__ inline SplitLimits split_limits(int32_t N, int64_t total, in
 // Whether a split in time can pay for N sequences of T tokens in either layout (the device
 // planner makes the choice).
 bool split_may_pay(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int slots);
-// The device planner (a decay probe over the first chunks, then one workgroup), writing the plan
-// laid out as PlanLayout{N, lim.Smax}.  a supplies g, cu (or fixed rows of T tokens), N, T, H,
+// The device planner (a decay probe over 8 chunks of the batch, then one workgroup), writing the
+// plan laid out as PlanLayout{N, lim.Smax}.  a supplies g, cu (or fixed rows of T tokens), N, T, H,
 // dk, dv and the stream.
 hipError_t launch_plan(const PrefillArgs& a, int32_t* plan, int slots, SplitLimits lim);
 // ok = every g[i], i < n, lies in [lo, hi] (NaN does not); synchronises `stream`

@@ -813,7 +813,7 @@ __device__ __forceinline__ void consumer(const PrefillArgs& a, char* smem, int c
     };
 
     const int64_t nchunks = (len + kC - 1) / kC;
-    int64_t dep = nchunks;   // transition columns: chunks before they are exactly zero
+    int64_t dep = nchunks;   // transition columns: chunks before they vanish
     if (nchunks > 0) prefetch_v(pa, 0);
     if (nchunks > 1) prefetch_v(pb, kC);
 
@@ -1257,9 +1257,9 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         }
     }
     // Second pass: eq. (17) gives the state of segment seg at each chunk as M S_in + S~, M the
-    // transition from the segment's start.  Once M is exactly zero (both of its 64-column slices
-    // stopped in the first pass), the outputs from there on are those of the first pass, run
-    // from 0: only the chunks before it run again.
+    // transition from the segment's start.  Once M has vanished (both of its 64-column slices
+    // stopped in the first pass: zero, or below 2^-140 of the identity), the outputs from there
+    // on are those of the first pass, run from 0: only the chunks before it run again.
     bool full = true;
     // (a deferred plan's last segment has no transition: it runs whole)
     if (PASS == 2 && mode == 2 && !(a.plan && !a.plan[3] && seg == nseg_n - 1)) {
@@ -1272,7 +1272,7 @@ __global__ __launch_bounds__(kNT) void prefill_kernel(PrefillArgs a) {
         }
     }
     // The entering state S_in(seg) = M_{seg-1} S_in(seg-1) + S~_{seg-1} is rebuilt from the last
-    // earlier segment whose transition is exactly zero (its chunks before zero are fewer than its
+    // earlier segment whose transition vanished (its chunks before that are fewer than its
     // chunks): the state after it is its S~, and the products with the earlier ones are +-0.
     int jfrom = 0;
     if (PASS == 2 && mode == 2) {

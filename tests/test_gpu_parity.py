@@ -638,10 +638,11 @@ def test_segmented_weak_decay_carries_state(gpu_lib, segments):
 
 @pytest.mark.parametrize("weak", [False, True], ids=["decay_vanishes", "weak_decay"])
 def test_segmented_transitions_stop_once_zero(gpu_lib, weak):
-    """The workgroups of a segment's transition columns stop as soon as those columns are exactly
-    zero (they stay zero).  With the workload's decay every transition a summary holds is +0.0 bit
-    for bit (the workspace is filled with 0xFF first, so the zeros were written); with weak decay
-    the transitions are carried in full.  Both runs match the oracle."""
+    """The workgroups of a segment's transition columns stop as soon as those columns vanish
+    (zero, or below 2^-140 of the identity they start from).  With the workload's decay every
+    transition a summary holds is +0.0 bit for bit (the workspace is filled with 0xFF first, so
+    the zeros were written); with weak decay over 32-chunk segments the transitions are carried
+    in full.  Both runs match the oracle."""
     from linear_attention_chunkwise_amd import binding
     H, dk, dv, P = 2, 128, 128, 4
     x = inputs.make_prefill_inputs(1, 4096, H, dk, dv, seed=43)
