@@ -1449,9 +1449,7 @@ __global__ __launch_bounds__(256) void probe_kernel(PrefillArgs a, int32_t* __re
 // 2 .. Pmax pieces) in both layouts with the model above and writes the plan of the best.
 __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __restrict__ plan, int slots,
                                                    SplitLimits lim) {
-    __shared__ double rd[5][256];
-    __shared__ int64_t ri[4][256];
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int N = a.N, H = a.H, nsl = a.dv / kDVT, nslt = (a.dv + a.dk) / kDVT;
     const PlanLayout lay{N, (int32_t)lim.Smax};
     // the lengths, staged once in LDS (up to kRankMax sequences; read from memory beyond)
@@ -1480,52 +1478,72 @@ __global__ __launch_bounds__(256) void plan_kernel(PrefillArgs a, int32_t* __res
         seq_bounds(a, n, row0, len);
         return len;
     };
-    // the cost of every sequence for the candidate L, summed (maxima for the critical paths)
-    auto price = [&](int64_t L, bool eg, SplitCost& c) {
+    // The cost of every sequence for the candidate L, priced by one wave: its lanes take the
+    // sequences in turn and a butterfly over the 64 lanes sums them (maxima for the critical
+    // paths), leaving the total in every lane.  The sums are of whole chunk counts, exact in
+    // double, so the result does not depend on the order.
+    auto price_wave = [&](int64_t L, bool eg) {
         SplitCost m;
-        for (int n = t; n < N; n += 256) {
+        for (int n = lane; n < N; n += 64) {
             const int64_t len = length(n);
             int P;
             int64_t Ls;
             split_of(len, L, lim.Pmax, P, Ls);
             split_add(m, len, P, Ls, L, nsl, nslt, eg, trans);
         }
-        rd[0][t] = m.work1;
-        rd[1][t] = m.work2;
-        rd[2][t] = m.work1f;
-        rd[3][t] = m.work2f;
-        rd[4][t] = m.big;
-        ri[0][t] = m.crit1;
-        ri[1][t] = m.crit2;
-        ri[2][t] = m.crit2f;
-        ri[3][t] = m.summaries;
-        __syncthreads();
-        for (int k = 128; k > 0; k >>= 1) {
-            if (t < k) {
-                for (int i = 0; i < 5; ++i) rd[i][t] += rd[i][t + k];
-                for (int i = 0; i < 3; ++i) ri[i][t] = max_i64(ri[i][t], ri[i][t + k]);
-                ri[3][t] += ri[3][t + k];
-            }
-            __syncthreads();
+        for (int k = 32; k > 0; k >>= 1) {
+            m.work1 += __shfl_xor(m.work1, k, 64);
+            m.work2 += __shfl_xor(m.work2, k, 64);
+            m.work1f += __shfl_xor(m.work1f, k, 64);
+            m.work2f += __shfl_xor(m.work2f, k, 64);
+            m.big += __shfl_xor(m.big, k, 64);
+            m.crit1 = max_i64(m.crit1, (int64_t)__shfl_xor((long long)m.crit1, k, 64));
+            m.crit2 = max_i64(m.crit2, (int64_t)__shfl_xor((long long)m.crit2, k, 64));
+            m.crit2f = max_i64(m.crit2f, (int64_t)__shfl_xor((long long)m.crit2f, k, 64));
+            m.summaries += (int64_t)__shfl_xor((long long)m.summaries, k, 64);
         }
-        c.work1 = rd[0][0];
-        c.work2 = rd[1][0];
-        c.work1f = rd[2][0];
-        c.work2f = rd[3][0];
-        c.big = rd[4][0];
-        c.crit1 = ri[0][0];
-        c.crit2 = ri[1][0];
-        c.crit2f = ri[2][0];
-        c.summaries = ri[3][0];
-        __syncthreads();
+        return m;
     };
-    SplitCost whole;
-    price(0, false, whole);
+    // every wave prices the whole schedule (the same total in each)
+    const SplitCost whole = price_wave(0, false);
     const int64_t longest = whole.crit1 * 32;   // in tokens, rounded up to whole chunks
     const double base = split_makespan(whole, 0, H, slots, false);
-    double se, sd;   // the better of the two layouts' best candidates
-    const int64_t Le = split_best(price, longest, lim, base, H, slots, true, se);
-    const int64_t Ld = split_best(price, longest, lim, base, H, slots, false, sd);
+    // the candidates, P = 2 .. Pmax in each layout (eager first), one wave each, four at a time;
+    // then the rule of split_best on each layout, in P order, and the better layout
+    constexpr int kMaxCand = 2 * 15;
+    __shared__ double cscore[kMaxCand];
+    __shared__ int64_t cL[kMaxCand];
+    __shared__ int cok[kMaxCand];
+    const int per = lim.Pmax - 1, ncand = 2 * per;
+    for (int i = wave; i < ncand; i += 4) {
+        const bool eg = i < per;
+        const int64_t L = split_candidate(longest, 2 + (eg ? i : i - per));
+        bool ok = false;
+        double score = 0.0;
+        if (L >= lim.Lmin) {
+            const SplitCost c = price_wave(L, eg);
+            const double m = split_makespan(c, L, H, slots, false), f = split_makespan(c, L, H, slots, true);
+            ok = c.summaries <= lim.Smax && m < base * kSplitGain && f <= base * kSplitRisk;
+            score = m + kSplitTie * f;
+        }
+        if (lane == 0) {
+            cok[i] = ok;
+            cscore[i] = score;
+            cL[i] = L;
+        }
+    }
+    __syncthreads();
+    int64_t Le = 0, Ld = 0;
+    double se = 0.0, sd = 0.0;
+    for (int i = 0; i < ncand; ++i) {
+        if (!cok[i]) continue;
+        int64_t& Lb = i < per ? Le : Ld;
+        double& sb = i < per ? se : sd;
+        if (Lb == 0 || cscore[i] < sb) {
+            Lb = cL[i];
+            sb = cscore[i];
+        }
+    }
     const bool eager = Le > 0 && (Ld == 0 || se <= sd);
     const int64_t bestL = eager ? Le : Ld;
     // The plan of bestL.  Sequences are taken longest first (ranked here for up to kRankMax of
