@@ -105,7 +105,7 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * vanish, prices each candidate segment length in both layouts with a model of the two passes on
  * this GPU's compute units (a pass lasts at least its longest workgroup and at least its total
  * work over the units) and splits only when the best is expected to beat the whole-sequence
- * schedule by 5 % and to take at most 1.25 times it should no transition vanish.  Batches
+ * schedule by 5 % and to take at most 1.5 times it should no transition vanish.  Batches
  * with more than 16 whole-sequence workgroups (n_seq H dv / 64) per compute unit run whole.
  * Results agree with the whole-sequence run within the operator's tolerance (not bit for bit);
  * the plan, and with it the result, is a deterministic function of the inputs.  With workspace

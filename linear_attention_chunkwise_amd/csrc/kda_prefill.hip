@@ -1375,7 +1375,7 @@ hipError_t launch_chunk_fwd(const PrefillArgs& a) {
 // expected to beat the whole schedule by kSplitGain and, should no transition vanish after all,
 // take at most kSplitRisk times as long as it; the lowest expected time wins, near ties going to
 // the lower worst case.
-constexpr double kSplitRisk = 1.25, kSplitTie = 0.05;
+constexpr double kSplitRisk = 1.5, kSplitTie = 0.05;
 template <class Price>
 __host__ __device__ inline int64_t split_best(Price&& price, int64_t longest, const SplitLimits& lim,
                                               double base, int H, int slots, bool eager, double& best) {
