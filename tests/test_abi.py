@@ -345,6 +345,11 @@ def test_chunk_fwd_workspace_size_plans_on_the_host(lib):
     assert size(1, 1 << 20, 32, 96, 128, 0) == 0
     # B=4, T=32768, H=32: 256 workgroups already fill the GPU, rows stay whole
     assert size(4, 4 * 32768, 32, 128, 128, 0) == 0
+    # fewer workgroups than compute units, or long rows: a split can pay, a workspace is asked for
+    for B, T, H in ((1, 32768, 32), (2, 32768, 32), (1, 131072, 16), (8, 8192, 8), (1, 16384, 4)):
+        assert size(B, B * T, H, 128, 128, 0) > 0, (B, T, H)
+    # rows too short for a segment of 1024 tokens never split
+    assert size(64, 64 * 1024, 1, 128, 128, 0) == 0
     summary = 32 * (128 * (128 + 128) + 2) * 4   # H x ([dk][dv + dk] float32 + dk / 64 int32)
 
     def bound(N, total, H=32, d=128):
