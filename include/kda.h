@@ -162,14 +162,17 @@ kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const
  *
  * z: [B, T, H, dk] in in_dtype, 16-byte aligned; A_log: device float32 [H], 4-byte aligned.  Every
  * other argument, the layouts and the results are those of kda_chunk_fwd evaluated on that g
- * (the map runs in float32).  o must not overlap z or A_log either.
+ * (the map runs in float32), the workspace and the split in time it enables included (its decay
+ * probe maps the logits it samples the same way; kda_chunk_fwd_workspace_size gives the size).
+ * o must not overlap z or A_log either.
  * Returns KDA_OK, KDA_ERR_INVALID_ARGUMENT (also: z or A_log NULL or misaligned),
  * KDA_ERR_UNSUPPORTED or KDA_ERR_HIP. */
 kda_status kda_chunk_fwd_gate(const void* q, const void* k, const void* v, const void* z,
                               const float* A_log, const void* beta, const float* S0,
                               const int32_t* cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t N,
                               int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype,
-                              float scale, void* o, float* S_T, hipStream_t stream);
+                              float scale, void* o, float* S_T, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace kda_chunk_fwd_cp needs: N * (segments - 1) * H * (dk * (dv + dk) + dk / 64)
  * * 4 (the summaries and stop counts below), 0 when segments <= 1 or a size is not positive,

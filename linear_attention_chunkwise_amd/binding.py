@@ -74,7 +74,8 @@ def load(path: str = LIB_PATH):
                                         ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.kda_recurrent_multi.restype = ctypes.c_int
     lib.kda_chunk_fwd_gate.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
-                                       i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp]
+                                       i32, ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
     lib.kda_chunk_fwd_gate.restype = ctypes.c_int
     lib.kda_recurrent_step_gate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp]
@@ -332,15 +333,26 @@ def chunk_fwd_cp_noalloc(q, k, v, g, beta, S0=None, cu_seqlens=None, *, segments
 
 
 def chunk_fwd_gate(q, k, v, z, A_log, beta, S0=None, cu_seqlens=None, *, scale: float = 1.0,
-                   out_dtype=None, output_final_state: bool = True, o=None, S_T=None):
+                   out_dtype=None, output_final_state: bool = True, o=None, S_T=None,
+                   workspace="auto"):
     """chunk_fwd with the decay map in the kernel: g = -5 Sigmoid(exp(A_log[h]) z) is formed from
-    the logits z [B,T,H,dk] (q's dtype) and A_log [H] float32 instead of being read."""
+    the logits z [B,T,H,dk] (q's dtype) and A_log [H] float32 instead of being read.  workspace as
+    for chunk_fwd (its split in time when that pays)."""
     lib = load()
     a = _Prefill(q, k, v, beta, S0, cu_seqlens, out_dtype, output_final_state, o, S_T, z=z,
                  A_log=A_log)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        need = chunk_fwd_workspace_size(a.N, a.B * a.T, a.H, a.dk, a.dv, cu_seqlens is not None,
+                                        a.dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.dev) if need else None
+    if workspace is not None:
+        _require(workspace, "workspace", a.dev, torch.uint8)
+    nbytes = 0 if workspace is None else workspace.numel()
     st = _on(a.dev, lib.kda_chunk_fwd_gate, _p(q), _p(k), _p(v), _p(z), _p(A_log), _p(beta),
              _p(S0), _p(cu_seqlens), *a.sizes(q), float(scale), _p(a.o), _p(a.S_T),
-             _stream(a.dev))
+             _p(workspace), nbytes, _stream(a.dev))
     _check(st)
     return a.o, a.S_T
 

@@ -358,10 +358,12 @@ kda_status kda_chunk_fwd_gate(const void* q, const void* k, const void* v, const
                               const float* A_log, const void* beta, const float* S0,
                               const int32_t* cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t N,
                               int32_t dk, int32_t dv, kda_dtype in_dtype, kda_dtype out_dtype,
-                              float scale, void* o, float* S_T, hipStream_t stream) {
+                              float scale, void* o, float* S_T, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
     if (!z) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL%.0lld", "z");
     return chunk_fwd_impl(q, k, v, nullptr, z, A_log, beta, S0, cu_seqlens, B, T, H, N, dk, dv,
-                          in_dtype, out_dtype, scale, o, S_T, 0, 0, nullptr, 1, nullptr, 0, stream);
+                          in_dtype, out_dtype, scale, o, S_T, 0, 0, nullptr, 0, workspace,
+                          workspace_bytes, stream);
 }
 
 size_t kda_chunk_fwd_cp_workspace_size(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t segments) {

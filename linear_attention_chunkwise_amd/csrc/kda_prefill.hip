@@ -1336,16 +1336,12 @@ template <int DK, bool F32IN, bool OUT_F32, bool GATE>
 static hipError_t launch_prefill(const PrefillArgs& a) {
     const bool rank = a.cu && !a.plan && a.N > 1 && a.N <= kRankMax;
     if (a.mode == 1 || a.mode == 2) {
-        // the passes of a split in time (the decay map is not offered there)
-        if constexpr (GATE) {
-            return hipErrorInvalidValue;
-        } else {
-            if (a.mode == 1)
-                return rank ? launch_one<DK, F32IN, OUT_F32, GATE, true, 1>(a)
-                            : launch_one<DK, F32IN, OUT_F32, GATE, false, 1>(a);
-            return rank ? launch_one<DK, F32IN, OUT_F32, GATE, true, 2>(a)
-                        : launch_one<DK, F32IN, OUT_F32, GATE, false, 2>(a);
-        }
+        // the passes of a split in time
+        if (a.mode == 1)
+            return rank ? launch_one<DK, F32IN, OUT_F32, GATE, true, 1>(a)
+                        : launch_one<DK, F32IN, OUT_F32, GATE, false, 1>(a);
+        return rank ? launch_one<DK, F32IN, OUT_F32, GATE, true, 2>(a)
+                    : launch_one<DK, F32IN, OUT_F32, GATE, false, 2>(a);
     }
     if (rank) return launch_one<DK, F32IN, OUT_F32, GATE, true, 0>(a);
     return launch_one<DK, F32IN, OUT_F32, GATE, false, 0>(a);
@@ -1418,7 +1414,8 @@ bool split_may_pay(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv, int 
 
 // Decay probe: workgroup (sample j, channel group) sums g over the 32 tokens that start at
 // j / kProbeChunks of the batch (rounded down to a multiple of 32) for its channels and records
-// the smallest decay among them (nats; 0 for a NaN sum, +inf for an empty sample).
+// the smallest decay among them (nats; 0 for a NaN sum, +inf for an empty sample).  With logits
+// z instead of g, g is formed by the map of eq. (5) first.
 __global__ __launch_bounds__(256) void probe_kernel(PrefillArgs a, int32_t* __restrict__ probe, int64_t tokens) {
     __shared__ float red[256];
     const int j = blockIdx.x / kProbeGroups, grp = blockIdx.x % kProbeGroups;
@@ -1427,8 +1424,20 @@ __global__ __launch_bounds__(256) void probe_kernel(PrefillArgs a, int32_t* __re
     float dmin = __builtin_inff();
     for (int64_t c = (int64_t)grp * 256 + threadIdx.x; c < nch && t0 < t1; c += 256 * kProbeGroups) {
         float x[32];
+        if (a.z) {
+            const float es = __expf(a.A_log[c / a.dk]);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = t0 + i < t1 ? a.g[(t0 + i) * nch + c] : 0.f;   // loads in flight together
+            for (int i = 0; i < 32; ++i) {
+                const int64_t idx = (t0 + i) * nch + c;
+                const float zv = t0 + i >= t1 ? 0.f
+                                 : a.in_f32 ? static_cast<const float*>(a.z)[idx]
+                                            : __builtin_bit_cast(float, (uint32_t)static_cast<const uint16_t*>(a.z)[idx] << 16);
+                x[i] = t0 + i < t1 ? kGmin / (1.f + __expf(-es * zv)) : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) x[i] = t0 + i < t1 ? a.g[(t0 + i) * nch + c] : 0.f;   // loads in flight together
+        }
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; ++i) sum += x[i];

@@ -246,12 +246,12 @@ def test_recurrent_multi_empty_work_is_ok(lib):
 
 def _gate(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, z=FAKE, A=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2,
-             N=1, dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None)
+             N=1, dk=128, dv=128, ind=0, outd=0, scale=1.0, o=FAKE * 8, ST=None, ws=None, wsb=0)
     a.update(kw)
     return lib.kda_chunk_fwd_gate(a["q"], a["k"], a["v"], a["z"], a["A"], a["beta"], a["S0"],
                                   a["cu"], a["B"], a["T"], a["H"], a["N"], a["dk"], a["dv"],
                                   a["ind"], a["outd"], ctypes.c_float(a["scale"]), a["o"], a["ST"],
-                                  None)
+                                  a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [

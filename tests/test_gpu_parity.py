@@ -1261,6 +1261,38 @@ def test_prefill_gate_varlen(gpu_lib):
     assert_close("S_T", ST.cpu().numpy(), rST)
 
 
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (64, 64, torch.float32)])
+def test_prefill_gate_split_in_time(gpu_lib, dk, dv, dtype):
+    """The decay map in the kernel with the automatic split in time: one long sequence of few
+    heads (the plan splits it; its probe maps the logits it samples) and a packed batch, against
+    the oracle fed the map of the same stored logits."""
+    from linear_attention_chunkwise_amd import binding
+    x = inputs.make_prefill_inputs(1, 12000, 2, dk, dv, dtype=dtype, seed=97, with_logits=True)
+    d = _to_dev(x)
+    need = binding.chunk_fwd_workspace_size(1, 12000, 2, dk, dv, False)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    o, ST = binding.chunk_fwd_gate(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta"], d["S0"],
+                                   out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    p = ws[:20].cpu().view(torch.int32).tolist()
+    print(f"  plan: L={p[0]} eager={p[3]} segments={p[4]}", flush=True)
+    assert p[0] > 0 and p[4] > 1 and p[3] == 1
+    ro, rST = _gate_oracle(x, x["S0"])
+    assert_close("o[gate split]", o.cpu().numpy(), ro)
+    assert_close("S_T[gate split]", ST.cpu().numpy(), rST)
+    cu = inputs.cu_from_lengths([9000, 300, 0, 4000, 1])
+    x = inputs.make_prefill_inputs(1, int(cu[-1]), 2, dk, dv, dtype=dtype, seed=98, cu_seqlens=cu,
+                                   with_logits=True)
+    d = _to_dev(x)
+    o, ST = binding.chunk_fwd_gate(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta"], d["S0"],
+                                   d["cu_seqlens"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rST = _gate_oracle(x, x["S0"], cu)
+    assert_close("o[gate split packed]", o.cpu().numpy(), ro)
+    assert_close("S_T[gate split packed]", ST.cpu().numpy(), rST)
+
+
 def test_workload_prefill_gate_b4_h32_t32k(gpu_lib):
     """The prefill workload with the map in the kernel, sampled (sequence, head) units."""
     from linear_attention_chunkwise_amd import binding
