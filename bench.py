@@ -431,7 +431,24 @@ def main():
             "what": "B=1, H=32, T=1048576, d=128 (13 of 128 key channels per head near g_min): "
                     "kda_chunk_fwd with the workspace of its automatic split (ms; plan as for "
                     "varlen64) and without (whole_ms, 64 workgroups)"}
-        del xl, ol, STl, ws
+        # the same sequence from logits: g formed in the kernel, whole and split in time
+        del xl
+        xz = inputs.make_prefill_inputs(lcfg.B, lcfg.T, lcfg.H, lcfg.dk, lcfg.dv, seed=0, device=dev,
+                                        A_std=lcfg.A_std, near_gmin_frac=lcfg.near_gmin_frac,
+                                        with_logits=True)
+        del xz["g"]
+        lz_ms = time_launches(lambda: binding.chunk_fwd_gate(xz["q"], xz["k"], xz["v"], xz["z"], xz["A_log"],
+                                                             xz["beta"], xz["S0"], o=ol, S_T=STl, workspace=None),
+                              reps=2, groups=1, warmup=1)
+        lza_ms = time_launches(lambda: binding.chunk_fwd_gate(xz["q"], xz["k"], xz["v"], xz["z"], xz["A_log"],
+                                                              xz["beta"], xz["S0"], o=ol, S_T=STl, workspace=ws),
+                               reps=2, groups=1, warmup=1)
+        res["prefill_long_t1m_gate"] = {
+            "tokens": lcfg.T, "ms": lza_ms, "whole_ms": lz_ms, "plan": plan_summary(ws if need else None, 1),
+            "tokens_per_s": lcfg.T / (lza_ms * 1e-3),
+            "what": "the same sequence from bf16 logits z and A_h: kda_chunk_fwd_gate with the "
+                    "workspace (ms) and without (whole_ms)"}
+        del xz, ol, STl, ws
         # context for the HBM fractions: what the vendor's own read+write kernels reach here
         xb = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         yb = torch.empty_like(xb)
